@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Benchmark of row-wise safe softmax on one MI355X.
+
+One step = one ``softmax_fwd`` call (dispatch + kernel) over the whole
+workload, inputs already resident in HBM.  The default workload is the fp16
+attention-score softmax [4,32,512,512] (65536 rows x 512 cols).  The metric is
+effective bandwidth: (bytes read + bytes written) / time, bytes = one read of
+the input plus one write of the output (GB = 1e9).
+
+Timing: W untimed warm-up steps, then exactly K steps bracketed by
+torch.cuda.synchronize() and HIP events recorded on the stream the kernels run
+on.  The input/output pairs rotate over enough buffers that the working set is
+at least 2x the 256 MB last-level cache, so reads come from HBM; a
+single-buffer ("hot") figure is reported separately.
+
+Also reported: the roofline of the dominant kernel (HBM, 8 TB/s), the 16-byte
+copy ceiling over the same bytes, and the CPU oracle's throughput on the host
+(a baseline, not a target).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--kernel FAMILY]
+    python bench.py --summarize-rocprof DIR   # turn rocprofv3 output into profiles/ text
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+# The pages' own figure for this metric and workload: 0.62 ms per call for
+# fp16 [4,32,512,512] on a 60-CU DCU (DCU case-study page, section 5.3),
+# i.e. 134217728 B / 0.62 ms.  Another machine: context only.
+PAGES_FP16_ATTN_GBPS = 134217728 / 0.62e-3 / 1e9
+KERNEL_SOURCES = ["rws_device.hpp", "rws_kernels.hpp", "rws_wave_row.hip",
+                  "rws_block_onepass.hip", "rws_two_pass.hip", "rws_splitk.hip"]
+KERNEL_SYMBOL = {"wave_row": "k_wave_row", "block_onepass": "k_block_onepass",
+                 "two_pass": "k_two_pass", "splitk": "k_splitk_stage"}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "row_wise_safe_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------
+# rocprofv3 summaries
+# --------------------------------------------------------------------------
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_rocprof(directory: str, workload: str, kernel: str, command: str) -> None:
+    """Write profiles/<kernel>_<workload>_*.txt from rocprofv3 output in `directory`.
+
+    Expects sub-directories 'trace' (--kernel-trace --stats), 'fetch'
+    (--pmc FETCH_SIZE) and 'write' (--pmc WRITE_SIZE), each holding the CSVs
+    rocprofv3 wrote.  FETCH_SIZE / WRITE_SIZE are KiB per dispatch; they are
+    scaled by what the same counter reads for the 16-byte copy kernel, whose
+    true traffic is known (its bytes read and written).
+    """
+    sym = KERNEL_SYMBOL[kernel]
+    lines = [f"# rocprofv3 summary: {kernel} on {workload}", f"# command: {command}", ""]
+    stats = glob.glob(os.path.join(directory, "trace", "**", "*kernel_stats.csv"), recursive=True)
+    if stats:
+        rows = _read_csv(stats[0])
+        lines.append("## kernel stats (--kernel-trace --stats)")
+        lines.append("name | calls | total_ns | average_ns | min_ns | max_ns | percentage")
+        for r in rows:
+            lines.append(" | ".join(str(r.get(k, "")) for k in
+                                    ("Name", "Calls", "TotalDurationNs", "AverageNs", "MinNs",
+                                     "MaxNs", "Percentage")))
+        lines.append("")
+    meta = {}
+    counters = {}
+    for which, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        files = glob.glob(os.path.join(directory, which, "**", "*counter_collection.csv"),
+                          recursive=True)
+        if not files:
+            continue
+        per = {}
+        for r in _read_csv(files[0]):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            per.setdefault(name, []).append(float(r.get("Counter_Value", 0.0)))
+        counters[counter] = per
+    copy_bytes = None
+    meta_path = os.path.join(directory, "bench_meta.json")
+    if os.path.exists(meta_path):
+        with open(meta_path) as f:
+            meta = json.load(f)
+        copy_bytes = meta.get("copy_bytes")
+    traffic = None
+    if counters.get("FETCH_SIZE") and counters.get("WRITE_SIZE") and copy_bytes:
+        def avg_for(per, pred):
+            vals = [v for name, vs in per.items() if pred(name) for v in vs]
+            return sum(vals) / len(vals) if vals else None
+        f_k = avg_for(counters["FETCH_SIZE"], lambda n: sym in n)
+        w_k = avg_for(counters["WRITE_SIZE"], lambda n: sym in n)
+        f_c = avg_for(counters["FETCH_SIZE"], lambda n: "k_copy16" in n)
+        w_c = avg_for(counters["WRITE_SIZE"], lambda n: "k_copy16" in n)
+        lines.append("## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch)")
+        lines.append(f"kernel {sym}: FETCH_SIZE {f_k} KiB, WRITE_SIZE {w_k} KiB")
+        lines.append(f"copy kernel k_copy16 ({copy_bytes} B read + {copy_bytes} B written): "
+                     f"FETCH_SIZE {f_c} KiB, WRITE_SIZE {w_c} KiB")
+        if None not in (f_k, w_k, f_c, w_c) and f_c > 0 and w_c > 0:
+            sf = copy_bytes / (f_c * 1024.0)
+            sw = copy_bytes / (w_c * 1024.0)
+            traffic = f_k * 1024.0 * sf + w_k * 1024.0 * sw
+            lines.append(f"scale factors (true bytes / counter bytes): fetch {sf:.4f}, write {sw:.4f}")
+            lines.append(f"traffic_bytes_per_launch: {traffic:.0f}")
+            if meta.get("bytes_per_call"):
+                lines.append(f"algorithmic_bytes_per_launch: {meta['bytes_per_call']}")
+                lines.append(f"traffic / algorithmic: {traffic / meta['bytes_per_call']:.4f}")
+        lines.append("")
+    lines.append(f"kernel_source_sha: {kernel_source_hash()}")
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"{kernel}_{workload}.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
+def read_traffic(workload: str, kernel: str):
+    """Counter-derived HBM bytes per launch from profiles/, or None when the
+    summary is missing or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    traffic = sha = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("traffic_bytes_per_launch:"):
+                traffic = float(line.split(":")[1])
+            elif line.startswith("kernel_source_sha:"):
+                sha = line.split(":")[1].strip()
+    if traffic is None or sha != kernel_source_hash():
+        return None
+    return traffic
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the oracle on the host cores
+# --------------------------------------------------------------------------
+def cpu_baseline(w, x_stored_f64, target_s: float = 10.0) -> dict:
+    import oracle
+    threads = max(1, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+                  else (os.cpu_count() or 1))
+    rows = x_stored_f64.shape[0]
+    t0 = time.perf_counter()
+    passes = 0
+    used = threads
+    while True:
+        _, used = oracle.safe_softmax_threads(x_stored_f64, threads)
+        passes += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    nbytes = 2 * rows * w.cols * w.elem_bytes * passes
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(used),
+            "kind": "oracle",
+            "sample": f"{passes} passes of the full {rows}x{w.cols} workload "
+                      f"(fp16 values widened to float64, fp64 libm exp), rows split over "
+                      f"{used} host threads; bytes counted as fp16 in+out, {dt:.1f} s"}
+
+
+# --------------------------------------------------------------------------
+# main
+# --------------------------------------------------------------------------
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="fp16_attn_4x32x512x512")
+    ap.add_argument("--kernel", default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--meta-out", default=None, help="write bench metadata JSON (for rocprof)")
+    ap.add_argument("--summarize-rocprof", default=None, metavar="DIR")
+    ap.add_argument("--profile-command", default="")
+    args = ap.parse_args()
+
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof, args.workload,
+                          args.kernel if args.kernel != "auto" else "wave_row",
+                          args.profile_command)
+        return 0
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows shard across GPUs with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import row_wise_safe_amd as rws
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    rws.load_library()
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    code = rws.dtype_code(tdt)
+    kid = rws.KERNEL_IDS[args.kernel]
+
+    log(f"[bench] generating {w.name} {w.rows}x{w.cols} {w.dtype}")
+    x64 = w.generate()
+    x_host = torch.from_numpy(x64).to(tdt)
+    del x64
+    nbytes = w.algorithmic_bytes
+    in_bytes = nbytes // 2
+    # rotate over enough input/output pairs to exceed 2 x 256 MB last-level cache
+    nbuf = max(2, -(-512 * 2**20 // nbytes))
+    xs = [x_host.to(dev) for _ in range(nbuf)]
+    ys = [torch.empty_like(xs[0]) for _ in range(nbuf)]
+    stream = torch.cuda.current_stream(dev)
+    sh = int(stream.cuda_stream)
+    desc = rws.softmax_describe_launch(w.rows, w.cols, code, xs[0].data_ptr(), ys[0].data_ptr(),
+                                       kid)
+    family = desc.split("<")[0]
+    log(f"[bench] launch: {desc}; {nbuf} rotating buffer pairs")
+
+    def step(i):
+        st = rws.softmax_fwd_kernel(xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), w.rows,
+                                    w.cols, code, sh, kid)
+        if st != rws.RWS_OK:
+            raise rws.SoftmaxError(st, rws.softmax_last_error())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] {ms * 1e3:.2f} us/call, {gbps:.1f} GB/s (rotating)")
+
+    # single buffer (hot, last-level-cache resident input)
+    for i in range(args.warmup):
+        rws.softmax_fwd_kernel(xs[0].data_ptr(), ys[0].data_ptr(), w.rows, w.cols, code, sh, kid)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    hot_steps = max(10, args.steps // 2)
+    for i in range(hot_steps):
+        rws.softmax_fwd_kernel(xs[0].data_ptr(), ys[0].data_ptr(), w.rows, w.cols, code, sh, kid)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    hot_ms = e0.elapsed_time(e1) / hot_steps
+
+    # copy ceiling: 16-byte copy of the input bytes, same rotation
+    for i in range(args.warmup):
+        rws.softmax_copy_bytes(xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), in_bytes, sh)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        rws.softmax_copy_bytes(xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), in_bytes, sh)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1) / args.steps
+    copy_gbps = nbytes / (copy_ms * 1e-3) / 1e9
+    log(f"[bench] copy ceiling {copy_ms * 1e3:.2f} us, {copy_gbps:.1f} GB/s")
+
+    if args.meta_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.meta_out)), exist_ok=True)
+        with open(args.meta_out, "w") as f:
+            json.dump({"workload": w.name, "bytes_per_call": nbytes, "copy_bytes": in_bytes,
+                       "launch": desc}, f)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        stored = x_host.to(torch.float64).numpy()
+        cpu = cpu_baseline(w, stored, args.cpu_seconds)
+        log(f"[bench] cpu oracle {cpu['value']} GB/s on {cpu['cores']} threads")
+
+    traffic = read_traffic(w.name, family)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    vs = round(gbps / PAGES_FP16_ATTN_GBPS, 3) if w.name == "fp16_attn_4x32x512x512" else None
+    result = {
+        "metric": f"effective HBM GB/s (read+write), {w.description}",
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "us_per_call": round(ms * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": vs,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "rows": w.rows, "cols": w.cols,
+                   "bytes_per_call": nbytes, "launch": desc, "rotating_buffers": nbuf,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic},
+        "hot_single_buffer": {"us_per_call": round(hot_ms * 1e3, 3),
+                              "GBps": round(nbytes / (hot_ms * 1e-3) / 1e9, 2)},
+        "copy_ceiling": {"us_per_call": round(copy_ms * 1e3, 3), "GBps": round(copy_gbps, 2),
+                         "frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,160 @@
+/*
+ * row_wise_softmax.h -- C ABI of the MI355X (gfx950) row-wise safe softmax
+ * library (librws_softmax.so).
+ *
+ * Operation.  For a contiguous row-major matrix X[rows, cols] the library
+ * writes, for every row r and column j,
+ *
+ *     Y[r, j] = exp(X[r, j] - m_r) / d_r,
+ *     m_r     = max_j X[r, j],
+ *     d_r     = sum_j exp(X[r, j] - m_r),
+ *
+ * i.e. softmax along the last dimension in its numerically safe form
+ * (HIP softmax tutorial page, sections 1 and 5; CUDA safe-online-softmax page,
+ * section 1).  Depending on the shape, the kernels obtain (m_r, d_r) directly,
+ * with the running update m' = max(m, x), d' = d e^(m - m') + e^(x - m')
+ * (DCU case-study page, section 4.3; CUDA safe-online-softmax page, section 1),
+ * or by merging per-chunk partials with
+ * (m, d) (+) (m', d') = (M, d e^(m - M) + d' e^(m' - M)), M = max(m, m')
+ * (CUDA safe-online-softmax page, sections 2.1.1 and 3.2).  All of these are
+ * re-associations of the same sums; every path accumulates in fp32.
+ *
+ * Data types (in dtype == out dtype, fp32 accumulation):
+ *     RWS_F32 = 0  IEEE binary32
+ *     RWS_F16 = 1  IEEE binary16
+ *     RWS_BF16 = 2 bfloat16
+ * Outputs are rounded to nearest-even from the fp32 result.
+ *
+ * Layout.  `in` and `out` point to rows*cols elements, row-major, row pitch
+ * == cols (no stride argument).  Pointers must be device memory of the current
+ * HIP device and aligned to the element size; 16-byte alignment is NOT
+ * required (rows of any length and any start address are handled).  Exact
+ * aliasing (in == out, in-place) is allowed; partial overlap is undefined.
+ *
+ * Streams.  `stream` is a hipStream_t passed as an opaque pointer (NULL = the
+ * null stream).  All work is enqueued on it; no call synchronises the host.
+ * The result is valid once the stream reaches the enqueued work.
+ *
+ * Ownership.  The caller owns `in` and `out`.  For the split-k path the
+ * library owns a small workspace (8 bytes per row per chunk) that it keeps
+ * per (device, stream) and grows on demand; the first call that needs a
+ * larger workspace allocates it (hipMalloc), later calls reuse it.  Calls on
+ * one stream are ordered, so reuse is safe; the workspaces are released when
+ * the library is unloaded.
+ *
+ * Errors.  Every entry point returns a status code (below) and never exits or
+ * throws.  rows == 0 or cols == 0 is a successful no-op.  A HIP launch error
+ * is reported as RWS_ERR_HIP; softmax_last_error() then returns the detail
+ * (thread-local, valid until the next call on the same thread).
+ */
+#ifndef ROW_WISE_SOFTMAX_H
+#define ROW_WISE_SOFTMAX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+enum {
+    RWS_F32 = 0,
+    RWS_F16 = 1,
+    RWS_BF16 = 2
+};
+
+/* Status codes. */
+enum {
+    RWS_OK = 0,
+    RWS_ERR_INVALID_ARG = 1,       /* negative size, NULL pointer with data, bad id */
+    RWS_ERR_UNSUPPORTED_DTYPE = 2, /* dtype not one of RWS_F32/F16/BF16 */
+    RWS_ERR_MISALIGNED = 3,        /* pointer not aligned to the element size */
+    RWS_ERR_HIP = 4,               /* HIP runtime error (see softmax_last_error) */
+    RWS_ERR_UNSUPPORTED_SHAPE = 5  /* forced kernel cannot take this shape */
+};
+
+/* Kernel families (ids for softmax_fwd_kernel / softmax_select_kernel). */
+enum {
+    RWS_KERNEL_AUTO = 0,      /* let the dispatcher choose */
+    RWS_KERNEL_WAVE_ROW = 1,  /* one row per 64-lane wave (or per 4..32-lane
+                                 group, several rows per wave); row cached in
+                                 registers; cross-lane reductions without LDS
+                                 (DCU case-study page, sections 4.1 and 8) */
+    RWS_KERNEL_BLOCK_ONEPASS = 2, /* one workgroup per row; the row is read
+                                 once and cached in registers, then LDS
+                                 (CUDA safe-online-softmax page, sections 2.1
+                                 and 2.2) */
+    RWS_KERNEL_TWO_PASS = 3,  /* one workgroup per row, any cols: pass 1 running
+                                 (m, d), pass 2 re-reads the row (CUDA
+                                 safe-online-softmax page, section 3.1) */
+    RWS_KERNEL_SPLITK = 4     /* several workgroups per row: stage 1 writes a
+                                 partial (m, d) per chunk, stage 2 merges a
+                                 row's partials and writes the outputs (CUDA
+                                 safe-online-softmax page, section 3.2) */
+};
+
+/*
+ * softmax_fwd -- Y = softmax(X) along the last dimension, kernel chosen by
+ * the dispatcher from (rows, cols, dtype, pointer alignment, device).
+ *   in, out : device pointers, rows*cols elements of `dtype` each
+ *   rows    : number of rows (>= 0)
+ *   cols    : row length (>= 0)
+ *   dtype   : RWS_F32, RWS_F16 or RWS_BF16
+ *   stream  : hipStream_t (NULL = null stream)
+ * Returns RWS_OK or an error status.
+ */
+int softmax_fwd(const void *in, void *out, int64_t rows, int64_t cols, int dtype,
+                void *stream);
+
+/*
+ * softmax_fwd_kernel -- as softmax_fwd, but runs the given kernel family
+ * (RWS_KERNEL_*; RWS_KERNEL_AUTO behaves like softmax_fwd).  Returns
+ * RWS_ERR_UNSUPPORTED_SHAPE if that family cannot take the shape (the
+ * register/LDS-cached families have a maximum row length).  For tests and
+ * measurement.
+ */
+int softmax_fwd_kernel(const void *in, void *out, int64_t rows, int64_t cols, int dtype,
+                       void *stream, int kernel_id);
+
+/*
+ * softmax_select_kernel -- the family softmax_fwd would run for this shape
+ * with pointers `in` and `out` (their alignment matters), on the current
+ * device.  Returns a RWS_KERNEL_* id (> 0), or a negative status on invalid
+ * arguments.  Performs no GPU work.
+ */
+int softmax_select_kernel(int64_t rows, int64_t cols, int dtype, const void *in,
+                          const void *out);
+
+/*
+ * softmax_describe_launch -- writes a one-line, NUL-terminated description of
+ * the launch softmax_fwd_kernel(kernel_id) would make (variant, grid, block,
+ * chunks) into buf (at most buflen bytes).  Returns RWS_OK or an error
+ * status.  Performs no GPU work.
+ */
+int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void *in,
+                            const void *out, int kernel_id, char *buf, int64_t buflen);
+
+/* Name of a kernel family ("wave_row", ...), or "unknown". Static storage. */
+const char *softmax_kernel_name(int kernel_id);
+
+/* Text of a status code. Static storage. */
+const char *softmax_status_string(int status);
+
+/* Detail of the last error on this thread ("" if none). */
+const char *softmax_last_error(void);
+
+/*
+ * softmax_copy_bytes -- plain device-to-device copy of `bytes` bytes with
+ * 16-byte loads and stores (both pointers 16-byte aligned, bytes % 16 == 0),
+ * on `stream`.  It is the reference point for the effective-bandwidth figure
+ * (bytes read plus bytes written per unit time, DCU case-study page, sections
+ * 3.2 and 5.3): the copy ceiling, and the calibration of hardware traffic
+ * counters.  Returns RWS_OK or an error status.
+ */
+int softmax_copy_bytes(const void *in, void *out, int64_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROW_WISE_SOFTMAX_H */

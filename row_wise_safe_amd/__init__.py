@@ -1,0 +1,186 @@
+"""Python binding of librws_softmax.so -- row-wise safe softmax on MI355X.
+
+Argument marshalling only: every step of the computation runs in the
+library's gfx950 HIP kernels.  The functions named ``softmax_*`` mirror the C
+ABI of ``include/row_wise_softmax.h`` one to one (plain integers for pointers,
+sizes and the stream); :func:`softmax` is the tensor-level convenience that
+fills them in from a torch tensor and the current stream.
+
+torch is imported first so that the process has a single HIP runtime (the
+library then binds to the one torch loaded).  If the library has not been
+built, every entry point raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "RWS_F32", "RWS_F16", "RWS_BF16",
+    "RWS_OK", "RWS_ERR_INVALID_ARG", "RWS_ERR_UNSUPPORTED_DTYPE", "RWS_ERR_MISALIGNED",
+    "RWS_ERR_HIP", "RWS_ERR_UNSUPPORTED_SHAPE",
+    "KERNELS", "KERNEL_IDS",
+    "library_path", "load_library",
+    "softmax_fwd", "softmax_fwd_kernel", "softmax_select_kernel", "softmax_describe_launch",
+    "softmax_kernel_name", "softmax_status_string", "softmax_last_error", "softmax_copy_bytes",
+    "softmax", "copy_bytes", "dtype_code", "SoftmaxError",
+]
+
+RWS_F32, RWS_F16, RWS_BF16 = 0, 1, 2
+RWS_OK = 0
+RWS_ERR_INVALID_ARG = 1
+RWS_ERR_UNSUPPORTED_DTYPE = 2
+RWS_ERR_MISALIGNED = 3
+RWS_ERR_HIP = 4
+RWS_ERR_UNSUPPORTED_SHAPE = 5
+
+KERNEL_IDS = {"auto": 0, "wave_row": 1, "block_onepass": 2, "two_pass": 3, "splitk": 4}
+KERNELS = tuple(k for k in KERNEL_IDS if k != "auto")
+
+_DTYPES = {torch.float32: RWS_F32, torch.float16: RWS_F16, torch.bfloat16: RWS_BF16}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class SoftmaxError(RuntimeError):
+    def __init__(self, status: int, detail: str = ""):
+        self.status = status
+        text = softmax_status_string(status) if _LIB is not None else f"status {status}"
+        super().__init__(f"{text}: {detail}" if detail else text)
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "librws_softmax.so")
+
+
+def load_library():
+    """Load librws_softmax.so; raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it first (python row_wise_safe_amd/build.py or "
+            "__graft_entry__.build()); there is no non-HIP fallback")
+    lib = ctypes.CDLL(path)
+    i64, vp, cint = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.softmax_fwd.argtypes = [vp, vp, i64, i64, cint, vp]
+    lib.softmax_fwd.restype = cint
+    lib.softmax_fwd_kernel.argtypes = [vp, vp, i64, i64, cint, vp, cint]
+    lib.softmax_fwd_kernel.restype = cint
+    lib.softmax_select_kernel.argtypes = [i64, i64, cint, vp, vp]
+    lib.softmax_select_kernel.restype = cint
+    lib.softmax_describe_launch.argtypes = [i64, i64, cint, vp, vp, cint, ctypes.c_char_p, i64]
+    lib.softmax_describe_launch.restype = cint
+    lib.softmax_kernel_name.argtypes = [cint]
+    lib.softmax_kernel_name.restype = ctypes.c_char_p
+    lib.softmax_status_string.argtypes = [cint]
+    lib.softmax_status_string.restype = ctypes.c_char_p
+    lib.softmax_last_error.argtypes = []
+    lib.softmax_last_error.restype = ctypes.c_char_p
+    lib.softmax_copy_bytes.argtypes = [vp, vp, i64, vp]
+    lib.softmax_copy_bytes.restype = cint
+    _LIB = lib
+    return lib
+
+
+# --- the C ABI, one to one --------------------------------------------------
+
+def softmax_fwd(in_ptr: int, out_ptr: int, rows: int, cols: int, dtype: int, stream: int) -> int:
+    return load_library().softmax_fwd(in_ptr, out_ptr, rows, cols, dtype, stream)
+
+
+def softmax_fwd_kernel(in_ptr: int, out_ptr: int, rows: int, cols: int, dtype: int, stream: int,
+                       kernel_id: int) -> int:
+    return load_library().softmax_fwd_kernel(in_ptr, out_ptr, rows, cols, dtype, stream,
+                                             kernel_id)
+
+
+def softmax_select_kernel(rows: int, cols: int, dtype: int, in_ptr: int = 0,
+                          out_ptr: int = 0) -> int:
+    return load_library().softmax_select_kernel(rows, cols, dtype, in_ptr, out_ptr)
+
+
+def softmax_describe_launch(rows: int, cols: int, dtype: int, in_ptr: int = 0, out_ptr: int = 0,
+                            kernel_id: int = 0) -> str:
+    buf = ctypes.create_string_buffer(256)
+    st = load_library().softmax_describe_launch(rows, cols, dtype, in_ptr, out_ptr, kernel_id,
+                                                buf, len(buf))
+    if st != RWS_OK:
+        raise SoftmaxError(st, softmax_last_error())
+    return buf.value.decode()
+
+
+def softmax_kernel_name(kernel_id: int) -> str:
+    return load_library().softmax_kernel_name(kernel_id).decode()
+
+
+def softmax_status_string(status: int) -> str:
+    return load_library().softmax_status_string(status).decode()
+
+
+def softmax_last_error() -> str:
+    return load_library().softmax_last_error().decode()
+
+
+def softmax_copy_bytes(in_ptr: int, out_ptr: int, nbytes: int, stream: int) -> int:
+    return load_library().softmax_copy_bytes(in_ptr, out_ptr, nbytes, stream)
+
+
+# --- tensor convenience -----------------------------------------------------
+
+def dtype_code(dtype: torch.dtype) -> int:
+    try:
+        return _DTYPES[dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {dtype}; expected float32, float16 or bfloat16")
+
+
+def _stream_handle(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def softmax(x: torch.Tensor, out: torch.Tensor | None = None, kernel: str = "auto",
+            stream=None) -> torch.Tensor:
+    """Softmax of ``x`` along its last dimension (any contiguous GPU tensor).
+
+    ``out`` (same shape and dtype, contiguous) may be ``x`` itself (in place).
+    ``kernel`` forces a family (``"wave_row"``, ``"block_onepass"``,
+    ``"two_pass"``, ``"splitk"``) instead of the dispatcher's choice.
+    Work is enqueued on ``stream`` (default: the current stream).
+    """
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    code = dtype_code(x.dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or \
+            out.device != x.device:
+        raise ValueError("out must be a contiguous tensor of x's shape, dtype and device")
+    cols = x.shape[-1] if x.dim() > 0 else 1
+    rows = x.numel() // cols if cols > 0 else 0
+    st = load_library().softmax_fwd_kernel(x.data_ptr(), out.data_ptr(), rows, cols, code,
+                                           _stream_handle(x.device, stream), KERNEL_IDS[kernel])
+    if st != RWS_OK:
+        raise SoftmaxError(st, softmax_last_error())
+    return out
+
+
+def copy_bytes(src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tensor:
+    """16-byte-vector device copy of src's bytes into dst (bandwidth reference)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    st = load_library().softmax_copy_bytes(src.data_ptr(), dst.data_ptr(), nbytes,
+                                           _stream_handle(src.device, stream))
+    if st != RWS_OK:
+        raise SoftmaxError(st, softmax_last_error())
+    return dst

@@ -1,0 +1,453 @@
+// rws_api.cpp -- C ABI of the row-wise softmax library: argument checks, the
+// cols-and-dtype dispatcher, the split-k workspace cache and error reporting.
+// The declarations and their contract are in include/row_wise_softmax.h.
+//
+// Dispatch (the choice of kernel per shape is the question the CUDA
+// safe-online-softmax page leaves open in its summary, section 4.3; the HIP
+// tutorial page, section 7, switches by a cols threshold and notes that the
+// threshold must be tuned per device):
+//   * the row window (16-byte granules covering a row) fits one wave's
+//     registers  -> wave_row, with the narrowest lane group that holds it;
+//   * few rows of long rows                     -> split-k over many workgroups;
+//   * fits a workgroup's registers (+ LDS)      -> block_onepass;
+//   * otherwise                                 -> two_pass.
+// The thresholds are set from measurements on MI355X.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <algorithm>
+#include <utility>
+
+#include "row_wise_softmax.h"
+#include "rws_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+    g_last_error = msg;
+    return status;
+}
+
+int elem_size(int dtype) { return dtype == RWS_F32 ? 4 : 2; }
+const char* dtype_name(int dtype) {
+    return dtype == RWS_F32 ? "f32" : dtype == RWS_F16 ? "f16" : "bf16";
+}
+
+// Longest row the kernels index with 32-bit element offsets.
+constexpr int64_t kMaxCols = (int64_t)1 << 30;
+
+struct DeviceInfo {
+    int cus = 256;
+    bool known = false;
+};
+
+DeviceInfo device_info() {
+    static std::mutex mu;
+    static std::map<int, DeviceInfo> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return DeviceInfo{};
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    DeviceInfo info;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0) {
+        info.cus = cus;
+        info.known = true;
+    } else {
+        (void)hipGetLastError();
+    }
+    cache[dev] = info;
+    return info;
+}
+
+struct Plan {
+    int family = 0;   // RWS_KERNEL_*
+    int variant = 0;  // index into that family's variant table
+    int P = 1;        // split-k chunks per row
+    int64_t max_rows_per_launch = 0;
+    bool aligned = false;
+    bool same_phase = false;
+};
+
+// Upper bound of the number of 16-byte granules that overlap one row.
+int64_t window_max(int64_t cols, int dtype, bool aligned) {
+    const int64_t bytes = cols * elem_size(dtype);
+    if (aligned) return bytes / 16;
+    return (bytes + 15 + 15) / 16;
+}
+
+int64_t onepass_capacity(const rws::OnepassVariant& v) { return (int64_t)v.block * (v.kr + v.kl); }
+
+// Choose among the wave_row variants: the narrowest lane group whose
+// registers hold the window, and enough row sets in flight per wave.
+int pick_wave_row(int64_t wmax) {
+    int best = -1;
+    int64_t best_key = 0;
+    for (int i = 0; i < rws::kNumWaveRow; ++i) {
+        const rws::WaveRowVariant& v = rws::kWaveRow[i];
+        if ((int64_t)v.G * v.K < wmax) continue;
+        // prefer the smallest capacity, then 4 granules in flight per lane
+        const int64_t cap = (int64_t)v.G * v.K;
+        const int inflight = v.K * v.U;
+        const int64_t key = cap * 64 + (inflight == 4 ? 0 : inflight < 4 ? 8 - inflight : inflight);
+        if (best < 0 || key < best_key) {
+            best = i;
+            best_key = key;
+        }
+    }
+    return best;
+}
+
+int pick_onepass(int64_t wmax) {
+    int best = -1;
+    for (int i = 0; i < rws::kNumOnepass; ++i) {
+        if (onepass_capacity(rws::kOnepass[i]) < wmax) continue;
+        if (best < 0 || onepass_capacity(rws::kOnepass[i]) < onepass_capacity(rws::kOnepass[best]))
+            best = i;
+    }
+    return best;
+}
+
+// Split-k chunking: the largest chunk that still gives every CU at least two
+// workgroups, else the smallest chunk.
+int pick_splitk(int64_t rows, int64_t wmax, int cus, int* P_out) {
+    int best = -1;
+    int bestP = 1;
+    for (int i = 0; i < rws::kNumSplitk; ++i) {
+        const rws::SplitkVariant& v = rws::kSplitk[i];
+        if (v.block != 256) continue;
+        const int64_t cg = (int64_t)v.block * v.kc;
+        const int64_t P = (wmax + cg - 1) / cg;
+        if (P > (1 << 20)) continue;
+        if (rows * P >= 2LL * cus) {
+            if (best < 0 || rws::kSplitk[i].kc > rws::kSplitk[best].kc) {
+                best = i;
+                bestP = (int)P;
+            }
+        }
+    }
+    if (best < 0) {
+        for (int i = 0; i < rws::kNumSplitk; ++i) {
+            const rws::SplitkVariant& v = rws::kSplitk[i];
+            if (v.block != 256) continue;
+            const int64_t cg = (int64_t)v.block * v.kc;
+            const int64_t P = (wmax + cg - 1) / cg;
+            if (best < 0 || v.kc < rws::kSplitk[best].kc) {
+                best = i;
+                bestP = (int)P;
+            }
+        }
+    }
+    *P_out = bestP;
+    return best;
+}
+
+int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
+                int kernel_id, Plan* p) {
+    const uintptr_t ai = (uintptr_t)in, ao = (uintptr_t)out;
+    p->aligned = (ai % 16 == 0) && (ao % 16 == 0) && ((cols * elem_size(dtype)) % 16 == 0);
+    p->same_phase = (ai % 16) == (ao % 16);
+    const int64_t wmax = window_max(cols, dtype, p->aligned);
+    const int cus = device_info().cus;
+
+    int family = kernel_id;
+    if (family == RWS_KERNEL_AUTO) {
+        const int64_t wave_cap = 64 * 8;  // largest wave_row window (G=64, K=8)
+        const bool few_rows = rows < 2LL * cus;
+        if (wmax <= 128) {
+            family = RWS_KERNEL_WAVE_ROW;
+        } else if (few_rows && wmax >= 2048) {
+            family = RWS_KERNEL_SPLITK;
+        } else if (wmax <= 512 && wmax <= wave_cap) {
+            family = RWS_KERNEL_WAVE_ROW;
+        } else if (pick_onepass(wmax) >= 0 && wmax <= 8192) {
+            family = RWS_KERNEL_BLOCK_ONEPASS;
+        } else if (few_rows) {
+            family = RWS_KERNEL_SPLITK;
+        } else if (pick_onepass(wmax) >= 0) {
+            family = RWS_KERNEL_BLOCK_ONEPASS;
+        } else {
+            family = RWS_KERNEL_TWO_PASS;
+        }
+    }
+    p->family = family;
+    switch (family) {
+        case RWS_KERNEL_WAVE_ROW: {
+            p->variant = pick_wave_row(wmax);
+            if (p->variant < 0)
+                return fail(RWS_ERR_UNSUPPORTED_SHAPE,
+                            "wave_row holds at most 512 granules (16 bytes) per row");
+            const rws::WaveRowVariant& v = rws::kWaveRow[p->variant];
+            // keep (workgroups x 256 threads) of one launch below 2^32
+            p->max_rows_per_launch = (int64_t)(64 / v.G) * v.U * 4 * ((int64_t)1 << 23);
+            break;
+        }
+        case RWS_KERNEL_BLOCK_ONEPASS: {
+            p->variant = pick_onepass(wmax);
+            if (p->variant < 0)
+                return fail(RWS_ERR_UNSUPPORTED_SHAPE,
+                            "block_onepass holds at most 16384 granules (16 bytes) per row");
+            p->max_rows_per_launch = (int64_t)1 << 22;
+            break;
+        }
+        case RWS_KERNEL_TWO_PASS: {
+            // 256 threads for short rows, 512 up to 4096 granules, then 1024
+            const int want_block = wmax > 4096 ? 1024 : wmax > 1024 ? 512 : 256;
+            p->variant = 0;
+            for (int i = 0; i < rws::kNumTwoPass; ++i)
+                if (rws::kTwoPass[i].block == want_block && rws::kTwoPass[i].u == 4) p->variant = i;
+            p->max_rows_per_launch = (int64_t)1 << 22;
+            break;
+        }
+        case RWS_KERNEL_SPLITK: {
+            int P = 1;
+            p->variant = pick_splitk(rows, wmax, cus, &P);
+            if (p->variant < 0) return fail(RWS_ERR_UNSUPPORTED_SHAPE, "split-k: no variant");
+            p->P = P;
+            p->max_rows_per_launch = std::max<int64_t>(1, ((int64_t)1 << 23) / P);
+            break;
+        }
+        default:
+            return fail(RWS_ERR_INVALID_ARG, "unknown kernel id " + std::to_string(kernel_id));
+    }
+    return RWS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// split-k workspace: one grow-only buffer per (device, stream).  Work on one
+// stream is ordered, so a buffer is never used by two launches at once.
+// ---------------------------------------------------------------------------
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace>* g_ws = nullptr;
+
+struct WorkspaceReaper {
+    ~WorkspaceReaper() {
+        // Buffers are released at unload; a device that is already torn down
+        // reports an error here, which is ignored.
+        if (!g_ws) return;
+        for (auto& kv : *g_ws)
+            if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+        delete g_ws;
+        g_ws = nullptr;
+    }
+} g_ws_reaper;
+
+int get_workspace(hipStream_t stream, size_t bytes, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RWS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    if (!g_ws) g_ws = new std::map<std::pair<int, hipStream_t>, Workspace>();
+    Workspace& w = (*g_ws)[std::make_pair(dev, stream)];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            // the old buffer may still be read by earlier work on this stream
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess)
+                return fail(RWS_ERR_HIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        size_t want = 4096;
+        while (want < bytes) want *= 2;
+        if (std::getenv("RWS_TEST_FAIL_ALLOC"))
+            return fail(RWS_ERR_HIP, "workspace allocation failed (RWS_TEST_FAIL_ALLOC)");
+        e = hipMalloc(&w.ptr, want);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            return fail(RWS_ERR_HIP, std::string("hipMalloc (split-k workspace): ") + hipGetErrorString(e));
+        }
+        w.bytes = want;
+    }
+    *out = w.ptr;
+    return RWS_OK;
+}
+
+int check_args(const void* in, void* out, int64_t rows, int64_t cols, int dtype, int kernel_id) {
+    if (dtype != RWS_F32 && dtype != RWS_F16 && dtype != RWS_BF16)
+        return fail(RWS_ERR_UNSUPPORTED_DTYPE, "dtype must be RWS_F32, RWS_F16 or RWS_BF16");
+    if (kernel_id < RWS_KERNEL_AUTO || kernel_id > RWS_KERNEL_SPLITK)
+        return fail(RWS_ERR_INVALID_ARG, "unknown kernel id " + std::to_string(kernel_id));
+    if (rows < 0 || cols < 0) return fail(RWS_ERR_INVALID_ARG, "rows and cols must be >= 0");
+    if (cols > kMaxCols) return fail(RWS_ERR_UNSUPPORTED_SHAPE, "cols above 2^30");
+    if (rows == 0 || cols == 0) return RWS_OK;
+    if (!in || !out) return fail(RWS_ERR_INVALID_ARG, "NULL pointer with a non-empty tensor");
+    const int es = elem_size(dtype);
+    if ((uintptr_t)in % es || (uintptr_t)out % es)
+        return fail(RWS_ERR_MISALIGNED, "pointer not aligned to the element size");
+    return RWS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int softmax_fwd_kernel(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
+                       void* stream, int kernel_id) {
+    g_last_error.clear();
+    int st = check_args(in, out, rows, cols, dtype, kernel_id);
+    if (st != RWS_OK || rows == 0 || cols == 0) return st;
+    Plan p;
+    st = plan_launch(rows, cols, dtype, in, out, kernel_id, &p);
+    if (st != RWS_OK) return st;
+
+    void* ws = nullptr;
+    hipStream_t s = (hipStream_t)stream;
+    if (p.family == RWS_KERNEL_SPLITK) {
+        const int64_t batch = std::min<int64_t>(rows, p.max_rows_per_launch);
+        st = get_workspace(s, (size_t)batch * p.P * sizeof(float2), &ws);
+        if (st != RWS_OK) return st;
+    }
+    const int64_t row_bytes = cols * elem_size(dtype);
+    for (int64_t r0 = 0; r0 < rows; r0 += p.max_rows_per_launch) {
+        rws::Launch L;
+        L.rows = std::min<int64_t>(p.max_rows_per_launch, rows - r0);
+        L.in = (const char*)in + r0 * row_bytes;
+        L.out = (char*)out + r0 * row_bytes;
+        L.cols = (int)cols;
+        L.dtype = dtype;
+        L.aligned = p.aligned;
+        L.same_phase = p.same_phase;
+        L.stream = s;
+        hipError_t e = hipSuccess;
+        switch (p.family) {
+            case RWS_KERNEL_WAVE_ROW: e = rws::launch_wave_row(L, p.variant); break;
+            case RWS_KERNEL_BLOCK_ONEPASS: e = rws::launch_block_onepass(L, p.variant); break;
+            case RWS_KERNEL_TWO_PASS: e = rws::launch_two_pass(L, p.variant); break;
+            case RWS_KERNEL_SPLITK: e = rws::launch_splitk(L, p.variant, p.P, (float2*)ws); break;
+        }
+        if (e != hipSuccess)
+            return fail(RWS_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    }
+    return RWS_OK;
+}
+
+int softmax_fwd(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream) {
+    return softmax_fwd_kernel(in, out, rows, cols, dtype, stream, RWS_KERNEL_AUTO);
+}
+
+int softmax_select_kernel(int64_t rows, int64_t cols, int dtype, const void* in, const void* out) {
+    g_last_error.clear();
+    if (dtype != RWS_F32 && dtype != RWS_F16 && dtype != RWS_BF16) return -RWS_ERR_UNSUPPORTED_DTYPE;
+    if (rows < 0 || cols < 0) return -RWS_ERR_INVALID_ARG;
+    if (cols > kMaxCols) return -RWS_ERR_UNSUPPORTED_SHAPE;
+    if (rows == 0 || cols == 0) return RWS_KERNEL_WAVE_ROW;  // nothing runs
+    Plan p;
+    const int st = plan_launch(rows, cols, dtype, in, out, RWS_KERNEL_AUTO, &p);
+    return st == RWS_OK ? p.family : -st;
+}
+
+int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void* in,
+                            const void* out, int kernel_id, char* buf, int64_t buflen) {
+    g_last_error.clear();
+    if (!buf || buflen <= 0) return fail(RWS_ERR_INVALID_ARG, "no output buffer");
+    buf[0] = 0;
+    if (dtype != RWS_F32 && dtype != RWS_F16 && dtype != RWS_BF16)
+        return fail(RWS_ERR_UNSUPPORTED_DTYPE, "dtype must be RWS_F32, RWS_F16 or RWS_BF16");
+    if (kernel_id < RWS_KERNEL_AUTO || kernel_id > RWS_KERNEL_SPLITK)
+        return fail(RWS_ERR_INVALID_ARG, "unknown kernel id " + std::to_string(kernel_id));
+    if (rows < 0 || cols < 0) return fail(RWS_ERR_INVALID_ARG, "rows and cols must be >= 0");
+    if (cols > kMaxCols) return fail(RWS_ERR_UNSUPPORTED_SHAPE, "cols above 2^30");
+    if (rows == 0 || cols == 0) {
+        std::snprintf(buf, (size_t)buflen, "empty: no launch");
+        return RWS_OK;
+    }
+    Plan p;
+    const int st = plan_launch(rows, cols, dtype, in, out, kernel_id, &p);
+    if (st != RWS_OK) return st;
+    const char* al = p.aligned ? "aligned" : (p.same_phase ? "unaligned" : "unaligned,split-phase");
+    const int64_t wmax = window_max(cols, dtype, p.aligned);
+    switch (p.family) {
+        case RWS_KERNEL_WAVE_ROW: {
+            const rws::WaveRowVariant& v = rws::kWaveRow[p.variant];
+            std::snprintf(buf, (size_t)buflen,
+                          "wave_row<%s,%s,G=%d,K=%d,U=%d> grid=%lld block=256 window<=%lld",
+                          dtype_name(dtype), al, v.G, v.K, v.U,
+                          (long long)rws::wave_row_grid(v, std::min(rows, p.max_rows_per_launch)),
+                          (long long)wmax);
+            break;
+        }
+        case RWS_KERNEL_BLOCK_ONEPASS: {
+            const rws::OnepassVariant& v = rws::kOnepass[p.variant];
+            std::snprintf(buf, (size_t)buflen,
+                          "block_onepass<%s,%s,B=%d,KR=%d,KL=%d> grid=%lld block=%d window<=%lld",
+                          dtype_name(dtype), al, v.block, v.kr, v.kl,
+                          (long long)std::min(rows, p.max_rows_per_launch), v.block, (long long)wmax);
+            break;
+        }
+        case RWS_KERNEL_TWO_PASS: {
+            const rws::TwoPassVariant& v = rws::kTwoPass[p.variant];
+            std::snprintf(buf, (size_t)buflen, "two_pass<%s,%s,B=%d,U=%d> grid=%lld block=%d window<=%lld",
+                          dtype_name(dtype), al, v.block, v.u,
+                          (long long)std::min(rows, p.max_rows_per_launch), v.block, (long long)wmax);
+            break;
+        }
+        case RWS_KERNEL_SPLITK: {
+            const rws::SplitkVariant& v = rws::kSplitk[p.variant];
+            std::snprintf(buf, (size_t)buflen,
+                          "splitk<%s,%s,B=%d,KC=%d> P=%d grid=%lld x2 block=%d window<=%lld",
+                          dtype_name(dtype), al, v.block, v.kc, p.P,
+                          (long long)(std::min(rows, p.max_rows_per_launch) * p.P), v.block,
+                          (long long)wmax);
+            break;
+        }
+    }
+    return RWS_OK;
+}
+
+const char* softmax_kernel_name(int kernel_id) {
+    switch (kernel_id) {
+        case RWS_KERNEL_AUTO: return "auto";
+        case RWS_KERNEL_WAVE_ROW: return "wave_row";
+        case RWS_KERNEL_BLOCK_ONEPASS: return "block_onepass";
+        case RWS_KERNEL_TWO_PASS: return "two_pass";
+        case RWS_KERNEL_SPLITK: return "splitk";
+    }
+    return "unknown";
+}
+
+const char* softmax_status_string(int status) {
+    switch (status) {
+        case RWS_OK: return "ok";
+        case RWS_ERR_INVALID_ARG: return "invalid argument";
+        case RWS_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+        case RWS_ERR_MISALIGNED: return "pointer misaligned for its element size";
+        case RWS_ERR_HIP: return "HIP runtime error";
+        case RWS_ERR_UNSUPPORTED_SHAPE: return "shape not supported by the requested kernel";
+    }
+    return "unknown status";
+}
+
+const char* softmax_last_error(void) { return g_last_error.c_str(); }
+
+int softmax_copy_bytes(const void* in, void* out, int64_t bytes, void* stream) {
+    g_last_error.clear();
+    if (bytes < 0) return fail(RWS_ERR_INVALID_ARG, "bytes must be >= 0");
+    if (bytes == 0) return RWS_OK;
+    if (!in || !out) return fail(RWS_ERR_INVALID_ARG, "NULL pointer");
+    if ((uintptr_t)in % 16 || (uintptr_t)out % 16 || bytes % 16)
+        return fail(RWS_ERR_MISALIGNED, "copy needs 16-byte aligned pointers and size");
+    hipError_t e = rws::launch_copy16(in, out, bytes / 16, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(RWS_ERR_HIP, std::string("copy launch: ") + hipGetErrorString(e));
+    return RWS_OK;
+}
+
+}  // extern "C"

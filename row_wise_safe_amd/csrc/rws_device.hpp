@@ -1,0 +1,327 @@
+// rws_device.hpp -- device primitives for the gfx950 row-wise softmax kernels.
+//
+//  * 16-byte "granules": every global access of a row body is one 128-bit
+//    load or store per lane (DCU case-study page, sections 4.2 and 8; CUDA
+//    safe-online-softmax page, section 2.1, the 128-bit pack).  A row that does
+//    not start or end on a 16-byte boundary is covered by the aligned granules
+//    that overlap it; the (at most two) partial granules at its ends are read
+//    and written element by element, so no byte outside the row is touched
+//    (InfiniTrain BF16 elementwise page: aligned vector body, scalar tail).
+//  * dtype widening to fp32 (exact) and RNE narrowing (v_cvt_pk_f16_f32,
+//    v_cvt_pk_bf16_f32 on gfx950) -- packed conversion as on the DCU
+//    case-study page, section 4.5.
+//  * Cross-lane reductions inside 4/8/16/32/64-lane groups with DPP
+//    (quad_perm, row_half_mirror, row_mirror) and the gfx950 permlane16/32
+//    swaps: no LDS round trip (DCU case-study page, section 5.2; CUDA
+//    safe-online-softmax page, section 2.1.1, there with 32-lane shuffles).
+//  * Cross-wave reductions through a few LDS words and one barrier.
+//  * exp(x - m) evaluated as 2^(x*log2(e) - m*log2(e)) with v_exp_f32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rws {
+
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kFltMax = 3.40282346638528859812e+38f;
+
+// ---------------------------------------------------------------------------
+// dtype traits: VEC elements per 16-byte granule, exact widening, RNE
+// narrowing, single-element access for partial granules.
+// ---------------------------------------------------------------------------
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<kF32> {
+    static constexpr int VEC = 4;
+    static constexpr int SIZE = 4;
+    __device__ static inline void widen(u32x4 g, float* v) {
+        f4_t f = __builtin_bit_cast(f4_t, g);
+        v[0] = f[0]; v[1] = f[1]; v[2] = f[2]; v[3] = f[3];
+    }
+    __device__ static inline u32x4 narrow(const float* v) {
+        f4_t f = {v[0], v[1], v[2], v[3]};
+        return __builtin_bit_cast(u32x4, f);
+    }
+    __device__ static inline float load1(const char* p) { return *(const float*)p; }
+    __device__ static inline void store1(char* p, float v) { *(float*)p = v; }
+};
+
+template <>
+struct Elem<kF16> {
+    static constexpr int VEC = 8;
+    static constexpr int SIZE = 2;
+    __device__ static inline void widen(u32x4 g, float* v) {
+        f8_t f = __builtin_convertvector(__builtin_bit_cast(h8_t, g), f8_t);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = f[i];
+    }
+    __device__ static inline u32x4 narrow(const float* v) {
+        f8_t f = {v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+        return __builtin_bit_cast(u32x4, __builtin_convertvector(f, h8_t));
+    }
+    __device__ static inline float load1(const char* p) { return (float)*(const _Float16*)p; }
+    __device__ static inline void store1(char* p, float v) { *(_Float16*)p = (_Float16)v; }
+};
+
+template <>
+struct Elem<kBF16> {
+    static constexpr int VEC = 8;
+    static constexpr int SIZE = 2;
+    // bf16 -> fp32 is the bf16 bit pattern in the top half of the word: exact.
+    __device__ static inline void widen(u32x4 g, float* v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(g[i] << 16);
+            v[2 * i + 1] = __uint_as_float(g[i] & 0xffff0000u);
+        }
+    }
+    __device__ static inline u32x4 narrow(const float* v) {
+        f8_t f = {v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+        return __builtin_bit_cast(u32x4, __builtin_convertvector(f, b8_t));
+    }
+    __device__ static inline float load1(const char* p) {
+        return __uint_as_float((unsigned)(*(const unsigned short*)p) << 16);
+    }
+    __device__ static inline void store1(char* p, float v) { *(__bf16*)p = (__bf16)v; }
+};
+
+// ---------------------------------------------------------------------------
+// Row window: the aligned granules that overlap one row.
+//   lead  = elements of the first granule that precede the row (0..VEC-1)
+//   ngran = number of granules overlapping the row
+// Granule k holds row columns c0 = k*VEC - lead .. c0+VEC-1; it is "interior"
+// (all VEC elements belong to the row) iff c0 >= 0 and c0 + VEC <= cols.
+// With ALIGNED (row start 16-byte aligned and cols*size % 16 == 0) lead == 0
+// and every granule is interior.
+//
+// Loads are split in two so that a thread issues all of its 128-bit loads
+// before it waits for any: fetch() only loads, widen() converts and masks.
+//  * ALIGNED: fetch(k) reads granule min(k, ngran-1) (always inside the row);
+//    widen() turns granules k >= ngran into -inf.
+//  * unaligned: fetch(k) reads the whole 16-byte granule whenever it lies
+//    inside the tensor [tbeg, tend) -- a partial granule then also holds bytes
+//    of the neighbouring row, which widen() replaces by -inf.  Only the first
+//    granule of the tensor and its last one can stick out of it; those two are
+//    read element by element inside widen(), so no byte outside the tensor is
+//    ever read.
+// ---------------------------------------------------------------------------
+template <int DT, bool ALIGNED>
+struct RowWin {
+    static constexpr int VEC = Elem<DT>::VEC;
+    static constexpr int ES = Elem<DT>::SIZE;
+    const char* gin;   // first granule of the row in `in` (16-byte aligned)
+    char* gout;        // same granule position in `out` (used when same_phase)
+    char* rout;        // row start in `out`
+    int lead;
+    int ngran;
+    int cols;
+
+    RowWin() = default;
+    __device__ inline RowWin(const void* in, void* out, int64_t row, int cols_) {
+        cols = cols_;
+        const char* rin = (const char*)in + row * (int64_t)cols_ * ES;
+        rout = (char*)out + row * (int64_t)cols_ * ES;
+        if (ALIGNED) {
+            lead = 0;
+            gin = rin;
+            gout = rout;
+            ngran = cols_ / VEC;
+        } else {
+            uintptr_t a = (uintptr_t)rin;
+            int mis = (int)(a & 15u);
+            lead = mis / ES;
+            gin = rin - mis;
+            gout = rout - mis;
+            ngran = (mis + cols_ * ES + 15) >> 4;
+        }
+    }
+
+    __device__ inline bool interior(int k) const {
+        if (ALIGNED) return k < ngran;
+        const int c0 = k * VEC - lead;
+        return c0 >= 0 && c0 + VEC <= cols;
+    }
+
+    // Issue the 128-bit load of granule k (no wait).
+    __device__ inline u32x4 fetch(int k, const char* tbeg, const char* tend) const {
+        if (ALIGNED) {
+            const int kk = k < ngran ? k : ngran - 1;
+            return *(const u32x4*)(gin + (int64_t)kk * 16);
+        }
+        const char* g = gin + (int64_t)k * 16;
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (g >= tbeg && g + 16 <= tend) raw = *(const u32x4*)g;
+        return raw;
+    }
+
+    // Widen a fetched granule into v[0..VEC); elements outside the row are -inf.
+    // `full` (uniform) promises k < ngran for ALIGNED windows and skips the
+    // check.
+    __device__ inline void widen(int k, u32x4 raw, float* v, const char* tbeg,
+                                 const char* tend, bool full = false) const {
+        Elem<DT>::widen(raw, v);
+        if (ALIGNED) {
+            if (full) return;
+            if (k >= ngran) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) v[e] = kNegInf;
+            }
+            return;
+        }
+        const int c0 = k * VEC - lead;
+        if (!(c0 >= 0 && c0 + VEC <= cols)) {
+            const char* g = gin + (int64_t)k * 16;
+            if (g >= tbeg && g + 16 <= tend) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const int c = c0 + e;
+                    if (!(c >= 0 && c < cols)) v[e] = kNegInf;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const int c = c0 + e;
+                    v[e] = (c >= 0 && c < cols) ? Elem<DT>::load1(g + e * ES) : kNegInf;
+                }
+            }
+        }
+    }
+
+    // Store granule k.  same_phase: `out` rows share the 16-byte phase of `in`
+    // rows, so interior granules are stored as 128-bit words; otherwise every
+    // element is stored on its own.  Elements outside the row are never
+    // written.
+    __device__ inline void store(int k, const float* v, bool same_phase) const {
+        if (ALIGNED) {
+            *(u32x4*)(gout + (int64_t)k * 16) = Elem<DT>::narrow(v);
+            return;
+        }
+        const int c0 = k * VEC - lead;
+        if (same_phase && c0 >= 0 && c0 + VEC <= cols) {
+            *(u32x4*)(gout + (int64_t)k * 16) = Elem<DT>::narrow(v);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const int c = c0 + e;
+                if (c >= 0 && c < cols) Elem<DT>::store1(rout + (int64_t)c * ES, v[e]);
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// exp(x - m) for one row.  With c = round(m * log2 e), the FMA
+// x*log2e - c is exact before its single rounding, so the error is relative
+// to |x - m| and the common offset (m*log2e - c) cancels in the
+// normalisation.  Rows whose max makes m*log2e overflow (|m| > 2.3e38, only
+// reachable in fp32/bf16), or m = +inf, take (x - m)*log2e instead.  m = -inf
+// (every entry -inf) keeps c = 0 so that the row becomes 0/0 = NaN like the
+// definition, and -inf entries under a finite max give exactly 0.
+// ---------------------------------------------------------------------------
+struct RowExp {
+    float m;
+    float negc;
+    bool big;
+    __device__ inline explicit RowExp(float m_) : m(m_) {
+        float c = m_ * kLog2e;
+        big = !(__builtin_fabsf(c) <= kFltMax) && (m_ != kNegInf);
+        negc = (m_ == kNegInf) ? 0.0f : -c;
+    }
+    template <int N>
+    __device__ inline void apply(float (&v)[N]) const {
+        if (__builtin_expect(big, 0)) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) v[i] = __builtin_amdgcn_exp2f((v[i] - m) * kLog2e);
+        } else {
+#pragma unroll
+            for (int i = 0; i < N; ++i) v[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(v[i], kLog2e, negc));
+        }
+    }
+    __device__ inline float one(float x) const {
+        return big ? __builtin_amdgcn_exp2f((x - m) * kLog2e)
+                   : __builtin_amdgcn_exp2f(__builtin_fmaf(x, kLog2e, negc));
+    }
+};
+
+// Scale factor e^(m_part - M) for merging a partial (m_part, d) into the row
+// maximum M; exactly 1 when m_part == M (this also covers -inf == -inf, so
+// the (-inf, 0) identity never produces NaN).
+__device__ inline float merge_scale(float m_part, float M) {
+    if (m_part == M) return 1.0f;
+    RowExp er(M);
+    return er.one(m_part);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions within aligned groups of G lanes (G = 4..64) of a
+// 64-lane wave.  Every lane of a group ends with the same bits (each step
+// combines a lane with its partner and the partner with it, and the ops are
+// commutative).  The whole wave must be active.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ inline float dpp(float v) {
+    // Every source lane of these permutations is inside the wave, so
+    // bound_ctrl never applies; it only lets the move fold into its consumer.
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Maximum that propagates NaN (v_maximum3_f32 on gfx950, no operand
+// canonicalisation).  A NaN input makes the row max NaN and so the whole row
+// NaN, the same outcome as the definition evaluated in IEEE arithmetic.
+__device__ inline float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+struct OpMax {
+    __device__ static inline float f(float a, float b) { return vmax(a, b); }
+};
+struct OpSum {
+    __device__ static inline float f(float a, float b) { return a + b; }
+};
+
+template <int G, class Op>
+__device__ inline float group_reduce(float v) {
+    static_assert(G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "group size");
+    v = Op::f(v, dpp<0xB1>(v));  // quad_perm [1,0,3,2]: partner lane ^ 1
+    v = Op::f(v, dpp<0x4E>(v));  // quad_perm [2,3,0,1]: partner lane ^ 2
+    if (G >= 8) v = Op::f(v, dpp<0x141>(v));  // row_half_mirror: other quad of 8
+    if (G >= 16) v = Op::f(v, dpp<0x140>(v));  // row_mirror: other half of 16
+    if (G >= 32) {  // rows 0<->1 and 2<->3 (lane ^ 16)
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = Op::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    if (G >= 64) {  // halves 0-31 <-> 32-63 (lane ^ 32)
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = Op::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    return v;
+}
+
+// Reduction over a whole workgroup of W waves: the wave result goes to
+// slots[wave], one barrier, every lane folds the W slots in the same order.
+// `slots` must not be reused by another reduction without a barrier.
+template <int W, class Op>
+__device__ inline float block_reduce(float v, float* slots) {
+    v = group_reduce<64, Op>(v);
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    if (W == 1) return v;
+    if (lane == 0) slots[wave] = v;
+    __syncthreads();
+    float r = slots[0];
+#pragma unroll
+    for (int i = 1; i < W; ++i) r = Op::f(r, slots[i]);
+    return r;
+}
+
+}  // namespace rws

@@ -1,0 +1,417 @@
+// rws_kernels.hpp -- the four gfx950 kernel families of row-wise safe
+// softmax, as templates.  Each .hip file of the library instantiates one
+// family for the variants the dispatcher uses.
+//
+// Per row every family computes m = max x, d = sum e^(x - m) in fp32 and writes
+// y = e^(x - m) * (1/d), rounded to the output dtype (HIP softmax tutorial
+// page, section 1).  They differ in how a row is spread over lanes and how
+// often its bytes cross HBM:
+//   wave_row       one row per group of G lanes (G = 4..64), row held in
+//                  registers: 1 read + 1 write, reductions in DPP/permlane only
+//                  (DCU case-study page, sections 4.1, 5.2 and 8).
+//   block_onepass  one workgroup per row, row held in registers then LDS:
+//                  1 read + 1 write (CUDA safe-online-softmax page, 2.1-2.2).
+//   two_pass       one workgroup per row, running (m, d) over the row, then a
+//                  second read: any length (same page, section 3.1).
+//   splitk         rows cut into chunks over many workgroups; stage 1 emits a
+//                  partial (m, d) per chunk, stage 2 merges a row's partials
+//                  and writes its chunk (same page, section 3.2).
+// Every kernel first issues all of a thread's 128-bit loads for a batch, then
+// converts, so the loads of a wave are in flight together.
+#pragma once
+
+#include "rws_device.hpp"
+
+namespace rws {
+
+template <int DT>
+__device__ inline const char* tensor_end(const void* in, int64_t rows, int cols) {
+    return (const char*)in + rows * (int64_t)cols * Elem<DT>::SIZE;
+}
+
+// ===========================================================================
+// wave_row: G lanes per row, 64/G rows per wave "set", U sets per wave, K
+// granules per lane and row.  Lane gl of a group holds granules gl + G*i, so
+// the G lanes of a group read consecutive 16-byte granules at every step.
+// Rows past the end are clamped to the last row for loading (in bounds) and
+// are not stored.
+// ===========================================================================
+template <int DT, bool ALIGNED, int G, int K, int U>
+__global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
+                                                  void* __restrict__ out, int64_t rows,
+                                                  int cols, int same_phase) {
+    constexpr int VEC = Elem<DT>::VEC;
+    constexpr int RPS = 64 / G;  // rows per set
+    constexpr int N = K * VEC;   // elements per lane per row
+    const int lane = threadIdx.x & 63;
+    const int gl = lane & (G - 1);
+    const int sub = lane / G;
+    // The wave index is uniform: readfirstlane keeps the row arithmetic scalar.
+    const int64_t wave_id =
+        (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t row0 = wave_id * (RPS * U);
+    const char* tbeg = (const char*)in;
+    const char* tend = tensor_end<DT>(in, rows, cols);
+    // ALIGNED rows whose window fills all G*K slots need no masking.
+    const bool full = ALIGNED && (cols / VEC >= G * K);
+
+    RowWin<DT, ALIGNED> w[U];
+    u32x4 raw[U][K];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        int64_t row = row0 + u * RPS + sub;
+        row = row < rows ? row : rows - 1;
+        w[u] = RowWin<DT, ALIGNED>(in, out, row, cols);
+#pragma unroll
+        for (int i = 0; i < K; ++i) raw[u][i] = w[u].fetch(gl + G * i, tbeg, tend);
+    }
+
+    float v[U][N];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int i = 0; i < K; ++i)
+            w[u].widen(gl + G * i, raw[u][i], &v[u][i * VEC], tbeg, tend, full);
+        float mx = v[u][0];
+#pragma unroll
+        for (int j = 1; j < N; ++j) mx = vmax(mx, v[u][j]);
+        mx = group_reduce<G, OpMax>(mx);
+        RowExp er(mx);
+        er.apply(v[u]);
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < N; ++j) s += v[u][j];
+        s = group_reduce<G, OpSum>(s);
+        const float r = __builtin_amdgcn_rcpf(s);
+#pragma unroll
+        for (int j = 0; j < N; ++j) v[u][j] *= r;
+    }
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t row = row0 + u * RPS + sub;
+        if (row < rows) {
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                const int k = gl + G * i;
+                if (k < w[u].ngran) w[u].store(k, &v[u][i * VEC], same_phase != 0);
+            }
+        }
+    }
+}
+
+// ===========================================================================
+// block_onepass: one workgroup of BLOCK threads per row.  Thread t holds
+// granules t + BLOCK*i (i < KR) widened in registers and parks granules
+// t + BLOCK*(KR + j) (j < KL) as raw bits in LDS (only thread t touches its
+// LDS slots, so they need no barrier; consecutive threads use consecutive
+// 16-byte slots).  Every byte of the row crosses HBM once each way.
+// ===========================================================================
+template <int DT, bool ALIGNED, int BLOCK, int KR, int KL>
+__global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict__ in,
+                                                         void* __restrict__ out, int64_t rows,
+                                                         int cols, int same_phase) {
+    constexpr int VEC = Elem<DT>::VEC;
+    constexpr int W = BLOCK / 64;
+    constexpr int N = KR * VEC;
+    __shared__ float red_max[W];
+    __shared__ float red_sum[W];
+    __shared__ u32x4 park[KL > 0 ? KL : 1][BLOCK];
+    const int t = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const char* tbeg = (const char*)in;
+    const char* tend = tensor_end<DT>(in, rows, cols);
+    const RowWin<DT, ALIGNED> w(in, out, row, cols);
+
+    u32x4 raw[KR];
+#pragma unroll
+    for (int i = 0; i < KR; ++i) raw[i] = w.fetch(t + BLOCK * i, tbeg, tend);
+    u32x4 rawl[KL > 0 ? KL : 1];
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+        const int k = t + BLOCK * (KR + j);
+        if (k < w.ngran) rawl[j] = w.fetch(k, tbeg, tend);
+    }
+
+    float v[N];
+#pragma unroll
+    for (int i = 0; i < KR; ++i) w.widen(t + BLOCK * i, raw[i], &v[i * VEC], tbeg, tend);
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < N; ++j) mx = vmax(mx, v[j]);
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+        const int k = t + BLOCK * (KR + j);
+        if (k < w.ngran) {
+            float f[VEC];
+            w.widen(k, rawl[j], f, tbeg, tend);
+            // partial granules are parked with -inf outside the row
+            park[j][t] = w.interior(k) ? rawl[j] : Elem<DT>::narrow(f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) mx = vmax(mx, f[e]);
+        }
+    }
+    mx = block_reduce<W, OpMax>(mx, red_max);
+
+    const RowExp er(mx);
+    er.apply(v);
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < N; ++j) s += v[j];
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+        const int k = t + BLOCK * (KR + j);
+        if (k < w.ngran) {
+            float f[VEC];
+            Elem<DT>::widen(park[j][t], f);
+            er.apply(f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) s += f[e];
+        }
+    }
+    s = block_reduce<W, OpSum>(s, red_sum);
+    const float r = __builtin_amdgcn_rcpf(s);
+
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+        const int k = t + BLOCK * i;
+        if (k < w.ngran) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[i * VEC + e] *= r;
+            w.store(k, &v[i * VEC], same_phase != 0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+        const int k = t + BLOCK * (KR + j);
+        if (k < w.ngran) {
+            float f[VEC];
+            Elem<DT>::widen(park[j][t], f);
+            er.apply(f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) f[e] *= r;
+            w.store(k, f, same_phase != 0);
+        }
+    }
+}
+
+// ===========================================================================
+// Running (m, d) of one thread over a batch of N values (-inf entries add 0):
+//   m' = max(m, max batch);  d' = d e^(m - m') + sum e^(x - m')
+// (DCU case-study page, section 4.3; CUDA safe-online-softmax page, section 1,
+// there per chunk of 256).
+// ===========================================================================
+template <int N>
+__device__ inline void online_update(float& m, float& d, const float (&v)[N]) {
+    float lm = v[0];
+#pragma unroll
+    for (int j = 1; j < N; ++j) lm = vmax(lm, v[j]);
+    const float mn = vmax(m, lm);
+    if (mn != kNegInf) {
+        const RowExp er(mn);
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < N; ++j) s += er.one(v[j]);
+        d = d * ((m == mn) ? 1.0f : er.one(m)) + s;
+        m = mn;
+    }
+}
+
+// Merge every thread's (m, d) into the row's (M, D) over the workgroup:
+// M = max over threads, D = sum over threads of d e^(m - M) -- the (m, d)
+// merge rule applied across the block, written as one max reduction and one
+// sum reduction (CUDA safe-online-softmax page, section 2.1.1).
+template <int W>
+__device__ inline void block_merge(float m, float d, float& M, float& D, float* red_max,
+                                   float* red_sum) {
+    M = block_reduce<W, OpMax>(m, red_max);
+    const float ds = (d == 0.0f) ? 0.0f : d * merge_scale(m, M);
+    D = block_reduce<W, OpSum>(ds, red_sum);
+}
+
+// ===========================================================================
+// two_pass: one workgroup per row, any row length.  Pass 1 streams the row in
+// batches of U granules per thread with the running (m, d); the block merges
+// the threads' pairs; pass 2 re-reads the row (from L2 / last-level cache when
+// the row was just read) and writes e^(x - M) / D.
+// ===========================================================================
+template <int DT, bool ALIGNED, int BLOCK, int U>
+__global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
+                                                    void* __restrict__ out, int64_t rows,
+                                                    int cols, int same_phase) {
+    constexpr int VEC = Elem<DT>::VEC;
+    constexpr int W = BLOCK / 64;
+    __shared__ float red_max[W];
+    __shared__ float red_sum[W];
+    const int t = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const char* tbeg = (const char*)in;
+    const char* tend = tensor_end<DT>(in, rows, cols);
+    const RowWin<DT, ALIGNED> w(in, out, row, cols);
+
+    float m = kNegInf, d = 0.0f;
+    for (int k0 = t; k0 < w.ngran; k0 += BLOCK * U) {
+        u32x4 raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = w.fetch(k0 + BLOCK * u, tbeg, tend);
+        float v[U * VEC];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = k0 + BLOCK * u;
+            w.widen(k, raw[u], &v[u * VEC], tbeg, tend);
+            if (!ALIGNED && k >= w.ngran) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) v[u * VEC + e] = kNegInf;
+            }
+        }
+        online_update(m, d, v);
+    }
+    float M, D;
+    block_merge<W>(m, d, M, D, red_max, red_sum);
+    const RowExp er(M);
+    const float r = __builtin_amdgcn_rcpf(D);
+
+    for (int k0 = t; k0 < w.ngran; k0 += BLOCK * U) {
+        u32x4 raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = w.fetch(k0 + BLOCK * u, tbeg, tend);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = k0 + BLOCK * u;
+            if (k < w.ngran) {
+                float f[VEC];
+                w.widen(k, raw[u], f, tbeg, tend);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) f[e] = er.one(f[e]) * r;
+                w.store(k, f, same_phase != 0);
+            }
+        }
+    }
+}
+
+// ===========================================================================
+// split-k.  A row's window of granules is cut into P chunks of CG = BLOCK*KC
+// granules; workgroup b handles chunk b % P of row b / P.
+//   stage 1: chunk max, chunk sum of e^(x - m_c) -> ws[row*P + chunk] = (m_c, d_c)
+//   stage 2: merge the row's P partials into (M, D), re-read the chunk,
+//            write e^(x - M) / D.
+// The launch boundary between the stages is the only grid-wide ordering.
+// ===========================================================================
+template <int DT, bool ALIGNED, int BLOCK, int KC>
+__global__ __launch_bounds__(BLOCK) void k_splitk_stage1(const void* __restrict__ in,
+                                                         int64_t rows, int cols, int P,
+                                                         float2* __restrict__ ws) {
+    constexpr int VEC = Elem<DT>::VEC;
+    constexpr int W = BLOCK / 64;
+    constexpr int N = KC * VEC;
+    __shared__ float red_max[W];
+    __shared__ float red_sum[W];
+    const int t = threadIdx.x;
+    const int64_t row = blockIdx.x / P;
+    const int chunk = blockIdx.x - (int)(row * P);
+    const char* tbeg = (const char*)in;
+    const char* tend = tensor_end<DT>(in, rows, cols);
+    const RowWin<DT, ALIGNED> w(in, const_cast<void*>(in), row, cols);  // out unused
+    const int kbase = chunk * (BLOCK * KC) + t;
+
+    u32x4 raw[KC];
+#pragma unroll
+    for (int i = 0; i < KC; ++i) raw[i] = w.fetch(kbase + BLOCK * i, tbeg, tend);
+    float v[N];
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        const int k = kbase + BLOCK * i;
+        w.widen(k, raw[i], &v[i * VEC], tbeg, tend);
+        if (!ALIGNED && k >= w.ngran) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[i * VEC + e] = kNegInf;
+        }
+    }
+    float mx = v[0];
+#pragma unroll
+    for (int j = 1; j < N; ++j) mx = vmax(mx, v[j]);
+    mx = block_reduce<W, OpMax>(mx, red_max);
+    const RowExp er(mx);
+    er.apply(v);
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < N; ++j) s += v[j];
+    s = block_reduce<W, OpSum>(s, red_sum);
+    if (t == 0) ws[row * P + chunk] = make_float2(mx, s);
+}
+
+template <int DT, bool ALIGNED, int BLOCK, int KC>
+__global__ __launch_bounds__(BLOCK) void k_splitk_stage2(const void* __restrict__ in,
+                                                         void* __restrict__ out, int64_t rows,
+                                                         int cols, int P,
+                                                         const float2* __restrict__ ws,
+                                                         int same_phase) {
+    constexpr int VEC = Elem<DT>::VEC;
+    constexpr int W = BLOCK / 64;
+    __shared__ float red_max[W];
+    __shared__ float red_sum[W];
+    const int t = threadIdx.x;
+    const int64_t row = blockIdx.x / P;
+    const int chunk = blockIdx.x - (int)(row * P);
+    const char* tbeg = (const char*)in;
+    const char* tend = tensor_end<DT>(in, rows, cols);
+    const RowWin<DT, ALIGNED> w(in, out, row, cols);
+    const int kbase = chunk * (BLOCK * KC) + t;
+
+    // Issue the chunk's loads first; the partial merge overlaps their latency.
+    u32x4 raw[KC];
+#pragma unroll
+    for (int i = 0; i < KC; ++i) raw[i] = w.fetch(kbase + BLOCK * i, tbeg, tend);
+
+    float m = kNegInf, d = 0.0f;
+    for (int j = t; j < P; j += BLOCK) {
+        const float2 p = ws[row * P + j];
+        const float mn = vmax(m, p.x);
+        const float a = (d == 0.0f) ? 0.0f : d * merge_scale(m, mn);
+        const float b = (p.y == 0.0f) ? 0.0f : p.y * merge_scale(p.x, mn);
+        m = mn;
+        d = a + b;
+    }
+    float M, D;
+    block_merge<W>(m, d, M, D, red_max, red_sum);
+    const RowExp er(M);
+    const float r = __builtin_amdgcn_rcpf(D);
+
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        const int k = kbase + BLOCK * i;
+        if (k < w.ngran) {
+            float f[VEC];
+            w.widen(k, raw[i], f, tbeg, tend);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) f[e] = er.one(f[e]) * r;
+            w.store(k, f, same_phase != 0);
+        }
+    }
+}
+
+// ===========================================================================
+// Plain 16-byte copy (the copy ceiling and counter calibration): every thread
+// moves UNROLL granules per grid-stride step, loads first.
+// ===========================================================================
+template <int UNROLL>
+__global__ __launch_bounds__(256) void k_copy16(const u32x4* __restrict__ in,
+                                                u32x4* __restrict__ out, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * 256 * UNROLL;
+    for (int64_t base = (int64_t)blockIdx.x * 256 * UNROLL + threadIdx.x; base < n;
+         base += stride) {
+        u32x4 g[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t i = base + (int64_t)u * 256;
+            if (i < n) g[u] = in[i];
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t i = base + (int64_t)u * 256;
+            if (i < n) out[i] = g[u];
+        }
+    }
+}
+
+}  // namespace rws

@@ -1,0 +1,51 @@
+// rws_launch.hpp -- host-side interface between the C ABI / dispatcher
+// (rws_api.cpp) and the kernel translation units.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rws {
+
+// One launch of a kernel family over `rows` rows starting at in/out.
+struct Launch {
+    const void* in;
+    void* out;
+    int64_t rows;
+    int cols;
+    int dtype;        // kF32 / kF16 / kBF16
+    bool aligned;     // in, out 16-byte aligned and cols*size % 16 == 0
+    bool same_phase;  // (in - out) % 16 == 0
+    hipStream_t stream;
+};
+
+struct WaveRowVariant { int G, K, U; };          // lanes per row, granules per lane, row sets
+struct OnepassVariant { int block, kr, kl; };    // threads, register granules, LDS granules
+struct TwoPassVariant { int block, u; };         // threads, granules per batch
+struct SplitkVariant { int block, kc; };         // threads, granules per thread per chunk
+
+extern const WaveRowVariant kWaveRow[];
+extern const int kNumWaveRow;
+extern const OnepassVariant kOnepass[];
+extern const int kNumOnepass;
+extern const TwoPassVariant kTwoPass[];
+extern const int kNumTwoPass;
+extern const SplitkVariant kSplitk[];
+extern const int kNumSplitk;
+
+// Grid of one wave_row launch (workgroups of 256 threads = 4 waves).
+inline int64_t wave_row_grid(const WaveRowVariant& v, int64_t rows) {
+    const int64_t rows_per_wave = (int64_t)(64 / v.G) * v.U;
+    const int64_t waves = (rows + rows_per_wave - 1) / rows_per_wave;
+    return (waves + 3) / 4;
+}
+
+hipError_t launch_wave_row(const Launch& L, int variant);
+hipError_t launch_block_onepass(const Launch& L, int variant);
+hipError_t launch_two_pass(const Launch& L, int variant);
+// Both split-k stages; ws holds rows*P (m, d) pairs.
+hipError_t launch_splitk(const Launch& L, int variant, int P, float2* ws);
+// n16 granules of 16 bytes.
+hipError_t launch_copy16(const void* in, void* out, int64_t n16, hipStream_t stream);
+
+}  // namespace rws

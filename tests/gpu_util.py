@@ -1,0 +1,53 @@
+"""Helpers for the GPU tests: put seeded float64 inputs into device tensors of
+a dtype (optionally at an element offset inside a larger buffer, so that the
+base pointer is not 16-byte aligned), run the library through its C ABI and
+read results back."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import row_wise_safe_amd as rws
+
+TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def have_gpu() -> bool:
+    return torch.cuda.is_available()
+
+
+def to_device(x64: np.ndarray, dtype: str, offset: int = 0, device="cuda"):
+    """Round to `dtype` on the host, copy to the GPU at `offset` elements into a
+    fresh buffer.  Returns (device view [rows, cols], stored values as float64)."""
+    t = torch.from_numpy(np.ascontiguousarray(x64)).to(TORCH_DTYPE[dtype])
+    stored = t.to(torch.float64).numpy()
+    buf = torch.empty(t.numel() + offset, dtype=t.dtype, device=device)
+    view = buf[offset:offset + t.numel()].view(t.shape)
+    view.copy_(t.to(device))
+    return view, stored
+
+
+def empty_like_at(x: torch.Tensor, offset: int = 0):
+    buf = torch.empty(x.numel() + offset, dtype=x.dtype, device=x.device)
+    return buf[offset:offset + x.numel()].view(x.shape)
+
+
+def run(x: torch.Tensor, out: torch.Tensor, kernel: str = "auto") -> np.ndarray:
+    rws.softmax(x, out=out, kernel=kernel)
+    torch.cuda.synchronize()
+    return out.to(torch.float64).cpu().numpy()
+
+
+def window_granules(cols: int, dtype: str, aligned: bool) -> int:
+    es = 4 if dtype == "f32" else 2
+    b = cols * es
+    return b // 16 if aligned else (b + 30) // 16
+
+
+def supports(kernel: str, cols: int, dtype: str, aligned: bool) -> bool:
+    w = window_granules(cols, dtype, aligned)
+    if kernel == "wave_row":
+        return w <= 512
+    if kernel == "block_onepass":
+        return w <= 16384
+    return True

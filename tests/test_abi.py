@@ -1,0 +1,124 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/row_wise_softmax.h declares, and its host-side logic (argument
+checks, status strings, kernel names, the dispatcher's choices) behaves as
+documented.  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import row_wise_safe_amd as rws
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "row_wise_softmax.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rws.library_path()):
+        from row_wise_safe_amd import build
+        build.build()
+    return rws.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(softmax_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("softmax_fwd", "softmax_fwd_kernel", "softmax_select_kernel",
+              "softmax_describe_launch", "softmax_kernel_name", "softmax_status_string",
+              "softmax_last_error", "softmax_copy_bytes"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    path = rws.library_path()
+    raw = ctypes.CDLL(path)
+    for n in declared_functions():
+        assert hasattr(raw, n), f"{n} not exported"
+
+
+def test_binding_mirrors_the_abi():
+    for n in declared_functions():
+        assert callable(getattr(rws, n)), n
+
+
+def test_status_strings_and_names(lib):
+    assert rws.softmax_status_string(rws.RWS_OK) == "ok"
+    for st in range(1, 6):
+        assert rws.softmax_status_string(st) not in ("", "ok", "unknown status")
+    assert rws.softmax_status_string(99) == "unknown status"
+    assert [rws.softmax_kernel_name(i) for i in range(5)] == \
+        ["auto", "wave_row", "block_onepass", "two_pass", "splitk"]
+    assert rws.softmax_kernel_name(17) == "unknown"
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 0, -1, 3, rws.RWS_F16, 0), rws.RWS_ERR_INVALID_ARG),
+    ((0, 0, 3, -1, rws.RWS_F16, 0), rws.RWS_ERR_INVALID_ARG),
+    ((0, 0, 3, 4, 3, 0), rws.RWS_ERR_UNSUPPORTED_DTYPE),
+    ((0, 0, 3, 4, -1, 0), rws.RWS_ERR_UNSUPPORTED_DTYPE),
+    ((0, 0, 3, 4, rws.RWS_F16, 0), rws.RWS_ERR_INVALID_ARG),        # NULL pointers
+    ((16, 0, 3, 4, rws.RWS_F16, 0), rws.RWS_ERR_INVALID_ARG),       # NULL out
+    ((17, 32, 3, 4, rws.RWS_F16, 0), rws.RWS_ERR_MISALIGNED),       # odd address for fp16
+    ((32, 18, 3, 4, rws.RWS_F32, 0), rws.RWS_ERR_MISALIGNED),       # 2-byte aligned fp32
+    ((32, 32, 3, (1 << 30) + 1, rws.RWS_F16, 0), rws.RWS_ERR_UNSUPPORTED_SHAPE),
+])
+def test_argument_checks_never_launch(lib, args, status):
+    assert rws.softmax_fwd(*args) == status
+    assert rws.softmax_last_error() != ""
+
+
+def test_empty_is_success_without_pointers(lib):
+    assert rws.softmax_fwd(0, 0, 0, 5, rws.RWS_F16, 0) == rws.RWS_OK
+    assert rws.softmax_fwd(0, 0, 5, 0, rws.RWS_BF16, 0) == rws.RWS_OK
+    assert rws.softmax_last_error() == ""
+
+
+def test_bad_kernel_id(lib):
+    assert rws.softmax_fwd_kernel(32, 32, 2, 2, rws.RWS_F32, 0, 9) == rws.RWS_ERR_INVALID_ARG
+
+
+def test_copy_argument_checks(lib):
+    assert rws.softmax_copy_bytes(16, 32, 15, 0) == rws.RWS_ERR_MISALIGNED
+    assert rws.softmax_copy_bytes(16, 32, -16, 0) == rws.RWS_ERR_INVALID_ARG
+    assert rws.softmax_copy_bytes(0, 0, 0, 0) == rws.RWS_OK
+
+
+def test_forced_wave_row_rejects_long_rows(lib):
+    buf = ctypes.create_string_buffer(256)
+    st = lib.softmax_describe_launch(2, 4800, rws.RWS_F16, 256, 256, 1, buf, 256)
+    assert st == rws.RWS_ERR_UNSUPPORTED_SHAPE
+
+
+# The dispatcher's routing for the five workloads (16-byte aligned pointers).
+@pytest.mark.parametrize("rows,cols,dtype,family", [
+    (2, 3, rws.RWS_F32, "wave_row"),
+    (64, 1000, rws.RWS_F32, "wave_row"),
+    (65536, 512, rws.RWS_F16, "wave_row"),
+    (1 << 20, 128, rws.RWS_BF16, "wave_row"),
+    (8192, 4097, rws.RWS_F16, "block_onepass"),
+    (16, 1 << 20, rws.RWS_F16, "splitk"),
+    (4096, 1 << 20, rws.RWS_F16, "two_pass"),
+])
+def test_dispatch_routes(lib, rows, cols, dtype, family):
+    kid = rws.softmax_select_kernel(rows, cols, dtype, 256, 512)
+    assert rws.softmax_kernel_name(kid) == family
+    desc = rws.softmax_describe_launch(rows, cols, dtype, 256, 512)
+    assert desc.startswith(family)
+
+
+def test_select_rejects_bad_args(lib):
+    assert rws.softmax_select_kernel(-1, 4, rws.RWS_F16) < 0
+    assert rws.softmax_select_kernel(4, 4, 5) < 0
+
+
+def test_describe_mentions_alignment(lib):
+    assert "unaligned" in rws.softmax_describe_launch(8, 100, rws.RWS_F16, 258, 258)
+    assert "split-phase" in rws.softmax_describe_launch(8, 100, rws.RWS_F16, 258, 256)
+    assert ",aligned" in rws.softmax_describe_launch(8, 128, rws.RWS_F16, 256, 512)
