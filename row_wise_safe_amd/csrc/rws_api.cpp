@@ -77,31 +77,57 @@ struct Plan {
     int variant = 0;  // index into that family's variant table
     int P = 1;        // split-k chunks per row
     int64_t max_rows_per_launch = 0;
+    int64_t window = 0;  // granules per row window (upper bound)
     bool aligned = false;
     bool same_phase = false;
+    bool remap = true;
 };
 
-// Upper bound of the number of 16-byte granules that overlap one row.
-int64_t window_max(int64_t cols, int dtype, bool aligned) {
-    const int64_t bytes = cols * elem_size(dtype);
-    if (aligned) return bytes / 16;
-    return (bytes + 15 + 15) / 16;
+// Alignment facts of one call.
+struct Geometry {
+    int64_t row_bytes;
+    bool a16;   // in, out and every row start 16-byte aligned
+    bool a128;  // ... 128-byte (cache line) aligned
+    bool same_phase;
+};
+
+Geometry geometry(int64_t cols, int dtype, const void* in, const void* out) {
+    const uintptr_t ai = (uintptr_t)in, ao = (uintptr_t)out;
+    Geometry g;
+    g.row_bytes = cols * elem_size(dtype);
+    g.a16 = ai % 16 == 0 && ao % 16 == 0 && g.row_bytes % 16 == 0;
+    g.a128 = ai % 128 == 0 && ao % 128 == 0 && g.row_bytes % 128 == 0;
+    g.same_phase = (ai % 16) == (ao % 16);
+    return g;
 }
+
+// Granules in a row window that starts on a `wa`-byte boundary (an upper
+// bound over all rows; exact when the rows are `wa`-aligned).
+int64_t window_granules(const Geometry& g, int wa) {
+    const bool aligned = wa == 128 ? g.a128 : g.a16;
+    if (aligned) return g.row_bytes / 16;
+    return (g.row_bytes + wa + 15) / 16;
+}
+
+int wave_row_wa(const rws::WaveRowVariant& v) { return v.G * 16 >= 128 ? 128 : 16; }
 
 int64_t onepass_capacity(const rws::OnepassVariant& v) { return (int64_t)v.block * (v.kr + v.kl); }
 
 // Choose among the wave_row variants: the narrowest lane group whose
-// registers hold the window, and enough row sets in flight per wave.
-int pick_wave_row(int64_t wmax) {
+// registers hold the window, then the number of row sets per wave that
+// measured fastest on MI355X: two for one-granule full-wave rows (fp16 512
+// columns: 19.9 us vs 20.5 us with one), one otherwise (bf16 128 columns with
+// 16-lane groups: 84.5 us vs 88.3 us with two).
+int pick_wave_row(const Geometry& g) {
     int best = -1;
     int64_t best_key = 0;
     for (int i = 0; i < rws::kNumWaveRow; ++i) {
         const rws::WaveRowVariant& v = rws::kWaveRow[i];
-        if ((int64_t)v.G * v.K < wmax) continue;
-        // prefer the smallest capacity, then 4 granules in flight per lane
+        const int64_t w = window_granules(g, wave_row_wa(v));
+        if ((int64_t)v.G * v.K < w) continue;
         const int64_t cap = (int64_t)v.G * v.K;
-        const int inflight = v.K * v.U;
-        const int64_t key = cap * 64 + (inflight == 4 ? 0 : inflight < 4 ? 8 - inflight : inflight);
+        const int want_u = (v.G == 64 && v.K == 1) ? 2 : 1;
+        const int64_t key = cap * 64 + (v.U == want_u ? 0 : v.U);
         if (best < 0 || key < best_key) {
             best = i;
             best_key = key;
@@ -110,10 +136,10 @@ int pick_wave_row(int64_t wmax) {
     return best;
 }
 
-int pick_onepass(int64_t wmax) {
+int pick_onepass(int64_t w) {
     int best = -1;
     for (int i = 0; i < rws::kNumOnepass; ++i) {
-        if (onepass_capacity(rws::kOnepass[i]) < wmax) continue;
+        if (onepass_capacity(rws::kOnepass[i]) < w) continue;
         if (best < 0 || onepass_capacity(rws::kOnepass[i]) < onepass_capacity(rws::kOnepass[best]))
             best = i;
     }
@@ -156,66 +182,75 @@ int pick_splitk(int64_t rows, int64_t wmax, int cus, int* P_out) {
 
 int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
                 int kernel_id, Plan* p) {
-    const uintptr_t ai = (uintptr_t)in, ao = (uintptr_t)out;
-    p->aligned = (ai % 16 == 0) && (ao % 16 == 0) && ((cols * elem_size(dtype)) % 16 == 0);
-    p->same_phase = (ai % 16) == (ao % 16);
-    const int64_t wmax = window_max(cols, dtype, p->aligned);
+    const Geometry g = geometry(cols, dtype, in, out);
+    p->same_phase = g.same_phase;
+    const int64_t wline = window_granules(g, 128);  // block-level kernels
     const int cus = device_info().cus;
 
     int family = kernel_id;
     if (family == RWS_KERNEL_AUTO) {
-        const int64_t wave_cap = 64 * 8;  // largest wave_row window (G=64, K=8)
         const bool few_rows = rows < 2LL * cus;
-        if (wmax <= 128) {
+        const bool wave_fits = pick_wave_row(g) >= 0;
+        if (wline <= 136 && wave_fits) {
             family = RWS_KERNEL_WAVE_ROW;
-        } else if (few_rows && wmax >= 2048) {
+        } else if (few_rows && wline >= 2048) {
             family = RWS_KERNEL_SPLITK;
-        } else if (wmax <= 512 && wmax <= wave_cap) {
+        } else if (wline <= 512 && wave_fits) {
             family = RWS_KERNEL_WAVE_ROW;
-        } else if (pick_onepass(wmax) >= 0 && wmax <= 8192) {
+        } else if (pick_onepass(wline) >= 0 && wline <= 8192) {
             family = RWS_KERNEL_BLOCK_ONEPASS;
         } else if (few_rows) {
             family = RWS_KERNEL_SPLITK;
-        } else if (pick_onepass(wmax) >= 0) {
+        } else if (pick_onepass(wline) >= 0) {
             family = RWS_KERNEL_BLOCK_ONEPASS;
         } else {
             family = RWS_KERNEL_TWO_PASS;
         }
     }
     p->family = family;
+    p->aligned = g.a128;
+    p->window = wline;
     switch (family) {
         case RWS_KERNEL_WAVE_ROW: {
-            p->variant = pick_wave_row(wmax);
+            p->variant = pick_wave_row(g);
             if (p->variant < 0)
                 return fail(RWS_ERR_UNSUPPORTED_SHAPE,
-                            "wave_row holds at most 512 granules (16 bytes) per row");
+                            "wave_row holds at most 512 granules (16 bytes) per row window");
             const rws::WaveRowVariant& v = rws::kWaveRow[p->variant];
+            const int wa = wave_row_wa(v);
+            p->aligned = wa == 128 ? g.a128 : g.a16;
+            p->window = window_granules(g, wa);
+            // XCD-aware order measured faster only for full-wave rows
+            p->remap = v.G == 64;
             // keep (workgroups x 256 threads) of one launch below 2^32
             p->max_rows_per_launch = (int64_t)(64 / v.G) * v.U * 4 * ((int64_t)1 << 23);
             break;
         }
         case RWS_KERNEL_BLOCK_ONEPASS: {
-            p->variant = pick_onepass(wmax);
+            p->variant = pick_onepass(wline);
             if (p->variant < 0)
                 return fail(RWS_ERR_UNSUPPORTED_SHAPE,
-                            "block_onepass holds at most 16384 granules (16 bytes) per row");
+                            "block_onepass holds at most 16384 granules (16 bytes) per row window");
+            p->remap = false;
             p->max_rows_per_launch = (int64_t)1 << 22;
             break;
         }
         case RWS_KERNEL_TWO_PASS: {
             // 256 threads for short rows, 512 up to 4096 granules, then 1024
-            const int want_block = wmax > 4096 ? 1024 : wmax > 1024 ? 512 : 256;
+            const int want_block = wline > 4096 ? 1024 : wline > 1024 ? 512 : 256;
             p->variant = 0;
             for (int i = 0; i < rws::kNumTwoPass; ++i)
                 if (rws::kTwoPass[i].block == want_block && rws::kTwoPass[i].u == 4) p->variant = i;
+            p->remap = false;
             p->max_rows_per_launch = (int64_t)1 << 22;
             break;
         }
         case RWS_KERNEL_SPLITK: {
             int P = 1;
-            p->variant = pick_splitk(rows, wmax, cus, &P);
+            p->variant = pick_splitk(rows, wline, cus, &P);
             if (p->variant < 0) return fail(RWS_ERR_UNSUPPORTED_SHAPE, "split-k: no variant");
             p->P = P;
+            p->remap = false;
             p->max_rows_per_launch = std::max<int64_t>(1, ((int64_t)1 << 23) / P);
             break;
         }
@@ -326,6 +361,7 @@ int softmax_fwd_kernel(const void* in, void* out, int64_t rows, int64_t cols, in
         L.dtype = dtype;
         L.aligned = p.aligned;
         L.same_phase = p.same_phase;
+        L.remap = p.remap;
         L.stream = s;
         hipError_t e = hipSuccess;
         switch (p.family) {
@@ -374,13 +410,13 @@ int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void* i
     const int st = plan_launch(rows, cols, dtype, in, out, kernel_id, &p);
     if (st != RWS_OK) return st;
     const char* al = p.aligned ? "aligned" : (p.same_phase ? "unaligned" : "unaligned,split-phase");
-    const int64_t wmax = window_max(cols, dtype, p.aligned);
+    const int64_t wmax = p.window;
     switch (p.family) {
         case RWS_KERNEL_WAVE_ROW: {
             const rws::WaveRowVariant& v = rws::kWaveRow[p.variant];
             std::snprintf(buf, (size_t)buflen,
-                          "wave_row<%s,%s,G=%d,K=%d,U=%d> grid=%lld block=256 window<=%lld",
-                          dtype_name(dtype), al, v.G, v.K, v.U,
+                          "wave_row<%s,%s,G=%d,K=%d,U=%d>%s grid=%lld block=256 window<=%lld",
+                          dtype_name(dtype), al, v.G, v.K, v.U, p.remap ? " xcd" : "",
                           (long long)rws::wave_row_grid(v, std::min(rows, p.max_rows_per_launch)),
                           (long long)wmax);
             break;
@@ -388,23 +424,23 @@ int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void* i
         case RWS_KERNEL_BLOCK_ONEPASS: {
             const rws::OnepassVariant& v = rws::kOnepass[p.variant];
             std::snprintf(buf, (size_t)buflen,
-                          "block_onepass<%s,%s,B=%d,KR=%d,KL=%d> grid=%lld block=%d window<=%lld",
-                          dtype_name(dtype), al, v.block, v.kr, v.kl,
+                          "block_onepass<%s,%s,B=%d,KR=%d,KL=%d>%s grid=%lld block=%d window<=%lld",
+                          dtype_name(dtype), al, v.block, v.kr, v.kl, p.remap ? " xcd" : "",
                           (long long)std::min(rows, p.max_rows_per_launch), v.block, (long long)wmax);
             break;
         }
         case RWS_KERNEL_TWO_PASS: {
             const rws::TwoPassVariant& v = rws::kTwoPass[p.variant];
-            std::snprintf(buf, (size_t)buflen, "two_pass<%s,%s,B=%d,U=%d> grid=%lld block=%d window<=%lld",
-                          dtype_name(dtype), al, v.block, v.u,
+            std::snprintf(buf, (size_t)buflen, "two_pass<%s,%s,B=%d,U=%d>%s grid=%lld block=%d window<=%lld",
+                          dtype_name(dtype), al, v.block, v.u, p.remap ? " xcd" : "",
                           (long long)std::min(rows, p.max_rows_per_launch), v.block, (long long)wmax);
             break;
         }
         case RWS_KERNEL_SPLITK: {
             const rws::SplitkVariant& v = rws::kSplitk[p.variant];
             std::snprintf(buf, (size_t)buflen,
-                          "splitk<%s,%s,B=%d,KC=%d> P=%d grid=%lld x2 block=%d window<=%lld",
-                          dtype_name(dtype), al, v.block, v.kc, p.P,
+                          "splitk<%s,%s,B=%d,KC=%d>%s P=%d grid=%lld x2 block=%d window<=%lld",
+                          dtype_name(dtype), al, v.block, v.kc, p.remap ? " xcd" : "", p.P,
                           (long long)(std::min(rows, p.max_rows_per_launch) * p.P), v.block,
                           (long long)wmax);
             break;

@@ -98,31 +98,40 @@ struct Elem<kBF16> {
 };
 
 // ---------------------------------------------------------------------------
-// Row window: the aligned granules that overlap one row.
-//   lead  = elements of the first granule that precede the row (0..VEC-1)
-//   ngran = number of granules overlapping the row
+// Row window: the granules, starting on a WA-byte boundary (WA = 128, one
+// cache line, or 16 for lane groups narrower than a line), that cover one row.
+//   lead  = elements of the window that precede the row (0 .. WA/size - 1)
+//   ngran = number of granules in the window
 // Granule k holds row columns c0 = k*VEC - lead .. c0+VEC-1; it is "interior"
 // (all VEC elements belong to the row) iff c0 >= 0 and c0 + VEC <= cols.
-// With ALIGNED (row start 16-byte aligned and cols*size % 16 == 0) lead == 0
+// Starting the window on a line boundary means that the 64 lanes of a wave
+// writing 64 consecutive granules cover 8 whole 128-byte lines; only the
+// row's first and last line are shared with the neighbouring rows.  (A window
+// that started on the row's 16-byte granule would split two lines per store
+// instruction for every row that is not line-aligned.)
+// With ALIGNED (row start 128-byte aligned and cols*size % 128 == 0) lead == 0
 // and every granule is interior.
 //
 // Loads are split in two so that a thread issues all of its 128-bit loads
 // before it waits for any: fetch() only loads, widen() converts and masks.
 //  * ALIGNED: fetch(k) reads granule min(k, ngran-1) (always inside the row);
 //    widen() turns granules k >= ngran into -inf.
-//  * unaligned: fetch(k) reads the whole 16-byte granule whenever it lies
-//    inside the tensor [tbeg, tend) -- a partial granule then also holds bytes
-//    of the neighbouring row, which widen() replaces by -inf.  Only the first
-//    granule of the tensor and its last one can stick out of it; those two are
-//    read element by element inside widen(), so no byte outside the tensor is
-//    ever read.
+//  * unaligned: fetch(k) reads the whole 16-byte granule whenever it overlaps
+//    the row and lies inside the tensor [tbeg, tend) -- a partial granule then
+//    also holds bytes of the neighbouring row, which widen() replaces by
+//    -inf.  Only the first granule of the tensor and its last one can stick
+//    out of it; those two are read element by element inside widen(), so no
+//    byte outside the tensor is ever read.
 // ---------------------------------------------------------------------------
-template <int DT, bool ALIGNED>
+constexpr int kLineBytes = 128;
+
+template <int DT, bool ALIGNED, int WA = kLineBytes>
 struct RowWin {
+    static_assert(WA == 16 || WA == 32 || WA == 64 || WA == 128, "window alignment");
     static constexpr int VEC = Elem<DT>::VEC;
     static constexpr int ES = Elem<DT>::SIZE;
-    const char* gin;   // first granule of the row in `in` (16-byte aligned)
-    char* gout;        // same granule position in `out` (used when same_phase)
+    const char* gin;   // first granule of the window in `in` (line aligned)
+    char* gout;        // same position in `out` (used when same_phase)
     char* rout;        // row start in `out`
     int lead;
     int ngran;
@@ -140,7 +149,7 @@ struct RowWin {
             ngran = cols_ / VEC;
         } else {
             uintptr_t a = (uintptr_t)rin;
-            int mis = (int)(a & 15u);
+            int mis = (int)(a & (WA - 1));
             lead = mis / ES;
             gin = rin - mis;
             gout = rout - mis;
@@ -161,8 +170,9 @@ struct RowWin {
             return *(const u32x4*)(gin + (int64_t)kk * 16);
         }
         const char* g = gin + (int64_t)k * 16;
+        const int c0 = k * VEC - lead;
         u32x4 raw = {0u, 0u, 0u, 0u};
-        if (g >= tbeg && g + 16 <= tend) raw = *(const u32x4*)g;
+        if (c0 + VEC > 0 && c0 < cols && g >= tbeg && g + 16 <= tend) raw = *(const u32x4*)g;
         return raw;
     }
 
@@ -202,15 +212,17 @@ struct RowWin {
     // Store granule k.  same_phase: `out` rows share the 16-byte phase of `in`
     // rows, so interior granules are stored as 128-bit words; otherwise every
     // element is stored on its own.  Elements outside the row are never
-    // written.
+    // written.  The 128-bit stores are non-temporal: the output is written
+    // once and not read back by the kernel, and streaming it past the caches
+    // measured about 15% faster on MI355X than ordinary stores.
     __device__ inline void store(int k, const float* v, bool same_phase) const {
         if (ALIGNED) {
-            *(u32x4*)(gout + (int64_t)k * 16) = Elem<DT>::narrow(v);
+            __builtin_nontemporal_store(Elem<DT>::narrow(v), (u32x4*)(gout + (int64_t)k * 16));
             return;
         }
         const int c0 = k * VEC - lead;
         if (same_phase && c0 >= 0 && c0 + VEC <= cols) {
-            *(u32x4*)(gout + (int64_t)k * 16) = Elem<DT>::narrow(v);
+            __builtin_nontemporal_store(Elem<DT>::narrow(v), (u32x4*)(gout + (int64_t)k * 16));
         } else {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
@@ -262,6 +274,22 @@ __device__ inline float merge_scale(float m_part, float M) {
     if (m_part == M) return 1.0f;
     RowExp er(M);
     return er.one(m_part);
+}
+
+// ---------------------------------------------------------------------------
+// XCD-aware workgroup order.  MI355X has 8 XCDs (each with its own L2) and
+// hands out consecutive workgroups round-robin across them, so workgroup b
+// runs on XCD b % 8.  Renumbering gives each XCD one contiguous range of the
+// logical work (rows).  The map is a bijection of [0, nb) for any nb; the
+// dispatcher enables it per kernel family where it measured faster.
+// ---------------------------------------------------------------------------
+constexpr int kXcds = 8;
+
+__device__ inline int64_t xcd_remap(int64_t b, int64_t nb) {
+    const int64_t x = b % kXcds;       // XCD this workgroup runs on
+    const int64_t j = b / kXcds;       // its rank among that XCD's workgroups
+    const int64_t q = nb / kXcds, r = nb % kXcds;
+    return x * q + (x < r ? x : r) + j;
 }
 
 // ---------------------------------------------------------------------------

@@ -39,7 +39,7 @@ __device__ inline const char* tensor_end(const void* in, int64_t rows, int cols)
 template <int DT, bool ALIGNED, int G, int K, int U>
 __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
                                                   void* __restrict__ out, int64_t rows,
-                                                  int cols, int same_phase) {
+                                                  int cols, int same_phase, int remap) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int RPS = 64 / G;  // rows per set
     constexpr int N = K * VEC;   // elements per lane per row
@@ -47,21 +47,23 @@ __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
     const int gl = lane & (G - 1);
     const int sub = lane / G;
     // The wave index is uniform: readfirstlane keeps the row arithmetic scalar.
-    const int64_t wave_id =
-        (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t block = (remap ? xcd_remap(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
+    const int64_t wave_id = block * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t row0 = wave_id * (RPS * U);
     const char* tbeg = (const char*)in;
     const char* tend = tensor_end<DT>(in, rows, cols);
     // ALIGNED rows whose window fills all G*K slots need no masking.
     const bool full = ALIGNED && (cols / VEC >= G * K);
 
-    RowWin<DT, ALIGNED> w[U];
+    // lane groups of at least one cache line get line-aligned windows
+    constexpr int WA = G * 16 >= kLineBytes ? kLineBytes : 16;
+    RowWin<DT, ALIGNED, WA> w[U];
     u32x4 raw[U][K];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         int64_t row = row0 + u * RPS + sub;
         row = row < rows ? row : rows - 1;
-        w[u] = RowWin<DT, ALIGNED>(in, out, row, cols);
+        w[u] = RowWin<DT, ALIGNED, WA>(in, out, row, cols);
 #pragma unroll
         for (int i = 0; i < K; ++i) raw[u][i] = w[u].fetch(gl + G * i, tbeg, tend);
     }
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
 template <int DT, bool ALIGNED, int BLOCK, int KR, int KL>
 __global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict__ in,
                                                          void* __restrict__ out, int64_t rows,
-                                                         int cols, int same_phase) {
+                                                         int cols, int same_phase, int remap) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     constexpr int N = KR * VEC;
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict_
     __shared__ float red_sum[W];
     __shared__ u32x4 park[KL > 0 ? KL : 1][BLOCK];
     const int t = threadIdx.x;
-    const int64_t row = blockIdx.x;
+    const int64_t row = (remap ? xcd_remap(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
     const char* tbeg = (const char*)in;
     const char* tend = tensor_end<DT>(in, rows, cols);
     const RowWin<DT, ALIGNED> w(in, out, row, cols);
@@ -238,13 +240,13 @@ __device__ inline void block_merge(float m, float d, float& M, float& D, float* 
 template <int DT, bool ALIGNED, int BLOCK, int U>
 __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
                                                     void* __restrict__ out, int64_t rows,
-                                                    int cols, int same_phase) {
+                                                    int cols, int same_phase, int remap) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     __shared__ float red_max[W];
     __shared__ float red_sum[W];
     const int t = threadIdx.x;
-    const int64_t row = blockIdx.x;
+    const int64_t row = (remap ? xcd_remap(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
     const char* tbeg = (const char*)in;
     const char* tend = tensor_end<DT>(in, rows, cols);
     const RowWin<DT, ALIGNED> w(in, out, row, cols);
@@ -300,15 +302,16 @@ __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
 template <int DT, bool ALIGNED, int BLOCK, int KC>
 __global__ __launch_bounds__(BLOCK) void k_splitk_stage1(const void* __restrict__ in,
                                                          int64_t rows, int cols, int P,
-                                                         float2* __restrict__ ws) {
+                                                         float2* __restrict__ ws, int remap) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     constexpr int N = KC * VEC;
     __shared__ float red_max[W];
     __shared__ float red_sum[W];
     const int t = threadIdx.x;
-    const int64_t row = blockIdx.x / P;
-    const int chunk = blockIdx.x - (int)(row * P);
+    const int64_t b = (remap ? xcd_remap(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
+    const int64_t row = b / P;
+    const int chunk = (int)(b - row * P);
     const char* tbeg = (const char*)in;
     const char* tend = tensor_end<DT>(in, rows, cols);
     const RowWin<DT, ALIGNED> w(in, const_cast<void*>(in), row, cols);  // out unused
@@ -345,14 +348,15 @@ __global__ __launch_bounds__(BLOCK) void k_splitk_stage2(const void* __restrict_
                                                          void* __restrict__ out, int64_t rows,
                                                          int cols, int P,
                                                          const float2* __restrict__ ws,
-                                                         int same_phase) {
+                                                         int same_phase, int remap) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     __shared__ float red_max[W];
     __shared__ float red_sum[W];
     const int t = threadIdx.x;
-    const int64_t row = blockIdx.x / P;
-    const int chunk = blockIdx.x - (int)(row * P);
+    const int64_t b = (remap ? xcd_remap(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
+    const int64_t row = b / P;
+    const int chunk = (int)(b - row * P);
     const char* tbeg = (const char*)in;
     const char* tend = tensor_end<DT>(in, rows, cols);
     const RowWin<DT, ALIGNED> w(in, out, row, cols);
@@ -386,30 +390,6 @@ __global__ __launch_bounds__(BLOCK) void k_splitk_stage2(const void* __restrict_
 #pragma unroll
             for (int e = 0; e < VEC; ++e) f[e] = er.one(f[e]) * r;
             w.store(k, f, same_phase != 0);
-        }
-    }
-}
-
-// ===========================================================================
-// Plain 16-byte copy (the copy ceiling and counter calibration): every thread
-// moves UNROLL granules per grid-stride step, loads first.
-// ===========================================================================
-template <int UNROLL>
-__global__ __launch_bounds__(256) void k_copy16(const u32x4* __restrict__ in,
-                                                u32x4* __restrict__ out, int64_t n) {
-    const int64_t stride = (int64_t)gridDim.x * 256 * UNROLL;
-    for (int64_t base = (int64_t)blockIdx.x * 256 * UNROLL + threadIdx.x; base < n;
-         base += stride) {
-        u32x4 g[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int64_t i = base + (int64_t)u * 256;
-            if (i < n) g[u] = in[i];
-        }
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-            const int64_t i = base + (int64_t)u * 256;
-            if (i < n) out[i] = g[u];
         }
     }
 }

@@ -4,6 +4,8 @@
 #include "rws_kernels.hpp"
 #include "rws_launch.hpp"
 
+#include <algorithm>
+
 namespace rws {
 
 // (threads, granules per thread per chunk)
@@ -22,11 +24,11 @@ template <int DT, bool AL, int B, int KC>
 static hipError_t go(const Launch& L, int P, float2* ws) {
     const dim3 grid((unsigned)(L.rows * P));
     hipLaunchKernelGGL((k_splitk_stage1<DT, AL, B, KC>), grid, dim3(B), 0, L.stream, L.in, L.rows,
-                       L.cols, P, ws);
+                       L.cols, P, ws, (int)L.remap);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_splitk_stage2<DT, AL, B, KC>), grid, dim3(B), 0, L.stream, L.in, L.out,
-                       L.rows, L.cols, P, (const float2*)ws, (int)L.same_phase);
+                       L.rows, L.cols, P, (const float2*)ws, (int)L.same_phase, (int)L.remap);
     return hipGetLastError();
 }
 
@@ -50,14 +52,28 @@ hipError_t launch_splitk(const Launch& L, int variant, int P, float2* ws) {
     return hipErrorInvalidValue;
 }
 
+// ===========================================================================
+// Plain 16-byte copy (the copy ceiling and the calibration of the traffic
+// counters): one granule per thread, non-temporal stores like the softmax
+// kernels (the fastest plain copy measured on MI355X).
+// ===========================================================================
+__global__ __launch_bounds__(256) void k_copy16(const u32x4* __restrict__ in,
+                                                u32x4* __restrict__ out, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) __builtin_nontemporal_store(in[i], out + i);
+}
+
 hipError_t launch_copy16(const void* in, void* out, int64_t n16, hipStream_t stream) {
-    constexpr int UNROLL = 4;
-    int64_t grid = (n16 + 256 * UNROLL - 1) / (256 * UNROLL);
-    if (grid > (1 << 20)) grid = 1 << 20;
-    if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((k_copy16<UNROLL>), dim3((unsigned)grid), dim3(256), 0, stream,
-                       (const u32x4*)in, (u32x4*)out, n16);
-    return hipGetLastError();
+    for (int64_t done = 0; done < n16;) {
+        // at most 2^23 workgroups of 256 threads per launch
+        const int64_t n = std::min<int64_t>(n16 - done, (int64_t)1 << 31);
+        hipLaunchKernelGGL(k_copy16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                           (const u32x4*)in + done, (u32x4*)out + done, n);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        done += n;
+    }
+    return hipSuccess;
 }
 
 }  // namespace rws

@@ -39,13 +39,15 @@ def run(x: torch.Tensor, out: torch.Tensor, kernel: str = "auto") -> np.ndarray:
 
 
 def window_granules(cols: int, dtype: str, aligned: bool) -> int:
+    """Granules of a row window that starts on a 128-byte line (upper bound)."""
     es = 4 if dtype == "f32" else 2
     b = cols * es
-    return b // 16 if aligned else (b + 30) // 16
+    return b // 16 if aligned else (b + 143) // 16
 
 
 def supports(kernel: str, cols: int, dtype: str, aligned: bool) -> bool:
-    w = window_granules(cols, dtype, aligned)
+    es = 4 if dtype == "f32" else 2
+    w = window_granules(cols, dtype, aligned and (cols * es) % 128 == 0)
     if kernel == "wave_row":
         return w <= 512
     if kernel == "block_onepass":

@@ -234,7 +234,8 @@ def test_nonfinite_rows(dtype):
 
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_deterministic(kernel):
-    x, _ = to_device(_gen(33, 4097, seed=77), "f16", offset=1)
+    cols = 4001 if kernel == "wave_row" else 4097  # wave_row holds <= 512 granules
+    x, _ = to_device(_gen(33, cols, seed=77), "f16", offset=1)
     a = torch.empty_like(x)
     b = torch.empty_like(x)
     rws.softmax(x, out=a, kernel=kernel)
