@@ -38,9 +38,11 @@ PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 # i.e. 134217728 B / 0.62 ms.  Another machine: context only.
 PAGES_FP16_ATTN_GBPS = 134217728 / 0.62e-3 / 1e9
 KERNEL_SOURCES = ["rws_device.hpp", "rws_kernels.hpp", "rws_wave_row.hip",
-                  "rws_block_onepass.hip", "rws_two_pass.hip", "rws_splitk.hip"]
+                  "rws_block_onepass.hip", "rws_two_pass.hip", "rws_splitk.hip",
+                  "rws_splitk_fused.hip"]
 KERNEL_SYMBOL = {"wave_row": "k_wave_row", "block_onepass": "k_block_onepass",
-                 "two_pass": "k_two_pass", "splitk": "k_splitk_stage"}
+                 "two_pass": "k_two_pass", "splitk": "k_splitk_stage",
+                 "splitk_fused": "k_splitk_fused"}
 
 
 def kernel_source_hash() -> str:

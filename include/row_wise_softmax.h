@@ -35,12 +35,13 @@
  * null stream).  All work is enqueued on it; no call synchronises the host.
  * The result is valid once the stream reaches the enqueued work.
  *
- * Ownership.  The caller owns `in` and `out`.  For the split-k path the
- * library owns a small workspace (8 bytes per row per chunk) that it keeps
- * per (device, stream) and grows on demand; the first call that needs a
- * larger workspace allocates it (hipMalloc), later calls reuse it.  Calls on
- * one stream are ordered, so reuse is safe; the workspaces are released when
- * the library is unloaded.
+ * Ownership.  The caller owns `in` and `out`.  For the split-k paths the
+ * library owns a small workspace (8 bytes per row per chunk, plus 256 bytes
+ * per row of arrival counters for the single-launch form) that it keeps per
+ * (device, stream) and grows on demand; the first call that needs a larger
+ * workspace allocates it (hipMalloc; counters are zeroed once then), later
+ * calls reuse it.  Calls on one stream are ordered, so reuse is safe; the
+ * workspaces are released when the library is unloaded.
  *
  * Errors.  Every entry point returns a status code (below) and never exits or
  * throws.  rows == 0 or cols == 0 is a successful no-op.  A HIP launch error
@@ -87,10 +88,21 @@ enum {
     RWS_KERNEL_TWO_PASS = 3,  /* one workgroup per row, any cols: pass 1 running
                                  (m, d), pass 2 re-reads the row (CUDA
                                  safe-online-softmax page, section 3.1) */
-    RWS_KERNEL_SPLITK = 4     /* several workgroups per row: stage 1 writes a
+    RWS_KERNEL_SPLITK = 4,    /* several workgroups per row: stage 1 writes a
                                  partial (m, d) per chunk, stage 2 merges a
                                  row's partials and writes the outputs (CUDA
                                  safe-online-softmax page, section 3.2) */
+    RWS_KERNEL_SPLITK_FUSED = 5 /* split-k in one cooperative launch: each
+                                 workgroup keeps its chunk in registers, the
+                                 row's workgroups exchange partial (m, d) through
+                                 memory and a per-row arrival counter, so the
+                                 input is read once (the single-kernel form the
+                                 same page, section 3.2, mentions).  Returns
+                                 RWS_ERR_UNSUPPORTED_SHAPE when the grid cannot
+                                 be co-resident on the device.  Never chosen
+                                 by the dispatcher: on MI355X its cross-XCD
+                                 synchronisation costs more than the re-read
+                                 it saves */
 };
 
 /*

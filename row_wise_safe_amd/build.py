@@ -24,6 +24,7 @@ SOURCES = [
     "rws_block_onepass.hip",
     "rws_two_pass.hip",
     "rws_splitk.hip",
+    "rws_splitk_fused.hip",
 ]
 
 COMMON_FLAGS = [

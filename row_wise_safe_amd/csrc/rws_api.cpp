@@ -18,6 +18,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <tuple>
 #include <mutex>
 #include <string>
 #include <algorithm>
@@ -180,6 +181,53 @@ int pick_splitk(int64_t rows, int64_t wmax, int cus, int* P_out) {
     return best;
 }
 
+// Co-resident workgroup capacity of a fused split-k variant on the current
+// device (cached); without a device, an estimate of two per CU.
+int64_t fused_capacity(int variant, int dtype, bool aligned) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, int, int, int>, int64_t> cache;
+    const DeviceInfo info = device_info();
+    if (!info.known) return 2LL * info.cus;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const auto key = std::make_tuple(dev, variant, dtype, aligned ? 1 : 0);
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int64_t blocks = 0;
+    const hipError_t e = rws::splitk_fused_capacity(variant, dtype, aligned, info.cus, &blocks);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        blocks = -(int64_t)e;  // negative: the occupancy query failed with this error
+    }
+    cache[key] = blocks;
+    return blocks;
+}
+
+// Single-launch split-k: the largest chunk whose grid still gives every CU
+// two workgroups and fits the co-resident capacity; else any chunk that fits.
+// Returns -1 when no variant's grid can be co-resident.
+int pick_splitk_fused(int64_t rows, int64_t wmax, int dtype, bool aligned, int cus, int* P_out) {
+    int best = -1, bestP = 1;
+    for (int pass = 0; pass < 2 && best < 0; ++pass) {
+        for (int i = 0; i < rws::kNumSplitkFused; ++i) {
+            const rws::SplitkVariant& v = rws::kSplitkFused[i];
+            const int64_t cg = (int64_t)v.block * v.kc;
+            const int64_t P = (wmax + cg - 1) / cg;
+            if (rows * P > fused_capacity(i, dtype, aligned)) continue;
+            if (pass == 0 && rows * P < 2LL * cus) continue;
+            const bool better = best < 0 || (pass == 0 ? v.kc > rws::kSplitkFused[best].kc
+                                                       : v.kc < rws::kSplitkFused[best].kc);
+            if (better) {
+                best = i;
+                bestP = (int)P;
+            }
+        }
+    }
+    *P_out = bestP;
+    return best;
+}
+
 int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
                 int kernel_id, Plan* p) {
     const Geometry g = geometry(cols, dtype, in, out);
@@ -245,6 +293,25 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
             p->max_rows_per_launch = (int64_t)1 << 22;
             break;
         }
+        case RWS_KERNEL_SPLITK_FUSED: {
+            int P = 1;
+            p->variant = pick_splitk_fused(rows, wline, dtype, g.a128, cus, &P);
+            if (p->variant < 0) {
+                std::string caps;
+                for (int i = 0; i < rws::kNumSplitkFused; ++i) {
+                    const int64_t cg = (int64_t)rws::kSplitkFused[i].block * rws::kSplitkFused[i].kc;
+                    caps += " " + std::to_string(rows * ((wline + cg - 1) / cg)) + "/" +
+                            std::to_string(fused_capacity(i, dtype, g.a128));
+                }
+                return fail(RWS_ERR_UNSUPPORTED_SHAPE,
+                            "single-launch split-k: the grid cannot be co-resident on this device "
+                            "(workgroups/capacity per variant:" + caps + ")");
+            }
+            p->P = P;
+            p->remap = false;
+            p->max_rows_per_launch = rows;
+            break;
+        }
         case RWS_KERNEL_SPLITK: {
             int P = 1;
             p->variant = pick_splitk(rows, wline, cus, &P);
@@ -265,8 +332,11 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
 // stream is ordered, so a buffer is never used by two launches at once.
 // ---------------------------------------------------------------------------
 struct Workspace {
-    void* ptr = nullptr;
+    void* ptr = nullptr;        // split-k partials
     size_t bytes = 0;
+    unsigned* sync = nullptr;   // single-launch split-k: kSyncWordsPerRow words per row
+    int64_t sync_rows = 0;
+    unsigned epoch = 0;         // last epoch handed to a single-launch call
 };
 
 std::mutex g_ws_mu;
@@ -277,34 +347,42 @@ struct WorkspaceReaper {
         // Buffers are released at unload; a device that is already torn down
         // reports an error here, which is ignored.
         if (!g_ws) return;
-        for (auto& kv : *g_ws)
+        for (auto& kv : *g_ws) {
             if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+            if (kv.second.sync) (void)hipFree(kv.second.sync);
+        }
         delete g_ws;
         g_ws = nullptr;
     }
 } g_ws_reaper;
 
-int get_workspace(hipStream_t stream, size_t bytes, void** out) {
+// Grow-only workspace of (device, stream): `bytes` of partials and, when
+// sync_rows > 0, kSyncWordsPerRow*sync_rows zeroed counter words.  Returns the epoch for a
+// single-launch call in *epoch (when epoch != nullptr).
+int get_workspace(hipStream_t stream, size_t bytes, int64_t sync_rows, void** out,
+                  unsigned** sync, unsigned* epoch) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(RWS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
     std::lock_guard<std::mutex> lock(g_ws_mu);
     if (!g_ws) g_ws = new std::map<std::pair<int, hipStream_t>, Workspace>();
     Workspace& w = (*g_ws)[std::make_pair(dev, stream)];
-    if (w.bytes < bytes) {
-        if (w.ptr) {
-            // the old buffer may still be read by earlier work on this stream
-            e = hipStreamSynchronize(stream);
-            if (e != hipSuccess)
-                return fail(RWS_ERR_HIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
-            (void)hipFree(w.ptr);
-            w.ptr = nullptr;
-            w.bytes = 0;
-        }
+    const bool grow_partials = w.bytes < bytes;
+    const bool grow_sync = sync_rows > w.sync_rows;
+    if ((grow_partials || grow_sync) && (w.ptr || w.sync)) {
+        // the old buffers may still be in use by earlier work on this stream
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess)
+            return fail(RWS_ERR_HIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+    }
+    if (std::getenv("RWS_TEST_FAIL_ALLOC") && (grow_partials || grow_sync))
+        return fail(RWS_ERR_HIP, "workspace allocation failed (RWS_TEST_FAIL_ALLOC)");
+    if (grow_partials) {
+        if (w.ptr) (void)hipFree(w.ptr);
+        w.ptr = nullptr;
+        w.bytes = 0;
         size_t want = 4096;
         while (want < bytes) want *= 2;
-        if (std::getenv("RWS_TEST_FAIL_ALLOC"))
-            return fail(RWS_ERR_HIP, "workspace allocation failed (RWS_TEST_FAIL_ALLOC)");
         e = hipMalloc(&w.ptr, want);
         if (e != hipSuccess) {
             w.ptr = nullptr;
@@ -312,14 +390,35 @@ int get_workspace(hipStream_t stream, size_t bytes, void** out) {
         }
         w.bytes = want;
     }
+    if (grow_sync) {
+        if (w.sync) (void)hipFree(w.sync);
+        w.sync = nullptr;
+        w.sync_rows = 0;
+        int64_t want = 256;
+        while (want < sync_rows) want *= 2;
+        const size_t sync_bytes = (size_t)want * rws::kSyncWordsPerRow * sizeof(unsigned);
+        e = hipMalloc((void**)&w.sync, sync_bytes);
+        if (e == hipSuccess) e = hipMemset(w.sync, 0, sync_bytes);
+        if (e != hipSuccess) {
+            if (w.sync) (void)hipFree(w.sync);
+            w.sync = nullptr;
+            return fail(RWS_ERR_HIP, std::string("split-k counters: ") + hipGetErrorString(e));
+        }
+        w.sync_rows = want;
+    }
     *out = w.ptr;
+    if (sync) *sync = w.sync;
+    if (epoch) {
+        if (++w.epoch == 0) ++w.epoch;  // 0 is the value of a fresh counter word
+        *epoch = w.epoch;
+    }
     return RWS_OK;
 }
 
 int check_args(const void* in, void* out, int64_t rows, int64_t cols, int dtype, int kernel_id) {
     if (dtype != RWS_F32 && dtype != RWS_F16 && dtype != RWS_BF16)
         return fail(RWS_ERR_UNSUPPORTED_DTYPE, "dtype must be RWS_F32, RWS_F16 or RWS_BF16");
-    if (kernel_id < RWS_KERNEL_AUTO || kernel_id > RWS_KERNEL_SPLITK)
+    if (kernel_id < RWS_KERNEL_AUTO || kernel_id > RWS_KERNEL_SPLITK_FUSED)
         return fail(RWS_ERR_INVALID_ARG, "unknown kernel id " + std::to_string(kernel_id));
     if (rows < 0 || cols < 0) return fail(RWS_ERR_INVALID_ARG, "rows and cols must be >= 0");
     if (cols > kMaxCols) return fail(RWS_ERR_UNSUPPORTED_SHAPE, "cols above 2^30");
@@ -345,10 +444,15 @@ int softmax_fwd_kernel(const void* in, void* out, int64_t rows, int64_t cols, in
     if (st != RWS_OK) return st;
 
     void* ws = nullptr;
+    unsigned* sync = nullptr;
+    unsigned epoch = 0;
     hipStream_t s = (hipStream_t)stream;
     if (p.family == RWS_KERNEL_SPLITK) {
         const int64_t batch = std::min<int64_t>(rows, p.max_rows_per_launch);
-        st = get_workspace(s, (size_t)batch * p.P * sizeof(float2), &ws);
+        st = get_workspace(s, (size_t)batch * p.P * sizeof(float2), 0, &ws, nullptr, nullptr);
+        if (st != RWS_OK) return st;
+    } else if (p.family == RWS_KERNEL_SPLITK_FUSED) {
+        st = get_workspace(s, (size_t)rows * p.P * sizeof(float2), rows, &ws, &sync, &epoch);
         if (st != RWS_OK) return st;
     }
     const int64_t row_bytes = cols * elem_size(dtype);
@@ -369,6 +473,9 @@ int softmax_fwd_kernel(const void* in, void* out, int64_t rows, int64_t cols, in
             case RWS_KERNEL_BLOCK_ONEPASS: e = rws::launch_block_onepass(L, p.variant); break;
             case RWS_KERNEL_TWO_PASS: e = rws::launch_two_pass(L, p.variant); break;
             case RWS_KERNEL_SPLITK: e = rws::launch_splitk(L, p.variant, p.P, (float2*)ws); break;
+            case RWS_KERNEL_SPLITK_FUSED:
+                e = rws::launch_splitk_fused(L, p.variant, p.P, (float2*)ws, sync, epoch);
+                break;
         }
         if (e != hipSuccess)
             return fail(RWS_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
@@ -398,7 +505,7 @@ int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void* i
     buf[0] = 0;
     if (dtype != RWS_F32 && dtype != RWS_F16 && dtype != RWS_BF16)
         return fail(RWS_ERR_UNSUPPORTED_DTYPE, "dtype must be RWS_F32, RWS_F16 or RWS_BF16");
-    if (kernel_id < RWS_KERNEL_AUTO || kernel_id > RWS_KERNEL_SPLITK)
+    if (kernel_id < RWS_KERNEL_AUTO || kernel_id > RWS_KERNEL_SPLITK_FUSED)
         return fail(RWS_ERR_INVALID_ARG, "unknown kernel id " + std::to_string(kernel_id));
     if (rows < 0 || cols < 0) return fail(RWS_ERR_INVALID_ARG, "rows and cols must be >= 0");
     if (cols > kMaxCols) return fail(RWS_ERR_UNSUPPORTED_SHAPE, "cols above 2^30");
@@ -436,6 +543,15 @@ int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void* i
                           (long long)std::min(rows, p.max_rows_per_launch), v.block, (long long)wmax);
             break;
         }
+        case RWS_KERNEL_SPLITK_FUSED: {
+            const rws::SplitkVariant& v = rws::kSplitkFused[p.variant];
+            std::snprintf(buf, (size_t)buflen,
+                          "splitk_fused<%s,%s,B=%d,KC=%d> P=%d grid=%lld cooperative block=%d "
+                          "window<=%lld",
+                          dtype_name(dtype), al, v.block, v.kc, p.P, (long long)(rows * p.P),
+                          v.block, (long long)wmax);
+            break;
+        }
         case RWS_KERNEL_SPLITK: {
             const rws::SplitkVariant& v = rws::kSplitk[p.variant];
             std::snprintf(buf, (size_t)buflen,
@@ -456,6 +572,7 @@ const char* softmax_kernel_name(int kernel_id) {
         case RWS_KERNEL_BLOCK_ONEPASS: return "block_onepass";
         case RWS_KERNEL_TWO_PASS: return "two_pass";
         case RWS_KERNEL_SPLITK: return "splitk";
+        case RWS_KERNEL_SPLITK_FUSED: return "splitk_fused";
     }
     return "unknown";
 }

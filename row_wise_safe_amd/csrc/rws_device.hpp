@@ -219,6 +219,38 @@ struct RowWin {
         }
     }
 
+    // Mask a fetched granule in its raw form: slots outside the row get the
+    // dtype's -inf bits; a granule that sticks out of the tensor has its row
+    // slots read one by one here.  Integer ops only (no widening).
+    __device__ inline u32x4 mask_raw(int k, u32x4 raw, const char* tbeg, const char* tend) const {
+        const int c0 = k * VEC - lead;
+        const char* g = gin + (int64_t)k * 16;
+        const bool whole = g >= tbeg && g + 16 <= tend;
+        u32x4 o;
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+            if (ES == 4) {
+                const int c = c0 + wd;
+                const bool ok = c >= 0 && c < cols;
+                unsigned v = raw[wd];
+                if (!whole) v = ok ? *(const unsigned*)(g + 4 * wd) : 0u;
+                o[wd] = ok ? v : 0xff800000u;
+            } else {
+                const unsigned ninf = DT == kF16 ? 0xfc00u : 0xff80u;
+                const int c = c0 + 2 * wd;
+                const bool ok0 = c >= 0 && c < cols;
+                const bool ok1 = c + 1 >= 0 && c + 1 < cols;
+                unsigned lo = raw[wd] & 0xffffu, hi = raw[wd] >> 16;
+                if (!whole) {
+                    lo = ok0 ? *(const unsigned short*)(g + 4 * wd) : 0u;
+                    hi = ok1 ? *(const unsigned short*)(g + 4 * wd + 2) : 0u;
+                }
+                o[wd] = (ok0 ? lo : ninf) | ((ok1 ? hi : ninf) << 16);
+            }
+        }
+        return o;
+    }
+
     // Store granule k.  same_phase: `out` rows share the 16-byte phase of `in`
     // rows, so interior granules are stored as 128-bit words; otherwise every
     // element is stored on its own.  Elements outside the row are never

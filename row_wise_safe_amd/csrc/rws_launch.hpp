@@ -33,6 +33,8 @@ extern const TwoPassVariant kTwoPass[];
 extern const int kNumTwoPass;
 extern const SplitkVariant kSplitk[];
 extern const int kNumSplitk;
+extern const SplitkVariant kSplitkFused[];
+extern const int kNumSplitkFused;
 
 // Grid of one wave_row launch (workgroups of 256 threads = 4 waves).
 inline int64_t wave_row_grid(const WaveRowVariant& v, int64_t rows) {
@@ -46,6 +48,14 @@ hipError_t launch_block_onepass(const Launch& L, int variant);
 hipError_t launch_two_pass(const Launch& L, int variant);
 // Both split-k stages; ws holds rows*P (m, d) pairs.
 hipError_t launch_splitk(const Launch& L, int variant, int P, float2* ws);
+// Single-launch split-k (cooperative): ws holds rows*P (m, d) pairs, sync
+// kSyncWordsPerRow words per row (zero-initialised once), epoch grows by one
+// per call on the same sync buffer.
+constexpr int kSyncWordsPerRow = 64;
+hipError_t launch_splitk_fused(const Launch& L, int variant, int P, float2* ws, unsigned* sync,
+                               unsigned epoch);
+// Workgroups of this variant that can be resident at once on `cus` CUs.
+hipError_t splitk_fused_capacity(int variant, int dtype, bool aligned, int cus, int64_t* blocks);
 // n16 granules of 16 bytes.
 hipError_t launch_copy16(const void* in, void* out, int64_t n16, hipStream_t stream);
 

@@ -32,8 +32,17 @@ def empty_like_at(x: torch.Tensor, offset: int = 0):
     return buf[offset:offset + x.numel()].view(x.shape)
 
 
+class NotCoResident(Exception):
+    """The single-launch split-k grid does not fit the device at once."""
+
+
 def run(x: torch.Tensor, out: torch.Tensor, kernel: str = "auto") -> np.ndarray:
-    rws.softmax(x, out=out, kernel=kernel)
+    try:
+        rws.softmax(x, out=out, kernel=kernel)
+    except rws.SoftmaxError as e:
+        if kernel == "splitk_fused" and e.status == rws.RWS_ERR_UNSUPPORTED_SHAPE:
+            raise NotCoResident(str(e))
+        raise
     torch.cuda.synchronize()
     return out.to(torch.float64).cpu().numpy()
 

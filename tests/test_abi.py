@@ -53,8 +53,8 @@ def test_status_strings_and_names(lib):
     for st in range(1, 6):
         assert rws.softmax_status_string(st) not in ("", "ok", "unknown status")
     assert rws.softmax_status_string(99) == "unknown status"
-    assert [rws.softmax_kernel_name(i) for i in range(5)] == \
-        ["auto", "wave_row", "block_onepass", "two_pass", "splitk"]
+    assert [rws.softmax_kernel_name(i) for i in range(6)] == \
+        ["auto", "wave_row", "block_onepass", "two_pass", "splitk", "splitk_fused"]
     assert rws.softmax_kernel_name(17) == "unknown"
 
 
@@ -82,6 +82,7 @@ def test_empty_is_success_without_pointers(lib):
 
 def test_bad_kernel_id(lib):
     assert rws.softmax_fwd_kernel(32, 32, 2, 2, rws.RWS_F32, 0, 9) == rws.RWS_ERR_INVALID_ARG
+    assert rws.softmax_fwd_kernel(32, 32, 2, 2, rws.RWS_F32, 0, 6) == rws.RWS_ERR_INVALID_ARG
 
 
 def test_copy_argument_checks(lib):
