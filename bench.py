@@ -37,17 +37,26 @@ PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 # fp16 [4,32,512,512] on a 60-CU DCU (DCU case-study page, section 5.3),
 # i.e. 134217728 B / 0.62 ms.  Another machine: context only.
 PAGES_FP16_ATTN_GBPS = 134217728 / 0.62e-3 / 1e9
-KERNEL_SOURCES = ["rws_device.hpp", "rws_kernels.hpp", "rws_wave_row.hip",
-                  "rws_block_onepass.hip", "rws_two_pass.hip", "rws_splitk.hip",
-                  "rws_splitk_fused.hip"]
+# Sources that define each family's kernels (the copy kernel used for the
+# counter calibration lives in rws_splitk.hip): a profile summary is valid
+# while these are unchanged.
+KERNEL_SOURCES = {
+    "wave_row": ["rws_device.hpp", "rws_kernels.hpp", "rws_wave_row.hip", "rws_splitk.hip"],
+    "block_onepass": ["rws_device.hpp", "rws_kernels.hpp", "rws_block_onepass.hip",
+                      "rws_splitk.hip"],
+    "two_pass": ["rws_device.hpp", "rws_kernels.hpp", "rws_two_pass.hip", "rws_splitk.hip"],
+    "splitk": ["rws_device.hpp", "rws_kernels.hpp", "rws_splitk.hip"],
+    "splitk_fused": ["rws_device.hpp", "rws_kernels.hpp", "rws_splitk_fused.hip",
+                     "rws_splitk.hip"],
+}
 KERNEL_SYMBOL = {"wave_row": "k_wave_row", "block_onepass": "k_block_onepass",
                  "two_pass": "k_two_pass", "splitk": "k_splitk_stage",
                  "splitk_fused": "k_splitk_fused"}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(family: str) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, "row_wise_safe_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -109,28 +118,33 @@ def summarize_rocprof(directory: str, workload: str, kernel: str, command: str) 
         copy_bytes = meta.get("copy_bytes")
     traffic = None
     if counters.get("FETCH_SIZE") and counters.get("WRITE_SIZE") and copy_bytes:
-        def avg_for(per, pred):
-            vals = [v for name, vs in per.items() if pred(name) for v in vs]
-            return sum(vals) / len(vals) if vals else None
-        f_k = avg_for(counters["FETCH_SIZE"], lambda n: sym in n)
-        w_k = avg_for(counters["WRITE_SIZE"], lambda n: sym in n)
-        f_c = avg_for(counters["FETCH_SIZE"], lambda n: "k_copy16" in n)
-        w_c = avg_for(counters["WRITE_SIZE"], lambda n: "k_copy16" in n)
+        def avg(vs):
+            return sum(vs) / len(vs) if vs else None
+        fetch, write = counters["FETCH_SIZE"], counters["WRITE_SIZE"]
+        copy_name = next((n for n in fetch if "k_copy16" in n), None)
+        f_c = avg(fetch.get(copy_name, [])) if copy_name else None
+        w_c = avg(write.get(copy_name, [])) if copy_name else None
+        names = sorted(n for n in fetch if sym in n)
         lines.append("## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch)")
-        lines.append(f"kernel {sym}: FETCH_SIZE {f_k} KiB, WRITE_SIZE {w_k} KiB")
         lines.append(f"copy kernel k_copy16 ({copy_bytes} B read + {copy_bytes} B written): "
                      f"FETCH_SIZE {f_c} KiB, WRITE_SIZE {w_c} KiB")
-        if None not in (f_k, w_k, f_c, w_c) and f_c > 0 and w_c > 0:
+        if names and f_c and w_c:
             sf = copy_bytes / (f_c * 1024.0)
             sw = copy_bytes / (w_c * 1024.0)
-            traffic = f_k * 1024.0 * sf + w_k * 1024.0 * sw
             lines.append(f"scale factors (true bytes / counter bytes): fetch {sf:.4f}, write {sw:.4f}")
-            lines.append(f"traffic_bytes_per_launch: {traffic:.0f}")
+            traffic = 0.0
+            for n in names:
+                f_k, w_k = avg(fetch[n]), avg(write.get(n, []))
+                lines.append(f"kernel {n}: FETCH_SIZE {f_k:.1f} KiB, WRITE_SIZE {w_k:.1f} KiB "
+                             f"-> {f_k * 1024.0 * sf + w_k * 1024.0 * sw:.0f} B")
+                traffic += f_k * 1024.0 * sf + w_k * 1024.0 * sw
+            lines.append(f"traffic_bytes_per_launch: {traffic:.0f}"
+                         + ("  (sum of the step's kernels)" if len(names) > 1 else ""))
             if meta.get("bytes_per_call"):
                 lines.append(f"algorithmic_bytes_per_launch: {meta['bytes_per_call']}")
                 lines.append(f"traffic / algorithmic: {traffic / meta['bytes_per_call']:.4f}")
         lines.append("")
-    lines.append(f"kernel_source_sha: {kernel_source_hash()}")
+    lines.append(f"kernel_source_sha: {kernel_source_hash(kernel)}")
     os.makedirs(PROFILES, exist_ok=True)
     out = os.path.join(PROFILES, f"{kernel}_{workload}.txt")
     with open(out, "w") as f:
@@ -151,7 +165,7 @@ def read_traffic(workload: str, kernel: str):
                 traffic = float(line.split(":")[1])
             elif line.startswith("kernel_source_sha:"):
                 sha = line.split(":")[1].strip()
-    if traffic is None or sha != kernel_source_hash():
+    if traffic is None or sha != kernel_source_hash(kernel):
         return None
     return traffic
 
