@@ -206,6 +206,9 @@ def main() -> int:
     ap.add_argument("--workload", default="fp16_attn_4x32x512x512")
     ap.add_argument("--kernel", default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--masked", action="store_true",
+                    help="attention-score form: softmax(x/8 + mask[S,S] + causal) with S = cols "
+                         "(softmax_fwd_masked)")
     ap.add_argument("--skip-hot", action="store_true",
                     help="skip the single-buffer figure (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -257,11 +260,26 @@ def main() -> int:
     desc = rws.softmax_describe_launch(w.rows, w.cols, code, xs[0].data_ptr(), ys[0].data_ptr(),
                                        kid)
     family = desc.split("<")[0]
+    mask = None
+    if args.masked:
+        if w.rows % w.cols:
+            print("--masked needs rows to be a multiple of cols (square score blocks)",
+                  file=sys.stderr)
+            return 2
+        g = np.random.Generator(np.random.PCG64(w.seed + 100))
+        mask = torch.from_numpy(g.normal(0.0, 1.0, (w.cols, w.cols))).to(tdt).to(dev)
+        nbytes += mask.numel() * mask.element_size()  # the mask is read once per call
+        desc = "masked " + desc
     log(f"[bench] launch: {desc}; {nbuf} rotating buffer pairs")
 
     def step(i):
-        st = rws.softmax_fwd_kernel(xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), w.rows,
-                                    w.cols, code, sh, kid)
+        if mask is None:
+            st = rws.softmax_fwd_kernel(xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), w.rows,
+                                        w.cols, code, sh, kid)
+        else:
+            st = rws.softmax_fwd_masked(xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), w.rows,
+                                        w.cols, code, 0.125, mask.data_ptr(), w.cols, w.cols, sh,
+                                        kid)
         if st != rws.RWS_OK:
             raise rws.SoftmaxError(st, rws.softmax_last_error())
 
@@ -283,14 +301,12 @@ def main() -> int:
     hot = None
     if not args.skip_hot:
         for i in range(args.warmup):
-            rws.softmax_fwd_kernel(xs[0].data_ptr(), ys[0].data_ptr(), w.rows, w.cols, code, sh,
-                                   kid)
+            step(0)
         torch.cuda.synchronize()
         e0.record(stream)
         hot_steps = max(10, args.steps // 2)
         for i in range(hot_steps):
-            rws.softmax_fwd_kernel(xs[0].data_ptr(), ys[0].data_ptr(), w.rows, w.cols, code, sh,
-                                   kid)
+            step(0)
         e1.record(stream)
         torch.cuda.synchronize()
         hot_ms = e0.elapsed_time(e1) / hot_steps
@@ -307,7 +323,7 @@ def main() -> int:
     e1.record(stream)
     torch.cuda.synchronize()
     copy_ms = e0.elapsed_time(e1) / args.steps
-    copy_gbps = nbytes / (copy_ms * 1e-3) / 1e9
+    copy_gbps = 2 * in_bytes / (copy_ms * 1e-3) / 1e9
     log(f"[bench] copy ceiling {copy_ms * 1e3:.2f} us, {copy_gbps:.1f} GB/s")
 
     if args.meta_out:
@@ -326,8 +342,11 @@ def main() -> int:
     traffic = read_traffic(w.name, family)
     achieved = nbytes / (ms * 1e-3) / 1e9
     vs = round(gbps / PAGES_FP16_ATTN_GBPS, 3) if w.name == "fp16_attn_4x32x512x512" else None
+    if mask is not None:
+        vs = None
     result = {
-        "metric": f"effective HBM GB/s (read+write), {w.description}",
+        "metric": f"effective HBM GB/s (read+write), {w.description}"
+                  + (", softmax(x/8 + mask + causal)" if mask is not None else ""),
         "value": round(gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,

@@ -129,6 +129,32 @@ int softmax_fwd_kernel(const void *in, void *out, int64_t rows, int64_t cols, in
                        void *stream, int kernel_id);
 
 /*
+ * softmax_fwd_masked -- softmax of attention scores with the scale and mask
+ * folded in (DCU case-study page, section 9: a mask parameter in the softmax
+ * kernel saves a launch; Pangu-Weather profile page, section 6: bias + mask +
+ * softmax):
+ *     z[r, j] = scale * X[r, j] + M[r mod mask_rows, j]      (M optional)
+ *     z[r, j] = -inf   when causal_q > 0 and j > (r mod causal_q) + cols - causal_q
+ *     Y[r, :] = softmax(z[r, :])  as in softmax_fwd.
+ *   scale     : fp32 factor applied to X (1 for none)
+ *   mask      : NULL, or an additive mask with X's dtype, mask_rows x cols,
+ *               row pitch cols, aligned to the element size; row r of X uses
+ *               row (r mod mask_rows), e.g. a [S, S] mask broadcast over the
+ *               batch and heads of [B, H, S, S] scores (rows = B*H*S)
+ *   mask_rows : rows of the mask (>= 1 when mask != NULL; ignored otherwise)
+ *   causal_q  : 0 for none, else the query length q: row r is query
+ *               (r mod q) and sees keys j <= (r mod q) + cols - q (the last
+ *               query sees every key)
+ *   kernel_id : RWS_KERNEL_AUTO, or RWS_KERNEL_WAVE_ROW / BLOCK_ONEPASS /
+ *               TWO_PASS (no split-k form; RWS_ERR_UNSUPPORTED_SHAPE)
+ * A row whose every entry ends up -inf becomes NaN (0/0), as the definition
+ * gives.  Other arguments, layout, streams and errors as softmax_fwd.
+ */
+int softmax_fwd_masked(const void *in, void *out, int64_t rows, int64_t cols, int dtype,
+                       float scale, const void *mask, int64_t mask_rows, int64_t causal_q,
+                       void *stream, int kernel_id);
+
+/*
  * softmax_select_kernel -- the family softmax_fwd would run for this shape
  * with pointers `in` and `out` (their alignment matters), on the current
  * device.  Returns a RWS_KERNEL_* id (> 0), or a negative status on invalid

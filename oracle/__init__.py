@@ -18,6 +18,8 @@ Thin ctypes wrappers over ``softmax_oracle.c`` (plain C, IEEE double, libm
 * :func:`splitk_softmax` -- per-chunk partial (m, d) merged with the (m, d)
   rule, CUDA safe-online-softmax page, section 3.2.
 * :func:`md_merge`      -- the (m, d) merge rule itself.
+* :func:`masked_softmax` -- softmax of scale*x + mask (+ causal limit), the
+  attention-score fusion the DCU case-study page proposes (section 9).
 
 Inputs are float64 arrays holding the values as stored in the tensor's dtype.
 """
@@ -55,6 +57,8 @@ def _load():
     lib.oracle_splitk_softmax.restype = None
     lib.oracle_md_merge.argtypes = [ctypes.c_double] * 4 + [_D, _D]
     lib.oracle_md_merge.restype = None
+    lib.oracle_masked_softmax.argtypes = [_D, _D, _I64, _I64, ctypes.c_double, _D, _I64, _I64]
+    lib.oracle_masked_softmax.restype = None
     lib.oracle_safe_softmax_threads.argtypes = [_D, _D, _I64, _I64, ctypes.c_int]
     lib.oracle_safe_softmax_threads.restype = ctypes.c_int
     _lib = lib
@@ -135,3 +139,20 @@ def md_merge(a, b):
     _load().oracle_md_merge(float(a[0]), float(a[1]), float(b[0]), float(b[1]),
                             ctypes.byref(m), ctypes.byref(d))
     return m.value, d.value
+
+
+def masked_softmax(x, scale: float = 1.0, mask=None, causal_q: int = 0) -> np.ndarray:
+    """Softmax of scale*x + mask[r % mask_rows] with an optional causal limit:
+    column j of row r is excluded when j > (r % causal_q) + cols - causal_q."""
+    a = _as_2d(x)
+    y = np.empty_like(a)
+    if mask is None:
+        mp, mrows = None, 1
+    else:
+        m = _as_2d(mask)
+        if m.shape[1] != a.shape[1]:
+            raise ValueError("mask must have the same number of columns")
+        mp, mrows = _p(m), m.shape[0]
+    _load().oracle_masked_softmax(_p(a), _p(y), a.shape[0], a.shape[1], float(scale), mp,
+                                  mrows, int(causal_q))
+    return y

@@ -195,6 +195,37 @@ void oracle_splitk_softmax(const double *x, double *y, int64_t rows, int64_t col
 }
 
 /* ---------------------------------------------------------------------------
+ * Scaled, masked softmax of attention scores (DCU case-study page, section
+ * 9: a mask parameter in the softmax kernel; Pangu-Weather profile page,
+ * section 6: bias + mask + softmax).  For row r and column j:
+ *     z_rj = scale * x_rj + mask[(r mod mask_rows), j]     (mask may be NULL)
+ *     z_rj = -inf  if causal_q > 0 and j > (r mod causal_q) + cols - causal_q
+ * then the definition above on z.  Reading: the causal limit aligns the last
+ * query with the last key (keys may outnumber queries).
+ * ------------------------------------------------------------------------- */
+void oracle_masked_softmax(const double *x, double *y, int64_t rows, int64_t cols, double scale,
+                           const double *mask, int64_t mask_rows, int64_t causal_q)
+{
+    double *z = (double *)malloc(sizeof(double) * (size_t)(cols > 0 ? cols : 1));
+    if (!z)
+        return;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *xr = x + r * cols;
+        const double *mr = mask ? mask + (r % mask_rows) * cols : NULL;
+        for (int64_t j = 0; j < cols; ++j) {
+            double v = scale * xr[j];
+            if (mr)
+                v += mr[j];
+            if (causal_q > 0 && j > (r % causal_q) + cols - causal_q)
+                v = -INFINITY;
+            z[j] = v;
+        }
+        safe_softmax_row(z, y + r * cols, cols);
+    }
+    free(z);
+}
+
+/* ---------------------------------------------------------------------------
  * The definition run over row ranges on several host threads: rows are
  * independent, so each thread applies safe_softmax_row to its own
  * contiguous range.  Used to time the oracle on the host's cores.

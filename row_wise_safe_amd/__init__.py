@@ -23,9 +23,10 @@ __all__ = [
     "RWS_ERR_HIP", "RWS_ERR_UNSUPPORTED_SHAPE",
     "KERNELS", "KERNEL_IDS",
     "library_path", "load_library",
-    "softmax_fwd", "softmax_fwd_kernel", "softmax_select_kernel", "softmax_describe_launch",
+    "softmax_fwd", "softmax_fwd_kernel", "softmax_fwd_masked", "softmax_select_kernel",
+    "softmax_describe_launch",
     "softmax_kernel_name", "softmax_status_string", "softmax_last_error", "softmax_copy_bytes",
-    "softmax", "copy_bytes", "dtype_code", "SoftmaxError",
+    "softmax", "softmax_masked", "copy_bytes", "dtype_code", "SoftmaxError",
 ]
 
 RWS_F32, RWS_F16, RWS_BF16 = 0, 1, 2
@@ -73,6 +74,9 @@ def load_library():
     lib.softmax_fwd.restype = cint
     lib.softmax_fwd_kernel.argtypes = [vp, vp, i64, i64, cint, vp, cint]
     lib.softmax_fwd_kernel.restype = cint
+    lib.softmax_fwd_masked.argtypes = [vp, vp, i64, i64, cint, ctypes.c_float, vp, i64, i64, vp,
+                                       cint]
+    lib.softmax_fwd_masked.restype = cint
     lib.softmax_select_kernel.argtypes = [i64, i64, cint, vp, vp]
     lib.softmax_select_kernel.restype = cint
     lib.softmax_describe_launch.argtypes = [i64, i64, cint, vp, vp, cint, ctypes.c_char_p, i64]
@@ -98,6 +102,14 @@ def softmax_fwd(in_ptr: int, out_ptr: int, rows: int, cols: int, dtype: int, str
 def softmax_fwd_kernel(in_ptr: int, out_ptr: int, rows: int, cols: int, dtype: int, stream: int,
                        kernel_id: int) -> int:
     return load_library().softmax_fwd_kernel(in_ptr, out_ptr, rows, cols, dtype, stream,
+                                             kernel_id)
+
+
+def softmax_fwd_masked(in_ptr: int, out_ptr: int, rows: int, cols: int, dtype: int, scale: float,
+                       mask_ptr: int, mask_rows: int, causal_q: int, stream: int,
+                       kernel_id: int = 0) -> int:
+    return load_library().softmax_fwd_masked(in_ptr, out_ptr, rows, cols, dtype, scale,
+                                             mask_ptr or None, mask_rows, causal_q, stream,
                                              kernel_id)
 
 
@@ -170,6 +182,39 @@ def softmax(x: torch.Tensor, out: torch.Tensor | None = None, kernel: str = "aut
     cols = x.shape[-1] if x.dim() > 0 else 1
     rows = x.numel() // cols if cols > 0 else 0
     st = load_library().softmax_fwd_kernel(x.data_ptr(), out.data_ptr(), rows, cols, code,
+                                           _stream_handle(x.device, stream), KERNEL_IDS[kernel])
+    if st != RWS_OK:
+        raise SoftmaxError(st, softmax_last_error())
+    return out
+
+
+def softmax_masked(x: torch.Tensor, scale: float = 1.0, mask: torch.Tensor | None = None,
+                   causal_q: int = 0, out: torch.Tensor | None = None, kernel: str = "auto",
+                   stream=None) -> torch.Tensor:
+    """softmax(scale * x + mask (+ causal limit)) along the last dimension.
+
+    ``mask`` (optional) has x's dtype and last dimension; its rows are
+    broadcast cyclically over x's rows (row r uses mask row r % mask_rows), so
+    a [S, S] mask serves [B, H, S, S] scores.  ``causal_q`` > 0 excludes keys
+    j > (r % causal_q) + cols - causal_q.
+    """
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous GPU tensor")
+    code = dtype_code(x.dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of x's shape and dtype")
+    cols = x.shape[-1] if x.dim() > 0 else 1
+    rows = x.numel() // cols if cols > 0 else 0
+    mask_ptr, mask_rows = None, 0
+    if mask is not None:
+        if mask.dtype != x.dtype or not mask.is_contiguous() or mask.shape[-1] != cols or \
+                mask.device != x.device:
+            raise ValueError("mask must be contiguous, on x's device, with x's dtype and columns")
+        mask_ptr, mask_rows = mask.data_ptr(), mask.numel() // cols
+    st = load_library().softmax_fwd_masked(x.data_ptr(), out.data_ptr(), rows, cols, code,
+                                           float(scale), mask_ptr, mask_rows, int(causal_q),
                                            _stream_handle(x.device, stream), KERNEL_IDS[kernel])
     if st != RWS_OK:
         raise SoftmaxError(st, softmax_last_error())

@@ -25,6 +25,7 @@ SOURCES = [
     "rws_two_pass.hip",
     "rws_splitk.hip",
     "rws_splitk_fused.hip",
+    "rws_masked.hip",
 ]
 
 COMMON_FLAGS = [

@@ -137,9 +137,10 @@ int pick_wave_row(const Geometry& g) {
     return best;
 }
 
-int pick_onepass(int64_t w) {
+int pick_onepass(int64_t w, bool regs_only = false) {
     int best = -1;
     for (int i = 0; i < rws::kNumOnepass; ++i) {
+        if (regs_only && rws::kOnepass[i].kl != 0) continue;
         if (onepass_capacity(rws::kOnepass[i]) < w) continue;
         if (best < 0 || onepass_capacity(rws::kOnepass[i]) < onepass_capacity(rws::kOnepass[best]))
             best = i;
@@ -229,7 +230,7 @@ int pick_splitk_fused(int64_t rows, int64_t wmax, int dtype, bool aligned, int c
 }
 
 int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
-                int kernel_id, Plan* p) {
+                int kernel_id, Plan* p, bool masked = false) {
     const Geometry g = geometry(cols, dtype, in, out);
     p->same_phase = g.same_phase;
     const int64_t wline = window_granules(g, 128);  // block-level kernels
@@ -255,6 +256,16 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
             family = RWS_KERNEL_TWO_PASS;
         }
     }
+    if (masked && kernel_id == RWS_KERNEL_AUTO) {
+        // the masked forms exist for wave_row, register-only block_onepass
+        // and two_pass; long rows with few rows go to two_pass
+        if (family == RWS_KERNEL_SPLITK || family == RWS_KERNEL_SPLITK_FUSED)
+            family = RWS_KERNEL_TWO_PASS;
+        if (family == RWS_KERNEL_BLOCK_ONEPASS && pick_onepass(wline, true) < 0)
+            family = RWS_KERNEL_TWO_PASS;
+    }
+    if (masked && (family == RWS_KERNEL_SPLITK || family == RWS_KERNEL_SPLITK_FUSED))
+        return fail(RWS_ERR_UNSUPPORTED_SHAPE, "the masked form has no split-k kernel");
     p->family = family;
     p->aligned = g.a128;
     p->window = wline;
@@ -275,7 +286,7 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
             break;
         }
         case RWS_KERNEL_BLOCK_ONEPASS: {
-            p->variant = pick_onepass(wline);
+            p->variant = pick_onepass(wline, masked);
             if (p->variant < 0)
                 return fail(RWS_ERR_UNSUPPORTED_SHAPE,
                             "block_onepass holds at most 16384 granules (16 bytes) per row window");
@@ -430,17 +441,12 @@ int check_args(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
     return RWS_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int softmax_fwd_kernel(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
-                       void* stream, int kernel_id) {
-    g_last_error.clear();
-    int st = check_args(in, out, rows, cols, dtype, kernel_id);
-    if (st != RWS_OK || rows == 0 || cols == 0) return st;
+// One call: plan, get the workspace if needed, launch in row batches.
+// `mask` selects the masked/scaled form (nullptr: plain softmax).
+int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream,
+        int kernel_id, const rws::MaskArgs* mask) {
     Plan p;
-    st = plan_launch(rows, cols, dtype, in, out, kernel_id, &p);
+    int st = plan_launch(rows, cols, dtype, in, out, kernel_id, &p, mask != nullptr);
     if (st != RWS_OK) return st;
 
     void* ws = nullptr;
@@ -468,19 +474,66 @@ int softmax_fwd_kernel(const void* in, void* out, int64_t rows, int64_t cols, in
         L.remap = p.remap;
         L.stream = s;
         hipError_t e = hipSuccess;
-        switch (p.family) {
-            case RWS_KERNEL_WAVE_ROW: e = rws::launch_wave_row(L, p.variant); break;
-            case RWS_KERNEL_BLOCK_ONEPASS: e = rws::launch_block_onepass(L, p.variant); break;
-            case RWS_KERNEL_TWO_PASS: e = rws::launch_two_pass(L, p.variant); break;
-            case RWS_KERNEL_SPLITK: e = rws::launch_splitk(L, p.variant, p.P, (float2*)ws); break;
-            case RWS_KERNEL_SPLITK_FUSED:
-                e = rws::launch_splitk_fused(L, p.variant, p.P, (float2*)ws, sync, epoch);
-                break;
+        if (mask) {
+            rws::MaskArgs M = *mask;
+            M.row_base = r0;
+            switch (p.family) {
+                case RWS_KERNEL_WAVE_ROW: e = rws::launch_wave_row_masked(L, p.variant, M); break;
+                case RWS_KERNEL_BLOCK_ONEPASS:
+                    e = rws::launch_block_onepass_masked(L, p.variant, M);
+                    break;
+                case RWS_KERNEL_TWO_PASS: e = rws::launch_two_pass_masked(L, p.variant, M); break;
+                default: e = hipErrorInvalidValue;
+            }
+        } else {
+            switch (p.family) {
+                case RWS_KERNEL_WAVE_ROW: e = rws::launch_wave_row(L, p.variant); break;
+                case RWS_KERNEL_BLOCK_ONEPASS: e = rws::launch_block_onepass(L, p.variant); break;
+                case RWS_KERNEL_TWO_PASS: e = rws::launch_two_pass(L, p.variant); break;
+                case RWS_KERNEL_SPLITK:
+                    e = rws::launch_splitk(L, p.variant, p.P, (float2*)ws);
+                    break;
+                case RWS_KERNEL_SPLITK_FUSED:
+                    e = rws::launch_splitk_fused(L, p.variant, p.P, (float2*)ws, sync, epoch);
+                    break;
+            }
         }
         if (e != hipSuccess)
             return fail(RWS_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     }
     return RWS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int softmax_fwd_kernel(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
+                       void* stream, int kernel_id) {
+    g_last_error.clear();
+    const int st = check_args(in, out, rows, cols, dtype, kernel_id);
+    if (st != RWS_OK || rows == 0 || cols == 0) return st;
+    return run(in, out, rows, cols, dtype, stream, kernel_id, nullptr);
+}
+
+int softmax_fwd_masked(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
+                       float scale, const void* mask, int64_t mask_rows, int64_t causal_q,
+                       void* stream, int kernel_id) {
+    g_last_error.clear();
+    const int st = check_args(in, out, rows, cols, dtype, kernel_id);
+    if (st != RWS_OK) return st;
+    if (causal_q < 0) return fail(RWS_ERR_INVALID_ARG, "causal_q must be >= 0");
+    if (mask && mask_rows < 1) return fail(RWS_ERR_INVALID_ARG, "mask_rows must be >= 1");
+    if (mask && (uintptr_t)mask % elem_size(dtype))
+        return fail(RWS_ERR_MISALIGNED, "mask not aligned to the element size");
+    if (rows == 0 || cols == 0) return RWS_OK;
+    rws::MaskArgs M;
+    M.scale = scale;
+    M.mask = mask;
+    M.mask_rows = mask ? mask_rows : 1;
+    M.causal_q = causal_q;
+    M.row_base = 0;
+    return run(in, out, rows, cols, dtype, stream, kernel_id, &M);
 }
 
 int softmax_fwd(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream) {

@@ -2,19 +2,9 @@
 // family (one workgroup per row, row cached in registers, then LDS).
 #include "rws_kernels.hpp"
 #include "rws_launch.hpp"
+#include "rws_variants.hpp"
 
 namespace rws {
-
-// (threads, register granules per thread, LDS granules per thread)
-#define RWS_ONEPASS_VARIANTS(X) \
-    X(256, 2, 0)                \
-    X(192, 3, 0)                \
-    X(256, 3, 0)                \
-    X(256, 4, 0)                \
-    X(512, 4, 0)                \
-    X(1024, 4, 0)               \
-    X(1024, 8, 0)               \
-    X(1024, 8, 8)
 
 #define RWS_ROW(b, kr, kl) {b, kr, kl},
 const OnepassVariant kOnepass[] = {RWS_ONEPASS_VARIANTS(RWS_ROW)};
@@ -24,7 +14,7 @@ const int kNumOnepass = sizeof(kOnepass) / sizeof(kOnepass[0]);
 template <int DT, bool AL, int B, int KR, int KL>
 static hipError_t go(const Launch& L) {
     hipLaunchKernelGGL((k_block_onepass<DT, AL, B, KR, KL>), dim3((unsigned)L.rows), dim3(B), 0,
-                       L.stream, L.in, L.out, L.rows, L.cols, (int)L.same_phase, (int)L.remap);
+                       L.stream, L.in, L.out, L.rows, L.cols, (int)L.same_phase, (int)L.remap, NoPre());
     return hipGetLastError();
 }
 

@@ -278,19 +278,24 @@ struct RowWin {
 // ---------------------------------------------------------------------------
 // exp(x - m) for one row.  With c = round(m * log2 e), the FMA
 // x*log2e - c is exact before its single rounding, so the error is relative
-// to |x - m| and the common offset (m*log2e - c) cancels in the
-// normalisation.  Rows whose max makes m*log2e overflow (|m| > 2.3e38, only
-// reachable in fp32/bf16), or m = +inf, take (x - m)*log2e instead.  m = -inf
-// (every entry -inf) keeps c = 0 so that the row becomes 0/0 = NaN like the
-// definition, and -inf entries under a finite max give exactly 0.
+// to |x - m| and the common offset delta = m*log2e - c cancels in the
+// normalisation.  delta is at most half an ulp of c, so the form is used only
+// while |c| < 2^22 (|m| < 2.9e6, delta <= 1/8, far from over/underflowing
+// exp2).  Rows with a larger |m| -- possible in fp32 and bf16, and for the
+// running max of a thread that has only seen masked entries -- or with
+// m = +inf take (x - m)*log2e instead.  m = -inf (every entry -inf) keeps
+// c = 0 so that the row becomes 0/0 = NaN like the definition, and -inf
+// entries under a finite max give exactly 0.
 // ---------------------------------------------------------------------------
+constexpr float kFmaExpLimit = 4194304.0f;  // 2^22
+
 struct RowExp {
     float m;
     float negc;
     bool big;
     __device__ inline explicit RowExp(float m_) : m(m_) {
         float c = m_ * kLog2e;
-        big = !(__builtin_fabsf(c) <= kFltMax) && (m_ != kNegInf);
+        big = !(__builtin_fabsf(c) < kFmaExpLimit) && (m_ != kNegInf);
         negc = (m_ == kNegInf) ? 0.0f : -c;
     }
     template <int N>

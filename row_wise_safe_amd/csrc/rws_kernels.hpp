@@ -21,6 +21,7 @@
 #pragma once
 
 #include "rws_device.hpp"
+#include "rws_pre.hpp"
 
 namespace rws {
 
@@ -36,10 +37,11 @@ __device__ inline const char* tensor_end(const void* in, int64_t rows, int cols)
 // Rows past the end are clamped to the last row for loading (in bounds) and
 // are not stored.
 // ===========================================================================
-template <int DT, bool ALIGNED, int G, int K, int U>
+template <int DT, bool ALIGNED, int G, int K, int U, class Pre = NoPre>
 __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
                                                   void* __restrict__ out, int64_t rows,
-                                                  int cols, int same_phase, int remap) {
+                                                  int cols, int same_phase, int remap,
+                                                  Pre pre = Pre()) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int RPS = 64 / G;  // rows per set
     constexpr int N = K * VEC;   // elements per lane per row
@@ -58,22 +60,33 @@ __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
     // lane groups of at least one cache line get line-aligned windows
     constexpr int WA = G * 16 >= kLineBytes ? kLineBytes : 16;
     RowWin<DT, ALIGNED, WA> w[U];
+    int64_t lrow[U];  // row each set loads (clamped to the last row)
     u32x4 raw[U][K];
+    u32x4 praw[Pre::kActive ? U : 1][Pre::kActive ? K : 1];  // prologue operands
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         int64_t row = row0 + u * RPS + sub;
         row = row < rows ? row : rows - 1;
+        lrow[u] = row;
         w[u] = RowWin<DT, ALIGNED, WA>(in, out, row, cols);
 #pragma unroll
-        for (int i = 0; i < K; ++i) raw[u][i] = w[u].fetch(gl + G * i, tbeg, tend);
+        for (int i = 0; i < K; ++i) {
+            raw[u][i] = w[u].fetch(gl + G * i, tbeg, tend);
+            if (Pre::kActive) praw[Pre::kActive ? u : 0][Pre::kActive ? i : 0] =
+                pre.fetch(row, w[u], gl + G * i);
+        }
     }
 
     float v[U][N];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int i = 0; i < K; ++i)
+        for (int i = 0; i < K; ++i) {
             w[u].widen(gl + G * i, raw[u][i], &v[u][i * VEC], tbeg, tend, full);
+            if (Pre::kActive)
+                pre.apply(lrow[u], w[u], gl + G * i, &v[u][i * VEC],
+                          praw[Pre::kActive ? u : 0][Pre::kActive ? i : 0]);
+        }
         float mx = v[u][0];
 #pragma unroll
         for (int j = 1; j < N; ++j) mx = vmax(mx, v[u][j]);
@@ -109,10 +122,12 @@ __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
 // LDS slots, so they need no barrier; consecutive threads use consecutive
 // 16-byte slots).  Every byte of the row crosses HBM once each way.
 // ===========================================================================
-template <int DT, bool ALIGNED, int BLOCK, int KR, int KL>
+template <int DT, bool ALIGNED, int BLOCK, int KR, int KL, class Pre = NoPre>
 __global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict__ in,
                                                          void* __restrict__ out, int64_t rows,
-                                                         int cols, int same_phase, int remap) {
+                                                         int cols, int same_phase, int remap,
+                                                         Pre pre = Pre()) {
+    static_assert(!Pre::kActive || KL == 0, "prologues apply to register-held rows only");
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     constexpr int N = KR * VEC;
@@ -126,8 +141,12 @@ __global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict_
     const RowWin<DT, ALIGNED> w(in, out, row, cols);
 
     u32x4 raw[KR];
+    u32x4 praw[Pre::kActive ? KR : 1];  // prologue operands
 #pragma unroll
-    for (int i = 0; i < KR; ++i) raw[i] = w.fetch(t + BLOCK * i, tbeg, tend);
+    for (int i = 0; i < KR; ++i) {
+        raw[i] = w.fetch(t + BLOCK * i, tbeg, tend);
+        if (Pre::kActive) praw[Pre::kActive ? i : 0] = pre.fetch(row, w, t + BLOCK * i);
+    }
     u32x4 rawl[KL > 0 ? KL : 1];
 #pragma unroll
     for (int j = 0; j < KL; ++j) {
@@ -137,7 +156,10 @@ __global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict_
 
     float v[N];
 #pragma unroll
-    for (int i = 0; i < KR; ++i) w.widen(t + BLOCK * i, raw[i], &v[i * VEC], tbeg, tend);
+    for (int i = 0; i < KR; ++i) {
+        w.widen(t + BLOCK * i, raw[i], &v[i * VEC], tbeg, tend);
+        if (Pre::kActive) pre.apply(row, w, t + BLOCK * i, &v[i * VEC], praw[Pre::kActive ? i : 0]);
+    }
     float mx = kNegInf;
 #pragma unroll
     for (int j = 0; j < N; ++j) mx = vmax(mx, v[j]);
@@ -237,10 +259,11 @@ __device__ inline void block_merge(float m, float d, float& M, float& D, float* 
 // the threads' pairs; pass 2 re-reads the row (from L2 / last-level cache when
 // the row was just read) and writes e^(x - M) / D.
 // ===========================================================================
-template <int DT, bool ALIGNED, int BLOCK, int U>
+template <int DT, bool ALIGNED, int BLOCK, int U, class Pre = NoPre>
 __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
                                                     void* __restrict__ out, int64_t rows,
-                                                    int cols, int same_phase, int remap) {
+                                                    int cols, int same_phase, int remap,
+                                                    Pre pre = Pre()) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     __shared__ float red_max[W];
@@ -254,8 +277,12 @@ __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
     float m = kNegInf, d = 0.0f;
     for (int k0 = t; k0 < w.ngran; k0 += BLOCK * U) {
         u32x4 raw[U];
+        u32x4 praw[Pre::kActive ? U : 1];
 #pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = w.fetch(k0 + BLOCK * u, tbeg, tend);
+        for (int u = 0; u < U; ++u) {
+            raw[u] = w.fetch(k0 + BLOCK * u, tbeg, tend);
+            if (Pre::kActive) praw[Pre::kActive ? u : 0] = pre.fetch(row, w, k0 + BLOCK * u);
+        }
         float v[U * VEC];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -265,6 +292,7 @@ __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) v[u * VEC + e] = kNegInf;
             }
+            if (Pre::kActive) pre.apply(row, w, k, &v[u * VEC], praw[Pre::kActive ? u : 0]);
         }
         online_update(m, d, v);
     }
@@ -275,14 +303,19 @@ __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
 
     for (int k0 = t; k0 < w.ngran; k0 += BLOCK * U) {
         u32x4 raw[U];
+        u32x4 praw[Pre::kActive ? U : 1];
 #pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = w.fetch(k0 + BLOCK * u, tbeg, tend);
+        for (int u = 0; u < U; ++u) {
+            raw[u] = w.fetch(k0 + BLOCK * u, tbeg, tend);
+            if (Pre::kActive) praw[Pre::kActive ? u : 0] = pre.fetch(row, w, k0 + BLOCK * u);
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k = k0 + BLOCK * u;
             if (k < w.ngran) {
                 float f[VEC];
                 w.widen(k, raw[u], f, tbeg, tend);
+                if (Pre::kActive) pre.apply(row, w, k, f, praw[Pre::kActive ? u : 0]);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) f[e] = er.one(f[e]) * r;
                 w.store(k, f, same_phase != 0);

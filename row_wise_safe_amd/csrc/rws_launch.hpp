@@ -20,6 +20,17 @@ struct Launch {
     hipStream_t stream;
 };
 
+// Attention-score prologue of the masked entry point: z = scale*x + mask
+// (+ causal limit), see rws_pre.hpp.  row_base is the global index of the
+// launch's first row (mask rows and causal queries follow global rows).
+struct MaskArgs {
+    float scale;
+    const void* mask;
+    int64_t mask_rows;
+    int64_t causal_q;
+    int64_t row_base;
+};
+
 struct WaveRowVariant { int G, K, U; };          // lanes per row, granules per lane, row sets
 struct OnepassVariant { int block, kr, kl; };    // threads, register granules, LDS granules
 struct TwoPassVariant { int block, u; };         // threads, granules per batch
@@ -56,6 +67,11 @@ hipError_t launch_splitk_fused(const Launch& L, int variant, int P, float2* ws, 
                                unsigned epoch);
 // Workgroups of this variant that can be resident at once on `cus` CUs.
 hipError_t splitk_fused_capacity(int variant, int dtype, bool aligned, int cus, int64_t* blocks);
+// The masked forms (same variant tables; block_onepass only for variants
+// without LDS parking).
+hipError_t launch_wave_row_masked(const Launch& L, int variant, const MaskArgs& M);
+hipError_t launch_block_onepass_masked(const Launch& L, int variant, const MaskArgs& M);
+hipError_t launch_two_pass_masked(const Launch& L, int variant, const MaskArgs& M);
 // n16 granules of 16 bytes.
 hipError_t launch_copy16(const void* in, void* out, int64_t n16, hipStream_t stream);
 

@@ -2,15 +2,9 @@
 // (one workgroup per row, any row length, the row is read twice).
 #include "rws_kernels.hpp"
 #include "rws_launch.hpp"
+#include "rws_variants.hpp"
 
 namespace rws {
-
-// (threads, granules per thread per batch)
-#define RWS_TWO_PASS_VARIANTS(X) \
-    X(256, 4)                    \
-    X(512, 4)                    \
-    X(1024, 2)                   \
-    X(1024, 4)
 
 #define RWS_ROW(b, u) {b, u},
 const TwoPassVariant kTwoPass[] = {RWS_TWO_PASS_VARIANTS(RWS_ROW)};
@@ -20,7 +14,7 @@ const int kNumTwoPass = sizeof(kTwoPass) / sizeof(kTwoPass[0]);
 template <int DT, bool AL, int B, int U>
 static hipError_t go(const Launch& L) {
     hipLaunchKernelGGL((k_two_pass<DT, AL, B, U>), dim3((unsigned)L.rows), dim3(B), 0, L.stream,
-                       L.in, L.out, L.rows, L.cols, (int)L.same_phase, (int)L.remap);
+                       L.in, L.out, L.rows, L.cols, (int)L.same_phase, (int)L.remap, NoPre());
     return hipGetLastError();
 }
 

@@ -1,24 +1,9 @@
 // rws_wave_row.hip -- instantiations and launcher of the wave_row family.
 #include "rws_kernels.hpp"
 #include "rws_launch.hpp"
+#include "rws_variants.hpp"
 
 namespace rws {
-
-// (G lanes per row, K granules per lane, U row sets per wave)
-#define RWS_WAVE_ROW_VARIANTS(X) \
-    X(4, 1, 1)                   \
-    X(4, 1, 2)                   \
-    X(8, 1, 1)                   \
-    X(8, 1, 2)                   \
-    X(16, 1, 1)                  \
-    X(16, 1, 2)                  \
-    X(32, 1, 1)                  \
-    X(32, 1, 2)                  \
-    X(64, 1, 1)                  \
-    X(64, 1, 2)                  \
-    X(64, 2, 1)                  \
-    X(64, 4, 1)                  \
-    X(64, 8, 1)
 
 #define RWS_ROW(g, k, u) {g, k, u},
 const WaveRowVariant kWaveRow[] = {RWS_WAVE_ROW_VARIANTS(RWS_ROW)};
@@ -30,7 +15,7 @@ static hipError_t go(const Launch& L) {
     const WaveRowVariant v = {G, K, U};
     const int64_t grid = wave_row_grid(v, L.rows);
     hipLaunchKernelGGL((k_wave_row<DT, AL, G, K, U>), dim3((unsigned)grid), dim3(256), 0,
-                       L.stream, L.in, L.out, L.rows, L.cols, (int)L.same_phase, (int)L.remap);
+                       L.stream, L.in, L.out, L.rows, L.cols, (int)L.same_phase, (int)L.remap, NoPre());
     return hipGetLastError();
 }
 

@@ -123,3 +123,13 @@ def test_describe_mentions_alignment(lib):
     assert "unaligned" in rws.softmax_describe_launch(8, 100, rws.RWS_F16, 258, 258)
     assert "split-phase" in rws.softmax_describe_launch(8, 100, rws.RWS_F16, 258, 256)
     assert ",aligned" in rws.softmax_describe_launch(8, 128, rws.RWS_F16, 256, 512)
+
+
+def test_masked_argument_checks(lib):
+    f16 = rws.RWS_F16
+    assert rws.softmax_fwd_masked(256, 256, 2, 8, f16, 1.0, 0, 0, -1, 0, 0) == rws.RWS_ERR_INVALID_ARG
+    assert rws.softmax_fwd_masked(256, 256, 2, 8, f16, 1.0, 257, 2, 0, 0, 0) == rws.RWS_ERR_MISALIGNED
+    assert rws.softmax_fwd_masked(256, 256, 2, 8, f16, 1.0, 512, 0, 0, 0, 0) == rws.RWS_ERR_INVALID_ARG
+    assert rws.softmax_fwd_masked(0, 0, 0, 8, f16, 1.0, 0, 0, 0, 0, 0) == rws.RWS_OK
+    assert rws.softmax_fwd_masked(256, 256, 2, 8, 9, 1.0, 0, 0, 0, 0, 0) == \
+        rws.RWS_ERR_UNSUPPORTED_DTYPE

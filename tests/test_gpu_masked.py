@@ -1,0 +1,121 @@
+"""GPU parity of the masked/scaled softmax (softmax_fwd_masked) against the
+oracle's masked_softmax: attention-score shapes [B, H, S, S] with a [S, S]
+mask broadcast over B and H, causal limits (keys may outnumber queries),
+scales, -inf mask entries, a mask whose rows have another 16-byte phase than
+the input's, every kernel family that has a masked form."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import row_wise_safe_amd as rws
+from gpu_util import TORCH_DTYPE, have_gpu, to_device
+from tolerance import check
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not have_gpu(), reason="needs an MI355X GPU")]
+
+DTYPES = ["f32", "f16", "bf16"]
+KERNELS = ["auto", "wave_row", "block_onepass", "two_pass"]
+
+
+def _supports(kernel, cols, dtype):
+    es = 4 if dtype == "f32" else 2
+    w = (cols * es + 143) // 16
+    return kernel != "wave_row" or w <= 512
+
+
+def _masked(x, scale, mask, causal_q, kernel):
+    out = torch.empty_like(x)
+    rws.softmax_masked(x, scale=scale, mask=mask, causal_q=causal_q, out=out, kernel=kernel)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("S", [64, 100, 1000])
+def test_attention_scores_mask_and_causal(dtype, S):
+    B, H = 2, 3
+    g = np.random.Generator(np.random.PCG64(S))
+    x64 = g.normal(0.0, 4.0, (B * H * S, S))
+    m64 = g.normal(0.0, 2.0, (S, S))
+    m64[:, 3::7] = -math.inf if dtype != "bf16" else -1.0e30  # key 0 stays visible
+    x, xs = to_device(x64, dtype)
+    m, ms = to_device(m64, dtype)
+    scale = 1.0 / math.sqrt(64.0)
+    for causal in (0, S):
+        ref = oracle.masked_softmax(xs, scale, ms, causal)
+        for kernel in KERNELS:
+            if not _supports(kernel, S, dtype):
+                continue
+            y = _masked(x, scale, m, causal, kernel)
+            check(y, ref, dtype, f"{kernel} S={S} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_causal_more_keys_than_queries(dtype):
+    q, cols = 17, 33
+    x, xs = to_device(np.random.Generator(np.random.PCG64(1)).normal(0, 3, (4 * q, cols)), dtype)
+    ref = oracle.masked_softmax(xs, 0.7, None, q)
+    for kernel in KERNELS:
+        y = _masked(x, 0.7, None, q, kernel)
+        check(y, ref, dtype, kernel)
+        r = np.arange(4 * q)[:, None] % q
+        j = np.arange(cols)[None, :]
+        assert np.all(y[j > r + cols - q] == 0.0)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("scale", [1.0, -1.5, 0.0, 0.125])
+def test_scale_only(dtype, scale):
+    x, xs = to_device(np.random.Generator(np.random.PCG64(2)).normal(0, 5, (37, 777)), dtype)
+    ref = oracle.masked_softmax(xs, scale, None, 0)
+    for kernel in KERNELS:
+        check(_masked(x, scale, None, 0, kernel), ref, dtype, f"{kernel} scale={scale}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_identity_prologue_equals_plain(kernel):
+    x, _ = to_device(np.random.Generator(np.random.PCG64(3)).normal(0, 4, (65, 512)), "f16")
+    a = _masked(x, 1.0, None, 0, kernel)
+    b = rws.softmax(x, kernel=kernel)
+    torch.cuda.synchronize()
+    assert np.array_equal(a, b.double().cpu().numpy())
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_mask_with_other_phase(dtype):
+    rows, cols = 24, 1001
+    g = np.random.Generator(np.random.PCG64(4))
+    x, xs = to_device(g.normal(0, 2, (rows, cols)), dtype)
+    m, ms = to_device(g.normal(0, 2, (5, cols)), dtype, offset=1)  # mask rows misaligned
+    ref = oracle.masked_softmax(xs, 2.0, ms, 0)
+    for kernel in KERNELS:
+        check(_masked(x, 2.0, m, 0, kernel), ref, dtype, kernel)
+
+
+def test_fully_masked_rows_are_nan():
+    x, xs = to_device(np.zeros((6, 4)), "f32")
+    y = _masked(x, 1.0, None, 6, "auto")  # q > cols: queries 0 and 1 see no key
+    ref = oracle.masked_softmax(xs, 1.0, None, 6)
+    assert np.all(np.isnan(y[[0, 1]])) and np.all(np.isnan(ref[[0, 1]]))
+    check(y[2:], ref[2:], "f32", "partly masked rows")
+
+
+def test_masked_rejects_splitk_and_bad_args():
+    x = torch.zeros(4, 1 << 16, dtype=torch.float16, device="cuda")
+    with pytest.raises(rws.SoftmaxError) as e:
+        rws.softmax_masked(x, kernel="splitk")
+    assert e.value.status == rws.RWS_ERR_UNSUPPORTED_SHAPE
+    st = rws.softmax_fwd_masked(x.data_ptr(), x.data_ptr(), 4, 1 << 16, rws.RWS_F16, 1.0, 0, 0,
+                                -1, 0, 0)
+    assert st == rws.RWS_ERR_INVALID_ARG
+
+
+def test_long_rows_masked_use_two_pass():
+    x, xs = to_device(np.random.Generator(np.random.PCG64(5)).normal(0, 2, (3, 300001)), "f16")
+    assert rws.softmax_describe_launch(3, 300001, rws.RWS_F16, x.data_ptr(), x.data_ptr()) \
+        .startswith("splitk")
+    check(_masked(x, 0.5, None, 0, "auto"), oracle.masked_softmax(xs, 0.5, None, 0), "f16", "auto")

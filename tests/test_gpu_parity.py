@@ -212,6 +212,33 @@ def test_plus_minus_1e4(dtype):
         check(y, ref, dtype, kernel)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_huge_magnitudes(dtype):
+    # rows whose max is far beyond fp16 range: the exp argument must not
+    # carry an offset of half an ulp of max*log2(e)
+    cols = 2000
+    g = np.random.Generator(np.random.PCG64(21))
+    x64 = g.normal(0, 4, (8, cols))
+    x64[0] += 1.0e10
+    x64[1] -= 1.0e10
+    x64[2] = -1.0e30
+    x64[2, 1500:] = g.normal(0, 4, cols - 1500)
+    x64[3] += 3.0e6
+    x64[4] = g.normal(0, 1e5, cols)
+    x64[5] = 1.0e30 * g.normal(0, 1, cols)
+    x64[6] = -3.0e38 + 1e32 * g.uniform(0, 1, cols)
+    x, stored = to_device(x64, dtype)
+    ref = oracle.safe_softmax(stored)
+    for kernel in ["auto"] + KERNELS:
+        if kernel != "auto" and not supports(kernel, cols, dtype, False):
+            continue
+        try:
+            y = run(x, torch.empty_like(x), kernel)
+        except NotCoResident:
+            continue
+        check(y, ref, dtype, kernel)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_constant_rows_and_single_column(dtype):
     for cols in (1, 2, 1000, 5000):
