@@ -209,6 +209,9 @@ def main() -> int:
     ap.add_argument("--masked", action="store_true",
                     help="attention-score form: softmax(x/8 + mask[S,S] + causal) with S = cols "
                          "(softmax_fwd_masked)")
+    ap.add_argument("--backward", action="store_true",
+                    help="softmax backward dx = y*(dy - sum(dy*y)) on the workload's shape "
+                         "(softmax_bwd): 2 reads + 1 write per element")
     ap.add_argument("--skip-hot", action="store_true",
                     help="skip the single-buffer figure (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -260,6 +263,17 @@ def main() -> int:
     desc = rws.softmax_describe_launch(w.rows, w.cols, code, xs[0].data_ptr(), ys[0].data_ptr(),
                                        kid)
     family = desc.split("<")[0]
+    dys = None
+    if args.backward:
+        # y = the forward output of each input, dy ~ N(0, 1); dx goes to ys[i]
+        g = np.random.Generator(np.random.PCG64(w.seed + 200))
+        dy_host = torch.from_numpy(g.standard_normal((w.rows, w.cols))).to(tdt)
+        dys = [dy_host.to(dev) for _ in range(nbuf)]
+        for i in range(nbuf):
+            rws.softmax(xs[i], out=xs[i])  # xs now hold y
+        torch.cuda.synchronize()
+        nbytes = 3 * w.rows * w.cols * w.elem_bytes
+        desc = "backward " + desc.split("<")[0]
     mask = None
     if args.masked:
         if w.rows % w.cols:
@@ -273,7 +287,10 @@ def main() -> int:
     log(f"[bench] launch: {desc}; {nbuf} rotating buffer pairs")
 
     def step(i):
-        if mask is None:
+        if dys is not None:
+            st = rws.softmax_bwd_kernel(xs[i % nbuf].data_ptr(), dys[i % nbuf].data_ptr(),
+                                        ys[i % nbuf].data_ptr(), w.rows, w.cols, code, sh, kid)
+        elif mask is None:
             st = rws.softmax_fwd_kernel(xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), w.rows,
                                         w.cols, code, sh, kid)
         else:
@@ -342,11 +359,12 @@ def main() -> int:
     traffic = read_traffic(w.name, family)
     achieved = nbytes / (ms * 1e-3) / 1e9
     vs = round(gbps / PAGES_FP16_ATTN_GBPS, 3) if w.name == "fp16_attn_4x32x512x512" else None
-    if mask is not None:
+    if mask is not None or dys is not None:
         vs = None
     result = {
         "metric": f"effective HBM GB/s (read+write), {w.description}"
-                  + (", softmax(x/8 + mask + causal)" if mask is not None else ""),
+                  + (", softmax(x/8 + mask + causal)" if mask is not None else "")
+                  + (", backward dx = y*(dy - sum(dy*y))" if dys is not None else ""),
         "value": round(gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,

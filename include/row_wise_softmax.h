@@ -155,6 +155,30 @@ int softmax_fwd_masked(const void *in, void *out, int64_t rows, int64_t cols, in
                        void *stream, int kernel_id);
 
 /*
+ * softmax_bwd -- gradient through the row-wise softmax (the backward pass the
+ * DCU case-study page, section 5.4, says training needs checked on its own):
+ *     dX[r, j] = Y[r, j] * (dY[r, j] - sum_i dY[r, i] * Y[r, i])
+ *   y  : the forward output Y (device, rows*cols of dtype)
+ *   dy : the gradient with respect to Y (same shape and dtype)
+ *   dx : the gradient with respect to the forward input (same shape and
+ *        dtype); may alias dy or y exactly (in place)
+ * fp32 accumulation; reads y and dy once (rows that fit a workgroup's
+ * registers) and writes dx once.  Layout, alignment, streams and errors as
+ * softmax_fwd.
+ */
+int softmax_bwd(const void *y, const void *dy, void *dx, int64_t rows, int64_t cols, int dtype,
+                void *stream);
+
+/*
+ * softmax_bwd_kernel -- as softmax_bwd with a forced kernel: RWS_KERNEL_AUTO,
+ * RWS_KERNEL_WAVE_ROW (row in one wave's registers), RWS_KERNEL_BLOCK_ONEPASS
+ * (row in one workgroup's registers) or RWS_KERNEL_TWO_PASS (any length; y
+ * and dy are read twice).  Other ids: RWS_ERR_INVALID_ARG.
+ */
+int softmax_bwd_kernel(const void *y, const void *dy, void *dx, int64_t rows, int64_t cols,
+                       int dtype, void *stream, int kernel_id);
+
+/*
  * softmax_select_kernel -- the family softmax_fwd would run for this shape
  * with pointers `in` and `out` (their alignment matters), on the current
  * device.  Returns a RWS_KERNEL_* id (> 0), or a negative status on invalid

@@ -20,6 +20,8 @@ Thin ctypes wrappers over ``softmax_oracle.c`` (plain C, IEEE double, libm
 * :func:`md_merge`      -- the (m, d) merge rule itself.
 * :func:`masked_softmax` -- softmax of scale*x + mask (+ causal limit), the
   attention-score fusion the DCU case-study page proposes (section 9).
+* :func:`softmax_backward` -- dx = y * (dy - sum(dy * y)) per row, the
+  backward pass the same page (section 5.4) says needs its own check.
 
 Inputs are float64 arrays holding the values as stored in the tensor's dtype.
 """
@@ -59,6 +61,8 @@ def _load():
     lib.oracle_md_merge.restype = None
     lib.oracle_masked_softmax.argtypes = [_D, _D, _I64, _I64, ctypes.c_double, _D, _I64, _I64]
     lib.oracle_masked_softmax.restype = None
+    lib.oracle_softmax_backward.argtypes = [_D, _D, _D, _I64, _I64]
+    lib.oracle_softmax_backward.restype = None
     lib.oracle_safe_softmax_threads.argtypes = [_D, _D, _I64, _I64, ctypes.c_int]
     lib.oracle_safe_softmax_threads.restype = ctypes.c_int
     _lib = lib
@@ -156,3 +160,14 @@ def masked_softmax(x, scale: float = 1.0, mask=None, causal_q: int = 0) -> np.nd
     _load().oracle_masked_softmax(_p(a), _p(y), a.shape[0], a.shape[1], float(scale), mp,
                                   mrows, int(causal_q))
     return y
+
+
+def softmax_backward(y, dy) -> np.ndarray:
+    """Gradient with respect to the softmax input: y * (dy - sum_j dy_j y_j)."""
+    a = _as_2d(y)
+    g = _as_2d(dy)
+    if a.shape != g.shape:
+        raise ValueError("y and dy must have the same shape")
+    dx = np.empty_like(a)
+    _load().oracle_softmax_backward(_p(a), _p(g), _p(dx), a.shape[0], a.shape[1])
+    return dx

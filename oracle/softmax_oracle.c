@@ -226,6 +226,30 @@ void oracle_masked_softmax(const double *x, double *y, int64_t rows, int64_t col
 }
 
 /* ---------------------------------------------------------------------------
+ * Softmax backward (the training step the DCU case-study page, section 5.4,
+ * says needs its own check).  With y the forward output of a row and dy the
+ * gradient of the loss with respect to y, the gradient with respect to the
+ * row's input is the Jacobian transpose times dy:
+ *     dx_j = sum_i dy_i * dy_i/dx_j = y_j * (dy_j - sum_i dy_i * y_i),
+ * since dy_i/dx_j = y_i * (delta_ij - y_j).  Plain order: the dot product
+ * over the row first, then each element.
+ * ------------------------------------------------------------------------- */
+void oracle_softmax_backward(const double *y, const double *dy, double *dx, int64_t rows,
+                             int64_t cols)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *yr = y + r * cols;
+        const double *gr = dy + r * cols;
+        double *xr = dx + r * cols;
+        double dot = 0.0;
+        for (int64_t j = 0; j < cols; ++j)
+            dot += gr[j] * yr[j];
+        for (int64_t j = 0; j < cols; ++j)
+            xr[j] = yr[j] * (gr[j] - dot);
+    }
+}
+
+/* ---------------------------------------------------------------------------
  * The definition run over row ranges on several host threads: rows are
  * independent, so each thread applies safe_softmax_row to its own
  * contiguous range.  Used to time the oracle on the host's cores.

@@ -23,10 +23,11 @@ __all__ = [
     "RWS_ERR_HIP", "RWS_ERR_UNSUPPORTED_SHAPE",
     "KERNELS", "KERNEL_IDS",
     "library_path", "load_library",
-    "softmax_fwd", "softmax_fwd_kernel", "softmax_fwd_masked", "softmax_select_kernel",
+    "softmax_fwd", "softmax_fwd_kernel", "softmax_fwd_masked", "softmax_bwd",
+    "softmax_bwd_kernel", "softmax_select_kernel",
     "softmax_describe_launch",
     "softmax_kernel_name", "softmax_status_string", "softmax_last_error", "softmax_copy_bytes",
-    "softmax", "softmax_masked", "copy_bytes", "dtype_code", "SoftmaxError",
+    "softmax", "softmax_masked", "softmax_backward", "copy_bytes", "dtype_code", "SoftmaxError",
 ]
 
 RWS_F32, RWS_F16, RWS_BF16 = 0, 1, 2
@@ -77,6 +78,10 @@ def load_library():
     lib.softmax_fwd_masked.argtypes = [vp, vp, i64, i64, cint, ctypes.c_float, vp, i64, i64, vp,
                                        cint]
     lib.softmax_fwd_masked.restype = cint
+    lib.softmax_bwd.argtypes = [vp, vp, vp, i64, i64, cint, vp]
+    lib.softmax_bwd.restype = cint
+    lib.softmax_bwd_kernel.argtypes = [vp, vp, vp, i64, i64, cint, vp, cint]
+    lib.softmax_bwd_kernel.restype = cint
     lib.softmax_select_kernel.argtypes = [i64, i64, cint, vp, vp]
     lib.softmax_select_kernel.restype = cint
     lib.softmax_describe_launch.argtypes = [i64, i64, cint, vp, vp, cint, ctypes.c_char_p, i64]
@@ -110,6 +115,17 @@ def softmax_fwd_masked(in_ptr: int, out_ptr: int, rows: int, cols: int, dtype: i
                        kernel_id: int = 0) -> int:
     return load_library().softmax_fwd_masked(in_ptr, out_ptr, rows, cols, dtype, scale,
                                              mask_ptr or None, mask_rows, causal_q, stream,
+                                             kernel_id)
+
+
+def softmax_bwd(y_ptr: int, dy_ptr: int, dx_ptr: int, rows: int, cols: int, dtype: int,
+                stream: int) -> int:
+    return load_library().softmax_bwd(y_ptr, dy_ptr, dx_ptr, rows, cols, dtype, stream)
+
+
+def softmax_bwd_kernel(y_ptr: int, dy_ptr: int, dx_ptr: int, rows: int, cols: int, dtype: int,
+                       stream: int, kernel_id: int) -> int:
+    return load_library().softmax_bwd_kernel(y_ptr, dy_ptr, dx_ptr, rows, cols, dtype, stream,
                                              kernel_id)
 
 
@@ -216,6 +232,30 @@ def softmax_masked(x: torch.Tensor, scale: float = 1.0, mask: torch.Tensor | Non
     st = load_library().softmax_fwd_masked(x.data_ptr(), out.data_ptr(), rows, cols, code,
                                            float(scale), mask_ptr, mask_rows, int(causal_q),
                                            _stream_handle(x.device, stream), KERNEL_IDS[kernel])
+    if st != RWS_OK:
+        raise SoftmaxError(st, softmax_last_error())
+    return out
+
+
+def softmax_backward(y: torch.Tensor, dy: torch.Tensor, out: torch.Tensor | None = None,
+                     kernel: str = "auto", stream=None) -> torch.Tensor:
+    """Gradient with respect to the softmax input, from its output ``y`` and
+    the upstream gradient ``dy`` (both contiguous, same shape and dtype)."""
+    for t, name in ((y, "y"), (dy, "dy")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if dy.shape != y.shape or dy.dtype != y.dtype:
+        raise ValueError("y and dy must have the same shape and dtype")
+    code = dtype_code(y.dtype)
+    if out is None:
+        out = torch.empty_like(y)
+    if out.shape != y.shape or out.dtype != y.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of y's shape and dtype")
+    cols = y.shape[-1] if y.dim() > 0 else 1
+    rows = y.numel() // cols if cols > 0 else 0
+    st = load_library().softmax_bwd_kernel(y.data_ptr(), dy.data_ptr(), out.data_ptr(), rows, cols,
+                                           code, _stream_handle(y.device, stream),
+                                           KERNEL_IDS[kernel])
     if st != RWS_OK:
         raise SoftmaxError(st, softmax_last_error())
     return out

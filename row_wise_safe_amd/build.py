@@ -26,6 +26,7 @@ SOURCES = [
     "rws_splitk.hip",
     "rws_splitk_fused.hip",
     "rws_masked.hip",
+    "rws_backward.hip",
 ]
 
 COMMON_FLAGS = [

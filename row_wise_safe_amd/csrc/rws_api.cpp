@@ -536,6 +536,94 @@ int softmax_fwd_masked(const void* in, void* out, int64_t rows, int64_t cols, in
     return run(in, out, rows, cols, dtype, stream, kernel_id, &M);
 }
 
+// Softmax backward: family 1 (wave, registers), 2 (block, registers) or 3
+// (stream, any length), chosen like the forward kernels by the row window.
+int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, int64_t cols,
+                       int dtype, void* stream, int kernel_id) {
+    g_last_error.clear();
+    if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
+        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS)
+        return fail(RWS_ERR_INVALID_ARG, "backward kernels: auto, wave_row, block_onepass, two_pass");
+    int st = check_args(y, dx, rows, cols, dtype, RWS_KERNEL_AUTO);
+    if (st != RWS_OK || rows == 0 || cols == 0) return st;
+    if (!dy) return fail(RWS_ERR_INVALID_ARG, "NULL dy with a non-empty tensor");
+    if ((uintptr_t)dy % elem_size(dtype))
+        return fail(RWS_ERR_MISALIGNED, "dy not aligned to the element size");
+    const Geometry g = geometry(cols, dtype, y, dx);
+    const int64_t wline = window_granules(g, 128);
+    int family = kernel_id == RWS_KERNEL_AUTO ? 0 : kernel_id;  // 1 wave, 2 block, 3 stream
+    int variant = -1;
+    bool aligned = g.a128;
+    auto pick_wave = [&]() {
+        int best = -1;
+        int64_t best_cap = 0;
+        for (int i = 0; i < rws::kNumBwdWave; ++i) {
+            const rws::WaveRowVariant& v = rws::kBwdWave[i];
+            if ((int64_t)v.G * v.K < window_granules(g, wave_row_wa(v))) continue;
+            if (best < 0 || (int64_t)v.G * v.K < best_cap) {
+                best = i;
+                best_cap = (int64_t)v.G * v.K;
+            }
+        }
+        return best;
+    };
+    auto pick_block = [&]() {
+        int best = -1;
+        for (int i = 0; i < rws::kNumBwdBlock; ++i) {
+            const int64_t cap = (int64_t)rws::kBwdBlock[i].block * rws::kBwdBlock[i].u;
+            if (cap < wline) continue;
+            if (best < 0 || cap < (int64_t)rws::kBwdBlock[best].block * rws::kBwdBlock[best].u)
+                best = i;
+        }
+        return best;
+    };
+    if (family == 0) {
+        if (wline <= 512 && pick_wave() >= 0) family = 1;
+        else if (pick_block() >= 0) family = 2;
+        else family = 3;
+    }
+    if (family == 1) {
+        variant = pick_wave();
+        if (variant < 0)
+            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "backward wave kernel holds at most 512 granules");
+        aligned = wave_row_wa(rws::kBwdWave[variant]) == 128 ? g.a128 : g.a16;
+    } else if (family == 2) {
+        variant = pick_block();
+        if (variant < 0)
+            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "backward block kernel holds at most 4096 granules");
+    } else {
+        variant = 0;
+        for (int i = 0; i < rws::kNumBwdStream; ++i)
+            if (rws::kBwdStream[i].block == (wline > 4096 ? 1024 : 256)) variant = i;
+    }
+    const int64_t max_rows = family == 1
+        ? (int64_t)(64 / rws::kBwdWave[variant].G) * rws::kBwdWave[variant].U * 4 * ((int64_t)1 << 23)
+        : ((int64_t)1 << 22);
+    const int64_t row_bytes = cols * elem_size(dtype);
+    for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
+        rws::BwdLaunch B;
+        B.rows = std::min<int64_t>(max_rows, rows - r0);
+        B.y = (const char*)y + r0 * row_bytes;
+        B.dy = (const char*)dy + r0 * row_bytes;
+        B.dx = (char*)dx + r0 * row_bytes;
+        B.cols = (int)cols;
+        B.dtype = dtype;
+        B.aligned = aligned;
+        B.same_phase = g.same_phase;
+        B.dy_vec = (((uintptr_t)dy - (uintptr_t)y) % 16) == 0;
+        B.stream = (hipStream_t)stream;
+        const hipError_t e = rws::launch_bwd(B, family, variant);
+        if (e != hipSuccess)
+            return fail(RWS_ERR_HIP, std::string("backward launch: ") + hipGetErrorString(e));
+    }
+    return RWS_OK;
+}
+
+int softmax_bwd(const void* y, const void* dy, void* dx, int64_t rows, int64_t cols, int dtype,
+                void* stream) {
+    return softmax_bwd_kernel(y, dy, dx, rows, cols, dtype, stream, RWS_KERNEL_AUTO);
+}
+
 int softmax_fwd(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream) {
     return softmax_fwd_kernel(in, out, rows, cols, dtype, stream, RWS_KERNEL_AUTO);
 }

@@ -72,6 +72,27 @@ hipError_t splitk_fused_capacity(int variant, int dtype, bool aligned, int cus, 
 hipError_t launch_wave_row_masked(const Launch& L, int variant, const MaskArgs& M);
 hipError_t launch_block_onepass_masked(const Launch& L, int variant, const MaskArgs& M);
 hipError_t launch_two_pass_masked(const Launch& L, int variant, const MaskArgs& M);
+// Softmax backward: dx = y * (dy - sum(dy * y)) per row.
+struct BwdLaunch {
+    const void* y;
+    const void* dy;
+    void* dx;
+    int64_t rows;
+    int cols;
+    int dtype;
+    bool aligned;     // y, dx 128-byte aligned and cols*size % 128 == 0
+    bool same_phase;  // (dx - y) % 16 == 0
+    bool dy_vec;      // (dy - y) % 16 == 0
+    hipStream_t stream;
+};
+extern const WaveRowVariant kBwdWave[];
+extern const int kNumBwdWave;
+extern const TwoPassVariant kBwdBlock[];  // (threads, register granules per thread)
+extern const int kNumBwdBlock;
+extern const TwoPassVariant kBwdStream[];  // (threads, granules per thread per batch)
+extern const int kNumBwdStream;
+// family: 1 wave (kBwdWave), 2 block (kBwdBlock), 3 stream (kBwdStream)
+hipError_t launch_bwd(const BwdLaunch& B, int family, int variant);
 // n16 granules of 16 bytes.
 hipError_t launch_copy16(const void* in, void* out, int64_t n16, hipStream_t stream);
 

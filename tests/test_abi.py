@@ -133,3 +133,12 @@ def test_masked_argument_checks(lib):
     assert rws.softmax_fwd_masked(0, 0, 0, 8, f16, 1.0, 0, 0, 0, 0, 0) == rws.RWS_OK
     assert rws.softmax_fwd_masked(256, 256, 2, 8, 9, 1.0, 0, 0, 0, 0, 0) == \
         rws.RWS_ERR_UNSUPPORTED_DTYPE
+
+
+def test_backward_argument_checks(lib):
+    f16 = rws.RWS_F16
+    assert rws.softmax_bwd(256, 0, 256, 2, 8, f16, 0) == rws.RWS_ERR_INVALID_ARG   # NULL dy
+    assert rws.softmax_bwd(256, 257, 256, 2, 8, f16, 0) == rws.RWS_ERR_MISALIGNED
+    assert rws.softmax_bwd(0, 0, 0, 0, 8, f16, 0) == rws.RWS_OK
+    assert rws.softmax_bwd_kernel(256, 256, 256, 2, 8, f16, 0, 4) == rws.RWS_ERR_INVALID_ARG
+    assert rws.softmax_bwd(256, 256, 256, 2, 8, 7, 0) == rws.RWS_ERR_UNSUPPORTED_DTYPE
