@@ -22,6 +22,9 @@ Thin ctypes wrappers over ``softmax_oracle.c`` (plain C, IEEE double, libm
   attention-score fusion the DCU case-study page proposes (section 9).
 * :func:`softmax_backward` -- dx = y * (dy - sum(dy * y)) per row, the
   backward pass the same page (section 5.4) says needs its own check.
+* :func:`layernorm`, :func:`rmsnorm` -- the row normalisations the same page
+  (section 9) names as having softmax's structure, and the Pangu-Weather
+  profile page (section 3) runs as a wave-per-row kernel (``norm_oracle.c``).
 
 Inputs are float64 arrays holding the values as stored in the tensor's dtype.
 """
@@ -44,7 +47,8 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_build.LIBRARY):
+    if not os.path.exists(_build.LIBRARY) or any(
+            os.path.getmtime(src) > os.path.getmtime(_build.LIBRARY) for src in _build.SOURCES):
         _build.build()
     lib = ctypes.CDLL(_build.LIBRARY)
     lib.oracle_safe_softmax.argtypes = [_D, _D, _I64, _I64]
@@ -63,6 +67,10 @@ def _load():
     lib.oracle_masked_softmax.restype = None
     lib.oracle_softmax_backward.argtypes = [_D, _D, _D, _I64, _I64]
     lib.oracle_softmax_backward.restype = None
+    lib.oracle_layernorm.argtypes = [_D, _D, _I64, _I64, ctypes.c_double, _D, _D, _D, _D]
+    lib.oracle_layernorm.restype = None
+    lib.oracle_rmsnorm.argtypes = [_D, _D, _I64, _I64, ctypes.c_double, _D, _D]
+    lib.oracle_rmsnorm.restype = None
     lib.oracle_safe_softmax_threads.argtypes = [_D, _D, _I64, _I64, ctypes.c_int]
     lib.oracle_safe_softmax_threads.restype = ctypes.c_int
     _lib = lib
@@ -171,3 +179,38 @@ def softmax_backward(y, dy) -> np.ndarray:
     dx = np.empty_like(a)
     _load().oracle_softmax_backward(_p(a), _p(g), _p(dx), a.shape[0], a.shape[1])
     return dx
+
+
+def _vec(v, cols):
+    if v is None:
+        return None, None
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.float64)).reshape(-1)
+    if a.shape[0] != cols:
+        raise ValueError("weight/bias must have one entry per column")
+    return a, _p(a)
+
+
+def layernorm(x, eps: float = 1e-5, weight=None, bias=None, return_stats: bool = False):
+    """LayerNorm along the last axis: (x - mean) / sqrt(var + eps) * w + b with
+    the biased variance.  With ``return_stats`` also returns per-row
+    ``(mean, rstd)``."""
+    a = _as_2d(x)
+    y = np.empty_like(a)
+    w, wp = _vec(weight, a.shape[1])
+    b, bp = _vec(bias, a.shape[1])
+    mean = np.empty(a.shape[0])
+    rstd = np.empty(a.shape[0])
+    _load().oracle_layernorm(_p(a), _p(y), a.shape[0], a.shape[1], float(eps), wp, bp,
+                             _p(mean), _p(rstd))
+    return (y, mean, rstd) if return_stats else y
+
+
+def rmsnorm(x, eps: float = 1e-5, weight=None, return_stats: bool = False):
+    """RMSNorm along the last axis: x / sqrt(mean(x^2) + eps) * w.  With
+    ``return_stats`` also returns per-row ``rstd``."""
+    a = _as_2d(x)
+    y = np.empty_like(a)
+    w, wp = _vec(weight, a.shape[1])
+    rstd = np.empty(a.shape[0])
+    _load().oracle_rmsnorm(_p(a), _p(y), a.shape[0], a.shape[1], float(eps), wp, _p(rstd))
+    return (y, rstd) if return_stats else y

@@ -9,18 +9,18 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCE = os.path.join(HERE, "softmax_oracle.c")
+SOURCES = [os.path.join(HERE, "softmax_oracle.c"), os.path.join(HERE, "norm_oracle.c")]
 LIBRARY = os.path.join(HERE, "libsoftmax_oracle.so")
 
 
 def build(verbose: bool = False) -> str:
-    """Compile softmax_oracle.c into libsoftmax_oracle.so and return its path.
+    """Compile the oracle's C sources into libsoftmax_oracle.so; return its path.
 
     Strict IEEE double: no -ffast-math, no FMA contraction.
     """
     tmp = LIBRARY + f".tmp{os.getpid()}"
     cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-ffp-contract=off",
-           "-fPIC", "-shared", "-o", tmp, SOURCE, "-lm", "-lpthread"]
+           "-fPIC", "-shared", "-o", tmp, *SOURCES, "-lm", "-lpthread"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

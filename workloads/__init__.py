@@ -1,7 +1,7 @@
-"""Seeded synthetic inputs for row-wise softmax.
+"""Seeded synthetic inputs for row-wise softmax and the row normalisations.
 
 This module is shared by the oracle side and the GPU side and therefore holds
-no softmax arithmetic at all: it only draws numbers.  Every array comes back as
+no softmax or normalisation arithmetic at all: it only draws numbers.  Every array comes back as
 float64 in row-major ``[rows, cols]`` order; the caller rounds it to the storage
 dtype (and both sides then read the *stored* values back).
 
@@ -18,6 +18,12 @@ Workloads, each named by what it is (dtype, shape, value distribution):
   independently replaced by +1e4 with probability 0.01.
 * ``fp16_16x1M``           -- fp16 [16, 1048576], i.i.d. N(0, 3^2), then each
   row's (first) largest entry is swapped to a column drawn uniformly per row.
+* ``ln_fp16_131040x192``, ``ln_fp16_32760x384`` (in ``NORM_WORKLOADS``, the
+  inputs of the row normalisations) -- the two LayerNorm shapes
+  of the Pangu-Weather profile page, section 3 ([1,131040,192] and
+  [1,32760,384] tokens x hidden width), as activations with a per-row offset
+  and spread: x = mu_r + sigma_r * z, mu_r ~ U[-4, 4], sigma_r ~ U[0.25, 4],
+  z ~ N(0, 1).
 
 Seeds are ``20260000 + k`` for the k-th workload of the list above (the worked
 example shares k = 1 with the 64x1000 tensor but is not random).
@@ -31,11 +37,13 @@ import numpy as np
 __all__ = [
     "Workload",
     "WORKLOADS",
+    "NORM_WORKLOADS",
     "generate",
     "normal",
     "uniform",
     "spiked_normal",
     "argmax_moved_normal",
+    "row_shifted_normal",
     "worked_example",
 ]
 
@@ -100,6 +108,17 @@ def argmax_moved_normal(rows: int, cols: int, seed: int, sigma: float = 3.0,
     return x
 
 
+def row_shifted_normal(rows: int, cols: int, seed: int, mu_lo: float = -4.0, mu_hi: float = 4.0,
+                       sigma_lo: float = 0.25, sigma_hi: float = 4.0) -> np.ndarray:
+    """x = mu_r + sigma_r * z: per-row offset mu_r ~ U[mu_lo, mu_hi) and spread
+    sigma_r ~ U[sigma_lo, sigma_hi), then z ~ N(0, 1) i.i.d. (drawn in that
+    order from one generator)."""
+    g = _rng(seed)
+    mu = g.uniform(mu_lo, mu_hi, size=(rows, 1))
+    sigma = g.uniform(sigma_lo, sigma_hi, size=(rows, 1))
+    return mu + sigma * g.standard_normal((rows, cols))
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str
@@ -144,6 +163,17 @@ WORKLOADS: dict[str, Workload] = {
     ]
 }
 
+# Inputs of the row normalisations (LayerNorm, RMSNorm).
+NORM_WORKLOADS: dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("ln_fp16_131040x192", "f16", 131040, 192, 20260006, "row_shifted_normal",
+                 {}, "fp16 [1,131040,192] tokens, per-row offset/spread normal"),
+        Workload("ln_fp16_32760x384", "f16", 32760, 384, 20260007, "row_shifted_normal",
+                 {}, "fp16 [1,32760,384] tokens, per-row offset/spread normal"),
+    ]
+}
+
 
 def generate(w: Workload, rows: int | None = None, row_offset: int = 0) -> np.ndarray:
     """Draw the workload's float64 input.
@@ -162,6 +192,8 @@ def generate(w: Workload, rows: int | None = None, row_offset: int = 0) -> np.nd
         x = spiked_normal(w.rows, w.cols, w.seed, **w.params)
     elif w.kind == "argmax_moved_normal":
         x = argmax_moved_normal(w.rows, w.cols, w.seed, **w.params)
+    elif w.kind == "row_shifted_normal":
+        x = row_shifted_normal(w.rows, w.cols, w.seed, **w.params)
     else:  # pragma: no cover
         raise ValueError(w.kind)
     if rows is None:
