@@ -195,6 +195,27 @@ def cpu_baseline(w, x_stored_f64, target_s: float = 10.0) -> dict:
                       f"{used} host threads; bytes counted as fp16 in+out, {dt:.1f} s"}
 
 
+def norm_cpu_baseline(w, x_stored_f64, mode: str, target_s: float = 10.0) -> dict:
+    """The oracle's layernorm / rmsnorm (one host thread) over a row sample."""
+    import oracle
+    rows = min(x_stored_f64.shape[0], 16384)
+    sample = x_stored_f64[:rows]
+    fn = oracle.layernorm if mode == "layernorm" else oracle.rmsnorm
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        fn(sample, 1e-5)
+        passes += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    dt = time.perf_counter() - t0
+    nbytes = 2 * rows * w.cols * w.elem_bytes * passes
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} passes over the first {rows} rows of {w.rows}x{w.cols} "
+                      f"({mode}, values widened to float64, one host thread); bytes counted "
+                      f"in the workload's dtype, in+out, {dt:.1f} s"}
+
+
 # --------------------------------------------------------------------------
 # main
 # --------------------------------------------------------------------------
@@ -212,6 +233,10 @@ def main() -> int:
     ap.add_argument("--backward", action="store_true",
                     help="softmax backward dx = y*(dy - sum(dy*y)) on the workload's shape "
                          "(softmax_bwd): 2 reads + 1 write per element")
+    ap.add_argument("--norm", choices=["layernorm", "rmsnorm"], default=None,
+                    help="row normalisation instead of softmax (layernorm_fwd / rmsnorm_fwd, no "
+                         "affine, eps 1e-5) on a normalisation workload (default "
+                         "ln_fp16_131040x192)")
     ap.add_argument("--skip-hot", action="store_true",
                     help="skip the single-buffer figure (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -242,7 +267,14 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     rws.load_library()
-    w = workloads.WORKLOADS[args.workload]
+    if args.norm:
+        if args.masked or args.backward:
+            print("--norm excludes --masked and --backward", file=sys.stderr)
+            return 2
+        name = args.workload if args.workload in workloads.NORM_WORKLOADS else "ln_fp16_131040x192"
+        w = workloads.NORM_WORKLOADS[name]
+    else:
+        w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
     code = rws.dtype_code(tdt)
@@ -263,6 +295,9 @@ def main() -> int:
     desc = rws.softmax_describe_launch(w.rows, w.cols, code, xs[0].data_ptr(), ys[0].data_ptr(),
                                        kid)
     family = desc.split("<")[0]
+    if args.norm:
+        desc = f"{args.norm} {args.kernel}"
+        family = None
     dys = None
     if args.backward:
         # y = the forward output of each input, dy ~ N(0, 1); dx goes to ys[i]
@@ -287,7 +322,13 @@ def main() -> int:
     log(f"[bench] launch: {desc}; {nbuf} rotating buffer pairs")
 
     def step(i):
-        if dys is not None:
+        if args.norm == "layernorm":
+            st = rws.layernorm_fwd_kernel(xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), w.rows,
+                                          w.cols, code, 1e-5, 0, 0, 0, 0, sh, kid)
+        elif args.norm == "rmsnorm":
+            st = rws.rmsnorm_fwd_kernel(xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), w.rows,
+                                        w.cols, code, 1e-5, 0, 0, sh, kid)
+        elif dys is not None:
             st = rws.softmax_bwd_kernel(xs[i % nbuf].data_ptr(), dys[i % nbuf].data_ptr(),
                                         ys[i % nbuf].data_ptr(), w.rows, w.cols, code, sh, kid)
         elif mask is None:
@@ -353,10 +394,11 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         stored = x_host.to(torch.float64).numpy()
-        cpu = cpu_baseline(w, stored, args.cpu_seconds)
+        cpu = (norm_cpu_baseline(w, stored, args.norm, args.cpu_seconds) if args.norm
+               else cpu_baseline(w, stored, args.cpu_seconds))
         log(f"[bench] cpu oracle {cpu['value']} GB/s on {cpu['cores']} threads")
 
-    traffic = read_traffic(w.name, family)
+    traffic = read_traffic(w.name, family) if family else None
     achieved = nbytes / (ms * 1e-3) / 1e9
     vs = round(gbps / PAGES_FP16_ATTN_GBPS, 3) if w.name == "fp16_attn_4x32x512x512" else None
     if mask is not None or dys is not None:
@@ -364,7 +406,8 @@ def main() -> int:
     result = {
         "metric": f"effective HBM GB/s (read+write), {w.description}"
                   + (", softmax(x/8 + mask + causal)" if mask is not None else "")
-                  + (", backward dx = y*(dy - sum(dy*y))" if dys is not None else ""),
+                  + (", backward dx = y*(dy - sum(dy*y))" if dys is not None else "")
+                  + (f", {args.norm} forward (eps 1e-5, no affine)" if args.norm else ""),
         "value": round(gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,

@@ -1,6 +1,7 @@
 /*
  * row_wise_softmax.h -- C ABI of the MI355X (gfx950) row-wise safe softmax
- * library (librws_softmax.so).
+ * library (librws_softmax.so), with the softmax backward and the LayerNorm /
+ * RMSNorm row normalisations on the same kernels' skeleton.
  *
  * Operation.  For a contiguous row-major matrix X[rows, cols] the library
  * writes, for every row r and column j,
@@ -177,6 +178,56 @@ int softmax_bwd(const void *y, const void *dy, void *dx, int64_t rows, int64_t c
  */
 int softmax_bwd_kernel(const void *y, const void *dy, void *dx, int64_t rows, int64_t cols,
                        int dtype, void *stream, int kernel_id);
+
+/*
+ * layernorm_fwd -- LayerNorm along the last dimension, the row normalisation
+ * the DCU case-study page (section 9) names as having softmax's read /
+ * reduce / normalise / write structure, and the Pangu-Weather profile page
+ * (section 3) runs as a wave-per-row kernel with fp16 data and fp32
+ * statistics:
+ *     mu_r   = (1/cols) sum_j X[r, j]
+ *     var_r  = (1/cols) sum_j (X[r, j] - mu_r)^2          (biased)
+ *     rstd_r = 1 / sqrt(var_r + eps)
+ *     Y[r, j] = (X[r, j] - mu_r) * rstd_r * W[j] + B[j]
+ *   eps    : >= 0 and finite (RWS_ERR_INVALID_ARG otherwise)
+ *   weight : NULL (W = 1) or cols elements of `dtype` on the device, aligned
+ *            to the element size
+ *   bias   : NULL (B = 0) or as weight
+ *   mean, rstd : NULL, or rows fp32 values each on the device (4-byte
+ *            aligned) that receive mu_r and rstd_r (for a backward pass)
+ * Statistics are accumulated in fp32 from the row held in registers (mean
+ * first, then the centred sum of squares); rows longer than a workgroup's
+ * registers merge per-thread (count, mean, sum of squared deviations)
+ * partials pairwise.  A row with var_r + eps == 0 gives NaN (0 * inf), as the
+ * definition does.  weight, bias, mean and rstd must not overlap `out`.
+ * Layout, in-place use, alignment, streams and errors as softmax_fwd.
+ */
+int layernorm_fwd(const void *in, void *out, int64_t rows, int64_t cols, int dtype, float eps,
+                  const void *weight, const void *bias, float *mean, float *rstd, void *stream);
+
+/*
+ * rmsnorm_fwd -- RMSNorm along the last dimension (named beside LayerNorm on
+ * the DCU case-study page, section 9):
+ *     rstd_r = 1 / sqrt((1/cols) sum_j X[r, j]^2 + eps),
+ *     Y[r, j] = X[r, j] * rstd_r * W[j]
+ * Arguments as layernorm_fwd (no bias, no mean).
+ */
+int rmsnorm_fwd(const void *in, void *out, int64_t rows, int64_t cols, int dtype, float eps,
+                const void *weight, float *rstd, void *stream);
+
+/*
+ * layernorm_fwd_kernel, rmsnorm_fwd_kernel -- as above with a forced kernel:
+ * RWS_KERNEL_AUTO, RWS_KERNEL_WAVE_ROW (row in one lane group's registers,
+ * window up to 512 granules), RWS_KERNEL_BLOCK_ONEPASS (row in one
+ * workgroup's registers, up to 4096 granules) or RWS_KERNEL_TWO_PASS (any
+ * length; the row is read twice).  Other ids: RWS_ERR_INVALID_ARG; a row too
+ * long for the forced kernel: RWS_ERR_UNSUPPORTED_SHAPE.
+ */
+int layernorm_fwd_kernel(const void *in, void *out, int64_t rows, int64_t cols, int dtype,
+                         float eps, const void *weight, const void *bias, float *mean, float *rstd,
+                         void *stream, int kernel_id);
+int rmsnorm_fwd_kernel(const void *in, void *out, int64_t rows, int64_t cols, int dtype, float eps,
+                       const void *weight, float *rstd, void *stream, int kernel_id);
 
 /*
  * softmax_select_kernel -- the family softmax_fwd would run for this shape

@@ -1,8 +1,10 @@
-"""Python binding of librws_softmax.so -- row-wise safe softmax on MI355X.
+"""Python binding of librws_softmax.so -- row-wise safe softmax on MI355X,
+with its backward and the LayerNorm / RMSNorm row normalisations.
 
 Argument marshalling only: every step of the computation runs in the
-library's gfx950 HIP kernels.  The functions named ``softmax_*`` mirror the C
-ABI of ``include/row_wise_softmax.h`` one to one (plain integers for pointers,
+library's gfx950 HIP kernels.  The functions named ``softmax_*``,
+``layernorm_*`` and ``rmsnorm_*`` mirror the C ABI of
+``include/row_wise_softmax.h`` one to one (plain integers for pointers,
 sizes and the stream); :func:`softmax` is the tensor-level convenience that
 fills them in from a torch tensor and the current stream.
 
@@ -27,7 +29,9 @@ __all__ = [
     "softmax_bwd_kernel", "softmax_select_kernel",
     "softmax_describe_launch",
     "softmax_kernel_name", "softmax_status_string", "softmax_last_error", "softmax_copy_bytes",
-    "softmax", "softmax_masked", "softmax_backward", "copy_bytes", "dtype_code", "SoftmaxError",
+    "layernorm_fwd", "layernorm_fwd_kernel", "rmsnorm_fwd", "rmsnorm_fwd_kernel",
+    "softmax", "softmax_masked", "softmax_backward", "layer_norm", "rms_norm", "copy_bytes",
+    "dtype_code", "SoftmaxError",
 ]
 
 RWS_F32, RWS_F16, RWS_BF16 = 0, 1, 2
@@ -94,6 +98,15 @@ def load_library():
     lib.softmax_last_error.restype = ctypes.c_char_p
     lib.softmax_copy_bytes.argtypes = [vp, vp, i64, vp]
     lib.softmax_copy_bytes.restype = cint
+    f32 = ctypes.c_float
+    lib.layernorm_fwd.argtypes = [vp, vp, i64, i64, cint, f32, vp, vp, vp, vp, vp]
+    lib.layernorm_fwd.restype = cint
+    lib.layernorm_fwd_kernel.argtypes = [vp, vp, i64, i64, cint, f32, vp, vp, vp, vp, vp, cint]
+    lib.layernorm_fwd_kernel.restype = cint
+    lib.rmsnorm_fwd.argtypes = [vp, vp, i64, i64, cint, f32, vp, vp, vp]
+    lib.rmsnorm_fwd.restype = cint
+    lib.rmsnorm_fwd_kernel.argtypes = [vp, vp, i64, i64, cint, f32, vp, vp, vp, cint]
+    lib.rmsnorm_fwd_kernel.restype = cint
     _LIB = lib
     return lib
 
@@ -126,6 +139,36 @@ def softmax_bwd(y_ptr: int, dy_ptr: int, dx_ptr: int, rows: int, cols: int, dtyp
 def softmax_bwd_kernel(y_ptr: int, dy_ptr: int, dx_ptr: int, rows: int, cols: int, dtype: int,
                        stream: int, kernel_id: int) -> int:
     return load_library().softmax_bwd_kernel(y_ptr, dy_ptr, dx_ptr, rows, cols, dtype, stream,
+                                             kernel_id)
+
+
+def layernorm_fwd(in_ptr: int, out_ptr: int, rows: int, cols: int, dtype: int, eps: float,
+                  weight_ptr: int, bias_ptr: int, mean_ptr: int, rstd_ptr: int,
+                  stream: int) -> int:
+    return load_library().layernorm_fwd(in_ptr, out_ptr, rows, cols, dtype, eps, weight_ptr or None,
+                                        bias_ptr or None, mean_ptr or None, rstd_ptr or None,
+                                        stream)
+
+
+def layernorm_fwd_kernel(in_ptr: int, out_ptr: int, rows: int, cols: int, dtype: int, eps: float,
+                         weight_ptr: int, bias_ptr: int, mean_ptr: int, rstd_ptr: int,
+                         stream: int, kernel_id: int) -> int:
+    return load_library().layernorm_fwd_kernel(in_ptr, out_ptr, rows, cols, dtype, eps,
+                                               weight_ptr or None, bias_ptr or None,
+                                               mean_ptr or None, rstd_ptr or None, stream,
+                                               kernel_id)
+
+
+def rmsnorm_fwd(in_ptr: int, out_ptr: int, rows: int, cols: int, dtype: int, eps: float,
+                weight_ptr: int, rstd_ptr: int, stream: int) -> int:
+    return load_library().rmsnorm_fwd(in_ptr, out_ptr, rows, cols, dtype, eps, weight_ptr or None,
+                                      rstd_ptr or None, stream)
+
+
+def rmsnorm_fwd_kernel(in_ptr: int, out_ptr: int, rows: int, cols: int, dtype: int, eps: float,
+                       weight_ptr: int, rstd_ptr: int, stream: int, kernel_id: int) -> int:
+    return load_library().rmsnorm_fwd_kernel(in_ptr, out_ptr, rows, cols, dtype, eps,
+                                             weight_ptr or None, rstd_ptr or None, stream,
                                              kernel_id)
 
 
@@ -255,6 +298,72 @@ def softmax_backward(y: torch.Tensor, dy: torch.Tensor, out: torch.Tensor | None
     rows = y.numel() // cols if cols > 0 else 0
     st = load_library().softmax_bwd_kernel(y.data_ptr(), dy.data_ptr(), out.data_ptr(), rows, cols,
                                            code, _stream_handle(y.device, stream),
+                                           KERNEL_IDS[kernel])
+    if st != RWS_OK:
+        raise SoftmaxError(st, softmax_last_error())
+    return out
+
+
+def _norm_operands(x, out, weight, bias):
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous GPU tensor")
+    code = dtype_code(x.dtype)
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or \
+            out.device != x.device:
+        raise ValueError("out must be a contiguous tensor of x's shape, dtype and device")
+    cols = x.shape[-1] if x.dim() > 0 else 1
+    rows = x.numel() // cols if cols > 0 else 0
+    ptrs = []
+    for t, name in ((weight, "weight"), (bias, "bias")):
+        if t is None:
+            ptrs.append(None)
+            continue
+        if t.dtype != x.dtype or not t.is_contiguous() or t.numel() != cols or \
+                t.device != x.device:
+            raise ValueError(f"{name} must be a contiguous vector of x's dtype with one entry "
+                             "per column, on x's device")
+        ptrs.append(t.data_ptr())
+    return code, out, rows, cols, ptrs[0], ptrs[1]
+
+
+def _stats_out(t, rows, device, name):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != rows or \
+            t.device != device:
+        raise ValueError(f"{name} must be a contiguous float32 tensor with one entry per row")
+    return t.data_ptr()
+
+
+def layer_norm(x: torch.Tensor, eps: float = 1e-5, weight: torch.Tensor | None = None,
+               bias: torch.Tensor | None = None, out: torch.Tensor | None = None,
+               mean: torch.Tensor | None = None, rstd: torch.Tensor | None = None,
+               kernel: str = "auto", stream=None) -> torch.Tensor:
+    """LayerNorm of ``x`` along its last dimension: (x - mean) / sqrt(var + eps)
+    * weight + bias with the biased variance.  ``weight``/``bias`` (optional)
+    have x's dtype and one entry per column; ``mean``/``rstd`` (optional,
+    float32, one entry per row) receive the row statistics."""
+    code, out, rows, cols, wp, bp = _norm_operands(x, out, weight, bias)
+    mp = _stats_out(mean, rows, x.device, "mean")
+    rp = _stats_out(rstd, rows, x.device, "rstd")
+    st = load_library().layernorm_fwd_kernel(x.data_ptr(), out.data_ptr(), rows, cols, code,
+                                             float(eps), wp, bp, mp, rp,
+                                             _stream_handle(x.device, stream), KERNEL_IDS[kernel])
+    if st != RWS_OK:
+        raise SoftmaxError(st, softmax_last_error())
+    return out
+
+
+def rms_norm(x: torch.Tensor, eps: float = 1e-5, weight: torch.Tensor | None = None,
+             out: torch.Tensor | None = None, rstd: torch.Tensor | None = None,
+             kernel: str = "auto", stream=None) -> torch.Tensor:
+    """RMSNorm of ``x`` along its last dimension: x / sqrt(mean(x^2) + eps) * weight."""
+    code, out, rows, cols, wp, _ = _norm_operands(x, out, weight, None)
+    rp = _stats_out(rstd, rows, x.device, "rstd")
+    st = load_library().rmsnorm_fwd_kernel(x.data_ptr(), out.data_ptr(), rows, cols, code,
+                                           float(eps), wp, rp, _stream_handle(x.device, stream),
                                            KERNEL_IDS[kernel])
     if st != RWS_OK:
         raise SoftmaxError(st, softmax_last_error())

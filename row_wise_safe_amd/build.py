@@ -27,6 +27,8 @@ SOURCES = [
     "rws_splitk_fused.hip",
     "rws_masked.hip",
     "rws_backward.hip",
+    "rws_norm_wave.hip",
+    "rws_norm_block.hip",
 ]
 
 COMMON_FLAGS = [

@@ -14,6 +14,7 @@
 // The thresholds are set from measurements on MI355X.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -622,6 +623,127 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
 int softmax_bwd(const void* y, const void* dy, void* dx, int64_t rows, int64_t cols, int dtype,
                 void* stream) {
     return softmax_bwd_kernel(y, dy, dx, rows, cols, dtype, stream, RWS_KERNEL_AUTO);
+}
+
+// Row normalisations: family 1 (norm_wave), 2 (norm_block) or 3
+// (norm_stream), chosen by the row window like the softmax backward.
+static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t cols, int dtype,
+                    float eps, const void* weight, const void* bias, float* mean, float* rstd,
+                    void* stream, int kernel_id) {
+    g_last_error.clear();
+    if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
+        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS)
+        return fail(RWS_ERR_INVALID_ARG, "normalisation kernels: auto, wave_row, block_onepass, two_pass");
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return fail(RWS_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    int st = check_args(in, out, rows, cols, dtype, RWS_KERNEL_AUTO);
+    if (st != RWS_OK || rows == 0 || cols == 0) return st;
+    const int es = elem_size(dtype);
+    if ((uintptr_t)weight % es || (uintptr_t)bias % es)
+        return fail(RWS_ERR_MISALIGNED, "weight/bias not aligned to the element size");
+    if ((uintptr_t)mean % 4 || (uintptr_t)rstd % 4)
+        return fail(RWS_ERR_MISALIGNED, "mean/rstd not aligned to 4 bytes");
+    const Geometry g = geometry(cols, dtype, in, out);
+    const int64_t wline = window_granules(g, 128);
+    auto pick_wave = [&]() {
+        int best = -1;
+        int64_t best_key = 0;
+        for (int i = 0; i < rws::kNumNormWave; ++i) {
+            const rws::WaveRowVariant& v = rws::kNormWave[i];
+            const int64_t cap = (int64_t)v.G * v.K;
+            if (cap < window_granules(g, wave_row_wa(v))) continue;
+            const int want_u = (v.G == 64 && v.K == 1) ? 2 : 1;
+            const int64_t key = cap * 64 + (v.U == want_u ? 0 : v.U);
+            if (best < 0 || key < best_key) {
+                best = i;
+                best_key = key;
+            }
+        }
+        return best;
+    };
+    auto pick_block = [&]() {
+        int best = -1;
+        for (int i = 0; i < rws::kNumNormBlock; ++i) {
+            const int64_t cap = (int64_t)rws::kNormBlock[i].block * rws::kNormBlock[i].u;
+            if (cap < wline) continue;
+            if (best < 0 || cap < (int64_t)rws::kNormBlock[best].block * rws::kNormBlock[best].u)
+                best = i;
+        }
+        return best;
+    };
+    int family = kernel_id == RWS_KERNEL_AUTO ? 0 : kernel_id;
+    if (family == 0) {
+        if (wline <= 512 && pick_wave() >= 0) family = 1;
+        else if (pick_block() >= 0) family = 2;
+        else family = 3;
+    }
+    int variant = -1;
+    bool aligned = g.a128;
+    if (family == 1) {
+        variant = pick_wave();
+        if (variant < 0)
+            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "normalisation wave kernel holds at most 512 granules");
+        aligned = wave_row_wa(rws::kNormWave[variant]) == 128 ? g.a128 : g.a16;
+    } else if (family == 2) {
+        variant = pick_block();
+        if (variant < 0)
+            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "normalisation block kernel holds at most 4096 granules");
+    } else {
+        variant = 0;
+        for (int i = 0; i < rws::kNumNormStream; ++i)
+            if (rws::kNormStream[i].block == (wline > 4096 ? 1024 : 256)) variant = i;
+    }
+    const int64_t max_rows = family == 1
+        ? (int64_t)(64 / rws::kNormWave[variant].G) * rws::kNormWave[variant].U * 4 * ((int64_t)1 << 23)
+        : ((int64_t)1 << 22);
+    const int64_t row_bytes = cols * es;
+    for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
+        rws::NormLaunch L;
+        L.rows = std::min<int64_t>(max_rows, rows - r0);
+        L.in = (const char*)in + r0 * row_bytes;
+        L.out = (char*)out + r0 * row_bytes;
+        L.cols = (int)cols;
+        L.dtype = dtype;
+        L.mode = mode;
+        L.aligned = aligned;
+        L.same_phase = g.same_phase;
+        L.args.w = weight;
+        L.args.b = bias;
+        L.args.mean = mean ? mean + r0 : nullptr;
+        L.args.rstd = rstd ? rstd + r0 : nullptr;
+        L.args.eps = eps;
+        L.args.n = (float)cols;
+        L.stream = (hipStream_t)stream;
+        const hipError_t e = family == 1 ? rws::launch_norm_wave(L, variant)
+                                         : rws::launch_norm_block(L, family, variant);
+        if (e != hipSuccess)
+            return fail(RWS_ERR_HIP, std::string("normalisation launch: ") + hipGetErrorString(e));
+    }
+    return RWS_OK;
+}
+
+int layernorm_fwd_kernel(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
+                         float eps, const void* weight, const void* bias, float* mean, float* rstd,
+                         void* stream, int kernel_id) {
+    return norm_run(rws::kLayerNorm, in, out, rows, cols, dtype, eps, weight, bias, mean, rstd,
+                    stream, kernel_id);
+}
+
+int layernorm_fwd(const void* in, void* out, int64_t rows, int64_t cols, int dtype, float eps,
+                  const void* weight, const void* bias, float* mean, float* rstd, void* stream) {
+    return layernorm_fwd_kernel(in, out, rows, cols, dtype, eps, weight, bias, mean, rstd, stream,
+                                RWS_KERNEL_AUTO);
+}
+
+int rmsnorm_fwd_kernel(const void* in, void* out, int64_t rows, int64_t cols, int dtype, float eps,
+                       const void* weight, float* rstd, void* stream, int kernel_id) {
+    return norm_run(rws::kRmsNorm, in, out, rows, cols, dtype, eps, weight, nullptr, nullptr, rstd,
+                    stream, kernel_id);
+}
+
+int rmsnorm_fwd(const void* in, void* out, int64_t rows, int64_t cols, int dtype, float eps,
+                const void* weight, float* rstd, void* stream) {
+    return rmsnorm_fwd_kernel(in, out, rows, cols, dtype, eps, weight, rstd, stream, RWS_KERNEL_AUTO);
 }
 
 int softmax_fwd(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream) {

@@ -58,21 +58,6 @@ struct Second {
     }
 };
 
-// y values of granule k with 0 (not -inf) outside the row.
-template <int DT, class Win>
-__device__ inline void widen_y(const Win& w, int k, u32x4 raw, float* v, const char* tbeg,
-                               const char* tend) {
-    w.widen(k, raw, v, tbeg, tend);
-    const int c0 = k * Elem<DT>::VEC - w.lead;
-    if (!(c0 >= 0 && c0 + Elem<DT>::VEC <= w.cols)) {
-#pragma unroll
-        for (int e = 0; e < Elem<DT>::VEC; ++e) {
-            const int c = c0 + e;
-            if (!(c >= 0 && c < w.cols)) v[e] = 0.0f;
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
 template <int DT, bool ALIGNED, int G, int K, int U>
 __global__ __launch_bounds__(256) void k_bwd_wave(const void* __restrict__ y,
@@ -113,7 +98,7 @@ __global__ __launch_bounds__(256) void k_bwd_wave(const void* __restrict__ y,
         float vy[N], vg[N];
 #pragma unroll
         for (int i = 0; i < K; ++i) {
-            widen_y<DT>(w[u], gl + G * i, ry[u][i], &vy[i * VEC], tbeg, tend);
+            widen_zero<DT>(w[u], gl + G * i, ry[u][i], &vy[i * VEC], tbeg, tend);
             s2.widen(w[u], gl + G * i, rg[u][i], &vg[i * VEC]);
         }
         float dot = 0.0f;
@@ -163,7 +148,7 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_block(const void* __restrict__ y,
     float vy[N], vg[N];
 #pragma unroll
     for (int i = 0; i < KR; ++i) {
-        widen_y<DT>(w, t + BLOCK * i, ry[i], &vy[i * VEC], tbeg, tend);
+        widen_zero<DT>(w, t + BLOCK * i, ry[i], &vy[i * VEC], tbeg, tend);
         s2.widen(w, t + BLOCK * i, rg[i], &vg[i * VEC]);
     }
     float dot = 0.0f;
@@ -210,7 +195,7 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_stream(const void* __restrict__ y
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float vy[VEC], vg[VEC];
-            widen_y<DT>(w, k0 + BLOCK * u, ry[u], vy, tbeg, tend);
+            widen_zero<DT>(w, k0 + BLOCK * u, ry[u], vy, tbeg, tend);
             s2.widen(w, k0 + BLOCK * u, rg[u], vg);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) dot = __builtin_fmaf(vy[e], vg[e], dot);
@@ -229,7 +214,7 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_stream(const void* __restrict__ y
             const int k = k0 + BLOCK * u;
             if (k < w.ngran) {
                 float vy[VEC], vg[VEC], o[VEC];
-                widen_y<DT>(w, k, ry[u], vy, tbeg, tend);
+                widen_zero<DT>(w, k, ry[u], vy, tbeg, tend);
                 s2.widen(w, k, rg[u], vg);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) o[e] = vy[e] * (vg[e] - dot);

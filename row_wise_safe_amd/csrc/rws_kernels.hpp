@@ -30,6 +30,22 @@ __device__ inline const char* tensor_end(const void* in, int64_t rows, int cols)
     return (const char*)in + rows * (int64_t)cols * Elem<DT>::SIZE;
 }
 
+// Values of a fetched granule with 0 (not -inf) outside the row: the form
+// that sums (dot products, moments) need.
+template <int DT, class Win>
+__device__ inline void widen_zero(const Win& w, int k, u32x4 raw, float* v, const char* tbeg,
+                                  const char* tend) {
+    w.widen(k, raw, v, tbeg, tend);
+    const int c0 = k * Elem<DT>::VEC - w.lead;
+    if (!(c0 >= 0 && c0 + Elem<DT>::VEC <= w.cols)) {
+#pragma unroll
+        for (int e = 0; e < Elem<DT>::VEC; ++e) {
+            const int c = c0 + e;
+            if (!(c >= 0 && c < w.cols)) v[e] = 0.0f;
+        }
+    }
+}
+
 // ===========================================================================
 // wave_row: G lanes per row, 64/G rows per wave "set", U sets per wave, K
 // granules per lane and row.  Lane gl of a group holds granules gl + G*i, so

@@ -93,6 +93,38 @@ extern const TwoPassVariant kBwdStream[];  // (threads, granules per thread per 
 extern const int kNumBwdStream;
 // family: 1 wave (kBwdWave), 2 block (kBwdBlock), 3 stream (kBwdStream)
 hipError_t launch_bwd(const BwdLaunch& B, int family, int variant);
+// Row normalisations (rws_norm.hpp).
+constexpr int kLayerNorm = 0;
+constexpr int kRmsNorm = 1;
+struct NormArgs {
+    const void* w;  // per-column weight (cols entries of the dtype) or nullptr
+    const void* b;  // per-column bias or nullptr (LayerNorm only)
+    float* mean;    // per-row mean out or nullptr (LayerNorm only)
+    float* rstd;    // per-row 1/sqrt(var + eps) out or nullptr
+    float eps;
+    float n;        // cols as a float
+};
+struct NormLaunch {
+    const void* in;
+    void* out;
+    int64_t rows;
+    int cols;
+    int dtype;
+    int mode;         // kLayerNorm / kRmsNorm
+    bool aligned;     // in, out 128-byte aligned and cols*size % 128 == 0
+    bool same_phase;  // (out - in) % 16 == 0
+    NormArgs args;    // mean/rstd already offset to the launch's first row
+    hipStream_t stream;
+};
+extern const WaveRowVariant kNormWave[];
+extern const int kNumNormWave;
+extern const TwoPassVariant kNormBlock[];   // (threads, register granules per thread)
+extern const int kNumNormBlock;
+extern const TwoPassVariant kNormStream[];  // (threads, granules per thread per batch)
+extern const int kNumNormStream;
+hipError_t launch_norm_wave(const NormLaunch& L, int variant);
+// family 2: block (kNormBlock), 3: stream (kNormStream)
+hipError_t launch_norm_block(const NormLaunch& L, int family, int variant);
 // n16 granules of 16 bytes.
 hipError_t launch_copy16(const void* in, void* out, int64_t n16, hipStream_t stream);
 

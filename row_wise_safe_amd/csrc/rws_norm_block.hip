@@ -1,0 +1,93 @@
+// rws_norm_block.hip -- instantiations and launchers of norm_block and
+// norm_stream (LayerNorm and RMSNorm with a workgroup per row, rws_norm.hpp).
+#include "rws_norm.hpp"
+
+namespace rws {
+
+// (threads, granules per thread held in registers)
+#define RWS_NORM_BLOCK_VARIANTS(X) \
+    X(256, 2)                      \
+    X(192, 3)                      \
+    X(256, 3)                      \
+    X(256, 4)                      \
+    X(512, 4)                      \
+    X(1024, 4)
+// (threads, granules per thread per batch)
+#define RWS_NORM_STREAM_VARIANTS(X) \
+    X(256, 4)                       \
+    X(1024, 4)
+
+#define RWS_ROW2(a, b) {a, b},
+const TwoPassVariant kNormBlock[] = {RWS_NORM_BLOCK_VARIANTS(RWS_ROW2)};
+const int kNumNormBlock = sizeof(kNormBlock) / sizeof(kNormBlock[0]);
+const TwoPassVariant kNormStream[] = {RWS_NORM_STREAM_VARIANTS(RWS_ROW2)};
+const int kNumNormStream = sizeof(kNormStream) / sizeof(kNormStream[0]);
+#undef RWS_ROW2
+
+template <int DT, bool AL, int BL, int KR, int MODE>
+static hipError_t nb_mode(const NormLaunch& L) {
+    const dim3 grid((unsigned)L.rows);
+    if (L.args.w || L.args.b)
+        hipLaunchKernelGGL((k_norm_block<DT, AL, BL, KR, MODE, true>), grid, dim3(BL), 0, L.stream,
+                           L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase);
+    else
+        hipLaunchKernelGGL((k_norm_block<DT, AL, BL, KR, MODE, false>), grid, dim3(BL), 0, L.stream,
+                           L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase);
+    return hipGetLastError();
+}
+
+template <int DT, bool AL, int BL, int KR>
+static hipError_t nb(const NormLaunch& L) {
+    return L.mode == kLayerNorm ? nb_mode<DT, AL, BL, KR, kLayerNorm>(L)
+                                : nb_mode<DT, AL, BL, KR, kRmsNorm>(L);
+}
+
+template <int DT, bool AL, int BL, int U, int MODE>
+static hipError_t ns_mode(const NormLaunch& L) {
+    const dim3 grid((unsigned)L.rows);
+    if (L.args.w || L.args.b)
+        hipLaunchKernelGGL((k_norm_stream<DT, AL, BL, U, MODE, true>), grid, dim3(BL), 0, L.stream,
+                           L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase);
+    else
+        hipLaunchKernelGGL((k_norm_stream<DT, AL, BL, U, MODE, false>), grid, dim3(BL), 0, L.stream,
+                           L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase);
+    return hipGetLastError();
+}
+
+template <int DT, bool AL, int BL, int U>
+static hipError_t ns(const NormLaunch& L) {
+    return L.mode == kLayerNorm ? ns_mode<DT, AL, BL, U, kLayerNorm>(L)
+                                : ns_mode<DT, AL, BL, U, kRmsNorm>(L);
+}
+
+#define RWS_NORM_DT_SWITCH(FN, A, B)                                                      \
+    switch (L.dtype) {                                                                    \
+        case kF32: return L.aligned ? FN<kF32, true, A, B>(L) : FN<kF32, false, A, B>(L);    \
+        case kF16: return L.aligned ? FN<kF16, true, A, B>(L) : FN<kF16, false, A, B>(L);    \
+        case kBF16: return L.aligned ? FN<kBF16, true, A, B>(L) : FN<kBF16, false, A, B>(L); \
+    }                                                                                     \
+    return hipErrorInvalidValue;
+
+hipError_t launch_norm_block(const NormLaunch& L, int family, int variant) {
+    int i = 0;
+    if (family == 2) {
+#define RWS_CASE(b, kr)                     \
+    if (variant == i) {                     \
+        RWS_NORM_DT_SWITCH(nb, b, kr)       \
+    }                                       \
+    ++i;
+        RWS_NORM_BLOCK_VARIANTS(RWS_CASE)
+#undef RWS_CASE
+    } else if (family == 3) {
+#define RWS_CASE(b, u)                      \
+    if (variant == i) {                     \
+        RWS_NORM_DT_SWITCH(ns, b, u)        \
+    }                                       \
+    ++i;
+        RWS_NORM_STREAM_VARIANTS(RWS_CASE)
+#undef RWS_CASE
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace rws

@@ -25,14 +25,15 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(softmax_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:softmax|layernorm|rmsnorm)_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("softmax_fwd", "softmax_fwd_kernel", "softmax_select_kernel",
               "softmax_describe_launch", "softmax_kernel_name", "softmax_status_string",
-              "softmax_last_error", "softmax_copy_bytes"):
+              "softmax_last_error", "softmax_copy_bytes", "layernorm_fwd", "rmsnorm_fwd",
+              "layernorm_fwd_kernel", "rmsnorm_fwd_kernel"):
         assert n in names
 
 
@@ -142,3 +143,31 @@ def test_backward_argument_checks(lib):
     assert rws.softmax_bwd(0, 0, 0, 0, 8, f16, 0) == rws.RWS_OK
     assert rws.softmax_bwd_kernel(256, 256, 256, 2, 8, f16, 0, 4) == rws.RWS_ERR_INVALID_ARG
     assert rws.softmax_bwd(256, 256, 256, 2, 8, 7, 0) == rws.RWS_ERR_UNSUPPORTED_DTYPE
+
+
+def test_norm_argument_checks(lib):
+    f16 = rws.RWS_F16
+    ok = rws.RWS_OK
+    assert rws.layernorm_fwd(256, 256, 2, 8, f16, -1.0, 0, 0, 0, 0, 0) == rws.RWS_ERR_INVALID_ARG
+    assert rws.layernorm_fwd(256, 256, 2, 8, f16, float("nan"), 0, 0, 0, 0, 0) == \
+        rws.RWS_ERR_INVALID_ARG
+    assert rws.layernorm_fwd(256, 256, 2, 8, f16, float("inf"), 0, 0, 0, 0, 0) == \
+        rws.RWS_ERR_INVALID_ARG
+    assert rws.layernorm_fwd(256, 256, 2, 8, f16, 1e-5, 257, 0, 0, 0, 0) == rws.RWS_ERR_MISALIGNED
+    assert rws.layernorm_fwd(256, 256, 2, 8, f16, 1e-5, 0, 259, 0, 0, 0) == rws.RWS_ERR_MISALIGNED
+    assert rws.layernorm_fwd(256, 256, 2, 8, f16, 1e-5, 0, 0, 258, 0, 0) == rws.RWS_ERR_MISALIGNED
+    assert rws.rmsnorm_fwd(256, 256, 2, 8, f16, 1e-5, 0, 2, 0) == rws.RWS_ERR_MISALIGNED
+    assert rws.layernorm_fwd(0, 0, 0, 8, f16, 1e-5, 0, 0, 0, 0, 0) == ok
+    assert rws.rmsnorm_fwd(0, 0, 3, 0, f16, 1e-5, 0, 0, 0) == ok
+    assert rws.layernorm_fwd(256, 256, 2, 8, 7, 1e-5, 0, 0, 0, 0, 0) == rws.RWS_ERR_UNSUPPORTED_DTYPE
+    assert rws.layernorm_fwd(0, 256, 2, 8, f16, 1e-5, 0, 0, 0, 0, 0) == rws.RWS_ERR_INVALID_ARG
+    for kid in (4, 5, 9, -1):
+        assert rws.layernorm_fwd_kernel(256, 256, 2, 8, f16, 1e-5, 0, 0, 0, 0, 0, kid) == \
+            rws.RWS_ERR_INVALID_ARG
+        assert rws.rmsnorm_fwd_kernel(256, 256, 2, 8, f16, 1e-5, 0, 0, 0, kid) == \
+            rws.RWS_ERR_INVALID_ARG
+    # rows too long for the register-held families are refused before any launch
+    assert rws.layernorm_fwd_kernel(256, 256, 2, 8192, f16, 1e-5, 0, 0, 0, 0, 0, 1) == \
+        rws.RWS_ERR_UNSUPPORTED_SHAPE
+    assert rws.rmsnorm_fwd_kernel(256, 256, 2, 70000, f16, 1e-5, 0, 0, 0, 2) == \
+        rws.RWS_ERR_UNSUPPORTED_SHAPE
