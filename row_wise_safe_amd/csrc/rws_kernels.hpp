@@ -46,6 +46,24 @@ __device__ inline void widen_zero(const Win& w, int k, u32x4 raw, float* v, cons
     }
 }
 
+// Issue the loads of input granule k and of its prologue operand, unless the
+// prologue says the granule cannot affect the result (then both stay zero and
+// the prologue overwrites the values).
+template <class Pre, class Win>
+__device__ inline void fetch_pre(const Pre& pre, const typename Pre::Ctx& pc, const Win& w, int k,
+                                 const char* tbeg, const char* tend, u32x4& raw, u32x4& praw) {
+    if (Pre::kActive) {
+        raw = u32x4{0u, 0u, 0u, 0u};
+        praw = u32x4{0u, 0u, 0u, 0u};
+        if (pre.needs_input(pc, w, k)) {
+            raw = w.fetch(k, tbeg, tend);
+            praw = pre.fetch(pc, w, k);
+        }
+    } else {
+        raw = w.fetch(k, tbeg, tend);
+    }
+}
+
 // ===========================================================================
 // wave_row: G lanes per row, 64/G rows per wave "set", U sets per wave, K
 // granules per lane and row.  Lane gl of a group holds granules gl + G*i, so
@@ -76,21 +94,19 @@ __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
     // lane groups of at least one cache line get line-aligned windows
     constexpr int WA = G * 16 >= kLineBytes ? kLineBytes : 16;
     RowWin<DT, ALIGNED, WA> w[U];
-    int64_t lrow[U];  // row each set loads (clamped to the last row)
+    typename Pre::Ctx pc[U];  // prologue context of the row each set loads
     u32x4 raw[U][K];
     u32x4 praw[Pre::kActive ? U : 1][Pre::kActive ? K : 1];  // prologue operands
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         int64_t row = row0 + u * RPS + sub;
         row = row < rows ? row : rows - 1;
-        lrow[u] = row;
         w[u] = RowWin<DT, ALIGNED, WA>(in, out, row, cols);
+        pc[u] = pre.ctx(row, w[u]);
 #pragma unroll
-        for (int i = 0; i < K; ++i) {
-            raw[u][i] = w[u].fetch(gl + G * i, tbeg, tend);
-            if (Pre::kActive) praw[Pre::kActive ? u : 0][Pre::kActive ? i : 0] =
-                pre.fetch(row, w[u], gl + G * i);
-        }
+        for (int i = 0; i < K; ++i)
+            fetch_pre(pre, pc[u], w[u], gl + G * i, tbeg, tend, raw[u][i],
+                      praw[Pre::kActive ? u : 0][Pre::kActive ? i : 0]);
     }
 
     float v[U][N];
@@ -100,7 +116,7 @@ __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
         for (int i = 0; i < K; ++i) {
             w[u].widen(gl + G * i, raw[u][i], &v[u][i * VEC], tbeg, tend, full);
             if (Pre::kActive)
-                pre.apply(lrow[u], w[u], gl + G * i, &v[u][i * VEC],
+                pre.apply(pc[u], w[u], gl + G * i, &v[u][i * VEC],
                           praw[Pre::kActive ? u : 0][Pre::kActive ? i : 0]);
         }
         float mx = v[u][0];
@@ -155,14 +171,13 @@ __global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict_
     const char* tbeg = (const char*)in;
     const char* tend = tensor_end<DT>(in, rows, cols);
     const RowWin<DT, ALIGNED> w(in, out, row, cols);
+    const typename Pre::Ctx pc = pre.ctx(row, w);
 
     u32x4 raw[KR];
     u32x4 praw[Pre::kActive ? KR : 1];  // prologue operands
 #pragma unroll
-    for (int i = 0; i < KR; ++i) {
-        raw[i] = w.fetch(t + BLOCK * i, tbeg, tend);
-        if (Pre::kActive) praw[Pre::kActive ? i : 0] = pre.fetch(row, w, t + BLOCK * i);
-    }
+    for (int i = 0; i < KR; ++i)
+        fetch_pre(pre, pc, w, t + BLOCK * i, tbeg, tend, raw[i], praw[Pre::kActive ? i : 0]);
     u32x4 rawl[KL > 0 ? KL : 1];
 #pragma unroll
     for (int j = 0; j < KL; ++j) {
@@ -174,7 +189,7 @@ __global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict_
 #pragma unroll
     for (int i = 0; i < KR; ++i) {
         w.widen(t + BLOCK * i, raw[i], &v[i * VEC], tbeg, tend);
-        if (Pre::kActive) pre.apply(row, w, t + BLOCK * i, &v[i * VEC], praw[Pre::kActive ? i : 0]);
+        if (Pre::kActive) pre.apply(pc, w, t + BLOCK * i, &v[i * VEC], praw[Pre::kActive ? i : 0]);
     }
     float mx = kNegInf;
 #pragma unroll
@@ -289,16 +304,15 @@ __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
     const char* tbeg = (const char*)in;
     const char* tend = tensor_end<DT>(in, rows, cols);
     const RowWin<DT, ALIGNED> w(in, out, row, cols);
+    const typename Pre::Ctx pc = pre.ctx(row, w);
 
     float m = kNegInf, d = 0.0f;
     for (int k0 = t; k0 < w.ngran; k0 += BLOCK * U) {
         u32x4 raw[U];
         u32x4 praw[Pre::kActive ? U : 1];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            raw[u] = w.fetch(k0 + BLOCK * u, tbeg, tend);
-            if (Pre::kActive) praw[Pre::kActive ? u : 0] = pre.fetch(row, w, k0 + BLOCK * u);
-        }
+        for (int u = 0; u < U; ++u)
+            fetch_pre(pre, pc, w, k0 + BLOCK * u, tbeg, tend, raw[u], praw[Pre::kActive ? u : 0]);
         float v[U * VEC];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -308,7 +322,7 @@ __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) v[u * VEC + e] = kNegInf;
             }
-            if (Pre::kActive) pre.apply(row, w, k, &v[u * VEC], praw[Pre::kActive ? u : 0]);
+            if (Pre::kActive) pre.apply(pc, w, k, &v[u * VEC], praw[Pre::kActive ? u : 0]);
         }
         online_update(m, d, v);
     }
@@ -321,17 +335,15 @@ __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
         u32x4 raw[U];
         u32x4 praw[Pre::kActive ? U : 1];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            raw[u] = w.fetch(k0 + BLOCK * u, tbeg, tend);
-            if (Pre::kActive) praw[Pre::kActive ? u : 0] = pre.fetch(row, w, k0 + BLOCK * u);
-        }
+        for (int u = 0; u < U; ++u)
+            fetch_pre(pre, pc, w, k0 + BLOCK * u, tbeg, tend, raw[u], praw[Pre::kActive ? u : 0]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k = k0 + BLOCK * u;
             if (k < w.ngran) {
                 float f[VEC];
                 w.widen(k, raw[u], f, tbeg, tend);
-                if (Pre::kActive) pre.apply(row, w, k, f, praw[Pre::kActive ? u : 0]);
+                if (Pre::kActive) pre.apply(pc, w, k, f, praw[Pre::kActive ? u : 0]);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) f[e] = er.one(f[e]) * r;
                 w.store(k, f, same_phase != 0);

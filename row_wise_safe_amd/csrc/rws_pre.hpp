@@ -8,15 +8,36 @@
 
 namespace rws {
 
+// Interface.  ctx() computes what a prologue needs per row, once per row;
+// fetch() issues the prologue operand's load for granule k; apply() rewrites
+// the widened values; needs_input() says whether granule k of the input can
+// affect the result at all (a granule wholly past the causal limit becomes
+// -inf whatever it holds, so its load is skipped).
 struct NoPre {
     static constexpr bool kActive = false;
+    struct Ctx {};
     template <class Win>
-    __device__ inline u32x4 fetch(int64_t, const Win&, int) const {
+    __device__ inline Ctx ctx(int64_t, const Win&) const {
+        return Ctx{};
+    }
+    template <class Win>
+    __device__ inline bool needs_input(const Ctx&, const Win&, int) const {
+        return true;
+    }
+    template <class Win>
+    __device__ inline u32x4 fetch(const Ctx&, const Win&, int) const {
         return u32x4{0u, 0u, 0u, 0u};
     }
     template <class Win>
-    __device__ inline void apply(int64_t, const Win&, int, float*, u32x4) const {}
+    __device__ inline void apply(const Ctx&, const Win&, int, float*, u32x4) const {}
 };
+
+// r mod d for r >= 0, d > 0; 32-bit division when both fit (the 64-bit one
+// is a long emulated sequence on the scalar unit).
+__device__ inline int64_t row_mod(int64_t r, int64_t d) {
+    if ((((uint64_t)r | (uint64_t)d) >> 32) == 0) return (int64_t)((uint32_t)r % (uint32_t)d);
+    return r % d;
+}
 
 // z = scale * x + mask[row % mask_rows, c]; columns past the causal limit
 // (c > (row % causal_q) + cols - causal_q, when causal_q > 0) and slots
@@ -34,60 +55,74 @@ struct MaskPre {
     int64_t causal_q;   // 0: no causal limit
     int64_t row_base;   // global index of the launch's first row
 
+    struct Ctx {
+        const char* mrow;  // the row's mask row (nullptr: no mask)
+        bool mvec;         // mask row has the input row's 16-byte phase
+        int limit;         // last column that takes part
+    };
+
     template <class Win>
-    __device__ inline const char* mask_row(int64_t lrow, const Win& w) const {
-        return mask + ((row_base + lrow) % mask_rows) * (int64_t)w.cols * Elem<DT>::SIZE;
+    __device__ inline Ctx ctx(int64_t lrow, const Win& w) const {
+        const int64_t row = row_base + lrow;
+        Ctx c;
+        c.mrow = nullptr;
+        c.mvec = false;
+        if (mask) {
+            c.mrow = mask + row_mod(row, mask_rows) * (int64_t)w.cols * Elem<DT>::SIZE;
+            const char* xrow = w.gin + (int64_t)w.lead * Elem<DT>::SIZE;  // the input row start
+            c.mvec = (((uintptr_t)c.mrow - (uintptr_t)xrow) & 15u) == 0;
+        }
+        c.limit = w.cols - 1;
+        if (causal_q > 0) c.limit = (int)row_mod(row, causal_q) + w.cols - (int)causal_q;
+        return c;
     }
+
+    // false when every column of granule k is past the causal limit: the
+    // prologue then sets the whole granule to -inf, so neither the input nor
+    // the mask granule is read (about half of a square causal score matrix).
     template <class Win>
-    __device__ inline bool vector_ok(const char* mrow, const Win& w, int c0) const {
-        const char* xrow = w.gin + (int64_t)w.lead * Elem<DT>::SIZE;  // the input row start
-        return c0 >= 0 && c0 + Elem<DT>::VEC <= w.cols &&
-               (((uintptr_t)mrow - (uintptr_t)xrow) & 15u) == 0;
+    __device__ inline bool needs_input(const Ctx& c, const Win& w, int k) const {
+        return k * Elem<DT>::VEC - w.lead <= c.limit;
     }
 
     template <class Win>
-    __device__ inline u32x4 fetch(int64_t lrow, const Win& w, int k) const {
+    __device__ inline u32x4 fetch(const Ctx& c, const Win& w, int k) const {
         u32x4 g = {0u, 0u, 0u, 0u};
-        if (mask) {
-            const char* mrow = mask_row(lrow, w);
-            const int c0 = k * Elem<DT>::VEC - w.lead;
-            if (vector_ok(mrow, w, c0)) g = *(const u32x4*)(mrow + (int64_t)c0 * Elem<DT>::SIZE);
-        }
+        const int c0 = k * Elem<DT>::VEC - w.lead;
+        if (c.mrow && c.mvec && c0 >= 0 && c0 + Elem<DT>::VEC <= w.cols)
+            g = *(const u32x4*)(c.mrow + (int64_t)c0 * Elem<DT>::SIZE);
         return g;
     }
 
     template <class Win>
-    __device__ inline void apply(int64_t lrow, const Win& w, int k, float* v, u32x4 mraw) const {
+    __device__ inline void apply(const Ctx& c, const Win& w, int k, float* v, u32x4 mraw) const {
         constexpr int VEC = Elem<DT>::VEC;
         constexpr int ES = Elem<DT>::SIZE;
-        const int64_t row = row_base + lrow;
         const int c0 = k * VEC - w.lead;
-        int limit = w.cols - 1;
-        if (causal_q > 0) limit = (int)(row % causal_q) + w.cols - (int)causal_q;
+        const bool inside = c0 >= 0 && c0 + VEC <= w.cols;
         float mv[VEC];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) mv[e] = 0.0f;
-        if (mask) {
-            const char* mrow = mask_row(lrow, w);
-            if (vector_ok(mrow, w, c0)) {
+        if (c.mrow) {
+            if (c.mvec && inside) {
                 Elem<DT>::widen(mraw, mv);
             } else {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    const int c = c0 + e;
-                    if (c >= 0 && c < w.cols) mv[e] = Elem<DT>::load1(mrow + (int64_t)c * ES);
+                    const int col = c0 + e;
+                    if (col >= 0 && col < w.cols) mv[e] = Elem<DT>::load1(c.mrow + (int64_t)col * ES);
                 }
             }
         }
-        if (c0 >= 0 && c0 + VEC - 1 <= limit && c0 + VEC <= w.cols) {
+        if (inside && c0 + VEC - 1 <= c.limit) {
             // the whole granule is inside the row and the causal limit
 #pragma unroll
             for (int e = 0; e < VEC; ++e) v[e] = __builtin_fmaf(scale, v[e], mv[e]);
         } else {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const int c = c0 + e;
-                const bool ok = c >= 0 && c <= limit && c < w.cols;
+                const int col = c0 + e;
+                const bool ok = col >= 0 && col <= c.limit && col < w.cols;
                 v[e] = ok ? __builtin_fmaf(scale, v[e], mv[e]) : kNegInf;
             }
         }
