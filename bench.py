@@ -410,7 +410,10 @@ def main() -> int:
                else cpu_baseline(w, stored, args.cpu_seconds))
         log(f"[bench] cpu oracle {cpu['value']} GB/s on {cpu['cores']} threads")
 
-    traffic = read_traffic(w.name, family) if family else None
+    # Counter summaries exist for the plain forward kernels only (a masked or
+    # backward launch of the same family is a different kernel).
+    plain = family and mask is None and dys is None
+    traffic = read_traffic(w.name, family) if plain else None
     achieved = nbytes / (ms * 1e-3) / 1e9
     vs = round(gbps / PAGES_FP16_ATTN_GBPS, 3) if w.name == "fp16_attn_4x32x512x512" else None
     if mask is not None or dys is not None:
