@@ -38,21 +38,28 @@ PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 # fp16 [4,32,512,512] on a 60-CU DCU (DCU case-study page, section 5.3),
 # i.e. 134217728 B / 0.62 ms.  Another machine: context only.
 PAGES_FP16_ATTN_GBPS = 134217728 / 0.62e-3 / 1e9
-# Sources that define each family's kernels (the copy kernel used for the
-# counter calibration lives in rws_splitk.hip): a profile summary is valid
-# while these are unchanged.
+# Profile summaries live in profiles/<key>_<workload>.txt.  The key is the
+# kernel family for plain softmax, else the operation.  A summary is valid
+# while the sources that define its kernels are unchanged (the copy kernel
+# used for the counter calibration lives in rws_splitk.hip).
+_SOFTMAX_COMMON = ["rws_device.hpp", "rws_pre.hpp", "rws_kernels.hpp", "rws_splitk.hip"]
 KERNEL_SOURCES = {
-    "wave_row": ["rws_device.hpp", "rws_kernels.hpp", "rws_wave_row.hip", "rws_splitk.hip"],
-    "block_onepass": ["rws_device.hpp", "rws_kernels.hpp", "rws_block_onepass.hip",
-                      "rws_splitk.hip"],
-    "two_pass": ["rws_device.hpp", "rws_kernels.hpp", "rws_two_pass.hip", "rws_splitk.hip"],
-    "splitk": ["rws_device.hpp", "rws_kernels.hpp", "rws_splitk.hip"],
-    "splitk_fused": ["rws_device.hpp", "rws_kernels.hpp", "rws_splitk_fused.hip",
-                     "rws_splitk.hip"],
+    "wave_row": _SOFTMAX_COMMON + ["rws_wave_row.hip"],
+    "block_onepass": _SOFTMAX_COMMON + ["rws_block_onepass.hip"],
+    "two_pass": _SOFTMAX_COMMON + ["rws_two_pass.hip"],
+    "splitk": _SOFTMAX_COMMON,
+    "splitk_fused": _SOFTMAX_COMMON + ["rws_splitk_fused.hip"],
+    "masked": _SOFTMAX_COMMON + ["rws_masked.hip"],
+    "backward": _SOFTMAX_COMMON + ["rws_backward.hip"],
+    "layernorm": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_norm.hpp", "rws_norm_wave.hip",
+                                    "rws_norm_block.hip"],
 }
+KERNEL_SOURCES["rmsnorm"] = KERNEL_SOURCES["layernorm"]
+# Substring that names the step's kernels in a trace.
 KERNEL_SYMBOL = {"wave_row": "k_wave_row", "block_onepass": "k_block_onepass",
                  "two_pass": "k_two_pass", "splitk": "k_splitk_stage",
-                 "splitk_fused": "k_splitk_fused"}
+                 "splitk_fused": "k_splitk_fused", "masked": "MaskPre", "backward": "k_bwd_",
+                 "layernorm": "k_norm_", "rmsnorm": "k_norm_"}
 
 
 def kernel_source_hash(family: str) -> str:
@@ -243,7 +250,10 @@ def main() -> int:
                     help="skip the single-buffer figure (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--meta-out", default=None, help="write bench metadata JSON (for rocprof)")
-    ap.add_argument("--summarize-rocprof", default=None, metavar="DIR")
+    ap.add_argument("--summarize-rocprof", default=None, metavar="DIR",
+                    help="write profiles/<key>_<workload>.txt from rocprofv3 output; --kernel "
+                         "names the key (a softmax family, or masked, backward, layernorm, "
+                         "rmsnorm)")
     ap.add_argument("--profile-command", default="")
     args = ap.parse_args()
 
@@ -299,7 +309,6 @@ def main() -> int:
     family = desc.split("<")[0]
     if args.norm:
         desc = f"{args.norm} {args.kernel}"
-        family = None
     dys = None
     if args.backward:
         # y = the forward output of each input, dy ~ N(0, 1); dx goes to ys[i]
@@ -410,10 +419,9 @@ def main() -> int:
                else cpu_baseline(w, stored, args.cpu_seconds))
         log(f"[bench] cpu oracle {cpu['value']} GB/s on {cpu['cores']} threads")
 
-    # Counter summaries exist for the plain forward kernels only (a masked or
-    # backward launch of the same family is a different kernel).
-    plain = family and mask is None and dys is None
-    traffic = read_traffic(w.name, family) if plain else None
+    profile_key = (args.norm if args.norm else "masked" if mask is not None
+                   else "backward" if dys is not None else family)
+    traffic = read_traffic(w.name, profile_key)
     achieved = nbytes / (ms * 1e-3) / 1e9
     vs = round(gbps / PAGES_FP16_ATTN_GBPS, 3) if w.name == "fp16_attn_4x32x512x512" else None
     if mask is not None or dys is not None:
