@@ -370,13 +370,16 @@ struct WorkspaceReaper {
 
 // Grow-only workspace of (device, stream): `bytes` of partials and, when
 // sync_rows > 0, kSyncWordsPerRow*sync_rows zeroed counter words.  Returns the epoch for a
-// single-launch call in *epoch (when epoch != nullptr).
+// single-launch call in *epoch (when epoch != nullptr).  The caller holds
+// g_ws_mu from this call until its launches are enqueued: a call from another
+// host thread on the same stream that grows the buffer synchronises the
+// stream and frees the old one, which is only safe once every launch that
+// uses it is on the stream.
 int get_workspace(hipStream_t stream, size_t bytes, int64_t sync_rows, void** out,
                   unsigned** sync, unsigned* epoch) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(RWS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
-    std::lock_guard<std::mutex> lock(g_ws_mu);
     if (!g_ws) g_ws = new std::map<std::pair<int, hipStream_t>, Workspace>();
     Workspace& w = (*g_ws)[std::make_pair(dev, stream)];
     const bool grow_partials = w.bytes < bytes;
@@ -454,6 +457,9 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
     unsigned* sync = nullptr;
     unsigned epoch = 0;
     hipStream_t s = (hipStream_t)stream;
+    // split-k: keep the workspace locked until this call's launches are enqueued
+    std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
+    if (p.family == RWS_KERNEL_SPLITK || p.family == RWS_KERNEL_SPLITK_FUSED) ws_lock.lock();
     if (p.family == RWS_KERNEL_SPLITK) {
         const int64_t batch = std::min<int64_t>(rows, p.max_rows_per_launch);
         st = get_workspace(s, (size_t)batch * p.P * sizeof(float2), 0, &ws, nullptr, nullptr);
