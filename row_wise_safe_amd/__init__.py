@@ -226,7 +226,8 @@ def softmax(x: torch.Tensor, out: torch.Tensor | None = None, kernel: str = "aut
     ``kernel`` forces a family (``"wave_row"``, ``"block_onepass"``,
     ``"two_pass"``, ``"splitk"``, ``"splitk_fused"``) instead of the
     dispatcher's choice.
-    Work is enqueued on ``stream`` (default: the current stream).
+    Work is enqueued on ``stream`` (default: the current stream of x's
+    device); the call runs with x's device current, as the C ABI requires.
     """
     if not x.is_cuda:
         raise ValueError("x must be a GPU tensor")
@@ -240,8 +241,10 @@ def softmax(x: torch.Tensor, out: torch.Tensor | None = None, kernel: str = "aut
         raise ValueError("out must be a contiguous tensor of x's shape, dtype and device")
     cols = x.shape[-1] if x.dim() > 0 else 1
     rows = x.numel() // cols if cols > 0 else 0
-    st = load_library().softmax_fwd_kernel(x.data_ptr(), out.data_ptr(), rows, cols, code,
-                                           _stream_handle(x.device, stream), KERNEL_IDS[kernel])
+    with torch.cuda.device(x.device):
+        st = load_library().softmax_fwd_kernel(x.data_ptr(), out.data_ptr(), rows, cols, code,
+                                               _stream_handle(x.device, stream),
+                                               KERNEL_IDS[kernel])
     if st != RWS_OK:
         raise SoftmaxError(st, softmax_last_error())
     return out
@@ -272,9 +275,11 @@ def softmax_masked(x: torch.Tensor, scale: float = 1.0, mask: torch.Tensor | Non
                 mask.device != x.device:
             raise ValueError("mask must be contiguous, on x's device, with x's dtype and columns")
         mask_ptr, mask_rows = mask.data_ptr(), mask.numel() // cols
-    st = load_library().softmax_fwd_masked(x.data_ptr(), out.data_ptr(), rows, cols, code,
-                                           float(scale), mask_ptr, mask_rows, int(causal_q),
-                                           _stream_handle(x.device, stream), KERNEL_IDS[kernel])
+    with torch.cuda.device(x.device):
+        st = load_library().softmax_fwd_masked(x.data_ptr(), out.data_ptr(), rows, cols, code,
+                                               float(scale), mask_ptr, mask_rows, int(causal_q),
+                                               _stream_handle(x.device, stream),
+                                               KERNEL_IDS[kernel])
     if st != RWS_OK:
         raise SoftmaxError(st, softmax_last_error())
     return out
@@ -296,9 +301,12 @@ def softmax_backward(y: torch.Tensor, dy: torch.Tensor, out: torch.Tensor | None
         raise ValueError("out must be a contiguous tensor of y's shape and dtype")
     cols = y.shape[-1] if y.dim() > 0 else 1
     rows = y.numel() // cols if cols > 0 else 0
-    st = load_library().softmax_bwd_kernel(y.data_ptr(), dy.data_ptr(), out.data_ptr(), rows, cols,
-                                           code, _stream_handle(y.device, stream),
-                                           KERNEL_IDS[kernel])
+    if dy.device != y.device or out.device != y.device:
+        raise ValueError("y, dy and out must be on the same device")
+    with torch.cuda.device(y.device):
+        st = load_library().softmax_bwd_kernel(y.data_ptr(), dy.data_ptr(), out.data_ptr(), rows,
+                                               cols, code, _stream_handle(y.device, stream),
+                                               KERNEL_IDS[kernel])
     if st != RWS_OK:
         raise SoftmaxError(st, softmax_last_error())
     return out
@@ -348,9 +356,11 @@ def layer_norm(x: torch.Tensor, eps: float = 1e-5, weight: torch.Tensor | None =
     code, out, rows, cols, wp, bp = _norm_operands(x, out, weight, bias)
     mp = _stats_out(mean, rows, x.device, "mean")
     rp = _stats_out(rstd, rows, x.device, "rstd")
-    st = load_library().layernorm_fwd_kernel(x.data_ptr(), out.data_ptr(), rows, cols, code,
-                                             float(eps), wp, bp, mp, rp,
-                                             _stream_handle(x.device, stream), KERNEL_IDS[kernel])
+    with torch.cuda.device(x.device):
+        st = load_library().layernorm_fwd_kernel(x.data_ptr(), out.data_ptr(), rows, cols, code,
+                                                 float(eps), wp, bp, mp, rp,
+                                                 _stream_handle(x.device, stream),
+                                                 KERNEL_IDS[kernel])
     if st != RWS_OK:
         raise SoftmaxError(st, softmax_last_error())
     return out
@@ -362,9 +372,11 @@ def rms_norm(x: torch.Tensor, eps: float = 1e-5, weight: torch.Tensor | None = N
     """RMSNorm of ``x`` along its last dimension: x / sqrt(mean(x^2) + eps) * weight."""
     code, out, rows, cols, wp, _ = _norm_operands(x, out, weight, None)
     rp = _stats_out(rstd, rows, x.device, "rstd")
-    st = load_library().rmsnorm_fwd_kernel(x.data_ptr(), out.data_ptr(), rows, cols, code,
-                                           float(eps), wp, rp, _stream_handle(x.device, stream),
-                                           KERNEL_IDS[kernel])
+    with torch.cuda.device(x.device):
+        st = load_library().rmsnorm_fwd_kernel(x.data_ptr(), out.data_ptr(), rows, cols, code,
+                                               float(eps), wp, rp,
+                                               _stream_handle(x.device, stream),
+                                               KERNEL_IDS[kernel])
     if st != RWS_OK:
         raise SoftmaxError(st, softmax_last_error())
     return out
@@ -375,8 +387,9 @@ def copy_bytes(src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tenso
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("dst is smaller than src")
-    st = load_library().softmax_copy_bytes(src.data_ptr(), dst.data_ptr(), nbytes,
-                                           _stream_handle(src.device, stream))
+    with torch.cuda.device(src.device):
+        st = load_library().softmax_copy_bytes(src.data_ptr(), dst.data_ptr(), nbytes,
+                                               _stream_handle(src.device, stream))
     if st != RWS_OK:
         raise SoftmaxError(st, softmax_last_error())
     return dst

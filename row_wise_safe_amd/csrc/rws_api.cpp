@@ -149,23 +149,27 @@ int pick_onepass(int64_t w, bool regs_only = false) {
     return best;
 }
 
-// Split-k chunking: the largest chunk that still gives every CU at least two
-// workgroups, else the smallest chunk.
+// Split-k chunking: the largest chunk that still gives every CU eight
+// workgroups, else two, else the smallest chunk.  Measured on fp16
+// [16, 1048576]: 2048 workgroups of 256x4 granules 14.8-15.0 us, 1024 of
+// 256x8 15.1-15.2 us, 4096 of 256x2 17.6 us, 512 of 256x16 18.0 us.
 int pick_splitk(int64_t rows, int64_t wmax, int cus, int* P_out) {
     int best = -1;
     int bestP = 1;
-    for (int i = 0; i < rws::kNumSplitk; ++i) {
-        const rws::SplitkVariant& v = rws::kSplitk[i];
-        if (v.block != 256) continue;
-        const int64_t cg = (int64_t)v.block * v.kc;
-        const int64_t P = (wmax + cg - 1) / cg;
-        if (P > (1 << 20)) continue;
-        if (rows * P >= 2LL * cus) {
-            if (best < 0 || rws::kSplitk[i].kc > rws::kSplitk[best].kc) {
+    for (const int per_cu : {8, 2}) {
+        for (int i = 0; i < rws::kNumSplitk; ++i) {
+            const rws::SplitkVariant& v = rws::kSplitk[i];
+            if (v.block != 256) continue;
+            const int64_t cg = (int64_t)v.block * v.kc;
+            const int64_t P = (wmax + cg - 1) / cg;
+            if (P > (1 << 20)) continue;
+            if (rows * P >= (int64_t)per_cu * cus &&
+                (best < 0 || rws::kSplitk[i].kc > rws::kSplitk[best].kc)) {
                 best = i;
                 bestP = (int)P;
             }
         }
+        if (best >= 0) break;
     }
     if (best < 0) {
         for (int i = 0; i < rws::kNumSplitk; ++i) {
@@ -651,7 +655,23 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
         return fail(RWS_ERR_MISALIGNED, "mean/rstd not aligned to 4 bytes");
     const Geometry g = geometry(cols, dtype, in, out);
     const int64_t wline = window_granules(g, 128);
+    // Lane groups measured on MI355X (fp16 LayerNorm / RMSNorm, rotating
+    // buffers): windows of 9-32 granules take (16,2,1) ([131040,192]: 17.9 us,
+    // (8,3,1) 18.3 us, (32,1,1) 21.5 us), windows of 33-48 take (8,6,1)
+    // ([32760,384]: 9.0 us, (16,3,1) 10.2 us, (64,1,1) 11.4 us); other
+    // lengths the narrowest group that holds the window.
+    auto norm_variant = [&](int G, int K, int U) {
+        for (int i = 0; i < rws::kNumNormWave; ++i) {
+            const rws::WaveRowVariant& v = rws::kNormWave[i];
+            if (v.G == G && v.K == K && v.U == U &&
+                (int64_t)G * K >= window_granules(g, wave_row_wa(v)))
+                return i;
+        }
+        return -1;
+    };
     auto pick_wave = [&]() {
+        if (wline > 8 && wline <= 32 && norm_variant(16, 2, 1) >= 0) return norm_variant(16, 2, 1);
+        if (wline > 32 && wline <= 48 && norm_variant(8, 6, 1) >= 0) return norm_variant(8, 6, 1);
         int best = -1;
         int64_t best_key = 0;
         for (int i = 0; i < rws::kNumNormWave; ++i) {

@@ -110,33 +110,33 @@ __device__ inline void norm_store(const Win& w, int k0, int stride, const float*
                 w.store(k, o, same_phase);
             }
         }
-        return;
     } else {
-    const ColParam<DT, Win> pw(A.w, w), pb(A.b, w);
-    u32x4 rw[KG], rb[KG];
+        const ColParam<DT, Win> pw(A.w, w), pb(A.b, w);
+        u32x4 rw[KG], rb[KG];
 #pragma unroll
-    for (int i = 0; i < KG; ++i) {
-        const int k = k0 + stride * i;
-        rw[i] = A.w ? pw.fetch(w, k) : u32x4{0u, 0u, 0u, 0u};
-        rb[i] = A.b ? pb.fetch(w, k) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < KG; ++i) {
-        const int k = k0 + stride * i;
-        if (k < w.ngran) {
-            float fw[VEC], fb[VEC], o[VEC];
-            if (A.w) pw.widen(w, k, rw[i], fw);
-            if (A.b) pb.widen(w, k, rb[i], fb);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                float t = MODE == kLayerNorm ? (v[i * VEC + e] - mu) * rstd : v[i * VEC + e] * rstd;
-                if (A.w) t *= fw[e];
-                if (A.b) t += fb[e];
-                o[e] = t;
-            }
-            w.store(k, o, same_phase);
+        for (int i = 0; i < KG; ++i) {
+            const int k = k0 + stride * i;
+            rw[i] = A.w ? pw.fetch(w, k) : u32x4{0u, 0u, 0u, 0u};
+            rb[i] = A.b ? pb.fetch(w, k) : u32x4{0u, 0u, 0u, 0u};
         }
-    }
+#pragma unroll
+        for (int i = 0; i < KG; ++i) {
+            const int k = k0 + stride * i;
+            if (k < w.ngran) {
+                float fw[VEC], fb[VEC], o[VEC];
+                if (A.w) pw.widen(w, k, rw[i], fw);
+                if (A.b) pb.widen(w, k, rb[i], fb);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    float t = MODE == kLayerNorm ? (v[i * VEC + e] - mu) * rstd
+                                                 : v[i * VEC + e] * rstd;
+                    if (A.w) t *= fw[e];
+                    if (A.b) t += fb[e];
+                    o[e] = t;
+                }
+                w.store(k, o, same_phase);
+            }
+        }
     }
 }
 

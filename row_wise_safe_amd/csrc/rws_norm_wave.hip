@@ -5,14 +5,15 @@
 namespace rws {
 
 // (lanes per row G, granules per lane K, row sets per wave U).  G*K
-// granules of 16 bytes hold the row window; (8,3) and (16,3) fit the fp16
-// widths 192 and 384 (24 and 48 granules) without idle lanes.
+// granules of 16 bytes hold the row window.  (16,2) and (8,6) are the
+// measured choices for windows of 9-32 and 33-48 granules (the fp16 widths
+// 192 and 384); the others are the narrowest group for the other lengths.
 #define RWS_NORM_WAVE_VARIANTS(X) \
     X(4, 1, 1)                    \
     X(8, 1, 1)                    \
-    X(8, 3, 1)                    \
     X(16, 1, 1)                   \
-    X(16, 3, 1)                   \
+    X(16, 2, 1)                   \
+    X(8, 6, 1)                    \
     X(32, 1, 1)                   \
     X(64, 1, 1)                   \
     X(64, 1, 2)                   \
