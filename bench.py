@@ -43,13 +43,15 @@ PAGES_FP16_ATTN_GBPS = 134217728 / 0.62e-3 / 1e9
 # kernel family for plain softmax, else the operation.  A summary is valid
 # while the sources that define its kernels are unchanged (the copy kernel
 # used for the counter calibration lives in rws_splitk.hip).
-_SOFTMAX_COMMON = ["rws_device.hpp", "rws_pre.hpp", "rws_kernels.hpp", "rws_splitk.hip"]
+_SOFTMAX_COMMON = ["rws_device.hpp", "rws_pre.hpp", "rws_kernels.hpp", "rws_variants.hpp",
+                   "rws_splitk.hip"]
 KERNEL_SOURCES = {
     "wave_row": _SOFTMAX_COMMON + ["rws_wave_row.hip"],
     "block_onepass": _SOFTMAX_COMMON + ["rws_block_onepass.hip"],
     "two_pass": _SOFTMAX_COMMON + ["rws_two_pass.hip"],
     "splitk": _SOFTMAX_COMMON,
     "splitk_fused": _SOFTMAX_COMMON + ["rws_splitk_fused.hip"],
+    "splitk_ordered": _SOFTMAX_COMMON + ["rws_splitk_ordered.hip"],
     "masked": _SOFTMAX_COMMON + ["rws_masked.hip"],
     "backward": _SOFTMAX_COMMON + ["rws_backward.hip"],
     "layernorm": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_norm.hpp", "rws_norm_wave.hip",
@@ -59,7 +61,8 @@ KERNEL_SOURCES["rmsnorm"] = KERNEL_SOURCES["layernorm"]
 # Substring that names the step's kernels in a trace.
 KERNEL_SYMBOL = {"wave_row": "k_wave_row", "block_onepass": "k_block_onepass",
                  "two_pass": "k_two_pass", "splitk": "k_splitk_stage",
-                 "splitk_fused": "k_splitk_fused", "masked": "MaskPre", "backward": "k_bwd_",
+                 "splitk_fused": "k_splitk_fused", "splitk_ordered": "k_splitk_ordered",
+                 "masked": "MaskPre", "backward": "k_bwd_",
                  "layernorm": "k_norm_", "rmsnorm": "k_norm_"}
 
 

@@ -37,12 +37,14 @@
  * The result is valid once the stream reaches the enqueued work.
  *
  * Ownership.  The caller owns `in` and `out`.  For the split-k paths the
- * library owns a small workspace (8 bytes per row per chunk, plus 256 bytes
- * per row of arrival counters for the single-launch form) that it keeps per
- * (device, stream) and grows on demand; the first call that needs a larger
- * workspace allocates it (hipMalloc; counters are zeroed once then), later
- * calls reuse it.  Calls on one stream are ordered, so reuse is safe; the
- * workspaces are released when the library is unloaded.
+ * library owns a small workspace (8 bytes per row per chunk for the two-launch
+ * form, 16 bytes per row per chunk of epoch-tagged words for the ordered
+ * single launch, plus 256 bytes per row of arrival counters for the
+ * cooperative form) that it keeps per (device, stream) and grows on demand;
+ * the first call that needs a larger workspace allocates it (hipMalloc;
+ * counters and tag words are zeroed then, the tag words by a kernel on the
+ * call's stream), later calls reuse it.  Calls on one stream are ordered, so
+ * reuse is safe; the workspaces are released when the library is unloaded.
  *
  * Errors.  Every entry point returns a status code (below) and never exits or
  * throws.  rows == 0 or cols == 0 is a successful no-op.  A HIP launch error
@@ -93,7 +95,7 @@ enum {
                                  partial (m, d) per chunk, stage 2 merges a
                                  row's partials and writes the outputs (CUDA
                                  safe-online-softmax page, section 3.2) */
-    RWS_KERNEL_SPLITK_FUSED = 5 /* split-k in one cooperative launch: each
+    RWS_KERNEL_SPLITK_FUSED = 5, /* split-k in one cooperative launch: each
                                  workgroup keeps its chunk in registers, the
                                  row's workgroups exchange partial (m, d) through
                                  memory and a per-row arrival counter, so the
@@ -104,6 +106,19 @@ enum {
                                  by the dispatcher: on MI355X its cross-XCD
                                  synchronisation costs more than the re-read
                                  it saves */
+    RWS_KERNEL_SPLITK_ORDERED = 6 /* split-k in one ordinary launch: the
+                                 stage-1 workgroups (partial (m, d) per chunk)
+                                 come first in the grid, the stage-2
+                                 workgroups (merge, re-read, write) after
+                                 them and poll the row's partials, which
+                                 travel as epoch-tagged 64-bit words (no grid
+                                 barrier, no memory fence; the single-kernel
+                                 form the same page, section 3.2, mentions).
+                                 Relies on workgroups being dispatched in
+                                 increasing index order; a wait that runs
+                                 out of its bound writes NaN for its chunk
+                                 instead of hanging.  The dispatcher's choice
+                                 for few long rows */
 };
 
 /*

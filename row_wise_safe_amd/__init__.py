@@ -43,7 +43,7 @@ RWS_ERR_HIP = 4
 RWS_ERR_UNSUPPORTED_SHAPE = 5
 
 KERNEL_IDS = {"auto": 0, "wave_row": 1, "block_onepass": 2, "two_pass": 3, "splitk": 4,
-              "splitk_fused": 5}
+              "splitk_fused": 5, "splitk_ordered": 6}
 KERNELS = tuple(k for k in KERNEL_IDS if k != "auto")
 
 _DTYPES = {torch.float32: RWS_F32, torch.float16: RWS_F16, torch.bfloat16: RWS_BF16}
@@ -224,7 +224,7 @@ def softmax(x: torch.Tensor, out: torch.Tensor | None = None, kernel: str = "aut
 
     ``out`` (same shape and dtype, contiguous) may be ``x`` itself (in place).
     ``kernel`` forces a family (``"wave_row"``, ``"block_onepass"``,
-    ``"two_pass"``, ``"splitk"``, ``"splitk_fused"``) instead of the
+    ``"two_pass"``, ``"splitk"``, ``"splitk_fused"``, ``"splitk_ordered"``) instead of the
     dispatcher's choice.
     Work is enqueued on ``stream`` (default: the current stream of x's
     device); the call runs with x's device current, as the C ABI requires.

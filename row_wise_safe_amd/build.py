@@ -25,6 +25,7 @@ SOURCES = [
     "rws_two_pass.hip",
     "rws_splitk.hip",
     "rws_splitk_fused.hip",
+    "rws_splitk_ordered.hip",
     "rws_masked.hip",
     "rws_backward.hip",
     "rws_norm_wave.hip",

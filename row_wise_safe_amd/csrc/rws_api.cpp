@@ -74,6 +74,13 @@ DeviceInfo device_info() {
     return info;
 }
 
+constexpr int kOrderedMaxP = 1024;
+
+bool is_splitk(int family) {
+    return family == RWS_KERNEL_SPLITK || family == RWS_KERNEL_SPLITK_FUSED ||
+           family == RWS_KERNEL_SPLITK_ORDERED;
+}
+
 struct Plan {
     int family = 0;   // RWS_KERNEL_*
     int variant = 0;  // index into that family's variant table
@@ -248,13 +255,13 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
         if (wline <= 136 && wave_fits) {
             family = RWS_KERNEL_WAVE_ROW;
         } else if (few_rows && wline >= 2048) {
-            family = RWS_KERNEL_SPLITK;
+            family = RWS_KERNEL_SPLITK_ORDERED;
         } else if (wline <= 512 && wave_fits) {
             family = RWS_KERNEL_WAVE_ROW;
         } else if (pick_onepass(wline) >= 0 && wline <= 8192) {
             family = RWS_KERNEL_BLOCK_ONEPASS;
         } else if (few_rows) {
-            family = RWS_KERNEL_SPLITK;
+            family = RWS_KERNEL_SPLITK_ORDERED;
         } else if (pick_onepass(wline) >= 0) {
             family = RWS_KERNEL_BLOCK_ONEPASS;
         } else {
@@ -264,12 +271,11 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
     if (masked && kernel_id == RWS_KERNEL_AUTO) {
         // the masked forms exist for wave_row, register-only block_onepass
         // and two_pass; long rows with few rows go to two_pass
-        if (family == RWS_KERNEL_SPLITK || family == RWS_KERNEL_SPLITK_FUSED)
-            family = RWS_KERNEL_TWO_PASS;
+        if (is_splitk(family)) family = RWS_KERNEL_TWO_PASS;
         if (family == RWS_KERNEL_BLOCK_ONEPASS && pick_onepass(wline, true) < 0)
             family = RWS_KERNEL_TWO_PASS;
     }
-    if (masked && (family == RWS_KERNEL_SPLITK || family == RWS_KERNEL_SPLITK_FUSED))
+    if (masked && is_splitk(family))
         return fail(RWS_ERR_UNSUPPORTED_SHAPE, "the masked form has no split-k kernel");
     p->family = family;
     p->aligned = g.a128;
@@ -328,13 +334,24 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
             p->max_rows_per_launch = rows;
             break;
         }
-        case RWS_KERNEL_SPLITK: {
+        case RWS_KERNEL_SPLITK:
+        case RWS_KERNEL_SPLITK_ORDERED: {
             int P = 1;
             p->variant = pick_splitk(rows, wline, cus, &P);
             if (p->variant < 0) return fail(RWS_ERR_UNSUPPORTED_SHAPE, "split-k: no variant");
             p->P = P;
             p->remap = false;
-            p->max_rows_per_launch = std::max<int64_t>(1, ((int64_t)1 << 23) / P);
+            // Every stage-2 workgroup of the ordered form polls all P of its
+            // row's partials (two tagged words each, read past the L2): past
+            // kOrderedMaxP chunks per row that costs more than the launch it
+            // saves, and the dispatcher keeps the two launches.
+            if (family == RWS_KERNEL_SPLITK_ORDERED && kernel_id == RWS_KERNEL_AUTO &&
+                P > kOrderedMaxP)
+                family = p->family = RWS_KERNEL_SPLITK;
+            // at most 2^23 workgroups per launch (both stages of the ordered
+            // form count)
+            const int64_t per_row = family == RWS_KERNEL_SPLITK_ORDERED ? 2LL * P : (int64_t)P;
+            p->max_rows_per_launch = std::max<int64_t>(1, ((int64_t)1 << 23) / per_row);
             break;
         }
         default:
@@ -353,6 +370,9 @@ struct Workspace {
     unsigned* sync = nullptr;   // single-launch split-k: kSyncWordsPerRow words per row
     int64_t sync_rows = 0;
     unsigned epoch = 0;         // last epoch handed to a single-launch call
+    uint64_t* tags = nullptr;   // ordered split-k: epoch-tagged partial words
+    int64_t tag_words = 0;
+    unsigned tag_epoch = 0;     // last epoch used on `tags`
 };
 
 std::mutex g_ws_mu;
@@ -366,6 +386,7 @@ struct WorkspaceReaper {
         for (auto& kv : *g_ws) {
             if (kv.second.ptr) (void)hipFree(kv.second.ptr);
             if (kv.second.sync) (void)hipFree(kv.second.sync);
+            if (kv.second.tags) (void)hipFree(kv.second.tags);
         }
         delete g_ws;
         g_ws = nullptr;
@@ -434,10 +455,61 @@ int get_workspace(hipStream_t stream, size_t bytes, int64_t sync_rows, void** ou
     return RWS_OK;
 }
 
+// Tag words of the ordered split-k for (device, stream): grow-only, zeroed
+// (by a kernel on `stream`) when allocated.  Reserves `launches` consecutive
+// epochs and returns the first in *epoch0; when the 32-bit epoch would wrap,
+// the words are zeroed again and the epochs restart at 1, so a word left by
+// an earlier launch never carries a live epoch.  The caller holds g_ws_mu
+// until its launches are enqueued (as for get_workspace).
+int get_tag_workspace(hipStream_t stream, int64_t words, int64_t launches, uint64_t** out,
+                      unsigned* epoch0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RWS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (!g_ws) g_ws = new std::map<std::pair<int, hipStream_t>, Workspace>();
+    Workspace& w = (*g_ws)[std::make_pair(dev, stream)];
+    if (w.tag_words < words) {
+        if (w.tags) {
+            // the old words may still be in use by earlier work on this stream
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess)
+                return fail(RWS_ERR_HIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+            (void)hipFree(w.tags);
+            w.tags = nullptr;
+            w.tag_words = 0;
+        }
+        if (std::getenv("RWS_TEST_FAIL_ALLOC"))
+            return fail(RWS_ERR_HIP, "workspace allocation failed (RWS_TEST_FAIL_ALLOC)");
+        int64_t want = 512;
+        while (want < words) want *= 2;
+        e = hipMalloc((void**)&w.tags, (size_t)want * sizeof(uint64_t));
+        if (e == hipSuccess) e = rws::launch_zero_words(w.tags, want, stream);
+        if (e != hipSuccess) {
+            if (w.tags) (void)hipFree(w.tags);
+            w.tags = nullptr;
+            return fail(RWS_ERR_HIP, std::string("split-k tag words: ") + hipGetErrorString(e));
+        }
+        w.tag_words = want;
+        // test hook: start a fresh buffer's epochs just below the 32-bit wrap
+        const char* start = std::getenv("RWS_TEST_TAG_EPOCH");
+        w.tag_epoch = start ? (unsigned)std::strtoul(start, nullptr, 0) : 0u;
+    }
+    if ((uint64_t)w.tag_epoch + (uint64_t)launches > 0xffffffffull) {
+        e = rws::launch_zero_words(w.tags, w.tag_words, stream);
+        if (e != hipSuccess)
+            return fail(RWS_ERR_HIP, std::string("split-k tag words: ") + hipGetErrorString(e));
+        w.tag_epoch = 0;
+    }
+    *out = w.tags;
+    *epoch0 = w.tag_epoch + 1;
+    w.tag_epoch += (unsigned)launches;
+    return RWS_OK;
+}
+
 int check_args(const void* in, void* out, int64_t rows, int64_t cols, int dtype, int kernel_id) {
     if (dtype != RWS_F32 && dtype != RWS_F16 && dtype != RWS_BF16)
         return fail(RWS_ERR_UNSUPPORTED_DTYPE, "dtype must be RWS_F32, RWS_F16 or RWS_BF16");
-    if (kernel_id < RWS_KERNEL_AUTO || kernel_id > RWS_KERNEL_SPLITK_FUSED)
+    if (kernel_id < RWS_KERNEL_AUTO || kernel_id > RWS_KERNEL_SPLITK_ORDERED)
         return fail(RWS_ERR_INVALID_ARG, "unknown kernel id " + std::to_string(kernel_id));
     if (rows < 0 || cols < 0) return fail(RWS_ERR_INVALID_ARG, "rows and cols must be >= 0");
     if (cols > kMaxCols) return fail(RWS_ERR_UNSUPPORTED_SHAPE, "cols above 2^30");
@@ -463,13 +535,21 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
     hipStream_t s = (hipStream_t)stream;
     // split-k: keep the workspace locked until this call's launches are enqueued
     std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
-    if (p.family == RWS_KERNEL_SPLITK || p.family == RWS_KERNEL_SPLITK_FUSED) ws_lock.lock();
+    uint64_t* tags = nullptr;
+    if (is_splitk(p.family)) ws_lock.lock();
     if (p.family == RWS_KERNEL_SPLITK) {
         const int64_t batch = std::min<int64_t>(rows, p.max_rows_per_launch);
         st = get_workspace(s, (size_t)batch * p.P * sizeof(float2), 0, &ws, nullptr, nullptr);
         if (st != RWS_OK) return st;
     } else if (p.family == RWS_KERNEL_SPLITK_FUSED) {
         st = get_workspace(s, (size_t)rows * p.P * sizeof(float2), rows, &ws, &sync, &epoch);
+        if (st != RWS_OK) return st;
+    } else if (p.family == RWS_KERNEL_SPLITK_ORDERED) {
+        const int64_t batch = std::min<int64_t>(rows, p.max_rows_per_launch);
+        const int64_t launches = (rows + p.max_rows_per_launch - 1) / p.max_rows_per_launch;
+        if (launches >= ((int64_t)1 << 31))
+            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "ordered split-k: too many launches for one call");
+        st = get_tag_workspace(s, 2 * batch * p.P, launches, &tags, &epoch);
         if (st != RWS_OK) return st;
     }
     const int64_t row_bytes = cols * elem_size(dtype);
@@ -506,6 +586,11 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
                     break;
                 case RWS_KERNEL_SPLITK_FUSED:
                     e = rws::launch_splitk_fused(L, p.variant, p.P, (float2*)ws, sync, epoch);
+                    break;
+                case RWS_KERNEL_SPLITK_ORDERED:
+                    // one epoch per launch: the batches reuse the same tag words
+                    e = rws::launch_splitk_ordered(L, p.variant, p.P, tags,
+                                                   epoch + (unsigned)(r0 / p.max_rows_per_launch));
                     break;
             }
         }
@@ -794,7 +879,7 @@ int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void* i
     buf[0] = 0;
     if (dtype != RWS_F32 && dtype != RWS_F16 && dtype != RWS_BF16)
         return fail(RWS_ERR_UNSUPPORTED_DTYPE, "dtype must be RWS_F32, RWS_F16 or RWS_BF16");
-    if (kernel_id < RWS_KERNEL_AUTO || kernel_id > RWS_KERNEL_SPLITK_FUSED)
+    if (kernel_id < RWS_KERNEL_AUTO || kernel_id > RWS_KERNEL_SPLITK_ORDERED)
         return fail(RWS_ERR_INVALID_ARG, "unknown kernel id " + std::to_string(kernel_id));
     if (rows < 0 || cols < 0) return fail(RWS_ERR_INVALID_ARG, "rows and cols must be >= 0");
     if (cols > kMaxCols) return fail(RWS_ERR_UNSUPPORTED_SHAPE, "cols above 2^30");
@@ -850,6 +935,16 @@ int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void* i
                           (long long)wmax);
             break;
         }
+        case RWS_KERNEL_SPLITK_ORDERED: {
+            const rws::SplitkVariant& v = rws::kSplitk[p.variant];
+            std::snprintf(buf, (size_t)buflen,
+                          "splitk_ordered<%s,%s,B=%d,KC=%d> P=%d grid=%lld (2 stages) block=%d "
+                          "window<=%lld",
+                          dtype_name(dtype), al, v.block, v.kc, p.P,
+                          (long long)(2 * std::min(rows, p.max_rows_per_launch) * p.P), v.block,
+                          (long long)wmax);
+            break;
+        }
     }
     return RWS_OK;
 }
@@ -862,6 +957,7 @@ const char* softmax_kernel_name(int kernel_id) {
         case RWS_KERNEL_TWO_PASS: return "two_pass";
         case RWS_KERNEL_SPLITK: return "splitk";
         case RWS_KERNEL_SPLITK_FUSED: return "splitk_fused";
+        case RWS_KERNEL_SPLITK_ORDERED: return "splitk_ordered";
     }
     return "unknown";
 }

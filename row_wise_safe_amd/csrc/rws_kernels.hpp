@@ -355,32 +355,30 @@ __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
 // ===========================================================================
 // split-k.  A row's window of granules is cut into P chunks of CG = BLOCK*KC
 // granules; workgroup b handles chunk b % P of row b / P.
-//   stage 1: chunk max, chunk sum of e^(x - m_c) -> ws[row*P + chunk] = (m_c, d_c)
+//   stage 1: chunk max, chunk sum of e^(x - m_c) -> partial (m_c, d_c)
 //   stage 2: merge the row's P partials into (M, D), re-read the chunk,
 //            write e^(x - M) / D.
-// The launch boundary between the stages is the only grid-wide ordering.
+// The two-launch form orders the stages by the launch boundary; the ordered
+// single launch (rws_splitk_ordered.hip) runs both stages as workgroups of
+// one grid.  Both share the stage bodies below.
 // ===========================================================================
+
+// Issue the loads of one chunk (KC granules per thread, BLOCK granules apart).
 template <int DT, bool ALIGNED, int BLOCK, int KC>
-__global__ __launch_bounds__(BLOCK) void k_splitk_stage1(const void* __restrict__ in,
-                                                         int64_t rows, int cols, int P,
-                                                         float2* __restrict__ ws, int remap) {
+__device__ inline void splitk_fetch(const RowWin<DT, ALIGNED>& w, int kbase, const char* tbeg,
+                                    const char* tend, u32x4 (&raw)[KC]) {
+#pragma unroll
+    for (int i = 0; i < KC; ++i) raw[i] = w.fetch(kbase + BLOCK * i, tbeg, tend);
+}
+
+// Stage 1 body: the chunk's (max, sum of e^(x - max)), in every thread.
+template <int DT, bool ALIGNED, int BLOCK, int KC>
+__device__ inline float2 splitk_partial(const RowWin<DT, ALIGNED>& w, int kbase,
+                                        const u32x4 (&raw)[KC], const char* tbeg,
+                                        const char* tend, float* red_max, float* red_sum) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     constexpr int N = KC * VEC;
-    __shared__ float red_max[W];
-    __shared__ float red_sum[W];
-    const int t = threadIdx.x;
-    const int64_t b = (remap ? xcd_remap(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
-    const int64_t row = b / P;
-    const int chunk = (int)(b - row * P);
-    const char* tbeg = (const char*)in;
-    const char* tend = tensor_end<DT>(in, rows, cols);
-    const RowWin<DT, ALIGNED> w(in, const_cast<void*>(in), row, cols);  // out unused
-    const int kbase = chunk * (BLOCK * KC) + t;
-
-    u32x4 raw[KC];
-#pragma unroll
-    for (int i = 0; i < KC; ++i) raw[i] = w.fetch(kbase + BLOCK * i, tbeg, tend);
     float v[N];
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
@@ -401,7 +399,60 @@ __global__ __launch_bounds__(BLOCK) void k_splitk_stage1(const void* __restrict_
 #pragma unroll
     for (int j = 0; j < N; ++j) s += v[j];
     s = block_reduce<W, OpSum>(s, red_sum);
-    if (t == 0) ws[row * P + chunk] = make_float2(mx, s);
+    return make_float2(mx, s);
+}
+
+// Fold one partial (pm, pd) into a thread's running (m, d) (the merge rule
+// with (-inf, 0) as identity: a side with d == 0 contributes nothing).
+__device__ inline void md_fold(float& m, float& d, float pm, float pd) {
+    const float mn = vmax(m, pm);
+    const float a = (d == 0.0f) ? 0.0f : d * merge_scale(m, mn);
+    const float b = (pd == 0.0f) ? 0.0f : pd * merge_scale(pm, mn);
+    m = mn;
+    d = a + b;
+}
+
+// Stage 2 tail: write y = e^(x - M) * r for the chunk already in `raw`.
+template <int DT, bool ALIGNED, int BLOCK, int KC>
+__device__ inline void splitk_write(const RowWin<DT, ALIGNED>& w, int kbase,
+                                    const u32x4 (&raw)[KC], const char* tbeg, const char* tend,
+                                    float M, float r, bool same_phase) {
+    constexpr int VEC = Elem<DT>::VEC;
+    const RowExp er(M);
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        const int k = kbase + BLOCK * i;
+        if (k < w.ngran) {
+            float f[VEC];
+            w.widen(k, raw[i], f, tbeg, tend);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) f[e] = er.one(f[e]) * r;
+            w.store(k, f, same_phase);
+        }
+    }
+}
+
+template <int DT, bool ALIGNED, int BLOCK, int KC>
+__global__ __launch_bounds__(BLOCK) void k_splitk_stage1(const void* __restrict__ in,
+                                                         int64_t rows, int cols, int P,
+                                                         float2* __restrict__ ws, int remap) {
+    constexpr int W = BLOCK / 64;
+    __shared__ float red_max[W];
+    __shared__ float red_sum[W];
+    const int t = threadIdx.x;
+    const int64_t b = (remap ? xcd_remap(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
+    const int64_t row = b / P;
+    const int chunk = (int)(b - row * P);
+    const char* tbeg = (const char*)in;
+    const char* tend = tensor_end<DT>(in, rows, cols);
+    const RowWin<DT, ALIGNED> w(in, const_cast<void*>(in), row, cols);  // out unused
+    const int kbase = chunk * (BLOCK * KC) + t;
+
+    u32x4 raw[KC];
+    splitk_fetch<DT, ALIGNED, BLOCK, KC>(w, kbase, tbeg, tend, raw);
+    const float2 md =
+        splitk_partial<DT, ALIGNED, BLOCK, KC>(w, kbase, raw, tbeg, tend, red_max, red_sum);
+    if (t == 0) ws[row * P + chunk] = md;
 }
 
 template <int DT, bool ALIGNED, int BLOCK, int KC>
@@ -410,7 +461,6 @@ __global__ __launch_bounds__(BLOCK) void k_splitk_stage2(const void* __restrict_
                                                          int cols, int P,
                                                          const float2* __restrict__ ws,
                                                          int same_phase, int remap) {
-    constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     __shared__ float red_max[W];
     __shared__ float red_sum[W];
@@ -425,34 +475,16 @@ __global__ __launch_bounds__(BLOCK) void k_splitk_stage2(const void* __restrict_
 
     // Issue the chunk's loads first; the partial merge overlaps their latency.
     u32x4 raw[KC];
-#pragma unroll
-    for (int i = 0; i < KC; ++i) raw[i] = w.fetch(kbase + BLOCK * i, tbeg, tend);
-
+    splitk_fetch<DT, ALIGNED, BLOCK, KC>(w, kbase, tbeg, tend, raw);
     float m = kNegInf, d = 0.0f;
     for (int j = t; j < P; j += BLOCK) {
         const float2 p = ws[row * P + j];
-        const float mn = vmax(m, p.x);
-        const float a = (d == 0.0f) ? 0.0f : d * merge_scale(m, mn);
-        const float b = (p.y == 0.0f) ? 0.0f : p.y * merge_scale(p.x, mn);
-        m = mn;
-        d = a + b;
+        md_fold(m, d, p.x, p.y);
     }
     float M, D;
     block_merge<W>(m, d, M, D, red_max, red_sum);
-    const RowExp er(M);
-    const float r = __builtin_amdgcn_rcpf(D);
-
-#pragma unroll
-    for (int i = 0; i < KC; ++i) {
-        const int k = kbase + BLOCK * i;
-        if (k < w.ngran) {
-            float f[VEC];
-            w.widen(k, raw[i], f, tbeg, tend);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) f[e] = er.one(f[e]) * r;
-            w.store(k, f, same_phase != 0);
-        }
-    }
+    splitk_write<DT, ALIGNED, BLOCK, KC>(w, kbase, raw, tbeg, tend, M, __builtin_amdgcn_rcpf(D),
+                                        same_phase != 0);
 }
 
 }  // namespace rws

@@ -67,6 +67,13 @@ hipError_t launch_splitk_fused(const Launch& L, int variant, int P, float2* ws, 
                                unsigned epoch);
 // Workgroups of this variant that can be resident at once on `cus` CUs.
 hipError_t splitk_fused_capacity(int variant, int dtype, bool aligned, int cus, int64_t* blocks);
+// Split-k in one ordinary launch (kSplitk variants): grid 2*rows*P, tags
+// holds 2*rows*P epoch-tagged words, epoch is unique to this launch on this
+// tag buffer (never 0; the buffer starts zeroed).
+hipError_t launch_splitk_ordered(const Launch& L, int variant, int P, uint64_t* tags,
+                                 unsigned epoch);
+// Zero n 64-bit words on `stream`.
+hipError_t launch_zero_words(uint64_t* p, int64_t n, hipStream_t stream);
 // The masked forms (same variant tables; block_onepass only for variants
 // without LDS parking).
 hipError_t launch_wave_row_masked(const Launch& L, int variant, const MaskArgs& M);

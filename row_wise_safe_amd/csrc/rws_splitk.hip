@@ -3,17 +3,11 @@
 // 16-byte copy kernel used as the bandwidth reference.
 #include "rws_kernels.hpp"
 #include "rws_launch.hpp"
+#include "rws_variants.hpp"
 
 #include <algorithm>
 
 namespace rws {
-
-// (threads, granules per thread per chunk)
-#define RWS_SPLITK_VARIANTS(X) \
-    X(256, 2)                  \
-    X(256, 4)                  \
-    X(256, 8)                  \
-    X(512, 8)
 
 #define RWS_ROW(b, kc) {b, kc},
 const SplitkVariant kSplitk[] = {RWS_SPLITK_VARIANTS(RWS_ROW)};

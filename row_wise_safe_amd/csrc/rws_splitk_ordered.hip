@@ -1,0 +1,164 @@
+// rws_splitk_ordered.hip -- split-k in one ordinary launch.
+//
+// The grid holds both stages of split-k (CUDA safe-online-softmax page,
+// section 3.2): workgroups [0, rows*P) are stage 1 (one chunk's partial
+// (m, d) each), workgroups [rows*P, 2*rows*P) are stage 2 (merge the row's P
+// partials, re-read the chunk, write it).  The page orders the stages with a
+// second launch, and names a single launch with polling as the alternative;
+// this is that alternative, built so that it needs neither a grid-wide
+// barrier nor any memory fence:
+//
+//  * No fences.  A partial travels as two 64-bit words, (epoch << 32 | bits
+//    of m) and (epoch << 32 | bits of d), stored and polled with relaxed
+//    agent-scope atomics.  Coherence of each single word is all the exchange
+//    needs: a stage-2 thread waits until both words of a partial carry this
+//    launch's epoch, and the words themselves are the data.  (A flag plus
+//    separate data would need a release/acquire pair, which on this
+//    multi-XCD part writes back and invalidates the XCD's L2 -- about 20 us
+//    over the grid, measured.)
+//  * No co-residency requirement.  Every stage-2 workgroup waits only for
+//    stage-1 workgroups, and every stage-1 workgroup has a lower index than
+//    every stage-2 workgroup; workgroups are handed to each XCD in increasing
+//    index order, so a waiting stage-2 workgroup is never ahead of a stage-1
+//    workgroup it needs, and stage-1 workgroups never wait.
+//  * Bounded waiting.  A poll gives up after kOrderedSpinLimit tries (each
+//    a sleep plus a load round trip: at least ~0.5 s in all); the workgroup
+//    then writes NaN for its chunk, so a broken ordering assumption shows as
+//    NaN output, never as a hang.
+//
+// The epoch grows by one per launch on the same tag buffer (host side), and
+// the buffer is zero-filled when it is allocated and when the 32-bit epoch
+// wraps, so a word from an earlier launch never matches.
+//
+// Measured on MI355X, fp16 [16, 1M]: 14.3-14.6 us against 15.2-15.5 us for
+// the two launches (the stage-2 workgroups start while the last stage-1
+// workgroups finish, instead of after a kernel boundary).
+#include "rws_kernels.hpp"
+#include "rws_launch.hpp"
+#include "rws_variants.hpp"
+
+#include <algorithm>
+
+namespace rws {
+
+constexpr unsigned kOrderedSpinLimit = 1u << 21;
+
+__device__ inline uint64_t md_word(unsigned epoch, float v) {
+    return ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(v);
+}
+
+// Poll one tagged word until it carries `epoch`; returns its value bits and
+// sets `late` when the limit ran out (a thread that is already late does not
+// wait again, so one thread waits at most one limit in total).
+__device__ inline float poll_word(const uint64_t* p, unsigned epoch, int& late) {
+    for (unsigned it = 0; it < (late ? 1u : kOrderedSpinLimit); ++it) {
+        const uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((unsigned)(v >> 32) == epoch) return __uint_as_float((unsigned)v);
+        __builtin_amdgcn_s_sleep(2);
+    }
+    late = 1;
+    return 0.0f;
+}
+
+template <int DT, bool ALIGNED, int BLOCK, int KC>
+__global__ __launch_bounds__(BLOCK) void k_splitk_ordered(const void* __restrict__ in,
+                                                          void* __restrict__ out, int64_t rows,
+                                                          int cols, int P,
+                                                          uint64_t* __restrict__ tags,
+                                                          unsigned epoch, int same_phase) {
+    constexpr int W = BLOCK / 64;
+    __shared__ float red_max[W];
+    __shared__ float red_sum[W];
+    const int t = threadIdx.x;
+    const int64_t RP = rows * P;
+    int64_t b = blockIdx.x;
+    const bool merge_stage = b >= RP;
+    if (merge_stage) b -= RP;
+    const int64_t row = b / P;
+    const int chunk = (int)(b - row * P);
+    const char* tbeg = (const char*)in;
+    const char* tend = tensor_end<DT>(in, rows, cols);
+    const RowWin<DT, ALIGNED> w(in, out, row, cols);
+    const int kbase = chunk * (BLOCK * KC) + t;
+    uint64_t* row_tags = tags + 2 * row * P;
+
+    // Both stages start by loading the chunk; a stage-2 workgroup's loads
+    // are then in flight while it waits for the partials.
+    u32x4 raw[KC];
+    splitk_fetch<DT, ALIGNED, BLOCK, KC>(w, kbase, tbeg, tend, raw);
+
+    if (!merge_stage) {
+        const float2 md =
+            splitk_partial<DT, ALIGNED, BLOCK, KC>(w, kbase, raw, tbeg, tend, red_max, red_sum);
+        if (t == 0) {
+            __hip_atomic_store(row_tags + 2 * chunk, md_word(epoch, md.x), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(row_tags + 2 * chunk + 1, md_word(epoch, md.y), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return;
+    }
+
+    float m = kNegInf, d = 0.0f;
+    int late = 0;
+    for (int j = t; j < P; j += BLOCK) {
+        const float pm = poll_word(row_tags + 2 * j, epoch, late);
+        const float pd = poll_word(row_tags + 2 * j + 1, epoch, late);
+        md_fold(m, d, pm, pd);
+    }
+    float M, D;
+    block_merge<W>(m, d, M, D, red_max, red_sum);
+    const bool failed = __syncthreads_or(late) != 0;
+    const float r = failed ? __builtin_nanf("") : __builtin_amdgcn_rcpf(D);
+    splitk_write<DT, ALIGNED, BLOCK, KC>(w, kbase, raw, tbeg, tend, M, r, same_phase != 0);
+}
+
+// Zero n 64-bit words (a kernel rather than a memset, so that the clear is an
+// ordinary node if a caller captures the stream into a graph).
+__global__ __launch_bounds__(256) void k_zero_words(uint64_t* __restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+hipError_t launch_zero_words(uint64_t* p, int64_t n, hipStream_t stream) {
+    for (int64_t done = 0; done < n;) {
+        const int64_t c = std::min<int64_t>(n - done, (int64_t)1 << 31);
+        hipLaunchKernelGGL(k_zero_words, dim3((unsigned)((c + 255) / 256)), dim3(256), 0, stream,
+                           p + done, c);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        done += c;
+    }
+    return hipSuccess;
+}
+
+template <int DT, bool AL, int B, int KC>
+static hipError_t go(const Launch& L, int P, uint64_t* tags, unsigned epoch) {
+    hipLaunchKernelGGL((k_splitk_ordered<DT, AL, B, KC>), dim3((unsigned)(2 * L.rows * P)),
+                       dim3(B), 0, L.stream, L.in, L.out, L.rows, L.cols, P, tags, epoch,
+                       (int)L.same_phase);
+    return hipGetLastError();
+}
+
+template <int B, int KC>
+static hipError_t go_any(const Launch& L, int P, uint64_t* tags, unsigned epoch) {
+    switch (L.dtype) {
+        case kF32: return L.aligned ? go<kF32, true, B, KC>(L, P, tags, epoch) : go<kF32, false, B, KC>(L, P, tags, epoch);
+        case kF16: return L.aligned ? go<kF16, true, B, KC>(L, P, tags, epoch) : go<kF16, false, B, KC>(L, P, tags, epoch);
+        case kBF16: return L.aligned ? go<kBF16, true, B, KC>(L, P, tags, epoch) : go<kBF16, false, B, KC>(L, P, tags, epoch);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_splitk_ordered(const Launch& L, int variant, int P, uint64_t* tags,
+                                 unsigned epoch) {
+    int i = 0;
+#define RWS_CASE(b, kc) \
+    if (variant == i) return go_any<b, kc>(L, P, tags, epoch); \
+    ++i;
+    RWS_SPLITK_VARIANTS(RWS_CASE)
+#undef RWS_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace rws

@@ -36,3 +36,12 @@
     X(512, 4)                    \
     X(1024, 2)                   \
     X(1024, 4)
+
+// split-k (threads, granules per thread per chunk): the two-launch and the
+// ordered single-launch forms share the list, so the dispatcher's chunking
+// applies to both.
+#define RWS_SPLITK_VARIANTS(X) \
+    X(256, 2)                  \
+    X(256, 4)                  \
+    X(256, 8)                  \
+    X(512, 8)

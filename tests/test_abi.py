@@ -54,8 +54,9 @@ def test_status_strings_and_names(lib):
     for st in range(1, 6):
         assert rws.softmax_status_string(st) not in ("", "ok", "unknown status")
     assert rws.softmax_status_string(99) == "unknown status"
-    assert [rws.softmax_kernel_name(i) for i in range(6)] == \
-        ["auto", "wave_row", "block_onepass", "two_pass", "splitk", "splitk_fused"]
+    assert [rws.softmax_kernel_name(i) for i in range(7)] == \
+        ["auto", "wave_row", "block_onepass", "two_pass", "splitk", "splitk_fused",
+         "splitk_ordered"]
     assert rws.softmax_kernel_name(17) == "unknown"
 
 
@@ -83,7 +84,8 @@ def test_empty_is_success_without_pointers(lib):
 
 def test_bad_kernel_id(lib):
     assert rws.softmax_fwd_kernel(32, 32, 2, 2, rws.RWS_F32, 0, 9) == rws.RWS_ERR_INVALID_ARG
-    assert rws.softmax_fwd_kernel(32, 32, 2, 2, rws.RWS_F32, 0, 6) == rws.RWS_ERR_INVALID_ARG
+    assert rws.softmax_fwd_kernel(32, 32, 2, 2, rws.RWS_F32, 0, 7) == rws.RWS_ERR_INVALID_ARG
+    assert rws.softmax_fwd_kernel(32, 32, 2, 2, rws.RWS_F32, 0, -1) == rws.RWS_ERR_INVALID_ARG
 
 
 def test_copy_argument_checks(lib):
@@ -105,7 +107,9 @@ def test_forced_wave_row_rejects_long_rows(lib):
     (65536, 512, rws.RWS_F16, "wave_row"),
     (1 << 20, 128, rws.RWS_BF16, "wave_row"),
     (8192, 4097, rws.RWS_F16, "block_onepass"),
-    (16, 1 << 20, rws.RWS_F16, "splitk"),
+    (16, 1 << 20, rws.RWS_F16, "splitk_ordered"),
+    (3, (1 << 20) - 1, rws.RWS_F16, "splitk_ordered"),
+    (1, 1 << 30, rws.RWS_F32, "splitk"),  # P = 131072 chunks: two launches
     (4096, 1 << 20, rws.RWS_F16, "two_pass"),
 ])
 def test_dispatch_routes(lib, rows, cols, dtype, family):

@@ -105,6 +105,7 @@ def test_backward_attention_workload():
 
 def test_backward_rejects_split_kernels():
     y = torch.zeros(2, 64, dtype=torch.float16, device="cuda")
-    st = rws.softmax_bwd_kernel(y.data_ptr(), y.data_ptr(), y.data_ptr(), 2, 64, rws.RWS_F16, 0,
-                                rws.KERNEL_IDS["splitk"])
-    assert st == rws.RWS_ERR_INVALID_ARG
+    for kernel in ("splitk", "splitk_fused", "splitk_ordered"):
+        st = rws.softmax_bwd_kernel(y.data_ptr(), y.data_ptr(), y.data_ptr(), 2, 64, rws.RWS_F16,
+                                    0, rws.KERNEL_IDS[kernel])
+        assert st == rws.RWS_ERR_INVALID_ARG

@@ -106,9 +106,10 @@ def test_fully_masked_rows_are_nan():
 
 def test_masked_rejects_splitk_and_bad_args():
     x = torch.zeros(4, 1 << 16, dtype=torch.float16, device="cuda")
-    with pytest.raises(rws.SoftmaxError) as e:
-        rws.softmax_masked(x, kernel="splitk")
-    assert e.value.status == rws.RWS_ERR_UNSUPPORTED_SHAPE
+    for kernel in ("splitk", "splitk_fused", "splitk_ordered"):
+        with pytest.raises(rws.SoftmaxError) as e:
+            rws.softmax_masked(x, kernel=kernel)
+        assert e.value.status == rws.RWS_ERR_UNSUPPORTED_SHAPE
     st = rws.softmax_fwd_masked(x.data_ptr(), x.data_ptr(), 4, 1 << 16, rws.RWS_F16, 1.0, 0, 0,
                                 -1, 0, 0)
     assert st == rws.RWS_ERR_INVALID_ARG

@@ -267,6 +267,8 @@ def test_norm_rejects_split_kernels():
         rws.layer_norm(x, kernel="splitk")
     with pytest.raises(rws.SoftmaxError):
         rws.rms_norm(x, kernel="splitk_fused")
+    with pytest.raises(rws.SoftmaxError):
+        rws.layer_norm(x, kernel="splitk_ordered")
 
 
 def test_norm_deterministic():

@@ -24,7 +24,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not have_gpu(), reason="needs an MI355X GPU")]
 
 DTYPES = ["f32", "f16", "bf16"]
-KERNELS = ["wave_row", "block_onepass", "two_pass", "splitk", "splitk_fused"]
+KERNELS = ["wave_row", "block_onepass", "two_pass", "splitk", "splitk_fused", "splitk_ordered"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -80,7 +80,7 @@ def test_workload_attn_each_kernel(kernel):
     check(y, oracle.safe_softmax(stored), w.dtype, kernel)
 
 
-@pytest.mark.parametrize("kernel", ["splitk", "splitk_fused", "two_pass", "auto"])
+@pytest.mark.parametrize("kernel", ["splitk", "splitk_fused", "splitk_ordered", "two_pass", "auto"])
 def test_long_rows_max_at_chunk_edges(kernel):
     cols = 1 << 20
     columns = np.array([0, cols - 1, 16383, 16384, 8191, 131072])

@@ -21,7 +21,8 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not have_gpu(), reason="needs an MI355X GPU")]
 
 
-def test_two_threads_one_stream_while_the_workspace_grows():
+@pytest.mark.parametrize("kernel", ["splitk", "splitk_ordered"])
+def test_two_threads_one_stream_while_the_workspace_grows(kernel):
     xa, xsa = to_device(workloads.argmax_moved_normal(4, 1 << 17, 901), "f16")
     xb, xsb = to_device(workloads.argmax_moved_normal(32, 1 << 19, 902), "f16")
     ref_a = oracle.safe_softmax(xsa)
@@ -36,7 +37,7 @@ def test_two_threads_one_stream_while_the_workspace_grows():
         def call(x, y):
             try:
                 barrier.wait()
-                rws.softmax(x, out=y, kernel="splitk", stream=s)
+                rws.softmax(x, out=y, kernel=kernel, stream=s)
             except Exception as e:  # reported below
                 errors.append(e)
 
