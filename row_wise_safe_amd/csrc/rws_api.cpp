@@ -123,10 +123,10 @@ int wave_row_wa(const rws::WaveRowVariant& v) { return v.G * 16 >= 128 ? 128 : 1
 int64_t onepass_capacity(const rws::OnepassVariant& v) { return (int64_t)v.block * (v.kr + v.kl); }
 
 // Choose among the wave_row variants: the narrowest lane group whose
-// registers hold the window, then the number of row sets per wave that
-// measured fastest on MI355X: two for one-granule full-wave rows (fp16 512
-// columns: 19.9 us vs 20.5 us with one), one otherwise (bf16 128 columns with
-// 16-lane groups: 84.5 us vs 88.3 us with two).
+// registers hold the window, with one row set per wave, which measured
+// fastest on MI355X with rows streamed from HBM (fp16 512 columns: 21.7 us
+// vs 23.8 us with two; bf16 128 columns with 16-lane groups: 79.8 us vs
+// 81.8 us with two).
 int pick_wave_row(const Geometry& g) {
     int best = -1;
     int64_t best_key = 0;
@@ -135,8 +135,7 @@ int pick_wave_row(const Geometry& g) {
         const int64_t w = window_granules(g, wave_row_wa(v));
         if ((int64_t)v.G * v.K < w) continue;
         const int64_t cap = (int64_t)v.G * v.K;
-        const int want_u = (v.G == 64 && v.K == 1) ? 2 : 1;
-        const int64_t key = cap * 64 + (v.U == want_u ? 0 : v.U);
+        const int64_t key = cap * 64 + v.U;
         if (best < 0 || key < best_key) {
             best = i;
             best_key = key;
@@ -290,9 +289,12 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
             const int wa = wave_row_wa(v);
             p->aligned = wa == 128 ? g.a128 : g.a16;
             p->window = window_granules(g, wa);
-            // XCD-aware order measured faster only for full-wave rows
-            p->remap = v.G == 64;
-            // keep (workgroups x 256 threads) of one launch below 2^32
+            // Consecutive workgroups go round-robin over the 8 XCDs, which
+            // spreads neighbouring rows over all of them; the XCD-contiguous
+            // order measured slower with rows streamed from HBM (fp16
+            // [65536,512]: 23.1 us vs 21.7 us).
+            p->remap = false;
+            // keep the threads of one launch below 2^32 (2^25 waves)
             p->max_rows_per_launch = (int64_t)(64 / v.G) * v.U * 4 * ((int64_t)1 << 23);
             break;
         }
@@ -763,8 +765,7 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
             const rws::WaveRowVariant& v = rws::kNormWave[i];
             const int64_t cap = (int64_t)v.G * v.K;
             if (cap < window_granules(g, wave_row_wa(v))) continue;
-            const int want_u = (v.G == 64 && v.K == 1) ? 2 : 1;
-            const int64_t key = cap * 64 + (v.U == want_u ? 0 : v.U);
+            const int64_t key = cap * 64 + v.U;
             if (best < 0 || key < best_key) {
                 best = i;
                 best_key = key;
@@ -896,10 +897,10 @@ int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void* i
         case RWS_KERNEL_WAVE_ROW: {
             const rws::WaveRowVariant& v = rws::kWaveRow[p.variant];
             std::snprintf(buf, (size_t)buflen,
-                          "wave_row<%s,%s,G=%d,K=%d,U=%d>%s grid=%lld block=256 window<=%lld",
+                          "wave_row<%s,%s,G=%d,K=%d,U=%d>%s grid=%lld block=%d window<=%lld",
                           dtype_name(dtype), al, v.G, v.K, v.U, p.remap ? " xcd" : "",
                           (long long)rws::wave_row_grid(v, std::min(rows, p.max_rows_per_launch)),
-                          (long long)wmax);
+                          rws::kWaveGroupThreads, (long long)wmax);
             break;
         }
         case RWS_KERNEL_BLOCK_ONEPASS: {

@@ -30,12 +30,13 @@ struct Second {
     int64_t delta;      // dy - y in bytes
     bool vec;           // delta % 16 == 0
 
+    template <bool NT = true>  // load policy: see load16
     __device__ inline u32x4 fetch(const Win& w, int k) const {
         u32x4 g = {0u, 0u, 0u, 0u};
         if (!vec) return g;
         const int c0 = k * VEC - w.lead;
         const char* p = w.gin + (int64_t)k * 16 + delta;
-        if (c0 + VEC > 0 && c0 < w.cols && p >= base && p + 16 <= end) g = *(const u32x4*)p;
+        if (c0 + VEC > 0 && c0 < w.cols && p >= base && p + 16 <= end) g = load16<NT>(p);
         return g;
     }
     // dy values of granule k (0 outside the row)
@@ -72,8 +73,8 @@ __global__ __launch_bounds__(256) void k_bwd_wave(const void* __restrict__ y,
     const int lane = threadIdx.x & 63;
     const int gl = lane & (G - 1);
     const int sub = lane / G;
-    const int64_t wave_id =
-        (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t wave_id = (int64_t)blockIdx.x * (int64_t)(blockDim.x >> 6) +
+                            __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t row0 = wave_id * (RPS * U);
     const char* tbeg = (const char*)y;
     const char* tend = tensor_end<DT>(y, rows, cols);
@@ -188,9 +189,9 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_stream(const void* __restrict__ y
     for (int k0 = t; k0 < w.ngran; k0 += BLOCK * U) {
         u32x4 ry[U], rg[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            ry[u] = w.fetch(k0 + BLOCK * u, tbeg, tend);
-            rg[u] = s2.fetch(w, k0 + BLOCK * u);
+        for (int u = 0; u < U; ++u) {  // cached: pass 2 reads both again
+            ry[u] = w.template fetch<false>(k0 + BLOCK * u, tbeg, tend);
+            rg[u] = s2.template fetch<false>(w, k0 + BLOCK * u);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_stream(const void* __restrict__ y
     X(8, 1, 1)                   \
     X(16, 1, 1)                  \
     X(32, 1, 1)                  \
-    X(64, 1, 2)                  \
+    X(64, 1, 1)                  \
     X(64, 2, 1)                  \
     X(64, 4, 1)                  \
     X(64, 8, 1)
@@ -270,7 +271,7 @@ template <int DT, bool AL, int G, int K, int U>
 static hipError_t bw(const BwdLaunch& B) {
     const WaveRowVariant v = {G, K, U};
     hipLaunchKernelGGL((k_bwd_wave<DT, AL, G, K, U>), dim3((unsigned)wave_row_grid(v, B.rows)),
-                       dim3(256), 0, B.stream, B.y, B.dy, B.dx, B.rows, B.cols, (int)B.dy_vec,
+                       dim3(kWaveGroupThreads), 0, B.stream, B.y, B.dy, B.dx, B.rows, B.cols, (int)B.dy_vec,
                        (int)B.same_phase);
     return hipGetLastError();
 }

@@ -48,19 +48,20 @@ __device__ inline void widen_zero(const Win& w, int k, u32x4 raw, float* v, cons
 
 // Issue the loads of input granule k and of its prologue operand, unless the
 // prologue says the granule cannot affect the result (then both stay zero and
-// the prologue overwrites the values).
-template <class Pre, class Win>
+// the prologue overwrites the values).  NT: the input's load policy
+// (load16); the prologue operand is shared by many rows and loads cached.
+template <bool NT = true, class Pre, class Win>
 __device__ inline void fetch_pre(const Pre& pre, const typename Pre::Ctx& pc, const Win& w, int k,
                                  const char* tbeg, const char* tend, u32x4& raw, u32x4& praw) {
     if (Pre::kActive) {
         raw = u32x4{0u, 0u, 0u, 0u};
         praw = u32x4{0u, 0u, 0u, 0u};
         if (pre.needs_input(pc, w, k)) {
-            raw = w.fetch(k, tbeg, tend);
+            raw = w.template fetch<NT>(k, tbeg, tend);
             praw = pre.fetch(pc, w, k);
         }
     } else {
-        raw = w.fetch(k, tbeg, tend);
+        raw = w.template fetch<NT>(k, tbeg, tend);
     }
 }
 
@@ -69,7 +70,8 @@ __device__ inline void fetch_pre(const Pre& pre, const typename Pre::Ctx& pc, co
 // granules per lane and row.  Lane gl of a group holds granules gl + G*i, so
 // the G lanes of a group read consecutive 16-byte granules at every step.
 // Rows past the end are clamped to the last row for loading (in bounds) and
-// are not stored.
+// are not stored.  A workgroup holds blockDim.x / 64 waves (the launcher's
+// choice, kWaveGroupWaves); wave w of workgroup b is wave b*(that) + w.
 // ===========================================================================
 template <int DT, bool ALIGNED, int G, int K, int U, class Pre = NoPre>
 __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
@@ -84,7 +86,8 @@ __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
     const int sub = lane / G;
     // The wave index is uniform: readfirstlane keeps the row arithmetic scalar.
     const int64_t block = (remap ? xcd_remap(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
-    const int64_t wave_id = block * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t wave_id = block * (int64_t)(blockDim.x >> 6) +
+                            __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t row0 = wave_id * (RPS * U);
     const char* tbeg = (const char*)in;
     const char* tend = tensor_end<DT>(in, rows, cols);
@@ -311,8 +314,9 @@ __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
         u32x4 raw[U];
         u32x4 praw[Pre::kActive ? U : 1];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            fetch_pre(pre, pc, w, k0 + BLOCK * u, tbeg, tend, raw[u], praw[Pre::kActive ? u : 0]);
+        for (int u = 0; u < U; ++u)  // cached: pass 2 reads the row again
+            fetch_pre<false>(pre, pc, w, k0 + BLOCK * u, tbeg, tend, raw[u],
+                             praw[Pre::kActive ? u : 0]);
         float v[U * VEC];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -364,11 +368,13 @@ __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
 // ===========================================================================
 
 // Issue the loads of one chunk (KC granules per thread, BLOCK granules apart).
-template <int DT, bool ALIGNED, int BLOCK, int KC>
+// Stage 1 loads cached (NT = false: stage 2 reads the chunk again), stage 2
+// non-temporal (the last read).
+template <int DT, bool ALIGNED, int BLOCK, int KC, bool NT>
 __device__ inline void splitk_fetch(const RowWin<DT, ALIGNED>& w, int kbase, const char* tbeg,
                                     const char* tend, u32x4 (&raw)[KC]) {
 #pragma unroll
-    for (int i = 0; i < KC; ++i) raw[i] = w.fetch(kbase + BLOCK * i, tbeg, tend);
+    for (int i = 0; i < KC; ++i) raw[i] = w.template fetch<NT>(kbase + BLOCK * i, tbeg, tend);
 }
 
 // Stage 1 body: the chunk's (max, sum of e^(x - max)), in every thread.
@@ -449,7 +455,7 @@ __global__ __launch_bounds__(BLOCK) void k_splitk_stage1(const void* __restrict_
     const int kbase = chunk * (BLOCK * KC) + t;
 
     u32x4 raw[KC];
-    splitk_fetch<DT, ALIGNED, BLOCK, KC>(w, kbase, tbeg, tend, raw);
+    splitk_fetch<DT, ALIGNED, BLOCK, KC, false>(w, kbase, tbeg, tend, raw);
     const float2 md =
         splitk_partial<DT, ALIGNED, BLOCK, KC>(w, kbase, raw, tbeg, tend, red_max, red_sum);
     if (t == 0) ws[row * P + chunk] = md;
@@ -475,7 +481,7 @@ __global__ __launch_bounds__(BLOCK) void k_splitk_stage2(const void* __restrict_
 
     // Issue the chunk's loads first; the partial merge overlaps their latency.
     u32x4 raw[KC];
-    splitk_fetch<DT, ALIGNED, BLOCK, KC>(w, kbase, tbeg, tend, raw);
+    splitk_fetch<DT, ALIGNED, BLOCK, KC, true>(w, kbase, tbeg, tend, raw);
     float m = kNegInf, d = 0.0f;
     for (int j = t; j < P; j += BLOCK) {
         const float2 p = ws[row * P + j];

@@ -47,11 +47,19 @@ extern const int kNumSplitk;
 extern const SplitkVariant kSplitkFused[];
 extern const int kNumSplitkFused;
 
-// Grid of one wave_row launch (workgroups of 256 threads = 4 waves).
+// Waves per workgroup of the wave-per-row kernels (wave_row, bwd_wave,
+// norm_wave; the kernels read it from blockDim).  One-wave workgroups
+// measured fastest on MI355X for rows streamed from HBM: fp16 [65536,512]
+// softmax 21.7 us against 22.8 us with four waves, bf16 [1048576,128]
+// 79.8 us against 81.3 us; a plain 64 MiB copy 21.9 us against 22.8 us.
+constexpr int kWaveGroupWaves = 1;
+constexpr int kWaveGroupThreads = 64 * kWaveGroupWaves;
+
+// Grid of one wave-per-row launch.
 inline int64_t wave_row_grid(const WaveRowVariant& v, int64_t rows) {
     const int64_t rows_per_wave = (int64_t)(64 / v.G) * v.U;
     const int64_t waves = (rows + rows_per_wave - 1) / rows_per_wave;
-    return (waves + 3) / 4;
+    return (waves + kWaveGroupWaves - 1) / kWaveGroupWaves;
 }
 
 hipError_t launch_wave_row(const Launch& L, int variant);

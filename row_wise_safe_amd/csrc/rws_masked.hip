@@ -24,7 +24,7 @@ template <int DT, bool AL, int G, int K, int U>
 static hipError_t wr(const Launch& L, const MaskArgs& M) {
     const WaveRowVariant v = {G, K, U};
     hipLaunchKernelGGL((k_wave_row<DT, AL, G, K, U, MaskPre<DT>>),
-                       dim3((unsigned)wave_row_grid(v, L.rows)), dim3(256), 0, L.stream, L.in,
+                       dim3((unsigned)wave_row_grid(v, L.rows)), dim3(kWaveGroupThreads), 0, L.stream, L.in,
                        L.out, L.rows, L.cols, (int)L.same_phase, (int)L.remap, make_pre<DT>(M));
     return hipGetLastError();
 }

@@ -163,8 +163,8 @@ __global__ __launch_bounds__(256) void k_norm_wave(const void* __restrict__ in,
     const int lane = threadIdx.x & 63;
     const int gl = lane & (G - 1);
     const int sub = lane / G;
-    const int64_t wave_id =
-        (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t wave_id = (int64_t)blockIdx.x * (int64_t)(blockDim.x >> 6) +
+                            __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t row0 = wave_id * (RPS * U);
     const char* tbeg = (const char*)in;
     const char* tend = tensor_end<DT>(in, rows, cols);
@@ -329,12 +329,12 @@ __global__ __launch_bounds__(BLOCK) void k_norm_stream(const void* __restrict__ 
     const char* tend = tensor_end<DT>(in, rows, cols);
     const Win w(in, out, row, cols);
 
-    // pass 1: moments
+    // pass 1: moments (cached loads: pass 2 reads the row again)
     float n = 0.0f, m = 0.0f, q = 0.0f;
     for (int k0 = t; k0 < w.ngran; k0 += BLOCK * U) {
         u32x4 raw[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = w.fetch(k0 + BLOCK * u, tbeg, tend);
+        for (int u = 0; u < U; ++u) raw[u] = w.template fetch<false>(k0 + BLOCK * u, tbeg, tend);
         float v[U * VEC];
 #pragma unroll
         for (int u = 0; u < U; ++u) widen_zero<DT>(w, k0 + BLOCK * u, raw[u], &v[u * VEC], tbeg, tend);

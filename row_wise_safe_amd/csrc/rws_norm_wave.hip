@@ -16,7 +16,6 @@ namespace rws {
     X(8, 6, 1)                    \
     X(32, 1, 1)                   \
     X(64, 1, 1)                   \
-    X(64, 1, 2)                   \
     X(64, 2, 1)                   \
     X(64, 4, 1)                   \
     X(64, 8, 1)
@@ -31,10 +30,10 @@ static hipError_t nw_mode(const NormLaunch& L) {
     const WaveRowVariant v = {G, K, U};
     const dim3 grid((unsigned)wave_row_grid(v, L.rows));
     if (L.args.w || L.args.b)
-        hipLaunchKernelGGL((k_norm_wave<DT, AL, G, K, U, MODE, true>), grid, dim3(256), 0, L.stream,
+        hipLaunchKernelGGL((k_norm_wave<DT, AL, G, K, U, MODE, true>), grid, dim3(kWaveGroupThreads), 0, L.stream,
                            L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase);
     else
-        hipLaunchKernelGGL((k_norm_wave<DT, AL, G, K, U, MODE, false>), grid, dim3(256), 0, L.stream,
+        hipLaunchKernelGGL((k_norm_wave<DT, AL, G, K, U, MODE, false>), grid, dim3(kWaveGroupThreads), 0, L.stream,
                            L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase);
     return hipGetLastError();
 }

@@ -48,20 +48,22 @@ hipError_t launch_splitk(const Launch& L, int variant, int P, float2* ws) {
 
 // ===========================================================================
 // Plain 16-byte copy (the copy ceiling and the calibration of the traffic
-// counters): one granule per thread, non-temporal stores like the softmax
-// kernels (the fastest plain copy measured on MI355X).
+// counters): one granule per thread, non-temporal loads and stores,
+// one-wave workgroups -- like the wave_row kernels, and the fastest copy of
+// HBM-resident data measured on MI355X (64 MiB: 21.9 us; 23.1 us with
+// cached loads and four-wave workgroups).
 // ===========================================================================
-__global__ __launch_bounds__(256) void k_copy16(const u32x4* __restrict__ in,
-                                                u32x4* __restrict__ out, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) __builtin_nontemporal_store(in[i], out + i);
+__global__ __launch_bounds__(64) void k_copy16(const u32x4* __restrict__ in,
+                                               u32x4* __restrict__ out, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    if (i < n) __builtin_nontemporal_store(__builtin_nontemporal_load(in + i), out + i);
 }
 
 hipError_t launch_copy16(const void* in, void* out, int64_t n16, hipStream_t stream) {
     for (int64_t done = 0; done < n16;) {
-        // at most 2^23 workgroups of 256 threads per launch
+        // at most 2^25 one-wave workgroups per launch
         const int64_t n = std::min<int64_t>(n16 - done, (int64_t)1 << 31);
-        hipLaunchKernelGGL(k_copy16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+        hipLaunchKernelGGL(k_copy16, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, stream,
                            (const u32x4*)in + done, (u32x4*)out + done, n);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -85,7 +85,10 @@ __global__ __launch_bounds__(BLOCK) void k_splitk_ordered(const void* __restrict
     // Both stages start by loading the chunk; a stage-2 workgroup's loads
     // are then in flight while it waits for the partials.
     u32x4 raw[KC];
-    splitk_fetch<DT, ALIGNED, BLOCK, KC>(w, kbase, tbeg, tend, raw);
+    if (merge_stage)
+        splitk_fetch<DT, ALIGNED, BLOCK, KC, true>(w, kbase, tbeg, tend, raw);
+    else
+        splitk_fetch<DT, ALIGNED, BLOCK, KC, false>(w, kbase, tbeg, tend, raw);
 
     if (!merge_stage) {
         const float2 md =

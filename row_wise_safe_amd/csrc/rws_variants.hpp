@@ -6,15 +6,10 @@
 // (G lanes per row, K granules per lane, U row sets per wave)
 #define RWS_WAVE_ROW_VARIANTS(X) \
     X(4, 1, 1)                   \
-    X(4, 1, 2)                   \
     X(8, 1, 1)                   \
-    X(8, 1, 2)                   \
     X(16, 1, 1)                  \
-    X(16, 1, 2)                  \
     X(32, 1, 1)                  \
-    X(32, 1, 2)                  \
     X(64, 1, 1)                  \
-    X(64, 1, 2)                  \
     X(64, 2, 1)                  \
     X(64, 4, 1)                  \
     X(64, 8, 1)
