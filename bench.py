@@ -314,7 +314,7 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     sh = int(stream.cuda_stream)
     desc = rws.softmax_describe_launch(w.rows, w.cols, code, xs[0].data_ptr(), ys[0].data_ptr(),
-                                       kid)
+                                       kid, masked=args.masked)
     family = desc.split("<")[0]
     if args.norm:
         desc = f"{args.norm} {args.kernel}"

@@ -262,6 +262,14 @@ int softmax_select_kernel(int64_t rows, int64_t cols, int dtype, const void *in,
 int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void *in,
                             const void *out, int kernel_id, char *buf, int64_t buflen);
 
+/*
+ * softmax_describe_launch_masked -- the same for the launch
+ * softmax_fwd_masked(kernel_id) would make (the masked form may choose
+ * another variant of the family).  Performs no GPU work.
+ */
+int softmax_describe_launch_masked(int64_t rows, int64_t cols, int dtype, const void *in,
+                                   const void *out, int kernel_id, char *buf, int64_t buflen);
+
 /* Name of a kernel family ("wave_row", ...), or "unknown". Static storage. */
 const char *softmax_kernel_name(int kernel_id);
 

@@ -123,11 +123,13 @@ int wave_row_wa(const rws::WaveRowVariant& v) { return v.G * 16 >= 128 ? 128 : 1
 int64_t onepass_capacity(const rws::OnepassVariant& v) { return (int64_t)v.block * (v.kr + v.kl); }
 
 // Choose among the wave_row variants: the narrowest lane group whose
-// registers hold the window, with one row set per wave, which measured
-// fastest on MI355X with rows streamed from HBM (fp16 512 columns: 21.7 us
-// vs 23.8 us with two; bf16 128 columns with 16-lane groups: 79.8 us vs
-// 81.8 us with two).
-int pick_wave_row(const Geometry& g) {
+// registers hold the window, then the number of row sets per wave that
+// measured fastest on MI355X with rows streamed from HBM: one for plain
+// softmax (fp16 512 columns: 21.9 us vs 23.1 us with two; bf16 128 columns
+// with 16-lane groups: 79.8 us vs 81.8 us), two for the masked form of
+// one-granule full-wave rows (fp16 [65536,512] with a [512,512] mask and
+// causal limit: 22.7 us vs 25.4 us with one).
+int pick_wave_row(const Geometry& g, bool masked = false) {
     int best = -1;
     int64_t best_key = 0;
     for (int i = 0; i < rws::kNumWaveRow; ++i) {
@@ -135,7 +137,8 @@ int pick_wave_row(const Geometry& g) {
         const int64_t w = window_granules(g, wave_row_wa(v));
         if ((int64_t)v.G * v.K < w) continue;
         const int64_t cap = (int64_t)v.G * v.K;
-        const int64_t key = cap * 64 + v.U;
+        const int want_u = (masked && v.G == 64 && v.K == 1) ? 2 : 1;
+        const int64_t key = cap * 64 + (v.U == want_u ? 0 : v.U);
         if (best < 0 || key < best_key) {
             best = i;
             best_key = key;
@@ -281,7 +284,7 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
     p->window = wline;
     switch (family) {
         case RWS_KERNEL_WAVE_ROW: {
-            p->variant = pick_wave_row(g);
+            p->variant = pick_wave_row(g, masked);
             if (p->variant < 0)
                 return fail(RWS_ERR_UNSUPPORTED_SHAPE,
                             "wave_row holds at most 512 granules (16 bytes) per row window");
@@ -873,8 +876,8 @@ int softmax_select_kernel(int64_t rows, int64_t cols, int dtype, const void* in,
     return st == RWS_OK ? p.family : -st;
 }
 
-int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void* in,
-                            const void* out, int kernel_id, char* buf, int64_t buflen) {
+static int describe_launch(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
+                           int kernel_id, bool masked, char* buf, int64_t buflen) {
     g_last_error.clear();
     if (!buf || buflen <= 0) return fail(RWS_ERR_INVALID_ARG, "no output buffer");
     buf[0] = 0;
@@ -889,7 +892,7 @@ int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void* i
         return RWS_OK;
     }
     Plan p;
-    const int st = plan_launch(rows, cols, dtype, in, out, kernel_id, &p);
+    const int st = plan_launch(rows, cols, dtype, in, out, kernel_id, &p, masked);
     if (st != RWS_OK) return st;
     const char* al = p.aligned ? "aligned" : (p.same_phase ? "unaligned" : "unaligned,split-phase");
     const int64_t wmax = p.window;
@@ -948,6 +951,16 @@ int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void* i
         }
     }
     return RWS_OK;
+}
+
+int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void* in,
+                            const void* out, int kernel_id, char* buf, int64_t buflen) {
+    return describe_launch(rows, cols, dtype, in, out, kernel_id, false, buf, buflen);
+}
+
+int softmax_describe_launch_masked(int64_t rows, int64_t cols, int dtype, const void* in,
+                                   const void* out, int kernel_id, char* buf, int64_t buflen) {
+    return describe_launch(rows, cols, dtype, in, out, kernel_id, true, buf, buflen);
 }
 
 const char* softmax_kernel_name(int kernel_id) {

@@ -10,6 +10,7 @@
     X(16, 1, 1)                  \
     X(32, 1, 1)                  \
     X(64, 1, 1)                  \
+    X(64, 1, 2)                  \
     X(64, 2, 1)                  \
     X(64, 4, 1)                  \
     X(64, 8, 1)

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("softmax_fwd", "softmax_fwd_kernel", "softmax_select_kernel",
-              "softmax_describe_launch", "softmax_kernel_name", "softmax_status_string",
+              "softmax_describe_launch", "softmax_describe_launch_masked",
+              "softmax_kernel_name", "softmax_status_string",
               "softmax_last_error", "softmax_copy_bytes", "layernorm_fwd", "rmsnorm_fwd",
               "layernorm_fwd_kernel", "rmsnorm_fwd_kernel"):
         assert n in names
@@ -128,6 +129,15 @@ def test_describe_mentions_alignment(lib):
     assert "unaligned" in rws.softmax_describe_launch(8, 100, rws.RWS_F16, 258, 258)
     assert "split-phase" in rws.softmax_describe_launch(8, 100, rws.RWS_F16, 258, 256)
     assert ",aligned" in rws.softmax_describe_launch(8, 128, rws.RWS_F16, 256, 512)
+
+
+def test_masked_launch_choice(lib):
+    # full-wave fp16 rows: one row set per wave for plain softmax, two for the
+    # masked form (each measured fastest on MI355X)
+    plain = rws.softmax_describe_launch(65536, 512, rws.RWS_F16, 256, 512)
+    masked = rws.softmax_describe_launch(65536, 512, rws.RWS_F16, 256, 512, masked=True)
+    assert "G=64,K=1,U=1" in plain and "block=64" in plain
+    assert "G=64,K=1,U=2" in masked
 
 
 def test_masked_argument_checks(lib):
