@@ -89,7 +89,6 @@ struct Plan {
     int64_t window = 0;  // granules per row window (upper bound)
     bool aligned = false;
     bool same_phase = false;
-    bool remap = true;
 };
 
 // Alignment facts of one call.
@@ -292,11 +291,6 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
             const int wa = wave_row_wa(v);
             p->aligned = wa == 128 ? g.a128 : g.a16;
             p->window = window_granules(g, wa);
-            // Consecutive workgroups go round-robin over the 8 XCDs, which
-            // spreads neighbouring rows over all of them; the XCD-contiguous
-            // order measured slower with rows streamed from HBM (fp16
-            // [65536,512]: 23.1 us vs 21.7 us).
-            p->remap = false;
             // keep the threads of one launch below 2^32 (2^25 waves)
             p->max_rows_per_launch = (int64_t)(64 / v.G) * v.U * 4 * ((int64_t)1 << 23);
             break;
@@ -306,7 +300,6 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
             if (p->variant < 0)
                 return fail(RWS_ERR_UNSUPPORTED_SHAPE,
                             "block_onepass holds at most 16384 granules (16 bytes) per row window");
-            p->remap = false;
             p->max_rows_per_launch = (int64_t)1 << 22;
             break;
         }
@@ -316,7 +309,6 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
             p->variant = 0;
             for (int i = 0; i < rws::kNumTwoPass; ++i)
                 if (rws::kTwoPass[i].block == want_block && rws::kTwoPass[i].u == 4) p->variant = i;
-            p->remap = false;
             p->max_rows_per_launch = (int64_t)1 << 22;
             break;
         }
@@ -335,7 +327,6 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
                             "(workgroups/capacity per variant:" + caps + ")");
             }
             p->P = P;
-            p->remap = false;
             p->max_rows_per_launch = rows;
             break;
         }
@@ -345,7 +336,6 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
             p->variant = pick_splitk(rows, wline, cus, &P);
             if (p->variant < 0) return fail(RWS_ERR_UNSUPPORTED_SHAPE, "split-k: no variant");
             p->P = P;
-            p->remap = false;
             // Every stage-2 workgroup of the ordered form polls all P of its
             // row's partials (two tagged words each, read past the L2): past
             // kOrderedMaxP chunks per row that costs more than the launch it
@@ -567,7 +557,6 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
         L.dtype = dtype;
         L.aligned = p.aligned;
         L.same_phase = p.same_phase;
-        L.remap = p.remap;
         L.stream = s;
         hipError_t e = hipSuccess;
         if (mask) {
@@ -900,8 +889,8 @@ static int describe_launch(int64_t rows, int64_t cols, int dtype, const void* in
         case RWS_KERNEL_WAVE_ROW: {
             const rws::WaveRowVariant& v = rws::kWaveRow[p.variant];
             std::snprintf(buf, (size_t)buflen,
-                          "wave_row<%s,%s,G=%d,K=%d,U=%d>%s grid=%lld block=%d window<=%lld",
-                          dtype_name(dtype), al, v.G, v.K, v.U, p.remap ? " xcd" : "",
+                          "wave_row<%s,%s,G=%d,K=%d,U=%d> grid=%lld block=%d window<=%lld",
+                          dtype_name(dtype), al, v.G, v.K, v.U,
                           (long long)rws::wave_row_grid(v, std::min(rows, p.max_rows_per_launch)),
                           rws::kWaveGroupThreads, (long long)wmax);
             break;
@@ -909,15 +898,15 @@ static int describe_launch(int64_t rows, int64_t cols, int dtype, const void* in
         case RWS_KERNEL_BLOCK_ONEPASS: {
             const rws::OnepassVariant& v = rws::kOnepass[p.variant];
             std::snprintf(buf, (size_t)buflen,
-                          "block_onepass<%s,%s,B=%d,KR=%d,KL=%d>%s grid=%lld block=%d window<=%lld",
-                          dtype_name(dtype), al, v.block, v.kr, v.kl, p.remap ? " xcd" : "",
+                          "block_onepass<%s,%s,B=%d,KR=%d,KL=%d> grid=%lld block=%d window<=%lld",
+                          dtype_name(dtype), al, v.block, v.kr, v.kl,
                           (long long)std::min(rows, p.max_rows_per_launch), v.block, (long long)wmax);
             break;
         }
         case RWS_KERNEL_TWO_PASS: {
             const rws::TwoPassVariant& v = rws::kTwoPass[p.variant];
-            std::snprintf(buf, (size_t)buflen, "two_pass<%s,%s,B=%d,U=%d>%s grid=%lld block=%d window<=%lld",
-                          dtype_name(dtype), al, v.block, v.u, p.remap ? " xcd" : "",
+            std::snprintf(buf, (size_t)buflen, "two_pass<%s,%s,B=%d,U=%d> grid=%lld block=%d window<=%lld",
+                          dtype_name(dtype), al, v.block, v.u,
                           (long long)std::min(rows, p.max_rows_per_launch), v.block, (long long)wmax);
             break;
         }
@@ -933,8 +922,8 @@ static int describe_launch(int64_t rows, int64_t cols, int dtype, const void* in
         case RWS_KERNEL_SPLITK: {
             const rws::SplitkVariant& v = rws::kSplitk[p.variant];
             std::snprintf(buf, (size_t)buflen,
-                          "splitk<%s,%s,B=%d,KC=%d>%s P=%d grid=%lld x2 block=%d window<=%lld",
-                          dtype_name(dtype), al, v.block, v.kc, p.remap ? " xcd" : "", p.P,
+                          "splitk<%s,%s,B=%d,KC=%d> P=%d grid=%lld x2 block=%d window<=%lld",
+                          dtype_name(dtype), al, v.block, v.kc, p.P,
                           (long long)(std::min(rows, p.max_rows_per_launch) * p.P), v.block,
                           (long long)wmax);
             break;

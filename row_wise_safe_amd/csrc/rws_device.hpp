@@ -340,22 +340,6 @@ __device__ inline float merge_scale(float m_part, float M) {
 }
 
 // ---------------------------------------------------------------------------
-// XCD-aware workgroup order.  MI355X has 8 XCDs (each with its own L2) and
-// hands out consecutive workgroups round-robin across them, so workgroup b
-// runs on XCD b % 8.  Renumbering gives each XCD one contiguous range of the
-// logical work (rows).  The map is a bijection of [0, nb) for any nb; the
-// dispatcher enables it per kernel family where it measured faster.
-// ---------------------------------------------------------------------------
-constexpr int kXcds = 8;
-
-__device__ inline int64_t xcd_remap(int64_t b, int64_t nb) {
-    const int64_t x = b % kXcds;       // XCD this workgroup runs on
-    const int64_t j = b / kXcds;       // its rank among that XCD's workgroups
-    const int64_t q = nb / kXcds, r = nb % kXcds;
-    return x * q + (x < r ? x : r) + j;
-}
-
-// ---------------------------------------------------------------------------
 // Cross-lane reductions within aligned groups of G lanes (G = 4..64) of a
 // 64-lane wave.  Every lane of a group ends with the same bits (each step
 // combines a lane with its partner and the partner with it, and the ops are

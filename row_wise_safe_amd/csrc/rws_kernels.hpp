@@ -76,7 +76,7 @@ __device__ inline void fetch_pre(const Pre& pre, const typename Pre::Ctx& pc, co
 template <int DT, bool ALIGNED, int G, int K, int U, class Pre = NoPre>
 __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
                                                   void* __restrict__ out, int64_t rows,
-                                                  int cols, int same_phase, int remap,
+                                                  int cols, int same_phase,
                                                   Pre pre = Pre()) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int RPS = 64 / G;  // rows per set
@@ -85,8 +85,7 @@ __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
     const int gl = lane & (G - 1);
     const int sub = lane / G;
     // The wave index is uniform: readfirstlane keeps the row arithmetic scalar.
-    const int64_t block = (remap ? xcd_remap(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
-    const int64_t wave_id = block * (int64_t)(blockDim.x >> 6) +
+    const int64_t wave_id = (int64_t)blockIdx.x * (int64_t)(blockDim.x >> 6) +
                             __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t row0 = wave_id * (RPS * U);
     const char* tbeg = (const char*)in;
@@ -160,7 +159,7 @@ __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
 template <int DT, bool ALIGNED, int BLOCK, int KR, int KL, class Pre = NoPre>
 __global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict__ in,
                                                          void* __restrict__ out, int64_t rows,
-                                                         int cols, int same_phase, int remap,
+                                                         int cols, int same_phase,
                                                          Pre pre = Pre()) {
     static_assert(!Pre::kActive || KL == 0, "prologues apply to register-held rows only");
     constexpr int VEC = Elem<DT>::VEC;
@@ -170,7 +169,7 @@ __global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict_
     __shared__ float red_sum[W];
     __shared__ u32x4 park[KL > 0 ? KL : 1][BLOCK];
     const int t = threadIdx.x;
-    const int64_t row = (remap ? xcd_remap(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
+    const int64_t row = blockIdx.x;
     const char* tbeg = (const char*)in;
     const char* tend = tensor_end<DT>(in, rows, cols);
     const RowWin<DT, ALIGNED> w(in, out, row, cols);
@@ -296,14 +295,14 @@ __device__ inline void block_merge(float m, float d, float& M, float& D, float* 
 template <int DT, bool ALIGNED, int BLOCK, int U, class Pre = NoPre>
 __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
                                                     void* __restrict__ out, int64_t rows,
-                                                    int cols, int same_phase, int remap,
+                                                    int cols, int same_phase,
                                                     Pre pre = Pre()) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     __shared__ float red_max[W];
     __shared__ float red_sum[W];
     const int t = threadIdx.x;
-    const int64_t row = (remap ? xcd_remap(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
+    const int64_t row = blockIdx.x;
     const char* tbeg = (const char*)in;
     const char* tend = tensor_end<DT>(in, rows, cols);
     const RowWin<DT, ALIGNED> w(in, out, row, cols);
@@ -441,12 +440,12 @@ __device__ inline void splitk_write(const RowWin<DT, ALIGNED>& w, int kbase,
 template <int DT, bool ALIGNED, int BLOCK, int KC>
 __global__ __launch_bounds__(BLOCK) void k_splitk_stage1(const void* __restrict__ in,
                                                          int64_t rows, int cols, int P,
-                                                         float2* __restrict__ ws, int remap) {
+                                                         float2* __restrict__ ws) {
     constexpr int W = BLOCK / 64;
     __shared__ float red_max[W];
     __shared__ float red_sum[W];
     const int t = threadIdx.x;
-    const int64_t b = (remap ? xcd_remap(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
+    const int64_t b = blockIdx.x;
     const int64_t row = b / P;
     const int chunk = (int)(b - row * P);
     const char* tbeg = (const char*)in;
@@ -466,12 +465,12 @@ __global__ __launch_bounds__(BLOCK) void k_splitk_stage2(const void* __restrict_
                                                          void* __restrict__ out, int64_t rows,
                                                          int cols, int P,
                                                          const float2* __restrict__ ws,
-                                                         int same_phase, int remap) {
+                                                         int same_phase) {
     constexpr int W = BLOCK / 64;
     __shared__ float red_max[W];
     __shared__ float red_sum[W];
     const int t = threadIdx.x;
-    const int64_t b = (remap ? xcd_remap(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x);
+    const int64_t b = blockIdx.x;
     const int64_t row = b / P;
     const int chunk = (int)(b - row * P);
     const char* tbeg = (const char*)in;

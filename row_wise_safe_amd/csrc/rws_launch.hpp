@@ -16,7 +16,6 @@ struct Launch {
     int dtype;        // kF32 / kF16 / kBF16
     bool aligned;     // in, out 128-byte aligned and cols*size % 128 == 0
     bool same_phase;  // (in - out) % 16 == 0
-    bool remap;       // XCD-aware workgroup order
     hipStream_t stream;
 };
 

@@ -18,11 +18,11 @@ template <int DT, bool AL, int B, int KC>
 static hipError_t go(const Launch& L, int P, float2* ws) {
     const dim3 grid((unsigned)(L.rows * P));
     hipLaunchKernelGGL((k_splitk_stage1<DT, AL, B, KC>), grid, dim3(B), 0, L.stream, L.in, L.rows,
-                       L.cols, P, ws, (int)L.remap);
+                       L.cols, P, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_splitk_stage2<DT, AL, B, KC>), grid, dim3(B), 0, L.stream, L.in, L.out,
-                       L.rows, L.cols, P, (const float2*)ws, (int)L.same_phase, (int)L.remap);
+                       L.rows, L.cols, P, (const float2*)ws, (int)L.same_phase);
     return hipGetLastError();
 }
 
