@@ -385,7 +385,8 @@ def main() -> int:
     gbps = nbytes / (ms * 1e-3) / 1e9
     log(f"[bench] {ms * 1e3:.2f} us/call, {gbps:.1f} GB/s (rotating)")
 
-    # single buffer (hot, last-level-cache resident input)
+    # single buffer: the same input and output every call (the kernels load
+    # their input non-temporally, so little of it stays cached between calls)
     hot = None
     if not args.skip_hot:
         for i in range(args.warmup):

@@ -30,8 +30,8 @@
 // the buffer is zero-filled when it is allocated and when the 32-bit epoch
 // wraps, so a word from an earlier launch never matches.
 //
-// Measured on MI355X, fp16 [16, 1M]: 14.3-14.6 us against 15.2-15.5 us for
-// the two launches (the stage-2 workgroups start while the last stage-1
+// Measured on MI355X, fp16 [16, 1M] read from HBM: 14.1 us against 15.2 us
+// for the two launches (the stage-2 workgroups start while the last stage-1
 // workgroups finish, instead of after a kernel boundary).
 #include "rws_kernels.hpp"
 #include "rws_launch.hpp"

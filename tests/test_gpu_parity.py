@@ -179,7 +179,9 @@ def test_guard_zones_untouched(dtype, cols):
     for kernel in ["auto"] + KERNELS:
         if kernel != "auto" and not supports(kernel, cols, dtype, False):
             continue
-        for off in (0, 1):
+        # off 3: the output has the input's 16-byte phase, so partial
+        # granules go out as aligned pieces; 0 and 1: element stores
+        for off in (0, 1, 3):
             buf = torch.full((rows * cols + 2 * guard + off,), -7.0, dtype=x.dtype, device="cuda")
             before = buf.clone()
             out = buf[guard + off:guard + off + rows * cols].view(rows, cols)
