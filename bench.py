@@ -184,12 +184,54 @@ def read_traffic(workload: str, kernel: str):
 
 
 # --------------------------------------------------------------------------
+# HIP runtime queries used only for reporting (device HBM figures, the
+# runtime's own device-to-device copy as a second reference)
+# --------------------------------------------------------------------------
+_HIP_ATTR_MEMORY_BUS_WIDTH = 59   # hipDeviceAttributeMemoryBusWidth (bits)
+_HIP_ATTR_MEMORY_CLOCK_RATE = 60  # hipDeviceAttributeMemoryClockRate (kHz)
+
+
+def _hip_runtime():
+    import ctypes
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+    lib.hipDeviceGetAttribute.restype = ctypes.c_int
+    lib.hipMemcpyDtoDAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]
+    lib.hipMemcpyDtoDAsync.restype = ctypes.c_int
+    return lib
+
+
+def device_hbm(device: int = 0) -> dict:
+    """Memory clock and bus width as the runtime reports them, next to the
+    published peak the roofline uses: the transfers per reported clock that
+    the published 8 TB/s implies over that bus (MI355X reports a 2 GHz
+    memory clock and an 8192-bit bus, so 8 TB/s is ~3.9 transfers per clock,
+    i.e. ~7.8 Gb/s per pin)."""
+    import ctypes
+    lib = _hip_runtime()
+    vals = {}
+    for key, attr in (("memory_clock_khz", _HIP_ATTR_MEMORY_CLOCK_RATE),
+                      ("bus_width_bits", _HIP_ATTR_MEMORY_BUS_WIDTH)):
+        v = ctypes.c_int(0)
+        vals[key] = v.value if lib.hipDeviceGetAttribute(ctypes.byref(v), attr, device) == 0 \
+            else None
+    vals["published_peak_GBps"] = PEAK_HBM_GBPS
+    if vals["memory_clock_khz"] and vals["bus_width_bits"]:
+        bus_bytes_per_clock = vals["memory_clock_khz"] * 1e3 * vals["bus_width_bits"] / 8
+        vals["published_peak_transfers_per_clock"] = round(PEAK_HBM_GBPS * 1e9
+                                                           / bus_bytes_per_clock, 3)
+    return vals
+
+
+# --------------------------------------------------------------------------
 # CPU baseline: the oracle on the host cores
 # --------------------------------------------------------------------------
-def cpu_baseline(w, x_stored_f64, target_s: float = 10.0) -> dict:
+def cpu_baseline(w, x_stored_f64, target_s: float = 10.0, threads: int | None = None) -> dict:
     import oracle
-    threads = max(1, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
-                  else (os.cpu_count() or 1))
+    if threads is None:
+        threads = max(1, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+                      else (os.cpu_count() or 1))
     rows = x_stored_f64.shape[0]
     t0 = time.perf_counter()
     passes = 0
@@ -415,19 +457,36 @@ def main() -> int:
     copy_gbps = 2 * in_bytes / (copy_ms * 1e-3) / 1e9
     log(f"[bench] copy ceiling {copy_ms * 1e3:.2f} us, {copy_gbps:.1f} GB/s")
 
+    # the runtime's device-to-device copy of the same bytes, same rotation
+    hip = _hip_runtime()
+    for i in range(min(args.warmup, 200)):
+        hip.hipMemcpyDtoDAsync(ys[i % nbuf].data_ptr(), xs[i % nbuf].data_ptr(), in_bytes, sh)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        hip.hipMemcpyDtoDAsync(ys[i % nbuf].data_ptr(), xs[i % nbuf].data_ptr(), in_bytes, sh)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    memcpy_ms = e0.elapsed_time(e1) / args.steps
+    memcpy_gbps = 2 * in_bytes / (memcpy_ms * 1e-3) / 1e9
+    log(f"[bench] hipMemcpyDtoDAsync {memcpy_ms * 1e3:.2f} us, {memcpy_gbps:.1f} GB/s")
+
     if args.meta_out:
         os.makedirs(os.path.dirname(os.path.abspath(args.meta_out)), exist_ok=True)
         with open(args.meta_out, "w") as f:
             json.dump({"workload": w.name, "bytes_per_call": nbytes, "copy_bytes": in_bytes,
                        "launch": desc}, f)
 
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         stored = x_host.to(torch.float64).numpy()
         cpu = (norm_cpu_baseline(w, stored, args.norm, args.cpu_seconds) if args.norm
                else cpu_baseline(w, stored, args.cpu_seconds))
         log(f"[bench] cpu oracle {cpu['value']} GB/s on {cpu['cores']} threads")
+        if not args.norm and cpu["cores"] > 1:
+            cpu1 = cpu_baseline(w, stored, args.cpu_seconds / 3, threads=1)
+            log(f"[bench] cpu oracle {cpu1['value']} GB/s on 1 thread")
 
     profile_key = (args.norm if args.norm else "masked" if mask is not None
                    else "backward" if dys is not None else family)
@@ -467,7 +526,11 @@ def main() -> int:
         "hot_single_buffer": hot,
         "copy_ceiling": {"us_per_call": round(copy_ms * 1e3, 3), "GBps": round(copy_gbps, 2),
                          "frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4)},
+        "hip_memcpy_dtod": {"us_per_call": round(memcpy_ms * 1e3, 3),
+                            "GBps": round(memcpy_gbps, 2)},
+        "device_hbm": device_hbm(dev.index or 0),
         "cpu_baseline": cpu,
+        "cpu_baseline_single_thread": cpu1,
     }
     print(json.dumps(result), flush=True)
     return 0
