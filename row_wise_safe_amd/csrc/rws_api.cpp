@@ -121,6 +121,13 @@ int wave_row_wa(const rws::WaveRowVariant& v) { return v.G * 16 >= 128 ? 128 : 1
 
 int64_t onepass_capacity(const rws::OnepassVariant& v) { return (int64_t)v.block * (v.kr + v.kl); }
 
+// Rows per launch of a workgroup-per-row kernel: the launch's thread count
+// (rows x block) must stay below 2^32, the width of the dispatch's grid size;
+// batches of at most 2^31 threads and 2^22 rows.
+int64_t block_rows_per_launch(int block) {
+    return std::min<int64_t>((int64_t)1 << 22, ((int64_t)1 << 31) / block);
+}
+
 // Choose among the wave_row variants: the narrowest lane group whose
 // registers hold the window, then the number of row sets per wave that
 // measured fastest on MI355X with rows streamed from HBM: one for plain
@@ -128,13 +135,14 @@ int64_t onepass_capacity(const rws::OnepassVariant& v) { return (int64_t)v.block
 // with 16-lane groups: 79.8 us vs 81.8 us), two for the masked form of
 // one-granule full-wave rows (fp16 [65536,512] with a [512,512] mask and
 // causal limit: 22.7 us vs 25.4 us with one).
-int pick_wave_row(const Geometry& g, bool masked = false) {
+// max_k limits the granules per lane.
+int pick_wave_row(const Geometry& g, bool masked = false, int max_k = 1 << 30) {
     int best = -1;
     int64_t best_key = 0;
     for (int i = 0; i < rws::kNumWaveRow; ++i) {
         const rws::WaveRowVariant& v = rws::kWaveRow[i];
         const int64_t w = window_granules(g, wave_row_wa(v));
-        if ((int64_t)v.G * v.K < w) continue;
+        if ((int64_t)v.G * v.K < w || v.K > max_k) continue;
         const int64_t cap = (int64_t)v.G * v.K;
         const int want_u = (masked && v.G == 64 && v.K == 1) ? 2 : 1;
         const int64_t key = cap * 64 + (v.U == want_u ? 0 : v.U);
@@ -146,13 +154,46 @@ int pick_wave_row(const Geometry& g, bool masked = false) {
     return best;
 }
 
-int pick_onepass(int64_t w, bool regs_only = false) {
+// A launch with few waves: at one granule per thread (and at most 16 waves
+// per row) it fills each CU with at most kFewWavesPerCu waves, so it is
+// latency-bound and each row is best spread over many threads.
+constexpr int64_t kFewWavesPerCu = 32;
+
+bool few_waves(int64_t rows, int64_t w, int cus) {
+    return rows * std::min<int64_t>((w + 63) / 64, 16) <= kFewWavesPerCu * cus;
+}
+
+// Choose a block_onepass variant for rows of w granules (line window), by
+// sweeps on MI355X with inputs in HBM:
+//  * few waves: the fewest granules per thread, then the smallest workgroup
+//    (fp32 [64,1000]: 2.84 us with 320x1 against 4.36 us for one wave per row
+//    with 8 granules per lane; fp16 [1024,2000]: 4.03 us with 320x1, 4.29
+//    with 192x2, 5.66 with one wave per row);
+//  * otherwise: 2-5 register granules per thread with the fewest idle slots,
+//    ties to fewer granules per thread -- the fastest shape of each sweep:
+//    fp16 rows of 1000 columns (window 133) 64x3, 2000 (258) 64x5, 4000 (508)
+//    256x2, 4097 (521) 192x3, 8000 (1008) 512x2;
+//  * rows longer than those shapes hold: the smallest capacity.
+int pick_onepass(int64_t w, int64_t rows, int cus, bool regs_only = false) {
+    const bool few = few_waves(rows, w, cus);
     int best = -1;
+    int64_t best_key = 0;
     for (int i = 0; i < rws::kNumOnepass; ++i) {
-        if (regs_only && rws::kOnepass[i].kl != 0) continue;
-        if (onepass_capacity(rws::kOnepass[i]) < w) continue;
-        if (best < 0 || onepass_capacity(rws::kOnepass[i]) < onepass_capacity(rws::kOnepass[best]))
+        const rws::OnepassVariant& v = rws::kOnepass[i];
+        if (regs_only && v.kl != 0) continue;
+        const int64_t cap = onepass_capacity(v);
+        if (cap < w) continue;
+        int64_t key;
+        if (few)
+            key = (int64_t)(v.kr + v.kl) * (1 << 20) + cap;
+        else if (v.kl == 0 && v.kr >= 2 && v.kr <= 5)
+            key = (cap - w) * 8 + v.kr;
+        else
+            key = ((int64_t)1 << 40) + cap;
+        if (best < 0 || key < best_key) {
             best = i;
+            best_key = key;
+        }
     }
     return best;
 }
@@ -249,21 +290,29 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
     const int64_t wline = window_granules(g, 128);  // block-level kernels
     const int cus = device_info().cus;
 
+    // Family: a lane group holding the row at one granule per lane ->
+    // wave_row; few long rows -> split-k; many rows of up to two granules per
+    // lane of a full wave -> wave_row; else one workgroup per row while its
+    // registers (then LDS) hold the row; then split-k for few rows, two_pass.
+    // (One wave per row with 4 or 8 granules per lane measured slower than
+    // block_onepass at every row count tried: fp16 [32768,1000] 27.2 us
+    // against 24.5, fp16 [16384,2000] 32.8 against 23.5.)
     int family = kernel_id;
     if (family == RWS_KERNEL_AUTO) {
         const bool few_rows = rows < 2LL * cus;
-        const bool wave_fits = pick_wave_row(g) >= 0;
-        if (wline <= 136 && wave_fits) {
+        const bool onepass_fits = pick_onepass(wline, rows, cus) >= 0;
+        if (pick_wave_row(g, masked, 1) >= 0) {
             family = RWS_KERNEL_WAVE_ROW;
         } else if (few_rows && wline >= 2048) {
             family = RWS_KERNEL_SPLITK_ORDERED;
-        } else if (wline <= 512 && wave_fits) {
+        } else if (wline <= 128 && !few_waves(rows, wline, cus) &&
+                   pick_wave_row(g, masked, 2) >= 0) {
             family = RWS_KERNEL_WAVE_ROW;
-        } else if (pick_onepass(wline) >= 0 && wline <= 8192) {
+        } else if (onepass_fits && wline <= 8192) {
             family = RWS_KERNEL_BLOCK_ONEPASS;
         } else if (few_rows) {
             family = RWS_KERNEL_SPLITK_ORDERED;
-        } else if (pick_onepass(wline) >= 0) {
+        } else if (onepass_fits) {
             family = RWS_KERNEL_BLOCK_ONEPASS;
         } else {
             family = RWS_KERNEL_TWO_PASS;
@@ -273,7 +322,7 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
         // the masked forms exist for wave_row, register-only block_onepass
         // and two_pass; long rows with few rows go to two_pass
         if (is_splitk(family)) family = RWS_KERNEL_TWO_PASS;
-        if (family == RWS_KERNEL_BLOCK_ONEPASS && pick_onepass(wline, true) < 0)
+        if (family == RWS_KERNEL_BLOCK_ONEPASS && pick_onepass(wline, rows, cus, true) < 0)
             family = RWS_KERNEL_TWO_PASS;
     }
     if (masked && is_splitk(family))
@@ -296,11 +345,11 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
             break;
         }
         case RWS_KERNEL_BLOCK_ONEPASS: {
-            p->variant = pick_onepass(wline, masked);
+            p->variant = pick_onepass(wline, rows, cus, masked);
             if (p->variant < 0)
                 return fail(RWS_ERR_UNSUPPORTED_SHAPE,
                             "block_onepass holds at most 16384 granules (16 bytes) per row window");
-            p->max_rows_per_launch = (int64_t)1 << 22;
+            p->max_rows_per_launch = block_rows_per_launch(rws::kOnepass[p->variant].block);
             break;
         }
         case RWS_KERNEL_TWO_PASS: {
@@ -309,7 +358,7 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
             p->variant = 0;
             for (int i = 0; i < rws::kNumTwoPass; ++i)
                 if (rws::kTwoPass[i].block == want_block && rws::kTwoPass[i].u == 4) p->variant = i;
-            p->max_rows_per_launch = (int64_t)1 << 22;
+            p->max_rows_per_launch = block_rows_per_launch(rws::kTwoPass[p->variant].block);
             break;
         }
         case RWS_KERNEL_SPLITK_FUSED: {
@@ -688,7 +737,8 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
     }
     const int64_t max_rows = family == 1
         ? (int64_t)(64 / rws::kBwdWave[variant].G) * rws::kBwdWave[variant].U * 4 * ((int64_t)1 << 23)
-        : ((int64_t)1 << 22);
+        : block_rows_per_launch(family == 2 ? rws::kBwdBlock[variant].block
+                                            : rws::kBwdStream[variant].block);
     const int64_t row_bytes = cols * elem_size(dtype);
     for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
         rws::BwdLaunch B;
@@ -799,7 +849,8 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
     }
     const int64_t max_rows = family == 1
         ? (int64_t)(64 / rws::kNormWave[variant].G) * rws::kNormWave[variant].U * 4 * ((int64_t)1 << 23)
-        : ((int64_t)1 << 22);
+        : block_rows_per_launch(family == 2 ? rws::kNormBlock[variant].block
+                                            : rws::kNormStream[variant].block);
     const int64_t row_bytes = cols * es;
     for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
         rws::NormLaunch L;

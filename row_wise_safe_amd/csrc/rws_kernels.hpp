@@ -167,7 +167,7 @@ __global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict_
     constexpr int N = KR * VEC;
     __shared__ float red_max[W];
     __shared__ float red_sum[W];
-    __shared__ u32x4 park[KL > 0 ? KL : 1][BLOCK];
+    __shared__ u32x4 park[KL > 0 ? KL : 1][KL > 0 ? BLOCK : 1];
     const int t = threadIdx.x;
     const int64_t row = blockIdx.x;
     const char* tbeg = (const char*)in;

@@ -104,7 +104,7 @@ def test_forced_wave_row_rejects_long_rows(lib):
 # The dispatcher's routing for the five workloads (16-byte aligned pointers).
 @pytest.mark.parametrize("rows,cols,dtype,family", [
     (2, 3, rws.RWS_F32, "wave_row"),
-    (64, 1000, rws.RWS_F32, "wave_row"),
+    (64, 1000, rws.RWS_F32, "block_onepass"),  # few waves: one granule per thread
     (65536, 512, rws.RWS_F16, "wave_row"),
     (1 << 20, 128, rws.RWS_BF16, "wave_row"),
     (8192, 4097, rws.RWS_F16, "block_onepass"),
@@ -118,6 +118,43 @@ def test_dispatch_routes(lib, rows, cols, dtype, family):
     assert rws.softmax_kernel_name(kid) == family
     desc = rws.softmax_describe_launch(rows, cols, dtype, 256, 512)
     assert desc.startswith(family)
+
+
+# The launch shape chosen for rows held by one workgroup (16-byte aligned
+# pointers, 256 CUs assumed without a device): one granule per thread when the
+# launch has few waves, else 2-5 granules per thread with the fewest idle
+# slots -- the fastest shapes of sweeps on MI355X.
+@pytest.mark.parametrize("rows,cols,dtype,shape", [
+    (64, 1000, rws.RWS_F32, "B=320,KR=1"),
+    (1024, 2000, rws.RWS_F16, "B=320,KR=1"),
+    (64, 8000, rws.RWS_F16, "B=1024,KR=1"),
+    (32768, 1000, rws.RWS_F16, "B=64,KR=3"),
+    (16384, 2000, rws.RWS_F16, "B=64,KR=5"),
+    (8192, 4000, rws.RWS_F16, "B=256,KR=2"),
+    (8192, 4097, rws.RWS_F16, "B=192,KR=3"),
+    (4096, 8000, rws.RWS_F16, "B=512,KR=2"),
+])
+def test_block_shape_choice(lib, rows, cols, dtype, shape):
+    desc = rws.softmax_describe_launch(rows, cols, dtype, 256, 512)
+    assert desc.startswith("block_onepass") and shape in desc, desc
+
+
+def test_many_rows_of_two_granules_stay_on_one_wave(lib):
+    # fp16 rows of 960 columns (1920 bytes, line-aligned): 120 granules, two per lane
+    desc = rws.softmax_describe_launch(65536, 960, rws.RWS_F16, 256, 512)
+    assert desc.startswith("wave_row<f16,aligned,G=64,K=2"), desc
+    # few rows of the same length: a workgroup of one granule per thread
+    assert "KR=1" in rws.softmax_describe_launch(64, 960, rws.RWS_F16, 256, 512)
+
+
+@pytest.mark.parametrize("rows,cols", [((1 << 22) + 5, 12000), ((1 << 22) + 5, 24)])
+def test_block_launch_stays_below_2_32_threads(lib, rows, cols):
+    # the grid of one launch times its workgroup size must fit the 32-bit grid size
+    for kernel in (2, 3):  # block_onepass, two_pass
+        desc = rws.softmax_describe_launch(rows, cols, rws.RWS_F16, 256, 512, kernel)
+        grid = int(re.search(r"grid=(\d+)", desc).group(1))
+        block = int(re.search(r"block=(\d+)", desc).group(1))
+        assert grid * block < 1 << 32, desc
 
 
 def test_select_rejects_bad_args(lib):
