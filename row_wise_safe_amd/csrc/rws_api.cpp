@@ -804,7 +804,9 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
         }
         return -1;
     };
-    auto pick_wave = [&]() {
+    // max_k limits the granules per lane of the other groups; the tuned
+    // groups are taken for their windows whatever it is.
+    auto pick_wave = [&](int max_k) {
         if (wline > 8 && wline <= 32 && norm_variant(16, 2, 1) >= 0) return norm_variant(16, 2, 1);
         if (wline > 32 && wline <= 48 && norm_variant(8, 6, 1) >= 0) return norm_variant(8, 6, 1);
         int best = -1;
@@ -812,7 +814,7 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
         for (int i = 0; i < rws::kNumNormWave; ++i) {
             const rws::WaveRowVariant& v = rws::kNormWave[i];
             const int64_t cap = (int64_t)v.G * v.K;
-            if (cap < window_granules(g, wave_row_wa(v))) continue;
+            if (cap < window_granules(g, wave_row_wa(v)) || v.K > max_k) continue;
             const int64_t key = cap * 64 + v.U;
             if (best < 0 || key < best_key) {
                 best = i;
@@ -831,16 +833,24 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
         }
         return best;
     };
+    // Forms: the tuned lane groups above, or one wave per row while a lane
+    // group holds the row at one granule per lane; else one workgroup per row
+    // with one granule per thread (one wave per row with 4 or 8 granules per
+    // lane measured 1.7-2.2x slower: LayerNorm fp16 [32768,1000] 54.5 us
+    // against 32.9 with 192x1, [16384,2000] 43.9 against 30.1 with 320x1,
+    // [8192,4000] 28.8 against 25.0 with 512x1); any length streams.
     int family = kernel_id == RWS_KERNEL_AUTO ? 0 : kernel_id;
     if (family == 0) {
-        if (wline <= 512 && pick_wave() >= 0) family = 1;
+        if (pick_wave(1) >= 0) family = 1;
         else if (pick_block() >= 0) family = 2;
         else family = 3;
     }
     int variant = -1;
     bool aligned = g.a128;
     if (family == 1) {
-        variant = pick_wave();
+        // the dispatcher's choice takes one granule per lane (or a tuned
+        // group); a forced wave form takes any group that holds the row
+        variant = pick_wave(kernel_id == RWS_KERNEL_AUTO ? 1 : 1 << 30);
         if (variant < 0)
             return fail(RWS_ERR_UNSUPPORTED_SHAPE, "normalisation wave kernel holds at most 512 granules");
         aligned = wave_row_wa(rws::kNormWave[variant]) == 128 ? g.a128 : g.a16;

@@ -5,13 +5,11 @@
 namespace rws {
 
 // (threads, granules per thread held in registers)
-#define RWS_NORM_BLOCK_VARIANTS(X) \
-    X(256, 2)                      \
-    X(192, 3)                      \
-    X(256, 3)                      \
-    X(256, 4)                      \
-    X(512, 4)                      \
-    X(1024, 4)
+// (threads, register granules per thread): one granule per thread up to
+// 1024 granules per row, then 1024-thread workgroups.
+#define RWS_NORM_BLOCK_VARIANTS(X)                                       \
+    X(128, 1) X(192, 1) X(256, 1) X(320, 1) X(384, 1) X(512, 1) X(576, 1) \
+    X(640, 1) X(768, 1) X(1024, 1) X(1024, 2) X(1024, 3) X(1024, 4)
 // (threads, granules per thread per batch)
 #define RWS_NORM_STREAM_VARIANTS(X) \
     X(256, 4)                       \
