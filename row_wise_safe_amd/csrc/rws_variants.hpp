@@ -17,17 +17,15 @@
 
 // (threads, register granules per thread, LDS granules per thread): one
 // granule per thread for launches with few waves, 2-5 for many rows (the
-// dispatcher takes the shape with the fewest idle slots), and the shapes for
-// long rows.
+// dispatcher takes the shape with the fewest idle slots; these are the ones
+// that rule can reach), and the shapes for long rows.
 #define RWS_ONEPASS_VARIANTS(X)                                              \
     X(128, 1, 0) X(192, 1, 0) X(256, 1, 0) X(320, 1, 0) X(384, 1, 0)        \
     X(512, 1, 0) X(640, 1, 0) X(768, 1, 0) X(1024, 1, 0)                    \
     X(128, 2, 0) X(192, 2, 0) X(256, 2, 0) X(320, 2, 0) X(384, 2, 0)        \
     X(512, 2, 0) X(768, 2, 0) X(1024, 2, 0)                                 \
-    X(64, 3, 0) X(128, 3, 0) X(192, 3, 0) X(256, 3, 0) X(384, 3, 0)         \
-    X(512, 3, 0) X(1024, 3, 0)                                              \
-    X(64, 4, 0) X(128, 4, 0) X(256, 4, 0) X(512, 4, 0) X(1024, 4, 0)        \
-    X(64, 5, 0) X(128, 5, 0)                                                \
+    X(64, 3, 0) X(192, 3, 0) X(384, 3, 0) X(1024, 3, 0)                     \
+    X(1024, 4, 0) X(64, 5, 0)                                               \
     X(1024, 6, 0) X(1024, 8, 0) X(1024, 8, 8)
 
 // (threads, granules per thread per batch)
