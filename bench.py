@@ -91,8 +91,9 @@ def summarize_rocprof(directory: str, workload: str, kernel: str, command: str) 
     """Write profiles/<kernel>_<workload>_*.txt from rocprofv3 output in `directory`.
 
     Expects sub-directories 'trace' (--kernel-trace --stats), 'fetch'
-    (--pmc FETCH_SIZE) and 'write' (--pmc WRITE_SIZE), each holding the CSVs
-    rocprofv3 wrote.  FETCH_SIZE / WRITE_SIZE are KiB per dispatch; they are
+    (--pmc FETCH_SIZE) and 'write' (--pmc WRITE_SIZE), and optionally
+    'occupancy' (--pmc MeanOccupancyPerCU) and 'valu' (--pmc VALUBusy), each
+    holding the CSVs rocprofv3 wrote.  FETCH_SIZE / WRITE_SIZE are KiB per dispatch; they are
     scaled by what the same counter reads for the 16-byte copy kernel, whose
     true traffic is known (its bytes read and written).
     """
@@ -155,6 +156,25 @@ def summarize_rocprof(directory: str, workload: str, kernel: str, command: str) 
             if meta.get("bytes_per_call"):
                 lines.append(f"algorithmic_bytes_per_launch: {meta['bytes_per_call']}")
                 lines.append(f"traffic / algorithmic: {traffic / meta['bytes_per_call']:.4f}")
+        lines.append("")
+    # occupancy and vector-ALU activity (one derived metric per pass)
+    extra = []
+    for which, metric, unit in (("occupancy", "MeanOccupancyPerCU",
+                                 "mean resident waves per CU over the kernel (max 32)"),
+                                ("valu", "VALUBusy", "% of kernel time the vector ALUs issue")):
+        files = glob.glob(os.path.join(directory, which, "**", "*counter_collection.csv"),
+                          recursive=True)
+        if not files:
+            continue
+        per = {}
+        for r in _read_csv(files[0]):
+            if r.get("Counter_Name") == metric and sym in r.get("Kernel_Name", ""):
+                per.setdefault(r["Kernel_Name"], []).append(float(r.get("Counter_Value", 0.0)))
+        for n in sorted(per):
+            extra.append(f"kernel {n}: {metric} {sum(per[n]) / len(per[n]):.2f} ({unit})")
+    if extra:
+        lines.append("## occupancy and VALU activity (--pmc MeanOccupancyPerCU, then --pmc VALUBusy)")
+        lines.extend(extra)
         lines.append("")
     lines.append(f"kernel_source_sha: {kernel_source_hash(kernel)}")
     os.makedirs(PROFILES, exist_ok=True)
