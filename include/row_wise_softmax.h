@@ -281,8 +281,9 @@ const char *softmax_last_error(void);
 
 /*
  * softmax_copy_bytes -- plain device-to-device copy of `bytes` bytes with
- * 16-byte loads and stores (both pointers 16-byte aligned, bytes % 16 == 0),
- * on `stream`.  It is the reference point for the effective-bandwidth figure
+ * 16-byte non-temporal loads and stores, written through when `out` is
+ * 128-byte aligned (both pointers 16-byte aligned, bytes % 16 == 0), on
+ * `stream`.  It is the reference point for the effective-bandwidth figure
  * (bytes read plus bytes written per unit time, DCU case-study page, sections
  * 3.2 and 5.3): the copy ceiling, and the calibration of hardware traffic
  * counters.  Returns RWS_OK or an error status.

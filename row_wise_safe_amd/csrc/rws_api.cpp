@@ -89,6 +89,7 @@ struct Plan {
     int64_t window = 0;  // granules per row window (upper bound)
     bool aligned = false;
     bool same_phase = false;
+    bool wt = false;  // write-through 128-bit stores (line-aligned wave_row)
 };
 
 // Alignment facts of one call.
@@ -340,6 +341,9 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
             const int wa = wave_row_wa(v);
             p->aligned = wa == 128 ? g.a128 : g.a16;
             p->window = window_granules(g, wa);
+            // every 128-byte line of the output is written by one wave:
+            // store it through (faster there; slower where lines are shared)
+            p->wt = g.a128;
             // keep the threads of one launch below 2^32 (2^25 waves)
             p->max_rows_per_launch = (int64_t)(64 / v.G) * v.U * 4 * ((int64_t)1 << 23);
             break;
@@ -606,6 +610,7 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
         L.dtype = dtype;
         L.aligned = p.aligned;
         L.same_phase = p.same_phase;
+        L.wt = p.wt;
         L.stream = s;
         hipError_t e = hipSuccess;
         if (mask) {
@@ -956,10 +961,10 @@ static int describe_launch(int64_t rows, int64_t cols, int dtype, const void* in
         case RWS_KERNEL_WAVE_ROW: {
             const rws::WaveRowVariant& v = rws::kWaveRow[p.variant];
             std::snprintf(buf, (size_t)buflen,
-                          "wave_row<%s,%s,G=%d,K=%d,U=%d> grid=%lld block=%d window<=%lld",
+                          "wave_row<%s,%s,G=%d,K=%d,U=%d> grid=%lld block=%d window<=%lld%s",
                           dtype_name(dtype), al, v.G, v.K, v.U,
                           (long long)rws::wave_row_grid(v, std::min(rows, p.max_rows_per_launch)),
-                          rws::kWaveGroupThreads, (long long)wmax);
+                          rws::kWaveGroupThreads, (long long)wmax, p.wt ? " store=wt" : "");
             break;
         }
         case RWS_KERNEL_BLOCK_ONEPASS: {

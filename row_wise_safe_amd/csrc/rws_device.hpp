@@ -116,6 +116,20 @@ struct Elem<kBF16> {
 // 22.5 us vs 23.1 us).  A first pass whose data a later pass of the same
 // kernel reads again loads without it, so the re-read can hit the caches.
 // ---------------------------------------------------------------------------
+// 128-bit store with the non-temporal and device-scope bits
+// (`global_store_dwordx4 ... nt sc1`): the line is written through past the
+// XCD's L2 instead of being held there dirty.  On MI355X this moves a copy of
+// HBM-resident data 2.9% faster (64 MiB: 21.1 us against 21.7 us with `nt`
+// alone) and the forward wave_row kernels 1-1.7% faster on line-aligned
+// rows; where two workgroups write parts of one line (rows that are not
+// line-aligned) it is far slower (fp16 [8192,4097]: 40.9 us against 24.0),
+// and the backward and split-k kernels measured 1.4-2% slower, so only
+// callers that ask for it use it.  (No compiler builtin gives this bit
+// combination for a global store, hence the one-instruction asm.)
+__device__ inline void store16_wt(char* p, u32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off nt sc1" : : "v"(p), "v"(v) : "memory");
+}
+
 template <bool NT>
 __device__ inline u32x4 load16(const char* p) {
     if (NT) return __builtin_nontemporal_load((const u32x4*)p);
@@ -311,9 +325,14 @@ struct RowWin {
     // non-temporal: the output is written once and not read back by the
     // kernel, and streaming it past the caches measured 15-25% faster on
     // MI355X than ordinary stores.
-    __device__ inline void store(int k, const float* v, bool same_phase) const {
+    // wt (uniform): rows are line-aligned and the caller wants the 128-bit
+    // stores written through (store16_wt).
+    __device__ inline void store(int k, const float* v, bool same_phase, bool wt = false) const {
         if (ALIGNED) {
-            __builtin_nontemporal_store(Elem<DT>::narrow(v), (u32x4*)(gout + (int64_t)k * 16));
+            if (wt)
+                store16_wt(gout + (int64_t)k * 16, Elem<DT>::narrow(v));
+            else
+                __builtin_nontemporal_store(Elem<DT>::narrow(v), (u32x4*)(gout + (int64_t)k * 16));
             return;
         }
         const int c0 = k * VEC - lead;

@@ -72,11 +72,12 @@ __device__ inline void fetch_pre(const Pre& pre, const typename Pre::Ctx& pc, co
 // Rows past the end are clamped to the last row for loading (in bounds) and
 // are not stored.  A workgroup holds blockDim.x / 64 waves (the launcher's
 // choice, kWaveGroupWaves); wave w of workgroup b is wave b*(that) + w.
+// wt: the rows are line-aligned; store through (store16_wt).
 // ===========================================================================
 template <int DT, bool ALIGNED, int G, int K, int U, class Pre = NoPre>
 __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
                                                   void* __restrict__ out, int64_t rows,
-                                                  int cols, int same_phase,
+                                                  int cols, int same_phase, int wt,
                                                   Pre pre = Pre()) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int RPS = 64 / G;  // rows per set
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
 #pragma unroll
             for (int i = 0; i < K; ++i) {
                 const int k = gl + G * i;
-                if (k < w[u].ngran) w[u].store(k, &v[u][i * VEC], same_phase != 0);
+                if (k < w[u].ngran) w[u].store(k, &v[u][i * VEC], same_phase != 0, wt != 0);
             }
         }
     }

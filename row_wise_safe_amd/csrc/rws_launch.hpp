@@ -16,6 +16,7 @@ struct Launch {
     int dtype;        // kF32 / kF16 / kBF16
     bool aligned;     // in, out 128-byte aligned and cols*size % 128 == 0
     bool same_phase;  // (in - out) % 16 == 0
+    bool wt = false;  // wave_row: line-aligned rows, write-through stores
     hipStream_t stream;
 };
 

@@ -25,7 +25,7 @@ static hipError_t wr(const Launch& L, const MaskArgs& M) {
     const WaveRowVariant v = {G, K, U};
     hipLaunchKernelGGL((k_wave_row<DT, AL, G, K, U, MaskPre<DT>>),
                        dim3((unsigned)wave_row_grid(v, L.rows)), dim3(kWaveGroupThreads), 0, L.stream, L.in,
-                       L.out, L.rows, L.cols, (int)L.same_phase, make_pre<DT>(M));
+                       L.out, L.rows, L.cols, (int)L.same_phase, (int)L.wt, make_pre<DT>(M));
     return hipGetLastError();
 }
 

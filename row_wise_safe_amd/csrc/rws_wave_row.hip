@@ -15,7 +15,7 @@ static hipError_t go(const Launch& L) {
     const WaveRowVariant v = {G, K, U};
     const int64_t grid = wave_row_grid(v, L.rows);
     hipLaunchKernelGGL((k_wave_row<DT, AL, G, K, U>), dim3((unsigned)grid), dim3(kWaveGroupThreads), 0,
-                       L.stream, L.in, L.out, L.rows, L.cols, (int)L.same_phase, NoPre());
+                       L.stream, L.in, L.out, L.rows, L.cols, (int)L.same_phase, (int)L.wt, NoPre());
     return hipGetLastError();
 }
 

@@ -147,6 +147,26 @@ def test_many_rows_of_two_granules_stay_on_one_wave(lib):
     assert "KR=1" in rws.softmax_describe_launch(64, 960, rws.RWS_F16, 256, 512)
 
 
+# Write-through stores only where every output line is written by one wave:
+# wave_row on line-aligned rows (plain and masked), not on rows that start
+# mid-line, and never for the other families.
+@pytest.mark.parametrize("rows,cols,dtype,inp,out,masked,wt", [
+    (65536, 512, rws.RWS_F16, 256, 512, False, True),
+    (65536, 512, rws.RWS_F16, 256, 512, True, True),
+    (1 << 20, 128, rws.RWS_BF16, 256, 512, False, True),
+    (65536, 512, rws.RWS_F16, 256 + 16, 512 + 16, False, False),  # 16-byte aligned only
+    (65536, 504, rws.RWS_F16, 256, 512, False, False),  # rows of 1008 bytes
+    (8192, 4097, rws.RWS_F16, 256, 512, False, False),  # block_onepass
+    (16, 1 << 20, rws.RWS_F16, 256, 512, False, False),  # split-k
+])
+def test_write_through_only_on_line_aligned_wave_rows(lib, rows, cols, dtype, inp, out,
+                                                      masked, wt):
+    desc = rws.softmax_describe_launch(rows, cols, dtype, inp, out, masked=masked)
+    assert ("store=wt" in desc) == wt, desc
+    if wt:
+        assert desc.startswith("wave_row<") and ",aligned," in desc, desc
+
+
 @pytest.mark.parametrize("rows,cols", [((1 << 22) + 5, 12000), ((1 << 22) + 5, 24)])
 def test_block_launch_stays_below_2_32_threads(lib, rows, cols):
     # the grid of one launch times its workgroup size must fit the 32-bit grid size
