@@ -127,14 +127,15 @@ template <int DT, bool ALIGNED, int BLOCK, int KR>
 __global__ __launch_bounds__(BLOCK) void k_bwd_block(const void* __restrict__ y,
                                                      const void* __restrict__ dy,
                                                      void* __restrict__ dx, int64_t rows,
-                                                     int cols, int dy_vec, int same_phase) {
+                                                     int cols, int dy_vec, int same_phase,
+                                                     int lgrun) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     constexpr int N = KR * VEC;
     using Win = RowWin<DT, ALIGNED>;
     __shared__ float red[W];
     const int t = threadIdx.x;
-    const int64_t row = blockIdx.x;
+    const int64_t row = xcd_run(blockIdx.x, gridDim.x, lgrun);
     const char* tbeg = (const char*)y;
     const char* tend = tensor_end<DT>(y, rows, cols);
     const Second<DT, Win> s2{(const char*)dy, tensor_end<DT>(dy, rows, cols),
@@ -173,13 +174,14 @@ template <int DT, bool ALIGNED, int BLOCK, int U>
 __global__ __launch_bounds__(BLOCK) void k_bwd_stream(const void* __restrict__ y,
                                                       const void* __restrict__ dy,
                                                       void* __restrict__ dx, int64_t rows,
-                                                      int cols, int dy_vec, int same_phase) {
+                                                      int cols, int dy_vec, int same_phase,
+                                                      int lgrun) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     using Win = RowWin<DT, ALIGNED>;
     __shared__ float red[W];
     const int t = threadIdx.x;
-    const int64_t row = blockIdx.x;
+    const int64_t row = xcd_run(blockIdx.x, gridDim.x, lgrun);
     const char* tbeg = (const char*)y;
     const char* tend = tensor_end<DT>(y, rows, cols);
     const Second<DT, Win> s2{(const char*)dy, tensor_end<DT>(dy, rows, cols),
@@ -277,14 +279,14 @@ template <int DT, bool AL, int BL, int KR>
 static hipError_t bb(const BwdLaunch& B) {
     hipLaunchKernelGGL((k_bwd_block<DT, AL, BL, KR>), dim3((unsigned)B.rows), dim3(BL), 0,
                        B.stream, B.y, B.dy, B.dx, B.rows, B.cols, (int)B.dy_vec,
-                       (int)B.same_phase);
+                       (int)B.same_phase, B.lgrun);
     return hipGetLastError();
 }
 template <int DT, bool AL, int BL, int U>
 static hipError_t bs(const BwdLaunch& B) {
     hipLaunchKernelGGL((k_bwd_stream<DT, AL, BL, U>), dim3((unsigned)B.rows), dim3(BL), 0,
                        B.stream, B.y, B.dy, B.dx, B.rows, B.cols, (int)B.dy_vec,
-                       (int)B.same_phase);
+                       (int)B.same_phase, B.lgrun);
     return hipGetLastError();
 }
 

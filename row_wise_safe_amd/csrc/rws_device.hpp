@@ -130,6 +130,21 @@ __device__ inline void store16_wt(char* p, u32x4 v) {
     asm volatile("global_store_dwordx4 %0, %1, off nt sc1" : : "v"(p), "v"(v) : "memory");
 }
 
+// Row handled by workgroup `id` of a launch of `n` one-row workgroups when
+// runs of 2^lg consecutive rows go to one XCD.  Workgroups are dispatched to
+// the 8 XCDs round-robin by id, so in launch order XCD x gets rows x, x+8,
+// x+16, ...; here each span of 8 * 2^lg rows is split so that XCD x gets the
+// run [x * 2^lg, (x + 1) * 2^lg) of it.  A trailing partial span keeps launch
+// order; lg = 0 is launch order.  (The dispatcher picks lg for the
+// workgroup-per-row families; measurements are with that rule.)
+__device__ inline int64_t xcd_run(int64_t id, int64_t n, int lg) {
+    const int sh = 3 + lg;
+    const int64_t full = (n >> sh) << sh;
+    if (lg == 0 || id >= full) return id;
+    const int r = (int)(id & ((1 << sh) - 1));
+    return (id - r) + ((int64_t)(r & 7) << lg) + (r >> 3);
+}
+
 template <bool NT>
 __device__ inline u32x4 load16(const char* p) {
     if (NT) return __builtin_nontemporal_load((const u32x4*)p);

@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
 template <int DT, bool ALIGNED, int BLOCK, int KR, int KL, class Pre = NoPre>
 __global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict__ in,
                                                          void* __restrict__ out, int64_t rows,
-                                                         int cols, int same_phase,
+                                                         int cols, int same_phase, int lgrun,
                                                          Pre pre = Pre()) {
     static_assert(!Pre::kActive || KL == 0, "prologues apply to register-held rows only");
     constexpr int VEC = Elem<DT>::VEC;
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict_
     __shared__ float red_sum[W];
     __shared__ u32x4 park[KL > 0 ? KL : 1][KL > 0 ? BLOCK : 1];
     const int t = threadIdx.x;
-    const int64_t row = blockIdx.x;
+    const int64_t row = xcd_run(blockIdx.x, gridDim.x, lgrun);
     const char* tbeg = (const char*)in;
     const char* tend = tensor_end<DT>(in, rows, cols);
     const RowWin<DT, ALIGNED> w(in, out, row, cols);
@@ -296,14 +296,14 @@ __device__ inline void block_merge(float m, float d, float& M, float& D, float* 
 template <int DT, bool ALIGNED, int BLOCK, int U, class Pre = NoPre>
 __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
                                                     void* __restrict__ out, int64_t rows,
-                                                    int cols, int same_phase,
+                                                    int cols, int same_phase, int lgrun,
                                                     Pre pre = Pre()) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     __shared__ float red_max[W];
     __shared__ float red_sum[W];
     const int t = threadIdx.x;
-    const int64_t row = blockIdx.x;
+    const int64_t row = xcd_run(blockIdx.x, gridDim.x, lgrun);
     const char* tbeg = (const char*)in;
     const char* tend = tensor_end<DT>(in, rows, cols);
     const RowWin<DT, ALIGNED> w(in, out, row, cols);

@@ -17,6 +17,7 @@ struct Launch {
     bool aligned;     // in, out 128-byte aligned and cols*size % 128 == 0
     bool same_phase;  // (in - out) % 16 == 0
     bool wt = false;  // wave_row: line-aligned rows, write-through stores
+    int lgrun = 0;    // one-row-per-workgroup kernels: XCD runs of 2^lgrun rows
     hipStream_t stream;
 };
 
@@ -98,6 +99,7 @@ struct BwdLaunch {
     bool aligned;     // y, dx 128-byte aligned and cols*size % 128 == 0
     bool same_phase;  // (dx - y) % 16 == 0
     bool dy_vec;      // (dy - y) % 16 == 0
+    int lgrun = 0;    // bwd_block / bwd_stream: XCD runs of 2^lgrun rows
     hipStream_t stream;
 };
 extern const WaveRowVariant kBwdWave[];
@@ -129,6 +131,7 @@ struct NormLaunch {
     bool aligned;     // in, out 128-byte aligned and cols*size % 128 == 0
     bool same_phase;  // (out - in) % 16 == 0
     NormArgs args;    // mean/rstd already offset to the launch's first row
+    int lgrun = 0;    // norm_block / norm_stream: XCD runs of 2^lgrun rows
     hipStream_t stream;
 };
 extern const WaveRowVariant kNormWave[];

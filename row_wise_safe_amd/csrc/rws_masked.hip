@@ -53,7 +53,8 @@ hipError_t launch_wave_row_masked(const Launch& L, int variant, const MaskArgs& 
 template <int DT, bool AL, int B, int KR>
 static hipError_t bo(const Launch& L, const MaskArgs& M) {
     hipLaunchKernelGGL((k_block_onepass<DT, AL, B, KR, 0, MaskPre<DT>>), dim3((unsigned)L.rows),
-                       dim3(B), 0, L.stream, L.in, L.out, L.rows, L.cols, (int)L.same_phase, make_pre<DT>(M));
+                       dim3(B), 0, L.stream, L.in, L.out, L.rows, L.cols, (int)L.same_phase, L.lgrun,
+                       make_pre<DT>(M));
     return hipGetLastError();
 }
 
@@ -85,7 +86,7 @@ hipError_t launch_block_onepass_masked(const Launch& L, int variant, const MaskA
 template <int DT, bool AL, int B, int U>
 static hipError_t tp(const Launch& L, const MaskArgs& M) {
     hipLaunchKernelGGL((k_two_pass<DT, AL, B, U, MaskPre<DT>>), dim3((unsigned)L.rows), dim3(B), 0,
-                       L.stream, L.in, L.out, L.rows, L.cols, (int)L.same_phase,
+                       L.stream, L.in, L.out, L.rows, L.cols, (int)L.same_phase, L.lgrun,
                        make_pre<DT>(M));
     return hipGetLastError();
 }

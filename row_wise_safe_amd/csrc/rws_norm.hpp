@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void k_norm_wave(const void* __restrict__ in,
 template <int DT, bool ALIGNED, int BLOCK, int KR, int MODE, bool AFF>
 __global__ __launch_bounds__(BLOCK) void k_norm_block(const void* __restrict__ in,
                                                       void* __restrict__ out, int64_t rows,
-                                                      int cols, NormArgs A, int same_phase) {
+                                                      int cols, NormArgs A, int same_phase, int lgrun) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     constexpr int N = KR * VEC;
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(BLOCK) void k_norm_block(const void* __restrict__ i
     __shared__ float red1[W];
     __shared__ float red2[W];
     const int t = threadIdx.x;
-    const int64_t row = blockIdx.x;
+    const int64_t row = xcd_run(blockIdx.x, gridDim.x, lgrun);
     const char* tbeg = (const char*)in;
     const char* tend = tensor_end<DT>(in, rows, cols);
     const Win w(in, out, row, cols);
@@ -316,7 +316,7 @@ __device__ inline void moments_block(float& n, float& m, float& q, float* sn, fl
 template <int DT, bool ALIGNED, int BLOCK, int U, int MODE, bool AFF>
 __global__ __launch_bounds__(BLOCK) void k_norm_stream(const void* __restrict__ in,
                                                        void* __restrict__ out, int64_t rows,
-                                                       int cols, NormArgs A, int same_phase) {
+                                                       int cols, NormArgs A, int same_phase, int lgrun) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     using Win = RowWin<DT, ALIGNED>;
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(BLOCK) void k_norm_stream(const void* __restrict__ 
     __shared__ float sm[W];
     __shared__ float sq[W];
     const int t = threadIdx.x;
-    const int64_t row = blockIdx.x;
+    const int64_t row = xcd_run(blockIdx.x, gridDim.x, lgrun);
     const char* tbeg = (const char*)in;
     const char* tend = tensor_end<DT>(in, rows, cols);
     const Win w(in, out, row, cols);

@@ -27,10 +27,10 @@ static hipError_t nb_mode(const NormLaunch& L) {
     const dim3 grid((unsigned)L.rows);
     if (L.args.w || L.args.b)
         hipLaunchKernelGGL((k_norm_block<DT, AL, BL, KR, MODE, true>), grid, dim3(BL), 0, L.stream,
-                           L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase);
+                           L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase, L.lgrun);
     else
         hipLaunchKernelGGL((k_norm_block<DT, AL, BL, KR, MODE, false>), grid, dim3(BL), 0, L.stream,
-                           L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase);
+                           L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase, L.lgrun);
     return hipGetLastError();
 }
 
@@ -45,10 +45,10 @@ static hipError_t ns_mode(const NormLaunch& L) {
     const dim3 grid((unsigned)L.rows);
     if (L.args.w || L.args.b)
         hipLaunchKernelGGL((k_norm_stream<DT, AL, BL, U, MODE, true>), grid, dim3(BL), 0, L.stream,
-                           L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase);
+                           L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase, L.lgrun);
     else
         hipLaunchKernelGGL((k_norm_stream<DT, AL, BL, U, MODE, false>), grid, dim3(BL), 0, L.stream,
-                           L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase);
+                           L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase, L.lgrun);
     return hipGetLastError();
 }
 

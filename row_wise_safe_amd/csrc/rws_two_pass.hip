@@ -14,7 +14,7 @@ const int kNumTwoPass = sizeof(kTwoPass) / sizeof(kTwoPass[0]);
 template <int DT, bool AL, int B, int U>
 static hipError_t go(const Launch& L) {
     hipLaunchKernelGGL((k_two_pass<DT, AL, B, U>), dim3((unsigned)L.rows), dim3(B), 0, L.stream,
-                       L.in, L.out, L.rows, L.cols, (int)L.same_phase, NoPre());
+                       L.in, L.out, L.rows, L.cols, (int)L.same_phase, L.lgrun, NoPre());
     return hipGetLastError();
 }
 

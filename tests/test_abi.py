@@ -167,6 +167,25 @@ def test_write_through_only_on_line_aligned_wave_rows(lib, rows, cols, dtype, in
         assert desc.startswith("wave_row<") and ",aligned," in desc, desc
 
 
+# Runs of consecutive rows per XCD for block_onepass on rows that are not
+# line-aligned: the smallest power of two of at least 128 KiB of rows.
+@pytest.mark.parametrize("rows,cols,inp,run", [
+    (8192, 4097, 256, 16),      # 8194-byte rows
+    (16384, 2001, 256, 64),     # 4002-byte rows
+    (32768, 1000, 256, 128),    # 2000-byte rows
+    (4096, 8000, 256, None),    # 16000-byte rows, line-aligned
+    (8192, 4096, 256, None),    # 8192-byte rows, line-aligned
+    (8192, 4096, 256 + 2, 16),  # the same rows starting mid-line
+])
+def test_xcd_run_length(lib, rows, cols, inp, run):
+    desc = rws.softmax_describe_launch(rows, cols, rws.RWS_F16, inp, inp + 256)
+    assert desc.startswith("block_onepass"), desc
+    if run is None:
+        assert "xcd_run" not in desc, desc
+    else:
+        assert desc.endswith(f" xcd_run={run}"), desc
+
+
 @pytest.mark.parametrize("rows,cols", [((1 << 22) + 5, 12000), ((1 << 22) + 5, 24)])
 def test_block_launch_stays_below_2_32_threads(lib, rows, cols):
     # the grid of one launch times its workgroup size must fit the 32-bit grid size
