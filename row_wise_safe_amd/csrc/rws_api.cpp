@@ -182,8 +182,14 @@ bool few_waves(int64_t rows, int64_t w, int cus) {
     return rows * std::min<int64_t>((w + 63) / 64, 16) <= kFewWavesPerCu * cus;
 }
 
-// Choose a block_onepass variant for rows of w granules (line window), by
-// sweeps on MI355X with inputs in HBM:
+// A workgroup-per-row shape: `block` threads, `kr` granules per thread in
+// registers, `kl` more parked in LDS.
+struct BlockShape {
+    int block, kr, kl;
+};
+
+// Choose a workgroup-per-row shape for rows of w granules (line window) among
+// shapes(0..n-1), by sweeps on MI355X with inputs in HBM:
 //  * few waves: the fewest granules per thread, then the smallest workgroup
 //    (fp32 [64,1000]: 2.84 us with 320x1 against 4.36 us for one wave per row
 //    with 8 granules per lane; fp16 [1024,2000]: 4.03 us with 320x1, 4.29
@@ -191,16 +197,20 @@ bool few_waves(int64_t rows, int64_t w, int cus) {
 //  * otherwise: 2-5 register granules per thread with the fewest idle slots,
 //    ties to fewer granules per thread -- the fastest shape of each sweep:
 //    fp16 rows of 1000 columns (window 133) 64x3, 2000 (258) 64x5, 4000 (508)
-//    256x2, 4097 (521) 192x3, 8000 (1008) 512x2;
+//    256x2, 4097 (521) 192x3, 8000 (1008) 512x2; the same shapes are the
+//    fastest for LayerNorm and RMSNorm (1000 columns: 24.9 / 24.3 us against
+//    33.2 / 30.0 with 192x1; 2000: 24.5 / 23.8 against 30.5 / 27.3 with
+//    320x1; 4097: 24.3 / 23.8 against 32.7 / 30.2 with 576x1);
 //  * rows longer than those shapes hold: the smallest capacity.
-int pick_onepass(int64_t w, int64_t rows, int cus, bool regs_only = false) {
+template <class Shape>
+int pick_block_shape(int n, Shape shape, int64_t w, int64_t rows, int cus) {
     const bool few = few_waves(rows, w, cus);
     int best = -1;
     int64_t best_key = 0;
-    for (int i = 0; i < rws::kNumOnepass; ++i) {
-        const rws::OnepassVariant& v = rws::kOnepass[i];
-        if (regs_only && v.kl != 0) continue;
-        const int64_t cap = onepass_capacity(v);
+    for (int i = 0; i < n; ++i) {
+        const BlockShape v = shape(i);
+        if (v.block <= 0) continue;
+        const int64_t cap = (int64_t)v.block * (v.kr + v.kl);
         if (cap < w) continue;
         int64_t key;
         if (few)
@@ -215,6 +225,17 @@ int pick_onepass(int64_t w, int64_t rows, int cus, bool regs_only = false) {
         }
     }
     return best;
+}
+
+// block_onepass variant (regs_only: no LDS parking, as the masked form needs).
+int pick_onepass(int64_t w, int64_t rows, int cus, bool regs_only = false) {
+    return pick_block_shape(
+        rws::kNumOnepass,
+        [&](int i) {
+            const rws::OnepassVariant& v = rws::kOnepass[i];
+            return regs_only && v.kl != 0 ? BlockShape{0, 0, 0} : BlockShape{v.block, v.kr, v.kl};
+        },
+        w, rows, cus);
 }
 
 // Split-k chunking: the largest chunk that still gives every CU eight
@@ -798,22 +819,17 @@ int softmax_bwd(const void* y, const void* dy, void* dx, int64_t rows, int64_t c
 
 // Row normalisations: family 1 (norm_wave), 2 (norm_block) or 3
 // (norm_stream), chosen by the row window like the softmax backward.
-static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t cols, int dtype,
-                    float eps, const void* weight, const void* bias, float* mean, float* rstd,
-                    void* stream, int kernel_id) {
-    g_last_error.clear();
-    if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
-        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS)
-        return fail(RWS_ERR_INVALID_ARG, "normalisation kernels: auto, wave_row, block_onepass, two_pass");
-    if (!(eps >= 0.0f) || !std::isfinite(eps))
-        return fail(RWS_ERR_INVALID_ARG, "eps must be finite and >= 0");
-    int st = check_args(in, out, rows, cols, dtype, RWS_KERNEL_AUTO);
-    if (st != RWS_OK || rows == 0 || cols == 0) return st;
-    const int es = elem_size(dtype);
-    if ((uintptr_t)weight % es || (uintptr_t)bias % es)
-        return fail(RWS_ERR_MISALIGNED, "weight/bias not aligned to the element size");
-    if ((uintptr_t)mean % 4 || (uintptr_t)rstd % 4)
-        return fail(RWS_ERR_MISALIGNED, "mean/rstd not aligned to 4 bytes");
+struct NormPlan {
+    int family = 0;
+    int variant = 0;
+    bool aligned = false;
+    bool same_phase = false;
+    int lgrun = 0;
+    int64_t max_rows = 0;
+};
+
+static int plan_norm(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
+                     int kernel_id, NormPlan* np) {
     const Geometry g = geometry(cols, dtype, in, out);
     const int64_t wline = window_granules(g, 128);
     // Lane groups measured on MI355X (fp16 LayerNorm / RMSNorm, rotating
@@ -850,21 +866,18 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
         return best;
     };
     auto pick_block = [&]() {
-        int best = -1;
-        for (int i = 0; i < rws::kNumNormBlock; ++i) {
-            const int64_t cap = (int64_t)rws::kNormBlock[i].block * rws::kNormBlock[i].u;
-            if (cap < wline) continue;
-            if (best < 0 || cap < (int64_t)rws::kNormBlock[best].block * rws::kNormBlock[best].u)
-                best = i;
-        }
-        return best;
+        return pick_block_shape(
+            rws::kNumNormBlock,
+            [](int i) { return BlockShape{rws::kNormBlock[i].block, rws::kNormBlock[i].u, 0}; },
+            wline, rows, device_info().cus);
     };
     // Forms: the tuned lane groups above, or one wave per row while a lane
     // group holds the row at one granule per lane; else one workgroup per row
-    // with one granule per thread (one wave per row with 4 or 8 granules per
-    // lane measured 1.7-2.2x slower: LayerNorm fp16 [32768,1000] 54.5 us
-    // against 32.9 with 192x1, [16384,2000] 43.9 against 30.1 with 320x1,
-    // [8192,4000] 28.8 against 25.0 with 512x1); any length streams.
+    // in the forward softmax's shapes (one wave per row with 4 or 8 granules
+    // per lane measured 1.7-2.2x slower than even one granule per thread:
+    // LayerNorm fp16 [32768,1000] 54.5 us against 32.9 with 192x1,
+    // [16384,2000] 43.9 against 30.1 with 320x1, [8192,4000] 28.8 against 25.0
+    // with 512x1); any length streams.
     int family = kernel_id == RWS_KERNEL_AUTO ? 0 : kernel_id;
     if (family == 0) {
         if (pick_wave(1) >= 0) family = 1;
@@ -893,6 +906,36 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
         ? (int64_t)(64 / rws::kNormWave[variant].G) * rws::kNormWave[variant].U * 4 * ((int64_t)1 << 23)
         : block_rows_per_launch(family == 2 ? rws::kNormBlock[variant].block
                                             : rws::kNormStream[variant].block);
+    np->family = family;
+    np->variant = variant;
+    np->aligned = aligned;
+    np->same_phase = g.same_phase;
+    np->lgrun = 0;
+    np->max_rows = max_rows;
+    return RWS_OK;
+}
+
+static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t cols, int dtype,
+                    float eps, const void* weight, const void* bias, float* mean, float* rstd,
+                    void* stream, int kernel_id) {
+    g_last_error.clear();
+    if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
+        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS)
+        return fail(RWS_ERR_INVALID_ARG, "normalisation kernels: auto, wave_row, block_onepass, two_pass");
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return fail(RWS_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    int st = check_args(in, out, rows, cols, dtype, RWS_KERNEL_AUTO);
+    if (st != RWS_OK || rows == 0 || cols == 0) return st;
+    const int es = elem_size(dtype);
+    if ((uintptr_t)weight % es || (uintptr_t)bias % es)
+        return fail(RWS_ERR_MISALIGNED, "weight/bias not aligned to the element size");
+    if ((uintptr_t)mean % 4 || (uintptr_t)rstd % 4)
+        return fail(RWS_ERR_MISALIGNED, "mean/rstd not aligned to 4 bytes");
+    NormPlan np;
+    st = plan_norm(rows, cols, dtype, in, out, kernel_id, &np);
+    if (st != RWS_OK) return st;
+    const int family = np.family, variant = np.variant;
+    const int64_t max_rows = np.max_rows;
     const int64_t row_bytes = cols * es;
     for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
         rws::NormLaunch L;
@@ -902,8 +945,9 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
         L.cols = (int)cols;
         L.dtype = dtype;
         L.mode = mode;
-        L.aligned = aligned;
-        L.same_phase = g.same_phase;
+        L.aligned = np.aligned;
+        L.same_phase = np.same_phase;
+        L.lgrun = np.lgrun;
         L.args.w = weight;
         L.args.b = bias;
         L.args.mean = mean ? mean + r0 : nullptr;
@@ -1046,6 +1090,45 @@ int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void* i
 int softmax_describe_launch_masked(int64_t rows, int64_t cols, int dtype, const void* in,
                                    const void* out, int kernel_id, char* buf, int64_t buflen) {
     return describe_launch(rows, cols, dtype, in, out, kernel_id, true, buf, buflen);
+}
+
+int norm_describe_launch(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
+                         int kernel_id, char* buf, int64_t buflen) {
+    g_last_error.clear();
+    if (!buf || buflen <= 0) return fail(RWS_ERR_INVALID_ARG, "no output buffer");
+    buf[0] = 0;
+    if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
+        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS)
+        return fail(RWS_ERR_INVALID_ARG, "normalisation kernels: auto, wave_row, block_onepass, two_pass");
+    if (dtype != RWS_F32 && dtype != RWS_F16 && dtype != RWS_BF16)
+        return fail(RWS_ERR_UNSUPPORTED_DTYPE, "dtype must be RWS_F32, RWS_F16 or RWS_BF16");
+    if (rows < 0 || cols < 0) return fail(RWS_ERR_INVALID_ARG, "rows and cols must be >= 0");
+    if (cols > kMaxCols) return fail(RWS_ERR_UNSUPPORTED_SHAPE, "cols above 2^30");
+    if (rows == 0 || cols == 0) {
+        std::snprintf(buf, (size_t)buflen, "empty: no launch");
+        return RWS_OK;
+    }
+    NormPlan np;
+    const int st = plan_norm(rows, cols, dtype, in, out, kernel_id, &np);
+    if (st != RWS_OK) return st;
+    const char* al = np.aligned ? "aligned" : (np.same_phase ? "unaligned" : "unaligned,split-phase");
+    const int64_t r = std::min(rows, np.max_rows);
+    const long long wline = (long long)window_granules(geometry(cols, dtype, in, out), 128);
+    if (np.family == 1) {
+        const rws::WaveRowVariant& v = rws::kNormWave[np.variant];
+        std::snprintf(buf, (size_t)buflen, "norm_wave<%s,%s,G=%d,K=%d,U=%d> grid=%lld block=%d",
+                      dtype_name(dtype), al, v.G, v.K, v.U, (long long)rws::wave_row_grid(v, r),
+                      rws::kWaveGroupThreads);
+    } else {
+        const rws::TwoPassVariant& v =
+            np.family == 2 ? rws::kNormBlock[np.variant] : rws::kNormStream[np.variant];
+        char run[32] = "";
+        if (np.lgrun > 0) std::snprintf(run, sizeof run, " xcd_run=%d", 1 << np.lgrun);
+        std::snprintf(buf, (size_t)buflen, "%s<%s,%s,B=%d,%s=%d> grid=%lld block=%d window<=%lld%s",
+                      np.family == 2 ? "norm_block" : "norm_stream", dtype_name(dtype), al, v.block,
+                      np.family == 2 ? "KR" : "U", v.u, (long long)r, v.block, wline, run);
+    }
+    return RWS_OK;
 }
 
 const char* softmax_kernel_name(int kernel_id) {

@@ -210,9 +210,15 @@ __global__ __launch_bounds__(256) void k_norm_wave(const void* __restrict__ in,
 
 // ===========================================================================
 // norm_block: one workgroup of BLOCK threads per row, KR granules per thread.
+// With 2-5 granules per thread the compiler is asked for six waves per SIMD
+// (at most 85 VGPRs): left to itself it took 132-166 VGPRs for 3-4 granules
+// (three waves per SIMD), and LayerNorm fp16 [32768,1000] with 64x3 ran
+// 39.8 us against 24.9 us capped (RMSNorm 36.9 / 24.3; [8192,4097] with
+// 192x3 32.0 / 24.3).  No spills at that cap.
 // ===========================================================================
 template <int DT, bool ALIGNED, int BLOCK, int KR, int MODE, bool AFF>
-__global__ __launch_bounds__(BLOCK) void k_norm_block(const void* __restrict__ in,
+__global__ __launch_bounds__(BLOCK)
+__attribute__((amdgpu_waves_per_eu((KR == 2 || KR == 3) && !(AFF && ALIGNED) ? 6 : 1))) void k_norm_block(const void* __restrict__ in,
                                                       void* __restrict__ out, int64_t rows,
                                                       int cols, NormArgs A, int same_phase, int lgrun) {
     constexpr int VEC = Elem<DT>::VEC;

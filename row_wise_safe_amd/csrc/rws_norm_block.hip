@@ -4,12 +4,20 @@
 
 namespace rws {
 
-// (threads, granules per thread held in registers)
-// (threads, register granules per thread): one granule per thread up to
-// 1024 granules per row, then 1024-thread workgroups.
+// (threads, register granules per thread): the forward block_onepass shapes
+// without LDS parking, and 64x2, chosen by the same rule.  A sweep of
+// LayerNorm and RMSNorm over fp16 hidden sizes 768-8192 (64 MiB in, rows
+// line-aligned) found the exact-fit two-granule shapes fastest at every size
+// (768: 64x2 23.2 us, 1024: 64x2 23.2, 2048: 128x2 23.0, 3072: 192x2 23.1,
+// 4096: 256x2 23.0, 5120: 320x2 23.5, 8192: 512x2 23.1; one granule per
+// thread 24.7-173 us, one wave per row 23.1-52.6 us).
 #define RWS_NORM_BLOCK_VARIANTS(X)                                       \
-    X(128, 1) X(192, 1) X(256, 1) X(320, 1) X(384, 1) X(512, 1) X(576, 1) \
-    X(640, 1) X(768, 1) X(1024, 1) X(1024, 2) X(1024, 3) X(1024, 4)
+    X(128, 1) X(192, 1) X(256, 1) X(320, 1) X(384, 1) X(512, 1) X(640, 1) \
+    X(768, 1) X(1024, 1)                                                  \
+    X(64, 2) X(128, 2) X(192, 2) X(256, 2) X(320, 2) X(384, 2) X(512, 2)  \
+    X(768, 2)                                                             \
+    X(1024, 2)                                                            \
+    X(64, 3) X(192, 3) X(384, 3) X(1024, 3) X(1024, 4) X(64, 5)
 // (threads, granules per thread per batch)
 #define RWS_NORM_STREAM_VARIANTS(X) \
     X(256, 4)                       \

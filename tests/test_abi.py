@@ -167,6 +167,26 @@ def test_write_through_only_on_line_aligned_wave_rows(lib, rows, cols, dtype, in
         assert desc.startswith("wave_row<") and ",aligned," in desc, desc
 
 
+# Normalisation shapes: the tuned lane groups, then the forward's workgroup
+# shapes (exact-fit two-granule shapes at common fp16 hidden sizes).
+@pytest.mark.parametrize("rows,cols,shape", [
+    (131040, 192, "norm_wave<f16,aligned,G=16,K=2,U=1>"),
+    (32760, 384, "norm_wave<f16,aligned,G=8,K=6,U=1>"),
+    (43690, 768, "norm_block<f16,aligned,B=64,KR=2>"),
+    (32768, 1024, "norm_block<f16,aligned,B=64,KR=2>"),
+    (16384, 2048, "norm_block<f16,aligned,B=128,KR=2>"),
+    (8192, 4096, "norm_block<f16,aligned,B=256,KR=2>"),
+    (4096, 8192, "norm_block<f16,aligned,B=512,KR=2>"),
+    (32768, 1000, "norm_block<f16,unaligned,B=64,KR=3>"),
+    (8192, 4097, "norm_block<f16,unaligned,B=192,KR=3>"),
+    (64, 1000, "norm_block<f16,unaligned,B=192,KR=1>"),
+    (1024, 40000, "norm_stream<f16,aligned,B=1024,U=4>"),
+])
+def test_norm_shape_choice(lib, rows, cols, shape):
+    desc = rws.norm_describe_launch(rows, cols, rws.RWS_F16, 256, 512)
+    assert desc.startswith(shape), desc
+
+
 # Runs of consecutive rows per XCD for block_onepass on rows that are not
 # line-aligned: the smallest power of two of at least 128 KiB of rows.
 @pytest.mark.parametrize("rows,cols,inp,run", [

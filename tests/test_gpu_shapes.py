@@ -79,3 +79,29 @@ def test_every_masked_block_shape(few):
         ref = oracle.masked_softmax(xs, 0.25, ms, causal_q=causal)
         check(y.double().cpu().numpy(), ref, dtype, f"masked B={b},KR={kr} rows={rows} cols={cols}")
         del x, y
+
+
+def _norm_cases(dtype: str, few: bool):
+    """{(B, KR): (rows, cols)} of the normalisations' workgroup-per-row shapes."""
+    es = ES[dtype]
+    seen = {}
+    step = 16 // es
+    for cols in range(step, 4096 * step, step):
+        w = (cols * es + 143) // 16
+        rows = 16 if few else FEW_WAVES // min((w + 63) // 64, 16) + 1
+        desc = rws.norm_describe_launch(rows, cols, CODE[dtype], 256, 512)
+        m = re.match(r"norm_block<[^>]*B=(\d+),KR=(\d+)>", desc)
+        if m:
+            seen.setdefault(tuple(int(v) for v in m.groups()), (rows, cols))
+    return seen
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+@pytest.mark.parametrize("few", [True, False])
+def test_every_norm_block_shape(dtype, few):
+    from test_gpu_norm import _case
+    cases = _norm_cases(dtype, few)
+    assert len(cases) >= (6 if few else 10), cases
+    for (b, kr), (rows, cols) in sorted(cases.items()):
+        for mode in ("layernorm", "rmsnorm"):
+            _case(mode, dtype, rows, cols, "auto", seed=rows * 7 + cols + kr)
