@@ -312,6 +312,9 @@ def main() -> int:
                     help="row normalisation instead of softmax (layernorm_fwd / rmsnorm_fwd, no "
                          "affine, eps 1e-5) on a normalisation workload (default "
                          "ln_fp16_131040x192)")
+    ap.add_argument("--affine", action="store_true",
+                    help="with --norm: per-column weight and bias (LayerNorm) or weight (RMSNorm), "
+                         "read once per call")
     ap.add_argument("--skip-hot", action="store_true",
                     help="skip the single-buffer figure (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -401,15 +404,29 @@ def main() -> int:
         mask = torch.from_numpy(g.normal(0.0, 1.0, (w.cols, w.cols))).to(tdt).to(dev)
         nbytes += mask.numel() * mask.element_size()  # the mask is read once per call
         desc = "masked " + desc
+    wptr = bptr = 0
+    if args.affine:
+        if not args.norm:
+            print("--affine needs --norm", file=sys.stderr)
+            return 2
+        g = np.random.Generator(np.random.PCG64(w.seed + 300))
+        weight = torch.from_numpy(g.uniform(0.5, 1.5, w.cols)).to(tdt).to(dev)
+        wptr = weight.data_ptr()
+        nbytes += weight.numel() * weight.element_size()
+        if args.norm == "layernorm":
+            bias = torch.from_numpy(g.normal(0.0, 1.0, w.cols)).to(tdt).to(dev)
+            bptr = bias.data_ptr()
+            nbytes += bias.numel() * bias.element_size()
+        desc += " affine"
     log(f"[bench] launch: {desc}; {nbuf} rotating buffer pairs")
 
     def step(i):
         if args.norm == "layernorm":
             st = rws.layernorm_fwd_kernel(xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), w.rows,
-                                          w.cols, code, 1e-5, 0, 0, 0, 0, sh, kid)
+                                          w.cols, code, 1e-5, wptr, bptr, 0, 0, sh, kid)
         elif args.norm == "rmsnorm":
             st = rws.rmsnorm_fwd_kernel(xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), w.rows,
-                                        w.cols, code, 1e-5, 0, 0, sh, kid)
+                                        w.cols, code, 1e-5, wptr, 0, sh, kid)
         elif dys is not None:
             st = rws.softmax_bwd_kernel(xs[i % nbuf].data_ptr(), dys[i % nbuf].data_ptr(),
                                         ys[i % nbuf].data_ptr(), w.rows, w.cols, code, sh, kid)
@@ -510,7 +527,8 @@ def main() -> int:
 
     profile_key = (args.norm if args.norm else "masked" if mask is not None
                    else "backward" if dys is not None else family)
-    traffic = read_traffic(w.name, profile_key)
+    # the committed profiles cover the forms without weight and bias
+    traffic = None if args.affine else read_traffic(w.name, profile_key)
     achieved = nbytes / (ms * 1e-3) / 1e9
     headline = (w.name == "fp16_attn_4x32x512x512" and mask is None and dys is None
                 and not args.norm)
@@ -520,7 +538,8 @@ def main() -> int:
                    f"effective HBM GB/s (read+write) and µs/call, {w.description}"
                    + (", softmax(x/8 + mask + causal)" if mask is not None else "")
                    + (", backward dx = y*(dy - sum(dy*y))" if dys is not None else "")
-                   + (f", {args.norm} forward (eps 1e-5, no affine)" if args.norm else "")),
+                   + (f", {args.norm} forward (eps 1e-5, "
+                      f"{'weight and bias' if args.affine else 'no affine'})" if args.norm else "")),
         "value": round(gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,

@@ -274,11 +274,12 @@ int softmax_describe_launch_masked(int64_t rows, int64_t cols, int dtype, const 
  * norm_describe_launch -- the same for the launch layernorm_fwd_kernel /
  * rmsnorm_fwd_kernel(kernel_id) would make on these tensors (both use the
  * same choice: norm_wave, norm_block or norm_stream, with its shape).
- * kernel_id: RWS_KERNEL_AUTO, _WAVE_ROW, _BLOCK_ONEPASS or _TWO_PASS.
- * Performs no GPU work.
+ * affine: nonzero when a weight and/or bias is passed (it can change the
+ * lane group).  kernel_id: RWS_KERNEL_AUTO, _WAVE_ROW, _BLOCK_ONEPASS or
+ * _TWO_PASS.  Performs no GPU work.
  */
 int norm_describe_launch(int64_t rows, int64_t cols, int dtype, const void *in, const void *out,
-                         int kernel_id, char *buf, int64_t buflen);
+                         int affine, int kernel_id, char *buf, int64_t buflen);
 
 /* Name of a kernel family ("wave_row", ...), or "unknown". Static storage. */
 const char *softmax_kernel_name(int kernel_id);

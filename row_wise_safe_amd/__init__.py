@@ -95,7 +95,7 @@ def load_library():
     lib.softmax_describe_launch_masked.argtypes = [i64, i64, cint, vp, vp, cint,
                                                    ctypes.c_char_p, i64]
     lib.softmax_describe_launch_masked.restype = cint
-    lib.norm_describe_launch.argtypes = [i64, i64, cint, vp, vp, cint, ctypes.c_char_p, i64]
+    lib.norm_describe_launch.argtypes = [i64, i64, cint, vp, vp, cint, cint, ctypes.c_char_p, i64]
     lib.norm_describe_launch.restype = cint
     lib.softmax_kernel_name.argtypes = [cint]
     lib.softmax_kernel_name.restype = ctypes.c_char_p
@@ -201,11 +201,12 @@ def softmax_describe_launch_masked(rows: int, cols: int, dtype: int, in_ptr: int
 
 
 def norm_describe_launch(rows: int, cols: int, dtype: int, in_ptr: int = 0, out_ptr: int = 0,
-                         kernel_id: int = 0) -> str:
-    """The launch layer_norm / rms_norm would make (kernel_id: KERNEL_IDS)."""
+                         kernel_id: int = 0, affine: bool = False) -> str:
+    """The launch layer_norm / rms_norm would make (kernel_id: KERNEL_IDS;
+    affine: a weight and/or bias is passed)."""
     buf = ctypes.create_string_buffer(256)
-    st = load_library().norm_describe_launch(rows, cols, dtype, in_ptr, out_ptr, kernel_id, buf,
-                                             len(buf))
+    st = load_library().norm_describe_launch(rows, cols, dtype, in_ptr, out_ptr, int(affine),
+                                             kernel_id, buf, len(buf))
     if st != RWS_OK:
         raise SoftmaxError(st, softmax_last_error())
     return buf.value.decode()

@@ -829,14 +829,19 @@ struct NormPlan {
 };
 
 static int plan_norm(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
-                     int kernel_id, NormPlan* np) {
+                     bool affine, int kernel_id, NormPlan* np) {
     const Geometry g = geometry(cols, dtype, in, out);
     const int64_t wline = window_granules(g, 128);
     // Lane groups measured on MI355X (fp16 LayerNorm / RMSNorm, rotating
     // buffers): windows of 9-32 granules take (16,2,1) ([131040,192]: 17.9 us,
     // (8,3,1) 18.3 us, (32,1,1) 21.5 us), windows of 33-48 take (8,6,1)
     // ([32760,384]: 9.0 us, (16,3,1) 10.2 us, (64,1,1) 11.4 us); other
-    // lengths the narrowest group that holds the window.
+    // lengths the narrowest group that holds the window.  With weight and/or
+    // bias the affine loads shift the balance to fewer rows per wave:
+    // windows of 17-24 take (8,3,1) (LayerNorm [131040,192] 19.5 us against
+    // 21.1 with (16,2,1); RMSNorm 18.7 either way) and 33-48 take (16,3,1)
+    // ([32760,384] LayerNorm 11.9 us against 12.7 with (8,6,1), RMSNorm 11.0
+    // against 11.3).
     auto norm_variant = [&](int G, int K, int U) {
         for (int i = 0; i < rws::kNumNormWave; ++i) {
             const rws::WaveRowVariant& v = rws::kNormWave[i];
@@ -849,6 +854,10 @@ static int plan_norm(int64_t rows, int64_t cols, int dtype, const void* in, cons
     // max_k limits the granules per lane of the other groups; the tuned
     // groups are taken for their windows whatever it is.
     auto pick_wave = [&](int max_k) {
+        if (affine && wline > 16 && wline <= 24 && norm_variant(8, 3, 1) >= 0)
+            return norm_variant(8, 3, 1);
+        if (affine && wline > 32 && wline <= 48 && norm_variant(16, 3, 1) >= 0)
+            return norm_variant(16, 3, 1);
         if (wline > 8 && wline <= 32 && norm_variant(16, 2, 1) >= 0) return norm_variant(16, 2, 1);
         if (wline > 32 && wline <= 48 && norm_variant(8, 6, 1) >= 0) return norm_variant(8, 6, 1);
         int best = -1;
@@ -932,7 +941,7 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
     if ((uintptr_t)mean % 4 || (uintptr_t)rstd % 4)
         return fail(RWS_ERR_MISALIGNED, "mean/rstd not aligned to 4 bytes");
     NormPlan np;
-    st = plan_norm(rows, cols, dtype, in, out, kernel_id, &np);
+    st = plan_norm(rows, cols, dtype, in, out, weight || bias, kernel_id, &np);
     if (st != RWS_OK) return st;
     const int family = np.family, variant = np.variant;
     const int64_t max_rows = np.max_rows;
@@ -948,6 +957,11 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
         L.aligned = np.aligned;
         L.same_phase = np.same_phase;
         L.lgrun = np.lgrun;
+        // aligned rows start at in's 16-byte phase; so do w and b when
+        // their offset from in is a multiple of 16 bytes
+        L.aff_matched = np.aligned &&
+                        (!weight || ((uintptr_t)weight - (uintptr_t)in) % 16 == 0) &&
+                        (!bias || ((uintptr_t)bias - (uintptr_t)in) % 16 == 0);
         L.args.w = weight;
         L.args.b = bias;
         L.args.mean = mean ? mean + r0 : nullptr;
@@ -1093,7 +1107,7 @@ int softmax_describe_launch_masked(int64_t rows, int64_t cols, int dtype, const 
 }
 
 int norm_describe_launch(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
-                         int kernel_id, char* buf, int64_t buflen) {
+                         int affine, int kernel_id, char* buf, int64_t buflen) {
     g_last_error.clear();
     if (!buf || buflen <= 0) return fail(RWS_ERR_INVALID_ARG, "no output buffer");
     buf[0] = 0;
@@ -1109,7 +1123,7 @@ int norm_describe_launch(int64_t rows, int64_t cols, int dtype, const void* in, 
         return RWS_OK;
     }
     NormPlan np;
-    const int st = plan_norm(rows, cols, dtype, in, out, kernel_id, &np);
+    const int st = plan_norm(rows, cols, dtype, in, out, affine != 0, kernel_id, &np);
     if (st != RWS_OK) return st;
     const char* al = np.aligned ? "aligned" : (np.same_phase ? "unaligned" : "unaligned,split-phase");
     const int64_t r = std::min(rows, np.max_rows);

@@ -131,6 +131,7 @@ struct NormLaunch {
     bool aligned;     // in, out 128-byte aligned and cols*size % 128 == 0
     bool same_phase;  // (out - in) % 16 == 0
     NormArgs args;    // mean/rstd already offset to the launch's first row
+    bool aff_matched = false;  // aligned rows; w and b (if given) at the rows' 16-byte phase
     int lgrun = 0;    // norm_block / norm_stream: XCD runs of 2^lgrun rows
     hipStream_t stream;
 };

@@ -21,9 +21,10 @@
 // The weight and bias vectors (cols entries of the tensor's dtype, optional)
 // are read on each row's granule grid: one 128-bit load per interior granule
 // when the vector shares the row's 16-byte phase, element loads otherwise.
-// They are small and stay in the caches; they are loaded after the
-// reductions, and kernels are instantiated with and without them (AFF) so
-// that the plain normalisation keeps its registers for the row.
+// They are small and stay in the caches; their loads are issued with the
+// row's own loads (affine_fetch), and kernels are instantiated with and
+// without them (AFF) so that the plain normalisation keeps its registers for
+// the row.
 #pragma once
 
 #include "rws_kernels.hpp"
@@ -31,8 +32,13 @@
 
 namespace rws {
 
-// A per-column vector (weight or bias) on a row window's granule grid.
-template <int DT, class Win>
+// A per-column vector (weight or bias) on a row window's granule grid.  PM
+// (phase-matched): the windows are ALIGNED and the vector starts at the
+// rows' 16-byte phase, so every granule k < ngran is one 128-bit load and
+// the element-by-element fallback is not compiled.  That fallback, present
+// in a kernel, costs registers even where no row takes it (fp16 norm_wave
+// (16,2) LayerNorm with weight and bias: 97 VGPRs with it, 59 without).
+template <int DT, class Win, bool PM = false>
 struct ColParam {
     static constexpr int VEC = Elem<DT>::VEC;
     static constexpr int ES = Elem<DT>::SIZE;
@@ -41,19 +47,23 @@ struct ColParam {
 
     __device__ inline ColParam(const void* p_, const Win& w) : p((const char*)p_) {
         const uintptr_t rin = (uintptr_t)w.gin + (uintptr_t)(w.lead * ES);
-        vec = (((uintptr_t)p - rin) & 15) == 0;
+        vec = PM || (((uintptr_t)p - rin) & 15) == 0;
     }
     // 128-bit load for an interior granule with a matching phase (no wait).
     __device__ inline u32x4 fetch(const Win& w, int k) const {
         u32x4 g = {0u, 0u, 0u, 0u};
+        if (PM) {
+            if (k < w.ngran) g = *(const u32x4*)(p + (int64_t)k * 16);
+            return g;
+        }
         const int c0 = k * VEC - w.lead;
         if (vec && c0 >= 0 && c0 + VEC <= w.cols) g = *(const u32x4*)(p + (int64_t)c0 * ES);
         return g;
     }
-    // Values of granule k's columns (0 outside the row).
+    // Values of granule k's columns (0 outside the row); k < ngran.
     __device__ inline void widen(const Win& w, int k, u32x4 raw, float* v) const {
         const int c0 = k * VEC - w.lead;
-        if (vec && c0 >= 0 && c0 + VEC <= w.cols) {
+        if (PM || (vec && c0 >= 0 && c0 + VEC <= w.cols)) {
             Elem<DT>::widen(raw, v);
             return;
         }
@@ -92,50 +102,49 @@ __device__ inline float centred_squares(const Win& w, int k0, int stride, const 
     return q;
 }
 
+// Issue the weight / bias loads of granules k0 + stride*i (i < KG) of one
+// row (no wait).  Called with the row's own loads: issued after the
+// reductions instead, the loads' cache latency lands on every row's critical
+// path (LayerNorm fp16 [32768,1000] with weight and bias 35.8 us against
+// 32.5 us issued early; RMSNorm with weight 31.0 against 26.9).
+template <int KG, class Win, class CP>
+__device__ inline void affine_fetch(const Win& w, int k0, int stride, const NormArgs& A,
+                                    const CP& pw, const CP& pb, u32x4* rw, u32x4* rb) {
+#pragma unroll
+    for (int i = 0; i < KG; ++i) {
+        const int k = k0 + stride * i;
+        rw[i] = A.w ? pw.fetch(w, k) : u32x4{0u, 0u, 0u, 0u};
+        rb[i] = A.b ? pb.fetch(w, k) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
 // Normalise and store granules k0 + stride*i (i < KG) of one row.  AFF:
-// apply A.w and/or A.b (whichever is not null).
-template <int DT, int MODE, bool AFF, int KG, class Win>
+// apply A.w and/or A.b (whichever is not null) from the granules
+// affine_fetch loaded into rw / rb.
+template <int DT, int MODE, bool AFF, int KG, class Win, class CP>
 __device__ inline void norm_store(const Win& w, int k0, int stride, const float* v, float mu,
-                                  float rstd, const NormArgs& A, bool same_phase) {
+                                  float rstd, const NormArgs& A, bool same_phase, const CP* pw,
+                                  const CP* pb, const u32x4* rw, const u32x4* rb) {
     constexpr int VEC = Elem<DT>::VEC;
-    if constexpr (!AFF) {
 #pragma unroll
-        for (int i = 0; i < KG; ++i) {
-            const int k = k0 + stride * i;
-            if (k < w.ngran) {
-                float o[VEC];
+    for (int i = 0; i < KG; ++i) {
+        const int k = k0 + stride * i;
+        if (k < w.ngran) {
+            float o[VEC];
 #pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    o[e] = MODE == kLayerNorm ? (v[i * VEC + e] - mu) * rstd : v[i * VEC + e] * rstd;
-                w.store(k, o, same_phase);
-            }
-        }
-    } else {
-        const ColParam<DT, Win> pw(A.w, w), pb(A.b, w);
-        u32x4 rw[KG], rb[KG];
-#pragma unroll
-        for (int i = 0; i < KG; ++i) {
-            const int k = k0 + stride * i;
-            rw[i] = A.w ? pw.fetch(w, k) : u32x4{0u, 0u, 0u, 0u};
-            rb[i] = A.b ? pb.fetch(w, k) : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int i = 0; i < KG; ++i) {
-            const int k = k0 + stride * i;
-            if (k < w.ngran) {
-                float fw[VEC], fb[VEC], o[VEC];
-                if (A.w) pw.widen(w, k, rw[i], fw);
-                if (A.b) pb.widen(w, k, rb[i], fb);
+            for (int e = 0; e < VEC; ++e)
+                o[e] = MODE == kLayerNorm ? (v[i * VEC + e] - mu) * rstd : v[i * VEC + e] * rstd;
+            if constexpr (AFF) {
+                float fw[VEC], fb[VEC];
+                if (A.w) pw->widen(w, k, rw[i], fw);
+                if (A.b) pb->widen(w, k, rb[i], fb);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    float t = MODE == kLayerNorm ? (v[i * VEC + e] - mu) * rstd
-                                                 : v[i * VEC + e] * rstd;
-                    if (A.w) t *= fw[e];
-                    if (A.b) t += fb[e];
-                    o[e] = t;
+                    if (A.w) o[e] *= fw[e];
+                    if (A.b) o[e] += fb[e];
                 }
-                w.store(k, o, same_phase);
             }
+            w.store(k, o, same_phase);
         }
     }
 }
@@ -151,7 +160,9 @@ __device__ inline float norm_rstd(float q, const NormArgs& A) {
 // norm_wave: G lanes per row, 64/G rows per set, U sets per wave, K granules
 // per lane (the wave_row layout of the softmax kernels).
 // ===========================================================================
-template <int DT, bool ALIGNED, int G, int K, int U, int MODE, bool AFF>
+// AFF: 0 no weight or bias, 1 either or both, 2 the same with every row's
+// phase matched (ColParam PM; ALIGNED only).
+template <int DT, bool ALIGNED, int G, int K, int U, int MODE, int AFF>
 __global__ __launch_bounds__(256) void k_norm_wave(const void* __restrict__ in,
                                                    void* __restrict__ out, int64_t rows, int cols,
                                                    NormArgs A, int same_phase) {
@@ -160,6 +171,8 @@ __global__ __launch_bounds__(256) void k_norm_wave(const void* __restrict__ in,
     constexpr int N = K * VEC;
     constexpr int WA = G * 16 >= kLineBytes ? kLineBytes : 16;
     using Win = RowWin<DT, ALIGNED, WA>;
+    static_assert(AFF != 2 || ALIGNED, "phase-matched parameters need aligned rows");
+    using CP = ColParam<DT, Win, AFF == 2>;
     const int lane = threadIdx.x & 63;
     const int gl = lane & (G - 1);
     const int sub = lane / G;
@@ -171,6 +184,8 @@ __global__ __launch_bounds__(256) void k_norm_wave(const void* __restrict__ in,
 
     Win w[U];
     u32x4 raw[U][K];
+    constexpr int KA = AFF ? K : 1;
+    u32x4 rw[AFF ? U : 1][KA], rb[AFF ? U : 1][KA];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         int64_t row = row0 + u * RPS + sub;
@@ -178,6 +193,7 @@ __global__ __launch_bounds__(256) void k_norm_wave(const void* __restrict__ in,
         w[u] = Win(in, out, row, cols);
 #pragma unroll
         for (int i = 0; i < K; ++i) raw[u][i] = w[u].fetch(gl + G * i, tbeg, tend);
+        if constexpr (AFF != 0) affine_fetch<K>(w[u], gl, G, A, CP(A.w, w[u]), CP(A.b, w[u]), rw[u], rb[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -199,7 +215,9 @@ __global__ __launch_bounds__(256) void k_norm_wave(const void* __restrict__ in,
         const float rstd = norm_rstd(q, A);
         const int64_t row = row0 + u * RPS + sub;
         if (row < rows) {
-            norm_store<DT, MODE, AFF, K>(w[u], gl, G, v, mu, rstd, A, same_phase != 0);
+            const CP pw(A.w, w[u]), pb(A.b, w[u]);
+            norm_store<DT, MODE, (AFF != 0), K>(w[u], gl, G, v, mu, rstd, A, same_phase != 0, &pw,
+                                                &pb, rw[AFF ? u : 0], rb[AFF ? u : 0]);
             if (gl == 0) {
                 if (A.mean) A.mean[row] = mu;
                 if (A.rstd) A.rstd[row] = rstd;
@@ -216,15 +234,33 @@ __global__ __launch_bounds__(256) void k_norm_wave(const void* __restrict__ in,
 // 39.8 us against 24.9 us capped (RMSNorm 36.9 / 24.3; [8192,4097] with
 // 192x3 32.0 / 24.3).  No spills at that cap.
 // ===========================================================================
-template <int DT, bool ALIGNED, int BLOCK, int KR, int MODE, bool AFF>
+// Waves per SIMD asked of the compiler for a norm_block kernel (1: no
+// request): six for 2-3 granules per thread, five for fp32 rows with weight
+// or bias at 3 (six spilled there); none where the kernel fits anyway
+// (aligned affine forms) or the workgroup size already bounds the registers.
+constexpr int norm_block_waves(int dt, bool aligned, int block, int kr, bool aff) {
+    if (kr != 2 && kr != 3) return 1;
+    if (block == 1024 || (aff && aligned)) return 1;
+    if (aff && kr == 3 && dt == kF32) return 5;
+    return 6;
+}
+
+// 1024-thread workgroups have at most 128 VGPRs; holding 3-4 granules of
+// weight and bias from the start spilled there, so those load them late.
+constexpr bool norm_block_early_affine(int block, int kr) { return !(block == 1024 && kr >= 3); }
+
+// AFF as for k_norm_wave.
+template <int DT, bool ALIGNED, int BLOCK, int KR, int MODE, int AFF>
 __global__ __launch_bounds__(BLOCK)
-__attribute__((amdgpu_waves_per_eu((KR == 2 || KR == 3) && !(AFF && ALIGNED) ? 6 : 1))) void k_norm_block(const void* __restrict__ in,
+__attribute__((amdgpu_waves_per_eu(norm_block_waves(DT, ALIGNED, BLOCK, KR, AFF != 0)))) void k_norm_block(const void* __restrict__ in,
                                                       void* __restrict__ out, int64_t rows,
                                                       int cols, NormArgs A, int same_phase, int lgrun) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     constexpr int N = KR * VEC;
     using Win = RowWin<DT, ALIGNED>;
+    static_assert(AFF != 2 || ALIGNED, "phase-matched parameters need aligned rows");
+    using CP = ColParam<DT, Win, AFF == 2>;
     __shared__ float red1[W];
     __shared__ float red2[W];
     const int t = threadIdx.x;
@@ -235,6 +271,10 @@ __attribute__((amdgpu_waves_per_eu((KR == 2 || KR == 3) && !(AFF && ALIGNED) ? 6
     u32x4 raw[KR];
 #pragma unroll
     for (int i = 0; i < KR; ++i) raw[i] = w.fetch(t + BLOCK * i, tbeg, tend);
+    const CP pw(A.w, w), pb(A.b, w);
+    u32x4 rw[AFF ? KR : 1], rb[AFF ? KR : 1];
+    constexpr bool kEarly = norm_block_early_affine(BLOCK, KR);
+    if constexpr (AFF != 0 && kEarly) affine_fetch<KR>(w, t, BLOCK, A, pw, pb, rw, rb);
     float v[N];
 #pragma unroll
     for (int i = 0; i < KR; ++i) widen_zero<DT>(w, t + BLOCK * i, raw[i], &v[i * VEC], tbeg, tend);
@@ -251,7 +291,8 @@ __attribute__((amdgpu_waves_per_eu((KR == 2 || KR == 3) && !(AFF && ALIGNED) ? 6
     }
     q = block_reduce<W, OpSum>(q, red2);
     const float rstd = norm_rstd(q, A);
-    norm_store<DT, MODE, AFF, KR>(w, t, BLOCK, v, mu, rstd, A, same_phase != 0);
+    if constexpr (AFF != 0 && !kEarly) affine_fetch<KR>(w, t, BLOCK, A, pw, pb, rw, rb);
+    norm_store<DT, MODE, (AFF != 0), KR>(w, t, BLOCK, v, mu, rstd, A, same_phase != 0, &pw, &pb, rw, rb);
     if (t == 0) {
         if (A.mean) A.mean[row] = mu;
         if (A.rstd) A.rstd[row] = rstd;
@@ -375,6 +416,7 @@ __global__ __launch_bounds__(BLOCK) void k_norm_stream(const void* __restrict__ 
     const float rstd = norm_rstd(q, A);
 
     // pass 2: normalise and write
+    const ColParam<DT, Win> pw(A.w, w), pb(A.b, w);
     for (int k0 = t; k0 < w.ngran; k0 += BLOCK * U) {
         u32x4 raw[U];
 #pragma unroll
@@ -382,7 +424,9 @@ __global__ __launch_bounds__(BLOCK) void k_norm_stream(const void* __restrict__ 
         float v[U * VEC];
 #pragma unroll
         for (int u = 0; u < U; ++u) widen_zero<DT>(w, k0 + BLOCK * u, raw[u], &v[u * VEC], tbeg, tend);
-        norm_store<DT, MODE, AFF, U>(w, k0, BLOCK, v, mu, rstd, A, same_phase != 0);
+        u32x4 rw[AFF ? U : 1], rb[AFF ? U : 1];
+        if constexpr (AFF) affine_fetch<U>(w, k0, BLOCK, A, pw, pb, rw, rb);
+        norm_store<DT, MODE, AFF, U>(w, k0, BLOCK, v, mu, rstd, A, same_phase != 0, &pw, &pb, rw, rb);
     }
     if (t == 0) {
         if (A.mean) A.mean[row] = mu;

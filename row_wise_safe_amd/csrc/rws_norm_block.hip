@@ -33,11 +33,20 @@ const int kNumNormStream = sizeof(kNormStream) / sizeof(kNormStream[0]);
 template <int DT, bool AL, int BL, int KR, int MODE>
 static hipError_t nb_mode(const NormLaunch& L) {
     const dim3 grid((unsigned)L.rows);
-    if (L.args.w || L.args.b)
-        hipLaunchKernelGGL((k_norm_block<DT, AL, BL, KR, MODE, true>), grid, dim3(BL), 0, L.stream,
+    if (!L.args.w && !L.args.b)
+        hipLaunchKernelGGL((k_norm_block<DT, AL, BL, KR, MODE, 0>), grid, dim3(BL), 0, L.stream,
                            L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase, L.lgrun);
-    else
-        hipLaunchKernelGGL((k_norm_block<DT, AL, BL, KR, MODE, false>), grid, dim3(BL), 0, L.stream,
+    else if constexpr (AL) {
+        if (L.aff_matched)
+            hipLaunchKernelGGL((k_norm_block<DT, AL, BL, KR, MODE, 2>), grid, dim3(BL), 0,
+                               L.stream, L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase,
+                               L.lgrun);
+        else
+            hipLaunchKernelGGL((k_norm_block<DT, AL, BL, KR, MODE, 1>), grid, dim3(BL), 0,
+                               L.stream, L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase,
+                               L.lgrun);
+    } else
+        hipLaunchKernelGGL((k_norm_block<DT, AL, BL, KR, MODE, 1>), grid, dim3(BL), 0, L.stream,
                            L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase, L.lgrun);
     return hipGetLastError();
 }

@@ -14,6 +14,8 @@ namespace rws {
     X(16, 1, 1)                   \
     X(16, 2, 1)                   \
     X(8, 6, 1)                    \
+    X(8, 3, 1)                    \
+    X(16, 3, 1)                   \
     X(32, 1, 1)                   \
     X(64, 1, 1)                   \
     X(64, 2, 1)                   \
@@ -29,12 +31,20 @@ template <int DT, bool AL, int G, int K, int U, int MODE>
 static hipError_t nw_mode(const NormLaunch& L) {
     const WaveRowVariant v = {G, K, U};
     const dim3 grid((unsigned)wave_row_grid(v, L.rows));
-    if (L.args.w || L.args.b)
-        hipLaunchKernelGGL((k_norm_wave<DT, AL, G, K, U, MODE, true>), grid, dim3(kWaveGroupThreads), 0, L.stream,
-                           L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase);
-    else
-        hipLaunchKernelGGL((k_norm_wave<DT, AL, G, K, U, MODE, false>), grid, dim3(kWaveGroupThreads), 0, L.stream,
-                           L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase);
+    const dim3 block(kWaveGroupThreads);
+    if (!L.args.w && !L.args.b)
+        hipLaunchKernelGGL((k_norm_wave<DT, AL, G, K, U, MODE, 0>), grid, block, 0, L.stream, L.in,
+                           L.out, L.rows, L.cols, L.args, (int)L.same_phase);
+    else if constexpr (AL) {
+        if (L.aff_matched)
+            hipLaunchKernelGGL((k_norm_wave<DT, AL, G, K, U, MODE, 2>), grid, block, 0, L.stream,
+                               L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase);
+        else
+            hipLaunchKernelGGL((k_norm_wave<DT, AL, G, K, U, MODE, 1>), grid, block, 0, L.stream,
+                               L.in, L.out, L.rows, L.cols, L.args, (int)L.same_phase);
+    } else
+        hipLaunchKernelGGL((k_norm_wave<DT, AL, G, K, U, MODE, 1>), grid, block, 0, L.stream, L.in,
+                           L.out, L.rows, L.cols, L.args, (int)L.same_phase);
     return hipGetLastError();
 }
 

@@ -187,6 +187,18 @@ def test_norm_shape_choice(lib, rows, cols, shape):
     assert desc.startswith(shape), desc
 
 
+# With weight and/or bias the two tuned widths take groups of fewer rows.
+@pytest.mark.parametrize("rows,cols,shape", [
+    (131040, 192, "norm_wave<f16,aligned,G=8,K=3,U=1>"),
+    (32760, 384, "norm_wave<f16,aligned,G=16,K=3,U=1>"),
+    (131040, 184, "norm_wave<f16,unaligned,G=16,K=2,U=1>"),  # window 31: (8,3) too small
+    (8192, 4096, "norm_block<f16,aligned,B=256,KR=2>"),
+])
+def test_norm_affine_shape_choice(lib, rows, cols, shape):
+    desc = rws.norm_describe_launch(rows, cols, rws.RWS_F16, 256, 512, affine=True)
+    assert desc.startswith(shape), desc
+
+
 # Runs of consecutive rows per XCD for block_onepass on rows that are not
 # line-aligned: the smallest power of two of at least 128 KiB of rows.
 @pytest.mark.parametrize("rows,cols,inp,run", [

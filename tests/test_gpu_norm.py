@@ -145,6 +145,20 @@ def test_norm_workload_full_size(name, mode):
     assert e <= 2.0 ** -8 * 2
 
 
+# the same shapes with weight and bias (RMSNorm: weight) in the lane groups
+# taken with them, the vectors at the rows' 16-byte phase (the phase-matched
+# kernels) and 2 elements off it (element loads)
+@pytest.mark.parametrize("w_off", [0, 2])
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("name", list(workloads.NORM_WORKLOADS))
+def test_norm_workload_affine(name, mode, w_off):
+    wl = workloads.NORM_WORKLOADS[name]
+    desc = rws.norm_describe_launch(wl.rows, wl.cols, rws.RWS_F16, 256, 512, affine=True)
+    print(f"\n{name} {mode} w_off={w_off}: {desc}", flush=True)
+    _case(mode, wl.dtype, wl.rows, wl.cols, "auto", seed=wl.seed + 1, affine=True, w_off=w_off,
+          x64=wl.generate())
+
+
 # --------------------------------------------------------------------------
 # sweep: row lengths across the three families' ranges and their ragged
 # edges, every dtype, each family forced, both modes
