@@ -271,6 +271,16 @@ int softmax_describe_launch_masked(int64_t rows, int64_t cols, int dtype, const 
                                    const void *out, int kernel_id, char *buf, int64_t buflen);
 
 /*
+ * softmax_bwd_describe_launch -- the same for the launch
+ * softmax_bwd_kernel(kernel_id) would make with these y and dx pointers
+ * (bwd_wave, bwd_block or bwd_stream, with its shape).  kernel_id:
+ * RWS_KERNEL_AUTO, _WAVE_ROW, _BLOCK_ONEPASS or _TWO_PASS.  Performs no GPU
+ * work.
+ */
+int softmax_bwd_describe_launch(int64_t rows, int64_t cols, int dtype, const void *y,
+                                const void *dx, int kernel_id, char *buf, int64_t buflen);
+
+/*
  * norm_describe_launch -- the same for the launch layernorm_fwd_kernel /
  * rmsnorm_fwd_kernel(kernel_id) would make on these tensors (both use the
  * same choice: norm_wave, norm_block or norm_stream, with its shape).

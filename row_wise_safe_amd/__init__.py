@@ -30,6 +30,7 @@ __all__ = [
     "softmax_describe_launch",
     "softmax_describe_launch_masked",
     "norm_describe_launch",
+    "softmax_bwd_describe_launch",
     "softmax_kernel_name", "softmax_status_string", "softmax_last_error", "softmax_copy_bytes",
     "layernorm_fwd", "layernorm_fwd_kernel", "rmsnorm_fwd", "rmsnorm_fwd_kernel",
     "softmax", "softmax_masked", "softmax_backward", "layer_norm", "rms_norm", "copy_bytes",
@@ -97,6 +98,8 @@ def load_library():
     lib.softmax_describe_launch_masked.restype = cint
     lib.norm_describe_launch.argtypes = [i64, i64, cint, vp, vp, cint, cint, ctypes.c_char_p, i64]
     lib.norm_describe_launch.restype = cint
+    lib.softmax_bwd_describe_launch.argtypes = [i64, i64, cint, vp, vp, cint, ctypes.c_char_p, i64]
+    lib.softmax_bwd_describe_launch.restype = cint
     lib.softmax_kernel_name.argtypes = [cint]
     lib.softmax_kernel_name.restype = ctypes.c_char_p
     lib.softmax_status_string.argtypes = [cint]
@@ -198,6 +201,17 @@ def softmax_describe_launch(rows: int, cols: int, dtype: int, in_ptr: int = 0, o
 def softmax_describe_launch_masked(rows: int, cols: int, dtype: int, in_ptr: int = 0,
                                    out_ptr: int = 0, kernel_id: int = 0) -> str:
     return softmax_describe_launch(rows, cols, dtype, in_ptr, out_ptr, kernel_id, masked=True)
+
+
+def softmax_bwd_describe_launch(rows: int, cols: int, dtype: int, y_ptr: int = 0, dx_ptr: int = 0,
+                                kernel_id: int = 0) -> str:
+    """The launch softmax_backward would make (kernel_id: KERNEL_IDS)."""
+    buf = ctypes.create_string_buffer(256)
+    st = load_library().softmax_bwd_describe_launch(rows, cols, dtype, y_ptr, dx_ptr, kernel_id,
+                                                    buf, len(buf))
+    if st != RWS_OK:
+        raise SoftmaxError(st, softmax_last_error())
+    return buf.value.decode()
 
 
 def norm_describe_launch(rows: int, cols: int, dtype: int, in_ptr: int = 0, out_ptr: int = 0,

@@ -723,17 +723,18 @@ int softmax_fwd_masked(const void* in, void* out, int64_t rows, int64_t cols, in
 
 // Softmax backward: family 1 (wave, registers), 2 (block, registers) or 3
 // (stream, any length), chosen like the forward kernels by the row window.
-int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, int64_t cols,
-                       int dtype, void* stream, int kernel_id) {
-    g_last_error.clear();
-    if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
-        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS)
-        return fail(RWS_ERR_INVALID_ARG, "backward kernels: auto, wave_row, block_onepass, two_pass");
-    int st = check_args(y, dx, rows, cols, dtype, RWS_KERNEL_AUTO);
-    if (st != RWS_OK || rows == 0 || cols == 0) return st;
-    if (!dy) return fail(RWS_ERR_INVALID_ARG, "NULL dy with a non-empty tensor");
-    if ((uintptr_t)dy % elem_size(dtype))
-        return fail(RWS_ERR_MISALIGNED, "dy not aligned to the element size");
+struct BwdPlan {
+    int family = 0;  // 1 wave, 2 block, 3 stream
+    int variant = 0;
+    bool aligned = false;
+    bool same_phase = false;
+    int lgrun = 0;
+    int64_t max_rows = 0;
+};
+
+static int plan_bwd(int64_t rows, int64_t cols, int dtype, const void* y, const void* dx,
+                    int kernel_id, BwdPlan* bp) {
+    (void)rows;
     const Geometry g = geometry(cols, dtype, y, dx);
     const int64_t wline = window_granules(g, 128);
     int family = kernel_id == RWS_KERNEL_AUTO ? 0 : kernel_id;  // 1 wave, 2 block, 3 stream
@@ -741,10 +742,10 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
     bool aligned = g.a128;
     // Forms, by sweeps on MI355X with inputs in HBM: one wave per row while a
     // lane group holds the row at one granule per lane, else one workgroup
-    // per row with one granule per thread (fp16 [32768,1000]: 36.3 us against
-    // 76.1 us for one wave per row with 4 granules per lane; [131072,480]:
-    // 76.8 us against 88.6 with 2 per lane; [8192,4097]: 37.2, the same as
-    // 192x3 or 320x2), longer rows on 1024 threads; any length streams.
+    // per row (fp16 [32768,1000]: 36.3 us with 192x1 against 76.1 us for one
+    // wave per row with 4 granules per lane; [131072,480]: 76.8 us against
+    // 88.6 with 2 per lane; shapes below), longer rows on 1024 threads; any
+    // length streams.
     auto pick_wave = [&](int max_k) {
         int best = -1;
         int64_t best_cap = 0;
@@ -758,13 +759,24 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
         }
         return best;
     };
+    // Block shape: the smallest capacity that holds the row; at equal
+    // capacity the one with more granules per thread (fewer waves per row).
+    // Sweeps on MI355X (fp16, three tensors, inputs in HBM): [8192,4097]
+    // 192x3 34.1 us against 576x1 37.3; [32768,1000] 64x3 33.6 against 192x1
+    // 34.7; where one granule per thread fits exactly it wins ([8192,4096]
+    // 512x1 32.8 against 256x2 33.5; [16384,2048] 256x1 33.3; [32768,1024]
+    // 128x1 32.7), and [16384,2000] keeps 320x1 (32.9; 128x3 33.3, 64x5 34.0).
     auto pick_block = [&]() {
         int best = -1;
+        int64_t best_key = 0;
         for (int i = 0; i < rws::kNumBwdBlock; ++i) {
             const int64_t cap = (int64_t)rws::kBwdBlock[i].block * rws::kBwdBlock[i].u;
             if (cap < wline) continue;
-            if (best < 0 || cap < (int64_t)rws::kBwdBlock[best].block * rws::kBwdBlock[best].u)
+            const int64_t key = cap * 16 - rws::kBwdBlock[i].u;
+            if (best < 0 || key < best_key) {
                 best = i;
+                best_key = key;
+            }
         }
         return best;
     };
@@ -791,6 +803,31 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
         ? (int64_t)(64 / rws::kBwdWave[variant].G) * rws::kBwdWave[variant].U * 4 * ((int64_t)1 << 23)
         : block_rows_per_launch(family == 2 ? rws::kBwdBlock[variant].block
                                             : rws::kBwdStream[variant].block);
+    bp->family = family;
+    bp->variant = variant;
+    bp->aligned = aligned;
+    bp->same_phase = g.same_phase;
+    bp->lgrun = family == 2 ? xcd_run_lg(g) : 0;
+    bp->max_rows = max_rows;
+    return RWS_OK;
+}
+
+int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, int64_t cols,
+                       int dtype, void* stream, int kernel_id) {
+    g_last_error.clear();
+    if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
+        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS)
+        return fail(RWS_ERR_INVALID_ARG, "backward kernels: auto, wave_row, block_onepass, two_pass");
+    int st = check_args(y, dx, rows, cols, dtype, RWS_KERNEL_AUTO);
+    if (st != RWS_OK || rows == 0 || cols == 0) return st;
+    if (!dy) return fail(RWS_ERR_INVALID_ARG, "NULL dy with a non-empty tensor");
+    if ((uintptr_t)dy % elem_size(dtype))
+        return fail(RWS_ERR_MISALIGNED, "dy not aligned to the element size");
+    BwdPlan bp;
+    st = plan_bwd(rows, cols, dtype, y, dx, kernel_id, &bp);
+    if (st != RWS_OK) return st;
+    const int family = bp.family, variant = bp.variant;
+    const int64_t max_rows = bp.max_rows;
     const int64_t row_bytes = cols * elem_size(dtype);
     for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
         rws::BwdLaunch B;
@@ -800,10 +837,10 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
         B.dx = (char*)dx + r0 * row_bytes;
         B.cols = (int)cols;
         B.dtype = dtype;
-        B.aligned = aligned;
-        B.same_phase = g.same_phase;
+        B.aligned = bp.aligned;
+        B.same_phase = bp.same_phase;
         B.dy_vec = (((uintptr_t)dy - (uintptr_t)y) % 16) == 0;
-        B.lgrun = family == 2 ? xcd_run_lg(g) : 0;
+        B.lgrun = bp.lgrun;
         B.stream = (hipStream_t)stream;
         const hipError_t e = rws::launch_bwd(B, family, variant);
         if (e != hipSuccess)
@@ -1104,6 +1141,44 @@ int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void* i
 int softmax_describe_launch_masked(int64_t rows, int64_t cols, int dtype, const void* in,
                                    const void* out, int kernel_id, char* buf, int64_t buflen) {
     return describe_launch(rows, cols, dtype, in, out, kernel_id, true, buf, buflen);
+}
+
+int softmax_bwd_describe_launch(int64_t rows, int64_t cols, int dtype, const void* y,
+                                const void* dx, int kernel_id, char* buf, int64_t buflen) {
+    g_last_error.clear();
+    if (!buf || buflen <= 0) return fail(RWS_ERR_INVALID_ARG, "no output buffer");
+    buf[0] = 0;
+    if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
+        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS)
+        return fail(RWS_ERR_INVALID_ARG, "backward kernels: auto, wave_row, block_onepass, two_pass");
+    if (dtype != RWS_F32 && dtype != RWS_F16 && dtype != RWS_BF16)
+        return fail(RWS_ERR_UNSUPPORTED_DTYPE, "dtype must be RWS_F32, RWS_F16 or RWS_BF16");
+    if (rows < 0 || cols < 0) return fail(RWS_ERR_INVALID_ARG, "rows and cols must be >= 0");
+    if (cols > kMaxCols) return fail(RWS_ERR_UNSUPPORTED_SHAPE, "cols above 2^30");
+    if (rows == 0 || cols == 0) {
+        std::snprintf(buf, (size_t)buflen, "empty: no launch");
+        return RWS_OK;
+    }
+    BwdPlan bp;
+    const int st = plan_bwd(rows, cols, dtype, y, dx, kernel_id, &bp);
+    if (st != RWS_OK) return st;
+    const char* al = bp.aligned ? "aligned" : (bp.same_phase ? "unaligned" : "unaligned,split-phase");
+    const int64_t r = std::min(rows, bp.max_rows);
+    if (bp.family == 1) {
+        const rws::WaveRowVariant& v = rws::kBwdWave[bp.variant];
+        std::snprintf(buf, (size_t)buflen, "bwd_wave<%s,%s,G=%d,K=%d,U=%d> grid=%lld block=%d",
+                      dtype_name(dtype), al, v.G, v.K, v.U, (long long)rws::wave_row_grid(v, r),
+                      rws::kWaveGroupThreads);
+    } else {
+        const rws::TwoPassVariant& v =
+            bp.family == 2 ? rws::kBwdBlock[bp.variant] : rws::kBwdStream[bp.variant];
+        char run[32] = "";
+        if (bp.lgrun > 0) std::snprintf(run, sizeof run, " xcd_run=%d", 1 << bp.lgrun);
+        std::snprintf(buf, (size_t)buflen, "%s<%s,%s,B=%d,%s=%d> grid=%lld block=%d%s",
+                      bp.family == 2 ? "bwd_block" : "bwd_stream", dtype_name(dtype), al, v.block,
+                      bp.family == 2 ? "KR" : "U", v.u, (long long)r, v.block, run);
+    }
+    return RWS_OK;
 }
 
 int norm_describe_launch(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,

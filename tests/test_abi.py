@@ -199,6 +199,22 @@ def test_norm_affine_shape_choice(lib, rows, cols, shape):
     assert desc.startswith(shape), desc
 
 
+# Backward block shapes: the smallest capacity, at equal capacity the one
+# with more granules per thread.
+@pytest.mark.parametrize("rows,cols,shape", [
+    (65536, 512, "bwd_wave<f16,aligned,G=64,K=1,U=1>"),
+    (32768, 1000, "bwd_block<f16,unaligned,B=64,KR=3> grid=32768 block=64 xcd_run=128"),
+    (32768, 1024, "bwd_block<f16,aligned,B=128,KR=1>"),
+    (16384, 2000, "bwd_block<f16,unaligned,B=320,KR=1>"),
+    (8192, 4096, "bwd_block<f16,aligned,B=512,KR=1>"),
+    (8192, 4097, "bwd_block<f16,unaligned,B=192,KR=3> grid=8192 block=192 xcd_run=16"),
+    (64, 40000, "bwd_stream<f16,aligned,B=1024,U=4>"),
+])
+def test_bwd_shape_choice(lib, rows, cols, shape):
+    desc = rws.softmax_bwd_describe_launch(rows, cols, rws.RWS_F16, 256, 512)
+    assert desc.startswith(shape), desc
+
+
 # Runs of consecutive rows per XCD for block_onepass on rows that are not
 # line-aligned: the smallest power of two of at least 128 KiB of rows.
 @pytest.mark.parametrize("rows,cols,inp,run", [

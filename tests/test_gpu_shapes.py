@@ -105,3 +105,32 @@ def test_every_norm_block_shape(dtype, few):
     for (b, kr), (rows, cols) in sorted(cases.items()):
         for mode in ("layernorm", "rmsnorm"):
             _case(mode, dtype, rows, cols, "auto", seed=rows * 7 + cols + kr)
+
+
+def _bwd_cases(dtype: str):
+    """{(B, KR): (rows, cols)} of the backward's workgroup-per-row shapes."""
+    es = ES[dtype]
+    seen = {}
+    step = 16 // es
+    for cols in range(step, 4096 * step, step):
+        desc = rws.softmax_bwd_describe_launch(64, cols, CODE[dtype], 256, 512)
+        m = re.match(r"bwd_block<[^>]*B=(\d+),KR=(\d+)>", desc)
+        if m:
+            seen.setdefault(tuple(int(v) for v in m.groups()), (64, cols))
+    return seen
+
+
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_every_bwd_block_shape(dtype):
+    from test_gpu_backward import _check as check_backward
+    cases = _bwd_cases(dtype)
+    assert len(cases) >= 13, cases
+    for (b, kr), (rows, cols) in sorted(cases.items()):
+        g = np.random.Generator(np.random.PCG64(rows * 11 + cols))
+        y, ys = to_device(oracle.safe_softmax(g.normal(0.0, 2.0, (rows, cols))), dtype)
+        dy, gs = to_device(g.normal(0.0, 1.0, (rows, cols)), dtype)
+        desc = rws.softmax_bwd_describe_launch(rows, cols, CODE[dtype], y.data_ptr(), y.data_ptr())
+        assert f"B={b},KR={kr}" in desc, desc
+        dx = rws.softmax_backward(y, dy)
+        torch.cuda.synchronize()
+        check_backward(dx.double().cpu().numpy(), ys, gs, dtype, f"{desc} rows={rows} cols={cols}")
