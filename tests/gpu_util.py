@@ -56,9 +56,11 @@ def window_granules(cols: int, dtype: str, aligned: bool) -> int:
 
 def supports(kernel: str, cols: int, dtype: str, aligned: bool) -> bool:
     es = 4 if dtype == "f32" else 2
-    w = window_granules(cols, dtype, aligned and (cols * es) % 128 == 0)
+    line = aligned and (cols * es) % 128 == 0
+    w = window_granules(cols, dtype, line)
     if kernel == "wave_row":
         return w <= 512
     if kernel == "block_onepass":
-        return w <= 16384
+        # rows that are not line-aligned: at most 6 register granules per thread
+        return w <= (16384 if line else 6144)
     return True
