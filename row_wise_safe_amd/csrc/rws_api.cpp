@@ -227,19 +227,21 @@ int pick_block_shape(int n, Shape shape, int64_t w, int64_t rows, int cus) {
     return best;
 }
 
-// block_onepass variant (regs_only: no LDS parking, as the masked form
-// needs).  On rows that are not line-aligned the shapes with 8 register
-// granules are left out: their kernels exceed the 128 VGPRs of a 1024-thread
-// workgroup and spill (172-240 bytes per lane), and ran at ~2.9 TB/s where
-// two_pass reaches 4.2-4.9 (bf16 [16384,50257]: 1131 us against 790; fp16
-// [4096,128257] 707 against 425).  Aligned, they spill 40-72 bytes and stay
-// ahead of two_pass (fp16 [4096,128256] 436 us against 448).
-int pick_onepass(int64_t w, int64_t rows, int cus, bool regs_only, bool aligned) {
+// block_onepass variant (masked: no LDS parking, and the widened kernel
+// form).  On rows that are not line-aligned, 8-granule shapes whose kernel
+// exceeds the 128 VGPRs of a 1024-thread workgroup and spills are left out:
+// those with LDS parking (136-240 bytes per lane), and the masked 16-bit
+// form (172).  They ran at ~2.9 TB/s where two_pass reaches 4.2-5.0 (fp16
+// [4096,128257]: 707 us against 422).  The plain 16-bit form at 8 register
+// granules holds the row as raw granules (k_block_onepass_raw) and fits.
+int pick_onepass(int64_t w, int64_t rows, int cus, bool masked, bool aligned, int dtype) {
     return pick_block_shape(
         rws::kNumOnepass,
         [&](int i) {
             const rws::OnepassVariant& v = rws::kOnepass[i];
-            if ((regs_only && v.kl != 0) || (!aligned && v.kr + v.kl >= 8)) return BlockShape{0, 0, 0};
+            const bool spills = !aligned && v.kr + v.kl >= 8 &&
+                                (v.kl > 0 || (masked && dtype != RWS_F32));
+            if ((masked && v.kl != 0) || spills) return BlockShape{0, 0, 0};
             return BlockShape{v.block, v.kr, v.kl};
         },
         w, rows, cus);
@@ -347,7 +349,7 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
     int family = kernel_id;
     if (family == RWS_KERNEL_AUTO) {
         const bool few_rows = rows < 2LL * cus;
-        const bool onepass_fits = pick_onepass(wline, rows, cus, false, g.a128) >= 0;
+        const bool onepass_fits = pick_onepass(wline, rows, cus, false, g.a128, dtype) >= 0;
         if (pick_wave_row(g, masked, 1) >= 0) {
             family = RWS_KERNEL_WAVE_ROW;
         } else if (few_rows && wline >= 2048) {
@@ -369,7 +371,7 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
         // the masked forms exist for wave_row, register-only block_onepass
         // and two_pass; long rows with few rows go to two_pass
         if (is_splitk(family)) family = RWS_KERNEL_TWO_PASS;
-        if (family == RWS_KERNEL_BLOCK_ONEPASS && pick_onepass(wline, rows, cus, true, g.a128) < 0)
+        if (family == RWS_KERNEL_BLOCK_ONEPASS && pick_onepass(wline, rows, cus, true, g.a128, dtype) < 0)
             family = RWS_KERNEL_TWO_PASS;
     }
     if (masked && is_splitk(family))
@@ -395,11 +397,12 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
             break;
         }
         case RWS_KERNEL_BLOCK_ONEPASS: {
-            p->variant = pick_onepass(wline, rows, cus, masked, g.a128);
+            p->variant = pick_onepass(wline, rows, cus, masked, g.a128, dtype);
             if (p->variant < 0)
                 return fail(RWS_ERR_UNSUPPORTED_SHAPE,
                             "block_onepass holds at most 16384 granules (16 bytes) per row window "
-                            "on line-aligned rows, 6144 otherwise");
+                            "on line-aligned rows, 8192 otherwise (6144 for the masked 16-bit "
+                            "form)");
             p->max_rows_per_launch = block_rows_per_launch(rws::kOnepass[p->variant].block);
             p->lgrun = xcd_run_lg(g);
             break;

@@ -13,8 +13,13 @@ const int kNumOnepass = sizeof(kOnepass) / sizeof(kOnepass[0]);
 
 template <int DT, bool AL, int B, int KR, int KL>
 static hipError_t go(const Launch& L) {
-    hipLaunchKernelGGL((k_block_onepass<DT, AL, B, KR, KL>), dim3((unsigned)L.rows), dim3(B), 0,
-                       L.stream, L.in, L.out, L.rows, L.cols, (int)L.same_phase, L.lgrun, NoPre());
+    if constexpr (KR >= 8 && DT != kF32)
+        hipLaunchKernelGGL((k_block_onepass_raw<DT, AL, B, KR, KL>), dim3((unsigned)L.rows), dim3(B),
+                           0, L.stream, L.in, L.out, L.rows, L.cols, (int)L.same_phase, L.lgrun);
+    else
+        hipLaunchKernelGGL((k_block_onepass<DT, AL, B, KR, KL>), dim3((unsigned)L.rows), dim3(B), 0,
+                           L.stream, L.in, L.out, L.rows, L.cols, (int)L.same_phase, L.lgrun,
+                           NoPre());
     return hipGetLastError();
 }
 

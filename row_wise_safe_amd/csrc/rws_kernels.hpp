@@ -254,6 +254,123 @@ __global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict_
 }
 
 // ===========================================================================
+// block_onepass for 16-bit rows with 8 register granules per thread: the row
+// stays in registers as raw granules (slots outside the row set to -inf)
+// and is widened again for the sum and for the store, so exp is evaluated
+// twice per element.  The widened form needs more than the 128 VGPRs a
+// 1024-thread workgroup has and spills (40 bytes per lane on line-aligned
+// rows, 172 otherwise); this one fits.  MI355X, inputs in HBM: bf16
+// [16384,50257] 625 us against 1132 widened (and 788 for two_pass); fp16
+// [8192,65536] 390 against 403.  At 6 granules the widened form fits and
+// stays faster (fp16 [8192,49000] 294 us against 303).
+// ===========================================================================
+template <int DT, bool ALIGNED, int BLOCK, int KR, int KL>
+__global__ __launch_bounds__(BLOCK) void k_block_onepass_raw(const void* __restrict__ in,
+                                                             void* __restrict__ out, int64_t rows,
+                                                             int cols, int same_phase, int lgrun) {
+    static_assert(Elem<DT>::SIZE == 2, "raw rows are for 16-bit dtypes");
+    constexpr int VEC = Elem<DT>::VEC;
+    constexpr int W = BLOCK / 64;
+    __shared__ float red_max[W];
+    __shared__ float red_sum[W];
+    __shared__ u32x4 park[KL > 0 ? KL : 1][KL > 0 ? BLOCK : 1];
+    const int t = threadIdx.x;
+    const int64_t row = xcd_run(blockIdx.x, gridDim.x, lgrun);
+    const char* tbeg = (const char*)in;
+    const char* tend = tensor_end<DT>(in, rows, cols);
+    const RowWin<DT, ALIGNED> w(in, out, row, cols);
+
+    u32x4 raw[KR];
+#pragma unroll
+    for (int i = 0; i < KR; ++i) raw[i] = w.fetch(t + BLOCK * i, tbeg, tend);
+    u32x4 rawl[KL > 0 ? KL : 1];
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+        const int k = t + BLOCK * (KR + j);
+        if (k < w.ngran) rawl[j] = w.fetch(k, tbeg, tend);
+    }
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+        const int k = t + BLOCK * i;
+        if (!ALIGNED && k < w.ngran && !w.interior(k)) raw[i] = w.mask_raw(k, raw[i], tbeg, tend);
+    }
+
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+        if (t + BLOCK * i < w.ngran) {
+            float f[VEC];
+            Elem<DT>::widen(raw[i], f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) mx = vmax(mx, f[e]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+        const int k = t + BLOCK * (KR + j);
+        if (k < w.ngran) {
+            float f[VEC];
+            w.widen(k, rawl[j], f, tbeg, tend);
+            // partial granules are parked with -inf outside the row
+            park[j][t] = w.interior(k) ? rawl[j] : Elem<DT>::narrow(f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) mx = vmax(mx, f[e]);
+        }
+    }
+    mx = block_reduce<W, OpMax>(mx, red_max);
+
+    const RowExp er(mx);
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+        if (t + BLOCK * i < w.ngran) {
+            float f[VEC];
+            Elem<DT>::widen(raw[i], f);
+            er.apply(f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) s += f[e];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+        if (t + BLOCK * (KR + j) < w.ngran) {
+            float f[VEC];
+            Elem<DT>::widen(park[j][t], f);
+            er.apply(f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) s += f[e];
+        }
+    }
+    s = block_reduce<W, OpSum>(s, red_sum);
+    const float r = __builtin_amdgcn_rcpf(s);
+
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+        const int k = t + BLOCK * i;
+        if (k < w.ngran) {
+            float f[VEC];
+            Elem<DT>::widen(raw[i], f);
+            er.apply(f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) f[e] *= r;
+            w.store(k, f, same_phase != 0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+        const int k = t + BLOCK * (KR + j);
+        if (k < w.ngran) {
+            float f[VEC];
+            Elem<DT>::widen(park[j][t], f);
+            er.apply(f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) f[e] *= r;
+            w.store(k, f, same_phase != 0);
+        }
+    }
+}
+
+// ===========================================================================
 // Running (m, d) of one thread over a batch of N values (-inf entries add 0):
 //   m' = max(m, max batch);  d' = d e^(m - m') + sum e^(x - m')
 // (DCU case-study page, section 4.3; CUDA safe-online-softmax page, section 1,

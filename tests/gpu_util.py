@@ -61,6 +61,6 @@ def supports(kernel: str, cols: int, dtype: str, aligned: bool) -> bool:
     if kernel == "wave_row":
         return w <= 512
     if kernel == "block_onepass":
-        # rows that are not line-aligned: at most 6 register granules per thread
-        return w <= (16384 if line else 6144)
+        # rows that are not line-aligned: no LDS parking
+        return w <= (16384 if line else 8192)
     return True

@@ -134,3 +134,23 @@ def test_every_bwd_block_shape(dtype):
         dx = rws.softmax_backward(y, dy)
         torch.cuda.synchronize()
         check_backward(dx.double().cpu().numpy(), ys, gs, dtype, f"{desc} rows={rows} cols={cols}")
+
+
+# Long 16-bit rows at 8 register granules per thread take the raw-granule
+# form (k_block_onepass_raw), with and without LDS parking, on line-aligned
+# rows and on rows that are not; a row of -inf except one entry, and a ragged
+# tail, are in every case.
+@pytest.mark.parametrize("dtype,cols", [("bf16", 50257), ("f16", 49153), ("f16", 65536),
+                                        ("bf16", 65536), ("f16", 128256), ("bf16", 120000)])
+def test_raw_long_rows(dtype, cols):
+    rows = 6
+    g = np.random.Generator(np.random.PCG64(cols))
+    x64 = g.normal(0.0, 3.0, (rows, cols))
+    x64[2, :] = -np.inf
+    x64[2, cols // 3] = 1.0
+    x, xs = to_device(x64, dtype)
+    desc = rws.softmax_describe_launch(rows, cols, CODE[dtype], x.data_ptr(), x.data_ptr(),
+                                       rws.KERNEL_IDS["block_onepass"])
+    assert "KR=8" in desc, desc
+    y = run(x, torch.empty_like(x), "block_onepass")
+    check(y, oracle.safe_softmax(xs), dtype, f"{desc} cols={cols}")
