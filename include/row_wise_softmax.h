@@ -188,8 +188,12 @@ int softmax_bwd(const void *y, const void *dy, void *dx, int64_t rows, int64_t c
 /*
  * softmax_bwd_kernel -- as softmax_bwd with a forced kernel: RWS_KERNEL_AUTO,
  * RWS_KERNEL_WAVE_ROW (row in one wave's registers), RWS_KERNEL_BLOCK_ONEPASS
- * (row in one workgroup's registers) or RWS_KERNEL_TWO_PASS (any length; y
- * and dy are read twice).  Other ids: RWS_ERR_INVALID_ARG.
+ * (row in one workgroup's registers), RWS_KERNEL_TWO_PASS (any length; y
+ * and dy are read twice) or RWS_KERNEL_SPLITK_ORDERED (several workgroups
+ * per row in one launch: chunk dot products published as epoch-tagged
+ * words, as for softmax_fwd; the dispatcher's choice for few long rows; uses
+ * the per-stream tag words that the forward's ordered form allocates on
+ * first use).  Other ids: RWS_ERR_INVALID_ARG.
  */
 int softmax_bwd_kernel(const void *y, const void *dy, void *dx, int64_t rows, int64_t cols,
                        int dtype, void *stream, int kernel_id);
@@ -234,9 +238,12 @@ int rmsnorm_fwd(const void *in, void *out, int64_t rows, int64_t cols, int dtype
  * layernorm_fwd_kernel, rmsnorm_fwd_kernel -- as above with a forced kernel:
  * RWS_KERNEL_AUTO, RWS_KERNEL_WAVE_ROW (row in one lane group's registers,
  * window up to 512 granules), RWS_KERNEL_BLOCK_ONEPASS (row in one
- * workgroup's registers, up to 4096 granules) or RWS_KERNEL_TWO_PASS (any
- * length; the row is read twice).  Other ids: RWS_ERR_INVALID_ARG; a row too
- * long for the forced kernel: RWS_ERR_UNSUPPORTED_SHAPE.
+ * workgroup's registers, up to 4096 granules), RWS_KERNEL_TWO_PASS (any
+ * length; the row is read twice) or RWS_KERNEL_SPLITK_ORDERED (several
+ * workgroups per row in one launch, chunk statistics published as
+ * epoch-tagged words; the dispatcher's choice for few long rows).  Other
+ * ids: RWS_ERR_INVALID_ARG; a row too long for the forced kernel:
+ * RWS_ERR_UNSUPPORTED_SHAPE.
  */
 int layernorm_fwd_kernel(const void *in, void *out, int64_t rows, int64_t cols, int dtype,
                          float eps, const void *weight, const void *bias, float *mean, float *rstd,
@@ -273,9 +280,9 @@ int softmax_describe_launch_masked(int64_t rows, int64_t cols, int dtype, const 
 /*
  * softmax_bwd_describe_launch -- the same for the launch
  * softmax_bwd_kernel(kernel_id) would make with these y and dx pointers
- * (bwd_wave, bwd_block or bwd_stream, with its shape).  kernel_id:
- * RWS_KERNEL_AUTO, _WAVE_ROW, _BLOCK_ONEPASS or _TWO_PASS.  Performs no GPU
- * work.
+ * (bwd_wave, bwd_block, bwd_stream or bwd_ordered, with its shape).
+ * kernel_id: RWS_KERNEL_AUTO, _WAVE_ROW, _BLOCK_ONEPASS, _TWO_PASS or
+ * _SPLITK_ORDERED.  Performs no GPU work.
  */
 int softmax_bwd_describe_launch(int64_t rows, int64_t cols, int dtype, const void *y,
                                 const void *dx, int kernel_id, char *buf, int64_t buflen);
@@ -283,10 +290,11 @@ int softmax_bwd_describe_launch(int64_t rows, int64_t cols, int dtype, const voi
 /*
  * norm_describe_launch -- the same for the launch layernorm_fwd_kernel /
  * rmsnorm_fwd_kernel(kernel_id) would make on these tensors (both use the
- * same choice: norm_wave, norm_block or norm_stream, with its shape).
+ * same choice: norm_wave, norm_block, norm_stream or norm_ordered, with its
+ * shape).
  * affine: nonzero when a weight and/or bias is passed (it can change the
  * lane group).  kernel_id: RWS_KERNEL_AUTO, _WAVE_ROW, _BLOCK_ONEPASS or
- * _TWO_PASS.  Performs no GPU work.
+ * _TWO_PASS or _SPLITK_ORDERED.  Performs no GPU work.
  */
 int norm_describe_launch(int64_t rows, int64_t cols, int dtype, const void *in, const void *out,
                          int affine, int kernel_id, char *buf, int64_t buflen);

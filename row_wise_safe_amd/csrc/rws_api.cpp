@@ -131,6 +131,23 @@ int wave_row_wa(const rws::WaveRowVariant& v) { return v.G * 16 >= 128 ? 128 : 1
 // 37.3 against 37.6.  Not used for line-aligned rows ([8192,4096]: 23.0
 // against 22.6), two_pass (no change) or the normalisations ([8192,4097]
 // with 576 threads: 33.8 against 32.7).
+// Chunks per row of the backward's and the normalisations' ordered split-k
+// (chunks of 256 x 4 granules), and whether a call takes it: at most one row
+// per two CUs (one workgroup per row would leave most of the chip idle), of
+// at least 2048 granules.  MI355X, fp16, inputs in HBM, one workgroup per
+// row -> ordered: [16,1048576] backward 143 -> 25.1 us, LayerNorm 106 ->
+// 18.0, RMSNorm 75 -> 14.3; [64,262144] 42.4 -> 25.2, 31.2 -> 17.6, 22.6 ->
+// 13.7; but [256,65536] 23.3 -> 24.9, 15.7 -> 17.5, 13.0 -> 13.6 (256 rows
+// fill the chip one workgroup per row).
+int ordered_chunks(int64_t wline, int block, int kc) {
+    const int64_t span = (int64_t)block * kc;
+    return (int)((wline + span - 1) / span);
+}
+
+bool few_long_rows(int64_t rows, int64_t wline, int cus) {
+    return 2 * rows <= cus && wline >= 2048;
+}
+
 int xcd_run_lg(const Geometry& g) {
     if (g.a128 || g.row_bytes <= 0) return 0;
     int lg = 0;
@@ -735,8 +752,9 @@ int softmax_fwd_masked(const void* in, void* out, int64_t rows, int64_t cols, in
 // Softmax backward: family 1 (wave, registers), 2 (block, registers) or 3
 // (stream, any length), chosen like the forward kernels by the row window.
 struct BwdPlan {
-    int family = 0;  // 1 wave, 2 block, 3 stream
+    int family = 0;  // 1 wave, 2 block, 3 stream, RWS_KERNEL_SPLITK_ORDERED
     int variant = 0;
+    int P = 1;       // ordered split-k: chunks per row
     bool aligned = false;
     bool same_phase = false;
     int lgrun = 0;
@@ -748,9 +766,10 @@ static int plan_bwd(int64_t rows, int64_t cols, int dtype, const void* y, const 
     (void)rows;
     const Geometry g = geometry(cols, dtype, y, dx);
     const int64_t wline = window_granules(g, 128);
-    int family = kernel_id == RWS_KERNEL_AUTO ? 0 : kernel_id;  // 1 wave, 2 block, 3 stream
+    int family = kernel_id == RWS_KERNEL_AUTO ? 0 : kernel_id;  // 1 wave, 2 block, 3 stream, 6
     int variant = -1;
     bool aligned = g.a128;
+    const int cus = device_info().cus;
     // Forms, by sweeps on MI355X with inputs in HBM: one wave per row while a
     // lane group holds the row at one granule per lane, else one workgroup
     // per row (fp16 [32768,1000]: 36.3 us with 192x1 against 76.1 us for one
@@ -793,8 +812,20 @@ static int plan_bwd(int64_t rows, int64_t cols, int dtype, const void* y, const 
     };
     if (family == 0) {
         if (pick_wave(1) >= 0) family = 1;
+        else if (few_long_rows(rows, wline, cus)) family = RWS_KERNEL_SPLITK_ORDERED;
         else if (pick_block() >= 0) family = 2;
         else family = 3;
+    }
+    if (family == RWS_KERNEL_SPLITK_ORDERED) {
+        bp->family = family;
+        bp->variant = 0;
+        bp->P = ordered_chunks(wline, rws::kBwdOrderedBlock, rws::kBwdOrderedKc);
+        bp->aligned = aligned;
+        bp->same_phase = g.same_phase;
+        bp->lgrun = 0;
+        // at most 2^23 workgroups per launch, both stages counted
+        bp->max_rows = std::max<int64_t>(1, ((int64_t)1 << 23) / (2LL * bp->P));
+        return RWS_OK;
     }
     if (family == 1) {
         variant = pick_wave(1 << 30);
@@ -827,8 +858,10 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
                        int dtype, void* stream, int kernel_id) {
     g_last_error.clear();
     if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
-        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS)
-        return fail(RWS_ERR_INVALID_ARG, "backward kernels: auto, wave_row, block_onepass, two_pass");
+        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS &&
+        kernel_id != RWS_KERNEL_SPLITK_ORDERED)
+        return fail(RWS_ERR_INVALID_ARG,
+                    "backward kernels: auto, wave_row, block_onepass, two_pass, splitk_ordered");
     int st = check_args(y, dx, rows, cols, dtype, RWS_KERNEL_AUTO);
     if (st != RWS_OK || rows == 0 || cols == 0) return st;
     if (!dy) return fail(RWS_ERR_INVALID_ARG, "NULL dy with a non-empty tensor");
@@ -839,6 +872,17 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
     if (st != RWS_OK) return st;
     const int family = bp.family, variant = bp.variant;
     const int64_t max_rows = bp.max_rows;
+    // ordered split-k: keep the tag words locked until the launches are enqueued
+    std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
+    uint64_t* tags = nullptr;
+    unsigned epoch = 0;
+    if (family == RWS_KERNEL_SPLITK_ORDERED) {
+        ws_lock.lock();
+        const int64_t launches = (rows + max_rows - 1) / max_rows;
+        st = get_tag_workspace((hipStream_t)stream, 2 * std::min(rows, max_rows) * bp.P, launches,
+                               &tags, &epoch);
+        if (st != RWS_OK) return st;
+    }
     const int64_t row_bytes = cols * elem_size(dtype);
     for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
         rws::BwdLaunch B;
@@ -853,7 +897,10 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
         B.dy_vec = (((uintptr_t)dy - (uintptr_t)y) % 16) == 0;
         B.lgrun = bp.lgrun;
         B.stream = (hipStream_t)stream;
-        const hipError_t e = rws::launch_bwd(B, family, variant);
+        const hipError_t e =
+            family == RWS_KERNEL_SPLITK_ORDERED
+                ? rws::launch_bwd_ordered(B, bp.P, tags, epoch + (unsigned)(r0 / max_rows))
+                : rws::launch_bwd(B, family, variant);
         if (e != hipSuccess)
             return fail(RWS_ERR_HIP, std::string("backward launch: ") + hipGetErrorString(e));
     }
@@ -868,8 +915,9 @@ int softmax_bwd(const void* y, const void* dy, void* dx, int64_t rows, int64_t c
 // Row normalisations: family 1 (norm_wave), 2 (norm_block) or 3
 // (norm_stream), chosen by the row window like the softmax backward.
 struct NormPlan {
-    int family = 0;
+    int family = 0;  // 1 wave, 2 block, 3 stream, RWS_KERNEL_SPLITK_ORDERED
     int variant = 0;
+    int P = 1;       // ordered split-k: chunks per row
     bool aligned = false;
     bool same_phase = false;
     int lgrun = 0;
@@ -938,8 +986,20 @@ static int plan_norm(int64_t rows, int64_t cols, int dtype, const void* in, cons
     int family = kernel_id == RWS_KERNEL_AUTO ? 0 : kernel_id;
     if (family == 0) {
         if (pick_wave(1) >= 0) family = 1;
+        else if (few_long_rows(rows, wline, device_info().cus)) family = RWS_KERNEL_SPLITK_ORDERED;
         else if (pick_block() >= 0) family = 2;
         else family = 3;
+    }
+    if (family == RWS_KERNEL_SPLITK_ORDERED) {
+        np->family = family;
+        np->variant = 0;
+        np->P = ordered_chunks(wline, rws::kNormOrderedBlock, rws::kNormOrderedKc);
+        np->aligned = g.a128;
+        np->same_phase = g.same_phase;
+        np->lgrun = 0;
+        // at most 2^23 workgroups per launch, both stages counted
+        np->max_rows = std::max<int64_t>(1, ((int64_t)1 << 23) / (2LL * np->P));
+        return RWS_OK;
     }
     int variant = -1;
     bool aligned = g.a128;
@@ -977,8 +1037,10 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
                     void* stream, int kernel_id) {
     g_last_error.clear();
     if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
-        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS)
-        return fail(RWS_ERR_INVALID_ARG, "normalisation kernels: auto, wave_row, block_onepass, two_pass");
+        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS &&
+        kernel_id != RWS_KERNEL_SPLITK_ORDERED)
+        return fail(RWS_ERR_INVALID_ARG,
+                    "normalisation kernels: auto, wave_row, block_onepass, two_pass, splitk_ordered");
     if (!(eps >= 0.0f) || !std::isfinite(eps))
         return fail(RWS_ERR_INVALID_ARG, "eps must be finite and >= 0");
     int st = check_args(in, out, rows, cols, dtype, RWS_KERNEL_AUTO);
@@ -993,6 +1055,17 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
     if (st != RWS_OK) return st;
     const int family = np.family, variant = np.variant;
     const int64_t max_rows = np.max_rows;
+    // ordered split-k: keep the tag words locked until the launches are enqueued
+    std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
+    uint64_t* tags = nullptr;
+    unsigned epoch = 0;
+    if (family == RWS_KERNEL_SPLITK_ORDERED) {
+        ws_lock.lock();
+        const int64_t launches = (rows + max_rows - 1) / max_rows;
+        st = get_tag_workspace((hipStream_t)stream, 2 * std::min(rows, max_rows) * np.P, launches,
+                               &tags, &epoch);
+        if (st != RWS_OK) return st;
+    }
     const int64_t row_bytes = cols * es;
     for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
         rws::NormLaunch L;
@@ -1017,8 +1090,11 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
         L.args.eps = eps;
         L.args.n = (float)cols;
         L.stream = (hipStream_t)stream;
-        const hipError_t e = family == 1 ? rws::launch_norm_wave(L, variant)
-                                         : rws::launch_norm_block(L, family, variant);
+        const hipError_t e =
+            family == 1 ? rws::launch_norm_wave(L, variant)
+            : family == RWS_KERNEL_SPLITK_ORDERED
+                ? rws::launch_norm_ordered(L, np.P, tags, epoch + (unsigned)(r0 / max_rows))
+                : rws::launch_norm_block(L, family, variant);
         if (e != hipSuccess)
             return fail(RWS_ERR_HIP, std::string("normalisation launch: ") + hipGetErrorString(e));
     }
@@ -1160,8 +1236,10 @@ int softmax_bwd_describe_launch(int64_t rows, int64_t cols, int dtype, const voi
     if (!buf || buflen <= 0) return fail(RWS_ERR_INVALID_ARG, "no output buffer");
     buf[0] = 0;
     if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
-        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS)
-        return fail(RWS_ERR_INVALID_ARG, "backward kernels: auto, wave_row, block_onepass, two_pass");
+        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS &&
+        kernel_id != RWS_KERNEL_SPLITK_ORDERED)
+        return fail(RWS_ERR_INVALID_ARG,
+                    "backward kernels: auto, wave_row, block_onepass, two_pass, splitk_ordered");
     if (dtype != RWS_F32 && dtype != RWS_F16 && dtype != RWS_BF16)
         return fail(RWS_ERR_UNSUPPORTED_DTYPE, "dtype must be RWS_F32, RWS_F16 or RWS_BF16");
     if (rows < 0 || cols < 0) return fail(RWS_ERR_INVALID_ARG, "rows and cols must be >= 0");
@@ -1175,7 +1253,12 @@ int softmax_bwd_describe_launch(int64_t rows, int64_t cols, int dtype, const voi
     if (st != RWS_OK) return st;
     const char* al = bp.aligned ? "aligned" : (bp.same_phase ? "unaligned" : "unaligned,split-phase");
     const int64_t r = std::min(rows, bp.max_rows);
-    if (bp.family == 1) {
+    if (bp.family == RWS_KERNEL_SPLITK_ORDERED) {
+        std::snprintf(buf, (size_t)buflen,
+                      "bwd_ordered<%s,%s,B=%d,KC=%d> P=%d grid=%lld (2 stages) block=%d",
+                      dtype_name(dtype), al, rws::kBwdOrderedBlock, rws::kBwdOrderedKc, bp.P,
+                      (long long)(2 * r * bp.P), rws::kBwdOrderedBlock);
+    } else if (bp.family == 1) {
         const rws::WaveRowVariant& v = rws::kBwdWave[bp.variant];
         std::snprintf(buf, (size_t)buflen, "bwd_wave<%s,%s,G=%d,K=%d,U=%d> grid=%lld block=%d",
                       dtype_name(dtype), al, v.G, v.K, v.U, (long long)rws::wave_row_grid(v, r),
@@ -1198,8 +1281,10 @@ int norm_describe_launch(int64_t rows, int64_t cols, int dtype, const void* in, 
     if (!buf || buflen <= 0) return fail(RWS_ERR_INVALID_ARG, "no output buffer");
     buf[0] = 0;
     if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
-        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS)
-        return fail(RWS_ERR_INVALID_ARG, "normalisation kernels: auto, wave_row, block_onepass, two_pass");
+        kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS &&
+        kernel_id != RWS_KERNEL_SPLITK_ORDERED)
+        return fail(RWS_ERR_INVALID_ARG,
+                    "normalisation kernels: auto, wave_row, block_onepass, two_pass, splitk_ordered");
     if (dtype != RWS_F32 && dtype != RWS_F16 && dtype != RWS_BF16)
         return fail(RWS_ERR_UNSUPPORTED_DTYPE, "dtype must be RWS_F32, RWS_F16 or RWS_BF16");
     if (rows < 0 || cols < 0) return fail(RWS_ERR_INVALID_ARG, "rows and cols must be >= 0");
@@ -1214,7 +1299,12 @@ int norm_describe_launch(int64_t rows, int64_t cols, int dtype, const void* in, 
     const char* al = np.aligned ? "aligned" : (np.same_phase ? "unaligned" : "unaligned,split-phase");
     const int64_t r = std::min(rows, np.max_rows);
     const long long wline = (long long)window_granules(geometry(cols, dtype, in, out), 128);
-    if (np.family == 1) {
+    if (np.family == RWS_KERNEL_SPLITK_ORDERED) {
+        std::snprintf(buf, (size_t)buflen,
+                      "norm_ordered<%s,%s,B=%d,KC=%d> P=%d grid=%lld (2 stages) block=%d",
+                      dtype_name(dtype), al, rws::kNormOrderedBlock, rws::kNormOrderedKc, np.P,
+                      (long long)(2 * r * np.P), rws::kNormOrderedBlock);
+    } else if (np.family == 1) {
         const rws::WaveRowVariant& v = rws::kNormWave[np.variant];
         std::snprintf(buf, (size_t)buflen, "norm_wave<%s,%s,G=%d,K=%d,U=%d> grid=%lld block=%d",
                       dtype_name(dtype), al, v.G, v.K, v.U, (long long)rws::wave_row_grid(v, r),

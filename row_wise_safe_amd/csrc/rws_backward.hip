@@ -9,6 +9,9 @@
 //   bwd_block   one workgroup per row, registers
 //   bwd_stream  one workgroup per row, any length: pass 1 the dot product,
 //               pass 2 re-reads y and dy (L2 / last-level cache) and writes
+//   bwd_ordered few long rows: split-k in one launch (rws_ordered.hpp):
+//               stage 1 publishes each chunk's partial dot product, stage 2
+//               sums the row's partials, re-reads its chunk and writes
 //
 // y's row window (rws_device.hpp) drives all three tensors: dy's granule k
 // is at the same offset from y's plus the constant dy - y (both have pitch
@@ -17,6 +20,7 @@
 // the forward output.  No byte outside a tensor is read or written.
 #include "rws_kernels.hpp"
 #include "rws_launch.hpp"
+#include "rws_ordered.hpp"
 
 namespace rws {
 
@@ -234,6 +238,82 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_stream(const void* __restrict__ y
 // ---------------------------------------------------------------------------
 // variants and launchers
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// bwd_ordered: BLOCK threads x KC granules per chunk, P chunks per row.  The
+// dot product is summed chunk by chunk in a fixed order (partials 0..P-1
+// folded per thread, then the block reduction), so the result is the same
+// on every call.  Stage 1 loads cached (stage 2 reads the chunk again),
+// stage 2 non-temporally.
+template <int DT, bool ALIGNED, int BLOCK, int KC>
+__global__ __launch_bounds__(BLOCK) void k_bwd_ordered(const void* __restrict__ y,
+                                                       const void* __restrict__ dy,
+                                                       void* __restrict__ dx, int64_t rows,
+                                                       int cols, int P, uint64_t* __restrict__ tags,
+                                                       unsigned epoch, int dy_vec, int same_phase) {
+    constexpr int VEC = Elem<DT>::VEC;
+    constexpr int W = BLOCK / 64;
+    using Win = RowWin<DT, ALIGNED>;
+    __shared__ float red[W];
+    const int t = threadIdx.x;
+    const OrderedSlot slot = ordered_slot(blockIdx.x, rows, P);
+    const char* tbeg = (const char*)y;
+    const char* tend = tensor_end<DT>(y, rows, cols);
+    const Second<DT, Win> s2{(const char*)dy, tensor_end<DT>(dy, rows, cols),
+                             (int64_t)((const char*)dy - (const char*)y), dy_vec != 0};
+    const Win w(y, dx, slot.row, cols);
+    const int kbase = slot.chunk * (BLOCK * KC) + t;
+    uint64_t* row_tags = tags + 2 * slot.row * P;
+
+    u32x4 ry[KC], rg[KC];
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        const int k = kbase + BLOCK * i;
+        if (slot.merge_stage) {
+            ry[i] = w.template fetch<true>(k, tbeg, tend);
+            rg[i] = s2.template fetch<true>(w, k);
+        } else {
+            ry[i] = w.template fetch<false>(k, tbeg, tend);
+            rg[i] = s2.template fetch<false>(w, k);
+        }
+    }
+
+    if (!slot.merge_stage) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+            const int k = kbase + BLOCK * i;
+            if (k < w.ngran) {
+                float vy[VEC], vg[VEC];
+                widen_zero<DT>(w, k, ry[i], vy, tbeg, tend);
+                s2.widen(w, k, rg[i], vg);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) dot = __builtin_fmaf(vy[e], vg[e], dot);
+            }
+        }
+        dot = block_reduce<W, OpSum>(dot, red);
+        if (t == 0) publish_word(row_tags + 2 * slot.chunk, epoch, dot);
+        return;
+    }
+
+    float dot = 0.0f;
+    int late = 0;
+    for (int j = t; j < P; j += BLOCK) dot += poll_word(row_tags + 2 * j, epoch, late);
+    dot = block_reduce<W, OpSum>(dot, red);
+    if (__syncthreads_or(late) != 0) dot = __builtin_nanf("");
+#pragma unroll
+    for (int i = 0; i < KC; ++i) {
+        const int k = kbase + BLOCK * i;
+        if (k < w.ngran) {
+            float vy[VEC], vg[VEC], o[VEC];
+            widen_zero<DT>(w, k, ry[i], vy, tbeg, tend);
+            s2.widen(w, k, rg[i], vg);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) o[e] = vy[e] * (vg[e] - dot);
+            w.store(k, o, same_phase != 0);
+        }
+    }
+}
+
 #define RWS_BWD_WAVE_VARIANTS(X) \
     X(4, 1, 1)                   \
     X(8, 1, 1)                   \
@@ -295,6 +375,24 @@ static hipError_t bs(const BwdLaunch& B) {
                        B.stream, B.y, B.dy, B.dx, B.rows, B.cols, (int)B.dy_vec,
                        (int)B.same_phase, B.lgrun);
     return hipGetLastError();
+}
+
+template <int DT, bool AL>
+static hipError_t bo(const BwdLaunch& B, int P, uint64_t* tags, unsigned epoch) {
+    hipLaunchKernelGGL((k_bwd_ordered<DT, AL, kBwdOrderedBlock, kBwdOrderedKc>),
+                       dim3((unsigned)(2 * B.rows * P)), dim3(kBwdOrderedBlock), 0, B.stream, B.y,
+                       B.dy, B.dx, B.rows, B.cols, P, tags, epoch, (int)B.dy_vec,
+                       (int)B.same_phase);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_ordered(const BwdLaunch& B, int P, uint64_t* tags, unsigned epoch) {
+    switch (B.dtype) {
+        case kF32: return B.aligned ? bo<kF32, true>(B, P, tags, epoch) : bo<kF32, false>(B, P, tags, epoch);
+        case kF16: return B.aligned ? bo<kF16, true>(B, P, tags, epoch) : bo<kF16, false>(B, P, tags, epoch);
+        case kBF16: return B.aligned ? bo<kBF16, true>(B, P, tags, epoch) : bo<kBF16, false>(B, P, tags, epoch);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd(const BwdLaunch& B, int family, int variant) {

@@ -110,6 +110,12 @@ extern const TwoPassVariant kBwdStream[];  // (threads, granules per thread per 
 extern const int kNumBwdStream;
 // family: 1 wave (kBwdWave), 2 block (kBwdBlock), 3 stream (kBwdStream)
 hipError_t launch_bwd(const BwdLaunch& B, int family, int variant);
+// Few long rows: split-k in one launch, chunks of kBwdOrderedBlock x
+// kBwdOrderedKc granules, P chunks per row; tags holds 2*rows*P epoch-tagged
+// words, epoch is unique to this launch on that buffer.
+constexpr int kBwdOrderedBlock = 256;
+constexpr int kBwdOrderedKc = 4;
+hipError_t launch_bwd_ordered(const BwdLaunch& B, int P, uint64_t* tags, unsigned epoch);
 // Row normalisations (rws_norm.hpp).
 constexpr int kLayerNorm = 0;
 constexpr int kRmsNorm = 1;
@@ -144,6 +150,10 @@ extern const int kNumNormStream;
 hipError_t launch_norm_wave(const NormLaunch& L, int variant);
 // family 2: block (kNormBlock), 3: stream (kNormStream)
 hipError_t launch_norm_block(const NormLaunch& L, int family, int variant);
+// Few long rows: split-k in one launch (as launch_bwd_ordered).
+constexpr int kNormOrderedBlock = 256;
+constexpr int kNormOrderedKc = 4;
+hipError_t launch_norm_ordered(const NormLaunch& L, int P, uint64_t* tags, unsigned epoch);
 // n16 granules of 16 bytes.
 hipError_t launch_copy16(const void* in, void* out, int64_t n16, hipStream_t stream);
 

@@ -17,6 +17,10 @@
 //                them with Chan's pairwise rule -- the normalisation
 //                counterpart of the (m, d) merge; pass 2 re-reads the row and
 //                writes
+//   norm_ordered few long rows: split-k in one launch (rws_ordered.hpp):
+//                stage 1 publishes each chunk's (mean, squared deviations)
+//                (RMSNorm: sum of squares), stage 2 merges the row's
+//                partials with the same rule, re-reads its chunk and writes
 //
 // The weight and bias vectors (cols entries of the tensor's dtype, optional)
 // are read on each row's granule grid: one 128-bit load per interior granule
@@ -29,6 +33,7 @@
 
 #include "rws_kernels.hpp"
 #include "rws_launch.hpp"
+#include "rws_ordered.hpp"
 
 namespace rws {
 
@@ -431,6 +436,106 @@ __global__ __launch_bounds__(BLOCK) void k_norm_stream(const void* __restrict__ 
     if (t == 0) {
         if (A.mean) A.mean[row] = mu;
         if (A.rstd) A.rstd[row] = rstd;
+    }
+}
+
+// ===========================================================================
+// norm_ordered: BLOCK threads x KC granules per chunk, P chunks per row
+// (workgroups: ordered_slot).  A chunk's count of row elements follows from
+// its position, so LayerNorm publishes two words per chunk (mean, sum of
+// squared deviations about it) and RMSNorm one (sum of squares).  Stage 2
+// folds the partials in chunk order and merges across the workgroup with
+// moments_block, so the statistics are the same on every call.  Without
+// weight and bias the kernels are compiled for six waves per SIMD (left
+// alone, 125-160 VGPRs on rows that are not line-aligned; capped, 64-78 and
+// no spills; with weight and bias the cap spilled).
+// ===========================================================================
+template <class Win>
+__device__ inline float chunk_count(const Win& w, int chunk, int span) {
+    const int64_t g0 = (int64_t)chunk * span;
+    const int64_t lo = g0 * Win::VEC - w.lead;
+    const int64_t hi = (g0 + span) * Win::VEC - w.lead;
+    const int64_t n = (hi < w.cols ? hi : w.cols) - (lo > 0 ? lo : 0);
+    return n > 0 ? (float)n : 0.0f;
+}
+
+template <int DT, bool ALIGNED, int BLOCK, int KC, int MODE, bool AFF>
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(AFF ? 1 : 6))) void k_norm_ordered(const void* __restrict__ in,
+                                                        void* __restrict__ out, int64_t rows,
+                                                        int cols, NormArgs A, int P,
+                                                        uint64_t* __restrict__ tags,
+                                                        unsigned epoch, int same_phase) {
+    constexpr int VEC = Elem<DT>::VEC;
+    constexpr int W = BLOCK / 64;
+    constexpr int N = KC * VEC;
+    using Win = RowWin<DT, ALIGNED>;
+    __shared__ float sn[W];
+    __shared__ float sm[W];
+    __shared__ float sq[W];
+    const int t = threadIdx.x;
+    const OrderedSlot slot = ordered_slot(blockIdx.x, rows, P);
+    const char* tbeg = (const char*)in;
+    const char* tend = tensor_end<DT>(in, rows, cols);
+    const Win w(in, out, slot.row, cols);
+    const int kbase = slot.chunk * (BLOCK * KC) + t;
+    uint64_t* row_tags = tags + 2 * slot.row * P;
+
+    u32x4 raw[KC];
+#pragma unroll
+    for (int i = 0; i < KC; ++i)
+        raw[i] = slot.merge_stage ? w.template fetch<true>(kbase + BLOCK * i, tbeg, tend)
+                                  : w.template fetch<false>(kbase + BLOCK * i, tbeg, tend);
+    const ColParam<DT, Win> pw(A.w, w), pb(A.b, w);
+    u32x4 rw[AFF ? KC : 1], rb[AFF ? KC : 1];
+    if (AFF && slot.merge_stage) affine_fetch<KC>(w, kbase, BLOCK, A, pw, pb, rw, rb);
+    float v[N];
+#pragma unroll
+    for (int i = 0; i < KC; ++i) widen_zero<DT>(w, kbase + BLOCK * i, raw[i], &v[i * VEC], tbeg, tend);
+
+    if (!slot.merge_stage) {
+        if (MODE == kLayerNorm) {
+            float s = 0.0f;
+#pragma unroll
+            for (int j = 0; j < N; ++j) s += v[j];
+            s = block_reduce<W, OpSum>(s, sm);
+            const float mean = s / chunk_count(w, slot.chunk, BLOCK * KC);
+            float q = centred_squares<DT, KC>(w, kbase, BLOCK, v, mean);
+            q = block_reduce<W, OpSum>(q, sq);
+            if (t == 0) {
+                publish_word(row_tags + 2 * slot.chunk, epoch, mean);
+                publish_word(row_tags + 2 * slot.chunk + 1, epoch, q);
+            }
+        } else {
+            float q = 0.0f;
+#pragma unroll
+            for (int j = 0; j < N; ++j) q = __builtin_fmaf(v[j], v[j], q);
+            q = block_reduce<W, OpSum>(q, sq);
+            if (t == 0) publish_word(row_tags + 2 * slot.chunk, epoch, q);
+        }
+        return;
+    }
+
+    int late = 0;
+    float mu = 0.0f, q = 0.0f;
+    if (MODE == kLayerNorm) {
+        float n = 0.0f, m = 0.0f;
+        for (int j = t; j < P; j += BLOCK) {
+            const float pm = poll_word(row_tags + 2 * j, epoch, late);
+            const float pq = poll_word(row_tags + 2 * j + 1, epoch, late);
+            moments_merge(n, m, q, chunk_count(w, j, BLOCK * KC), pm, pq);
+        }
+        moments_block<W>(n, m, q, sn, sm, sq);
+        mu = m;
+    } else {
+        for (int j = t; j < P; j += BLOCK) q += poll_word(row_tags + 2 * j, epoch, late);
+        q = block_reduce<W, OpSum>(q, sq);
+    }
+    float rstd = norm_rstd(q, A);
+    if (__syncthreads_or(late) != 0) mu = rstd = __builtin_nanf("");
+    norm_store<DT, MODE, AFF, KC>(w, kbase, BLOCK, v, mu, rstd, A, same_phase != 0, &pw, &pb, rw, rb);
+    if (t == 0 && slot.chunk == 0) {
+        if (A.mean) A.mean[slot.row] = mu;
+        if (A.rstd) A.rstd[slot.row] = rstd;
     }
 }
 

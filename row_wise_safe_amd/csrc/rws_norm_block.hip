@@ -75,6 +75,33 @@ static hipError_t ns(const NormLaunch& L) {
                                 : ns_mode<DT, AL, BL, U, kRmsNorm>(L);
 }
 
+template <int DT, bool AL, int MODE, bool AFF>
+static hipError_t no(const NormLaunch& L, int P, uint64_t* tags, unsigned epoch) {
+    hipLaunchKernelGGL((k_norm_ordered<DT, AL, kNormOrderedBlock, kNormOrderedKc, MODE, AFF>),
+                       dim3((unsigned)(2 * L.rows * P)), dim3(kNormOrderedBlock), 0, L.stream, L.in,
+                       L.out, L.rows, L.cols, L.args, P, tags, epoch, (int)L.same_phase);
+    return hipGetLastError();
+}
+
+template <int DT, bool AL>
+static hipError_t no_dt(const NormLaunch& L, int P, uint64_t* tags, unsigned epoch) {
+    const bool aff = L.args.w || L.args.b;
+    if (L.mode == kLayerNorm)
+        return aff ? no<DT, AL, kLayerNorm, true>(L, P, tags, epoch)
+                   : no<DT, AL, kLayerNorm, false>(L, P, tags, epoch);
+    return aff ? no<DT, AL, kRmsNorm, true>(L, P, tags, epoch)
+               : no<DT, AL, kRmsNorm, false>(L, P, tags, epoch);
+}
+
+hipError_t launch_norm_ordered(const NormLaunch& L, int P, uint64_t* tags, unsigned epoch) {
+    switch (L.dtype) {
+        case kF32: return L.aligned ? no_dt<kF32, true>(L, P, tags, epoch) : no_dt<kF32, false>(L, P, tags, epoch);
+        case kF16: return L.aligned ? no_dt<kF16, true>(L, P, tags, epoch) : no_dt<kF16, false>(L, P, tags, epoch);
+        case kBF16: return L.aligned ? no_dt<kBF16, true>(L, P, tags, epoch) : no_dt<kBF16, false>(L, P, tags, epoch);
+    }
+    return hipErrorInvalidValue;
+}
+
 #define RWS_NORM_DT_SWITCH(FN, A, B)                                                      \
     switch (L.dtype) {                                                                    \
         case kF32: return L.aligned ? FN<kF32, true, A, B>(L) : FN<kF32, false, A, B>(L);    \

@@ -1,0 +1,58 @@
+// rws_ordered.hpp -- the exchange of the single-launch ("ordered") split-k
+// kernels: stage-1 workgroups publish a chunk's partial as epoch-tagged
+// 64-bit words, stage-2 workgroups of the same row poll them (see
+// rws_splitk_ordered.hip for why this needs no fence and no co-residency).
+// Shared by the softmax forward, the softmax backward and the row
+// normalisations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rws {
+
+// Tries of one poll before it gives up (each a sleep plus a load round trip:
+// at least ~0.5 s in all); the workgroup then writes NaN, so a broken
+// ordering assumption shows as NaN output, never as a hang.
+constexpr unsigned kOrderedSpinLimit = 1u << 21;
+
+__device__ inline uint64_t tag_word(unsigned epoch, float v) {
+    return ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(v);
+}
+
+__device__ inline void publish_word(uint64_t* p, unsigned epoch, float v) {
+    __hip_atomic_store(p, tag_word(epoch, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Poll one tagged word until it carries `epoch`; returns its value bits and
+// sets `late` when the limit ran out (a thread that is already late does not
+// wait again, so one thread waits at most one limit in total).
+__device__ inline float poll_word(const uint64_t* p, unsigned epoch, int& late) {
+    for (unsigned it = 0; it < (late ? 1u : kOrderedSpinLimit); ++it) {
+        const uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((unsigned)(v >> 32) == epoch) return __uint_as_float((unsigned)v);
+        __builtin_amdgcn_s_sleep(2);
+    }
+    late = 1;
+    return 0.0f;
+}
+
+// Workgroup b of an ordered launch over rows x P chunks: [0, rows*P) are
+// stage 1, [rows*P, 2*rows*P) stage 2, row-major within each stage.
+struct OrderedSlot {
+    bool merge_stage;
+    int64_t row;
+    int chunk;
+};
+
+__device__ inline OrderedSlot ordered_slot(int64_t b, int64_t rows, int P) {
+    OrderedSlot s;
+    const int64_t RP = rows * P;
+    s.merge_stage = b >= RP;
+    if (s.merge_stage) b -= RP;
+    s.row = b / P;
+    s.chunk = (int)(b - s.row * P);
+    return s;
+}
+
+}  // namespace rws

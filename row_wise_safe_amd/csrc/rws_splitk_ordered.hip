@@ -35,30 +35,12 @@
 // workgroups finish, instead of after a kernel boundary).
 #include "rws_kernels.hpp"
 #include "rws_launch.hpp"
+#include "rws_ordered.hpp"
 #include "rws_variants.hpp"
 
 #include <algorithm>
 
 namespace rws {
-
-constexpr unsigned kOrderedSpinLimit = 1u << 21;
-
-__device__ inline uint64_t md_word(unsigned epoch, float v) {
-    return ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(v);
-}
-
-// Poll one tagged word until it carries `epoch`; returns its value bits and
-// sets `late` when the limit ran out (a thread that is already late does not
-// wait again, so one thread waits at most one limit in total).
-__device__ inline float poll_word(const uint64_t* p, unsigned epoch, int& late) {
-    for (unsigned it = 0; it < (late ? 1u : kOrderedSpinLimit); ++it) {
-        const uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((unsigned)(v >> 32) == epoch) return __uint_as_float((unsigned)v);
-        __builtin_amdgcn_s_sleep(2);
-    }
-    late = 1;
-    return 0.0f;
-}
 
 template <int DT, bool ALIGNED, int BLOCK, int KC>
 __global__ __launch_bounds__(BLOCK) void k_splitk_ordered(const void* __restrict__ in,
@@ -94,10 +76,8 @@ __global__ __launch_bounds__(BLOCK) void k_splitk_ordered(const void* __restrict
         const float2 md =
             splitk_partial<DT, ALIGNED, BLOCK, KC>(w, kbase, raw, tbeg, tend, red_max, red_sum);
         if (t == 0) {
-            __hip_atomic_store(row_tags + 2 * chunk, md_word(epoch, md.x), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(row_tags + 2 * chunk + 1, md_word(epoch, md.y), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+            publish_word(row_tags + 2 * chunk, epoch, md.x);
+            publish_word(row_tags + 2 * chunk + 1, epoch, md.y);
         }
         return;
     }

@@ -208,11 +208,25 @@ def test_norm_affine_shape_choice(lib, rows, cols, shape):
     (16384, 2000, "bwd_block<f16,unaligned,B=320,KR=1>"),
     (8192, 4096, "bwd_block<f16,aligned,B=512,KR=1>"),
     (8192, 4097, "bwd_block<f16,unaligned,B=192,KR=3> grid=8192 block=192 xcd_run=16"),
-    (64, 40000, "bwd_stream<f16,aligned,B=1024,U=4>"),
+    (1024, 40000, "bwd_stream<f16,aligned,B=1024,U=4>"),
 ])
 def test_bwd_shape_choice(lib, rows, cols, shape):
     desc = rws.softmax_bwd_describe_launch(rows, cols, rws.RWS_F16, 256, 512)
     assert desc.startswith(shape), desc
+
+
+# Few long rows: the backward and the normalisations take the single-launch
+# split-k (chunks of 1024 granules), like the forward.
+@pytest.mark.parametrize("rows,cols,P", [(16, 1 << 20, 128), (64, 1 << 18, 32),
+                                         (128, 16384, 2)])
+def test_few_long_rows_take_ordered_split_k(lib, rows, cols, P):
+    b = rws.softmax_bwd_describe_launch(rows, cols, rws.RWS_F16, 256, 512)
+    n = rws.norm_describe_launch(rows, cols, rws.RWS_F16, 256, 512)
+    assert b.startswith("bwd_ordered") and f" P={P} " in b, b
+    assert n.startswith("norm_ordered") and f" P={P} " in n, n
+    # from one row per two CUs on, one workgroup per row
+    assert not rws.softmax_bwd_describe_launch(129, cols, rws.RWS_F16, 256, 512).startswith("bwd_ordered")
+    assert not rws.norm_describe_launch(129, cols, rws.RWS_F16, 256, 512).startswith("norm_ordered")
 
 
 # Runs of consecutive rows per XCD for block_onepass on rows that are not

@@ -113,10 +113,11 @@ def _bwd_cases(dtype: str):
     seen = {}
     step = 16 // es
     for cols in range(step, 4096 * step, step):
-        desc = rws.softmax_bwd_describe_launch(64, cols, CODE[dtype], 256, 512)
+        # 192 rows: beyond the few-rows limit of the ordered split-k
+        desc = rws.softmax_bwd_describe_launch(192, cols, CODE[dtype], 256, 512)
         m = re.match(r"bwd_block<[^>]*B=(\d+),KR=(\d+)>", desc)
         if m:
-            seen.setdefault(tuple(int(v) for v in m.groups()), (64, cols))
+            seen.setdefault(tuple(int(v) for v in m.groups()), (192, cols))
     return seen
 
 
