@@ -293,7 +293,7 @@ int softmax_bwd_describe_launch(int64_t rows, int64_t cols, int dtype, const voi
  * same choice: norm_wave, norm_block, norm_stream or norm_ordered, with its
  * shape).
  * affine: nonzero when a weight and/or bias is passed (it can change the
- * lane group).  kernel_id: RWS_KERNEL_AUTO, _WAVE_ROW, _BLOCK_ONEPASS or
+ * lane group).  kernel_id: RWS_KERNEL_AUTO, _WAVE_ROW, _BLOCK_ONEPASS,
  * _TWO_PASS or _SPLITK_ORDERED.  Performs no GPU work.
  */
 int norm_describe_launch(int64_t rows, int64_t cols, int dtype, const void *in, const void *out,
