@@ -349,8 +349,8 @@ int pick_splitk_fused(int64_t rows, int64_t wmax, int dtype, bool aligned, int c
     return best;
 }
 
-int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
-                int kernel_id, Plan* p, bool masked = false) {
+int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
+                         int kernel_id, Plan* p, bool masked) {
     const Geometry g = geometry(cols, dtype, in, out);
     p->same_phase = g.same_phase;
     const int64_t wline = window_granules(g, 128);  // block-level kernels
@@ -639,6 +639,54 @@ int check_args(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
 
 // One call: plan, get the workspace if needed, launch in row batches.
 // `mask` selects the masked/scaled form (nullptr: plain softmax).
+// The plan is a function of the shape, the dtype, the kernel request, the
+// pointers' offsets within a 128-byte line and the device.  The last few
+// plans are kept per thread, so a repeated call skips the variant searches
+// (about 0.4 us of the ~4 us a small call spends on the host, measured on
+// MI355X through ctypes).
+struct PlanKey {
+    int64_t rows, cols;
+    int dtype, kernel_id, dev;
+    unsigned in_line, out_line;
+    bool masked;
+    bool operator==(const PlanKey& o) const {
+        return rows == o.rows && cols == o.cols && dtype == o.dtype && kernel_id == o.kernel_id &&
+               dev == o.dev && in_line == o.in_line && out_line == o.out_line && masked == o.masked;
+    }
+};
+
+int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
+                int kernel_id, Plan* p, bool masked = false) {
+    struct Slot {
+        PlanKey key;
+        Plan plan;
+        bool used = false;
+    };
+    constexpr int kSlots = 8;
+    thread_local Slot slots[kSlots];
+    thread_local int next = 0;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        dev = -1;
+    }
+    const PlanKey key{rows, cols, dtype, kernel_id, dev, (unsigned)((uintptr_t)in % 128),
+                      (unsigned)((uintptr_t)out % 128), masked};
+    for (const Slot& sl : slots)
+        if (sl.used && sl.key == key) {
+            *p = sl.plan;
+            return RWS_OK;
+        }
+    const int st = plan_launch_uncached(rows, cols, dtype, in, out, kernel_id, p, masked);
+    if (st == RWS_OK) {
+        slots[next].key = key;
+        slots[next].plan = *p;
+        slots[next].used = true;
+        next = (next + 1) % kSlots;
+    }
+    return st;
+}
+
 int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream,
         int kernel_id, const rws::MaskArgs* mask) {
     Plan p;

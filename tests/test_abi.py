@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import row_wise_safe_amd as rws
@@ -323,3 +324,28 @@ def test_norm_argument_checks(lib):
         rws.RWS_ERR_UNSUPPORTED_SHAPE
     assert rws.rmsnorm_fwd_kernel(256, 256, 2, 70000, f16, 1e-5, 0, 0, 0, 2) == \
         rws.RWS_ERR_UNSUPPORTED_SHAPE
+
+
+def test_plan_cache_keeps_calls_apart(lib):
+    # the dispatcher keeps its last plans per thread, keyed on everything a
+    # plan depends on: the same queries in any order give the same answers
+    cases = []
+    for rows, cols in [(65536, 512), (64, 1000), (16, 1 << 20), (8192, 4097), (4096, 8000)]:
+        for dtype in (rws.RWS_F32, rws.RWS_F16):
+            for inp, out in [(256, 512), (258, 514), (256, 272)]:
+                for kid in (0, 2):
+                    for masked in (False, True):
+                        cases.append((rows, cols, dtype, inp, out, kid, masked))
+
+    def ask(c):
+        try:
+            return rws.softmax_describe_launch(*c[:6], masked=c[6])
+        except rws.SoftmaxError as e:
+            return f"error {e.status}"
+
+    first = [ask(c) for c in cases]
+    rng = np.random.Generator(np.random.PCG64(0))
+    for _ in range(3):
+        order = rng.permutation(len(cases))
+        for i in order:
+            assert ask(cases[i]) == first[i], cases[i]
