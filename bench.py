@@ -51,11 +51,11 @@ KERNEL_SOURCES = {
     "two_pass": _SOFTMAX_COMMON + ["rws_two_pass.hip"],
     "splitk": _SOFTMAX_COMMON,
     "splitk_fused": _SOFTMAX_COMMON + ["rws_splitk_fused.hip"],
-    "splitk_ordered": _SOFTMAX_COMMON + ["rws_splitk_ordered.hip"],
+    "splitk_ordered": _SOFTMAX_COMMON + ["rws_ordered.hpp", "rws_splitk_ordered.hip"],
     "masked": _SOFTMAX_COMMON + ["rws_masked.hip"],
-    "backward": _SOFTMAX_COMMON + ["rws_backward.hip"],
-    "layernorm": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_norm.hpp", "rws_norm_wave.hip",
-                                    "rws_norm_block.hip"],
+    "backward": _SOFTMAX_COMMON + ["rws_ordered.hpp", "rws_backward.hip"],
+    "layernorm": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_ordered.hpp", "rws_norm.hpp",
+                                    "rws_norm_wave.hip", "rws_norm_block.hip"],
 }
 KERNEL_SOURCES["rmsnorm"] = KERNEL_SOURCES["layernorm"]
 # Substring that names the step's kernels in a trace.
