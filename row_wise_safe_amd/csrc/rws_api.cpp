@@ -19,6 +19,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <vector>
 #include <tuple>
 #include <mutex>
 #include <string>
@@ -489,6 +490,8 @@ struct Workspace {
     uint64_t* tags = nullptr;   // ordered split-k: epoch-tagged partial words
     int64_t tag_words = 0;
     unsigned tag_epoch = 0;     // last epoch used on `tags`
+    bool captured = false;      // `ptr` is baked into a captured graph
+    std::vector<void*> retired; // partial buffers that graphs may still use
 };
 
 std::mutex g_ws_mu;
@@ -503,11 +506,27 @@ struct WorkspaceReaper {
             if (kv.second.ptr) (void)hipFree(kv.second.ptr);
             if (kv.second.sync) (void)hipFree(kv.second.sync);
             if (kv.second.tags) (void)hipFree(kv.second.tags);
+            for (void* p : kv.second.retired) (void)hipFree(p);
         }
         delete g_ws;
         g_ws = nullptr;
     }
 } g_ws_reaper;
+
+// True while `s` is being captured into a graph.  The single-launch split-k
+// forms tell one launch's partials from the last one's by an epoch passed as
+// a kernel argument, which a graph would replay unchanged (a replay's stage 2
+// could take the previous replay's partials).  Under capture they give way
+// to forms ordered by kernel boundaries: the forward's two-launch split-k,
+// the backward's and the normalisations' one-workgroup-per-row forms.
+bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return st != hipStreamCaptureStatusNone;
+}
 
 // Grow-only workspace of (device, stream): `bytes` of partials and, when
 // sync_rows > 0, kSyncWordsPerRow*sync_rows zeroed counter words.  Returns the epoch for a
@@ -515,7 +534,10 @@ struct WorkspaceReaper {
 // g_ws_mu from this call until its launches are enqueued: a call from another
 // host thread on the same stream that grows the buffer synchronises the
 // stream and frees the old one, which is only safe once every launch that
-// uses it is on the stream.
+// uses it is on the stream.  Under graph capture nothing is allocated (the
+// call fails if the buffer is too small) and the buffer handed out is marked
+// captured: when it grows later it is kept, not freed, since the graph's
+// launches still name it.
 int get_workspace(hipStream_t stream, size_t bytes, int64_t sync_rows, void** out,
                   unsigned** sync, unsigned* epoch) {
     int dev = 0;
@@ -525,6 +547,10 @@ int get_workspace(hipStream_t stream, size_t bytes, int64_t sync_rows, void** ou
     Workspace& w = (*g_ws)[std::make_pair(dev, stream)];
     const bool grow_partials = w.bytes < bytes;
     const bool grow_sync = sync_rows > w.sync_rows;
+    if ((grow_partials || grow_sync) && capturing(stream))
+        return fail(RWS_ERR_HIP,
+                    "split-k workspace too small during graph capture: run the call once on "
+                    "this stream before capturing it");
     if ((grow_partials || grow_sync) && (w.ptr || w.sync)) {
         // the old buffers may still be in use by earlier work on this stream
         e = hipStreamSynchronize(stream);
@@ -534,7 +560,11 @@ int get_workspace(hipStream_t stream, size_t bytes, int64_t sync_rows, void** ou
     if (std::getenv("RWS_TEST_FAIL_ALLOC") && (grow_partials || grow_sync))
         return fail(RWS_ERR_HIP, "workspace allocation failed (RWS_TEST_FAIL_ALLOC)");
     if (grow_partials) {
-        if (w.ptr) (void)hipFree(w.ptr);
+        if (w.ptr && w.captured)
+            w.retired.push_back(w.ptr);
+        else if (w.ptr)
+            (void)hipFree(w.ptr);
+        w.captured = false;
         w.ptr = nullptr;
         w.bytes = 0;
         size_t want = 4096;
@@ -562,6 +592,7 @@ int get_workspace(hipStream_t stream, size_t bytes, int64_t sync_rows, void** ou
         }
         w.sync_rows = want;
     }
+    if (capturing(stream)) w.captured = true;
     *out = w.ptr;
     if (sync) *sync = w.sync;
     if (epoch) {
@@ -584,6 +615,8 @@ int get_tag_workspace(hipStream_t stream, int64_t words, int64_t launches, uint6
     if (e != hipSuccess) return fail(RWS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
     if (!g_ws) g_ws = new std::map<std::pair<int, hipStream_t>, Workspace>();
     Workspace& w = (*g_ws)[std::make_pair(dev, stream)];
+    if (w.tag_words < words && capturing(stream))
+        return fail(RWS_ERR_HIP, "split-k tag words too small during graph capture");
     if (w.tag_words < words) {
         if (w.tags) {
             // the old words may still be in use by earlier work on this stream
@@ -692,6 +725,11 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
     Plan p;
     int st = plan_launch(rows, cols, dtype, in, out, kernel_id, &p, mask != nullptr);
     if (st != RWS_OK) return st;
+    if ((p.family == RWS_KERNEL_SPLITK_ORDERED || p.family == RWS_KERNEL_SPLITK_FUSED) &&
+        capturing((hipStream_t)stream)) {
+        st = plan_launch(rows, cols, dtype, in, out, RWS_KERNEL_SPLITK, &p, mask != nullptr);
+        if (st != RWS_OK) return st;
+    }
 
     void* ws = nullptr;
     unsigned* sync = nullptr;
@@ -701,6 +739,20 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
     std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
     uint64_t* tags = nullptr;
     if (is_splitk(p.family)) ws_lock.lock();
+    if (p.family == RWS_KERNEL_SPLITK_ORDERED || p.family == RWS_KERNEL_SPLITK_FUSED) {
+        // size the two-launch form's partials too (rows * P pairs, a few KiB
+        // for these shapes): a capture of the same call takes that form and
+        // must find its workspace already allocated (sized before the
+        // buffers below are taken, since growing frees the old buffer)
+        Plan p2;
+        if (plan_launch(rows, cols, dtype, in, out, RWS_KERNEL_SPLITK, &p2, mask != nullptr) ==
+            RWS_OK) {
+            void* ws2 = nullptr;
+            const int64_t batch2 = std::min<int64_t>(rows, p2.max_rows_per_launch);
+            st = get_workspace(s, (size_t)batch2 * p2.P * sizeof(float2), 0, &ws2, nullptr, nullptr);
+            if (st != RWS_OK) return st;
+        }
+    }
     if (p.family == RWS_KERNEL_SPLITK) {
         const int64_t batch = std::min<int64_t>(rows, p.max_rows_per_launch);
         st = get_workspace(s, (size_t)batch * p.P * sizeof(float2), 0, &ws, nullptr, nullptr);
@@ -809,9 +861,11 @@ struct BwdPlan {
     int64_t max_rows = 0;
 };
 
+// allow_ordered: false while the stream is captured (see capturing()); a
+// request for the ordered form then plans as RWS_KERNEL_AUTO without it.
 static int plan_bwd(int64_t rows, int64_t cols, int dtype, const void* y, const void* dx,
-                    int kernel_id, BwdPlan* bp) {
-    (void)rows;
+                    int kernel_id, BwdPlan* bp, bool allow_ordered = true) {
+    if (!allow_ordered && kernel_id == RWS_KERNEL_SPLITK_ORDERED) kernel_id = RWS_KERNEL_AUTO;
     const Geometry g = geometry(cols, dtype, y, dx);
     const int64_t wline = window_granules(g, 128);
     int family = kernel_id == RWS_KERNEL_AUTO ? 0 : kernel_id;  // 1 wave, 2 block, 3 stream, 6
@@ -860,7 +914,7 @@ static int plan_bwd(int64_t rows, int64_t cols, int dtype, const void* y, const 
     };
     if (family == 0) {
         if (pick_wave(1) >= 0) family = 1;
-        else if (few_long_rows(rows, wline, cus)) family = RWS_KERNEL_SPLITK_ORDERED;
+        else if (allow_ordered && few_long_rows(rows, wline, cus)) family = RWS_KERNEL_SPLITK_ORDERED;
         else if (pick_block() >= 0) family = 2;
         else family = 3;
     }
@@ -916,7 +970,7 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
     if ((uintptr_t)dy % elem_size(dtype))
         return fail(RWS_ERR_MISALIGNED, "dy not aligned to the element size");
     BwdPlan bp;
-    st = plan_bwd(rows, cols, dtype, y, dx, kernel_id, &bp);
+    st = plan_bwd(rows, cols, dtype, y, dx, kernel_id, &bp, !capturing((hipStream_t)stream));
     if (st != RWS_OK) return st;
     const int family = bp.family, variant = bp.variant;
     const int64_t max_rows = bp.max_rows;
@@ -972,8 +1026,10 @@ struct NormPlan {
     int64_t max_rows = 0;
 };
 
+// allow_ordered: as for plan_bwd.
 static int plan_norm(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
-                     bool affine, int kernel_id, NormPlan* np) {
+                     bool affine, int kernel_id, NormPlan* np, bool allow_ordered = true) {
+    if (!allow_ordered && kernel_id == RWS_KERNEL_SPLITK_ORDERED) kernel_id = RWS_KERNEL_AUTO;
     const Geometry g = geometry(cols, dtype, in, out);
     const int64_t wline = window_granules(g, 128);
     // Lane groups measured on MI355X (fp16 LayerNorm / RMSNorm, rotating
@@ -1034,7 +1090,8 @@ static int plan_norm(int64_t rows, int64_t cols, int dtype, const void* in, cons
     int family = kernel_id == RWS_KERNEL_AUTO ? 0 : kernel_id;
     if (family == 0) {
         if (pick_wave(1) >= 0) family = 1;
-        else if (few_long_rows(rows, wline, device_info().cus)) family = RWS_KERNEL_SPLITK_ORDERED;
+        else if (allow_ordered && few_long_rows(rows, wline, device_info().cus))
+            family = RWS_KERNEL_SPLITK_ORDERED;
         else if (pick_block() >= 0) family = 2;
         else family = 3;
     }
@@ -1099,7 +1156,8 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
     if ((uintptr_t)mean % 4 || (uintptr_t)rstd % 4)
         return fail(RWS_ERR_MISALIGNED, "mean/rstd not aligned to 4 bytes");
     NormPlan np;
-    st = plan_norm(rows, cols, dtype, in, out, weight || bias, kernel_id, &np);
+    st = plan_norm(rows, cols, dtype, in, out, weight || bias, kernel_id, &np,
+                   !capturing((hipStream_t)stream));
     if (st != RWS_OK) return st;
     const int family = np.family, variant = np.variant;
     const int64_t max_rows = np.max_rows;
