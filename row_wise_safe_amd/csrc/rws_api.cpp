@@ -534,11 +534,11 @@ bool capturing(hipStream_t s) {
 // g_ws_mu from this call until its launches are enqueued: a call from another
 // host thread on the same stream that grows the buffer synchronises the
 // stream and frees the old one, which is only safe once every launch that
-// uses it is on the stream.  Under graph capture nothing is allocated (the
-// call fails if the buffer is too small) and the buffer handed out is marked
-// captured: when it grows later it is kept, not freed, since the graph's
-// launches still name it.
-int get_workspace(hipStream_t stream, size_t bytes, int64_t sync_rows, void** out,
+// uses it is on the stream.  Under graph capture (`cap`: the stream is
+// capturing) nothing is allocated (the call fails if the buffer is too
+// small) and the buffer handed out is marked captured: when it grows later it
+// is kept, not freed, since the graph's launches still name it.
+int get_workspace(hipStream_t stream, bool cap, size_t bytes, int64_t sync_rows, void** out,
                   unsigned** sync, unsigned* epoch) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -547,7 +547,7 @@ int get_workspace(hipStream_t stream, size_t bytes, int64_t sync_rows, void** ou
     Workspace& w = (*g_ws)[std::make_pair(dev, stream)];
     const bool grow_partials = w.bytes < bytes;
     const bool grow_sync = sync_rows > w.sync_rows;
-    if ((grow_partials || grow_sync) && capturing(stream))
+    if ((grow_partials || grow_sync) && cap)
         return fail(RWS_ERR_HIP,
                     "split-k workspace too small during graph capture: run the call once on "
                     "this stream before capturing it");
@@ -592,7 +592,7 @@ int get_workspace(hipStream_t stream, size_t bytes, int64_t sync_rows, void** ou
         }
         w.sync_rows = want;
     }
-    if (capturing(stream)) w.captured = true;
+    if (cap) w.captured = true;
     *out = w.ptr;
     if (sync) *sync = w.sync;
     if (epoch) {
@@ -725,8 +725,8 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
     Plan p;
     int st = plan_launch(rows, cols, dtype, in, out, kernel_id, &p, mask != nullptr);
     if (st != RWS_OK) return st;
-    if ((p.family == RWS_KERNEL_SPLITK_ORDERED || p.family == RWS_KERNEL_SPLITK_FUSED) &&
-        capturing((hipStream_t)stream)) {
+    const bool cap = is_splitk(p.family) && capturing((hipStream_t)stream);
+    if (cap && p.family != RWS_KERNEL_SPLITK) {
         st = plan_launch(rows, cols, dtype, in, out, RWS_KERNEL_SPLITK, &p, mask != nullptr);
         if (st != RWS_OK) return st;
     }
@@ -749,16 +749,17 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
             RWS_OK) {
             void* ws2 = nullptr;
             const int64_t batch2 = std::min<int64_t>(rows, p2.max_rows_per_launch);
-            st = get_workspace(s, (size_t)batch2 * p2.P * sizeof(float2), 0, &ws2, nullptr, nullptr);
+            st = get_workspace(s, false, (size_t)batch2 * p2.P * sizeof(float2), 0, &ws2,
+                               nullptr, nullptr);
             if (st != RWS_OK) return st;
         }
     }
     if (p.family == RWS_KERNEL_SPLITK) {
         const int64_t batch = std::min<int64_t>(rows, p.max_rows_per_launch);
-        st = get_workspace(s, (size_t)batch * p.P * sizeof(float2), 0, &ws, nullptr, nullptr);
+        st = get_workspace(s, cap, (size_t)batch * p.P * sizeof(float2), 0, &ws, nullptr, nullptr);
         if (st != RWS_OK) return st;
     } else if (p.family == RWS_KERNEL_SPLITK_FUSED) {
-        st = get_workspace(s, (size_t)rows * p.P * sizeof(float2), rows, &ws, &sync, &epoch);
+        st = get_workspace(s, cap, (size_t)rows * p.P * sizeof(float2), rows, &ws, &sync, &epoch);
         if (st != RWS_OK) return st;
     } else if (p.family == RWS_KERNEL_SPLITK_ORDERED) {
         const int64_t batch = std::min<int64_t>(rows, p.max_rows_per_launch);
@@ -970,7 +971,9 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
     if ((uintptr_t)dy % elem_size(dtype))
         return fail(RWS_ERR_MISALIGNED, "dy not aligned to the element size");
     BwdPlan bp;
-    st = plan_bwd(rows, cols, dtype, y, dx, kernel_id, &bp, !capturing((hipStream_t)stream));
+    st = plan_bwd(rows, cols, dtype, y, dx, kernel_id, &bp);
+    if (st == RWS_OK && bp.family == RWS_KERNEL_SPLITK_ORDERED && capturing((hipStream_t)stream))
+        st = plan_bwd(rows, cols, dtype, y, dx, kernel_id, &bp, false);
     if (st != RWS_OK) return st;
     const int family = bp.family, variant = bp.variant;
     const int64_t max_rows = bp.max_rows;
@@ -1156,8 +1159,9 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
     if ((uintptr_t)mean % 4 || (uintptr_t)rstd % 4)
         return fail(RWS_ERR_MISALIGNED, "mean/rstd not aligned to 4 bytes");
     NormPlan np;
-    st = plan_norm(rows, cols, dtype, in, out, weight || bias, kernel_id, &np,
-                   !capturing((hipStream_t)stream));
+    st = plan_norm(rows, cols, dtype, in, out, weight || bias, kernel_id, &np);
+    if (st == RWS_OK && np.family == RWS_KERNEL_SPLITK_ORDERED && capturing((hipStream_t)stream))
+        st = plan_norm(rows, cols, dtype, in, out, weight || bias, kernel_id, &np, false);
     if (st != RWS_OK) return st;
     const int family = np.family, variant = np.variant;
     const int64_t max_rows = np.max_rows;
