@@ -46,19 +46,21 @@
  * call's stream), later calls reuse it.  Calls on one stream are ordered, so
  * reuse is safe; the workspaces are released when the library is unloaded.
  *
- * Graph capture.  Every entry point may be captured into a HIP graph.  While
- * `stream` is capturing, the single-launch split-k forms (ordered and
- * cooperative) give way to forms ordered by kernel boundaries, since they
- * tell one launch's partials from the last by an epoch that a replay would
- * repeat: the forward takes the two-launch split-k, the backward and the
- * normalisations one workgroup per row.  Nothing is allocated or cleared
- * during capture: capture a split-k call only after the same call (or a
- * larger one) has run once eagerly on the capturing stream, otherwise the
- * call returns RWS_ERR_HIP and enqueues nothing.  A partials buffer that a
- * graph captured is never freed while the library is loaded (a later, larger
- * call on that stream gets a new one), so the graph stays valid; replay it on
- * the capturing stream, or order it with that stream's other split-k calls,
- * since both use that buffer.
+ * Graph capture.  Every entry point may be captured into a HIP graph.  The
+ * single-launch split-k forms tell one launch's partials from the last by an
+ * epoch that a replay would repeat, so while `stream` is capturing the
+ * forward takes the two-launch split-k instead, and the backward and the
+ * normalisations take their epoch from device memory, advanced by a small
+ * kernel recorded before each of their split-k launches.  Nothing is
+ * allocated during capture: capture a forward split-k call only after the
+ * same call (or a larger one) has run once eagerly on the capturing stream,
+ * otherwise the call returns RWS_ERR_HIP and enqueues nothing; a backward or
+ * normalisation call that finds no workspace on the stream records its
+ * one-workgroup-per-row form (correct, slower for few long rows).  A
+ * workspace buffer that a graph captured is never freed while the library is
+ * loaded (a later, larger call on that stream gets a new one), so the graph
+ * stays valid; replay it on the capturing stream, or order it with that
+ * stream's other split-k calls, since both use that buffer.
  *
  * Errors.  Every entry point returns a status code (below) and never exits or
  * throws.  rows == 0 or cols == 0 is a successful no-op.  A HIP launch error

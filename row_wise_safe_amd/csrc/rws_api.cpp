@@ -491,8 +491,13 @@ struct Workspace {
     int64_t tag_words = 0;
     unsigned tag_epoch = 0;     // last epoch used on `tags`
     bool captured = false;      // `ptr` is baked into a captured graph
-    std::vector<void*> retired; // partial buffers that graphs may still use
+    bool tags_captured = false; // `tags` is baked into a captured graph
+    std::vector<void*> retired; // buffers that graphs may still use
 };
+
+// Words after a tag buffer's tag words: the device epoch of launches replayed
+// from graphs (rws_ordered.hpp), padded to a 128-byte line.
+constexpr int64_t kTagTailWords = 16;
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace>* g_ws = nullptr;
@@ -516,9 +521,12 @@ struct WorkspaceReaper {
 // True while `s` is being captured into a graph.  The single-launch split-k
 // forms tell one launch's partials from the last one's by an epoch passed as
 // a kernel argument, which a graph would replay unchanged (a replay's stage 2
-// could take the previous replay's partials).  Under capture they give way
-// to forms ordered by kernel boundaries: the forward's two-launch split-k,
-// the backward's and the normalisations' one-workgroup-per-row forms.
+// could take the previous replay's partials).  Under capture the forward
+// takes the two-launch split-k (ordered by its kernel boundary); the
+// backward and the normalisations keep their ordered launch but take its
+// epoch from a device word that a kernel recorded before it advances on
+// every replay (launch_bump_epoch), or, when the stream has no tag buffer
+// large enough, take their one-workgroup-per-row forms.
 bool capturing(hipStream_t s) {
     hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &st) != hipSuccess) {
@@ -603,10 +611,12 @@ int get_workspace(hipStream_t stream, bool cap, size_t bytes, int64_t sync_rows,
 }
 
 // Tag words of the ordered split-k for (device, stream): grow-only, zeroed
-// (by a kernel on `stream`) when allocated.  Reserves `launches` consecutive
-// epochs and returns the first in *epoch0; when the 32-bit epoch would wrap,
-// the words are zeroed again and the epochs restart at 1, so a word left by
-// an earlier launch never carries a live epoch.  The caller holds g_ws_mu
+// (by a kernel on `stream`) when allocated, followed by the device epoch word
+// of captured launches.  Reserves `launches` consecutive host epochs and
+// returns the first in *epoch0; when the host's range [1, 2^31) would run
+// out, the words are zeroed again and the epochs restart at 1, so a word left
+// by an earlier launch never carries a live epoch.  A buffer that a graph
+// captured is kept, not freed, when it grows.  The caller holds g_ws_mu
 // until its launches are enqueued (as for get_workspace).
 int get_tag_workspace(hipStream_t stream, int64_t words, int64_t launches, uint64_t** out,
                       unsigned* epoch0) {
@@ -618,33 +628,41 @@ int get_tag_workspace(hipStream_t stream, int64_t words, int64_t launches, uint6
     if (w.tag_words < words && capturing(stream))
         return fail(RWS_ERR_HIP, "split-k tag words too small during graph capture");
     if (w.tag_words < words) {
-        if (w.tags) {
+        if (w.tags && w.tags_captured) {
+            w.retired.push_back(w.tags);
+        } else if (w.tags) {
             // the old words may still be in use by earlier work on this stream
             e = hipStreamSynchronize(stream);
             if (e != hipSuccess)
                 return fail(RWS_ERR_HIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
             (void)hipFree(w.tags);
-            w.tags = nullptr;
-            w.tag_words = 0;
         }
+        w.tags = nullptr;
+        w.tag_words = 0;
+        w.tags_captured = false;
         if (std::getenv("RWS_TEST_FAIL_ALLOC"))
             return fail(RWS_ERR_HIP, "workspace allocation failed (RWS_TEST_FAIL_ALLOC)");
         int64_t want = 512;
         while (want < words) want *= 2;
-        e = hipMalloc((void**)&w.tags, (size_t)want * sizeof(uint64_t));
-        if (e == hipSuccess) e = rws::launch_zero_words(w.tags, want, stream);
+        e = hipMalloc((void**)&w.tags, (size_t)(want + kTagTailWords) * sizeof(uint64_t));
+        if (e == hipSuccess) e = rws::launch_fill_words(w.tags, want + kTagTailWords, 0, stream);
+        // test hooks: start a fresh buffer's host or device epochs just below
+        // the end of their range
+        const char* dev_start = std::getenv("RWS_TEST_DEVICE_EPOCH");
+        if (e == hipSuccess && dev_start)
+            e = rws::launch_fill_words(w.tags + want, 1, std::strtoull(dev_start, nullptr, 0),
+                                       stream);
         if (e != hipSuccess) {
             if (w.tags) (void)hipFree(w.tags);
             w.tags = nullptr;
             return fail(RWS_ERR_HIP, std::string("split-k tag words: ") + hipGetErrorString(e));
         }
         w.tag_words = want;
-        // test hook: start a fresh buffer's epochs just below the 32-bit wrap
         const char* start = std::getenv("RWS_TEST_TAG_EPOCH");
         w.tag_epoch = start ? (unsigned)std::strtoul(start, nullptr, 0) : 0u;
     }
-    if ((uint64_t)w.tag_epoch + (uint64_t)launches > 0xffffffffull) {
-        e = rws::launch_zero_words(w.tags, w.tag_words, stream);
+    if ((uint64_t)w.tag_epoch + (uint64_t)launches >= (uint64_t)rws::kDeviceEpochFirst) {
+        e = rws::launch_fill_words(w.tags, w.tag_words, 0, stream);
         if (e != hipSuccess)
             return fail(RWS_ERR_HIP, std::string("split-k tag words: ") + hipGetErrorString(e));
         w.tag_epoch = 0;
@@ -653,6 +671,26 @@ int get_tag_workspace(hipStream_t stream, int64_t words, int64_t launches, uint6
     *epoch0 = w.tag_epoch + 1;
     w.tag_epoch += (unsigned)launches;
     return RWS_OK;
+}
+
+// Under graph capture: the stream's tag buffer and its word count when it
+// holds `words` (it is then marked captured), else false: nothing may be
+// allocated while capturing, and the caller takes a form without tags.
+// Each captured ordered launch is preceded by launch_bump_epoch on the
+// buffer and reads its epoch from the word after the tag words.
+bool captured_tags(hipStream_t stream, int64_t words, uint64_t** tags, int64_t* n) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    if (!g_ws) return false;
+    auto it = g_ws->find(std::make_pair(dev, stream));
+    if (it == g_ws->end() || !it->second.tags || it->second.tag_words < words) return false;
+    it->second.tags_captured = true;
+    *tags = it->second.tags;
+    *n = it->second.tag_words;
+    return true;
 }
 
 int check_args(const void* in, void* out, int64_t rows, int64_t cols, int dtype, int kernel_id) {
@@ -862,8 +900,9 @@ struct BwdPlan {
     int64_t max_rows = 0;
 };
 
-// allow_ordered: false while the stream is captured (see capturing()); a
-// request for the ordered form then plans as RWS_KERNEL_AUTO without it.
+// allow_ordered: false when a captured call finds no tag buffer large enough
+// (see capturing()); a request for the ordered form then plans as
+// RWS_KERNEL_AUTO without it.
 static int plan_bwd(int64_t rows, int64_t cols, int dtype, const void* y, const void* dx,
                     int kernel_id, BwdPlan* bp, bool allow_ordered = true) {
     if (!allow_ordered && kernel_id == RWS_KERNEL_SPLITK_ORDERED) kernel_id = RWS_KERNEL_AUTO;
@@ -972,22 +1011,29 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
         return fail(RWS_ERR_MISALIGNED, "dy not aligned to the element size");
     BwdPlan bp;
     st = plan_bwd(rows, cols, dtype, y, dx, kernel_id, &bp);
-    if (st == RWS_OK && bp.family == RWS_KERNEL_SPLITK_ORDERED && capturing((hipStream_t)stream))
-        st = plan_bwd(rows, cols, dtype, y, dx, kernel_id, &bp, false);
     if (st != RWS_OK) return st;
-    const int family = bp.family, variant = bp.variant;
-    const int64_t max_rows = bp.max_rows;
     // ordered split-k: keep the tag words locked until the launches are enqueued
     std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
     uint64_t* tags = nullptr;
     unsigned epoch = 0;
-    if (family == RWS_KERNEL_SPLITK_ORDERED) {
+    int64_t tag_n = 0;  // captured: epochs come from tags[tag_n]
+    if (bp.family == RWS_KERNEL_SPLITK_ORDERED) {
         ws_lock.lock();
-        const int64_t launches = (rows + max_rows - 1) / max_rows;
-        st = get_tag_workspace((hipStream_t)stream, 2 * std::min(rows, max_rows) * bp.P, launches,
-                               &tags, &epoch);
-        if (st != RWS_OK) return st;
+        const int64_t words = 2 * std::min(rows, bp.max_rows) * bp.P;
+        if (capturing((hipStream_t)stream)) {
+            if (!captured_tags((hipStream_t)stream, words, &tags, &tag_n)) {
+                ws_lock.unlock();
+                st = plan_bwd(rows, cols, dtype, y, dx, kernel_id, &bp, false);
+                if (st != RWS_OK) return st;
+            }
+        } else {
+            const int64_t launches = (rows + bp.max_rows - 1) / bp.max_rows;
+            st = get_tag_workspace((hipStream_t)stream, words, launches, &tags, &epoch);
+            if (st != RWS_OK) return st;
+        }
     }
+    const int family = bp.family, variant = bp.variant;
+    const int64_t max_rows = bp.max_rows;
     const int64_t row_bytes = cols * elem_size(dtype);
     for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
         rws::BwdLaunch B;
@@ -1002,10 +1048,13 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
         B.dy_vec = (((uintptr_t)dy - (uintptr_t)y) % 16) == 0;
         B.lgrun = bp.lgrun;
         B.stream = (hipStream_t)stream;
-        const hipError_t e =
-            family == RWS_KERNEL_SPLITK_ORDERED
-                ? rws::launch_bwd_ordered(B, bp.P, tags, epoch + (unsigned)(r0 / max_rows))
-                : rws::launch_bwd(B, family, variant);
+        hipError_t e = hipSuccess;
+        if (family != RWS_KERNEL_SPLITK_ORDERED)
+            e = rws::launch_bwd(B, family, variant);
+        else if (tag_n == 0)
+            e = rws::launch_bwd_ordered(B, bp.P, tags, epoch + (unsigned)(r0 / max_rows));
+        else if ((e = rws::launch_bump_epoch(tags, tag_n, B.stream)) == hipSuccess)
+            e = rws::launch_bwd_ordered(B, bp.P, tags, 0, tags + tag_n);
         if (e != hipSuccess)
             return fail(RWS_ERR_HIP, std::string("backward launch: ") + hipGetErrorString(e));
     }
@@ -1160,22 +1209,29 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
         return fail(RWS_ERR_MISALIGNED, "mean/rstd not aligned to 4 bytes");
     NormPlan np;
     st = plan_norm(rows, cols, dtype, in, out, weight || bias, kernel_id, &np);
-    if (st == RWS_OK && np.family == RWS_KERNEL_SPLITK_ORDERED && capturing((hipStream_t)stream))
-        st = plan_norm(rows, cols, dtype, in, out, weight || bias, kernel_id, &np, false);
     if (st != RWS_OK) return st;
-    const int family = np.family, variant = np.variant;
-    const int64_t max_rows = np.max_rows;
     // ordered split-k: keep the tag words locked until the launches are enqueued
     std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
     uint64_t* tags = nullptr;
     unsigned epoch = 0;
-    if (family == RWS_KERNEL_SPLITK_ORDERED) {
+    int64_t tag_n = 0;  // captured: epochs come from tags[tag_n]
+    if (np.family == RWS_KERNEL_SPLITK_ORDERED) {
         ws_lock.lock();
-        const int64_t launches = (rows + max_rows - 1) / max_rows;
-        st = get_tag_workspace((hipStream_t)stream, 2 * std::min(rows, max_rows) * np.P, launches,
-                               &tags, &epoch);
-        if (st != RWS_OK) return st;
+        const int64_t words = 2 * std::min(rows, np.max_rows) * np.P;
+        if (capturing((hipStream_t)stream)) {
+            if (!captured_tags((hipStream_t)stream, words, &tags, &tag_n)) {
+                ws_lock.unlock();
+                st = plan_norm(rows, cols, dtype, in, out, weight || bias, kernel_id, &np, false);
+                if (st != RWS_OK) return st;
+            }
+        } else {
+            const int64_t launches = (rows + np.max_rows - 1) / np.max_rows;
+            st = get_tag_workspace((hipStream_t)stream, words, launches, &tags, &epoch);
+            if (st != RWS_OK) return st;
+        }
     }
+    const int family = np.family, variant = np.variant;
+    const int64_t max_rows = np.max_rows;
     const int64_t row_bytes = cols * es;
     for (int64_t r0 = 0; r0 < rows; r0 += max_rows) {
         rws::NormLaunch L;
@@ -1200,11 +1256,15 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
         L.args.eps = eps;
         L.args.n = (float)cols;
         L.stream = (hipStream_t)stream;
-        const hipError_t e =
-            family == 1 ? rws::launch_norm_wave(L, variant)
-            : family == RWS_KERNEL_SPLITK_ORDERED
-                ? rws::launch_norm_ordered(L, np.P, tags, epoch + (unsigned)(r0 / max_rows))
-                : rws::launch_norm_block(L, family, variant);
+        hipError_t e = hipSuccess;
+        if (family == 1)
+            e = rws::launch_norm_wave(L, variant);
+        else if (family != RWS_KERNEL_SPLITK_ORDERED)
+            e = rws::launch_norm_block(L, family, variant);
+        else if (tag_n == 0)
+            e = rws::launch_norm_ordered(L, np.P, tags, epoch + (unsigned)(r0 / max_rows));
+        else if ((e = rws::launch_bump_epoch(tags, tag_n, L.stream)) == hipSuccess)
+            e = rws::launch_norm_ordered(L, np.P, tags, 0, tags + tag_n);
         if (e != hipSuccess)
             return fail(RWS_ERR_HIP, std::string("normalisation launch: ") + hipGetErrorString(e));
     }

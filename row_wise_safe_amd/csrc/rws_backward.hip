@@ -249,12 +249,15 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_ordered(const void* __restrict__ 
                                                        const void* __restrict__ dy,
                                                        void* __restrict__ dx, int64_t rows,
                                                        int cols, int P, uint64_t* __restrict__ tags,
-                                                       unsigned epoch, int dy_vec, int same_phase) {
+                                                       unsigned epoch,
+                                                       const uint64_t* __restrict__ epoch_src,
+                                                       int dy_vec, int same_phase) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     using Win = RowWin<DT, ALIGNED>;
     __shared__ float red[W];
     const int t = threadIdx.x;
+    epoch = launch_epoch(epoch, epoch_src);
     const OrderedSlot slot = ordered_slot(blockIdx.x, rows, P);
     const char* tbeg = (const char*)y;
     const char* tend = tensor_end<DT>(y, rows, cols);
@@ -378,19 +381,21 @@ static hipError_t bs(const BwdLaunch& B) {
 }
 
 template <int DT, bool AL>
-static hipError_t bo(const BwdLaunch& B, int P, uint64_t* tags, unsigned epoch) {
+static hipError_t bo(const BwdLaunch& B, int P, uint64_t* tags, unsigned epoch,
+                     const uint64_t* src) {
     hipLaunchKernelGGL((k_bwd_ordered<DT, AL, kBwdOrderedBlock, kBwdOrderedKc>),
                        dim3((unsigned)(2 * B.rows * P)), dim3(kBwdOrderedBlock), 0, B.stream, B.y,
-                       B.dy, B.dx, B.rows, B.cols, P, tags, epoch, (int)B.dy_vec,
+                       B.dy, B.dx, B.rows, B.cols, P, tags, epoch, src, (int)B.dy_vec,
                        (int)B.same_phase);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_ordered(const BwdLaunch& B, int P, uint64_t* tags, unsigned epoch) {
+hipError_t launch_bwd_ordered(const BwdLaunch& B, int P, uint64_t* tags, unsigned epoch,
+                              const uint64_t* src) {
     switch (B.dtype) {
-        case kF32: return B.aligned ? bo<kF32, true>(B, P, tags, epoch) : bo<kF32, false>(B, P, tags, epoch);
-        case kF16: return B.aligned ? bo<kF16, true>(B, P, tags, epoch) : bo<kF16, false>(B, P, tags, epoch);
-        case kBF16: return B.aligned ? bo<kBF16, true>(B, P, tags, epoch) : bo<kBF16, false>(B, P, tags, epoch);
+        case kF32: return B.aligned ? bo<kF32, true>(B, P, tags, epoch, src) : bo<kF32, false>(B, P, tags, epoch, src);
+        case kF16: return B.aligned ? bo<kF16, true>(B, P, tags, epoch, src) : bo<kF16, false>(B, P, tags, epoch, src);
+        case kBF16: return B.aligned ? bo<kBF16, true>(B, P, tags, epoch, src) : bo<kBF16, false>(B, P, tags, epoch, src);
     }
     return hipErrorInvalidValue;
 }

@@ -81,8 +81,19 @@ hipError_t splitk_fused_capacity(int variant, int dtype, bool aligned, int cus, 
 // tag buffer (never 0; the buffer starts zeroed).
 hipError_t launch_splitk_ordered(const Launch& L, int variant, int P, uint64_t* tags,
                                  unsigned epoch);
-// Zero n 64-bit words on `stream`.
-hipError_t launch_zero_words(uint64_t* p, int64_t n, hipStream_t stream);
+// Epochs of eager ordered launches are handed out by the host from
+// [1, 2^31).  In a captured graph a kernel argument would be replayed
+// unchanged, so launches recorded there take theirs from a device word that
+// a one-workgroup kernel enqueued just before advances through [2^31, 2^32).
+// The two ranges never meet, so eager and replayed launches share one tag
+// buffer on a stream.
+constexpr unsigned kDeviceEpochFirst = 0x80000000u;
+// Graph capture: advance the device epoch held in words[n] (the word after a
+// tag buffer's n words) for the next ordered launch, which then reads its
+// epoch from &words[n] (epoch_src) instead of a kernel argument.
+hipError_t launch_bump_epoch(uint64_t* words, int64_t n, hipStream_t stream);
+// Set n 64-bit words to v on `stream`.
+hipError_t launch_fill_words(uint64_t* p, int64_t n, uint64_t v, hipStream_t stream);
 // The masked forms (same variant tables; block_onepass only for variants
 // without LDS parking).
 hipError_t launch_wave_row_masked(const Launch& L, int variant, const MaskArgs& M);
@@ -112,10 +123,12 @@ extern const int kNumBwdStream;
 hipError_t launch_bwd(const BwdLaunch& B, int family, int variant);
 // Few long rows: split-k in one launch, chunks of kBwdOrderedBlock x
 // kBwdOrderedKc granules, P chunks per row; tags holds 2*rows*P epoch-tagged
-// words, epoch is unique to this launch on that buffer.
+// words, epoch is unique to this launch on that buffer (or, when epoch_src is
+// given, the launch reads it from there: see launch_bump_epoch).
 constexpr int kBwdOrderedBlock = 256;
 constexpr int kBwdOrderedKc = 4;
-hipError_t launch_bwd_ordered(const BwdLaunch& B, int P, uint64_t* tags, unsigned epoch);
+hipError_t launch_bwd_ordered(const BwdLaunch& B, int P, uint64_t* tags, unsigned epoch,
+                              const uint64_t* epoch_src = nullptr);
 // Row normalisations (rws_norm.hpp).
 constexpr int kLayerNorm = 0;
 constexpr int kRmsNorm = 1;
@@ -153,7 +166,8 @@ hipError_t launch_norm_block(const NormLaunch& L, int family, int variant);
 // Few long rows: split-k in one launch (as launch_bwd_ordered).
 constexpr int kNormOrderedBlock = 256;
 constexpr int kNormOrderedKc = 4;
-hipError_t launch_norm_ordered(const NormLaunch& L, int P, uint64_t* tags, unsigned epoch);
+hipError_t launch_norm_ordered(const NormLaunch& L, int P, uint64_t* tags, unsigned epoch,
+                               const uint64_t* epoch_src = nullptr);
 // n16 granules of 16 bytes.
 hipError_t launch_copy16(const void* in, void* out, int64_t n16, hipStream_t stream);
 

@@ -464,10 +464,13 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(AFF ? 1 :
                                                         void* __restrict__ out, int64_t rows,
                                                         int cols, NormArgs A, int P,
                                                         uint64_t* __restrict__ tags,
-                                                        unsigned epoch, int same_phase) {
+                                                        unsigned epoch,
+                                                        const uint64_t* __restrict__ epoch_src,
+                                                        int same_phase) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     constexpr int N = KC * VEC;
+    epoch = launch_epoch(epoch, epoch_src);
     using Win = RowWin<DT, ALIGNED>;
     __shared__ float sn[W];
     __shared__ float sm[W];

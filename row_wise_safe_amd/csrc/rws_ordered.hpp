@@ -9,12 +9,21 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rws_launch.hpp"
+
 namespace rws {
 
 // Tries of one poll before it gives up (each a sleep plus a load round trip:
 // at least ~0.5 s in all); the workgroup then writes NaN, so a broken
 // ordering assumption shows as NaN output, never as a hang.
 constexpr unsigned kOrderedSpinLimit = 1u << 21;
+
+// The launch's epoch: the kernel argument, or the device word at `src`
+// (launches recorded in a graph, see kDeviceEpochFirst).
+__device__ inline unsigned launch_epoch(unsigned epoch, const uint64_t* src) {
+    return src ? (unsigned)__hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+               : epoch;
+}
 
 __device__ inline uint64_t tag_word(unsigned epoch, float v) {
     return ((uint64_t)epoch << 32) | (uint64_t)__float_as_uint(v);

@@ -27,8 +27,8 @@
 //    NaN output, never as a hang.
 //
 // The epoch grows by one per launch on the same tag buffer (host side), and
-// the buffer is zero-filled when it is allocated and when the 32-bit epoch
-// wraps, so a word from an earlier launch never matches.
+// the buffer is zero-filled when it is allocated and when the host's epoch
+// range wraps, so a word from an earlier launch never matches.
 //
 // Measured on MI355X, fp16 [16, 1M] read from HBM: 14.1 us against 15.2 us
 // for the two launches (the stage-2 workgroups start while the last stage-1
@@ -98,16 +98,36 @@ __global__ __launch_bounds__(BLOCK) void k_splitk_ordered(const void* __restrict
 
 // Zero n 64-bit words (a kernel rather than a memset, so that the clear is an
 // ordinary node if a caller captures the stream into a graph).
-__global__ __launch_bounds__(256) void k_zero_words(uint64_t* __restrict__ p, int64_t n) {
+__global__ __launch_bounds__(256) void k_fill_words(uint64_t* __restrict__ p, int64_t n,
+                                                    uint64_t v) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) p[i] = 0;
+    if (i < n) p[i] = v;
 }
 
-hipError_t launch_zero_words(uint64_t* p, int64_t n, hipStream_t stream) {
+// Advance a tag buffer's device epoch (the word after its n tag words) for
+// the next launch on the stream.  When the device range is used up, the
+// buffer's words are zeroed first, so no word left from the range's last
+// pass can match a new epoch.
+__global__ __launch_bounds__(256) void k_bump_epoch(uint64_t* __restrict__ words, int64_t n) {
+    const unsigned cur = (unsigned)words[n];
+    const bool wrap = cur == 0xffffffffu;
+    if (wrap)
+        for (int64_t i = threadIdx.x; i < n; i += 256) words[i] = 0;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        words[n] = (cur < kDeviceEpochFirst || wrap) ? kDeviceEpochFirst : cur + 1;
+}
+
+hipError_t launch_bump_epoch(uint64_t* words, int64_t n, hipStream_t stream) {
+    hipLaunchKernelGGL(k_bump_epoch, dim3(1), dim3(256), 0, stream, words, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_words(uint64_t* p, int64_t n, uint64_t v, hipStream_t stream) {
     for (int64_t done = 0; done < n;) {
         const int64_t c = std::min<int64_t>(n - done, (int64_t)1 << 31);
-        hipLaunchKernelGGL(k_zero_words, dim3((unsigned)((c + 255) / 256)), dim3(256), 0, stream,
-                           p + done, c);
+        hipLaunchKernelGGL(k_fill_words, dim3((unsigned)((c + 255) / 256)), dim3(256), 0, stream,
+                           p + done, c, v);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         done += c;

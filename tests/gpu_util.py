@@ -64,3 +64,23 @@ def supports(kernel: str, cols: int, dtype: str, aligned: bool) -> bool:
         # rows that are not line-aligned: no LDS parking
         return w <= (16384 if line else 8192)
     return True
+
+
+class FreshStream:
+    """A HIP stream that no earlier call used (torch's own streams come from a
+    pool that earlier tests used, so the library may already hold a workspace
+    for them), made with the HIP runtime the library is linked against.  The
+    library keys its workspaces by stream handle, and a destroyed stream's
+    handle can come back from the next create, so these streams are kept
+    until the process ends.  Use as `with FreshStream() as s:` (s is a torch
+    ExternalStream); the exit synchronises the device."""
+
+    def __enter__(self):
+        import ctypes
+        handle = ctypes.c_void_p()
+        assert rws.load_library().hipStreamCreate(ctypes.byref(handle)) == 0
+        return torch.cuda.ExternalStream(handle.value)
+
+    def __exit__(self, *exc):
+        torch.cuda.synchronize()
+        return False

@@ -1,13 +1,16 @@
 """Graph capture and replay.  The single-launch split-k forms of the forward,
 backward and normalisations tell one launch's partials from the previous
 one's by an epoch passed as a kernel argument, which a replayed graph would
-repeat; under capture the library takes forms ordered by kernel boundaries
-instead.  Each graph is captured after an eager call on its stream (which
-sizes the split-k workspace), replayed several times on fresh input contents
-with eager library work and synchronisations between the replays, and every
-replay is checked against the CPU oracle.  Nothing in these graphs is a
-memset node (the library clears nothing while capturing)."""
-import ctypes
+repeat.  Under capture the forward takes the two-launch split-k; the
+backward and normalisations keep the single launch with an epoch that a
+recorded kernel advances in device memory on every replay (or, with no tag
+buffer on the stream yet, take one workgroup per row).  Each graph is
+captured after an eager call on its stream (which sizes the workspace),
+replayed several times on fresh input contents with eager library work and
+synchronisations between the replays, and every replay is checked against
+the CPU oracle.  Nothing in these graphs is a memset node (the library
+clears nothing while capturing)."""
+import os
 
 import numpy as np
 import pytest
@@ -15,7 +18,7 @@ import torch
 
 import oracle
 import row_wise_safe_amd as rws
-from gpu_util import TORCH_DTYPE, have_gpu
+from gpu_util import TORCH_DTYPE, FreshStream, have_gpu
 from test_gpu_backward import _check as check_backward
 from test_gpu_norm import _check as check_norm
 from tolerance import check
@@ -215,19 +218,13 @@ def test_norm_few_long_rows(mode):
 
 
 def test_capture_without_workspace_fails_cleanly():
-    # a new stream whose split-k partials were never sized (torch's own
-    # streams come from a pool that earlier tests used, so the stream is made
-    # with the HIP runtime the library is linked against): the capture reports
+    # a stream whose split-k partials were never sized: the capture reports
     # an error instead of allocating, and the stream works eagerly afterwards
-    lib = rws.load_library()
-    handle = ctypes.c_void_p()
-    assert lib.hipStreamCreate(ctypes.byref(handle)) == 0
-    try:
-        s = torch.cuda.ExternalStream(handle.value)
-        rows, cols = 16, 1 << 20
-        x, y = _dev(rows, cols, "f16"), _dev(rows, cols, "f16")
-        stored = _fill(x, _host(rows, cols, 370))
-        torch.cuda.synchronize()
+    rows, cols = 16, 1 << 20
+    x, y = _dev(rows, cols, "f16"), _dev(rows, cols, "f16")
+    stored = _fill(x, _host(rows, cols, 370))
+    torch.cuda.synchronize()
+    with FreshStream() as s:
         g = torch.cuda.CUDAGraph()
         with pytest.raises(rws.SoftmaxError, match="graph capture"):
             with torch.cuda.graph(g, stream=s):
@@ -239,6 +236,55 @@ def test_capture_without_workspace_fails_cleanly():
         torch.cuda.synchronize()
         check(y.double().cpu().numpy(), oracle.safe_softmax(stored), "f16",
               "eager after failed capture")
+
+
+def test_backward_capture_without_tag_buffer():
+    # no tag buffer on the stream: the captured backward takes one workgroup
+    # per row and needs no workspace at all
+    rows, cols, dtype = 16, 300000, "f16"
+    y, dy, dx = _dev(rows, cols, dtype), _dev(rows, cols, dtype), _dev(rows, cols, dtype)
+    with FreshStream() as s:
+        g = _capture(lambda: rws.softmax_backward(y, dy, out=dx), s)
+        for i in range(REPLAYS):
+            sy = _fill(y, oracle.safe_softmax(_host(rows, cols, 380 + i)))
+            sdy = _fill(dy, _host(rows, cols, 385 + i, sigma=1.0))
+            dx.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            check_backward(dx.double().cpu().numpy(), sy, sdy, dtype,
+                           f"replay {i} of a backward captured without tags")
+
+
+def test_device_epoch_wrap():
+    # a fresh tag buffer whose device epoch starts 3 below the end of its
+    # range (test hook read at allocation): replays 3 and on cross the end,
+    # where the recorded kernel zeroes the tag words and restarts the range;
+    # eager ordered calls on the same buffer run between the replays
+    rows, cols, dtype = 16, 300000, "f16"
+    y, dy, dx = _dev(rows, cols, dtype), _dev(rows, cols, dtype), _dev(rows, cols, dtype)
+    x, out = _dev(rows, cols, dtype), _dev(rows, cols, dtype)
+    os.environ["RWS_TEST_DEVICE_EPOCH"] = str(0xFFFFFFFF - 3)
+    try:
+        with FreshStream() as s:
+            with torch.cuda.stream(s):
+                sy = _fill(y, oracle.safe_softmax(_host(rows, cols, 390)))
+                sdy = _fill(dy, _host(rows, cols, 391, sigma=1.0))
+                rws.softmax_backward(y, dy, out=dx)  # allocates the tag buffer
+            torch.cuda.synchronize()
+            g = _capture(lambda: rws.softmax_backward(y, dy, out=dx), s)
+            for i in range(8):
+                sy = _fill(y, oracle.safe_softmax(_host(rows, cols, 392 + i)))
+                sdy = _fill(dy, _host(rows, cols, 400 + i, sigma=1.0))
+                dx.fill_(float("nan"))
+                g.replay()
+                torch.cuda.synchronize()
+                check_backward(dx.double().cpu().numpy(), sy, sdy, dtype,
+                               f"replay {i} across the device epoch wrap")
+                with torch.cuda.stream(s):
+                    sx = _fill(x, _host(rows, cols, 410 + i))
+                    rws.layer_norm(x, 1e-5, out=out)
+                torch.cuda.synchronize()
+                check_norm("layernorm", dtype, out.double().cpu().numpy(), sx, 1e-5, None, None,
+                           f"eager LayerNorm after replay {i}")
     finally:
-        torch.cuda.synchronize()
-        lib.hipStreamDestroy(handle)
+        del os.environ["RWS_TEST_DEVICE_EPOCH"]

@@ -12,7 +12,7 @@ import torch
 import oracle
 import row_wise_safe_amd as rws
 import workloads
-from gpu_util import have_gpu, to_device
+from gpu_util import FreshStream, have_gpu, to_device
 from tolerance import check
 
 pytestmark = [pytest.mark.gpu,
@@ -104,46 +104,47 @@ def test_several_launches_in_one_call():
 
 
 def test_epoch_wrap():
-    # A fresh stream gets a fresh tag buffer whose epochs start 5 below the
-    # 32-bit wrap (test hook read at allocation); 12 calls cross the wrap,
-    # where the library zeroes the words and restarts at epoch 1.
-    s = torch.cuda.Stream()
+    # A fresh stream gets a fresh tag buffer whose host epochs start 5 below
+    # the end of their range [1, 2^31) (test hook read at allocation); 12
+    # calls cross the end, where the library zeroes the words and restarts at
+    # epoch 1.
     shapes = [(16, 65536 + 7), (4, 200000), (16, 65536 + 7)]
     cases = []
     for i, (r, c) in enumerate(shapes):
         x, stored = _x(r, c, seed=120 + i)
         cases.append((x, stored, oracle.safe_softmax(stored)))
     torch.cuda.synchronize()
-    os.environ["RWS_TEST_TAG_EPOCH"] = str(0xFFFFFFFF - 5)
+    os.environ["RWS_TEST_TAG_EPOCH"] = str(0x7FFFFFFF - 5)
     try:
-        for k in range(12):
-            x, _, ref = cases[k % len(cases)]
-            y = torch.empty_like(x)
-            with torch.cuda.stream(s):
-                rws.softmax(x, out=y, kernel="splitk_ordered")
-            s.synchronize()
-            check(y.double().cpu().numpy(), ref, "f16", f"call {k} across the epoch wrap")
+        with FreshStream() as s:
+            for k in range(12):
+                x, _, ref = cases[k % len(cases)]
+                y = torch.empty_like(x)
+                with torch.cuda.stream(s):
+                    rws.softmax(x, out=y, kernel="splitk_ordered")
+                s.synchronize()
+                check(y.double().cpu().numpy(), ref, "f16", f"call {k} across the epoch wrap")
     finally:
         del os.environ["RWS_TEST_TAG_EPOCH"]
 
 
 def test_workspace_allocation_failure_is_reported():
-    s = torch.cuda.Stream()  # a stream with no tag words yet
     x, stored = _x(4, 400000, seed=130)
     y = torch.empty_like(x)
     torch.cuda.synchronize()
-    os.environ["RWS_TEST_FAIL_ALLOC"] = "1"
-    try:
-        st = rws.softmax_fwd_kernel(x.data_ptr(), y.data_ptr(), 4, 400000, rws.RWS_F16,
-                                    int(s.cuda_stream), rws.KERNEL_IDS["splitk_ordered"])
-        assert st == rws.RWS_ERR_HIP
-        assert "workspace" in rws.softmax_last_error()
-    finally:
-        del os.environ["RWS_TEST_FAIL_ALLOC"]
-    with torch.cuda.stream(s):
-        rws.softmax(x, out=y, kernel="splitk_ordered")
-    s.synchronize()
-    check(y.double().cpu().numpy(), oracle.safe_softmax(stored), "f16", "after failure")
+    with FreshStream() as s:  # a stream with no workspace yet
+        os.environ["RWS_TEST_FAIL_ALLOC"] = "1"
+        try:
+            st = rws.softmax_fwd_kernel(x.data_ptr(), y.data_ptr(), 4, 400000, rws.RWS_F16,
+                                        int(s.cuda_stream), rws.KERNEL_IDS["splitk_ordered"])
+            assert st == rws.RWS_ERR_HIP
+            assert "workspace" in rws.softmax_last_error()
+        finally:
+            del os.environ["RWS_TEST_FAIL_ALLOC"]
+        with torch.cuda.stream(s):
+            rws.softmax(x, out=y, kernel="splitk_ordered")
+        s.synchronize()
+        check(y.double().cpu().numpy(), oracle.safe_softmax(stored), "f16", "after failure")
 
 
 def test_many_chunks_keep_two_launches():
