@@ -45,6 +45,8 @@
  * counters and tag words are zeroed then, the tag words by a kernel on the
  * call's stream), later calls reuse it.  Calls on one stream are ordered, so
  * reuse is safe; the workspaces are released when the library is unloaded.
+ * They are keyed by the stream handle: a destroyed stream's workspace stays
+ * allocated, and a stream created later with the same handle reuses it.
  *
  * Graph capture.  Every entry point may be captured into a HIP graph.  The
  * single-launch split-k forms tell one launch's partials from the last by an
