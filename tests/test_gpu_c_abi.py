@@ -1,7 +1,7 @@
 """The library through its C ABI alone: tests/c_abi/check_c_abi.c (plain C,
 hipMalloc'd buffers, a stream of its own, no Python or torch) runs softmax
-forward (fp32 and bf16, from the two-element-row example to the split-k
-shape), the backward and LayerNorm, compares every output with the CPU oracle
+forward (fp32 and bf16, from a [2, 3] tensor whose second row starts off
+a 16-byte boundary to the split-k shape), the backward and LayerNorm, compares every output with the CPU oracle
 under the same bounds as the Python parity tests, and checks the error
 statuses of bad arguments.  The binary is built by the package build."""
 import os
