@@ -315,6 +315,8 @@ def main() -> int:
     ap.add_argument("--affine", action="store_true",
                     help="with --norm: per-column weight and bias (LayerNorm) or weight (RMSNorm), "
                          "read once per call")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the calls replayed from a HIP graph (no host-side cost)")
     ap.add_argument("--skip-hot", action="store_true",
                     help="skip the single-buffer figure (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -420,7 +422,7 @@ def main() -> int:
         desc += " affine"
     log(f"[bench] launch: {desc}; {nbuf} rotating buffer pairs")
 
-    def step(i):
+    def step(i, sh=sh):
         if args.norm == "layernorm":
             st = rws.layernorm_fwd_kernel(xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), w.rows,
                                           w.cols, code, 1e-5, wptr, bptr, 0, 0, sh, kid)
@@ -480,6 +482,39 @@ def main() -> int:
         hot_ms = e0.elapsed_time(e1) / hot_steps
         hot = {"us_per_call": round(hot_ms * 1e3, 3),
                "GBps": round(nbytes / (hot_ms * 1e-3) / 1e9, 2)}
+
+    # the same calls replayed from a HIP graph (one graph of gcalls calls over
+    # the rotating buffers, captured on a stream of its own after eager calls
+    # there): the per-call time without host-side cost
+    graph = None
+    if args.graph:
+        gstream = torch.cuda.Stream(device=dev)
+        gsh = int(gstream.cuda_stream)
+        gcalls = 256
+        with torch.cuda.stream(gstream):
+            for i in range(nbuf):
+                step(i, gsh)  # sizes any split-k workspace of this stream
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gstream):
+            for i in range(gcalls):
+                step(i, gsh)
+        reps = max(2, args.steps // gcalls)
+        with torch.cuda.stream(gstream):
+            for _ in range(3):
+                g.replay()
+            gstream.synchronize()
+            e0.record(gstream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(gstream)
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / (reps * gcalls)
+        graph = {"us_per_call": round(graph_ms * 1e3, 3),
+                 "GBps": round(nbytes / (graph_ms * 1e-3) / 1e9, 2),
+                 "calls_per_graph": gcalls, "replays": reps}
+        log(f"[bench] graph replay {graph_ms * 1e3:.2f} us/call")
+        del g
 
     # copy ceiling: 16-byte copy of the input bytes, same rotation
     for i in range(args.warmup):
@@ -563,6 +598,7 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": traffic},
         "hot_single_buffer": hot,
+        "graph_replay": graph,
         "copy_ceiling": {"us_per_call": round(copy_ms * 1e3, 3), "GBps": round(copy_gbps, 2),
                          "frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4)},
         "hip_memcpy_dtod": {"us_per_call": round(memcpy_ms * 1e3, 3),
