@@ -288,3 +288,59 @@ def test_device_epoch_wrap():
                            f"eager LayerNorm after replay {i}")
     finally:
         del os.environ["RWS_TEST_DEVICE_EPOCH"]
+
+
+def _dev_at(rows, cols, dtype, offset):
+    """[rows, cols] view `offset` elements into a fresh buffer (offset 1: no
+    row starts on a 16-byte boundary)."""
+    buf = torch.empty(rows * cols + offset, dtype=TORCH_DTYPE[dtype], device="cuda")
+    return buf[offset:].view(rows, cols)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_captured_ordered_dtypes(dtype, offset):
+    # the captured ordered backward and RMSNorm (device epochs) in every dtype,
+    # on line-aligned and unaligned rows, replays interleaved with eager
+    # ordered calls of both on the same tag buffer
+    rows = 8
+    cols = 200064 if offset == 0 else 200001  # line-aligned rows / no row on a 16-byte boundary
+    y, dy, dx = (_dev_at(rows, cols, dtype, offset) for _ in range(3))
+    x, out = _dev_at(rows, cols, dtype, offset), _dev_at(rows, cols, dtype, offset)
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    code = rws.dtype_code(TORCH_DTYPE[dtype])
+    assert rws.softmax_bwd_describe_launch(rows, cols, code, y.data_ptr(), dx.data_ptr()) \
+        .startswith("bwd_ordered")
+    assert rws.norm_describe_launch(rows, cols, code, x.data_ptr(), out.data_ptr()) \
+        .startswith("norm_ordered")
+    s = torch.cuda.Stream()
+
+    def call():
+        rws.softmax_backward(y, dy, out=dx)
+        rws.rms_norm(x, 1e-5, out=out, rstd=rstd)
+
+    with torch.cuda.stream(s):
+        _fill(y, oracle.safe_softmax(_host(rows, cols, 420)))
+        _fill(dy, _host(rows, cols, 421, sigma=1.0))
+        _fill(x, _host(rows, cols, 422))
+        call()
+    torch.cuda.synchronize()
+    g = _capture(call, s)
+    for i in range(REPLAYS):
+        sy = _fill(y, oracle.safe_softmax(_host(rows, cols, 423 + i, sigma=2.0)))
+        sdy = _fill(dy, _host(rows, cols, 430 + i, sigma=1.0))
+        sx = _fill(x, 1.0 + _host(rows, cols, 440 + i))
+        dx.fill_(float("nan"))
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        what = f"{dtype} offset {offset} replay {i}"
+        check_backward(dx.double().cpu().numpy(), sy, sdy, dtype, f"backward {what}")
+        check_norm("rmsnorm", dtype, out.double().cpu().numpy(), sx, 1e-5, None, None,
+                   f"rmsnorm {what}", rstd=rstd.double().cpu().numpy())
+        with torch.cuda.stream(s):  # eager ordered calls on the same tag words
+            call()
+        torch.cuda.synchronize()
+        check_backward(dx.double().cpu().numpy(), sy, sdy, dtype, f"eager backward {what}")
+        check_norm("rmsnorm", dtype, out.double().cpu().numpy(), sx, 1e-5, None, None,
+                   f"eager rmsnorm {what}", rstd=rstd.double().cpu().numpy())
