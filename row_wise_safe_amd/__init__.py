@@ -304,8 +304,9 @@ def softmax_masked(x: torch.Tensor, scale: float = 1.0, mask: torch.Tensor | Non
     code = dtype_code(x.dtype)
     if out is None:
         out = torch.empty_like(x)
-    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor of x's shape and dtype")
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or \
+            out.device != x.device:
+        raise ValueError("out must be a contiguous tensor of x's shape, dtype and device")
     cols = x.shape[-1] if x.dim() > 0 else 1
     rows = x.numel() // cols if cols > 0 else 0
     mask_ptr, mask_rows = None, 0

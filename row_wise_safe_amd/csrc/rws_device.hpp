@@ -371,7 +371,8 @@ struct RowWin {
 // exp(x - m) for one row.  With c = round(m * log2 e), the FMA
 // x*log2e - c is exact before its single rounding, so the error is relative
 // to |x - m| and the common offset delta = m*log2e - c cancels in the
-// normalisation.  delta is at most half an ulp of c, so the form is used only
+// normalisation of a row taken against one maximum (sums taken against
+// different maxima are merged with merge_scale, which accounts for it).  delta is at most half an ulp of c, so the form is used only
 // while |c| < 2^22 (|m| < 2.9e6, delta <= 1/8, far from over/underflowing
 // exp2).  Rows with a larger |m| -- possible in fp32 and bf16, and for the
 // running max of a thread that has only seen masked entries -- or with
@@ -406,13 +407,29 @@ struct RowExp {
     }
 };
 
-// Scale factor e^(m_part - M) for merging a partial (m_part, d) into the row
-// maximum M; exactly 1 when m_part == M (this also covers -inf == -inf, so
-// the (-inf, 0) identity never produces NaN).
+// Scale factor for merging a partial sum d_part, accumulated as
+// sum 2^(x*log2e - off(m_part)) by RowExp(m_part), into a sum taken against
+// the larger maximum M:  2^(off(m_part) - off(M)).  The offset each RowExp
+// subtracts is off(m) = c = fl(m*log2e) on the FMA path and the exact
+// m*log2e on the `big` path; c differs from m*log2e by the product's rounding
+// error delta = m*log2e - c, which an FMA gives exactly.  A single maximum
+// lets delta cancel between the sum and the outputs, but partials taken
+// against different maxima each carry their own 2^delta (up to 2^(1/8) for
+// |m*log2e| near 2^22), so the merge uses the offsets actually subtracted:
+//   both on the FMA path:  2^(c_part - c_M)         (exact difference of the c's,
+//                                                    rounded once)
+//   otherwise:             2^((m_part - M)*log2e - delta_part + delta_M)
+// (delta = 0 on the big path).  Exactly 1 when m_part == M, which also covers
+// -inf == -inf, so the (-inf, 0) identity never produces NaN; 0 for a partial
+// that saw only -inf under a larger maximum.
 __device__ inline float merge_scale(float m_part, float M) {
     if (m_part == M) return 1.0f;
-    RowExp er(M);
-    return er.one(m_part);
+    if (m_part == kNegInf) return 0.0f;
+    const RowExp ep(m_part), eM(M);
+    if (!ep.big && !eM.big) return __builtin_amdgcn_exp2f(eM.negc - ep.negc);
+    const float dp = ep.big ? 0.0f : __builtin_fmaf(m_part, kLog2e, ep.negc);
+    const float dM = eM.big ? 0.0f : __builtin_fmaf(M, kLog2e, eM.negc);
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(m_part - M, kLog2e, dM - dp));
 }
 
 // ---------------------------------------------------------------------------

@@ -373,6 +373,7 @@ __global__ __launch_bounds__(BLOCK) void k_block_onepass_raw(const void* __restr
 // ===========================================================================
 // Running (m, d) of one thread over a batch of N values (-inf entries add 0):
 //   m' = max(m, max batch);  d' = d e^(m - m') + sum e^(x - m')
+// with d kept against RowExp(m)'s offset and rescaled by merge_scale.
 // (DCU case-study page, section 4.3; CUDA safe-online-softmax page, section 1,
 // there per chunk of 256).
 // ===========================================================================
@@ -387,7 +388,7 @@ __device__ inline void online_update(float& m, float& d, const float (&v)[N]) {
         float s = 0.0f;
 #pragma unroll
         for (int j = 0; j < N; ++j) s += er.one(v[j]);
-        d = d * ((m == mn) ? 1.0f : er.one(m)) + s;
+        d = d * merge_scale(m, mn) + s;
         m = mn;
     }
 }

@@ -120,3 +120,17 @@ def test_long_rows_masked_use_two_pass():
     assert rws.softmax_describe_launch(3, 300001, rws.RWS_F16, x.data_ptr(), x.data_ptr()) \
         .startswith("splitk")
     check(_masked(x, 0.5, None, 0, "auto"), oracle.masked_softmax(xs, 0.5, None, 0), "f16", "auto")
+
+
+def test_out_on_the_host_is_rejected_before_any_launch():
+    # a host tensor's pointer handed to a kernel would fault the GPU: every
+    # tensor-level entry point checks out's device first
+    x = torch.zeros(4, 64, dtype=torch.float16, device="cuda")
+    host = torch.empty(4, 64, dtype=torch.float16)
+    for call in (lambda: rws.softmax_masked(x, 0.5, out=host),
+                 lambda: rws.softmax(x, out=host),
+                 lambda: rws.softmax_backward(x, x, out=host),
+                 lambda: rws.layer_norm(x, out=host),
+                 lambda: rws.rms_norm(x, out=host)):
+        with pytest.raises(ValueError):
+            call()
