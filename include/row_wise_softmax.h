@@ -92,7 +92,9 @@ enum {
     RWS_ERR_UNSUPPORTED_DTYPE = 2, /* dtype not one of RWS_F32/F16/BF16 */
     RWS_ERR_MISALIGNED = 3,        /* pointer not aligned to the element size */
     RWS_ERR_HIP = 4,               /* HIP runtime error (see softmax_last_error) */
-    RWS_ERR_UNSUPPORTED_SHAPE = 5  /* forced kernel cannot take this shape */
+    RWS_ERR_UNSUPPORTED_SHAPE = 5, /* forced kernel cannot take this shape */
+    RWS_ERR_WAIT_TIMEOUT = 6       /* softmax_stream_status: a single-launch
+                                      split-k wait gave up (outputs NaN) */
 };
 
 /* Kernel families (ids for softmax_fwd_kernel / softmax_select_kernel). */
@@ -133,10 +135,13 @@ enum {
                                  barrier, no memory fence; the single-kernel
                                  form the same page, section 3.2, mentions).
                                  Relies on workgroups being dispatched in
-                                 increasing index order; a wait that runs
-                                 out of its bound writes NaN for its chunk
-                                 instead of hanging.  The dispatcher's choice
-                                 for few long rows */
+                                 increasing index order (within each XCD,
+                                 which the hardware does but HIP does not
+                                 promise); a wait that runs out of its bound
+                                 writes NaN for its chunk instead of hanging
+                                 and sets the stream's status word, which
+                                 softmax_stream_status reports.  The
+                                 dispatcher's choice for few long rows */
 };
 
 /*
@@ -325,6 +330,31 @@ const char *softmax_status_string(int status);
 
 /* Detail of the last error on this thread ("" if none). */
 const char *softmax_last_error(void);
+
+/*
+ * softmax_stream_status -- whether a single-launch split-k launch on `stream`
+ * (RWS_KERNEL_SPLITK_ORDERED of softmax_fwd, softmax_bwd, layernorm_fwd and
+ * rmsnorm_fwd, or RWS_KERNEL_SPLITK_FUSED) gave up waiting for its row's
+ * partials since the last query.  Such a launch cannot report through the
+ * call that enqueued it (the kernel runs after the call returns): its
+ * workgroup writes NaN for its chunk and sets a status word of the stream's,
+ * which this call reads.  It synchronises `stream`, reads and clears the
+ * word, and returns RWS_OK, or RWS_ERR_WAIT_TIMEOUT with the detail in
+ * softmax_last_error(), or RWS_ERR_HIP.  A stream that never ran such a
+ * launch gives RWS_OK at once.  Not for use while `stream` is being
+ * captured into a graph (it synchronises).
+ */
+int softmax_stream_status(void *stream);
+
+/*
+ * softmax_set_wait_limit -- tries of one poll of the single-launch split-k
+ * forms before a wait gives up, for launches enqueued after this call from
+ * any thread: `tries` >= 0 (0 gives up at once, so every stage-2 workgroup
+ * writes NaN and reports; for tests of the reporting path), or < 0 for the
+ * default (2^21 tries, at least ~0.5 s).  Returns RWS_OK, or
+ * RWS_ERR_INVALID_ARG above 2^32 - 1.  No GPU work.
+ */
+int softmax_set_wait_limit(int64_t tries);
 
 /*
  * softmax_copy_bytes -- plain device-to-device copy of `bytes` bytes with

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "RWS_F32", "RWS_F16", "RWS_BF16",
     "RWS_OK", "RWS_ERR_INVALID_ARG", "RWS_ERR_UNSUPPORTED_DTYPE", "RWS_ERR_MISALIGNED",
-    "RWS_ERR_HIP", "RWS_ERR_UNSUPPORTED_SHAPE",
+    "RWS_ERR_HIP", "RWS_ERR_UNSUPPORTED_SHAPE", "RWS_ERR_WAIT_TIMEOUT",
     "KERNELS", "KERNEL_IDS",
     "library_path", "load_library",
     "softmax_fwd", "softmax_fwd_kernel", "softmax_fwd_masked", "softmax_bwd",
@@ -32,6 +32,7 @@ __all__ = [
     "norm_describe_launch",
     "softmax_bwd_describe_launch",
     "softmax_kernel_name", "softmax_status_string", "softmax_last_error", "softmax_copy_bytes",
+    "softmax_stream_status", "softmax_set_wait_limit", "stream_status",
     "layernorm_fwd", "layernorm_fwd_kernel", "rmsnorm_fwd", "rmsnorm_fwd_kernel",
     "softmax", "softmax_masked", "softmax_backward", "layer_norm", "rms_norm", "copy_bytes",
     "dtype_code", "SoftmaxError",
@@ -44,6 +45,7 @@ RWS_ERR_UNSUPPORTED_DTYPE = 2
 RWS_ERR_MISALIGNED = 3
 RWS_ERR_HIP = 4
 RWS_ERR_UNSUPPORTED_SHAPE = 5
+RWS_ERR_WAIT_TIMEOUT = 6
 
 KERNEL_IDS = {"auto": 0, "wave_row": 1, "block_onepass": 2, "two_pass": 3, "splitk": 4,
               "splitk_fused": 5, "splitk_ordered": 6}
@@ -108,6 +110,10 @@ def load_library():
     lib.softmax_last_error.restype = ctypes.c_char_p
     lib.softmax_copy_bytes.argtypes = [vp, vp, i64, vp]
     lib.softmax_copy_bytes.restype = cint
+    lib.softmax_stream_status.argtypes = [vp]
+    lib.softmax_stream_status.restype = cint
+    lib.softmax_set_wait_limit.argtypes = [i64]
+    lib.softmax_set_wait_limit.restype = cint
     f32 = ctypes.c_float
     lib.layernorm_fwd.argtypes = [vp, vp, i64, i64, cint, f32, vp, vp, vp, vp, vp]
     lib.layernorm_fwd.restype = cint
@@ -240,6 +246,14 @@ def softmax_last_error() -> str:
 
 def softmax_copy_bytes(in_ptr: int, out_ptr: int, nbytes: int, stream: int) -> int:
     return load_library().softmax_copy_bytes(in_ptr, out_ptr, nbytes, stream)
+
+
+def softmax_stream_status(stream: int) -> int:
+    return load_library().softmax_stream_status(stream)
+
+
+def softmax_set_wait_limit(tries: int) -> int:
+    return load_library().softmax_set_wait_limit(tries)
 
 
 # --- tensor convenience -----------------------------------------------------
@@ -433,3 +447,15 @@ def copy_bytes(src: torch.Tensor, dst: torch.Tensor, stream=None) -> torch.Tenso
     if st != RWS_OK:
         raise SoftmaxError(st, softmax_last_error())
     return dst
+
+
+def stream_status(device=None, stream=None) -> None:
+    """Raise SoftmaxError if a single-launch split-k call on ``stream``
+    (default: the current stream of ``device``) gave up waiting since the
+    last check (its outputs are NaN); synchronises that stream."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None \
+        else torch.device(device)
+    with torch.cuda.device(dev):
+        st = load_library().softmax_stream_status(_stream_handle(dev, stream))
+    if st != RWS_OK:
+        raise SoftmaxError(st, softmax_last_error())

@@ -24,6 +24,7 @@
 #include <mutex>
 #include <string>
 #include <algorithm>
+#include <atomic>
 #include <utility>
 
 #include "row_wise_softmax.h"
@@ -492,8 +493,13 @@ struct Workspace {
     unsigned tag_epoch = 0;     // last epoch used on `tags`
     bool captured = false;      // `ptr` is baked into a captured graph
     bool tags_captured = false; // `tags` is baked into a captured graph
+    uint64_t* status = nullptr; // give-up status word of the single-launch
+                                // forms (allocated once, kept until unload)
     std::vector<void*> retired; // buffers that graphs may still use
 };
+
+// Tries of one poll of the ordered forms (softmax_set_wait_limit).
+std::atomic<unsigned> g_wait_limit{rws::kOrderedSpinLimit};
 
 // Words after a tag buffer's tag words: the device epoch of launches replayed
 // from graphs (rws_ordered.hpp), padded to a 128-byte line.
@@ -511,6 +517,7 @@ struct WorkspaceReaper {
             if (kv.second.ptr) (void)hipFree(kv.second.ptr);
             if (kv.second.sync) (void)hipFree(kv.second.sync);
             if (kv.second.tags) (void)hipFree(kv.second.tags);
+            if (kv.second.status) (void)hipFree(kv.second.status);
             for (void* p : kv.second.retired) (void)hipFree(p);
         }
         delete g_ws;
@@ -534,6 +541,32 @@ bool capturing(hipStream_t s) {
         return false;
     }
     return st != hipStreamCaptureStatusNone;
+}
+
+// The give-up status word of (device, stream) (see rws::OrderedSync): one
+// 128-byte line, zeroed by a kernel on `stream` when it is allocated on the
+// stream's first single-launch split-k call, never moved, so launches that
+// a graph recorded keep reporting into it.  nullptr when it does not exist
+// yet and `cap` (nothing may be allocated while capturing; the launch then
+// still writes NaN, it only cannot report).  The caller holds g_ws_mu.
+int get_status_word(hipStream_t stream, bool cap, uint64_t** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RWS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (!g_ws) g_ws = new std::map<std::pair<int, hipStream_t>, Workspace>();
+    Workspace& w = (*g_ws)[std::make_pair(dev, stream)];
+    if (!w.status && !cap) {
+        uint64_t* p = nullptr;
+        e = hipMalloc((void**)&p, 128);
+        if (e == hipSuccess) e = rws::launch_fill_words(p, 16, 0, stream);
+        if (e != hipSuccess) {
+            if (p) (void)hipFree(p);
+            return fail(RWS_ERR_HIP, std::string("status word: ") + hipGetErrorString(e));
+        }
+        w.status = p;
+    }
+    *out = w.status;
+    return RWS_OK;
 }
 
 // Grow-only workspace of (device, stream): `bytes` of partials and, when
@@ -807,6 +840,12 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
         st = get_tag_workspace(s, 2 * batch * p.P, launches, &tags, &epoch);
         if (st != RWS_OK) return st;
     }
+    uint64_t* status = nullptr;
+    if (p.family == RWS_KERNEL_SPLITK_FUSED || p.family == RWS_KERNEL_SPLITK_ORDERED) {
+        st = get_status_word(s, cap, &status);
+        if (st != RWS_OK) return st;
+    }
+    const unsigned wait_limit = g_wait_limit.load(std::memory_order_relaxed);
     const int64_t row_bytes = cols * elem_size(dtype);
     for (int64_t r0 = 0; r0 < rows; r0 += p.max_rows_per_launch) {
         rws::Launch L;
@@ -841,12 +880,15 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
                     e = rws::launch_splitk(L, p.variant, p.P, (float2*)ws);
                     break;
                 case RWS_KERNEL_SPLITK_FUSED:
-                    e = rws::launch_splitk_fused(L, p.variant, p.P, (float2*)ws, sync, epoch);
+                    e = rws::launch_splitk_fused(L, p.variant, p.P, (float2*)ws, sync, epoch,
+                                                 status);
                     break;
                 case RWS_KERNEL_SPLITK_ORDERED:
                     // one epoch per launch: the batches reuse the same tag words
-                    e = rws::launch_splitk_ordered(L, p.variant, p.P, tags,
-                                                   epoch + (unsigned)(r0 / p.max_rows_per_launch));
+                    e = rws::launch_splitk_ordered(
+                        L, p.variant, p.P,
+                        rws::OrderedSync{tags, epoch + (unsigned)(r0 / p.max_rows_per_launch),
+                                         nullptr, status, wait_limit});
                     break;
             }
         }
@@ -1017,6 +1059,7 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
     uint64_t* tags = nullptr;
     unsigned epoch = 0;
     int64_t tag_n = 0;  // captured: epochs come from tags[tag_n]
+    uint64_t* status = nullptr;
     if (bp.family == RWS_KERNEL_SPLITK_ORDERED) {
         ws_lock.lock();
         const int64_t words = 2 * std::min(rows, bp.max_rows) * bp.P;
@@ -1025,13 +1068,18 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
                 ws_lock.unlock();
                 st = plan_bwd(rows, cols, dtype, y, dx, kernel_id, &bp, false);
                 if (st != RWS_OK) return st;
+            } else if ((st = get_status_word((hipStream_t)stream, true, &status)) != RWS_OK) {
+                return st;
             }
         } else {
             const int64_t launches = (rows + bp.max_rows - 1) / bp.max_rows;
             st = get_tag_workspace((hipStream_t)stream, words, launches, &tags, &epoch);
             if (st != RWS_OK) return st;
+            st = get_status_word((hipStream_t)stream, false, &status);
+            if (st != RWS_OK) return st;
         }
     }
+    const unsigned wait_limit = g_wait_limit.load(std::memory_order_relaxed);
     const int family = bp.family, variant = bp.variant;
     const int64_t max_rows = bp.max_rows;
     const int64_t row_bytes = cols * elem_size(dtype);
@@ -1052,9 +1100,13 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
         if (family != RWS_KERNEL_SPLITK_ORDERED)
             e = rws::launch_bwd(B, family, variant);
         else if (tag_n == 0)
-            e = rws::launch_bwd_ordered(B, bp.P, tags, epoch + (unsigned)(r0 / max_rows));
+            e = rws::launch_bwd_ordered(
+                B, bp.P,
+                rws::OrderedSync{tags, epoch + (unsigned)(r0 / max_rows), nullptr, status,
+                                 wait_limit});
         else if ((e = rws::launch_bump_epoch(tags, tag_n, B.stream)) == hipSuccess)
-            e = rws::launch_bwd_ordered(B, bp.P, tags, 0, tags + tag_n);
+            e = rws::launch_bwd_ordered(
+                B, bp.P, rws::OrderedSync{tags, 0, tags + tag_n, status, wait_limit});
         if (e != hipSuccess)
             return fail(RWS_ERR_HIP, std::string("backward launch: ") + hipGetErrorString(e));
     }
@@ -1215,6 +1267,7 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
     uint64_t* tags = nullptr;
     unsigned epoch = 0;
     int64_t tag_n = 0;  // captured: epochs come from tags[tag_n]
+    uint64_t* status = nullptr;
     if (np.family == RWS_KERNEL_SPLITK_ORDERED) {
         ws_lock.lock();
         const int64_t words = 2 * std::min(rows, np.max_rows) * np.P;
@@ -1223,13 +1276,18 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
                 ws_lock.unlock();
                 st = plan_norm(rows, cols, dtype, in, out, weight || bias, kernel_id, &np, false);
                 if (st != RWS_OK) return st;
+            } else if ((st = get_status_word((hipStream_t)stream, true, &status)) != RWS_OK) {
+                return st;
             }
         } else {
             const int64_t launches = (rows + np.max_rows - 1) / np.max_rows;
             st = get_tag_workspace((hipStream_t)stream, words, launches, &tags, &epoch);
             if (st != RWS_OK) return st;
+            st = get_status_word((hipStream_t)stream, false, &status);
+            if (st != RWS_OK) return st;
         }
     }
+    const unsigned wait_limit = g_wait_limit.load(std::memory_order_relaxed);
     const int family = np.family, variant = np.variant;
     const int64_t max_rows = np.max_rows;
     const int64_t row_bytes = cols * es;
@@ -1262,9 +1320,13 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
         else if (family != RWS_KERNEL_SPLITK_ORDERED)
             e = rws::launch_norm_block(L, family, variant);
         else if (tag_n == 0)
-            e = rws::launch_norm_ordered(L, np.P, tags, epoch + (unsigned)(r0 / max_rows));
+            e = rws::launch_norm_ordered(
+                L, np.P,
+                rws::OrderedSync{tags, epoch + (unsigned)(r0 / max_rows), nullptr, status,
+                                 wait_limit});
         else if ((e = rws::launch_bump_epoch(tags, tag_n, L.stream)) == hipSuccess)
-            e = rws::launch_norm_ordered(L, np.P, tags, 0, tags + tag_n);
+            e = rws::launch_norm_ordered(
+                L, np.P, rws::OrderedSync{tags, 0, tags + tag_n, status, wait_limit});
         if (e != hipSuccess)
             return fail(RWS_ERR_HIP, std::string("normalisation launch: ") + hipGetErrorString(e));
     }
@@ -1512,11 +1574,55 @@ const char* softmax_status_string(int status) {
         case RWS_ERR_MISALIGNED: return "pointer misaligned for its element size";
         case RWS_ERR_HIP: return "HIP runtime error";
         case RWS_ERR_UNSUPPORTED_SHAPE: return "shape not supported by the requested kernel";
+        case RWS_ERR_WAIT_TIMEOUT:
+            return "a single-launch split-k wait gave up; its outputs are NaN";
     }
     return "unknown status";
 }
 
 const char* softmax_last_error(void) { return g_last_error.c_str(); }
+
+int softmax_set_wait_limit(int64_t tries) {
+    g_last_error.clear();
+    if (tries > (int64_t)0xffffffffu) return fail(RWS_ERR_INVALID_ARG, "tries above 2^32 - 1");
+    g_wait_limit.store(tries < 0 ? rws::kOrderedSpinLimit : (unsigned)tries,
+                       std::memory_order_relaxed);
+    return RWS_OK;
+}
+
+int softmax_stream_status(void* stream) {
+    g_last_error.clear();
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RWS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    uint64_t* status = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_ws_mu);
+        if (g_ws) {
+            auto it = g_ws->find(std::make_pair(dev, (hipStream_t)stream));
+            if (it != g_ws->end()) status = it->second.status;
+        }
+    }
+    if (!status) return RWS_OK;  // no single-launch split-k call on this stream yet
+    e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(RWS_ERR_HIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+    uint64_t v = 0;
+    e = hipMemcpy(&v, status, sizeof v, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && v != 0) {
+        // clear it for the next query (a kernel on the stream, then wait)
+        e = rws::launch_fill_words(status, 1, 0, (hipStream_t)stream);
+        if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    }
+    if (e != hipSuccess)
+        return fail(RWS_ERR_HIP, std::string("status word: ") + hipGetErrorString(e));
+    if (v & rws::kStatusLate)
+        return fail(RWS_ERR_WAIT_TIMEOUT,
+                    "a workgroup of a single-launch split-k call on this stream gave up waiting "
+                    "for its row's partials and wrote NaN (workgroups were not dispatched in "
+                    "index order, or the wait limit is set too low)");
+    return RWS_OK;
+}
 
 int softmax_copy_bytes(const void* in, void* out, int64_t bytes, void* stream) {
     g_last_error.clear();

@@ -248,16 +248,14 @@ template <int DT, bool ALIGNED, int BLOCK, int KC>
 __global__ __launch_bounds__(BLOCK) void k_bwd_ordered(const void* __restrict__ y,
                                                        const void* __restrict__ dy,
                                                        void* __restrict__ dx, int64_t rows,
-                                                       int cols, int P, uint64_t* __restrict__ tags,
-                                                       unsigned epoch,
-                                                       const uint64_t* __restrict__ epoch_src,
+                                                       int cols, int P, OrderedSync S,
                                                        int dy_vec, int same_phase) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     using Win = RowWin<DT, ALIGNED>;
     __shared__ float red[W];
     const int t = threadIdx.x;
-    epoch = launch_epoch(epoch, epoch_src);
+    const unsigned epoch = launch_epoch(S.epoch, S.epoch_src);
     const OrderedSlot slot = ordered_slot(blockIdx.x, rows, P);
     const char* tbeg = (const char*)y;
     const char* tend = tensor_end<DT>(y, rows, cols);
@@ -265,7 +263,7 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_ordered(const void* __restrict__ 
                              (int64_t)((const char*)dy - (const char*)y), dy_vec != 0};
     const Win w(y, dx, slot.row, cols);
     const int kbase = slot.chunk * (BLOCK * KC) + t;
-    uint64_t* row_tags = tags + 2 * slot.row * P;
+    uint64_t* row_tags = S.tags + 2 * slot.row * P;
 
     u32x4 ry[KC], rg[KC];
 #pragma unroll
@@ -300,9 +298,13 @@ __global__ __launch_bounds__(BLOCK) void k_bwd_ordered(const void* __restrict__ 
 
     float dot = 0.0f;
     int late = 0;
-    for (int j = t; j < P; j += BLOCK) dot += poll_word(row_tags + 2 * j, epoch, late);
+    for (int j = t; j < P; j += BLOCK)
+        dot += poll_word(row_tags + 2 * j, epoch, late, S.spin_limit);
     dot = block_reduce<W, OpSum>(dot, red);
-    if (__syncthreads_or(late) != 0) dot = __builtin_nanf("");
+    if (__syncthreads_or(late) != 0) {
+        dot = __builtin_nanf("");
+        if (t == 0) report_late(S.status);
+    }
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
         const int k = kbase + BLOCK * i;
@@ -381,21 +383,18 @@ static hipError_t bs(const BwdLaunch& B) {
 }
 
 template <int DT, bool AL>
-static hipError_t bo(const BwdLaunch& B, int P, uint64_t* tags, unsigned epoch,
-                     const uint64_t* src) {
+static hipError_t bo(const BwdLaunch& B, int P, const OrderedSync& S) {
     hipLaunchKernelGGL((k_bwd_ordered<DT, AL, kBwdOrderedBlock, kBwdOrderedKc>),
                        dim3((unsigned)(2 * B.rows * P)), dim3(kBwdOrderedBlock), 0, B.stream, B.y,
-                       B.dy, B.dx, B.rows, B.cols, P, tags, epoch, src, (int)B.dy_vec,
-                       (int)B.same_phase);
+                       B.dy, B.dx, B.rows, B.cols, P, S, (int)B.dy_vec, (int)B.same_phase);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_ordered(const BwdLaunch& B, int P, uint64_t* tags, unsigned epoch,
-                              const uint64_t* src) {
+hipError_t launch_bwd_ordered(const BwdLaunch& B, int P, const OrderedSync& S) {
     switch (B.dtype) {
-        case kF32: return B.aligned ? bo<kF32, true>(B, P, tags, epoch, src) : bo<kF32, false>(B, P, tags, epoch, src);
-        case kF16: return B.aligned ? bo<kF16, true>(B, P, tags, epoch, src) : bo<kF16, false>(B, P, tags, epoch, src);
-        case kBF16: return B.aligned ? bo<kBF16, true>(B, P, tags, epoch, src) : bo<kBF16, false>(B, P, tags, epoch, src);
+        case kF32: return B.aligned ? bo<kF32, true>(B, P, S) : bo<kF32, false>(B, P, S);
+        case kF16: return B.aligned ? bo<kF16, true>(B, P, S) : bo<kF16, false>(B, P, S);
+        case kBF16: return B.aligned ? bo<kBF16, true>(B, P, S) : bo<kBF16, false>(B, P, S);
     }
     return hipErrorInvalidValue;
 }

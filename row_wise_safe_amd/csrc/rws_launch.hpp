@@ -70,17 +70,34 @@ hipError_t launch_two_pass(const Launch& L, int variant);
 hipError_t launch_splitk(const Launch& L, int variant, int P, float2* ws);
 // Single-launch split-k (cooperative): ws holds rows*P (m, d) pairs, sync
 // kSyncWordsPerRow words per row (zero-initialised once), epoch grows by one
-// per call on the same sync buffer.
+// per call on the same sync buffer; a wait that runs out (it cannot while
+// the grid is co-resident) writes NaN and ORs kStatusLate into *status.
 constexpr int kSyncWordsPerRow = 64;
 hipError_t launch_splitk_fused(const Launch& L, int variant, int P, float2* ws, unsigned* sync,
-                               unsigned epoch);
+                               unsigned epoch, uint64_t* status);
 // Workgroups of this variant that can be resident at once on `cus` CUs.
 hipError_t splitk_fused_capacity(int variant, int dtype, bool aligned, int cus, int64_t* blocks);
-// Split-k in one ordinary launch (kSplitk variants): grid 2*rows*P, tags
-// holds 2*rows*P epoch-tagged words, epoch is unique to this launch on this
-// tag buffer (never 0; the buffer starts zeroed).
-hipError_t launch_splitk_ordered(const Launch& L, int variant, int P, uint64_t* tags,
-                                 unsigned epoch);
+// What an ordered (single-launch split-k) launch needs besides its tensors,
+// passed to the kernel as one argument:
+//   tags       2 * rows * P epoch-tagged 64-bit words (zeroed when allocated)
+//   epoch      this launch's epoch on `tags`, never 0 (unless epoch_src)
+//   epoch_src  launches recorded in a graph read their epoch from this device
+//              word instead (see kDeviceEpochFirst)
+//   status     the stream's status word: a workgroup whose wait for a
+//              partial gave up writes NaN outputs and ORs kStatusLate in
+//   spin_limit tries of one poll before it gives up (kOrderedSpinLimit by
+//              default: at least ~0.5 s; 0 gives up at once)
+struct OrderedSync {
+    uint64_t* tags;
+    unsigned epoch;
+    const uint64_t* epoch_src;
+    uint64_t* status;
+    unsigned spin_limit;
+};
+constexpr unsigned kOrderedSpinLimit = 1u << 21;
+constexpr uint64_t kStatusLate = 1;
+// Split-k in one ordinary launch (kSplitk variants): grid 2*rows*P.
+hipError_t launch_splitk_ordered(const Launch& L, int variant, int P, const OrderedSync& S);
 // Epochs of eager ordered launches are handed out by the host from
 // [1, 2^31).  In a captured graph a kernel argument would be replayed
 // unchanged, so launches recorded there take theirs from a device word that
@@ -122,13 +139,10 @@ extern const int kNumBwdStream;
 // family: 1 wave (kBwdWave), 2 block (kBwdBlock), 3 stream (kBwdStream)
 hipError_t launch_bwd(const BwdLaunch& B, int family, int variant);
 // Few long rows: split-k in one launch, chunks of kBwdOrderedBlock x
-// kBwdOrderedKc granules, P chunks per row; tags holds 2*rows*P epoch-tagged
-// words, epoch is unique to this launch on that buffer (or, when epoch_src is
-// given, the launch reads it from there: see launch_bump_epoch).
+// kBwdOrderedKc granules, P chunks per row (OrderedSync as for the forward).
 constexpr int kBwdOrderedBlock = 256;
 constexpr int kBwdOrderedKc = 4;
-hipError_t launch_bwd_ordered(const BwdLaunch& B, int P, uint64_t* tags, unsigned epoch,
-                              const uint64_t* epoch_src = nullptr);
+hipError_t launch_bwd_ordered(const BwdLaunch& B, int P, const OrderedSync& S);
 // Row normalisations (rws_norm.hpp).
 constexpr int kLayerNorm = 0;
 constexpr int kRmsNorm = 1;
@@ -166,8 +180,7 @@ hipError_t launch_norm_block(const NormLaunch& L, int family, int variant);
 // Few long rows: split-k in one launch (as launch_bwd_ordered).
 constexpr int kNormOrderedBlock = 256;
 constexpr int kNormOrderedKc = 4;
-hipError_t launch_norm_ordered(const NormLaunch& L, int P, uint64_t* tags, unsigned epoch,
-                               const uint64_t* epoch_src = nullptr);
+hipError_t launch_norm_ordered(const NormLaunch& L, int P, const OrderedSync& S);
 // n16 granules of 16 bytes.
 hipError_t launch_copy16(const void* in, void* out, int64_t n16, hipStream_t stream);
 

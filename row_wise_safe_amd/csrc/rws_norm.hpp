@@ -463,14 +463,11 @@ template <int DT, bool ALIGNED, int BLOCK, int KC, int MODE, bool AFF>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(AFF ? 1 : 6))) void k_norm_ordered(const void* __restrict__ in,
                                                         void* __restrict__ out, int64_t rows,
                                                         int cols, NormArgs A, int P,
-                                                        uint64_t* __restrict__ tags,
-                                                        unsigned epoch,
-                                                        const uint64_t* __restrict__ epoch_src,
-                                                        int same_phase) {
+                                                        OrderedSync S, int same_phase) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     constexpr int N = KC * VEC;
-    epoch = launch_epoch(epoch, epoch_src);
+    const unsigned epoch = launch_epoch(S.epoch, S.epoch_src);
     using Win = RowWin<DT, ALIGNED>;
     __shared__ float sn[W];
     __shared__ float sm[W];
@@ -481,7 +478,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(AFF ? 1 :
     const char* tend = tensor_end<DT>(in, rows, cols);
     const Win w(in, out, slot.row, cols);
     const int kbase = slot.chunk * (BLOCK * KC) + t;
-    uint64_t* row_tags = tags + 2 * slot.row * P;
+    uint64_t* row_tags = S.tags + 2 * slot.row * P;
 
     u32x4 raw[KC];
 #pragma unroll
@@ -523,18 +520,22 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(AFF ? 1 :
     if (MODE == kLayerNorm) {
         float n = 0.0f, m = 0.0f;
         for (int j = t; j < P; j += BLOCK) {
-            const float pm = poll_word(row_tags + 2 * j, epoch, late);
-            const float pq = poll_word(row_tags + 2 * j + 1, epoch, late);
+            const float pm = poll_word(row_tags + 2 * j, epoch, late, S.spin_limit);
+            const float pq = poll_word(row_tags + 2 * j + 1, epoch, late, S.spin_limit);
             moments_merge(n, m, q, chunk_count(w, j, BLOCK * KC), pm, pq);
         }
         moments_block<W>(n, m, q, sn, sm, sq);
         mu = m;
     } else {
-        for (int j = t; j < P; j += BLOCK) q += poll_word(row_tags + 2 * j, epoch, late);
+        for (int j = t; j < P; j += BLOCK)
+            q += poll_word(row_tags + 2 * j, epoch, late, S.spin_limit);
         q = block_reduce<W, OpSum>(q, sq);
     }
     float rstd = norm_rstd(q, A);
-    if (__syncthreads_or(late) != 0) mu = rstd = __builtin_nanf("");
+    if (__syncthreads_or(late) != 0) {
+        mu = rstd = __builtin_nanf("");
+        if (t == 0) report_late(S.status);
+    }
     norm_store<DT, MODE, AFF, KC>(w, kbase, BLOCK, v, mu, rstd, A, same_phase != 0, &pw, &pb, rw, rb);
     if (t == 0 && slot.chunk == 0) {
         if (A.mean) A.mean[slot.row] = mu;

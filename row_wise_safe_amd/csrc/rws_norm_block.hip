@@ -76,31 +76,26 @@ static hipError_t ns(const NormLaunch& L) {
 }
 
 template <int DT, bool AL, int MODE, bool AFF>
-static hipError_t no(const NormLaunch& L, int P, uint64_t* tags, unsigned epoch,
-                     const uint64_t* src) {
+static hipError_t no(const NormLaunch& L, int P, const OrderedSync& S) {
     hipLaunchKernelGGL((k_norm_ordered<DT, AL, kNormOrderedBlock, kNormOrderedKc, MODE, AFF>),
                        dim3((unsigned)(2 * L.rows * P)), dim3(kNormOrderedBlock), 0, L.stream, L.in,
-                       L.out, L.rows, L.cols, L.args, P, tags, epoch, src, (int)L.same_phase);
+                       L.out, L.rows, L.cols, L.args, P, S, (int)L.same_phase);
     return hipGetLastError();
 }
 
 template <int DT, bool AL>
-static hipError_t no_dt(const NormLaunch& L, int P, uint64_t* tags, unsigned epoch,
-                        const uint64_t* src) {
+static hipError_t no_dt(const NormLaunch& L, int P, const OrderedSync& S) {
     const bool aff = L.args.w || L.args.b;
     if (L.mode == kLayerNorm)
-        return aff ? no<DT, AL, kLayerNorm, true>(L, P, tags, epoch, src)
-                   : no<DT, AL, kLayerNorm, false>(L, P, tags, epoch, src);
-    return aff ? no<DT, AL, kRmsNorm, true>(L, P, tags, epoch, src)
-               : no<DT, AL, kRmsNorm, false>(L, P, tags, epoch, src);
+        return aff ? no<DT, AL, kLayerNorm, true>(L, P, S) : no<DT, AL, kLayerNorm, false>(L, P, S);
+    return aff ? no<DT, AL, kRmsNorm, true>(L, P, S) : no<DT, AL, kRmsNorm, false>(L, P, S);
 }
 
-hipError_t launch_norm_ordered(const NormLaunch& L, int P, uint64_t* tags, unsigned epoch,
-                               const uint64_t* src) {
+hipError_t launch_norm_ordered(const NormLaunch& L, int P, const OrderedSync& S) {
     switch (L.dtype) {
-        case kF32: return L.aligned ? no_dt<kF32, true>(L, P, tags, epoch, src) : no_dt<kF32, false>(L, P, tags, epoch, src);
-        case kF16: return L.aligned ? no_dt<kF16, true>(L, P, tags, epoch, src) : no_dt<kF16, false>(L, P, tags, epoch, src);
-        case kBF16: return L.aligned ? no_dt<kBF16, true>(L, P, tags, epoch, src) : no_dt<kBF16, false>(L, P, tags, epoch, src);
+        case kF32: return L.aligned ? no_dt<kF32, true>(L, P, S) : no_dt<kF32, false>(L, P, S);
+        case kF16: return L.aligned ? no_dt<kF16, true>(L, P, S) : no_dt<kF16, false>(L, P, S);
+        case kBF16: return L.aligned ? no_dt<kBF16, true>(L, P, S) : no_dt<kBF16, false>(L, P, S);
     }
     return hipErrorInvalidValue;
 }

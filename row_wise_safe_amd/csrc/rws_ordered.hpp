@@ -13,11 +13,6 @@
 
 namespace rws {
 
-// Tries of one poll before it gives up (each a sleep plus a load round trip:
-// at least ~0.5 s in all); the workgroup then writes NaN, so a broken
-// ordering assumption shows as NaN output, never as a hang.
-constexpr unsigned kOrderedSpinLimit = 1u << 21;
-
 // The launch's epoch: the kernel argument, or the device word at `src`
 // (launches recorded in a graph, see kDeviceEpochFirst).
 __device__ inline unsigned launch_epoch(unsigned epoch, const uint64_t* src) {
@@ -34,16 +29,25 @@ __device__ inline void publish_word(uint64_t* p, unsigned epoch, float v) {
 }
 
 // Poll one tagged word until it carries `epoch`; returns its value bits and
-// sets `late` when the limit ran out (a thread that is already late does not
-// wait again, so one thread waits at most one limit in total).
-__device__ inline float poll_word(const uint64_t* p, unsigned epoch, int& late) {
-    for (unsigned it = 0; it < (late ? 1u : kOrderedSpinLimit); ++it) {
+// sets `late` when `limit` tries ran out (a thread that is already late tries
+// once more at most, so one thread waits at most one limit in total; a limit
+// of 0 gives up without reading).
+__device__ inline float poll_word(const uint64_t* p, unsigned epoch, int& late, unsigned limit) {
+    const unsigned tries = late ? (limit ? 1u : 0u) : limit;
+    for (unsigned it = 0; it < tries; ++it) {
         const uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if ((unsigned)(v >> 32) == epoch) return __uint_as_float((unsigned)v);
         __builtin_amdgcn_s_sleep(2);
     }
     late = 1;
     return 0.0f;
+}
+
+// A workgroup whose wait gave up (its outputs are NaN) records it in the
+// stream's status word; one thread per workgroup calls this.
+__device__ inline void report_late(uint64_t* status) {
+    if (status)
+        __hip_atomic_fetch_or(status, kStatusLate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Workgroup b of an ordered launch over rows x P chunks: [0, rows*P) are

@@ -15,7 +15,8 @@
 // refuses grids that cannot be co-resident (the dispatcher then uses the
 // two-launch form).  The wait is also bounded: a workgroup that does not see
 // its row released after kSpinLimit polls stops waiting, so every wave
-// always reaches the end of the kernel.
+// always reaches the end of the kernel; it then writes NaN for its chunk and
+// sets the stream's status word (softmax_stream_status reports it).
 //
 // Synchronisation words (per row, in a library-owned zero-initialised
 // buffer, one 256-byte line per row so that rows do not contend): count
@@ -55,13 +56,15 @@ __global__ __launch_bounds__(BLOCK, fused_min_waves<KC>()) void k_splitk_fused(c
                                                         void* __restrict__ out, int64_t rows,
                                                         int cols, int P, float2* __restrict__ ws,
                                                         unsigned* __restrict__ sync,
-                                                        unsigned epoch, int same_phase) {
+                                                        unsigned epoch, uint64_t* status,
+                                                        int same_phase) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
     __shared__ float red_max[W];
     __shared__ float red_sum[W];
     __shared__ float red_max2[W];
     __shared__ float red_sum2[W];
+    __shared__ int timed_out;
     const int t = threadIdx.x;
     const int64_t b = blockIdx.x;
     const int64_t row = b / P;
@@ -104,6 +107,7 @@ __global__ __launch_bounds__(BLOCK, fused_min_waves<KC>()) void k_splitk_fused(c
 
     // publish the partial, arrive, wait for the row's release
     if (t == 0) {
+        timed_out = 0;
         ws[row * P + chunk] = make_float2(mc, dc);
         unsigned* count = sync + kSyncWordsPerRow * row;
         unsigned* flag = count + 1;
@@ -115,10 +119,17 @@ __global__ __launch_bounds__(BLOCK, fused_min_waves<KC>()) void k_splitk_fused(c
         } else {
             // Poll with relaxed loads (an acquire per poll would invalidate
             // the L2 every iteration); one acquire fence follows the wait.
-            for (unsigned it = 0; it < kSpinLimit; ++it) {
+            unsigned it = 0;
+            for (; it < kSpinLimit; ++it) {
                 if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch)
                     break;
                 __builtin_amdgcn_s_sleep(8);
+            }
+            if (it == kSpinLimit) {
+                timed_out = 1;
+                if (status)
+                    __hip_atomic_fetch_or(status, kStatusLate, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
@@ -143,7 +154,7 @@ __global__ __launch_bounds__(BLOCK, fused_min_waves<KC>()) void k_splitk_fused(c
     float M, D;
     block_merge<W>(m, d, M, D, red_max2, red_sum2);
     const RowExp er(M);
-    const float r = __builtin_amdgcn_rcpf(D);
+    const float r = timed_out ? __builtin_nanf("") : __builtin_amdgcn_rcpf(D);
 
     // y = e^(x - M) / D for the chunk held in registers
 #pragma unroll
@@ -207,7 +218,7 @@ hipError_t splitk_fused_capacity(int variant, int dtype, bool aligned, int cus, 
 }
 
 hipError_t launch_splitk_fused(const Launch& L, int variant, int P, float2* ws, unsigned* sync,
-                               unsigned epoch) {
+                               unsigned epoch, uint64_t* status) {
     const void* k = fused_kernel(variant, L.dtype, L.aligned);
     if (!k) return hipErrorInvalidValue;
     const void* in = L.in;
@@ -216,7 +227,8 @@ hipError_t launch_splitk_fused(const Launch& L, int variant, int P, float2* ws, 
     int cols = L.cols;
     int same_phase = L.same_phase ? 1 : 0;
     void* args[] = {(void*)&in, (void*)&out, (void*)&rows, (void*)&cols, (void*)&P,
-                    (void*)&ws, (void*)&sync, (void*)&epoch, (void*)&same_phase};
+                    (void*)&ws, (void*)&sync, (void*)&epoch, (void*)&status,
+                    (void*)&same_phase};
     return hipLaunchCooperativeKernel(k, dim3((unsigned)(L.rows * P)),
                                       dim3(kSplitkFused[variant].block), args, 0, L.stream);
 }

@@ -21,10 +21,12 @@
 //    every stage-2 workgroup; workgroups are handed to each XCD in increasing
 //    index order, so a waiting stage-2 workgroup is never ahead of a stage-1
 //    workgroup it needs, and stage-1 workgroups never wait.
-//  * Bounded waiting.  A poll gives up after kOrderedSpinLimit tries (each
-//    a sleep plus a load round trip: at least ~0.5 s in all); the workgroup
-//    then writes NaN for its chunk, so a broken ordering assumption shows as
-//    NaN output, never as a hang.
+//  * Bounded waiting.  A poll gives up after OrderedSync::spin_limit tries
+//    (by default kOrderedSpinLimit, each a sleep plus a load round trip: at
+//    least ~0.5 s in all); the workgroup then writes NaN for its chunk and
+//    sets the stream's status word, which softmax_stream_status reports, so a
+//    broken ordering assumption shows as NaN output and an error status,
+//    never as a hang.
 //
 // The epoch grows by one per launch on the same tag buffer (host side), and
 // the buffer is zero-filled when it is allocated and when the host's epoch
@@ -45,9 +47,8 @@ namespace rws {
 template <int DT, bool ALIGNED, int BLOCK, int KC>
 __global__ __launch_bounds__(BLOCK) void k_splitk_ordered(const void* __restrict__ in,
                                                           void* __restrict__ out, int64_t rows,
-                                                          int cols, int P,
-                                                          uint64_t* __restrict__ tags,
-                                                          unsigned epoch, int same_phase) {
+                                                          int cols, int P, OrderedSync S,
+                                                          int same_phase) {
     constexpr int W = BLOCK / 64;
     __shared__ float red_max[W];
     __shared__ float red_sum[W];
@@ -62,7 +63,8 @@ __global__ __launch_bounds__(BLOCK) void k_splitk_ordered(const void* __restrict
     const char* tend = tensor_end<DT>(in, rows, cols);
     const RowWin<DT, ALIGNED> w(in, out, row, cols);
     const int kbase = chunk * (BLOCK * KC) + t;
-    uint64_t* row_tags = tags + 2 * row * P;
+    uint64_t* row_tags = S.tags + 2 * row * P;
+    const unsigned epoch = launch_epoch(S.epoch, S.epoch_src);
 
     // Both stages start by loading the chunk; a stage-2 workgroup's loads
     // are then in flight while it waits for the partials.
@@ -85,13 +87,14 @@ __global__ __launch_bounds__(BLOCK) void k_splitk_ordered(const void* __restrict
     float m = kNegInf, d = 0.0f;
     int late = 0;
     for (int j = t; j < P; j += BLOCK) {
-        const float pm = poll_word(row_tags + 2 * j, epoch, late);
-        const float pd = poll_word(row_tags + 2 * j + 1, epoch, late);
+        const float pm = poll_word(row_tags + 2 * j, epoch, late, S.spin_limit);
+        const float pd = poll_word(row_tags + 2 * j + 1, epoch, late, S.spin_limit);
         md_fold(m, d, pm, pd);
     }
     float M, D;
     block_merge<W>(m, d, M, D, red_max, red_sum);
     const bool failed = __syncthreads_or(late) != 0;
+    if (failed && t == 0) report_late(S.status);
     const float r = failed ? __builtin_nanf("") : __builtin_amdgcn_rcpf(D);
     splitk_write<DT, ALIGNED, BLOCK, KC>(w, kbase, raw, tbeg, tend, M, r, same_phase != 0);
 }
@@ -136,28 +139,27 @@ hipError_t launch_fill_words(uint64_t* p, int64_t n, uint64_t v, hipStream_t str
 }
 
 template <int DT, bool AL, int B, int KC>
-static hipError_t go(const Launch& L, int P, uint64_t* tags, unsigned epoch) {
+static hipError_t go(const Launch& L, int P, const OrderedSync& S) {
     hipLaunchKernelGGL((k_splitk_ordered<DT, AL, B, KC>), dim3((unsigned)(2 * L.rows * P)),
-                       dim3(B), 0, L.stream, L.in, L.out, L.rows, L.cols, P, tags, epoch,
+                       dim3(B), 0, L.stream, L.in, L.out, L.rows, L.cols, P, S,
                        (int)L.same_phase);
     return hipGetLastError();
 }
 
 template <int B, int KC>
-static hipError_t go_any(const Launch& L, int P, uint64_t* tags, unsigned epoch) {
+static hipError_t go_any(const Launch& L, int P, const OrderedSync& S) {
     switch (L.dtype) {
-        case kF32: return L.aligned ? go<kF32, true, B, KC>(L, P, tags, epoch) : go<kF32, false, B, KC>(L, P, tags, epoch);
-        case kF16: return L.aligned ? go<kF16, true, B, KC>(L, P, tags, epoch) : go<kF16, false, B, KC>(L, P, tags, epoch);
-        case kBF16: return L.aligned ? go<kBF16, true, B, KC>(L, P, tags, epoch) : go<kBF16, false, B, KC>(L, P, tags, epoch);
+        case kF32: return L.aligned ? go<kF32, true, B, KC>(L, P, S) : go<kF32, false, B, KC>(L, P, S);
+        case kF16: return L.aligned ? go<kF16, true, B, KC>(L, P, S) : go<kF16, false, B, KC>(L, P, S);
+        case kBF16: return L.aligned ? go<kBF16, true, B, KC>(L, P, S) : go<kBF16, false, B, KC>(L, P, S);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_splitk_ordered(const Launch& L, int variant, int P, uint64_t* tags,
-                                 unsigned epoch) {
+hipError_t launch_splitk_ordered(const Launch& L, int variant, int P, const OrderedSync& S) {
     int i = 0;
 #define RWS_CASE(b, kc) \
-    if (variant == i) return go_any<b, kc>(L, P, tags, epoch); \
+    if (variant == i) return go_any<b, kc>(L, P, S); \
     ++i;
     RWS_SPLITK_VARIANTS(RWS_CASE)
 #undef RWS_CASE

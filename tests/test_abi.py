@@ -53,7 +53,7 @@ def test_binding_mirrors_the_abi():
 
 def test_status_strings_and_names(lib):
     assert rws.softmax_status_string(rws.RWS_OK) == "ok"
-    for st in range(1, 6):
+    for st in range(1, 7):
         assert rws.softmax_status_string(st) not in ("", "ok", "unknown status")
     assert rws.softmax_status_string(99) == "unknown status"
     assert [rws.softmax_kernel_name(i) for i in range(7)] == \
@@ -349,3 +349,12 @@ def test_plan_cache_keeps_calls_apart(lib):
         order = rng.permutation(len(cases))
         for i in order:
             assert ask(cases[i]) == first[i], cases[i]
+
+
+def test_wait_limit_argument_checks(lib):
+    # host-only setter: default (< 0), an explicit count, and out of range
+    assert rws.softmax_set_wait_limit(-1) == rws.RWS_OK
+    assert rws.softmax_set_wait_limit(1000) == rws.RWS_OK
+    assert rws.softmax_set_wait_limit(1 << 32) == rws.RWS_ERR_INVALID_ARG
+    assert "2^32" in rws.softmax_last_error()
+    assert rws.softmax_set_wait_limit(-1) == rws.RWS_OK
