@@ -92,14 +92,16 @@ def test_forward_few_long_rows(kernel):
     check(y.double().cpu().numpy(), oracle.safe_softmax(stored), "f16", f"eager {desc}")
     g = _capture(lambda: rws.softmax(x, out=y, kernel=kernel), s)
     for i in range(REPLAYS):
-        stored = _fill(x, _host(rows, cols, 301 + i, sigma=1.0 + i))
-        y.fill_(float("nan"))
-        g.replay()
+        # on the capturing stream, with eager split-k calls queued behind the
+        # replay (they share its workspace) and one synchronisation for both
+        with torch.cuda.stream(s):
+            stored = _fill(x, _host(rows, cols, 301 + i, sigma=1.0 + i))
+            y.fill_(float("nan"))
+            g.replay()
+            noise = _eager_noise(s, 310 + 2 * i)
         torch.cuda.synchronize()
         check(y.double().cpu().numpy(), oracle.safe_softmax(stored), "f16",
               f"replay {i} of {kernel} ({desc})")
-        noise = _eager_noise(s, 310 + 2 * i)
-        torch.cuda.synchronize()
         _check_noise(noise)
 
 
@@ -135,12 +137,12 @@ def test_forward_row_kernels(rows, cols, dtype, masked):
     torch.cuda.synchronize()
     g = _capture(call, s)
     for i in range(REPLAYS):
-        stored = _fill(x, _host(rows, cols, 322 + i))
-        g.replay()
+        with torch.cuda.stream(s):
+            stored = _fill(x, _host(rows, cols, 322 + i))
+            g.replay()
+            noise = _eager_noise(s, 330 + 2 * i)
         torch.cuda.synchronize()
         check(y.double().cpu().numpy(), ref(stored), dtype, f"replay {i} of [{rows},{cols}]")
-        noise = _eager_noise(s, 330 + 2 * i)
-        torch.cuda.synchronize()
         _check_noise(noise)
 
 
@@ -159,10 +161,11 @@ def test_backward_few_long_rows(kernel):
     torch.cuda.synchronize()
     g = _capture(lambda: rws.softmax_backward(y, dy, out=dx, kernel=kernel), s)
     for i in range(REPLAYS):
-        sy = _fill(y, oracle.safe_softmax(_host(rows, cols, 342 + i, sigma=1.0 + i)))
-        sdy = _fill(dy, _host(rows, cols, 350 + i, sigma=1.0))
-        dx.fill_(float("nan"))
-        g.replay()
+        with torch.cuda.stream(s):
+            sy = _fill(y, oracle.safe_softmax(_host(rows, cols, 342 + i, sigma=1.0 + i)))
+            sdy = _fill(dy, _host(rows, cols, 350 + i, sigma=1.0))
+            dx.fill_(float("nan"))
+            g.replay()
         torch.cuda.synchronize()
         check_backward(dx.double().cpu().numpy(), sy, sdy, dtype,
                        f"replay {i} of backward ({eager} eagerly)")
@@ -206,9 +209,10 @@ def test_norm_few_long_rows(mode):
     torch.cuda.synchronize()
     g = _capture(call, s)
     for i in range(REPLAYS):
-        stored = _fill(x, 2.0 + _host(rows, cols, 363 + i, sigma=1.0 + i))
-        out.fill_(float("nan"))
-        g.replay()
+        with torch.cuda.stream(s):
+            stored = _fill(x, 2.0 + _host(rows, cols, 363 + i, sigma=1.0 + i))
+            out.fill_(float("nan"))
+            g.replay()
         torch.cuda.synchronize()
         verify(stored, f"replay {i} of {mode}")
         with torch.cuda.stream(s):  # eager ordered normalisation between replays
@@ -246,10 +250,11 @@ def test_backward_capture_without_tag_buffer():
     with FreshStream() as s:
         g = _capture(lambda: rws.softmax_backward(y, dy, out=dx), s)
         for i in range(REPLAYS):
-            sy = _fill(y, oracle.safe_softmax(_host(rows, cols, 380 + i)))
-            sdy = _fill(dy, _host(rows, cols, 385 + i, sigma=1.0))
-            dx.fill_(float("nan"))
-            g.replay()
+            with torch.cuda.stream(s):
+                sy = _fill(y, oracle.safe_softmax(_host(rows, cols, 380 + i)))
+                sdy = _fill(dy, _host(rows, cols, 385 + i, sigma=1.0))
+                dx.fill_(float("nan"))
+                g.replay()
             torch.cuda.synchronize()
             check_backward(dx.double().cpu().numpy(), sy, sdy, dtype,
                            f"replay {i} of a backward captured without tags")
@@ -273,10 +278,11 @@ def test_device_epoch_wrap():
             torch.cuda.synchronize()
             g = _capture(lambda: rws.softmax_backward(y, dy, out=dx), s)
             for i in range(8):
-                sy = _fill(y, oracle.safe_softmax(_host(rows, cols, 392 + i)))
-                sdy = _fill(dy, _host(rows, cols, 400 + i, sigma=1.0))
-                dx.fill_(float("nan"))
-                g.replay()
+                with torch.cuda.stream(s):
+                    sy = _fill(y, oracle.safe_softmax(_host(rows, cols, 392 + i)))
+                    sdy = _fill(dy, _host(rows, cols, 400 + i, sigma=1.0))
+                    dx.fill_(float("nan"))
+                    g.replay()
                 torch.cuda.synchronize()
                 check_backward(dx.double().cpu().numpy(), sy, sdy, dtype,
                                f"replay {i} across the device epoch wrap")
@@ -327,12 +333,13 @@ def test_captured_ordered_dtypes(dtype, offset):
     torch.cuda.synchronize()
     g = _capture(call, s)
     for i in range(REPLAYS):
-        sy = _fill(y, oracle.safe_softmax(_host(rows, cols, 423 + i, sigma=2.0)))
-        sdy = _fill(dy, _host(rows, cols, 430 + i, sigma=1.0))
-        sx = _fill(x, 1.0 + _host(rows, cols, 440 + i))
-        dx.fill_(float("nan"))
-        out.fill_(float("nan"))
-        g.replay()
+        with torch.cuda.stream(s):
+            sy = _fill(y, oracle.safe_softmax(_host(rows, cols, 423 + i, sigma=2.0)))
+            sdy = _fill(dy, _host(rows, cols, 430 + i, sigma=1.0))
+            sx = _fill(x, 1.0 + _host(rows, cols, 440 + i))
+            dx.fill_(float("nan"))
+            out.fill_(float("nan"))
+            g.replay()
         torch.cuda.synchronize()
         what = f"{dtype} offset {offset} replay {i}"
         check_backward(dx.double().cpu().numpy(), sy, sdy, dtype, f"backward {what}")
