@@ -168,6 +168,28 @@ int softmax_fwd_kernel(const void *in, void *out, int64_t rows, int64_t cols, in
                        void *stream, int kernel_id);
 
 /*
+ * softmax_fwd_noalloc -- softmax_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the library allocates nothing on this path, on the
+ * first call or later.  The kernel is chosen as in softmax_fwd, except that
+ * a shape the dispatcher sends to split-k runs the two-launch split-k
+ * (RWS_KERNEL_SPLITK), whose per-chunk partial (m, d) pairs live in a
+ * 512 KiB array that the library's code object holds on every GPU it runs
+ * on, until the process ends.  Rows are launched in batches whose partials
+ * fit the array (8 bytes per row per chunk); a row needing more than the
+ * whole array (fp32 rows of more than 2^29 columns) is rejected with
+ * RWS_ERR_UNSUPPORTED_SHAPE before any launch.  The array keeps the last
+ * call's contents (nothing in it needs to start at zero).  All calls on one
+ * GPU share that GPU's array: calls on that GPU that can run at the same
+ * time (on different streams, or from different threads without ordering)
+ * race on it and give wrong results; calls ordered on one stream are safe,
+ * and so is replaying a captured call on its stream.  Arguments, layout,
+ * streams and errors as softmax_fwd.
+ */
+int softmax_fwd_noalloc(const void *in, void *out, int64_t rows, int64_t cols, int dtype,
+                        void *stream);
+
+/*
  * softmax_fwd_masked -- softmax of attention scores with the scale and mask
  * folded in (DCU case-study page, section 9: a mask parameter in the softmax
  * kernel saves a launch; Pangu-Weather profile page, section 6: bias + mask +

@@ -25,7 +25,8 @@ __all__ = [
     "RWS_ERR_HIP", "RWS_ERR_UNSUPPORTED_SHAPE", "RWS_ERR_WAIT_TIMEOUT",
     "KERNELS", "KERNEL_IDS",
     "library_path", "load_library",
-    "softmax_fwd", "softmax_fwd_kernel", "softmax_fwd_masked", "softmax_bwd",
+    "softmax_fwd", "softmax_fwd_kernel", "softmax_fwd_noalloc", "softmax_fwd_masked",
+    "softmax_bwd",
     "softmax_bwd_kernel", "softmax_select_kernel",
     "softmax_describe_launch",
     "softmax_describe_launch_masked",
@@ -84,6 +85,8 @@ def load_library():
     lib.softmax_fwd.restype = cint
     lib.softmax_fwd_kernel.argtypes = [vp, vp, i64, i64, cint, vp, cint]
     lib.softmax_fwd_kernel.restype = cint
+    lib.softmax_fwd_noalloc.argtypes = [vp, vp, i64, i64, cint, vp]
+    lib.softmax_fwd_noalloc.restype = cint
     lib.softmax_fwd_masked.argtypes = [vp, vp, i64, i64, cint, ctypes.c_float, vp, i64, i64, vp,
                                        cint]
     lib.softmax_fwd_masked.restype = cint
@@ -137,6 +140,11 @@ def softmax_fwd_kernel(in_ptr: int, out_ptr: int, rows: int, cols: int, dtype: i
                        kernel_id: int) -> int:
     return load_library().softmax_fwd_kernel(in_ptr, out_ptr, rows, cols, dtype, stream,
                                              kernel_id)
+
+
+def softmax_fwd_noalloc(in_ptr: int, out_ptr: int, rows: int, cols: int, dtype: int,
+                        stream: int) -> int:
+    return load_library().softmax_fwd_noalloc(in_ptr, out_ptr, rows, cols, dtype, stream)
 
 
 def softmax_fwd_masked(in_ptr: int, out_ptr: int, rows: int, cols: int, dtype: int, scale: float,

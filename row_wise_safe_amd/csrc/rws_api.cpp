@@ -900,7 +900,96 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Scratch of softmax_fwd_noalloc: split-k partials in device memory that the
+// library never allocates -- a file-scope array that every GPU the library
+// runs on holds from the load of its code object until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+constexpr int64_t kNoAllocScratchBytes = (int64_t)512 << 10;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;  // device -> address of its copy of `scratch`
+
+// The current device's copy of `scratch`; looked up on the first call on
+// that device.
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RWS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    auto it = g_scratch_ptr.find(dev);
+    if (it != g_scratch_ptr.end()) {
+        *out = it->second;
+        return RWS_OK;
+    }
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+        return fail(RWS_ERR_HIP, std::string("hipGetSymbolAddress (split-k scratch): ") +
+                                     hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+    *out = ptr;
+    return RWS_OK;
+}
+
+// softmax_fwd without device allocation: the dispatcher's plan, with a
+// split-k plan run as the two-launch split-k (kernel-boundary ordering: no
+// epochs, no words that must start at zero, and a captured launch replays
+// correctly) on partials in `scratch`, in row batches that fit it.
+int run_noalloc(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream) {
+    Plan p;
+    int st = plan_launch(rows, cols, dtype, in, out, RWS_KERNEL_AUTO, &p);
+    if (st != RWS_OK) return st;
+    if (!is_splitk(p.family)) return run(in, out, rows, cols, dtype, stream, RWS_KERNEL_AUTO, nullptr);
+    st = plan_launch(rows, cols, dtype, in, out, RWS_KERNEL_SPLITK, &p);
+    if (st != RWS_OK) return st;
+    const int64_t per_row = (int64_t)p.P * (int64_t)sizeof(float2);
+    if (per_row > kNoAllocScratchBytes)
+        return fail(RWS_ERR_UNSUPPORTED_SHAPE,
+                    "softmax_fwd_noalloc: a row of " + std::to_string(cols) + " columns needs " +
+                        std::to_string(per_row) + " bytes of split-k partials, above the " +
+                        std::to_string(kNoAllocScratchBytes) + "-byte scratch");
+    void* ptr = nullptr;
+    st = scratch_address(&ptr);
+    if (st != RWS_OK) return st;
+    const int64_t batch = std::min<int64_t>(p.max_rows_per_launch, kNoAllocScratchBytes / per_row);
+    const int64_t row_bytes = cols * elem_size(dtype);
+    for (int64_t r0 = 0; r0 < rows; r0 += batch) {
+        rws::Launch L;
+        L.rows = std::min<int64_t>(batch, rows - r0);
+        L.in = (const char*)in + r0 * row_bytes;
+        L.out = (char*)out + r0 * row_bytes;
+        L.cols = (int)cols;
+        L.dtype = dtype;
+        L.aligned = p.aligned;
+        L.same_phase = p.same_phase;
+        L.wt = p.wt;
+        L.lgrun = p.lgrun;
+        L.stream = (hipStream_t)stream;
+        const hipError_t e = rws::launch_splitk(L, p.variant, p.P, (float2*)ptr);
+        if (e != hipSuccess)
+            return fail(RWS_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    }
+    return RWS_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
+int softmax_fwd_noalloc(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
+                        void* stream) {
+    g_last_error.clear();
+    const int st = check_args(in, out, rows, cols, dtype, RWS_KERNEL_AUTO);
+    if (st != RWS_OK || rows == 0 || cols == 0) return st;
+    return run_noalloc(in, out, rows, cols, dtype, stream);
+}
 
 int softmax_fwd_kernel(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
                        void* stream, int kernel_id) {

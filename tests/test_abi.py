@@ -358,3 +358,16 @@ def test_wait_limit_argument_checks(lib):
     assert rws.softmax_set_wait_limit(1 << 32) == rws.RWS_ERR_INVALID_ARG
     assert "2^32" in rws.softmax_last_error()
     assert rws.softmax_set_wait_limit(-1) == rws.RWS_OK
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 0, -1, 3, rws.RWS_F16, 0), rws.RWS_ERR_INVALID_ARG),
+    ((0, 0, 3, 4, 3, 0), rws.RWS_ERR_UNSUPPORTED_DTYPE),
+    ((0, 0, 3, 4, rws.RWS_F16, 0), rws.RWS_ERR_INVALID_ARG),        # NULL pointers
+    ((17, 32, 3, 4, rws.RWS_F16, 0), rws.RWS_ERR_MISALIGNED),
+    ((32, 32, 3, (1 << 30) + 1, rws.RWS_F16, 0), rws.RWS_ERR_UNSUPPORTED_SHAPE),
+])
+def test_noalloc_argument_checks_never_launch(lib, args, status):
+    assert rws.softmax_fwd_noalloc(*args) == status
+    assert rws.softmax_last_error() != ""
+    assert rws.softmax_fwd_noalloc(0, 0, 0, 5, rws.RWS_F32, 0) == rws.RWS_OK  # empty: no-op
