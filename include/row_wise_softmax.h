@@ -38,12 +38,12 @@
  *
  * Ownership.  The caller owns `in` and `out`.  For the split-k paths the
  * library owns a small workspace (8 bytes per row per chunk for the two-launch
- * form, 16 bytes per row per chunk of epoch-tagged words for the ordered
- * single launch, plus 256 bytes per row of arrival counters for the
- * cooperative form) that it keeps per (device, stream) and grows on demand;
- * the first call that needs a larger workspace allocates it (hipMalloc;
- * counters and tag words are zeroed then, the tag words by a kernel on the
- * call's stream), later calls reuse it.  Calls on one stream are ordered, so
+ * form, 16 bytes per row per chunk of epoch-tagged words for the single-launch
+ * forms, and one 128-byte status word) that it keeps per (device, stream) and
+ * grows on demand; the first call that needs a larger workspace allocates it
+ * (hipMalloc; tag words and the status word are zeroed then, by a kernel on
+ * the call's stream), later calls reuse it (softmax_fwd_noalloc allocates
+ * nothing).  Calls on one stream are ordered, so
  * reuse is safe; the workspaces are released when the library is unloaded.
  * They are keyed by the stream handle: a destroyed stream's workspace stays
  * allocated, and a stream created later with the same handle reuses it.
@@ -117,15 +117,15 @@ enum {
                                  safe-online-softmax page, section 3.2) */
     RWS_KERNEL_SPLITK_FUSED = 5, /* split-k in one cooperative launch: each
                                  workgroup keeps its chunk in registers, the
-                                 row's workgroups exchange partial (m, d) through
-                                 memory and a per-row arrival counter, so the
-                                 input is read once (the single-kernel form the
-                                 same page, section 3.2, mentions).  Returns
+                                 row's workgroups exchange partial (m, d) as
+                                 epoch-tagged words (as the ordered form
+                                 below), so the input is read once (the
+                                 single-kernel form the same page, section
+                                 3.2, mentions).  Returns
                                  RWS_ERR_UNSUPPORTED_SHAPE when the grid cannot
                                  be co-resident on the device.  Never chosen
-                                 by the dispatcher: on MI355X its cross-XCD
-                                 synchronisation costs more than the re-read
-                                 it saves */
+                                 by the dispatcher: on MI355X the cooperative
+                                 launch costs more than the re-read it saves */
     RWS_KERNEL_SPLITK_ORDERED = 6 /* split-k in one ordinary launch: the
                                  stage-1 workgroups (partial (m, d) per chunk)
                                  come first in the grid, the stage-2

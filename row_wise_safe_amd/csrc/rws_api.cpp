@@ -485,10 +485,7 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
 struct Workspace {
     void* ptr = nullptr;        // split-k partials
     size_t bytes = 0;
-    unsigned* sync = nullptr;   // single-launch split-k: kSyncWordsPerRow words per row
-    int64_t sync_rows = 0;
-    unsigned epoch = 0;         // last epoch handed to a single-launch call
-    uint64_t* tags = nullptr;   // ordered split-k: epoch-tagged partial words
+    uint64_t* tags = nullptr;   // single-launch split-k: epoch-tagged partial words
     int64_t tag_words = 0;
     unsigned tag_epoch = 0;     // last epoch used on `tags`
     bool captured = false;      // `ptr` is baked into a captured graph
@@ -515,7 +512,6 @@ struct WorkspaceReaper {
         if (!g_ws) return;
         for (auto& kv : *g_ws) {
             if (kv.second.ptr) (void)hipFree(kv.second.ptr);
-            if (kv.second.sync) (void)hipFree(kv.second.sync);
             if (kv.second.tags) (void)hipFree(kv.second.tags);
             if (kv.second.status) (void)hipFree(kv.second.status);
             for (void* p : kv.second.retired) (void)hipFree(p);
@@ -569,9 +565,8 @@ int get_status_word(hipStream_t stream, bool cap, uint64_t** out) {
     return RWS_OK;
 }
 
-// Grow-only workspace of (device, stream): `bytes` of partials and, when
-// sync_rows > 0, kSyncWordsPerRow*sync_rows zeroed counter words.  Returns the epoch for a
-// single-launch call in *epoch (when epoch != nullptr).  The caller holds
+// Grow-only workspace of (device, stream): `bytes` of partials of the
+// two-launch split-k.  The caller holds
 // g_ws_mu from this call until its launches are enqueued: a call from another
 // host thread on the same stream that grows the buffer synchronises the
 // stream and frees the old one, which is only safe once every launch that
@@ -579,26 +574,24 @@ int get_status_word(hipStream_t stream, bool cap, uint64_t** out) {
 // capturing) nothing is allocated (the call fails if the buffer is too
 // small) and the buffer handed out is marked captured: when it grows later it
 // is kept, not freed, since the graph's launches still name it.
-int get_workspace(hipStream_t stream, bool cap, size_t bytes, int64_t sync_rows, void** out,
-                  unsigned** sync, unsigned* epoch) {
+int get_workspace(hipStream_t stream, bool cap, size_t bytes, void** out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(RWS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
     if (!g_ws) g_ws = new std::map<std::pair<int, hipStream_t>, Workspace>();
     Workspace& w = (*g_ws)[std::make_pair(dev, stream)];
     const bool grow_partials = w.bytes < bytes;
-    const bool grow_sync = sync_rows > w.sync_rows;
-    if ((grow_partials || grow_sync) && cap)
+    if (grow_partials && cap)
         return fail(RWS_ERR_HIP,
                     "split-k workspace too small during graph capture: run the call once on "
                     "this stream before capturing it");
-    if ((grow_partials || grow_sync) && (w.ptr || w.sync)) {
+    if (grow_partials && w.ptr) {
         // the old buffers may still be in use by earlier work on this stream
         e = hipStreamSynchronize(stream);
         if (e != hipSuccess)
             return fail(RWS_ERR_HIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
     }
-    if (std::getenv("RWS_TEST_FAIL_ALLOC") && (grow_partials || grow_sync))
+    if (std::getenv("RWS_TEST_FAIL_ALLOC") && grow_partials)
         return fail(RWS_ERR_HIP, "workspace allocation failed (RWS_TEST_FAIL_ALLOC)");
     if (grow_partials) {
         if (w.ptr && w.captured)
@@ -617,29 +610,8 @@ int get_workspace(hipStream_t stream, bool cap, size_t bytes, int64_t sync_rows,
         }
         w.bytes = want;
     }
-    if (grow_sync) {
-        if (w.sync) (void)hipFree(w.sync);
-        w.sync = nullptr;
-        w.sync_rows = 0;
-        int64_t want = 256;
-        while (want < sync_rows) want *= 2;
-        const size_t sync_bytes = (size_t)want * rws::kSyncWordsPerRow * sizeof(unsigned);
-        e = hipMalloc((void**)&w.sync, sync_bytes);
-        if (e == hipSuccess) e = hipMemset(w.sync, 0, sync_bytes);
-        if (e != hipSuccess) {
-            if (w.sync) (void)hipFree(w.sync);
-            w.sync = nullptr;
-            return fail(RWS_ERR_HIP, std::string("split-k counters: ") + hipGetErrorString(e));
-        }
-        w.sync_rows = want;
-    }
     if (cap) w.captured = true;
     *out = w.ptr;
-    if (sync) *sync = w.sync;
-    if (epoch) {
-        if (++w.epoch == 0) ++w.epoch;  // 0 is the value of a fresh counter word
-        *epoch = w.epoch;
-    }
     return RWS_OK;
 }
 
@@ -803,7 +775,6 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
     }
 
     void* ws = nullptr;
-    unsigned* sync = nullptr;
     unsigned epoch = 0;
     hipStream_t s = (hipStream_t)stream;
     // split-k: keep the workspace locked until this call's launches are enqueued
@@ -820,17 +791,16 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
             RWS_OK) {
             void* ws2 = nullptr;
             const int64_t batch2 = std::min<int64_t>(rows, p2.max_rows_per_launch);
-            st = get_workspace(s, false, (size_t)batch2 * p2.P * sizeof(float2), 0, &ws2,
-                               nullptr, nullptr);
+            st = get_workspace(s, false, (size_t)batch2 * p2.P * sizeof(float2), &ws2);
             if (st != RWS_OK) return st;
         }
     }
     if (p.family == RWS_KERNEL_SPLITK) {
         const int64_t batch = std::min<int64_t>(rows, p.max_rows_per_launch);
-        st = get_workspace(s, cap, (size_t)batch * p.P * sizeof(float2), 0, &ws, nullptr, nullptr);
+        st = get_workspace(s, cap, (size_t)batch * p.P * sizeof(float2), &ws);
         if (st != RWS_OK) return st;
     } else if (p.family == RWS_KERNEL_SPLITK_FUSED) {
-        st = get_workspace(s, cap, (size_t)rows * p.P * sizeof(float2), rows, &ws, &sync, &epoch);
+        st = get_tag_workspace(s, 2 * rows * p.P, 1, &tags, &epoch);
         if (st != RWS_OK) return st;
     } else if (p.family == RWS_KERNEL_SPLITK_ORDERED) {
         const int64_t batch = std::min<int64_t>(rows, p.max_rows_per_launch);
@@ -880,8 +850,9 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
                     e = rws::launch_splitk(L, p.variant, p.P, (float2*)ws);
                     break;
                 case RWS_KERNEL_SPLITK_FUSED:
-                    e = rws::launch_splitk_fused(L, p.variant, p.P, (float2*)ws, sync, epoch,
-                                                 status);
+                    e = rws::launch_splitk_fused(
+                        L, p.variant, p.P,
+                        rws::OrderedSync{tags, epoch, nullptr, status, wait_limit});
                     break;
                 case RWS_KERNEL_SPLITK_ORDERED:
                     // one epoch per launch: the batches reuse the same tag words

@@ -68,13 +68,6 @@ hipError_t launch_block_onepass(const Launch& L, int variant);
 hipError_t launch_two_pass(const Launch& L, int variant);
 // Both split-k stages; ws holds rows*P (m, d) pairs.
 hipError_t launch_splitk(const Launch& L, int variant, int P, float2* ws);
-// Single-launch split-k (cooperative): ws holds rows*P (m, d) pairs, sync
-// kSyncWordsPerRow words per row (zero-initialised once), epoch grows by one
-// per call on the same sync buffer; a wait that runs out (it cannot while
-// the grid is co-resident) writes NaN and ORs kStatusLate into *status.
-constexpr int kSyncWordsPerRow = 64;
-hipError_t launch_splitk_fused(const Launch& L, int variant, int P, float2* ws, unsigned* sync,
-                               unsigned epoch, uint64_t* status);
 // Workgroups of this variant that can be resident at once on `cus` CUs.
 hipError_t splitk_fused_capacity(int variant, int dtype, bool aligned, int cus, int64_t* blocks);
 // What an ordered (single-launch split-k) launch needs besides its tensors,
@@ -96,6 +89,10 @@ struct OrderedSync {
 };
 constexpr unsigned kOrderedSpinLimit = 1u << 21;
 constexpr uint64_t kStatusLate = 1;
+// Single-launch split-k that reads every element once (cooperative launch,
+// grid rows*P, every workgroup keeps its chunk in registers; OrderedSync as
+// for the ordered form below, with 2*rows*P tag words).
+hipError_t launch_splitk_fused(const Launch& L, int variant, int P, const OrderedSync& S);
 // Split-k in one ordinary launch (kSplitk variants): grid 2*rows*P.
 hipError_t launch_splitk_ordered(const Launch& L, int variant, int P, const OrderedSync& S);
 // Epochs of eager ordered launches are handed out by the host from

@@ -1,39 +1,34 @@
-// rws_splitk_fused.hip -- split-k in a single cooperative launch.
+// rws_splitk_fused.hip -- split-k in a single cooperative launch that reads
+// every element once.
 //
-// The two-launch split-k (rws_splitk.hip) reads every chunk twice: stage 1
-// for the chunk's partial (m, d), stage 2 again to write the outputs once the
-// row's partials are merged.  Here every workgroup keeps its chunk in
-// registers between the two halves: it publishes its partial, arrives on a
-// per-row counter and waits until the row's last workgroup has arrived; then
-// it merges the row's partials and writes its chunk from registers -- one
-// read and one write per element.  The CUDA safe-online-softmax page names
-// this single-kernel form (a grid-wide sync, or atomics with polling) in
-// section 3.2 and leaves it unbuilt; the (m, d) merge is the same rule.
+// The two-launch split-k (rws_splitk.hip) and its single-launch ordered form
+// (rws_splitk_ordered.hip) read every chunk twice: once for the chunk's
+// partial (m, d), again to write the outputs once the row's partials are
+// merged.  Here every workgroup keeps its chunk in registers between the two
+// halves: it publishes its partial, waits for the partials of the row's other
+// chunks, merges them and writes its chunk from registers -- one read and one
+// write per element.  The CUDA safe-online-softmax page names this
+// single-kernel form (a grid-wide sync, or atomics with polling) in section
+// 3.2 and leaves it unbuilt; the (m, d) merge is the same rule.
 //
-// Waiting across workgroups is only safe when all of them are resident at
-// once, so the kernel is launched with hipLaunchCooperativeKernel, which
-// refuses grids that cannot be co-resident (the dispatcher then uses the
-// two-launch form).  The wait is also bounded: a workgroup that does not see
-// its row released after kSpinLimit polls stops waiting, so every wave
-// always reaches the end of the kernel; it then writes NaN for its chunk and
-// sets the stream's status word (softmax_stream_status reports it).
+// Exchange: as in the ordered form (rws_ordered.hpp), a partial travels as
+// two 64-bit words, (epoch << 32 | bits of m) and (epoch << 32 | bits of d),
+// stored and polled with relaxed agent-scope atomics; each word carries its
+// own data, so no release/acquire fence (which on this multi-XCD part writes
+// back and invalidates an XCD's L2) is needed.
 //
-// Synchronisation words (per row, in a library-owned zero-initialised
-// buffer, one 256-byte line per row so that rows do not contend): count
-// (arrivals of the current call; reset to 0 by the last arrival) and flag (the
-// epoch of the last released call).  The host passes a per-buffer epoch that
-// grows by one per call, so a flag from an earlier call never matches.
-//
-// Cost on MI355X: the agent-scope release (each arrival) and acquire (each
-// waiter) write back and invalidate the XCD's L2, which measured about
-// 34 us for fp16 [16, 1M] against 15 us for the two-launch split-k, so the
-// dispatcher does not pick this family; it is available by request.
+// Waiting for other workgroups of the grid is only safe when all of them are
+// resident at once, so the kernel is launched with hipLaunchCooperativeKernel,
+// which refuses grids that cannot be co-resident (RWS_ERR_UNSUPPORTED_SHAPE
+// then).  The wait is also bounded: a workgroup that does not see a partial
+// after the launch's spin limit stops waiting, writes NaN for its chunk and
+// sets the stream's status word (softmax_stream_status reports it), so every
+// wave always reaches the end of the kernel.
 #include "rws_kernels.hpp"
 #include "rws_launch.hpp"
+#include "rws_ordered.hpp"
 
 namespace rws {
-
-constexpr unsigned kSpinLimit = 1u << 20;  // polls of ~500 cycles: ~0.2 s
 
 // Max of the VEC elements of a raw granule (exact; NaN propagates).
 template <int DT>
@@ -54,9 +49,7 @@ constexpr int fused_min_waves() { return KC <= 4 ? 8 : KC <= 8 ? 4 : 2; }
 template <int DT, bool ALIGNED, int BLOCK, int KC>
 __global__ __launch_bounds__(BLOCK, fused_min_waves<KC>()) void k_splitk_fused(const void* __restrict__ in,
                                                         void* __restrict__ out, int64_t rows,
-                                                        int cols, int P, float2* __restrict__ ws,
-                                                        unsigned* __restrict__ sync,
-                                                        unsigned epoch, uint64_t* status,
+                                                        int cols, int P, OrderedSync S,
                                                         int same_phase) {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int W = BLOCK / 64;
@@ -64,7 +57,6 @@ __global__ __launch_bounds__(BLOCK, fused_min_waves<KC>()) void k_splitk_fused(c
     __shared__ float red_sum[W];
     __shared__ float red_max2[W];
     __shared__ float red_sum2[W];
-    __shared__ int timed_out;
     const int t = threadIdx.x;
     const int64_t b = blockIdx.x;
     const int64_t row = b / P;
@@ -73,6 +65,8 @@ __global__ __launch_bounds__(BLOCK, fused_min_waves<KC>()) void k_splitk_fused(c
     const char* tend = tensor_end<DT>(in, rows, cols);
     const RowWin<DT, ALIGNED> w(in, out, row, cols);
     const int kbase = chunk * (BLOCK * KC) + t;
+    uint64_t* row_tags = S.tags + 2 * row * P;
+    const unsigned epoch = launch_epoch(S.epoch, S.epoch_src);
 
     // The chunk stays in registers as raw 16-byte granules (half the
     // registers of fp32 for 16-bit types); granules past the window or
@@ -104,57 +98,30 @@ __global__ __launch_bounds__(BLOCK, fused_min_waves<KC>()) void k_splitk_fused(c
         }
     }
     dc = block_reduce<W, OpSum>(dc, red_sum);
-
-    // publish the partial, arrive, wait for the row's release
     if (t == 0) {
-        timed_out = 0;
-        ws[row * P + chunk] = make_float2(mc, dc);
-        unsigned* count = sync + kSyncWordsPerRow * row;
-        unsigned* flag = count + 1;
-        const unsigned old =
-            __hip_atomic_fetch_add(count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == (unsigned)(P - 1)) {
-            __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(flag, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            // Poll with relaxed loads (an acquire per poll would invalidate
-            // the L2 every iteration); one acquire fence follows the wait.
-            unsigned it = 0;
-            for (; it < kSpinLimit; ++it) {
-                if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch)
-                    break;
-                __builtin_amdgcn_s_sleep(8);
-            }
-            if (it == kSpinLimit) {
-                timed_out = 1;
-                if (status)
-                    __hip_atomic_fetch_or(status, kStatusLate, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
+        publish_word(row_tags + 2 * chunk, epoch, mc);
+        publish_word(row_tags + 2 * chunk + 1, epoch, dc);
     }
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     // Keep only the raw granules live across the wait: without this the
     // compiler would reuse the widened fp32 values of the passes above and
     // hold twice the registers.  (An empty asm statement: no instruction.)
 #pragma unroll
     for (int i = 0; i < KC; ++i) asm volatile("" : "+v"(raw[i]));
 
-    // merge the row's partials: (M, D)
+    // merge the row's partials (this chunk's own included): (M, D)
     float m = kNegInf, d = 0.0f;
+    int late = 0;
     for (int j = t; j < P; j += BLOCK) {
-        const float2 p = ws[row * P + j];
-        const float mn = vmax(m, p.x);
-        const float a = (d == 0.0f) ? 0.0f : d * merge_scale(m, mn);
-        const float bb = (p.y == 0.0f) ? 0.0f : p.y * merge_scale(p.x, mn);
-        m = mn;
-        d = a + bb;
+        const float pm = poll_word(row_tags + 2 * j, epoch, late, S.spin_limit);
+        const float pd = poll_word(row_tags + 2 * j + 1, epoch, late, S.spin_limit);
+        md_fold(m, d, pm, pd);
     }
     float M, D;
     block_merge<W>(m, d, M, D, red_max2, red_sum2);
+    const bool failed = __syncthreads_or(late) != 0;
+    if (failed && t == 0) report_late(S.status);
     const RowExp er(M);
-    const float r = timed_out ? __builtin_nanf("") : __builtin_amdgcn_rcpf(D);
+    const float r = failed ? __builtin_nanf("") : __builtin_amdgcn_rcpf(D);
 
     // y = e^(x - M) / D for the chunk held in registers
 #pragma unroll
@@ -217,8 +184,7 @@ hipError_t splitk_fused_capacity(int variant, int dtype, bool aligned, int cus, 
     return hipSuccess;
 }
 
-hipError_t launch_splitk_fused(const Launch& L, int variant, int P, float2* ws, unsigned* sync,
-                               unsigned epoch, uint64_t* status) {
+hipError_t launch_splitk_fused(const Launch& L, int variant, int P, const OrderedSync& S) {
     const void* k = fused_kernel(variant, L.dtype, L.aligned);
     if (!k) return hipErrorInvalidValue;
     const void* in = L.in;
@@ -226,9 +192,9 @@ hipError_t launch_splitk_fused(const Launch& L, int variant, int P, float2* ws, 
     int64_t rows = L.rows;
     int cols = L.cols;
     int same_phase = L.same_phase ? 1 : 0;
+    OrderedSync sync = S;
     void* args[] = {(void*)&in, (void*)&out, (void*)&rows, (void*)&cols, (void*)&P,
-                    (void*)&ws, (void*)&sync, (void*)&epoch, (void*)&status,
-                    (void*)&same_phase};
+                    (void*)&sync, (void*)&same_phase};
     return hipLaunchCooperativeKernel(k, dim3((unsigned)(L.rows * P)),
                                       dim3(kSplitkFused[variant].block), args, 0, L.stream);
 }
