@@ -45,14 +45,14 @@ PAGES_FP16_ATTN_GBPS = 134217728 / 0.62e-3 / 1e9
 # Profile summaries live in profiles/<key>_<workload>.txt.  The key is the
 # kernel family for plain softmax, else the operation.  A summary is valid
 # while the sources that define its kernels are unchanged (the copy kernel
-# used for the counter calibration lives in rws_splitk.hip).
+# used for the counter calibration lives in rws_reference.hip).
 _SOFTMAX_COMMON = ["rws_device.hpp", "rws_pre.hpp", "rws_kernels.hpp", "rws_variants.hpp",
-                   "rws_splitk.hip"]
+                   "rws_reference.hip"]
 KERNEL_SOURCES = {
     "wave_row": _SOFTMAX_COMMON + ["rws_wave_row.hip"],
     "block_onepass": _SOFTMAX_COMMON + ["rws_block_onepass.hip"],
     "two_pass": _SOFTMAX_COMMON + ["rws_two_pass.hip"],
-    "splitk": _SOFTMAX_COMMON,
+    "splitk": _SOFTMAX_COMMON + ["rws_splitk.hip"],
     "splitk_fused": _SOFTMAX_COMMON + ["rws_splitk_fused.hip"],
     "splitk_ordered": _SOFTMAX_COMMON + ["rws_ordered.hpp", "rws_splitk_ordered.hip"],
     "masked": _SOFTMAX_COMMON + ["rws_masked.hip"],
@@ -163,7 +163,7 @@ def summarize_rocprof(directory: str, workload: str, kernel: str, command: str) 
     # absolute traffic from the L2-to-memory (EA) request counters, by request
     # size, beside the copy-calibrated figure above
     ea = {}
-    for which in ("ea_rd", "ea_wr", "ea_stall", "hits"):
+    for which in ("ea_rd", "ea_wr", "ea_stall", "hits", "levels"):
         files = glob.glob(os.path.join(directory, which, "**", "*counter_collection.csv"),
                           recursive=True)
         if not files:
@@ -179,10 +179,13 @@ def summarize_rocprof(directory: str, workload: str, kernel: str, command: str) 
         lines.append("## absolute EA traffic (--pmc TCC_EA0_RDREQ{,_128B,_64B,_32B}_sum; "
                      "--pmc TCC_EA0_WRREQ{,_64B}_sum TCC_EA0_{RD,WR}REQ_DRAM_sum; "
                      "--pmc TCC_EA0_{RD,WR}REQ_DRAM_CREDIT_STALL_sum TCC_EA0_WRREQ_STALL_sum "
-                     "GRBM_GUI_ACTIVE; --pmc TCC_HIT_sum TCC_MISS_sum; per dispatch)")
+                     "GRBM_GUI_ACTIVE; --pmc TCC_HIT_sum TCC_MISS_sum; --pmc "
+                     "TCC_EA0_{RD,WR}REQ_LEVEL_sum TCC_EA0_{RD,WR}REQ_sum GRBM_GUI_ACTIVE; "
+                     "per dispatch)")
         lines.append("read bytes = 128*RDREQ_128B + 64*RDREQ_64B + 32*RDREQ_32B; write bytes = "
                      "64*WRREQ_64B + 32*(WRREQ - WRREQ_64B); stalls are cycles summed over the "
-                     "L2 channels, per GRBM_GUI_ACTIVE cycle")
+                     "L2 channels, per GRBM_GUI_ACTIVE cycle; latency = LEVEL / requests "
+                     "(cycles), in flight = LEVEL / GRBM_GUI_ACTIVE (requests, all channels)")
         for n in sorted(ea):
             if not (sym in n or "k_copy16" in n):
                 continue
@@ -209,6 +212,12 @@ def summarize_rocprof(directory: str, workload: str, kernel: str, command: str) 
                 v = mean(per, c)
                 if v is not None and gui:
                     parts.append(f"{c[8:-4]} {v:.0f} ({v / gui:.3f}/cycle)")
+            for kind in ("RD", "WR"):
+                lvl = mean(per, f"TCC_EA0_{kind}REQ_LEVEL_sum")
+                req = mean(per, f"TCC_EA0_{kind}REQ_sum")
+                if lvl is not None and req and gui:
+                    parts.append(f"{kind} latency {lvl / req:.0f} cycles, in flight "
+                                 f"{lvl / gui:.0f}")
             hit, miss = mean(per, "TCC_HIT_sum"), mean(per, "TCC_MISS_sum")
             if hit is not None and miss is not None and hit + miss > 0:
                 parts.append(f"L2 hit {hit:.0f} miss {miss:.0f} ({hit / (hit + miss):.3f})")
@@ -355,6 +364,89 @@ def norm_cpu_baseline(w, x_stored_f64, mode: str, target_s: float = 10.0) -> dic
 
 
 # --------------------------------------------------------------------------
+# HBM ceilings: the copy, read-only and write-only references and the fp16
+# softmax of rows of 512 over a sweep of sizes
+# --------------------------------------------------------------------------
+def ceilings(steps: int, warmup: int) -> dict:
+    """Per-call time of the 16-byte copy, read-only and write-only kernels
+    and of the fp16 [rows,512] softmax, for 16..256 MiB per direction, each
+    over rotating buffers whose inputs fill 1 GiB, median of REPEATS windows
+    of `steps` calls.  A least-squares line t = t0 + bytes / rate over the
+    sizes >= 64 MiB separates the fixed cost of a launch (t0: ramp-up and
+    drain) from the streaming rate."""
+    import torch
+    import row_wise_safe_amd as rws
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sh = int(stream.cuda_stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def median_us(call):
+        for i in range(warmup):
+            call(i)
+        out = []
+        for r in range(REPEATS):
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(steps):
+                call(r * steps + i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) * 1e3 / steps)
+        return statistics.median(out)
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(20260010)
+    rows_out = []
+    for mib in (16, 32, 64, 128, 256):
+        nbytes = mib << 20
+        nbuf = max(2, (1 << 30) // nbytes)
+        xs = [torch.randn(nbytes // 2, generator=g, device=dev).mul_(8.0).to(torch.float16)
+              for _ in range(nbuf)]
+        ys = [torch.empty_like(x) for x in xs]
+        rows = nbytes // 1024
+        log(f"[bench] ceilings {mib} MiB, {nbuf} buffers")
+        t = {
+            "copy": median_us(lambda i: rws.softmax_copy_bytes(
+                xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), nbytes, sh)),
+            "read_only": median_us(lambda i: rws.softmax_read_bytes(
+                xs[i % nbuf].data_ptr(), nbytes, sh)),
+            "write_only": median_us(lambda i: rws.softmax_write_bytes(
+                ys[i % nbuf].data_ptr(), nbytes, sh)),
+            "softmax_fp16_512": median_us(lambda i: rws.softmax_fwd(
+                xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), rows, 512, rws.RWS_F16, sh)),
+        }
+        moved = {"copy": 2 * nbytes, "read_only": nbytes, "write_only": nbytes,
+                 "softmax_fp16_512": 2 * nbytes}
+        entry = {"MiB_per_direction": mib}
+        for k, us in t.items():
+            gbps = moved[k] / (us * 1e-6) / 1e9
+            entry[k] = {"us": round(us, 3), "GBps": round(gbps, 1),
+                        "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+        log("[bench]   " + ", ".join(f"{k} {v['us']} us ({v['frac_of_peak']:.3f})"
+                                     for k, v in entry.items() if isinstance(v, dict)))
+        rows_out.append(entry)
+        del xs, ys
+        torch.cuda.empty_cache()
+    fit = {}
+    big = [e for e in rows_out if e["MiB_per_direction"] >= 64]
+    for k in ("copy", "read_only", "write_only", "softmax_fp16_512"):
+        mult = 1 if k in ("read_only", "write_only") else 2
+        xb = [mult * (e["MiB_per_direction"] << 20) for e in big]
+        yt = [e[k]["us"] for e in big]
+        mx, my = statistics.fmean(xb), statistics.fmean(yt)
+        slope = sum((a - mx) * (b - my) for a, b in zip(xb, yt)) / sum((a - mx) ** 2 for a in xb)
+        rate = 1e-3 / slope  # GB/s from us per byte
+        fit[k] = {"fixed_us_per_launch": round(my - slope * mx, 3),
+                  "streaming_GBps": round(rate, 1),
+                  "streaming_frac_of_peak": round(rate / PEAK_HBM_GBPS, 4)}
+    return {"ceilings": rows_out, "fit_over_64_to_256_MiB": fit,
+            "protocol": f"median of {REPEATS} windows of {steps} calls after {warmup} warm-up "
+                        "calls; inputs rotate over 1 GiB; bytes moved = read + written"}
+
+
+# --------------------------------------------------------------------------
 # main
 # --------------------------------------------------------------------------
 def main() -> int:
@@ -389,6 +481,9 @@ def main() -> int:
                          "names the key (a softmax family, or masked, backward, layernorm, "
                          "rmsnorm)")
     ap.add_argument("--profile-command", default="")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="time the copy, read-only and write-only references and the fp16 "
+                         "[rows,512] softmax over 16..256 MiB and fit fixed cost + streaming rate")
     args = ap.parse_args()
 
     if args.summarize_rocprof:
@@ -413,6 +508,9 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     rws.load_library()
+    if args.ceilings:
+        print(json.dumps(ceilings(args.steps, args.warmup)), flush=True)
+        return 0
     if args.norm:
         if args.masked or args.backward:
             print("--norm excludes --masked and --backward", file=sys.stderr)
@@ -420,7 +518,8 @@ def main() -> int:
         name = args.workload if args.workload in workloads.NORM_WORKLOADS else "ln_fp16_131040x192"
         w = workloads.NORM_WORKLOADS[name]
     else:
-        w = workloads.WORKLOADS[args.workload]
+        w = (workloads.WORKLOADS.get(args.workload)
+             or workloads.LONG_ROW_WORKLOADS[args.workload])
     dev = torch.device("cuda:0")
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
     code = rws.dtype_code(tdt)

@@ -389,6 +389,18 @@ int softmax_set_wait_limit(int64_t tries);
  */
 int softmax_copy_bytes(const void *in, void *out, int64_t bytes, void *stream);
 
+/*
+ * softmax_read_bytes, softmax_write_bytes -- a pure read stream (`bytes` of
+ * `in` read non-temporally, nothing written) and a pure write stream
+ * (`bytes` of `out` overwritten with a pattern of the 16-byte granule index,
+ * written through when `out` is 128-byte aligned), with 16-byte accesses and
+ * 16 KiB per workgroup, on `stream`: the HBM ceilings of reading alone and
+ * of writing alone beside the copy's mixed stream.  Pointers and `bytes`
+ * 16-byte aligned.  Returns RWS_OK or an error status.
+ */
+int softmax_read_bytes(const void *in, int64_t bytes, void *stream);
+int softmax_write_bytes(void *out, int64_t bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

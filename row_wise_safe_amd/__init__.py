@@ -34,6 +34,7 @@ __all__ = [
     "softmax_bwd_describe_launch",
     "softmax_kernel_name", "softmax_status_string", "softmax_last_error", "softmax_copy_bytes",
     "softmax_stream_status", "softmax_set_wait_limit", "stream_status",
+    "softmax_read_bytes", "softmax_write_bytes",
     "layernorm_fwd", "layernorm_fwd_kernel", "rmsnorm_fwd", "rmsnorm_fwd_kernel",
     "softmax", "softmax_masked", "softmax_backward", "layer_norm", "rms_norm", "copy_bytes",
     "dtype_code", "SoftmaxError",
@@ -113,6 +114,10 @@ def load_library():
     lib.softmax_last_error.restype = ctypes.c_char_p
     lib.softmax_copy_bytes.argtypes = [vp, vp, i64, vp]
     lib.softmax_copy_bytes.restype = cint
+    lib.softmax_read_bytes.argtypes = [vp, i64, vp]
+    lib.softmax_read_bytes.restype = cint
+    lib.softmax_write_bytes.argtypes = [vp, i64, vp]
+    lib.softmax_write_bytes.restype = cint
     lib.softmax_stream_status.argtypes = [vp]
     lib.softmax_stream_status.restype = cint
     lib.softmax_set_wait_limit.argtypes = [i64]
@@ -254,6 +259,14 @@ def softmax_last_error() -> str:
 
 def softmax_copy_bytes(in_ptr: int, out_ptr: int, nbytes: int, stream: int) -> int:
     return load_library().softmax_copy_bytes(in_ptr, out_ptr, nbytes, stream)
+
+
+def softmax_read_bytes(in_ptr: int, nbytes: int, stream: int) -> int:
+    return load_library().softmax_read_bytes(in_ptr, nbytes, stream)
+
+
+def softmax_write_bytes(out_ptr: int, nbytes: int, stream: int) -> int:
+    return load_library().softmax_write_bytes(out_ptr, nbytes, stream)
 
 
 def softmax_stream_status(stream: int) -> int:

@@ -24,6 +24,7 @@ SOURCES = [
     "rws_block_onepass.hip",
     "rws_two_pass.hip",
     "rws_splitk.hip",
+    "rws_reference.hip",
     "rws_splitk_fused.hip",
     "rws_splitk_ordered.hip",
     "rws_masked.hip",

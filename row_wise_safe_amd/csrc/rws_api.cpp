@@ -1696,4 +1696,28 @@ int softmax_copy_bytes(const void* in, void* out, int64_t bytes, void* stream) {
     return RWS_OK;
 }
 
+int softmax_read_bytes(const void* in, int64_t bytes, void* stream) {
+    g_last_error.clear();
+    if (bytes < 0) return fail(RWS_ERR_INVALID_ARG, "bytes must be >= 0");
+    if (bytes == 0) return RWS_OK;
+    if (!in) return fail(RWS_ERR_INVALID_ARG, "NULL pointer");
+    if ((uintptr_t)in % 16 || bytes % 16)
+        return fail(RWS_ERR_MISALIGNED, "read needs a 16-byte aligned pointer and size");
+    hipError_t e = rws::launch_read16(in, bytes / 16, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(RWS_ERR_HIP, std::string("read launch: ") + hipGetErrorString(e));
+    return RWS_OK;
+}
+
+int softmax_write_bytes(void* out, int64_t bytes, void* stream) {
+    g_last_error.clear();
+    if (bytes < 0) return fail(RWS_ERR_INVALID_ARG, "bytes must be >= 0");
+    if (bytes == 0) return RWS_OK;
+    if (!out) return fail(RWS_ERR_INVALID_ARG, "NULL pointer");
+    if ((uintptr_t)out % 16 || bytes % 16)
+        return fail(RWS_ERR_MISALIGNED, "write needs a 16-byte aligned pointer and size");
+    hipError_t e = rws::launch_write16(out, bytes / 16, (hipStream_t)stream);
+    if (e != hipSuccess) return fail(RWS_ERR_HIP, std::string("write launch: ") + hipGetErrorString(e));
+    return RWS_OK;
+}
+
 }  // extern "C"

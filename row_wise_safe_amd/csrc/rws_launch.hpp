@@ -178,7 +178,10 @@ hipError_t launch_norm_block(const NormLaunch& L, int family, int variant);
 constexpr int kNormOrderedBlock = 256;
 constexpr int kNormOrderedKc = 4;
 hipError_t launch_norm_ordered(const NormLaunch& L, int P, const OrderedSync& S);
-// n16 granules of 16 bytes.
+// n16 granules of 16 bytes: copy, read only, write only (the references of
+// the roofline).
 hipError_t launch_copy16(const void* in, void* out, int64_t n16, hipStream_t stream);
+hipError_t launch_read16(const void* in, int64_t n16, hipStream_t stream);
+hipError_t launch_write16(void* out, int64_t n16, hipStream_t stream);
 
 }  // namespace rws

@@ -1,6 +1,5 @@
 // rws_splitk.hip -- instantiations and launcher of the split-k family
-// (stage 1 partial (m, d) per chunk, stage 2 merge + normalise), plus the
-// 16-byte copy kernel used as the bandwidth reference.
+// (stage 1 partial (m, d) per chunk, stage 2 merge + normalise).
 #include "rws_kernels.hpp"
 #include "rws_launch.hpp"
 #include "rws_variants.hpp"
@@ -44,46 +43,6 @@ hipError_t launch_splitk(const Launch& L, int variant, int P, float2* ws) {
     RWS_SPLITK_VARIANTS(RWS_CASE)
 #undef RWS_CASE
     return hipErrorInvalidValue;
-}
-
-// ===========================================================================
-// Plain 16-byte copy (the copy ceiling and the calibration of the traffic
-// counters): one granule per thread, non-temporal loads, one-wave
-// workgroups -- like the wave_row kernels -- and, when the output starts on a
-// 128-byte line, write-through stores (store16_wt).  The fastest copy of
-// HBM-resident data measured on MI355X: 64 MiB in 21.1 us (21.7 us with
-// plain non-temporal stores, 23.1 us with cached loads and four-wave
-// workgroups).
-// ===========================================================================
-template <bool WT>
-__global__ __launch_bounds__(64) void k_copy16(const u32x4* __restrict__ in,
-                                               u32x4* __restrict__ out, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
-    if (i >= n) return;
-    const u32x4 v = __builtin_nontemporal_load(in + i);
-    if (WT)
-        store16_wt((char*)(out + i), v);
-    else
-        __builtin_nontemporal_store(v, out + i);
-}
-
-hipError_t launch_copy16(const void* in, void* out, int64_t n16, hipStream_t stream) {
-    const bool wt = (uintptr_t)out % 128 == 0;
-    for (int64_t done = 0; done < n16;) {
-        // at most 2^25 one-wave workgroups per launch
-        const int64_t n = std::min<int64_t>(n16 - done, (int64_t)1 << 31);
-        const dim3 grid((unsigned)((n + 63) / 64));
-        if (wt)
-            hipLaunchKernelGGL(k_copy16<true>, grid, dim3(64), 0, stream,
-                               (const u32x4*)in + done, (u32x4*)out + done, n);
-        else
-            hipLaunchKernelGGL(k_copy16<false>, grid, dim3(64), 0, stream,
-                               (const u32x4*)in + done, (u32x4*)out + done, n);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        done += n;
-    }
-    return hipSuccess;
 }
 
 }  // namespace rws

@@ -94,6 +94,12 @@ def test_copy_argument_checks(lib):
     assert rws.softmax_copy_bytes(16, 32, 15, 0) == rws.RWS_ERR_MISALIGNED
     assert rws.softmax_copy_bytes(16, 32, -16, 0) == rws.RWS_ERR_INVALID_ARG
     assert rws.softmax_copy_bytes(0, 0, 0, 0) == rws.RWS_OK
+    for fn in (rws.softmax_read_bytes, rws.softmax_write_bytes):
+        assert fn(16, 15, 0) == rws.RWS_ERR_MISALIGNED
+        assert fn(24, 32, 0) == rws.RWS_ERR_MISALIGNED
+        assert fn(16, -16, 0) == rws.RWS_ERR_INVALID_ARG
+        assert fn(0, 16, 0) == rws.RWS_ERR_INVALID_ARG
+        assert fn(0, 0, 0) == rws.RWS_OK
 
 
 def test_forced_wave_row_rejects_long_rows(lib):

@@ -18,7 +18,7 @@ import row_wise_safe_amd as rws
 import workloads
 from golden_io import load
 from gpu_util import NotCoResident, empty_like_at, have_gpu, run, supports, to_device
-from tolerance import check
+from tolerance import check, check_long_rows
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not have_gpu(), reason="needs an MI355X GPU")]
@@ -70,6 +70,22 @@ def test_workload_full_size(name):
         assert np.all(k > 0)
         assert np.max(np.abs(np.where(spikes, y - 1.0 / k, 0.0))) <= 1e-3
         assert np.all(np.where(~spikes, y == 0.0, True))
+
+
+@pytest.mark.parametrize("name", list(workloads.LONG_ROW_WORKLOADS))
+def test_long_row_workload_full_size(name):
+    # rows of 8M columns (512 chunks per row: the single launch) and 32M
+    # columns (2048 chunks, more than the single launch polls: two launches)
+    w = workloads.LONG_ROW_WORKLOADS[name]
+    x, stored = to_device(w.generate(), w.dtype)
+    desc = rws.softmax_describe_launch(w.rows, w.cols, rws.RWS_F16, x.data_ptr(), x.data_ptr())
+    print(f"\n{name}: {desc}", flush=True)
+    want = {"fp16_4x8M": "splitk_ordered<", "fp16_4x32M": "splitk<"}[name]
+    assert desc.startswith(want), desc
+    y = run(x, torch.empty_like(x))
+    del x
+    m = check_long_rows(y, oracle.safe_softmax(stored), w.dtype, name)
+    print(f"{name}: {m}", flush=True)
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
@@ -327,3 +343,24 @@ def test_copy_bytes():
     rws.copy_bytes(a, b)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_read_and_write_references():
+    # the write reference fills granule i with (i, i >> 32, 0x5a5a5a5a, ~i); the
+    # read reference leaves its input and everything else untouched
+    n16 = 1 << 16
+    buf = torch.zeros(4 * n16 + 64, dtype=torch.int32, device="cuda")
+    out = buf[32:32 + 4 * n16]  # 128-byte aligned: written through
+    s = torch.cuda.current_stream().cuda_stream
+    assert rws.softmax_write_bytes(out.data_ptr(), 16 * n16, s) == rws.RWS_OK
+    before = buf.clone()
+    assert rws.softmax_read_bytes(out.data_ptr(), 16 * n16, s) == rws.RWS_OK
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)
+    got = out.view(n16, 4).cpu().numpy().view(np.uint32)
+    i = np.arange(n16, dtype=np.uint64)
+    assert np.array_equal(got[:, 0], (i & 0xffffffff).astype(np.uint32))
+    assert np.array_equal(got[:, 1], (i >> 32).astype(np.uint32))
+    assert np.all(got[:, 2] == 0x5a5a5a5a)
+    assert np.array_equal(got[:, 3], (~i & 0xffffffff).astype(np.uint32))
+    assert torch.all(buf[:32] == 0) and torch.all(buf[32 + 4 * n16:] == 0)

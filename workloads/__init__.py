@@ -24,6 +24,9 @@ Workloads, each named by what it is (dtype, shape, value distribution):
   [1,32760,384] tokens x hidden width), as activations with a per-row offset
   and spread: x = mu_r + sigma_r * z, mu_r ~ U[-4, 4], sigma_r ~ U[0.25, 4],
   z ~ N(0, 1).
+* ``fp16_4x8M``, ``fp16_4x32M`` (in ``LONG_ROW_WORKLOADS``) -- the longest
+  rows the CUDA safe-online-softmax page times its split-k on (section 4:
+  [4, 8388608] and [4, 33554432] fp16), drawn like ``fp16_16x1M``.
 
 Seeds are ``20260000 + k`` for the k-th workload of the list above (the worked
 example shares k = 1 with the 64x1000 tensor but is not random).
@@ -38,6 +41,7 @@ __all__ = [
     "Workload",
     "WORKLOADS",
     "NORM_WORKLOADS",
+    "LONG_ROW_WORKLOADS",
     "generate",
     "normal",
     "uniform",
@@ -171,6 +175,19 @@ NORM_WORKLOADS: dict[str, Workload] = {
                  {}, "fp16 [1,131040,192] tokens, per-row offset/spread normal"),
         Workload("ln_fp16_32760x384", "f16", 32760, 384, 20260007, "row_shifted_normal",
                  {}, "fp16 [1,32760,384] tokens, per-row offset/spread normal"),
+    ]
+}
+
+
+# Few rows of many millions of columns (more chunks per row than the
+# single-launch split-k polls; the two-launch form runs them).
+LONG_ROW_WORKLOADS: dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("fp16_4x8M", "f16", 4, 8388608, 20260008, "argmax_moved_normal",
+                 dict(sigma=3.0), "fp16 [4,8388608] N(0,3^2), argmax at a random column"),
+        Workload("fp16_4x32M", "f16", 4, 33554432, 20260009, "argmax_moved_normal",
+                 dict(sigma=3.0), "fp16 [4,33554432] N(0,3^2), argmax at a random column"),
     ]
 }
 
