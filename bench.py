@@ -186,6 +186,7 @@ def summarize_rocprof(directory: str, workload: str, kernel: str, command: str) 
                      "64*WRREQ_64B + 32*(WRREQ - WRREQ_64B); stalls are cycles summed over the "
                      "L2 channels, per GRBM_GUI_ACTIVE cycle; latency = LEVEL / requests "
                      "(cycles), in flight = LEVEL / GRBM_GUI_ACTIVE (requests, all channels)")
+        abs_total = None
         for n in sorted(ea):
             if not (sym in n or "k_copy16" in n):
                 continue
@@ -223,11 +224,15 @@ def summarize_rocprof(directory: str, workload: str, kernel: str, command: str) 
                 parts.append(f"L2 hit {hit:.0f} miss {miss:.0f} ({hit / (hit + miss):.3f})")
             lines.append(" ".join(parts))
             if rd is not None and wr is not None and sym in n:
-                lines.append(f"absolute_bytes_per_launch: {rd + wr:.0f}"
-                             + (f"  (/ algorithmic {(rd + wr) / meta['bytes_per_call']:.4f}"
-                                if meta.get("bytes_per_call") else "")
-                             + (f", / copy-calibrated {(rd + wr) / traffic:.4f})" if traffic
-                                else ")" if meta.get("bytes_per_call") else ""))
+                abs_total = (abs_total or 0.0) + rd + wr
+        if abs_total is not None:
+            lines.append(f"absolute_bytes_per_launch: {abs_total:.0f}"
+                         + (f"  (/ algorithmic {abs_total / meta['bytes_per_call']:.4f}"
+                            if meta.get("bytes_per_call") else "")
+                         + (f", / copy-calibrated {abs_total / traffic:.4f})" if traffic
+                            else ")" if meta.get("bytes_per_call") else "")
+                         + ("  (sum of the step's kernels)" if sum(sym in n for n in ea) > 1
+                            else ""))
         lines.append("")
     # occupancy and vector-ALU activity (one derived metric per pass)
     extra = []
@@ -456,6 +461,13 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="fp16_attn_4x32x512x512")
     ap.add_argument("--kernel", default="auto")
+    ap.add_argument("--variant", type=int, default=-1,
+                    help="with --kernel FAMILY: that entry of the family's compiled shapes "
+                         "(softmax_fwd_variant) instead of the dispatcher's choice")
+    ap.add_argument("--shape", default=None, metavar="ROWSxCOLS",
+                    help="an N(0, 4^2) input of this shape instead of a named workload")
+    ap.add_argument("--dtype", default="f16", choices=["f32", "f16", "bf16"],
+                    help="with --shape: the element type")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--masked", action="store_true",
                     help="attention-score form: softmax(x/8 + mask[S,S] + causal) with S = cols "
@@ -517,6 +529,10 @@ def main() -> int:
             return 2
         name = args.workload if args.workload in workloads.NORM_WORKLOADS else "ln_fp16_131040x192"
         w = workloads.NORM_WORKLOADS[name]
+    elif args.shape:
+        r, c = (int(v) for v in args.shape.lower().split("x"))
+        w = workloads.Workload(f"{args.dtype}_{r}x{c}", args.dtype, r, c, 20260020, "normal",
+                               dict(sigma=4.0), f"{args.dtype} [{r},{c}] N(0,4^2)")
     else:
         w = (workloads.WORKLOADS.get(args.workload)
              or workloads.LONG_ROW_WORKLOADS[args.workload])
@@ -542,8 +558,15 @@ def main() -> int:
     ys = [torch.empty_like(xs[0]) for _ in range(nbuf)]
     stream = torch.cuda.current_stream(dev)
     sh = int(stream.cuda_stream)
-    desc = rws.softmax_describe_launch(w.rows, w.cols, code, xs[0].data_ptr(), ys[0].data_ptr(),
-                                       kid, masked=args.masked)
+    if args.variant >= 0:
+        if kid == 0 or args.masked or args.backward or args.norm:
+            print("--variant needs --kernel FAMILY of the plain forward", file=sys.stderr)
+            return 2
+        desc = rws.softmax_describe_variant(w.rows, w.cols, code, xs[0].data_ptr(),
+                                            ys[0].data_ptr(), kid, args.variant)
+    else:
+        desc = rws.softmax_describe_launch(w.rows, w.cols, code, xs[0].data_ptr(),
+                                           ys[0].data_ptr(), kid, masked=args.masked)
     family = desc.split("<")[0]
     if args.norm:
         desc = f"{args.norm} {args.kernel}"
@@ -594,6 +617,9 @@ def main() -> int:
         elif dys is not None:
             st = rws.softmax_bwd_kernel(xs[i % nbuf].data_ptr(), dys[i % nbuf].data_ptr(),
                                         ys[i % nbuf].data_ptr(), w.rows, w.cols, code, sh, kid)
+        elif mask is None and args.variant >= 0:
+            st = rws.softmax_fwd_variant(xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), w.rows,
+                                         w.cols, code, sh, kid, args.variant)
         elif mask is None:
             st = rws.softmax_fwd_kernel(xs[i % nbuf].data_ptr(), ys[i % nbuf].data_ptr(), w.rows,
                                         w.cols, code, sh, kid)
@@ -731,6 +757,7 @@ def main() -> int:
     traffic = None if args.affine else read_traffic(w.name, profile_key)
     achieved = nbytes / (ms * 1e-3) / 1e9
     headline = (w.name == "fp16_attn_4x32x512x512" and mask is None and dys is None
+                and args.variant < 0
                 and not args.norm)
     vs = round(gbps / PAGES_FP16_ATTN_GBPS, 3) if headline else None
     result = {

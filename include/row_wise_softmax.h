@@ -323,6 +323,31 @@ int softmax_describe_launch_masked(int64_t rows, int64_t cols, int dtype, const 
                                    const void *out, int kernel_id, char *buf, int64_t buflen);
 
 /*
+ * softmax_fwd_variant -- as softmax_fwd_kernel(kernel_id), with entry
+ * `variant` (0 .. softmax_variant_count(kernel_id) - 1) of that family's
+ * compiled shapes instead of the dispatcher's choice: lane-group size and
+ * granules per lane (wave_row), workgroup size and granules per thread
+ * (block_onepass, two_pass), chunk shape (the split-k forms).  The
+ * measurement surface that lets both candidates of a dispatcher threshold be
+ * timed and profiled on one shape.  RWS_ERR_INVALID_ARG for RWS_KERNEL_AUTO
+ * or variant < 0, RWS_ERR_UNSUPPORTED_SHAPE when the variant cannot hold the
+ * row (or its split-k grid would not fit).  Arguments otherwise as
+ * softmax_fwd_kernel.
+ */
+int softmax_fwd_variant(const void *in, void *out, int64_t rows, int64_t cols, int dtype,
+                        void *stream, int kernel_id, int variant);
+
+/* Number of compiled variants of a kernel family (0 for RWS_KERNEL_AUTO or an
+ * unknown id).  No GPU work. */
+int softmax_variant_count(int kernel_id);
+
+/* The launch softmax_fwd_variant would make, as softmax_describe_launch.
+ * No GPU work. */
+int softmax_describe_variant(int64_t rows, int64_t cols, int dtype, const void *in,
+                             const void *out, int kernel_id, int variant, char *buf,
+                             int64_t buflen);
+
+/*
  * softmax_bwd_describe_launch -- the same for the launch
  * softmax_bwd_kernel(kernel_id) would make with these y and dx pointers
  * (bwd_wave, bwd_block, bwd_stream or bwd_ordered, with its shape).

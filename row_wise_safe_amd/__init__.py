@@ -35,6 +35,7 @@ __all__ = [
     "softmax_kernel_name", "softmax_status_string", "softmax_last_error", "softmax_copy_bytes",
     "softmax_stream_status", "softmax_set_wait_limit", "stream_status",
     "softmax_read_bytes", "softmax_write_bytes",
+    "softmax_fwd_variant", "softmax_variant_count", "softmax_describe_variant",
     "layernorm_fwd", "layernorm_fwd_kernel", "rmsnorm_fwd", "rmsnorm_fwd_kernel",
     "softmax", "softmax_masked", "softmax_backward", "layer_norm", "rms_norm", "copy_bytes",
     "dtype_code", "SoftmaxError",
@@ -114,6 +115,13 @@ def load_library():
     lib.softmax_last_error.restype = ctypes.c_char_p
     lib.softmax_copy_bytes.argtypes = [vp, vp, i64, vp]
     lib.softmax_copy_bytes.restype = cint
+    lib.softmax_fwd_variant.argtypes = [vp, vp, i64, i64, cint, vp, cint, cint]
+    lib.softmax_fwd_variant.restype = cint
+    lib.softmax_variant_count.argtypes = [cint]
+    lib.softmax_variant_count.restype = cint
+    lib.softmax_describe_variant.argtypes = [i64, i64, cint, vp, vp, cint, cint, ctypes.c_char_p,
+                                             i64]
+    lib.softmax_describe_variant.restype = cint
     lib.softmax_read_bytes.argtypes = [vp, i64, vp]
     lib.softmax_read_bytes.restype = cint
     lib.softmax_write_bytes.argtypes = [vp, i64, vp]
@@ -259,6 +267,26 @@ def softmax_last_error() -> str:
 
 def softmax_copy_bytes(in_ptr: int, out_ptr: int, nbytes: int, stream: int) -> int:
     return load_library().softmax_copy_bytes(in_ptr, out_ptr, nbytes, stream)
+
+
+def softmax_fwd_variant(in_ptr: int, out_ptr: int, rows: int, cols: int, dtype: int, stream: int,
+                        kernel_id: int, variant: int) -> int:
+    return load_library().softmax_fwd_variant(in_ptr, out_ptr, rows, cols, dtype, stream,
+                                              kernel_id, variant)
+
+
+def softmax_variant_count(kernel_id: int) -> int:
+    return load_library().softmax_variant_count(kernel_id)
+
+
+def softmax_describe_variant(rows: int, cols: int, dtype: int, in_ptr: int = 0, out_ptr: int = 0,
+                             kernel_id: int = 1, variant: int = 0) -> str:
+    buf = ctypes.create_string_buffer(256)
+    st = load_library().softmax_describe_variant(rows, cols, dtype, in_ptr, out_ptr, kernel_id,
+                                                 variant, buf, len(buf))
+    if st != RWS_OK:
+        raise SoftmaxError(st, softmax_last_error())
+    return buf.value.decode()
 
 
 def softmax_read_bytes(in_ptr: int, nbytes: int, stream: int) -> int:

@@ -76,7 +76,8 @@ DeviceInfo device_info() {
     return info;
 }
 
-constexpr int kOrderedMaxP = 1024;
+constexpr int kOrderedMaxP = 512;
+constexpr int64_t kOrderedMaxBytes = (int64_t)32 << 20;
 
 bool is_splitk(int family) {
     return family == RWS_KERNEL_SPLITK || family == RWS_KERNEL_SPLITK_FUSED ||
@@ -351,8 +352,16 @@ int pick_splitk_fused(int64_t rows, int64_t wmax, int dtype, bool aligned, int c
     return best;
 }
 
+// forced_variant >= 0 (measurement surface, softmax_fwd_variant): that entry
+// of the family's variant table instead of the dispatcher's choice, when it
+// can hold the row.
 int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
-                         int kernel_id, Plan* p, bool masked) {
+                         int kernel_id, Plan* p, bool masked, int forced_variant = -1) {
+    auto bad_variant = [&](int n) {
+        return fail(RWS_ERR_UNSUPPORTED_SHAPE,
+                    "variant " + std::to_string(forced_variant) + " of " +
+                        std::to_string(n) + " cannot take this shape");
+    };
     const Geometry g = geometry(cols, dtype, in, out);
     p->same_phase = g.same_phase;
     const int64_t wline = window_granules(g, 128);  // block-level kernels
@@ -365,23 +374,33 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
     // (One wave per row with 4 or 8 granules per lane measured slower than
     // block_onepass at every row count tried: fp16 [32768,1000] 27.2 us
     // against 24.5, fp16 [16384,2000] 32.8 against 23.5.)
+    // "Few long rows" (rows of >= 2048 granules) takes split-k over
+    // block_onepass when block_onepass cannot hold the row, or would leave
+    // more than half the CUs without a row, or leaves half of them idle and
+    // parks part of the row in LDS.  MI355X, fp16, inputs in HBM, ordered
+    // split-k against block_onepass: [64,65536] 7.76 against 8.98 us;
+    // [128,131072] 14.4 against 18.8 (LDS parking); but [128,65536] 9.81
+    // against 9.48, [256,65536] 14.5 against 14.1, [256,16384] 7.71 against
+    // 5.42, [384,65536] 25.0 against 22.3, [256,131072] 32.0 against 29.9.
     int family = kernel_id;
     if (family == RWS_KERNEL_AUTO) {
         const bool few_rows = rows < 2LL * cus;
-        const bool onepass_fits = pick_onepass(wline, rows, cus, false, g.a128, dtype) >= 0;
+        const int ov = pick_onepass(wline, rows, cus, false, g.a128, dtype);
+        const bool onepass_fits = ov >= 0;
+        const bool parks = onepass_fits && rws::kOnepass[ov].kl > 0;
+        const bool splitk_rows =
+            !onepass_fits || 2 * rows < cus || (2 * rows <= cus && parks);
         if (pick_wave_row(g, masked, 1) >= 0) {
             family = RWS_KERNEL_WAVE_ROW;
-        } else if (few_rows && wline >= 2048) {
+        } else if (few_rows && wline >= 2048 && splitk_rows) {
             family = RWS_KERNEL_SPLITK_ORDERED;
         } else if (wline <= 128 && !few_waves(rows, wline, cus) &&
                    pick_wave_row(g, masked, 2) >= 0) {
             family = RWS_KERNEL_WAVE_ROW;
-        } else if (onepass_fits && wline <= 8192) {
+        } else if (onepass_fits) {
             family = RWS_KERNEL_BLOCK_ONEPASS;
         } else if (few_rows) {
             family = RWS_KERNEL_SPLITK_ORDERED;
-        } else if (onepass_fits) {
-            family = RWS_KERNEL_BLOCK_ONEPASS;
         } else {
             family = RWS_KERNEL_TWO_PASS;
         }
@@ -401,6 +420,13 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
     switch (family) {
         case RWS_KERNEL_WAVE_ROW: {
             p->variant = pick_wave_row(g, masked);
+            if (forced_variant >= 0) {
+                if (forced_variant >= rws::kNumWaveRow) return bad_variant(rws::kNumWaveRow);
+                const rws::WaveRowVariant& f = rws::kWaveRow[forced_variant];
+                if ((int64_t)f.G * f.K < window_granules(g, wave_row_wa(f)))
+                    return bad_variant(rws::kNumWaveRow);
+                p->variant = forced_variant;
+            }
             if (p->variant < 0)
                 return fail(RWS_ERR_UNSUPPORTED_SHAPE,
                             "wave_row holds at most 512 granules (16 bytes) per row window");
@@ -417,6 +443,13 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
         }
         case RWS_KERNEL_BLOCK_ONEPASS: {
             p->variant = pick_onepass(wline, rows, cus, masked, g.a128, dtype);
+            if (forced_variant >= 0) {
+                if (forced_variant >= rws::kNumOnepass) return bad_variant(rws::kNumOnepass);
+                const rws::OnepassVariant& f = rws::kOnepass[forced_variant];
+                if (onepass_capacity(f) < wline || (masked && f.kl != 0))
+                    return bad_variant(rws::kNumOnepass);
+                p->variant = forced_variant;
+            }
             if (p->variant < 0)
                 return fail(RWS_ERR_UNSUPPORTED_SHAPE,
                             "block_onepass holds at most 16384 granules (16 bytes) per row window "
@@ -432,12 +465,26 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
             p->variant = 0;
             for (int i = 0; i < rws::kNumTwoPass; ++i)
                 if (rws::kTwoPass[i].block == want_block && rws::kTwoPass[i].u == 4) p->variant = i;
+            if (forced_variant >= 0) {
+                if (forced_variant >= rws::kNumTwoPass) return bad_variant(rws::kNumTwoPass);
+                p->variant = forced_variant;
+            }
             p->max_rows_per_launch = block_rows_per_launch(rws::kTwoPass[p->variant].block);
             break;
         }
         case RWS_KERNEL_SPLITK_FUSED: {
             int P = 1;
             p->variant = pick_splitk_fused(rows, wline, dtype, g.a128, cus, &P);
+            if (forced_variant >= 0) {
+                if (forced_variant >= rws::kNumSplitkFused) return bad_variant(rws::kNumSplitkFused);
+                const int64_t cg = (int64_t)rws::kSplitkFused[forced_variant].block *
+                                   rws::kSplitkFused[forced_variant].kc;
+                const int64_t fp = (wline + cg - 1) / cg;
+                if (rows * fp > fused_capacity(forced_variant, dtype, g.a128))
+                    return bad_variant(rws::kNumSplitkFused);
+                p->variant = forced_variant;
+                P = (int)fp;
+            }
             if (p->variant < 0) {
                 std::string caps;
                 for (int i = 0; i < rws::kNumSplitkFused; ++i) {
@@ -457,14 +504,31 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
         case RWS_KERNEL_SPLITK_ORDERED: {
             int P = 1;
             p->variant = pick_splitk(rows, wline, cus, &P);
+            if (forced_variant >= 0) {
+                if (forced_variant >= rws::kNumSplitk) return bad_variant(rws::kNumSplitk);
+                const int64_t cg =
+                    (int64_t)rws::kSplitk[forced_variant].block * rws::kSplitk[forced_variant].kc;
+                const int64_t fp = (wline + cg - 1) / cg;
+                if (fp > (1 << 20)) return bad_variant(rws::kNumSplitk);
+                p->variant = forced_variant;
+                P = (int)fp;
+            }
             if (p->variant < 0) return fail(RWS_ERR_UNSUPPORTED_SHAPE, "split-k: no variant");
             p->P = P;
-            // Every stage-2 workgroup of the ordered form polls all P of its
-            // row's partials (two tagged words each, read past the L2): past
-            // kOrderedMaxP chunks per row that costs more than the launch it
-            // saves, and the dispatcher keeps the two launches.
+            // The ordered form saves the two-launch form's kernel boundary
+            // but every stage-2 workgroup polls all P of its row's partials
+            // (two tagged words each), and its stage-2 re-read overlaps the
+            // last stage-1 reads only while the input fits the L2 of the
+            // XCDs (8 x 4 MiB).  MI355X, fp16, inputs in HBM, ordered
+            // against two launches: 32 MiB inputs [16,1M] (P 128) 14.5
+            // against 15.6 us, [8,2M] (256) 14.7 against 15.7, [4,4M] (512)
+            // 15.9 against 16.3, but [2,8M] (1024) 18.9 against 17.6; 64 MiB
+            // inputs [32,1M] 31.9 against 31.4, [16,2M] 31.9 against 31.0,
+            // [8,4M] 31.8 against 30.8, [4,8M] 33.8 against 30.1.  Past
+            // either limit the dispatcher keeps the two launches.
             if (family == RWS_KERNEL_SPLITK_ORDERED && kernel_id == RWS_KERNEL_AUTO &&
-                P > kOrderedMaxP)
+                forced_variant < 0 &&
+                (P > kOrderedMaxP || rows * cols * elem_size(dtype) > kOrderedMaxBytes))
                 family = p->family = RWS_KERNEL_SPLITK;
             // at most 2^23 workgroups per launch (both stages of the ordered
             // form count)
@@ -725,14 +789,16 @@ struct PlanKey {
     int dtype, kernel_id, dev;
     unsigned in_line, out_line;
     bool masked;
+    int variant;
     bool operator==(const PlanKey& o) const {
         return rows == o.rows && cols == o.cols && dtype == o.dtype && kernel_id == o.kernel_id &&
-               dev == o.dev && in_line == o.in_line && out_line == o.out_line && masked == o.masked;
+               dev == o.dev && in_line == o.in_line && out_line == o.out_line &&
+               masked == o.masked && variant == o.variant;
     }
 };
 
 int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
-                int kernel_id, Plan* p, bool masked = false) {
+                int kernel_id, Plan* p, bool masked = false, int forced_variant = -1) {
     struct Slot {
         PlanKey key;
         Plan plan;
@@ -747,13 +813,14 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
         dev = -1;
     }
     const PlanKey key{rows, cols, dtype, kernel_id, dev, (unsigned)((uintptr_t)in % 128),
-                      (unsigned)((uintptr_t)out % 128), masked};
+                      (unsigned)((uintptr_t)out % 128), masked, forced_variant};
     for (const Slot& sl : slots)
         if (sl.used && sl.key == key) {
             *p = sl.plan;
             return RWS_OK;
         }
-    const int st = plan_launch_uncached(rows, cols, dtype, in, out, kernel_id, p, masked);
+    const int st =
+        plan_launch_uncached(rows, cols, dtype, in, out, kernel_id, p, masked, forced_variant);
     if (st == RWS_OK) {
         slots[next].key = key;
         slots[next].plan = *p;
@@ -764,13 +831,15 @@ int plan_launch(int64_t rows, int64_t cols, int dtype, const void* in, const voi
 }
 
 int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* stream,
-        int kernel_id, const rws::MaskArgs* mask) {
+        int kernel_id, const rws::MaskArgs* mask, int forced_variant = -1) {
     Plan p;
-    int st = plan_launch(rows, cols, dtype, in, out, kernel_id, &p, mask != nullptr);
+    int st = plan_launch(rows, cols, dtype, in, out, kernel_id, &p, mask != nullptr, forced_variant);
     if (st != RWS_OK) return st;
     const bool cap = is_splitk(p.family) && capturing((hipStream_t)stream);
     if (cap && p.family != RWS_KERNEL_SPLITK) {
-        st = plan_launch(rows, cols, dtype, in, out, RWS_KERNEL_SPLITK, &p, mask != nullptr);
+        // the ordered form shares the two-launch form's variant table
+        st = plan_launch(rows, cols, dtype, in, out, RWS_KERNEL_SPLITK, &p, mask != nullptr,
+                         p.family == RWS_KERNEL_SPLITK_ORDERED ? forced_variant : -1);
         if (st != RWS_OK) return st;
     }
 
@@ -1433,7 +1502,8 @@ int softmax_select_kernel(int64_t rows, int64_t cols, int dtype, const void* in,
 }
 
 static int describe_launch(int64_t rows, int64_t cols, int dtype, const void* in, const void* out,
-                           int kernel_id, bool masked, char* buf, int64_t buflen) {
+                           int kernel_id, bool masked, char* buf, int64_t buflen,
+                           int forced_variant = -1) {
     g_last_error.clear();
     if (!buf || buflen <= 0) return fail(RWS_ERR_INVALID_ARG, "no output buffer");
     buf[0] = 0;
@@ -1448,7 +1518,7 @@ static int describe_launch(int64_t rows, int64_t cols, int dtype, const void* in
         return RWS_OK;
     }
     Plan p;
-    const int st = plan_launch(rows, cols, dtype, in, out, kernel_id, &p, masked);
+    const int st = plan_launch(rows, cols, dtype, in, out, kernel_id, &p, masked, forced_variant);
     if (st != RWS_OK) return st;
     const char* al = p.aligned ? "aligned" : (p.same_phase ? "unaligned" : "unaligned,split-phase");
     const int64_t wmax = p.window;
@@ -1520,6 +1590,39 @@ int softmax_describe_launch(int64_t rows, int64_t cols, int dtype, const void* i
 int softmax_describe_launch_masked(int64_t rows, int64_t cols, int dtype, const void* in,
                                    const void* out, int kernel_id, char* buf, int64_t buflen) {
     return describe_launch(rows, cols, dtype, in, out, kernel_id, true, buf, buflen);
+}
+
+int softmax_describe_variant(int64_t rows, int64_t cols, int dtype, const void* in,
+                             const void* out, int kernel_id, int variant, char* buf,
+                             int64_t buflen) {
+    if (kernel_id == RWS_KERNEL_AUTO || variant < 0) {
+        g_last_error.clear();
+        if (buf && buflen > 0) buf[0] = 0;
+        return fail(RWS_ERR_INVALID_ARG, "a variant needs a kernel family and an index >= 0");
+    }
+    return describe_launch(rows, cols, dtype, in, out, kernel_id, false, buf, buflen, variant);
+}
+
+int softmax_variant_count(int kernel_id) {
+    switch (kernel_id) {
+        case RWS_KERNEL_WAVE_ROW: return rws::kNumWaveRow;
+        case RWS_KERNEL_BLOCK_ONEPASS: return rws::kNumOnepass;
+        case RWS_KERNEL_TWO_PASS: return rws::kNumTwoPass;
+        case RWS_KERNEL_SPLITK:
+        case RWS_KERNEL_SPLITK_ORDERED: return rws::kNumSplitk;
+        case RWS_KERNEL_SPLITK_FUSED: return rws::kNumSplitkFused;
+    }
+    return 0;
+}
+
+int softmax_fwd_variant(const void* in, void* out, int64_t rows, int64_t cols, int dtype,
+                        void* stream, int kernel_id, int variant) {
+    g_last_error.clear();
+    if (kernel_id == RWS_KERNEL_AUTO || variant < 0)
+        return fail(RWS_ERR_INVALID_ARG, "a variant needs a kernel family and an index >= 0");
+    const int st = check_args(in, out, rows, cols, dtype, kernel_id);
+    if (st != RWS_OK || rows == 0 || cols == 0) return st;
+    return run(in, out, rows, cols, dtype, stream, kernel_id, nullptr, variant);
 }
 
 int softmax_bwd_describe_launch(int64_t rows, int64_t cols, int dtype, const void* y,

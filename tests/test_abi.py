@@ -119,6 +119,20 @@ def test_forced_wave_row_rejects_long_rows(lib):
     (3, (1 << 20) - 1, rws.RWS_F16, "splitk_ordered"),
     (1, 1 << 30, rws.RWS_F32, "splitk"),  # P = 131072 chunks: two launches
     (4096, 1 << 20, rws.RWS_F16, "two_pass"),
+    # few long rows, from the measured crossovers (256 CUs assumed): split-k
+    # below half the CUs, or at half of them when block_onepass would park in LDS
+    (64, 65536, rws.RWS_F16, "splitk_ordered"),
+    (128, 65536, rws.RWS_F16, "block_onepass"),
+    (128, 131072, rws.RWS_F16, "splitk_ordered"),
+    (256, 131072, rws.RWS_F16, "block_onepass"),
+    (256, 16384, rws.RWS_F16, "block_onepass"),
+    (384, 65536, rws.RWS_F16, "block_onepass"),
+    # ordered single launch while the input fits 32 MiB and P <= 512
+    (8, 1 << 21, rws.RWS_F16, "splitk_ordered"),   # 32 MiB, P = 256
+    (4, 1 << 22, rws.RWS_F16, "splitk_ordered"),   # 32 MiB, P = 512
+    (2, 1 << 23, rws.RWS_F16, "splitk"),           # 32 MiB, P = 1024
+    (16, 1 << 21, rws.RWS_F16, "splitk"),          # 64 MiB
+    (4, 1 << 23, rws.RWS_F16, "splitk"),           # 64 MiB
 ])
 def test_dispatch_routes(lib, rows, cols, dtype, family):
     kid = rws.softmax_select_kernel(rows, cols, dtype, 256, 512)
@@ -377,3 +391,41 @@ def test_noalloc_argument_checks_never_launch(lib, args, status):
     assert rws.softmax_fwd_noalloc(*args) == status
     assert rws.softmax_last_error() != ""
     assert rws.softmax_fwd_noalloc(0, 0, 0, 5, rws.RWS_F32, 0) == rws.RWS_OK  # empty: no-op
+
+
+def test_variant_forcing_host_checks(lib):
+    counts = {k: rws.softmax_variant_count(rws.KERNEL_IDS[k]) for k in rws.KERNELS}
+    assert all(c > 0 for c in counts.values()), counts
+    assert rws.softmax_variant_count(0) == 0 and rws.softmax_variant_count(42) == 0
+    code, ip, op = rws.RWS_F16, 256, 256 + 4096
+    # every block_onepass shape that holds an fp16 row of 4097 describes itself
+    held = 0
+    for v in range(counts["block_onepass"]):
+        try:
+            d = rws.softmax_describe_variant(8192, 4097, code, ip, op, 2, v)
+        except rws.SoftmaxError as e:
+            assert e.status == rws.RWS_ERR_UNSUPPORTED_SHAPE
+            continue
+        assert d.startswith("block_onepass<f16,"), d
+        held += 1
+    assert held >= 5
+    # the dispatcher's own choice is one of them
+    auto = rws.softmax_describe_launch(8192, 4097, code, ip, op)
+    assert any(rws.softmax_describe_variant(8192, 4097, code, ip, op, 2, v) == auto
+               for v in range(counts["block_onepass"])
+               if "B=" in _try_describe(8192, 4097, code, ip, op, 2, v))
+    # a 4-lane group cannot hold 4097 columns; auto and negative ids are refused
+    with pytest.raises(rws.SoftmaxError) as e:
+        rws.softmax_describe_variant(8, 4097, code, ip, op, 1, 0)
+    assert e.value.status == rws.RWS_ERR_UNSUPPORTED_SHAPE
+    for kid, v in ((0, 0), (2, -1)):
+        assert rws.softmax_fwd_variant(16, 16, 4, 8, code, 0, kid, v) == rws.RWS_ERR_INVALID_ARG
+    assert rws.softmax_fwd_variant(16, 16, 4, 8, code, 0, 2, 10 ** 6) == \
+        rws.RWS_ERR_UNSUPPORTED_SHAPE
+
+
+def _try_describe(*args):
+    try:
+        return rws.softmax_describe_variant(*args)
+    except rws.SoftmaxError:
+        return ""

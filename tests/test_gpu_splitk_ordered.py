@@ -148,7 +148,10 @@ def test_workspace_allocation_failure_is_reported():
 
 
 def test_many_chunks_keep_two_launches():
-    # past 1024 chunks per row the dispatcher keeps the two-launch form
+    # past 512 chunks per row, or past 32 MiB of input, the dispatcher keeps
+    # the two-launch form
     assert rws.softmax_describe_launch(1, 1 << 28, rws.RWS_F16, 256, 256).startswith("splitk<")
-    assert rws.softmax_describe_launch(2, 1 << 24, rws.RWS_F16, 256, 256) \
+    assert rws.softmax_describe_launch(2, 1 << 23, rws.RWS_F16, 256, 256).startswith("splitk<")
+    assert rws.softmax_describe_launch(2, 1 << 24, rws.RWS_F16, 256, 256).startswith("splitk<")
+    assert rws.softmax_describe_launch(4, 1 << 22, rws.RWS_F16, 256, 256) \
         .startswith("splitk_ordered")
