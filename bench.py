@@ -523,10 +523,10 @@ def main() -> int:
     if args.ceilings:
         print(json.dumps(ceilings(args.steps, args.warmup)), flush=True)
         return 0
-    if args.norm:
-        if args.masked or args.backward:
-            print("--norm excludes --masked and --backward", file=sys.stderr)
-            return 2
+    if args.norm and (args.masked or args.backward):
+        print("--norm excludes --masked and --backward", file=sys.stderr)
+        return 2
+    if args.norm and not args.shape:
         name = args.workload if args.workload in workloads.NORM_WORKLOADS else "ln_fp16_131040x192"
         w = workloads.NORM_WORKLOADS[name]
     elif args.shape:

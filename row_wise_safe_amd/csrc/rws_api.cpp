@@ -135,20 +135,25 @@ int wave_row_wa(const rws::WaveRowVariant& v) { return v.G * 16 >= 128 ? 128 : 1
 // against 22.6), two_pass (no change) or the normalisations ([8192,4097]
 // with 576 threads: 33.8 against 32.7).
 // Chunks per row of the backward's and the normalisations' ordered split-k
-// (chunks of 256 x 4 granules), and whether a call takes it: at most one row
-// per two CUs (one workgroup per row would leave most of the chip idle), of
-// at least 2048 granules.  MI355X, fp16, inputs in HBM, one workgroup per
-// row -> ordered: [16,1048576] backward 143 -> 25.1 us, LayerNorm 106 ->
-// 18.0, RMSNorm 75 -> 14.3; [64,262144] 42.4 -> 25.2, 31.2 -> 17.6, 22.6 ->
-// 13.7; but [256,65536] 23.3 -> 24.9, 15.7 -> 17.5, 13.0 -> 13.6 (256 rows
-// fill the chip one workgroup per row).
+// (chunks of 256 x 4 granules), and whether a call takes it: rows too long
+// for their one-workgroup-per-row register form (more than 4096 granules),
+// fewer rows than CUs.  MI355X, fp16, inputs in HBM, streaming form ->
+// ordered: [16,1048576] backward 143 -> 25.1 us, LayerNorm 106 -> 18.0,
+// RMSNorm 75 -> 14.3; [64,262144] 42.4 -> 25.2, 31.2 -> 17.6, 22.6 -> 13.7;
+// [192,65536] backward 18.3 -> 16.6, LayerNorm 14.2 -> 13.0; but
+// [256,65536] 23.9 -> 25.5, 16.8 -> 18.5 (256 rows fill the chip one
+// workgroup per row).  Where the register form holds the row it is kept at
+// every row count: [128,16384] backward 5.14 us against 7.31 ordered,
+// LayerNorm 5.02 against 7.30; [64,32768] 6.52 / 5.47 against 7.17 / 7.38;
+// [16,16384] 4.16 / 4.80 against 5.88 / 6.85 (the backward gives up 2 % at
+// [8..16,32768]: 6.07 against 5.93).
 int ordered_chunks(int64_t wline, int block, int kc) {
     const int64_t span = (int64_t)block * kc;
     return (int)((wline + span - 1) / span);
 }
 
 bool few_long_rows(int64_t rows, int64_t wline, int cus) {
-    return 2 * rows <= cus && wline >= 2048;
+    return rows < cus && wline >= 2048;
 }
 
 int xcd_run_lg(const Geometry& g) {
@@ -1125,8 +1130,8 @@ static int plan_bwd(int64_t rows, int64_t cols, int dtype, const void* y, const 
     };
     if (family == 0) {
         if (pick_wave(1) >= 0) family = 1;
-        else if (allow_ordered && few_long_rows(rows, wline, cus)) family = RWS_KERNEL_SPLITK_ORDERED;
         else if (pick_block() >= 0) family = 2;
+        else if (allow_ordered && few_long_rows(rows, wline, cus)) family = RWS_KERNEL_SPLITK_ORDERED;
         else family = 3;
     }
     if (family == RWS_KERNEL_SPLITK_ORDERED) {
@@ -1323,9 +1328,9 @@ static int plan_norm(int64_t rows, int64_t cols, int dtype, const void* in, cons
     int family = kernel_id == RWS_KERNEL_AUTO ? 0 : kernel_id;
     if (family == 0) {
         if (pick_wave(1) >= 0) family = 1;
+        else if (pick_block() >= 0) family = 2;
         else if (allow_ordered && few_long_rows(rows, wline, device_info().cus))
             family = RWS_KERNEL_SPLITK_ORDERED;
-        else if (pick_block() >= 0) family = 2;
         else family = 3;
     }
     if (family == RWS_KERNEL_SPLITK_ORDERED) {

@@ -237,17 +237,26 @@ def test_bwd_shape_choice(lib, rows, cols, shape):
 
 
 # Few long rows: the backward and the normalisations take the single-launch
-# split-k (chunks of 1024 granules), like the forward.
+# split-k (chunks of 1024 granules) for rows their one-workgroup-per-row
+# register form cannot hold (more than 4096 granules) and fewer rows than
+# CUs (256 assumed without a device); where that form holds the row, it is
+# kept at any row count.
 @pytest.mark.parametrize("rows,cols,P", [(16, 1 << 20, 128), (64, 1 << 18, 32),
-                                         (128, 16384, 2)])
+                                         (192, 65536, 8)])
 def test_few_long_rows_take_ordered_split_k(lib, rows, cols, P):
     b = rws.softmax_bwd_describe_launch(rows, cols, rws.RWS_F16, 256, 512)
     n = rws.norm_describe_launch(rows, cols, rws.RWS_F16, 256, 512)
     assert b.startswith("bwd_ordered") and f" P={P} " in b, b
     assert n.startswith("norm_ordered") and f" P={P} " in n, n
-    # from one row per two CUs on, one workgroup per row
-    assert not rws.softmax_bwd_describe_launch(129, cols, rws.RWS_F16, 256, 512).startswith("bwd_ordered")
-    assert not rws.norm_describe_launch(129, cols, rws.RWS_F16, 256, 512).startswith("norm_ordered")
+    # from one row per CU on, the streaming form
+    assert rws.softmax_bwd_describe_launch(256, cols, rws.RWS_F16, 256, 512).startswith("bwd_stream")
+    assert rws.norm_describe_launch(256, cols, rws.RWS_F16, 256, 512).startswith("norm_stream")
+
+
+@pytest.mark.parametrize("rows,cols", [(16, 16384), (128, 16384), (8, 32768), (64, 32768)])
+def test_rows_the_register_form_holds_keep_it(lib, rows, cols):
+    assert rws.softmax_bwd_describe_launch(rows, cols, rws.RWS_F16, 256, 512).startswith("bwd_block")
+    assert rws.norm_describe_launch(rows, cols, rws.RWS_F16, 256, 512).startswith("norm_block")
 
 
 # Runs of consecutive rows per XCD for block_onepass on rows that are not
