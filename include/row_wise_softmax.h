@@ -115,17 +115,25 @@ enum {
                                  partial (m, d) per chunk, stage 2 merges a
                                  row's partials and writes the outputs (CUDA
                                  safe-online-softmax page, section 3.2) */
-    RWS_KERNEL_SPLITK_FUSED = 5, /* split-k in one cooperative launch: each
-                                 workgroup keeps its chunk in registers, the
-                                 row's workgroups exchange partial (m, d) as
+    RWS_KERNEL_SPLITK_FUSED = 5, /* split-k in one ordinary launch that
+                                 reads the input once: each workgroup keeps
+                                 its chunk in registers and waits for the
+                                 row's partial (m, d), which travel as
                                  epoch-tagged words (as the ordered form
-                                 below), so the input is read once (the
-                                 single-kernel form the same page, section
-                                 3.2, mentions).  Returns
-                                 RWS_ERR_UNSUPPORTED_SHAPE when the grid cannot
-                                 be co-resident on the device.  Never chosen
-                                 by the dispatcher: on MI355X the cooperative
-                                 launch costs more than the re-read it saves */
+                                 below; the single-kernel form the same
+                                 page, section 3.2, mentions).  Relies on the
+                                 same in-order dispatch as the ordered form,
+                                 and on one row's workgroups fitting on the
+                                 device at once: returns
+                                 RWS_ERR_UNSUPPORTED_SHAPE when they cannot.
+                                 A wait that runs out of its bound writes NaN
+                                 and sets the stream's status word.  The
+                                 dispatcher's choice for few long rows when
+                                 the whole grid fits at once (up to 64 MiB of
+                                 line-aligned 16-bit input on MI355X) and the
+                                 rows number at most four, exceed 32 MiB
+                                 together, or need more than 512 chunks
+                                 each */
     RWS_KERNEL_SPLITK_ORDERED = 6 /* split-k in one ordinary launch: the
                                  stage-1 workgroups (partial (m, d) per chunk)
                                  come first in the grid, the stage-2
@@ -141,7 +149,8 @@ enum {
                                  writes NaN for its chunk instead of hanging
                                  and sets the stream's status word, which
                                  softmax_stream_status reports.  The
-                                 dispatcher's choice for few long rows */
+                                 dispatcher's choice for few long rows of up
+                                 to 32 MiB together and 512 chunks each */
 };
 
 /*

@@ -78,6 +78,7 @@ DeviceInfo device_info() {
 
 constexpr int kOrderedMaxP = 512;
 constexpr int64_t kOrderedMaxBytes = (int64_t)32 << 20;
+constexpr int64_t kFusedFewRows = 4;
 
 bool is_splitk(int family) {
     return family == RWS_KERNEL_SPLITK || family == RWS_KERNEL_SPLITK_FUSED ||
@@ -311,12 +312,15 @@ int pick_splitk(int64_t rows, int64_t wmax, int cus, int* P_out) {
 }
 
 // Co-resident workgroup capacity of a fused split-k variant on the current
-// device (cached); without a device, an estimate of two per CU.
+// device (cached); without a device, the lower bound its compiled waves per
+// SIMD give (4 SIMDs per CU).
 int64_t fused_capacity(int variant, int dtype, bool aligned) {
     static std::mutex mu;
     static std::map<std::tuple<int, int, int, int>, int64_t> cache;
     const DeviceInfo info = device_info();
-    if (!info.known) return 2LL * info.cus;
+    if (!info.known)
+        return (int64_t)info.cus * 4 * rws::splitk_fused_min_waves(variant, dtype, aligned) /
+               (rws::kSplitkFused[variant].block / 64);
     int dev = 0;
     (void)hipGetDevice(&dev);
     const auto key = std::make_tuple(dev, variant, dtype, aligned ? 1 : 0);
@@ -333,17 +337,21 @@ int64_t fused_capacity(int variant, int dtype, bool aligned) {
     return blocks;
 }
 
-// Single-launch split-k: the largest chunk whose grid still gives every CU
-// two workgroups and fits the co-resident capacity; else any chunk that fits.
-// Returns -1 when no variant's grid can be co-resident.
-int pick_splitk_fused(int64_t rows, int64_t wmax, int dtype, bool aligned, int cus, int* P_out) {
+// Fused split-k chunking: the largest chunk whose grid still gives every CU
+// two workgroups and fits the co-resident capacity; else the smallest chunk
+// that fits.  `fit_rows` rows must fit at once: the whole grid for the
+// dispatcher's own choice, one row when the form is requested.  Returns -1
+// when no variant fits.  (fp16, inputs in HBM: [4,8M] 16 granules per
+// thread 25.3 us, 8 28.6, 4 34.4; [16,1M] 14.5-14.8, 15.6, 16.0.)
+int pick_splitk_fused(int64_t fit_rows, int64_t rows, int64_t wmax, int dtype, bool aligned, int cus,
+                      int* P_out) {
     int best = -1, bestP = 1;
     for (int pass = 0; pass < 2 && best < 0; ++pass) {
         for (int i = 0; i < rws::kNumSplitkFused; ++i) {
             const rws::SplitkVariant& v = rws::kSplitkFused[i];
             const int64_t cg = (int64_t)v.block * v.kc;
             const int64_t P = (wmax + cg - 1) / cg;
-            if (rows * P > fused_capacity(i, dtype, aligned)) continue;
+            if (P > (1 << 20) || fit_rows * P > fused_capacity(i, dtype, aligned)) continue;
             if (pass == 0 && rows * P < 2LL * cus) continue;
             const bool better = best < 0 || (pass == 0 ? v.kc > rws::kSplitkFused[best].kc
                                                        : v.kc < rws::kSplitkFused[best].kc);
@@ -478,14 +486,16 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
             break;
         }
         case RWS_KERNEL_SPLITK_FUSED: {
+            // requested: one row's workgroups must fit at once (rows beyond
+            // the capacity follow in dispatch order)
             int P = 1;
-            p->variant = pick_splitk_fused(rows, wline, dtype, g.a128, cus, &P);
+            p->variant = pick_splitk_fused(1, rows, wline, dtype, g.a128, cus, &P);
             if (forced_variant >= 0) {
                 if (forced_variant >= rws::kNumSplitkFused) return bad_variant(rws::kNumSplitkFused);
                 const int64_t cg = (int64_t)rws::kSplitkFused[forced_variant].block *
                                    rws::kSplitkFused[forced_variant].kc;
                 const int64_t fp = (wline + cg - 1) / cg;
-                if (rows * fp > fused_capacity(forced_variant, dtype, g.a128))
+                if (fp > fused_capacity(forced_variant, dtype, g.a128))
                     return bad_variant(rws::kNumSplitkFused);
                 p->variant = forced_variant;
                 P = (int)fp;
@@ -494,15 +504,16 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
                 std::string caps;
                 for (int i = 0; i < rws::kNumSplitkFused; ++i) {
                     const int64_t cg = (int64_t)rws::kSplitkFused[i].block * rws::kSplitkFused[i].kc;
-                    caps += " " + std::to_string(rows * ((wline + cg - 1) / cg)) + "/" +
+                    caps += " " + std::to_string((wline + cg - 1) / cg) + "/" +
                             std::to_string(fused_capacity(i, dtype, g.a128));
                 }
                 return fail(RWS_ERR_UNSUPPORTED_SHAPE,
-                            "single-launch split-k: the grid cannot be co-resident on this device "
-                            "(workgroups/capacity per variant:" + caps + ")");
+                            "fused split-k: one row's workgroups cannot be resident at once on "
+                            "this device (workgroups per row/capacity per variant:" + caps + ")");
             }
             p->P = P;
-            p->max_rows_per_launch = rows;
+            // at most 2^23 workgroups per launch
+            p->max_rows_per_launch = std::max<int64_t>(1, ((int64_t)1 << 23) / P);
             break;
         }
         case RWS_KERNEL_SPLITK:
@@ -531,10 +542,36 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
             // inputs [32,1M] 31.9 against 31.4, [16,2M] 31.9 against 31.0,
             // [8,4M] 31.8 against 30.8, [4,8M] 33.8 against 30.1.  Past
             // either limit the dispatcher keeps the two launches.
+            // The fused single launch reads the input once but writes only
+            // after all of a row's chunks are read; where its whole grid
+            // fits at once it beats the two launches everywhere measured and
+            // the ordered form for up to four rows.  MI355X, fp16, inputs in
+            // HBM, fused against the dispatcher's previous choice: 64 MiB
+            // [1,32M] 28.1 against 32.9 us (two launches), [4,8M] 25.3
+            // against 29.9, [32,1M] 24.4 against 31.3, [128,256K] 23.8
+            // against 31.4; 32 MiB [1,16M] 16.6 against 19.0, [2,8M] 15.1
+            // against 17.1, [4,4M] 14.9 against 15.8 (ordered); 8 MiB
+            // [4,1M] 8.1 against 9.0 (ordered), [1,4M] 9.0 against 9.5; but
+            // ordered ahead from eight rows: [8,1M] 10.3 against 11.0,
+            // [16,512K] 10.1 against 10.9, [16,1M] 14.2 against 14.5,
+            // [32,512K] 14.3 against 14.6 ([8,2M] 14.7 both).  Past 64 MiB
+            // the grid runs in several passes and only ties the two
+            // launches ([4,32M] 115.3 against 115.5), which are kept.
+            const bool ordered_fits =
+                P <= kOrderedMaxP && rows * cols * elem_size(dtype) <= kOrderedMaxBytes;
             if (family == RWS_KERNEL_SPLITK_ORDERED && kernel_id == RWS_KERNEL_AUTO &&
-                forced_variant < 0 &&
-                (P > kOrderedMaxP || rows * cols * elem_size(dtype) > kOrderedMaxBytes))
-                family = p->family = RWS_KERNEL_SPLITK;
+                forced_variant < 0) {
+                int fP = 1;
+                const int fv = pick_splitk_fused(rows, rows, wline, dtype, g.a128, cus, &fP);
+                if (fv >= 0 && (!ordered_fits || rows <= kFusedFewRows)) {
+                    p->family = RWS_KERNEL_SPLITK_FUSED;
+                    p->variant = fv;
+                    p->P = fP;
+                    p->max_rows_per_launch = rows;
+                    break;
+                }
+                if (!ordered_fits) family = p->family = RWS_KERNEL_SPLITK;
+            }
             // at most 2^23 workgroups per launch (both stages of the ordered
             // form count)
             const int64_t per_row = family == RWS_KERNEL_SPLITK_ORDERED ? 2LL * P : (int64_t)P;
@@ -873,14 +910,11 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
         const int64_t batch = std::min<int64_t>(rows, p.max_rows_per_launch);
         st = get_workspace(s, cap, (size_t)batch * p.P * sizeof(float2), &ws);
         if (st != RWS_OK) return st;
-    } else if (p.family == RWS_KERNEL_SPLITK_FUSED) {
-        st = get_tag_workspace(s, 2 * rows * p.P, 1, &tags, &epoch);
-        if (st != RWS_OK) return st;
-    } else if (p.family == RWS_KERNEL_SPLITK_ORDERED) {
+    } else if (p.family == RWS_KERNEL_SPLITK_ORDERED || p.family == RWS_KERNEL_SPLITK_FUSED) {
         const int64_t batch = std::min<int64_t>(rows, p.max_rows_per_launch);
         const int64_t launches = (rows + p.max_rows_per_launch - 1) / p.max_rows_per_launch;
         if (launches >= ((int64_t)1 << 31))
-            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "ordered split-k: too many launches for one call");
+            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "single-launch split-k: too many launches for one call");
         st = get_tag_workspace(s, 2 * batch * p.P, launches, &tags, &epoch);
         if (st != RWS_OK) return st;
     }
@@ -924,9 +958,11 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
                     e = rws::launch_splitk(L, p.variant, p.P, (float2*)ws);
                     break;
                 case RWS_KERNEL_SPLITK_FUSED:
+                    // one epoch per launch, as below
                     e = rws::launch_splitk_fused(
                         L, p.variant, p.P,
-                        rws::OrderedSync{tags, epoch, nullptr, status, wait_limit});
+                        rws::OrderedSync{tags, epoch + (unsigned)(r0 / p.max_rows_per_launch),
+                                         nullptr, status, wait_limit});
                     break;
                 case RWS_KERNEL_SPLITK_ORDERED:
                     // one epoch per launch: the batches reuse the same tag words
@@ -1558,10 +1594,10 @@ static int describe_launch(int64_t rows, int64_t cols, int dtype, const void* in
         case RWS_KERNEL_SPLITK_FUSED: {
             const rws::SplitkVariant& v = rws::kSplitkFused[p.variant];
             std::snprintf(buf, (size_t)buflen,
-                          "splitk_fused<%s,%s,B=%d,KC=%d> P=%d grid=%lld cooperative block=%d "
-                          "window<=%lld",
-                          dtype_name(dtype), al, v.block, v.kc, p.P, (long long)(rows * p.P),
-                          v.block, (long long)wmax);
+                          "splitk_fused<%s,%s,B=%d,KC=%d> P=%d grid=%lld block=%d window<=%lld",
+                          dtype_name(dtype), al, v.block, v.kc, p.P,
+                          (long long)(std::min(rows, p.max_rows_per_launch) * p.P), v.block,
+                          (long long)wmax);
             break;
         }
         case RWS_KERNEL_SPLITK: {

@@ -68,8 +68,11 @@ hipError_t launch_block_onepass(const Launch& L, int variant);
 hipError_t launch_two_pass(const Launch& L, int variant);
 // Both split-k stages; ws holds rows*P (m, d) pairs.
 hipError_t launch_splitk(const Launch& L, int variant, int P, float2* ws);
-// Workgroups of this variant that can be resident at once on `cus` CUs.
+// Workgroups of this fused variant that can be resident at once on `cus`
+// CUs (the device's occupancy query), and the waves per SIMD its kernels are
+// compiled to allow (a lower bound on that occupancy without a device).
 hipError_t splitk_fused_capacity(int variant, int dtype, bool aligned, int cus, int64_t* blocks);
+int splitk_fused_min_waves(int variant, int dtype, bool aligned);
 // What an ordered (single-launch split-k) launch needs besides its tensors,
 // passed to the kernel as one argument:
 //   tags       2 * rows * P epoch-tagged 64-bit words (zeroed when allocated)
@@ -89,9 +92,10 @@ struct OrderedSync {
 };
 constexpr unsigned kOrderedSpinLimit = 1u << 21;
 constexpr uint64_t kStatusLate = 1;
-// Single-launch split-k that reads every element once (cooperative launch,
-// grid rows*P, every workgroup keeps its chunk in registers; OrderedSync as
-// for the ordered form below, with 2*rows*P tag words).
+// Single-launch split-k that reads every element once (ordinary launch, grid
+// rows*P, every workgroup keeps its chunk in registers and waits for its
+// row's P partials, so P workgroups must fit on the device at once;
+// OrderedSync as for the ordered form below, with 2*rows*P tag words).
 hipError_t launch_splitk_fused(const Launch& L, int variant, int P, const OrderedSync& S);
 // Split-k in one ordinary launch (kSplitk variants): grid 2*rows*P.
 hipError_t launch_splitk_ordered(const Launch& L, int variant, int P, const OrderedSync& S);

@@ -1,4 +1,4 @@
-// rws_splitk_fused.hip -- split-k in a single cooperative launch that reads
+// rws_splitk_fused.hip -- split-k in a single ordinary launch that reads
 // every element once.
 //
 // The two-launch split-k (rws_splitk.hip) and its single-launch ordered form
@@ -17,13 +17,22 @@
 // own data, so no release/acquire fence (which on this multi-XCD part writes
 // back and invalidates an XCD's L2) is needed.
 //
-// Waiting for other workgroups of the grid is only safe when all of them are
-// resident at once, so the kernel is launched with hipLaunchCooperativeKernel,
-// which refuses grids that cannot be co-resident (RWS_ERR_UNSUPPORTED_SHAPE
-// then).  The wait is also bounded: a workgroup that does not see a partial
-// after the launch's spin limit stops waiting, writes NaN for its chunk and
-// sets the stream's status word (softmax_stream_status reports it), so every
-// wave always reaches the end of the kernel.
+// Waiting needs only the row's own workgroups at once, not the grid's.
+// Workgroups b = row * P + chunk are handed to each XCD in increasing index
+// order (the ordered form's assumption).  Take the lowest row that has not
+// finished: every earlier row has finished and left its slots, and on each
+// XCD no workgroup of a later row is dispatched before all of this row's
+// workgroups for that XCD are, so this row's P workgroups become resident
+// together provided P workgroups fit on the device -- and it finishes.  The
+// dispatcher therefore checks P against the co-resident capacity of the
+// variant (and, for its own choice, takes this form only when the whole grid
+// fits, measured fastest).  A launch through hipLaunchCooperativeKernel,
+// which guarantees the whole grid instead, cost ~17 us more per call on
+// MI355X (fp16 [16,1M]: 32.9 us against 14.3-14.5).  The wait is also
+// bounded: a workgroup that does not see a partial after the launch's spin
+// limit stops waiting, writes NaN for its chunk and sets the stream's status
+// word (softmax_stream_status reports it), so every wave always reaches the
+// end of the kernel.
 #include "rws_kernels.hpp"
 #include "rws_launch.hpp"
 #include "rws_ordered.hpp"
@@ -41,13 +50,21 @@ __device__ inline float granule_max(u32x4 g) {
     return m;
 }
 
-// Waves per SIMD the kernel must allow so that the grids the dispatcher
-// gives it fit at once (KC 4: 8 waves, i.e. <= 64 VGPRs; KC 8: 4; KC 16: 2).
-template <int KC>
-constexpr int fused_min_waves() { return KC <= 4 ? 8 : KC <= 8 ? 4 : 2; }
+// Waves per SIMD each kernel is compiled to allow: KC 4 at 8 (<= 64 VGPRs),
+// KC 8 at 4, KC 16 at 4 on line-aligned rows and 2 on the others, whose
+// element-wise row ends need more registers; fp32 rows that are not
+// line-aligned at 6 / 3 / 1, where the others would spill (42-236 VGPRs
+// without spills; 6-14 spilled otherwise).  KC 16 at four waves per SIMD
+// keeps 64 MiB of chunks resident on 256 CUs: inputs up to that size run in
+// one pass of the grid.
+template <int DT, bool ALIGNED, int KC>
+constexpr int fused_min_waves() {
+    return (DT == kF32 && !ALIGNED) ? (KC <= 4 ? 6 : KC <= 8 ? 3 : 1)
+                                    : (KC <= 4 ? 8 : KC <= 8 ? 4 : ALIGNED ? 4 : 2);
+}
 
 template <int DT, bool ALIGNED, int BLOCK, int KC>
-__global__ __launch_bounds__(BLOCK, fused_min_waves<KC>()) void k_splitk_fused(const void* __restrict__ in,
+__global__ __launch_bounds__(BLOCK, (fused_min_waves<DT, ALIGNED, KC>())) void k_splitk_fused(const void* __restrict__ in,
                                                         void* __restrict__ out, int64_t rows,
                                                         int cols, int P, OrderedSync S,
                                                         int same_phase) {
@@ -80,16 +97,24 @@ __global__ __launch_bounds__(BLOCK, fused_min_waves<KC>()) void k_splitk_fused(c
         if (!w.interior(k)) raw[i] = w.mask_raw(k, raw[i], tbeg, tend);
     }
 
-    // chunk max, chunk sum of e^(x - m_c)
+    // chunk max, chunk sum of e^(x - m_c).  Each pass takes the granules
+    // one at a time: the empty asm statements tie granule i to the running
+    // result of granules < i, so the compiler cannot widen (and hold) all KC
+    // granules' fp32 values at once -- KC 16 then fits 119 VGPRs instead of
+    // 237.  (An empty asm statement: no instruction.)
     float mc = granule_max<DT>(raw[0]);
 #pragma unroll
-    for (int i = 1; i < KC; ++i) mc = vmax(mc, granule_max<DT>(raw[i]));
+    for (int i = 1; i < KC; ++i) {
+        asm volatile("" : "+v"(raw[i]) : "v"(mc));
+        mc = vmax(mc, granule_max<DT>(raw[i]));
+    }
     mc = block_reduce<W, OpMax>(mc, red_max);
     float dc = 0.0f;
     {
         const RowExp er(mc);
 #pragma unroll
         for (int i = 0; i < KC; ++i) {
+            asm volatile("" : "+v"(raw[i]) : "v"(dc));
             float f[VEC];
             Elem<DT>::widen(raw[i], f);
             er.apply(f);
@@ -108,6 +133,19 @@ __global__ __launch_bounds__(BLOCK, fused_min_waves<KC>()) void k_splitk_fused(c
 #pragma unroll
     for (int i = 0; i < KC; ++i) asm volatile("" : "+v"(raw[i]));
 
+    // One thread first waits for the row's last chunk, dispatched last and
+    // so as a rule published last; the other threads wait at the barrier.
+    // Only then do all threads poll their share of the row's partials (by
+    // then mostly published).  Every thread polling all along multiplied the
+    // agent-scope loads during the long read phase: fp16 [4,8M] 29.3 us
+    // against 25.3 with this wait.  (Its result is not needed: the polls
+    // below check every word, bounded as always.)
+    if (t == 0) {
+        int ignored = 0;
+        (void)poll_word(row_tags + 2 * (P - 1) + 1, epoch, ignored, S.spin_limit);
+    }
+    __syncthreads();
+
     // merge the row's partials (this chunk's own included): (M, D)
     float m = kNegInf, d = 0.0f;
     int late = 0;
@@ -123,16 +161,20 @@ __global__ __launch_bounds__(BLOCK, fused_min_waves<KC>()) void k_splitk_fused(c
     const RowExp er(M);
     const float r = failed ? __builtin_nanf("") : __builtin_amdgcn_rcpf(D);
 
-    // y = e^(x - M) / D for the chunk held in registers
+    // y = e^(x - M) / D for the chunk held in registers, again one granule
+    // at a time (tied to the previous granule's first output)
+    float tok = r;
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
         const int k = kbase + BLOCK * i;
+        asm volatile("" : "+v"(raw[i]) : "v"(tok));
         if (k < w.ngran) {
             float f[VEC];
             Elem<DT>::widen(raw[i], f);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) f[e] = er.one(f[e]) * r;
             w.store(k, f, same_phase != 0);
+            tok = f[0];
         }
     }
 }
@@ -173,6 +215,26 @@ static const void* fused_kernel(int variant, int dtype, bool aligned) {
     return nullptr;
 }
 
+template <int KC>
+static int min_waves_any(int dtype, bool aligned) {
+    switch (dtype) {
+        case kF32: return aligned ? fused_min_waves<kF32, true, KC>() : fused_min_waves<kF32, false, KC>();
+        case kF16: return aligned ? fused_min_waves<kF16, true, KC>() : fused_min_waves<kF16, false, KC>();
+        case kBF16: return aligned ? fused_min_waves<kBF16, true, KC>() : fused_min_waves<kBF16, false, KC>();
+    }
+    return 0;
+}
+
+int splitk_fused_min_waves(int variant, int dtype, bool aligned) {
+    int i = 0;
+#define RWS_CASE(b, kc) \
+    if (variant == i) return min_waves_any<kc>(dtype, aligned); \
+    ++i;
+    RWS_SPLITK_FUSED_VARIANTS(RWS_CASE)
+#undef RWS_CASE
+    return 0;
+}
+
 hipError_t splitk_fused_capacity(int variant, int dtype, bool aligned, int cus, int64_t* blocks) {
     const void* k = fused_kernel(variant, dtype, aligned);
     if (!k) return hipErrorInvalidValue;
@@ -184,19 +246,31 @@ hipError_t splitk_fused_capacity(int variant, int dtype, bool aligned, int cus, 
     return hipSuccess;
 }
 
+template <int DT, bool AL, int B, int KC>
+static hipError_t go(const Launch& L, int P, const OrderedSync& S) {
+    hipLaunchKernelGGL((k_splitk_fused<DT, AL, B, KC>), dim3((unsigned)(L.rows * P)), dim3(B), 0,
+                       L.stream, L.in, L.out, L.rows, L.cols, P, S, (int)L.same_phase);
+    return hipGetLastError();
+}
+
+template <int B, int KC>
+static hipError_t go_any(const Launch& L, int P, const OrderedSync& S) {
+    switch (L.dtype) {
+        case kF32: return L.aligned ? go<kF32, true, B, KC>(L, P, S) : go<kF32, false, B, KC>(L, P, S);
+        case kF16: return L.aligned ? go<kF16, true, B, KC>(L, P, S) : go<kF16, false, B, KC>(L, P, S);
+        case kBF16: return L.aligned ? go<kBF16, true, B, KC>(L, P, S) : go<kBF16, false, B, KC>(L, P, S);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_splitk_fused(const Launch& L, int variant, int P, const OrderedSync& S) {
-    const void* k = fused_kernel(variant, L.dtype, L.aligned);
-    if (!k) return hipErrorInvalidValue;
-    const void* in = L.in;
-    void* out = L.out;
-    int64_t rows = L.rows;
-    int cols = L.cols;
-    int same_phase = L.same_phase ? 1 : 0;
-    OrderedSync sync = S;
-    void* args[] = {(void*)&in, (void*)&out, (void*)&rows, (void*)&cols, (void*)&P,
-                    (void*)&sync, (void*)&same_phase};
-    return hipLaunchCooperativeKernel(k, dim3((unsigned)(L.rows * P)),
-                                      dim3(kSplitkFused[variant].block), args, 0, L.stream);
+    int i = 0;
+#define RWS_CASE(b, kc) \
+    if (variant == i) return go_any<b, kc>(L, P, S); \
+    ++i;
+    RWS_SPLITK_FUSED_VARIANTS(RWS_CASE)
+#undef RWS_CASE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace rws

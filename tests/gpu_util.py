@@ -33,7 +33,7 @@ def empty_like_at(x: torch.Tensor, offset: int = 0):
 
 
 class NotCoResident(Exception):
-    """The single-launch split-k grid does not fit the device at once."""
+    """The fused split-k cannot hold one row's workgroups on the device at once."""
 
 
 def run(x: torch.Tensor, out: torch.Tensor, kernel: str = "auto") -> np.ndarray:

@@ -116,7 +116,7 @@ def test_forced_wave_row_rejects_long_rows(lib):
     (1 << 20, 128, rws.RWS_BF16, "wave_row"),
     (8192, 4097, rws.RWS_F16, "block_onepass"),
     (16, 1 << 20, rws.RWS_F16, "splitk_ordered"),
-    (3, (1 << 20) - 1, rws.RWS_F16, "splitk_ordered"),
+    (3, (1 << 20) - 1, rws.RWS_F16, "splitk_fused"),  # at most four rows
     (1, 1 << 30, rws.RWS_F32, "splitk"),  # P = 131072 chunks: two launches
     (4096, 1 << 20, rws.RWS_F16, "two_pass"),
     # few long rows, from the measured crossovers (256 CUs assumed): split-k
@@ -127,12 +127,21 @@ def test_forced_wave_row_rejects_long_rows(lib):
     (256, 131072, rws.RWS_F16, "block_onepass"),
     (256, 16384, rws.RWS_F16, "block_onepass"),
     (384, 65536, rws.RWS_F16, "block_onepass"),
-    # ordered single launch while the input fits 32 MiB and P <= 512
+    # ordered single launch while the input fits 32 MiB and P <= 512, from
+    # eight rows; the fused single launch while its whole grid fits at once
+    # (64 MiB of line-aligned 16-bit input; capacity from the compiled waves
+    # per SIMD without a device); two launches beyond
     (8, 1 << 21, rws.RWS_F16, "splitk_ordered"),   # 32 MiB, P = 256
-    (4, 1 << 22, rws.RWS_F16, "splitk_ordered"),   # 32 MiB, P = 512
-    (2, 1 << 23, rws.RWS_F16, "splitk"),           # 32 MiB, P = 1024
-    (16, 1 << 21, rws.RWS_F16, "splitk"),          # 64 MiB
-    (4, 1 << 23, rws.RWS_F16, "splitk"),           # 64 MiB
+    (8, 1 << 20, rws.RWS_F16, "splitk_ordered"),   # 16 MiB
+    (4, 1 << 22, rws.RWS_F16, "splitk_fused"),     # 32 MiB, four rows
+    (4, 1 << 20, rws.RWS_F16, "splitk_fused"),     # 8 MiB, four rows
+    (2, 1 << 23, rws.RWS_F16, "splitk_fused"),     # 32 MiB, P = 1024 ordered
+    (16, 1 << 21, rws.RWS_F16, "splitk_fused"),    # 64 MiB
+    (4, 1 << 23, rws.RWS_F16, "splitk_fused"),     # 64 MiB
+    (128, 1 << 18, rws.RWS_F16, "splitk_fused"),   # 64 MiB
+    (16, 1 << 20, rws.RWS_F32, "splitk_fused"),    # 64 MiB
+    (4, 1 << 25, rws.RWS_F16, "splitk"),           # 256 MiB: several passes
+    (16, 1 << 22, rws.RWS_F16, "splitk"),          # 128 MiB
 ])
 def test_dispatch_routes(lib, rows, cols, dtype, family):
     kid = rws.softmax_select_kernel(rows, cols, dtype, 256, 512)

@@ -104,7 +104,7 @@ def test_backward_attention_workload():
 
 
 def test_backward_rejects_split_kernels():
-    # the two-launch and cooperative split-k forms exist for the forward only
+    # the two-launch and fused split-k forms exist for the forward only
     # (the backward's split-k is the ordered form)
     y = torch.zeros(2, 64, dtype=torch.float16, device="cuda")
     for kernel in ("splitk", "splitk_fused"):

@@ -86,7 +86,7 @@ def test_forward_few_long_rows(kernel):
             rws.softmax(x, out=y, kernel=kernel)
         except rws.SoftmaxError as e:
             if kernel == "splitk_fused" and e.status == rws.RWS_ERR_UNSUPPORTED_SHAPE:
-                pytest.skip(f"fused grid not co-resident here: {e}")
+                pytest.skip(f"fused row not co-resident here: {e}")
             raise
     torch.cuda.synchronize()
     check(y.double().cpu().numpy(), oracle.safe_softmax(stored), "f16", f"eager {desc}")

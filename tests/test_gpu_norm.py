@@ -276,7 +276,7 @@ def test_norm_on_a_stream():
 
 
 def test_norm_rejects_split_kernels():
-    # the two-launch and cooperative split-k forms exist for the forward only
+    # the two-launch and fused split-k forms exist for the forward only
     # (the normalisations' split-k is the ordered form)
     x = torch.zeros((4, 64), dtype=torch.float16, device="cuda")
     with pytest.raises(rws.SoftmaxError):

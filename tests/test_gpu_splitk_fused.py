@@ -1,5 +1,8 @@
-"""Single-launch split-k: the per-row arrival counters and epochs across many
-calls, streams and shapes, the co-residency refusal, and the workspace
+"""Fused single-launch split-k (each workgroup keeps its chunk in registers
+and waits for its row's partials): epochs across many calls, streams and
+shapes, grids larger than the device holds at once (rows then follow in
+dispatch order), the refusal of a row whose workgroups cannot all be
+resident, the dispatcher's choice of it, and the workspace
 allocation-failure path (forced from the host)."""
 import os
 
@@ -9,7 +12,7 @@ import torch
 
 import oracle
 import row_wise_safe_amd as rws
-from gpu_util import have_gpu, to_device
+from gpu_util import FreshStream, have_gpu, to_device
 from tolerance import check
 
 pytestmark = [pytest.mark.gpu,
@@ -64,15 +67,48 @@ def test_fused_matches_two_launch(dtype):
     check(b.double().cpu().numpy(), ref, dtype, "two-launch")
 
 
-def test_refuses_grid_that_cannot_be_co_resident():
-    x = torch.zeros(100000, 1024, dtype=torch.float16, device="cuda")
+def test_refuses_row_that_cannot_be_co_resident():
+    # fp32 rows of 20M elements: 5M granules a row, more than any variant's
+    # resident workgroups hold at once (at most 4M granules); refused before
+    # any launch
+    x = torch.zeros(1, 20 << 20, dtype=torch.float32, device="cuda")
     with pytest.raises(rws.SoftmaxError) as e:
         rws.softmax(x, kernel="splitk_fused")
     assert e.value.status == rws.RWS_ERR_UNSUPPORTED_SHAPE
-    # the dispatcher never picks it for such a shape
+    # the dispatcher takes the two launches for such a row
     assert rws.softmax_kernel_name(
-        rws.softmax_select_kernel(100000, 1024, rws.RWS_F16, x.data_ptr(), x.data_ptr())) \
-        != "splitk_fused"
+        rws.softmax_select_kernel(1, 20 << 20, rws.RWS_F32, x.data_ptr(), x.data_ptr())) \
+        == "splitk"
+
+
+def test_grid_larger_than_the_device_runs_row_by_row():
+    # 48 rows of 1M fp16 (96 MiB): 1536 workgroups of 64 KiB, more than the
+    # 1024 the device holds at once; later rows start as earlier rows finish
+    rows, cols = 48, 1 << 20
+    x, stored = _x(rows, cols, seed=14)
+    desc = rws.softmax_describe_launch(rows, cols, rws.RWS_F16, x.data_ptr(), x.data_ptr(),
+                                       rws.KERNEL_IDS["splitk_fused"])
+    print(f"\n{desc}", flush=True)
+    assert "grid=1536 " in desc, desc
+    y = torch.empty_like(x)
+    with FreshStream() as s:
+        with torch.cuda.stream(s):
+            rws.softmax(x, out=y, kernel="splitk_fused")
+            rws.stream_status()
+    check(y.double().cpu().numpy(), oracle.safe_softmax(stored), "f16", "fused, two passes")
+
+
+@pytest.mark.parametrize("rows,cols,family", [
+    (4, 1 << 23, "splitk_fused"),      # 64 MiB: the whole grid fits at once
+    (32, 1 << 20, "splitk_fused"),     # 64 MiB
+    (4, 1 << 20, "splitk_fused"),      # at most four rows
+    (16, 1 << 20, "splitk_ordered"),   # 32 MiB, sixteen rows
+    (4, 1 << 25, "splitk"),            # 256 MiB: more than the device holds
+])
+def test_dispatcher_choice_on_the_device(rows, cols, family):
+    # the occupancy the device reports, not the compiled lower bound
+    kid = rws.softmax_select_kernel(rows, cols, rws.RWS_F16, 256, 512)
+    assert rws.softmax_kernel_name(kid) == family
 
 
 def test_workspace_allocation_failure_is_reported():

@@ -147,11 +147,15 @@ def test_workspace_allocation_failure_is_reported():
         check(y.double().cpu().numpy(), oracle.safe_softmax(stored), "f16", "after failure")
 
 
-def test_many_chunks_keep_two_launches():
-    # past 512 chunks per row, or past 32 MiB of input, the dispatcher keeps
-    # the two-launch form
-    assert rws.softmax_describe_launch(1, 1 << 28, rws.RWS_F16, 256, 256).startswith("splitk<")
-    assert rws.softmax_describe_launch(2, 1 << 23, rws.RWS_F16, 256, 256).startswith("splitk<")
-    assert rws.softmax_describe_launch(2, 1 << 24, rws.RWS_F16, 256, 256).startswith("splitk<")
-    assert rws.softmax_describe_launch(4, 1 << 22, rws.RWS_F16, 256, 256) \
-        .startswith("splitk_ordered")
+def test_ordered_only_up_to_its_limits():
+    # the ordered form from eight rows while the input fits 32 MiB and a row
+    # needs at most 512 chunks; past that, the fused single launch while its
+    # whole grid fits the device at once, else the two launches
+    def family(rows, cols):
+        return rws.softmax_describe_launch(rows, cols, rws.RWS_F16, 256, 256).split("<")[0]
+    assert family(16, 1 << 20) == "splitk_ordered"
+    assert family(8, 1 << 21) == "splitk_ordered"    # 32 MiB, P = 256
+    assert family(2, 1 << 23) == "splitk_fused"      # P = 1024
+    assert family(16, 1 << 21) == "splitk_fused"     # 64 MiB
+    assert family(2, 1 << 25) == "splitk"            # 128 MiB
+    assert family(1, 1 << 28) == "splitk"            # 512 MiB

@@ -1,12 +1,13 @@
 """The single-launch split-k forms report a wait that gave up.
 
-Their stage-2 workgroups poll the row's partials with a bounded wait (they
-rely on workgroups being dispatched in index order within each XCD; a wait
-that runs out means that order did not hold).  Such a workgroup writes NaN
+Their waiting workgroups (the ordered form's stage 2, every workgroup of the
+fused form) poll the row's partials with a bounded wait (they rely on
+workgroups being dispatched in index order within each XCD; a wait that runs
+out means that order did not hold).  Such a workgroup writes NaN
 for its chunk and sets the stream's status word; softmax_stream_status then
 returns RWS_ERR_WAIT_TIMEOUT once and clears it.  The tests force the
 give-up from the host by setting the wait limit to 0 tries, so every
-stage-2 workgroup gives up without polling and every kernel still ends
+waiting workgroup gives up without polling and every kernel still ends
 normally; then the default limit is restored and the same call must match
 the oracle with a clean status.
 """
@@ -57,12 +58,25 @@ def _forced_give_up_then_clean(call, ref_check):
 def test_forward_ordered_reports_give_up():
     x64 = np.random.Generator(np.random.PCG64(61)).normal(0.0, 3.0, (ROWS, COLS))
     x, xs = to_device(x64, "f16")
-    assert "splitk_ordered" in rws.softmax_describe_launch(ROWS, COLS, rws.RWS_F16, x.data_ptr(),
-                                                           x.data_ptr())
+    assert "splitk_ordered" in rws.softmax_describe_launch(
+        ROWS, COLS, rws.RWS_F16, x.data_ptr(), x.data_ptr(), rws.KERNEL_IDS["splitk_ordered"])
     print("forward ordered give-up", flush=True)
     _forced_give_up_then_clean(
-        lambda: rws.softmax(x),
+        lambda: rws.softmax(x, kernel="splitk_ordered"),
         lambda y: check(y.double().cpu().numpy(), oracle.safe_softmax(xs), "f16", "ordered"))
+
+
+def test_forward_fused_reports_give_up():
+    # four long rows: the dispatcher's fused single launch, whose every
+    # workgroup waits for its row's partials
+    x64 = np.random.Generator(np.random.PCG64(64)).normal(0.0, 3.0, (ROWS, COLS))
+    x, xs = to_device(x64, "f16")
+    assert "splitk_fused" in rws.softmax_describe_launch(ROWS, COLS, rws.RWS_F16, x.data_ptr(),
+                                                         x.data_ptr())
+    print("forward fused give-up", flush=True)
+    _forced_give_up_then_clean(
+        lambda: rws.softmax(x),
+        lambda y: check(y.double().cpu().numpy(), oracle.safe_softmax(xs), "f16", "fused"))
 
 
 def test_backward_ordered_reports_give_up():
