@@ -53,7 +53,7 @@ KERNEL_SOURCES = {
     "block_onepass": _SOFTMAX_COMMON + ["rws_block_onepass.hip"],
     "two_pass": _SOFTMAX_COMMON + ["rws_two_pass.hip"],
     "splitk": _SOFTMAX_COMMON + ["rws_splitk.hip"],
-    "splitk_fused": _SOFTMAX_COMMON + ["rws_splitk_fused.hip"],
+    "splitk_fused": _SOFTMAX_COMMON + ["rws_ordered.hpp", "rws_splitk_fused.hip"],
     "splitk_ordered": _SOFTMAX_COMMON + ["rws_ordered.hpp", "rws_splitk_ordered.hip"],
     "masked": _SOFTMAX_COMMON + ["rws_masked.hip"],
     "backward": _SOFTMAX_COMMON + ["rws_ordered.hpp", "rws_backward.hip"],
