@@ -56,7 +56,7 @@ KERNEL_SOURCES = {
     "splitk_fused": _SOFTMAX_COMMON + ["rws_ordered.hpp", "rws_splitk_fused.hip"],
     "splitk_ordered": _SOFTMAX_COMMON + ["rws_ordered.hpp", "rws_splitk_ordered.hip"],
     "masked": _SOFTMAX_COMMON + ["rws_masked.hip"],
-    "backward": _SOFTMAX_COMMON + ["rws_ordered.hpp", "rws_backward.hip"],
+    "backward": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_ordered.hpp", "rws_backward.hip"],
     "layernorm": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_ordered.hpp", "rws_norm.hpp",
                                     "rws_norm_wave.hip", "rws_norm_block.hip"],
 }
