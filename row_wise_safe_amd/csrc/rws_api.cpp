@@ -174,12 +174,19 @@ int64_t block_rows_per_launch(int block) {
 }
 
 // Choose among the wave_row variants: the narrowest lane group whose
-// registers hold the window, then the number of row sets per wave that
-// measured fastest on MI355X with rows streamed from HBM: one for plain
-// softmax (fp16 512 columns: 21.9 us vs 23.1 us with two; bf16 128 columns
-// with 16-lane groups: 79.8 us vs 81.8 us), two for the masked form of
-// one-granule full-wave rows (fp16 [65536,512] with a [512,512] mask and
-// causal limit: 22.7 us vs 25.4 us with one).
+// registers hold the window, then the form that measured fastest on MI355X
+// with rows streamed from HBM.  Plain softmax: one row set per wave and one
+// granule per lane where it holds the row (fp16 512 columns: 21.9 us vs 23.1
+// with two row sets, 22.8 with 32 lanes x 2 granules; bf16 128 columns with
+// 16-lane groups: 79.8 us vs 81.8 us with two row sets).  The masked form
+// (scale, mask and causal limit): two granules per lane on 8-32 lanes where
+// that holds the row, else two row sets for one-granule full-wave rows.
+// fp16 [rows,cols] with a [cols,cols] mask and causal limit, about 64 MiB
+// in: 128 columns 20.9 us (8x2) vs 22.9 (16x1); 192: 22.6 (16x2) vs 30.8
+// (32x1); 256: 20.0 (16x2) vs 23.3 (32x1); 384: 15.1 (32x2) vs 16.5 (64x1,
+// two row sets); 512: 19.8 (32x2) vs 20.7 (64x1, two row sets; 25.4 with
+// one); four granules on 32 lanes lost to two on 64 (768 columns 29.0 vs
+// 21.8, 1024: 26.1 vs 19.7).
 // max_k limits the granules per lane.
 int pick_wave_row(const Geometry& g, bool masked = false, int max_k = 1 << 30) {
     int best = -1;
@@ -189,8 +196,10 @@ int pick_wave_row(const Geometry& g, bool masked = false, int max_k = 1 << 30) {
         const int64_t w = window_granules(g, wave_row_wa(v));
         if ((int64_t)v.G * v.K < w || v.K > max_k) continue;
         const int64_t cap = (int64_t)v.G * v.K;
-        const int want_u = (masked && v.G == 64 && v.K == 1) ? 2 : 1;
-        const int64_t key = cap * 64 + (v.U == want_u ? 0 : v.U);
+        int pref = 2;
+        if (masked && v.K == 2 && v.G < 64) pref = 0;
+        else if (v.U == ((masked && v.G == 64 && v.K == 1) ? 2 : 1)) pref = 1;
+        const int64_t key = cap * 4 + pref;
         if (best < 0 || key < best_key) {
             best = i;
             best_key = key;

@@ -16,6 +16,8 @@ static MaskPre<DT> make_pre(const MaskArgs& M) {
     p.mask_rows = M.mask_rows > 0 ? M.mask_rows : 1;
     p.causal_q = M.causal_q;
     p.row_base = M.row_base;
+    p.mask_M = remainder_magic((uint64_t)p.mask_rows);
+    p.causal_M = p.causal_q > 0 ? remainder_magic((uint64_t)p.causal_q) : 0;
     return p;
 }
 

@@ -308,13 +308,23 @@ def test_describe_mentions_alignment(lib):
     assert ",aligned" in rws.softmax_describe_launch(8, 128, rws.RWS_F16, 256, 512)
 
 
-def test_masked_launch_choice(lib):
-    # full-wave fp16 rows: one row set per wave for plain softmax, two for the
-    # masked form (each measured fastest on MI355X)
-    plain = rws.softmax_describe_launch(65536, 512, rws.RWS_F16, 256, 512)
-    masked = rws.softmax_describe_launch(65536, 512, rws.RWS_F16, 256, 512, masked=True)
-    assert "G=64,K=1,U=1" in plain and "block=64" in plain
-    assert "G=64,K=1,U=2" in masked
+@pytest.mark.parametrize("cols,plain_group,masked_group", [
+    (512, "G=64,K=1,U=1", "G=32,K=2,U=1"),
+    (384, "G=64,K=1,U=1", "G=32,K=2,U=1"),
+    (256, "G=32,K=1,U=1", "G=16,K=2,U=1"),
+    (192, "G=32,K=1,U=1", "G=16,K=2,U=1"),
+    (128, "G=16,K=1,U=1", "G=8,K=2,U=1"),
+    (1024, "G=64,K=2,U=1", "G=64,K=2,U=1"),
+])
+def test_masked_launch_choice(lib, cols, plain_group, masked_group):
+    # one granule per lane for plain softmax where it holds the row; two
+    # granules per lane on half the lanes for the masked form (each measured
+    # fastest on MI355X); two granules on full waves for both past 64
+    rows = 64 * cols
+    plain = rws.softmax_describe_launch(rows, cols, rws.RWS_F16, 256, 512)
+    masked = rws.softmax_describe_launch(rows, cols, rws.RWS_F16, 256, 512, masked=True)
+    assert plain_group in plain and "block=64" in plain, plain
+    assert masked_group in masked and "block=64" in masked, masked
 
 
 def test_masked_argument_checks(lib):

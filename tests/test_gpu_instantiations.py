@@ -102,8 +102,8 @@ def test_every_forward_lane_group(dtype, masked):
     cases = _scan(_fwd_describe, dtype, ["auto", "wave_row"], extra=(masked,))
     groups = {k[3:6] for k in cases}
     assert len(groups) >= 8, sorted(groups)
-    if masked:  # the masked line's launch: two row sets per wave
-        assert (64, 1, 2) in groups
+    if masked:  # the masked line's launch: two granules per lane on 32 lanes
+        assert (32, 2, 1) in groups
     for key, (rows, cols, offs, kernel) in sorted(cases.items()):
         g = np.random.Generator(np.random.PCG64(rows * 131 + cols + offs[0] * 7 + offs[1]))
         x, xs = to_device(g.normal(0.0, 4.0, (rows, cols)), dtype, offset=offs[0])
@@ -182,7 +182,7 @@ def test_masked_bench_line_full_size():
     desc = rws.softmax_describe_launch(w.rows, w.cols, rws.RWS_F16, x.data_ptr(), out.data_ptr(),
                                        masked=True)
     print(desc, flush=True)
-    assert desc.startswith("wave_row<f16,aligned,G=64,K=1,U=2>") and desc.endswith("store=wt")
+    assert desc.startswith("wave_row<f16,aligned,G=32,K=2,U=1>") and desc.endswith("store=wt")
     rws.softmax_masked(x, 0.125, mask, causal_q=w.cols, out=out)
     torch.cuda.synchronize()
     ref = oracle.masked_softmax(xs, 0.125, ms, causal_q=w.cols)

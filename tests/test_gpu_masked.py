@@ -76,11 +76,37 @@ def test_scale_only(dtype, scale):
         check(_masked(x, scale, None, 0, kernel), ref, dtype, f"{kernel} scale={scale}")
 
 
+def _plain_same_launch(x, kernel):
+    """The plain softmax through the compiled variant the masked form picks
+    (the masked form prefers other lane groups than the plain one)."""
+    rows, cols = x.shape
+    code = rws.dtype_code(x.dtype)
+    desc = rws.softmax_describe_launch(rows, cols, code, x.data_ptr(), x.data_ptr(),
+                                       rws.KERNEL_IDS[kernel], masked=True)
+    family, shape = desc.split("<")[0], desc.split(">")[0].split(",", 2)[2]
+    kid = rws.KERNEL_IDS[family]
+    y = torch.empty_like(x)
+    for v in range(rws.softmax_variant_count(kid)):
+        try:
+            d = rws.softmax_describe_variant(rows, cols, code, x.data_ptr(), y.data_ptr(), kid, v)
+        except rws.SoftmaxError:
+            continue
+        if d.split(">")[0].split(",", 2)[2] == shape:
+            st = rws.softmax_fwd_variant(x.data_ptr(), y.data_ptr(), rows, cols, code,
+                                         torch.cuda.current_stream().cuda_stream, kid, v)
+            assert st == rws.RWS_OK
+            return y
+    raise AssertionError(f"no plain variant of {desc}")
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
-def test_identity_prologue_equals_plain(kernel):
-    x, _ = to_device(np.random.Generator(np.random.PCG64(3)).normal(0, 4, (65, 512)), "f16")
+@pytest.mark.parametrize("cols", [512, 256, 128])
+def test_identity_prologue_equals_plain(kernel, cols):
+    # scale 1, no mask, no causal limit: bit-identical to the plain kernel of
+    # the same shape
+    x, _ = to_device(np.random.Generator(np.random.PCG64(3)).normal(0, 4, (65, cols)), "f16")
     a = _masked(x, 1.0, None, 0, kernel)
-    b = rws.softmax(x, kernel=kernel)
+    b = _plain_same_launch(x, kernel)
     torch.cuda.synchronize()
     assert np.array_equal(a, b.double().cpu().numpy())
 
