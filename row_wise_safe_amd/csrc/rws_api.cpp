@@ -186,7 +186,11 @@ int64_t block_rows_per_launch(int block) {
 // (32x1); 256: 20.0 (16x2) vs 23.3 (32x1); 384: 15.1 (32x2) vs 16.5 (64x1,
 // two row sets); 512: 19.8 (32x2) vs 20.7 (64x1, two row sets; 25.4 with
 // one); four granules on 32 lanes lost to two on 64 (768 columns 29.0 vs
-// 21.8, 1024: 26.1 vs 19.7).
+// 21.8, 1024: 26.1 vs 19.7).  Rows that are not line-aligned take the same
+// two-granule groups (two to four rows per wave instead of one to two):
+// fp16 [131072,250] 34.2 us (32x2) vs 42.4 (64x1), [262144,120] 28.9 (16x2)
+// vs 37.4 (32x1), [524288,60] 35.4 (8x2) vs 40.6 (16x1); line-aligned rows
+// keep one granule per lane ([131072,256] 21.6 (32x1) vs 22.6 (16x2)).
 // max_k limits the granules per lane.
 int pick_wave_row(const Geometry& g, bool masked = false, int max_k = 1 << 30) {
     int best = -1;
@@ -197,7 +201,7 @@ int pick_wave_row(const Geometry& g, bool masked = false, int max_k = 1 << 30) {
         if ((int64_t)v.G * v.K < w || v.K > max_k) continue;
         const int64_t cap = (int64_t)v.G * v.K;
         int pref = 2;
-        if (masked && v.K == 2 && v.G < 64) pref = 0;
+        if ((masked || !g.a128) && v.K == 2 && v.G < 64) pref = 0;
         else if (v.U == ((masked && v.G == 64 && v.K == 1) ? 2 : 1)) pref = 1;
         const int64_t key = cap * 4 + pref;
         if (best < 0 || key < best_key) {
