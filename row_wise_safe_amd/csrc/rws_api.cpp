@@ -123,7 +123,10 @@ int64_t window_granules(const Geometry& g, int wa) {
     return (g.row_bytes + wa + 15) / 16;
 }
 
+// window alignment of the backward's and the normalisations' lane groups
 int wave_row_wa(const rws::WaveRowVariant& v) { return v.G * 16 >= 128 ? 128 : 16; }
+// and of the forward's (wave_row, plain and masked)
+int softmax_wave_wa(const rws::WaveRowVariant& v) { return rws::softmax_window_align(v.G); }
 
 // Rows per XCD run (log2) for the one-row-per-workgroup kernels that hold the
 // row in registers (block_onepass, the backward's bwd_block): on rows that are
@@ -197,7 +200,7 @@ int pick_wave_row(const Geometry& g, bool masked = false, int max_k = 1 << 30) {
     int64_t best_key = 0;
     for (int i = 0; i < rws::kNumWaveRow; ++i) {
         const rws::WaveRowVariant& v = rws::kWaveRow[i];
-        const int64_t w = window_granules(g, wave_row_wa(v));
+        const int64_t w = window_granules(g, softmax_wave_wa(v));
         if ((int64_t)v.G * v.K < w || v.K > max_k) continue;
         const int64_t cap = (int64_t)v.G * v.K;
         int pref = 2;
@@ -449,7 +452,7 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
             if (forced_variant >= 0) {
                 if (forced_variant >= rws::kNumWaveRow) return bad_variant(rws::kNumWaveRow);
                 const rws::WaveRowVariant& f = rws::kWaveRow[forced_variant];
-                if ((int64_t)f.G * f.K < window_granules(g, wave_row_wa(f)))
+                if ((int64_t)f.G * f.K < window_granules(g, softmax_wave_wa(f)))
                     return bad_variant(rws::kNumWaveRow);
                 p->variant = forced_variant;
             }
@@ -457,7 +460,7 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
                 return fail(RWS_ERR_UNSUPPORTED_SHAPE,
                             "wave_row holds at most 512 granules (16 bytes) per row window");
             const rws::WaveRowVariant& v = rws::kWaveRow[p->variant];
-            const int wa = wave_row_wa(v);
+            const int wa = softmax_wave_wa(v);
             p->aligned = wa == 128 ? g.a128 : g.a16;
             p->window = window_granules(g, wa);
             // every 128-byte line of the output is written by one wave:

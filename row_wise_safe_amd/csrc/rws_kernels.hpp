@@ -21,6 +21,7 @@
 #pragma once
 
 #include "rws_device.hpp"
+#include "rws_launch.hpp"
 #include "rws_pre.hpp"
 
 namespace rws {
@@ -94,8 +95,7 @@ __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
     // ALIGNED rows whose window fills all G*K slots need no masking.
     const bool full = ALIGNED && (cols / VEC >= G * K);
 
-    // lane groups of at least one cache line get line-aligned windows
-    constexpr int WA = G * 16 >= kLineBytes ? kLineBytes : 16;
+    constexpr int WA = softmax_window_align(G);
     RowWin<DT, ALIGNED, WA> w[U];
     typename Pre::Ctx pc[U];  // prologue context of the row each set loads
     u32x4 raw[U][K];

@@ -33,6 +33,17 @@ struct MaskArgs {
 };
 
 struct WaveRowVariant { int G, K, U; };          // lanes per row, granules per lane, row sets
+
+// Alignment (bytes) of the row windows of the forward's lane groups
+// (wave_row, plain and masked): a 128-byte line for groups of 16 lanes or
+// more, so that their lanes cover whole lines; 16 bytes for narrower groups,
+// whose rows are short enough that a line-aligned window would mostly load
+// neighbouring rows' bytes.  fp16 rows that are not line-aligned, 8-lane
+// groups: [1000000,33] 54.9 us against 93.9 with line-aligned windows,
+// [524288,60] 29.7 against 35.4 (line-aligned rows unchanged: [2097152,64]
+// 80.1 both).  The backward's and the normalisations' lane groups keep
+// line-aligned windows from 8 lanes.
+constexpr int softmax_window_align(int G) { return G * 16 > 128 ? 128 : 16; }
 struct OnepassVariant { int block, kr, kl; };    // threads, register granules, LDS granules
 struct TwoPassVariant { int block, u; };         // threads, granules per batch
 struct SplitkVariant { int block, kc; };         // threads, granules per thread per chunk
