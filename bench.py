@@ -55,6 +55,7 @@ KERNEL_SOURCES = {
     "splitk": _SOFTMAX_COMMON + ["rws_splitk.hip"],
     "splitk_fused": _SOFTMAX_COMMON + ["rws_ordered.hpp", "rws_splitk_fused.hip"],
     "splitk_ordered": _SOFTMAX_COMMON + ["rws_ordered.hpp", "rws_splitk_ordered.hip"],
+    "tile_rows": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_tile_rows.hip"],
     "masked": _SOFTMAX_COMMON + ["rws_masked.hip"],
     "backward": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_ordered.hpp", "rws_backward.hip"],
     "layernorm": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_ordered.hpp", "rws_norm.hpp",
@@ -65,6 +66,7 @@ KERNEL_SOURCES["rmsnorm"] = KERNEL_SOURCES["layernorm"]
 KERNEL_SYMBOL = {"wave_row": "k_wave_row", "block_onepass": "k_block_onepass",
                  "two_pass": "k_two_pass", "splitk": "k_splitk_stage",
                  "splitk_fused": "k_splitk_fused", "splitk_ordered": "k_splitk_ordered",
+                 "tile_rows": "k_tile_rows",
                  "masked": "MaskPre", "backward": "k_bwd_",
                  "layernorm": "k_norm_", "rmsnorm": "k_norm_"}
 

@@ -134,7 +134,7 @@ enum {
                                  rows number at most four, exceed 32 MiB
                                  together, or need more than 512 chunks
                                  each */
-    RWS_KERNEL_SPLITK_ORDERED = 6 /* split-k in one ordinary launch: the
+    RWS_KERNEL_SPLITK_ORDERED = 6, /* split-k in one ordinary launch: the
                                  stage-1 workgroups (partial (m, d) per chunk)
                                  come first in the grid, the stage-2
                                  workgroups (merge, re-read, write) after
@@ -151,6 +151,18 @@ enum {
                                  softmax_stream_status reports.  The
                                  dispatcher's choice for few long rows of up
                                  to 32 MiB together and 512 chunks each */
+    RWS_KERNEL_TILE_ROWS = 7     /* short rows whose byte length is not a
+                                 multiple of 16: one wave takes 4, 8 or 16
+                                 consecutive rows as one 16-byte-aligned
+                                 range (every granule read and written whole
+                                 by one lane) and reduces each row across the
+                                 lanes that hold it, through LDS.  Needs in
+                                 and out 16-byte aligned, rows of at least
+                                 one granule and at most 4096 bytes per tile
+                                 (RWS_ERR_UNSUPPORTED_SHAPE otherwise).  The
+                                 dispatcher's choice for many such rows of up
+                                 to 512 bytes (plain softmax; the masked form
+                                 has no tile form) */
 };
 
 /*

@@ -51,7 +51,7 @@ RWS_ERR_UNSUPPORTED_SHAPE = 5
 RWS_ERR_WAIT_TIMEOUT = 6
 
 KERNEL_IDS = {"auto": 0, "wave_row": 1, "block_onepass": 2, "two_pass": 3, "splitk": 4,
-              "splitk_fused": 5, "splitk_ordered": 6}
+              "splitk_fused": 5, "splitk_ordered": 6, "tile_rows": 7}
 KERNELS = tuple(k for k in KERNEL_IDS if k != "auto")
 
 _DTYPES = {torch.float32: RWS_F32, torch.float16: RWS_F16, torch.bfloat16: RWS_BF16}

@@ -21,6 +21,7 @@ ARCH = "gfx950"
 SOURCES = [
     "rws_api.cpp",
     "rws_wave_row.hip",
+    "rws_tile_rows.hip",
     "rws_block_onepass.hip",
     "rws_two_pass.hip",
     "rws_splitk.hip",

@@ -128,6 +128,45 @@ int wave_row_wa(const rws::WaveRowVariant& v) { return v.G * 16 >= 128 ? 128 : 1
 // and of the forward's (wave_row, plain and masked)
 int softmax_wave_wa(const rws::WaveRowVariant& v) { return rws::softmax_window_align(v.G); }
 
+// The dispatcher's rows for tile_rows: plain softmax over many rows of at
+// most kTileMaxRowBytes whose byte length is not a multiple of 16 (so every
+// row has partial granules at its ends), in and out 16-byte aligned.
+constexpr int64_t kTileMaxRowBytes = 2048;
+constexpr int64_t kTileMinRows = 64;
+
+int pick_tile_rows(int64_t cols, int es, int forced_t);
+
+bool tile_rows_fits(int64_t rows, int64_t cols, int dtype, const void* in, const void* out) {
+    const int es = elem_size(dtype);
+    const int64_t rb = cols * es;
+    return rows >= kTileMinRows && rb % 16 != 0 && rb <= kTileMaxRowBytes &&
+           (uintptr_t)in % 16 == 0 && (uintptr_t)out % 16 == 0 && pick_tile_rows(cols, es, 0) >= 0;
+}
+
+// tile_rows: the variant for rows of `cols` elements of size es, or -1.
+// Tiles of T rows start on a 16-byte boundary when T is a multiple of
+// 16 / gcd(row bytes, 16); the largest T (up to 16) whose tile fits 64 * K
+// granules with K <= 4, and the smallest such K.  forced_t > 0 asks for
+// that T.
+int pick_tile_rows(int64_t cols, int es, int forced_t) {
+    const int vec = 16 / es;
+    if (cols < vec || cols * es > 4096) return -1;
+    int g = 16;
+    while ((cols * es) % g) g /= 2;
+    const int p0 = 16 / g;  // rows per 16-byte period
+    int best = -1;
+    for (int i = 0; i < rws::kNumTileRows; ++i) {
+        const rws::TileRowsVariant& v = rws::kTileRows[i];
+        if (v.T % p0 || (forced_t > 0 && v.T != forced_t)) continue;
+        const int64_t gran = (int64_t)v.T * cols * es / 16;
+        if (gran > 64LL * v.K) continue;
+        if (best < 0 || v.T > rws::kTileRows[best].T ||
+            (v.T == rws::kTileRows[best].T && v.K < rws::kTileRows[best].K))
+            best = i;
+    }
+    return best;
+}
+
 // Rows per XCD run (log2) for the one-row-per-workgroup kernels that hold the
 // row in registers (block_onepass, the backward's bwd_block): on rows that are
 // not line-aligned, runs of at least 128 KiB of consecutive rows per XCD
@@ -419,7 +458,9 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
         const bool parks = onepass_fits && rws::kOnepass[ov].kl > 0;
         const bool splitk_rows =
             !onepass_fits || 2 * rows < cus || (2 * rows <= cus && parks);
-        if (pick_wave_row(g, masked, 1) >= 0) {
+        if (!masked && tile_rows_fits(rows, cols, dtype, in, out)) {
+            family = RWS_KERNEL_TILE_ROWS;
+        } else if (pick_wave_row(g, masked, 1) >= 0) {
             family = RWS_KERNEL_WAVE_ROW;
         } else if (few_rows && wline >= 2048 && splitk_rows) {
             family = RWS_KERNEL_SPLITK_ORDERED;
@@ -443,10 +484,33 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
     }
     if (masked && is_splitk(family))
         return fail(RWS_ERR_UNSUPPORTED_SHAPE, "the masked form has no split-k kernel");
+    if (masked && family == RWS_KERNEL_TILE_ROWS)
+        return fail(RWS_ERR_UNSUPPORTED_SHAPE, "the masked form has no tile_rows kernel");
     p->family = family;
     p->aligned = g.a128;
     p->window = wline;
     switch (family) {
+        case RWS_KERNEL_TILE_ROWS: {
+            const int es = elem_size(dtype);
+            if ((uintptr_t)in % 16 || (uintptr_t)out % 16)
+                return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows needs 16-byte aligned in and out");
+            p->variant = pick_tile_rows(cols, es, 0);
+            if (forced_variant >= 0) {
+                if (forced_variant >= rws::kNumTileRows) return bad_variant(rws::kNumTileRows);
+                if (pick_tile_rows(cols, es, rws::kTileRows[forced_variant].T) < 0) return bad_variant(rws::kNumTileRows);
+                const rws::TileRowsVariant& f = rws::kTileRows[forced_variant];
+                if ((int64_t)f.T * cols * es / 16 > 64LL * f.K) return bad_variant(rws::kNumTileRows);
+                p->variant = forced_variant;
+            }
+            if (p->variant < 0)
+                return fail(RWS_ERR_UNSUPPORTED_SHAPE,
+                            "tile_rows takes rows of one granule to 4096 bytes");
+            p->aligned = false;
+            p->window = (int64_t)rws::kTileRows[p->variant].T * cols * es / 16;
+            // tiles (workgroups) per launch below 2^31
+            p->max_rows_per_launch = (int64_t)rws::kTileRows[p->variant].T * ((int64_t)1 << 30);
+            break;
+        }
         case RWS_KERNEL_WAVE_ROW: {
             p->variant = pick_wave_row(g, masked);
             if (forced_variant >= 0) {
@@ -823,7 +887,7 @@ bool captured_tags(hipStream_t stream, int64_t words, uint64_t** tags, int64_t* 
 int check_args(const void* in, void* out, int64_t rows, int64_t cols, int dtype, int kernel_id) {
     if (dtype != RWS_F32 && dtype != RWS_F16 && dtype != RWS_BF16)
         return fail(RWS_ERR_UNSUPPORTED_DTYPE, "dtype must be RWS_F32, RWS_F16 or RWS_BF16");
-    if (kernel_id < RWS_KERNEL_AUTO || kernel_id > RWS_KERNEL_SPLITK_ORDERED)
+    if (kernel_id < RWS_KERNEL_AUTO || kernel_id > RWS_KERNEL_TILE_ROWS)
         return fail(RWS_ERR_INVALID_ARG, "unknown kernel id " + std::to_string(kernel_id));
     if (rows < 0 || cols < 0) return fail(RWS_ERR_INVALID_ARG, "rows and cols must be >= 0");
     if (cols > kMaxCols) return fail(RWS_ERR_UNSUPPORTED_SHAPE, "cols above 2^30");
@@ -968,6 +1032,7 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
         } else {
             switch (p.family) {
                 case RWS_KERNEL_WAVE_ROW: e = rws::launch_wave_row(L, p.variant); break;
+                case RWS_KERNEL_TILE_ROWS: e = rws::launch_tile_rows(L, p.variant); break;
                 case RWS_KERNEL_BLOCK_ONEPASS: e = rws::launch_block_onepass(L, p.variant); break;
                 case RWS_KERNEL_TWO_PASS: e = rws::launch_two_pass(L, p.variant); break;
                 case RWS_KERNEL_SPLITK:
@@ -1566,7 +1631,7 @@ static int describe_launch(int64_t rows, int64_t cols, int dtype, const void* in
     buf[0] = 0;
     if (dtype != RWS_F32 && dtype != RWS_F16 && dtype != RWS_BF16)
         return fail(RWS_ERR_UNSUPPORTED_DTYPE, "dtype must be RWS_F32, RWS_F16 or RWS_BF16");
-    if (kernel_id < RWS_KERNEL_AUTO || kernel_id > RWS_KERNEL_SPLITK_ORDERED)
+    if (kernel_id < RWS_KERNEL_AUTO || kernel_id > RWS_KERNEL_TILE_ROWS)
         return fail(RWS_ERR_INVALID_ARG, "unknown kernel id " + std::to_string(kernel_id));
     if (rows < 0 || cols < 0) return fail(RWS_ERR_INVALID_ARG, "rows and cols must be >= 0");
     if (cols > kMaxCols) return fail(RWS_ERR_UNSUPPORTED_SHAPE, "cols above 2^30");
@@ -1582,6 +1647,14 @@ static int describe_launch(int64_t rows, int64_t cols, int dtype, const void* in
     char run[32] = "";
     if (p.lgrun > 0) std::snprintf(run, sizeof run, " xcd_run=%d", 1 << p.lgrun);
     switch (p.family) {
+        case RWS_KERNEL_TILE_ROWS: {
+            const rws::TileRowsVariant& v = rws::kTileRows[p.variant];
+            std::snprintf(buf, (size_t)buflen, "tile_rows<%s,T=%d,K=%d> grid=%lld block=64 granules<=%lld",
+                          dtype_name(dtype), v.T, v.K,
+                          (long long)((std::min(rows, p.max_rows_per_launch) + v.T - 1) / v.T),
+                          (long long)wmax);
+            break;
+        }
         case RWS_KERNEL_WAVE_ROW: {
             const rws::WaveRowVariant& v = rws::kWaveRow[p.variant];
             std::snprintf(buf, (size_t)buflen,
@@ -1668,6 +1741,7 @@ int softmax_variant_count(int kernel_id) {
         case RWS_KERNEL_SPLITK:
         case RWS_KERNEL_SPLITK_ORDERED: return rws::kNumSplitk;
         case RWS_KERNEL_SPLITK_FUSED: return rws::kNumSplitkFused;
+        case RWS_KERNEL_TILE_ROWS: return rws::kNumTileRows;
     }
     return 0;
 }
@@ -1782,6 +1856,7 @@ const char* softmax_kernel_name(int kernel_id) {
         case RWS_KERNEL_SPLITK: return "splitk";
         case RWS_KERNEL_SPLITK_FUSED: return "splitk_fused";
         case RWS_KERNEL_SPLITK_ORDERED: return "splitk_ordered";
+        case RWS_KERNEL_TILE_ROWS: return "tile_rows";
     }
     return "unknown";
 }

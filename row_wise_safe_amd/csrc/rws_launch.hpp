@@ -47,6 +47,7 @@ constexpr int softmax_window_align(int G) { return G * 16 > 128 ? 128 : 16; }
 struct OnepassVariant { int block, kr, kl; };    // threads, register granules, LDS granules
 struct TwoPassVariant { int block, u; };         // threads, granules per batch
 struct SplitkVariant { int block, kc; };         // threads, granules per thread per chunk
+struct TileRowsVariant { int T, K; };            // rows per tile, granules per lane
 
 extern const WaveRowVariant kWaveRow[];
 extern const int kNumWaveRow;
@@ -58,6 +59,8 @@ extern const SplitkVariant kSplitk[];
 extern const int kNumSplitk;
 extern const SplitkVariant kSplitkFused[];
 extern const int kNumSplitkFused;
+extern const TileRowsVariant kTileRows[];
+extern const int kNumTileRows;
 
 // Waves per workgroup of the wave-per-row kernels (wave_row, bwd_wave,
 // norm_wave; the kernels read it from blockDim).  One-wave workgroups
@@ -75,6 +78,10 @@ inline int64_t wave_row_grid(const WaveRowVariant& v, int64_t rows) {
 }
 
 hipError_t launch_wave_row(const Launch& L, int variant);
+// Tiles of kTileRows[variant].T rows per one-wave workgroup; in and out
+// 16-byte aligned, T * cols * element size a multiple of 16, at most 64 * K
+// granules per tile.
+hipError_t launch_tile_rows(const Launch& L, int variant);
 hipError_t launch_block_onepass(const Launch& L, int variant);
 hipError_t launch_two_pass(const Launch& L, int variant);
 // Both split-k stages; ws holds rows*P (m, d) pairs.

@@ -56,9 +56,9 @@ def test_status_strings_and_names(lib):
     for st in range(1, 7):
         assert rws.softmax_status_string(st) not in ("", "ok", "unknown status")
     assert rws.softmax_status_string(99) == "unknown status"
-    assert [rws.softmax_kernel_name(i) for i in range(7)] == \
+    assert [rws.softmax_kernel_name(i) for i in range(8)] == \
         ["auto", "wave_row", "block_onepass", "two_pass", "splitk", "splitk_fused",
-         "splitk_ordered"]
+         "splitk_ordered", "tile_rows"]
     assert rws.softmax_kernel_name(17) == "unknown"
 
 
@@ -86,7 +86,7 @@ def test_empty_is_success_without_pointers(lib):
 
 def test_bad_kernel_id(lib):
     assert rws.softmax_fwd_kernel(32, 32, 2, 2, rws.RWS_F32, 0, 9) == rws.RWS_ERR_INVALID_ARG
-    assert rws.softmax_fwd_kernel(32, 32, 2, 2, rws.RWS_F32, 0, 7) == rws.RWS_ERR_INVALID_ARG
+    assert rws.softmax_fwd_kernel(32, 32, 2, 2, rws.RWS_F32, 0, 8) == rws.RWS_ERR_INVALID_ARG
     assert rws.softmax_fwd_kernel(32, 32, 2, 2, rws.RWS_F32, 0, -1) == rws.RWS_ERR_INVALID_ARG
 
 
