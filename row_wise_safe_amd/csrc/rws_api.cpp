@@ -129,8 +129,18 @@ int wave_row_wa(const rws::WaveRowVariant& v) { return v.G * 16 >= 128 ? 128 : 1
 int softmax_wave_wa(const rws::WaveRowVariant& v) { return rws::softmax_window_align(v.G); }
 
 // The dispatcher's rows for tile_rows: plain softmax over many rows of at
-// most kTileMaxRowBytes whose byte length is not a multiple of 16 (so every
-// row has partial granules at its ends), in and out 16-byte aligned.
+// most kTileMaxRowBytes that are not line-aligned -- with partial granules at
+// their ends (byte length not a multiple of 16), or 16-byte multiples above
+// 128 bytes -- in and out 16-byte aligned, and a tile the compiled shapes
+// hold.  MI355X, fp16, inputs in HBM, tile_rows against the lane-group form
+// (wave_row): [131072,250] 25.4 us vs 34.5, [1000000,33] 38.7 vs 55.0,
+// [1048576,100] 81.5 vs 122, [64000,500] 25.2 vs 30.2, fp32 [131072,125]
+// 25.1 vs 29.2; 16-byte multiples [262144,120] 25.1 vs 31.5, [131072,248]
+// 25.2 vs 29.9, [65536,504] 25.5 vs 29.3, but [524288,56] 24.2 vs 20.2 (one
+// granule per lane on 8 lanes, 16-byte windows, holds those rows whole).
+// Tiles of eight granules per lane (spilling 374-388 scalar registers) lost
+// to the lane groups and block_onepass: [65536,333] 26.2 vs 21.0,
+// [32768,1022] 29.2 vs 24.8; the tile shapes stop at four.
 constexpr int64_t kTileMaxRowBytes = 2048;
 constexpr int64_t kTileMinRows = 64;
 
@@ -139,7 +149,8 @@ int pick_tile_rows(int64_t cols, int es, int forced_t);
 bool tile_rows_fits(int64_t rows, int64_t cols, int dtype, const void* in, const void* out) {
     const int es = elem_size(dtype);
     const int64_t rb = cols * es;
-    return rows >= kTileMinRows && rb % 16 != 0 && rb <= kTileMaxRowBytes &&
+    return rows >= kTileMinRows && rb % 128 != 0 && (rb % 16 != 0 || rb > 128) &&
+           rb <= kTileMaxRowBytes &&
            (uintptr_t)in % 16 == 0 && (uintptr_t)out % 16 == 0 && pick_tile_rows(cols, es, 0) >= 0;
 }
 

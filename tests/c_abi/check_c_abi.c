@@ -291,6 +291,9 @@ int main(void)
     softmax_case("softmax_fwd fp32 [2,3] (row 1 unaligned)", RWS_F32, 2, 3, NULL, RWS_KERNEL_AUTO);
     softmax_case("softmax_fwd fp32 [64,1000]", RWS_F32, 64, 1000, NULL, RWS_KERNEL_AUTO);
     softmax_case("softmax_fwd bf16 [4096,512]", RWS_BF16, 4096, 512, s, RWS_KERNEL_AUTO);
+    softmax_case("softmax_fwd bf16 [1000,250] (tile_rows)", RWS_BF16, 1000, 250, s, RWS_KERNEL_AUTO);
+    softmax_case("softmax_fwd_kernel fp32 [999,77] tile_rows", RWS_F32, 999, 77, s,
+                 RWS_KERNEL_TILE_ROWS);
     softmax_case("softmax_fwd bf16 [16,300001] (split-k)", RWS_BF16, 16, 300001, s, RWS_KERNEL_AUTO);
     softmax_case("softmax_fwd_kernel fp32 [3,70001] two_pass", RWS_F32, 3, 70001, s,
                  RWS_KERNEL_TWO_PASS);
