@@ -54,6 +54,16 @@ def window_granules(cols: int, dtype: str, aligned: bool) -> int:
     return b // 16 if aligned else (b + 143) // 16
 
 
+def tile_supports(cols: int, dtype: str) -> bool:
+    """tile_rows takes the row (16-byte aligned tensors): at least one
+    granule, and a tile of max(4, phase period) rows within 4096 bytes."""
+    es = 4 if dtype == "f32" else 2
+    g = 16
+    while (cols * es) % g:
+        g //= 2
+    return cols >= 16 // es and max(4, 16 // g) * cols * es <= 4096
+
+
 def supports(kernel: str, cols: int, dtype: str, aligned: bool) -> bool:
     es = 4 if dtype == "f32" else 2
     line = aligned and (cols * es) % 128 == 0

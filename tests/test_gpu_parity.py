@@ -17,7 +17,8 @@ import oracle
 import row_wise_safe_amd as rws
 import workloads
 from golden_io import load
-from gpu_util import NotCoResident, empty_like_at, have_gpu, run, supports, to_device
+from gpu_util import (NotCoResident, empty_like_at, have_gpu, run, supports, tile_supports,
+                      to_device)
 from tolerance import check, check_long_rows
 
 pytestmark = [pytest.mark.gpu,
@@ -126,8 +127,11 @@ def test_sweep_all_kernels(dtype, cols):
     ref = oracle.safe_softmax(stored)
     aligned = (cols * x.element_size()) % 16 == 0
     ran = 0
-    for kernel in ["auto"] + KERNELS:
-        if kernel != "auto" and not supports(kernel, cols, dtype, aligned):
+    for kernel in ["auto"] + KERNELS + ["tile_rows"]:
+        if kernel == "tile_rows":
+            if not tile_supports(cols, dtype):  # the base here is 16-byte aligned
+                continue
+        elif kernel != "auto" and not supports(kernel, cols, dtype, aligned):
             continue
         try:
             y = run(x, torch.empty_like(x), kernel)

@@ -129,6 +129,8 @@ def test_extremes_and_non_finite():
     x64[3, :] += 1e4              # large shift
     x64[4, 0] = -np.inf           # a -inf entry under a finite max: 0
     x64[5, :] = 3.0               # constant row
+    x64[6, :] += 3e7              # maximum past the FMA form's range (exact form)
+    x64[7, :] = -3e7 + x64[7, :]  # the same, negative
     x, xs = to_device(x64, "f32")
     y = torch.empty_like(x)
     rws.softmax(x, out=y, kernel="tile_rows")
