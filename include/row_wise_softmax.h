@@ -261,7 +261,11 @@ int softmax_bwd(const void *y, const void *dy, void *dx, int64_t rows, int64_t c
  * per row in one launch: chunk dot products published as epoch-tagged
  * words, as for softmax_fwd; the dispatcher's choice for few long rows; uses
  * the per-stream tag words that the forward's ordered form allocates on
- * first use).  Other ids: RWS_ERR_INVALID_ARG.
+ * first use) or RWS_KERNEL_TILE_ROWS (several short rows per wave, as for
+ * softmax_fwd; y, dy and dx 16-byte aligned; the dispatcher's choice for
+ * many short rows that are not line-aligned).  Other ids:
+ * RWS_ERR_INVALID_ARG.  softmax_bwd_describe_launch reports the choice for
+ * a dy with y's 16-byte alignment.
  */
 int softmax_bwd_kernel(const void *y, const void *dy, void *dx, int64_t rows, int64_t cols,
                        int dtype, void *stream, int kernel_id);
@@ -309,9 +313,12 @@ int rmsnorm_fwd(const void *in, void *out, int64_t rows, int64_t cols, int dtype
  * workgroup's registers, up to 4096 granules), RWS_KERNEL_TWO_PASS (any
  * length; the row is read twice) or RWS_KERNEL_SPLITK_ORDERED (several
  * workgroups per row in one launch, chunk statistics published as
- * epoch-tagged words; the dispatcher's choice for few long rows).  Other
- * ids: RWS_ERR_INVALID_ARG; a row too long for the forced kernel:
- * RWS_ERR_UNSUPPORTED_SHAPE.
+ * epoch-tagged words; the dispatcher's choice for few long rows) or
+ * RWS_KERNEL_TILE_ROWS (several short rows per wave, as for softmax_fwd;
+ * in and out 16-byte aligned, no weight or bias; the dispatcher's choice
+ * for many short rows that are not line-aligned, without weight and bias).
+ * Other ids: RWS_ERR_INVALID_ARG; a row too long for the forced kernel, or
+ * weight/bias with RWS_KERNEL_TILE_ROWS: RWS_ERR_UNSUPPORTED_SHAPE.
  */
 int layernorm_fwd_kernel(const void *in, void *out, int64_t rows, int64_t cols, int dtype,
                          float eps, const void *weight, const void *bias, float *mean, float *rstd,

@@ -1207,8 +1207,9 @@ struct BwdPlan {
 // allow_ordered: false when a captured call finds no tag buffer large enough
 // (see capturing()); a request for the ordered form then plans as
 // RWS_KERNEL_AUTO without it.
+// dy16: dy is 16-byte aligned (the tile form needs y, dy and dx so).
 static int plan_bwd(int64_t rows, int64_t cols, int dtype, const void* y, const void* dx,
-                    int kernel_id, BwdPlan* bp, bool allow_ordered = true) {
+                    bool dy16, int kernel_id, BwdPlan* bp, bool allow_ordered = true) {
     if (!allow_ordered && kernel_id == RWS_KERNEL_SPLITK_ORDERED) kernel_id = RWS_KERNEL_AUTO;
     const Geometry g = geometry(cols, dtype, y, dx);
     const int64_t wline = window_granules(g, 128);
@@ -1257,10 +1258,25 @@ static int plan_bwd(int64_t rows, int64_t cols, int dtype, const void* y, const 
         return best;
     };
     if (family == 0) {
-        if (pick_wave(1) >= 0) family = 1;
+        if (dy16 && tile_rows_fits(rows, cols, dtype, y, dx)) family = RWS_KERNEL_TILE_ROWS;
+        else if (pick_wave(1) >= 0) family = 1;
         else if (pick_block() >= 0) family = 2;
         else if (allow_ordered && few_long_rows(rows, wline, cus)) family = RWS_KERNEL_SPLITK_ORDERED;
         else family = 3;
+    }
+    if (family == RWS_KERNEL_TILE_ROWS) {
+        if (!dy16 || (uintptr_t)y % 16 || (uintptr_t)dx % 16)
+            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows needs 16-byte aligned y, dy and dx");
+        const int v = pick_tile_rows(cols, elem_size(dtype), 0);
+        if (v < 0)
+            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows takes rows of one granule to 4096 bytes");
+        bp->family = family;
+        bp->variant = v;
+        bp->aligned = false;
+        bp->same_phase = true;
+        bp->lgrun = 0;
+        bp->max_rows = (int64_t)rws::kTileRows[v].T * ((int64_t)1 << 30);
+        return RWS_OK;
     }
     if (family == RWS_KERNEL_SPLITK_ORDERED) {
         bp->family = family;
@@ -1305,16 +1321,17 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
     g_last_error.clear();
     if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
         kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS &&
-        kernel_id != RWS_KERNEL_SPLITK_ORDERED)
-        return fail(RWS_ERR_INVALID_ARG,
-                    "backward kernels: auto, wave_row, block_onepass, two_pass, splitk_ordered");
+        kernel_id != RWS_KERNEL_SPLITK_ORDERED && kernel_id != RWS_KERNEL_TILE_ROWS)
+        return fail(RWS_ERR_INVALID_ARG, "backward kernels: auto, wave_row, block_onepass, "
+                                         "two_pass, splitk_ordered, tile_rows");
     int st = check_args(y, dx, rows, cols, dtype, RWS_KERNEL_AUTO);
     if (st != RWS_OK || rows == 0 || cols == 0) return st;
     if (!dy) return fail(RWS_ERR_INVALID_ARG, "NULL dy with a non-empty tensor");
     if ((uintptr_t)dy % elem_size(dtype))
         return fail(RWS_ERR_MISALIGNED, "dy not aligned to the element size");
+    const bool dy16 = (uintptr_t)dy % 16 == 0;
     BwdPlan bp;
-    st = plan_bwd(rows, cols, dtype, y, dx, kernel_id, &bp);
+    st = plan_bwd(rows, cols, dtype, y, dx, dy16, kernel_id, &bp);
     if (st != RWS_OK) return st;
     // ordered split-k: keep the tag words locked until the launches are enqueued
     std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);
@@ -1328,7 +1345,7 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
         if (capturing((hipStream_t)stream)) {
             if (!captured_tags((hipStream_t)stream, words, &tags, &tag_n)) {
                 ws_lock.unlock();
-                st = plan_bwd(rows, cols, dtype, y, dx, kernel_id, &bp, false);
+                st = plan_bwd(rows, cols, dtype, y, dx, dy16, kernel_id, &bp, false);
                 if (st != RWS_OK) return st;
             } else if ((st = get_status_word((hipStream_t)stream, true, &status)) != RWS_OK) {
                 return st;
@@ -1359,7 +1376,9 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
         B.lgrun = bp.lgrun;
         B.stream = (hipStream_t)stream;
         hipError_t e = hipSuccess;
-        if (family != RWS_KERNEL_SPLITK_ORDERED)
+        if (family == RWS_KERNEL_TILE_ROWS)
+            e = rws::launch_bwd_tile(B, variant);
+        else if (family != RWS_KERNEL_SPLITK_ORDERED)
             e = rws::launch_bwd(B, family, variant);
         else if (tag_n == 0)
             e = rws::launch_bwd_ordered(
@@ -1455,11 +1474,28 @@ static int plan_norm(int64_t rows, int64_t cols, int dtype, const void* in, cons
     // with 512x1); any length streams.
     int family = kernel_id == RWS_KERNEL_AUTO ? 0 : kernel_id;
     if (family == 0) {
-        if (pick_wave(1) >= 0) family = 1;
+        if (!affine && tile_rows_fits(rows, cols, dtype, in, out)) family = RWS_KERNEL_TILE_ROWS;
+        else if (pick_wave(1) >= 0) family = 1;
         else if (pick_block() >= 0) family = 2;
         else if (allow_ordered && few_long_rows(rows, wline, device_info().cus))
             family = RWS_KERNEL_SPLITK_ORDERED;
         else family = 3;
+    }
+    if (family == RWS_KERNEL_TILE_ROWS) {
+        if (affine)
+            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "the tile_rows normalisation takes no weight or bias");
+        if ((uintptr_t)in % 16 || (uintptr_t)out % 16)
+            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows needs 16-byte aligned in and out");
+        const int v = pick_tile_rows(cols, elem_size(dtype), 0);
+        if (v < 0)
+            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows takes rows of one granule to 4096 bytes");
+        np->family = family;
+        np->variant = v;
+        np->aligned = false;
+        np->same_phase = true;
+        np->lgrun = 0;
+        np->max_rows = (int64_t)rws::kTileRows[v].T * ((int64_t)1 << 30);
+        return RWS_OK;
     }
     if (family == RWS_KERNEL_SPLITK_ORDERED) {
         np->family = family;
@@ -1509,9 +1545,9 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
     g_last_error.clear();
     if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
         kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS &&
-        kernel_id != RWS_KERNEL_SPLITK_ORDERED)
-        return fail(RWS_ERR_INVALID_ARG,
-                    "normalisation kernels: auto, wave_row, block_onepass, two_pass, splitk_ordered");
+        kernel_id != RWS_KERNEL_SPLITK_ORDERED && kernel_id != RWS_KERNEL_TILE_ROWS)
+        return fail(RWS_ERR_INVALID_ARG, "normalisation kernels: auto, wave_row, block_onepass, "
+                                         "two_pass, splitk_ordered, tile_rows");
     if (!(eps >= 0.0f) || !std::isfinite(eps))
         return fail(RWS_ERR_INVALID_ARG, "eps must be finite and >= 0");
     int st = check_args(in, out, rows, cols, dtype, RWS_KERNEL_AUTO);
@@ -1577,7 +1613,9 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
         L.args.n = (float)cols;
         L.stream = (hipStream_t)stream;
         hipError_t e = hipSuccess;
-        if (family == 1)
+        if (family == RWS_KERNEL_TILE_ROWS)
+            e = rws::launch_norm_tile(L, variant);
+        else if (family == 1)
             e = rws::launch_norm_wave(L, variant);
         else if (family != RWS_KERNEL_SPLITK_ORDERED)
             e = rws::launch_norm_block(L, family, variant);
@@ -1774,9 +1812,9 @@ int softmax_bwd_describe_launch(int64_t rows, int64_t cols, int dtype, const voi
     buf[0] = 0;
     if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
         kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS &&
-        kernel_id != RWS_KERNEL_SPLITK_ORDERED)
-        return fail(RWS_ERR_INVALID_ARG,
-                    "backward kernels: auto, wave_row, block_onepass, two_pass, splitk_ordered");
+        kernel_id != RWS_KERNEL_SPLITK_ORDERED && kernel_id != RWS_KERNEL_TILE_ROWS)
+        return fail(RWS_ERR_INVALID_ARG, "backward kernels: auto, wave_row, block_onepass, "
+                                         "two_pass, splitk_ordered, tile_rows");
     if (dtype != RWS_F32 && dtype != RWS_F16 && dtype != RWS_BF16)
         return fail(RWS_ERR_UNSUPPORTED_DTYPE, "dtype must be RWS_F32, RWS_F16 or RWS_BF16");
     if (rows < 0 || cols < 0) return fail(RWS_ERR_INVALID_ARG, "rows and cols must be >= 0");
@@ -1785,12 +1823,17 @@ int softmax_bwd_describe_launch(int64_t rows, int64_t cols, int dtype, const voi
         std::snprintf(buf, (size_t)buflen, "empty: no launch");
         return RWS_OK;
     }
+    // dy is taken to share y's 16-byte alignment
     BwdPlan bp;
-    const int st = plan_bwd(rows, cols, dtype, y, dx, kernel_id, &bp);
+    const int st = plan_bwd(rows, cols, dtype, y, dx, (uintptr_t)y % 16 == 0, kernel_id, &bp);
     if (st != RWS_OK) return st;
     const char* al = bp.aligned ? "aligned" : (bp.same_phase ? "unaligned" : "unaligned,split-phase");
     const int64_t r = std::min(rows, bp.max_rows);
-    if (bp.family == RWS_KERNEL_SPLITK_ORDERED) {
+    if (bp.family == RWS_KERNEL_TILE_ROWS) {
+        const rws::TileRowsVariant& v = rws::kTileRows[bp.variant];
+        std::snprintf(buf, (size_t)buflen, "bwd_tile<%s,T=%d,K=%d> grid=%lld block=64",
+                      dtype_name(dtype), v.T, v.K, (long long)((r + v.T - 1) / v.T));
+    } else if (bp.family == RWS_KERNEL_SPLITK_ORDERED) {
         std::snprintf(buf, (size_t)buflen,
                       "bwd_ordered<%s,%s,B=%d,KC=%d> P=%d grid=%lld (2 stages) block=%d",
                       dtype_name(dtype), al, rws::kBwdOrderedBlock, rws::kBwdOrderedKc, bp.P,
@@ -1819,9 +1862,9 @@ int norm_describe_launch(int64_t rows, int64_t cols, int dtype, const void* in, 
     buf[0] = 0;
     if (kernel_id != RWS_KERNEL_AUTO && kernel_id != RWS_KERNEL_WAVE_ROW &&
         kernel_id != RWS_KERNEL_BLOCK_ONEPASS && kernel_id != RWS_KERNEL_TWO_PASS &&
-        kernel_id != RWS_KERNEL_SPLITK_ORDERED)
-        return fail(RWS_ERR_INVALID_ARG,
-                    "normalisation kernels: auto, wave_row, block_onepass, two_pass, splitk_ordered");
+        kernel_id != RWS_KERNEL_SPLITK_ORDERED && kernel_id != RWS_KERNEL_TILE_ROWS)
+        return fail(RWS_ERR_INVALID_ARG, "normalisation kernels: auto, wave_row, block_onepass, "
+                                         "two_pass, splitk_ordered, tile_rows");
     if (dtype != RWS_F32 && dtype != RWS_F16 && dtype != RWS_BF16)
         return fail(RWS_ERR_UNSUPPORTED_DTYPE, "dtype must be RWS_F32, RWS_F16 or RWS_BF16");
     if (rows < 0 || cols < 0) return fail(RWS_ERR_INVALID_ARG, "rows and cols must be >= 0");
@@ -1836,7 +1879,11 @@ int norm_describe_launch(int64_t rows, int64_t cols, int dtype, const void* in, 
     const char* al = np.aligned ? "aligned" : (np.same_phase ? "unaligned" : "unaligned,split-phase");
     const int64_t r = std::min(rows, np.max_rows);
     const long long wline = (long long)window_granules(geometry(cols, dtype, in, out), 128);
-    if (np.family == RWS_KERNEL_SPLITK_ORDERED) {
+    if (np.family == RWS_KERNEL_TILE_ROWS) {
+        const rws::TileRowsVariant& v = rws::kTileRows[np.variant];
+        std::snprintf(buf, (size_t)buflen, "norm_tile<%s,T=%d,K=%d> grid=%lld block=64",
+                      dtype_name(dtype), v.T, v.K, (long long)((r + v.T - 1) / v.T));
+    } else if (np.family == RWS_KERNEL_SPLITK_ORDERED) {
         std::snprintf(buf, (size_t)buflen,
                       "norm_ordered<%s,%s,B=%d,KC=%d> P=%d grid=%lld (2 stages) block=%d",
                       dtype_name(dtype), al, rws::kNormOrderedBlock, rws::kNormOrderedKc, np.P,

@@ -149,6 +149,9 @@ struct BwdLaunch {
     int lgrun = 0;    // bwd_block / bwd_stream: XCD runs of 2^lgrun rows
     hipStream_t stream;
 };
+// tile_rows form of the backward (kTileRows variants): y, dy and dx
+// 16-byte aligned, as launch_tile_rows.
+hipError_t launch_bwd_tile(const BwdLaunch& B, int variant);
 extern const WaveRowVariant kBwdWave[];
 extern const int kNumBwdWave;
 extern const TwoPassVariant kBwdBlock[];  // (threads, register granules per thread)
@@ -187,6 +190,9 @@ struct NormLaunch {
     int lgrun = 0;    // norm_block / norm_stream: XCD runs of 2^lgrun rows
     hipStream_t stream;
 };
+// tile_rows form of the normalisations without weight and bias
+// (kTileRows variants): in and out 16-byte aligned, as launch_tile_rows.
+hipError_t launch_norm_tile(const NormLaunch& N, int variant);
 extern const WaveRowVariant kNormWave[];
 extern const int kNumNormWave;
 extern const TwoPassVariant kNormBlock[];   // (threads, register granules per thread)

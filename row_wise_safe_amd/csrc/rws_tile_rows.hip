@@ -1,183 +1,102 @@
-// rws_tile_rows.hip -- short rows that do not start on a 16-byte boundary,
-// several rows per wave taken as one aligned range.
+// rws_tile_rows.hip -- the tile_rows forms (rws_tile.hpp): several short rows
+// per wave as one 16-byte-aligned range, for rows that are not line-aligned.
 //
-// A row of cols elements whose byte length is not a multiple of 16 starts
-// at a different 16-byte phase from its neighbours, so a per-row window
-// (wave_row) has a partial granule at each end: both neighbouring rows load
-// it, and each stores its own bytes of it with 2-, 4- or 8-byte stores.  For
-// short rows those ends are a large share of the traffic.  But the phase
-// repeats: P0 = 16 / gcd(cols * size, 16) consecutive rows (at most 8 for
-// 16-bit types, 4 for fp32) span a whole number of granules, so a tile of T
-// rows (T a multiple of P0) starts and ends on a 16-byte boundary whenever
-// the tensor does.  One wave takes one tile: lane l holds the tile's
-// granules l, l + 64, ... (coalesced 128-bit loads and stores, every granule
-// read and written once and whole).  A granule holds elements of at most two
-// rows (cols >= elements per granule), so each lane keeps two partial
-// results per granule -- one for the row its first element belongs to, one
-// for the next row -- and the row reductions go through LDS: after the
-// partials are written, GL = 64 / T lanes per row fold the granules of their
-// row (the first one takes its "next row" partial when the row starts inside
-// it), a DPP reduction over the GL lanes finishes the row, and one lane
-// publishes the row's result.  Max first, then the exponentials against each
-// element's row maximum and the same fold for the sums, then the scaling:
-// the row-wise definition (CUDA safe-online-softmax page, section 1), with
-// the reductions segmented by row.
-#include "rws_kernels.hpp"
+//   softmax     row max, then the exponentials against each element's row
+//               maximum and their row sum, then the scaling -- the row-wise
+//               definition (CUDA safe-online-softmax page, section 1) with
+//               the reductions segmented by row
+//   backward    dot = sum_j dy_j * y_j per row, dx_j = y_j * (dy_j - dot)
+//   LayerNorm   mean, then the sum of squared deviations from it (the
+//               two-pass form the other normalisation kernels use)
+//   RMSNorm     mean square; no weight or bias here (those rows take the
+//               other forms)
 #include "rws_launch.hpp"
+#include "rws_norm.hpp"
+#include "rws_tile.hpp"
 
 namespace rws {
 
-// q = floor(x / d) for 32-bit x and d >= 2, with M = remainder_magic(d):
-// the high 64 bits of M * x (the direct division of Lemire, Kaser and Kurz,
-// exact for every 32-bit x).
-__device__ inline uint32_t tile_div(uint32_t x, uint64_t M) {
-    const uint64_t lo = (uint64_t)(uint32_t)M * x;
-    const uint64_t hi = (uint64_t)(uint32_t)(M >> 32) * x;
-    return (uint32_t)((hi + (lo >> 32)) >> 32);
-}
-
-// One tile.  FULL: T whole rows (every tile but possibly the last), so the
-// tile is a whole number of granules; else the tensor's last, partial tile,
-// whose last granule may stop inside (element access there).
+// ---------------------------------------------------------------------------
+// softmax
+// ---------------------------------------------------------------------------
 template <int DT, int T, int K, bool FULL>
-__device__ inline void tile_rows_body(const char* __restrict__ gin, char* __restrict__ gout,
-                                      int nrows, int cols, uint64_t cmagic, float* part_a,
-                                      float* part_b, float* row_max, float* row_rcp) {
+__device__ inline void tile_softmax(const char* __restrict__ gin, char* __restrict__ gout,
+                                    int nrows, int cols, uint64_t cmagic, float* part_a,
+                                    float* part_b, float* row_max, float* row_rcp) {
     constexpr int VEC = Elem<DT>::VEC;
-    constexpr int ES = Elem<DT>::SIZE;
-    constexpr int GL = 64 / T;  // lanes per row in the row folds
-    const int lane = threadIdx.x;
-    const int nel = nrows * cols;  // elements of this tile
-
-    // load: whole granules; element by element only where the tensor ends
+    const TileSlots<DT, T, K> S(nrows, cols, cmagic);
     u32x4 raw[K];
-    int ra[K];     // tile row of the granule's first element
-    int split[K];  // elements of the granule in that row (>= VEC: all)
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-        const int j = lane + 64 * i;
-        const int x = j * VEC;
-        raw[i] = u32x4{0u, 0u, 0u, 0u};
-        if (x + VEC <= nel) {
-            raw[i] = load16<true>(gin + (int64_t)j * 16);
-        } else if (!FULL && x < nel) {
-            float f[VEC];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                f[e] = x + e < nel ? Elem<DT>::load1(gin + (int64_t)(x + e) * ES) : 0.0f;
-            raw[i] = Elem<DT>::narrow(f);
-        }
-        const int q = (int)tile_div((uint32_t)x, cmagic);
-        ra[i] = q < T - 1 ? q : T - 1;  // slots past the tile: clamped, never used
-        split[i] = (q + 1) * cols - x;
-    }
+    for (int i = 0; i < K; ++i) raw[i] = tile_load<DT, FULL>(gin, S.granule(i), S.nel);
 
     // widen; slots past the tile are -inf (they belong to no row)
     float v[K][VEC];
 #pragma unroll
     for (int i = 0; i < K; ++i) {
         Elem<DT>::widen(raw[i], v[i]);
-        const int x = (lane + 64 * i) * VEC;
-        if (x + VEC > nel) {
+        const int x = S.granule(i) * VEC;
+        if (x + VEC > S.nel) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) v[i][e] = x + e < nel ? v[i][e] : kNegInf;
+            for (int e = 0; e < VEC; ++e) v[i][e] = x + e < S.nel ? v[i][e] : kNegInf;
         }
     }
 
-    // the GL lanes of row r fold the partials of r's granules; the first
-    // granule contributes its "next row" part when r starts inside it
-    const int r = lane / GL;
-    const int t = lane & (GL - 1);
-    const int j0 = (r * cols) / VEC;
-    const int j1 = ((r + 1) * cols - 1) / VEC;
-    const bool first_in_b = j0 * VEC < r * cols;
-    const bool live = FULL || r < nrows;
-
-    // row maxima: each granule's maximum over its first row's elements (a)
-    // and over the next row's (b)
+    // row maxima
+    float pa[K], pb[K];
 #pragma unroll
     for (int i = 0; i < K; ++i) {
-        float ma = kNegInf, mb = kNegInf;
+        pa[i] = kNegInf;
+        pb[i] = kNegInf;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-            const bool in_a = e < split[i];
-            ma = vmax(ma, in_a ? v[i][e] : kNegInf);
-            mb = vmax(mb, in_a ? kNegInf : v[i][e]);
+            const bool in_a = S.in_a(i, e);
+            pa[i] = vmax(pa[i], in_a ? v[i][e] : kNegInf);
+            pb[i] = vmax(pb[i], in_a ? kNegInf : v[i][e]);
         }
-        part_a[lane + 64 * i] = ma;
-        part_b[lane + 64 * i] = mb;
     }
-    __syncthreads();
-    {
-        float m = kNegInf;
-        if (live)
-            for (int j = j0 + t; j <= j1; j += GL)
-                m = vmax(m, (j == j0 && first_in_b) ? part_b[j] : part_a[j]);
-        m = group_reduce<GL, OpMax>(m);
-        if (t == 0) row_max[r] = live ? m : 0.0f;
-    }
-    __syncthreads();
+    tile_fold<T, K, OpMax>(pa, pb, part_a, part_b, row_max, cols, nrows, VEC, kNegInf,
+                           [](float m) { return m; });
 
-    // exponentials against each element's row maximum (one exp2 per
-    // element: the FMA offset of the element's row is selected first; rows
-    // whose maximum takes the exact form -- |max| above 2.9e6 or +inf --
-    // take it for the whole granule), row sums
+    // exponentials against each element's row maximum (one exp2 per element:
+    // the FMA offset of the element's row is selected first; a granule with
+    // a row whose maximum takes the exact form -- |max| above 2.9e6 or
+    // +inf -- takes it per element), row sums
 #pragma unroll
     for (int i = 0; i < K; ++i) {
-        const int rb = ra[i] + 1 < T ? ra[i] + 1 : T - 1;  // next row (unused past the tile)
-        const RowExp ea(row_max[ra[i]]), eb(row_max[rb]);
-        float sa = 0.0f, sb = 0.0f;
+        const RowExp ea(row_max[S.ra[i]]), eb(row_max[S.rb(i)]);
+        pa[i] = 0.0f;
+        pb[i] = 0.0f;
         if (__builtin_expect(ea.big || eb.big, 0)) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const bool in_a = e < split[i];
+                const bool in_a = S.in_a(i, e);
                 const float y = in_a ? ea.one(v[i][e]) : eb.one(v[i][e]);
                 v[i][e] = y;
-                sa += in_a ? y : 0.0f;
-                sb += in_a ? 0.0f : y;
+                pa[i] += in_a ? y : 0.0f;
+                pb[i] += in_a ? 0.0f : y;
             }
         } else {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const bool in_a = e < split[i];
-                const float y =
-                    __builtin_amdgcn_exp2f(__builtin_fmaf(v[i][e], kLog2e, in_a ? ea.negc : eb.negc));
+                const bool in_a = S.in_a(i, e);
+                const float y = __builtin_amdgcn_exp2f(
+                    __builtin_fmaf(v[i][e], kLog2e, in_a ? ea.negc : eb.negc));
                 v[i][e] = y;
-                sa += in_a ? y : 0.0f;
-                sb += in_a ? 0.0f : y;
+                pa[i] += in_a ? y : 0.0f;
+                pb[i] += in_a ? 0.0f : y;
             }
         }
-        part_a[lane + 64 * i] = sa;
-        part_b[lane + 64 * i] = sb;
     }
-    __syncthreads();
-    {
-        float s = 0.0f;
-        if (live)
-            for (int j = j0 + t; j <= j1; j += GL)
-                s += (j == j0 && first_in_b) ? part_b[j] : part_a[j];
-        s = group_reduce<GL, OpSum>(s);
-        if (t == 0) row_rcp[r] = live ? __builtin_amdgcn_rcpf(s) : 0.0f;
-    }
-    __syncthreads();
+    tile_fold<T, K, OpSum>(pa, pb, part_a, part_b, row_rcp, cols, nrows, VEC, 0.0f,
+                           [](float s) { return __builtin_amdgcn_rcpf(s); });
 
-    // scale and store: whole granules; element by element where the tensor ends
+    // scale and store
 #pragma unroll
     for (int i = 0; i < K; ++i) {
-        const int j = lane + 64 * i;
-        const int x = j * VEC;
-        if (x >= nel) continue;
-        const int rb = ra[i] + 1 < T ? ra[i] + 1 : T - 1;
-        const float qa = row_rcp[ra[i]], qb = row_rcp[rb];
+        const float qa = row_rcp[S.ra[i]], qb = row_rcp[S.rb(i)];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) v[i][e] *= e < split[i] ? qa : qb;
-        if (x + VEC <= nel) {
-            __builtin_nontemporal_store(Elem<DT>::narrow(v[i]), (u32x4*)(gout + (int64_t)j * 16));
-        } else if (!FULL) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                if (x + e < nel) Elem<DT>::store1(gout + (int64_t)(x + e) * ES, v[i][e]);
-        }
+        for (int e = 0; e < VEC; ++e) v[i][e] *= S.in_a(i, e) ? qa : qb;
+        tile_store<DT, FULL>(gout, S.granule(i), S.nel, v[i]);
     }
 }
 
@@ -190,15 +109,188 @@ __global__ __launch_bounds__(64) void k_tile_rows(const void* __restrict__ in,
     __shared__ float row_max[T];
     __shared__ float row_rcp[T];
     const int64_t row0 = (int64_t)blockIdx.x * T;
-    const char* gin = (const char*)in + row0 * cols * Elem<DT>::SIZE;
-    char* gout = (char*)out + row0 * cols * Elem<DT>::SIZE;
+    const int64_t off = row0 * cols * Elem<DT>::SIZE;
+    const char* gin = (const char*)in + off;
+    char* gout = (char*)out + off;
     if (rows - row0 >= T)
-        tile_rows_body<DT, T, K, true>(gin, gout, T, cols, cmagic, part_a, part_b, row_max, row_rcp);
+        tile_softmax<DT, T, K, true>(gin, gout, T, cols, cmagic, part_a, part_b, row_max, row_rcp);
     else
-        tile_rows_body<DT, T, K, false>(gin, gout, (int)(rows - row0), cols, cmagic, part_a, part_b,
-                                        row_max, row_rcp);
+        tile_softmax<DT, T, K, false>(gin, gout, (int)(rows - row0), cols, cmagic, part_a, part_b,
+                                      row_max, row_rcp);
 }
 
+// ---------------------------------------------------------------------------
+// softmax backward
+// ---------------------------------------------------------------------------
+template <int DT, int T, int K, bool FULL>
+__device__ inline void tile_backward(const char* __restrict__ gy, const char* __restrict__ gdy,
+                                     char* __restrict__ gdx, int nrows, int cols, uint64_t cmagic,
+                                     float* part_a, float* part_b, float* row_dot) {
+    constexpr int VEC = Elem<DT>::VEC;
+    const TileSlots<DT, T, K> S(nrows, cols, cmagic);
+    u32x4 ry[K], rdy[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        ry[i] = tile_load<DT, FULL>(gy, S.granule(i), S.nel);
+        rdy[i] = tile_load<DT, FULL>(gdy, S.granule(i), S.nel);
+    }
+    // slots past the tile load as 0 and add nothing
+    float y[K][VEC], d[K][VEC];
+    float pa[K], pb[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        Elem<DT>::widen(ry[i], y[i]);
+        Elem<DT>::widen(rdy[i], d[i]);
+        pa[i] = 0.0f;
+        pb[i] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float p = y[i][e] * d[i][e];
+            const bool in_a = S.in_a(i, e);
+            pa[i] += in_a ? p : 0.0f;
+            pb[i] += in_a ? 0.0f : p;
+        }
+    }
+    tile_fold<T, K, OpSum>(pa, pb, part_a, part_b, row_dot, cols, nrows, VEC, 0.0f,
+                           [](float s) { return s; });
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        const float sa = row_dot[S.ra[i]], sb = row_dot[S.rb(i)];
+        float o[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = y[i][e] * (d[i][e] - (S.in_a(i, e) ? sa : sb));
+        tile_store<DT, FULL>(gdx, S.granule(i), S.nel, o);
+    }
+}
+
+template <int DT, int T, int K>
+__global__ __launch_bounds__(64) void k_bwd_tile(const void* __restrict__ y,
+                                                 const void* __restrict__ dy,
+                                                 void* __restrict__ dx, int64_t rows, int cols,
+                                                 uint64_t cmagic) {
+    __shared__ float part_a[64 * K];
+    __shared__ float part_b[64 * K];
+    __shared__ float row_dot[T];
+    const int64_t row0 = (int64_t)blockIdx.x * T;
+    const int64_t off = row0 * cols * Elem<DT>::SIZE;
+    const char* gy = (const char*)y + off;
+    const char* gdy = (const char*)dy + off;
+    char* gdx = (char*)dx + off;
+    if (rows - row0 >= T)
+        tile_backward<DT, T, K, true>(gy, gdy, gdx, T, cols, cmagic, part_a, part_b, row_dot);
+    else
+        tile_backward<DT, T, K, false>(gy, gdy, gdx, (int)(rows - row0), cols, cmagic, part_a,
+                                       part_b, row_dot);
+}
+
+// ---------------------------------------------------------------------------
+// LayerNorm / RMSNorm without weight and bias
+// ---------------------------------------------------------------------------
+template <int DT, int T, int K, int MODE, bool FULL>
+__device__ inline void tile_norm(const char* __restrict__ gin, char* __restrict__ gout, int nrows,
+                                 int cols, uint64_t cmagic, const NormArgs& A, int64_t row0,
+                                 float* part_a, float* part_b, float* row_mu, float* row_rstd) {
+    constexpr int VEC = Elem<DT>::VEC;
+    const TileSlots<DT, T, K> S(nrows, cols, cmagic);
+    u32x4 raw[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) raw[i] = tile_load<DT, FULL>(gin, S.granule(i), S.nel);
+    // slots past the tile load as 0; their partials are never folded into a row
+    float v[K][VEC];
+    float pa[K], pb[K];
+    if (MODE == kLayerNorm) {
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            Elem<DT>::widen(raw[i], v[i]);
+            pa[i] = 0.0f;
+            pb[i] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const bool in_a = S.in_a(i, e);
+                pa[i] += in_a ? v[i][e] : 0.0f;
+                pb[i] += in_a ? 0.0f : v[i][e];
+            }
+        }
+        const float n = A.n;
+        tile_fold<T, K, OpSum>(pa, pb, part_a, part_b, row_mu, cols, nrows, VEC, 0.0f,
+                               [n](float s) { return s / n; });
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            const float ma = row_mu[S.ra[i]], mb = row_mu[S.rb(i)];
+            pa[i] = 0.0f;
+            pb[i] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const bool in_a = S.in_a(i, e);
+                const float c = v[i][e] - (in_a ? ma : mb);
+                pa[i] = in_a ? __builtin_fmaf(c, c, pa[i]) : pa[i];
+                pb[i] = in_a ? pb[i] : __builtin_fmaf(c, c, pb[i]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            Elem<DT>::widen(raw[i], v[i]);
+            pa[i] = 0.0f;
+            pb[i] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const bool in_a = S.in_a(i, e);
+                pa[i] = in_a ? __builtin_fmaf(v[i][e], v[i][e], pa[i]) : pa[i];
+                pb[i] = in_a ? pb[i] : __builtin_fmaf(v[i][e], v[i][e], pb[i]);
+            }
+        }
+    }
+    const NormArgs Ac = A;
+    tile_fold<T, K, OpSum>(pa, pb, part_a, part_b, row_rstd, cols, nrows, VEC, 0.0f,
+                           [Ac](float q) { return norm_rstd(q, Ac); });
+    const int lane = threadIdx.x;
+    if (lane < nrows) {
+        if (MODE == kLayerNorm && A.mean) A.mean[row0 + lane] = row_mu[lane];
+        if (A.rstd) A.rstd[row0 + lane] = row_rstd[lane];
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        const float ra = row_rstd[S.ra[i]], rb = row_rstd[S.rb(i)];
+        float o[VEC];
+        if (MODE == kLayerNorm) {
+            const float ma = row_mu[S.ra[i]], mb = row_mu[S.rb(i)];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const bool in_a = S.in_a(i, e);
+                o[e] = (v[i][e] - (in_a ? ma : mb)) * (in_a ? ra : rb);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) o[e] = v[i][e] * (S.in_a(i, e) ? ra : rb);
+        }
+        tile_store<DT, FULL>(gout, S.granule(i), S.nel, o);
+    }
+}
+
+template <int DT, int T, int K, int MODE>
+__global__ __launch_bounds__(64) void k_norm_tile(const void* __restrict__ in,
+                                                  void* __restrict__ out, int64_t rows, int cols,
+                                                  uint64_t cmagic, NormArgs A) {
+    __shared__ float part_a[64 * K];
+    __shared__ float part_b[64 * K];
+    __shared__ float row_mu[T];
+    __shared__ float row_rstd[T];
+    const int64_t row0 = (int64_t)blockIdx.x * T;
+    const int64_t off = row0 * cols * Elem<DT>::SIZE;
+    const char* gin = (const char*)in + off;
+    char* gout = (char*)out + off;
+    if (rows - row0 >= T)
+        tile_norm<DT, T, K, MODE, true>(gin, gout, T, cols, cmagic, A, row0, part_a, part_b, row_mu,
+                                        row_rstd);
+    else
+        tile_norm<DT, T, K, MODE, false>(gin, gout, (int)(rows - row0), cols, cmagic, A, row0,
+                                         part_a, part_b, row_mu, row_rstd);
+}
+
+// ---------------------------------------------------------------------------
+// variants and launchers
+// ---------------------------------------------------------------------------
 // (rows per tile, granules per lane)
 #define RWS_TILE_ROWS_VARIANTS(X) \
     X(4, 1) X(4, 2) X(4, 4)       \
@@ -218,6 +310,27 @@ static hipError_t go(const Launch& L) {
     return hipGetLastError();
 }
 
+template <int DT, int T, int K>
+static hipError_t go_bwd(const BwdLaunch& B) {
+    const int64_t tiles = (B.rows + T - 1) / T;
+    hipLaunchKernelGGL((k_bwd_tile<DT, T, K>), dim3((unsigned)tiles), dim3(64), 0, B.stream, B.y,
+                       B.dy, B.dx, B.rows, B.cols, remainder_magic((uint64_t)B.cols));
+    return hipGetLastError();
+}
+
+template <int DT, int T, int K>
+static hipError_t go_norm(const NormLaunch& N) {
+    const int64_t tiles = (N.rows + T - 1) / T;
+    const uint64_t M = remainder_magic((uint64_t)N.cols);
+    if (N.mode == kLayerNorm)
+        hipLaunchKernelGGL((k_norm_tile<DT, T, K, kLayerNorm>), dim3((unsigned)tiles), dim3(64), 0,
+                           N.stream, N.in, N.out, N.rows, N.cols, M, N.args);
+    else
+        hipLaunchKernelGGL((k_norm_tile<DT, T, K, kRmsNorm>), dim3((unsigned)tiles), dim3(64), 0,
+                           N.stream, N.in, N.out, N.rows, N.cols, M, N.args);
+    return hipGetLastError();
+}
+
 template <int T, int K>
 static hipError_t go_any(const Launch& L) {
     switch (L.dtype) {
@@ -228,10 +341,50 @@ static hipError_t go_any(const Launch& L) {
     return hipErrorInvalidValue;
 }
 
+template <int T, int K>
+static hipError_t go_bwd_any(const BwdLaunch& B) {
+    switch (B.dtype) {
+        case kF32: return go_bwd<kF32, T, K>(B);
+        case kF16: return go_bwd<kF16, T, K>(B);
+        case kBF16: return go_bwd<kBF16, T, K>(B);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int T, int K>
+static hipError_t go_norm_any(const NormLaunch& N) {
+    switch (N.dtype) {
+        case kF32: return go_norm<kF32, T, K>(N);
+        case kF16: return go_norm<kF16, T, K>(N);
+        case kBF16: return go_norm<kBF16, T, K>(N);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_tile_rows(const Launch& L, int variant) {
     int i = 0;
 #define RWS_CASE(t, k) \
     if (variant == i) return go_any<t, k>(L); \
+    ++i;
+    RWS_TILE_ROWS_VARIANTS(RWS_CASE)
+#undef RWS_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_tile(const BwdLaunch& B, int variant) {
+    int i = 0;
+#define RWS_CASE(t, k) \
+    if (variant == i) return go_bwd_any<t, k>(B); \
+    ++i;
+    RWS_TILE_ROWS_VARIANTS(RWS_CASE)
+#undef RWS_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_norm_tile(const NormLaunch& N, int variant) {
+    int i = 0;
+#define RWS_CASE(t, k) \
+    if (variant == i) return go_norm_any<t, k>(N); \
     ++i;
     RWS_TILE_ROWS_VARIANTS(RWS_CASE)
 #undef RWS_CASE

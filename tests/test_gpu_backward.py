@@ -111,3 +111,45 @@ def test_backward_rejects_split_kernels():
         st = rws.softmax_bwd_kernel(y.data_ptr(), y.data_ptr(), y.data_ptr(), 2, 64, rws.RWS_F16,
                                     0, rws.KERNEL_IDS[kernel])
         assert st == rws.RWS_ERR_INVALID_ARG
+
+
+# --------------------------------------------------------------------------
+# tile_rows: several short rows per wave as one 16-byte-aligned range
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("cols", [9, 33, 100, 250, 333, 500, 1001])
+def test_tile_rows_form(dtype, cols):
+    from gpu_util import tile_supports
+    if not tile_supports(cols, dtype):
+        pytest.skip("outside the tile rows")
+    es = 4 if dtype == "f32" else 2
+    for rows in (64, 67, 777):
+        y, ys, dy, gs = _inputs(rows, cols, dtype, seed=cols * 13 + rows)
+        dx = empty_like_at(y)
+        desc = rws.softmax_bwd_describe_launch(rows, cols, rws.dtype_code(y.dtype), y.data_ptr(),
+                                               dx.data_ptr())
+        rb = cols * es
+        if rb <= 2048 and rb % 128 and (rb % 16 or rb > 128):
+            assert desc.startswith("bwd_tile<"), desc
+        for kernel in ("auto", "tile_rows"):
+            _run(y, dy, dx, kernel)
+            torch.cuda.synchronize()
+            _check(dx.double().cpu().numpy(), ys, gs, dtype, f"{kernel} {desc} rows={rows}")
+
+
+def test_tile_rows_form_in_place_and_refusals():
+    rows, cols = 70, 77
+    y, ys, dy, gs = _inputs(rows, cols, "f16", seed=5)
+    _run(y, dy, dy, "tile_rows")  # dx aliases dy
+    torch.cuda.synchronize()
+    _check(dy.double().cpu().numpy(), ys, gs, "f16", "tile_rows in place")
+    # dy that is not 16-byte aligned: refused by the tile form, another form for auto
+    y2, ys2, dy2, gs2 = _inputs(rows, cols, "f16", seed=6, offs=(0, 1))
+    dx2 = empty_like_at(y2)
+    st = rws.softmax_bwd_kernel(y2.data_ptr(), dy2.data_ptr(), dx2.data_ptr(), rows, cols,
+                                rws.RWS_F16, torch.cuda.current_stream().cuda_stream,
+                                rws.KERNEL_IDS["tile_rows"])
+    assert st == rws.RWS_ERR_UNSUPPORTED_SHAPE
+    _run(y2, dy2, dx2, "auto")
+    torch.cuda.synchronize()
+    _check(dx2.double().cpu().numpy(), ys2, gs2, "f16", "auto, dy unaligned")

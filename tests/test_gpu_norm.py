@@ -292,3 +292,52 @@ def test_norm_deterministic():
     b = rws.layer_norm(x)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# tile_rows: several short rows per wave as one 16-byte-aligned range (no
+# weight or bias)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("cols", [9, 33, 100, 250, 333, 500, 1001])
+def test_tile_rows_form(mode, dtype, cols):
+    from gpu_util import tile_supports
+    if not tile_supports(cols, dtype):
+        pytest.skip("outside the tile rows")
+    es = 4 if dtype == "f32" else 2
+    for rows in (64, 67, 777):
+        g = np.random.Generator(np.random.PCG64(cols * 17 + rows))
+        x, xs = to_device(g.normal(0.5, 2.0, (rows, cols)), dtype)
+        out = empty_like_at(x)
+        mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+        rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+        desc = rws.norm_describe_launch(rows, cols, rws.dtype_code(x.dtype), x.data_ptr(),
+                                        out.data_ptr())
+        rb = cols * es
+        if rb <= 2048 and rb % 128 and (rb % 16 or rb > 128):
+            assert desc.startswith("norm_tile<"), desc
+        for kernel in ("auto", "tile_rows"):
+            _call(mode, x, out, 1e-5, None, None, mean, rstd, kernel)
+            _check(mode, dtype, out.double().cpu().numpy(), xs, 1e-5, None, None,
+                   f"{mode} {kernel} {desc} rows={rows}",
+                   mean=mean.double().cpu().numpy() if mode == "layernorm" else None,
+                   rstd=rstd.double().cpu().numpy())
+
+
+def test_tile_rows_form_affine_and_constant_rows():
+    rows, cols = 66, 100
+    g = np.random.Generator(np.random.PCG64(9))
+    x, xs = to_device(g.normal(0.0, 1.0, (rows, cols)), "f16")
+    w, ws = to_device(g.uniform(0.5, 1.5, (1, cols)), "f16")
+    # with a weight the dispatcher keeps the lane groups; the tile form refuses it
+    desc = rws.norm_describe_launch(rows, cols, rws.RWS_F16, x.data_ptr(), x.data_ptr(),
+                                    affine=True)
+    assert not desc.startswith("norm_tile<"), desc
+    with pytest.raises(rws.SoftmaxError):
+        rws.layer_norm(x, 1e-5, w.view(cols), None, kernel="tile_rows")
+    # constant rows normalise to exact zeros
+    c, cs = to_device(np.full((rows, cols), 3.25), "f16")
+    y = rws.layer_norm(c, 1e-5, kernel="tile_rows")
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
