@@ -55,11 +55,13 @@ KERNEL_SOURCES = {
     "splitk": _SOFTMAX_COMMON + ["rws_splitk.hip"],
     "splitk_fused": _SOFTMAX_COMMON + ["rws_ordered.hpp", "rws_splitk_fused.hip"],
     "splitk_ordered": _SOFTMAX_COMMON + ["rws_ordered.hpp", "rws_splitk_ordered.hip"],
-    "tile_rows": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_tile_rows.hip"],
+    "tile_rows": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_tile.hpp", "rws_tile_rows.hip"],
     "masked": _SOFTMAX_COMMON + ["rws_masked.hip"],
-    "backward": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_ordered.hpp", "rws_backward.hip"],
+    "backward": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_ordered.hpp", "rws_backward.hip",
+                                   "rws_tile.hpp", "rws_tile_rows.hip"],
     "layernorm": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_ordered.hpp", "rws_norm.hpp",
-                                    "rws_norm_wave.hip", "rws_norm_block.hip"],
+                                    "rws_norm_wave.hip", "rws_norm_block.hip", "rws_tile.hpp",
+                                    "rws_tile_rows.hip"],
 }
 KERNEL_SOURCES["rmsnorm"] = KERNEL_SOURCES["layernorm"]
 # Substring that names the step's kernels in a trace.

@@ -152,19 +152,21 @@ enum {
                                  dispatcher's choice for few long rows of up
                                  to 32 MiB together and 512 chunks each */
     RWS_KERNEL_TILE_ROWS = 7     /* short rows that are not line-aligned:
-                                 one wave takes 4, 8 or 16 consecutive rows
-                                 as one 16-byte-aligned range (every granule
-                                 read and written whole by one lane, a row
-                                 may start and end inside a granule) and
-                                 reduces each row across the lanes that hold
-                                 it, through LDS (the row-wise definition,
-                                 CUDA safe-online-softmax page, section 1).
-                                 Needs in and out 16-byte aligned, rows of at
-                                 least one granule, and a tile of at most
-                                 4096 bytes (RWS_ERR_UNSUPPORTED_SHAPE
+                                 one wave takes 4 to 64 consecutive rows
+                                 (as many as fill its 64*K granule slots,
+                                 K = 1..4 the variant) as one 16-byte-aligned
+                                 range (every granule read and written whole
+                                 by one lane, a row may start and end inside
+                                 a granule) and reduces each row across the
+                                 lanes that hold it, through LDS (the
+                                 row-wise definition, CUDA
+                                 safe-online-softmax page, section 1).  Needs
+                                 in and out 16-byte aligned, rows of one
+                                 granule to 1024 bytes, and a tile of at
+                                 least 4 rows (RWS_ERR_UNSUPPORTED_SHAPE
                                  otherwise).  The dispatcher's choice for
-                                 many such rows of up to 2048 bytes (plain
-                                 softmax; the masked form has none) */
+                                 many such rows (plain softmax; the masked
+                                 form has none) */
 };
 
 /*

@@ -94,7 +94,8 @@ struct Plan {
     bool aligned = false;
     bool same_phase = false;
     bool wt = false;  // write-through 128-bit stores (line-aligned wave_row)
-    int lgrun = 0;    // XCD runs of 2^lgrun rows (workgroup-per-row kernels)
+    int lgrun = 0;    // XCD runs of 2^lgrun rows (workgroup-per-row kernels) or tiles
+    int tile_t = 0;   // tile_rows: rows per tile
 };
 
 // Alignment facts of one call.
@@ -131,52 +132,80 @@ int softmax_wave_wa(const rws::WaveRowVariant& v) { return rws::softmax_window_a
 // The dispatcher's rows for tile_rows: plain softmax over many rows of at
 // most kTileMaxRowBytes that are not line-aligned -- with partial granules at
 // their ends (byte length not a multiple of 16), or 16-byte multiples above
-// 128 bytes -- in and out 16-byte aligned, and a tile the compiled shapes
-// hold.  MI355X, fp16, inputs in HBM, tile_rows against the lane-group form
-// (wave_row): [131072,250] 25.4 us vs 34.5, [1000000,33] 38.7 vs 55.0,
-// [1048576,100] 81.5 vs 122, [64000,500] 25.2 vs 30.2, fp32 [131072,125]
-// 25.1 vs 29.2; 16-byte multiples [262144,120] 25.1 vs 31.5, [131072,248]
+// 128 bytes -- in and out 16-byte aligned, and a tile of at least 4 rows.
+// MI355X, fp16, inputs in HBM, tile_rows against the lane-group form
+// (wave_row): [131072,250] 25.3 us vs 34.5, [1000000,33] 27.0 vs 55.0,
+// [1048576,100] 74.6 vs 122, [64000,500] 24.9 vs 30.2, fp32 [131072,125]
+// 25.0 vs 29.2; 16-byte multiples [262144,120] 25.1 vs 31.5, [131072,248]
 // 25.2 vs 29.9, [65536,504] 25.5 vs 29.3, but [524288,56] 24.2 vs 20.2 (one
 // granule per lane on 8 lanes, 16-byte windows, holds those rows whole).
 // Tiles of eight granules per lane (spilling 374-388 scalar registers) lost
 // to the lane groups and block_onepass: [65536,333] 26.2 vs 21.0,
-// [32768,1022] 29.2 vs 24.8; the tile shapes stop at four.
-constexpr int64_t kTileMaxRowBytes = 2048;
+// [32768,1022] 29.2 vs 24.8; the tile shapes stop at four.  Tile heights
+// of 4, 8 or 16 rows only (a tile filling half of its slots): [1000000,33]
+// 38.8 us, [1048576,100] 83.1.
+constexpr int64_t kTileMaxRowBytes = 1024;
 constexpr int64_t kTileMinRows = 64;
 
-int pick_tile_rows(int64_t cols, int es, int forced_t);
+int pick_tile_rows(int64_t cols, int es, int forced_variant, int* T_out);
 
 bool tile_rows_fits(int64_t rows, int64_t cols, int dtype, const void* in, const void* out) {
     const int es = elem_size(dtype);
     const int64_t rb = cols * es;
     return rows >= kTileMinRows && rb % 128 != 0 && (rb % 16 != 0 || rb > 128) &&
-           rb <= kTileMaxRowBytes &&
-           (uintptr_t)in % 16 == 0 && (uintptr_t)out % 16 == 0 && pick_tile_rows(cols, es, 0) >= 0;
+           rb <= kTileMaxRowBytes && (uintptr_t)in % 16 == 0 && (uintptr_t)out % 16 == 0 &&
+           pick_tile_rows(cols, es, -1, nullptr) >= 0;
 }
 
-// tile_rows: the variant for rows of `cols` elements of size es, or -1.
-// Tiles of T rows start on a 16-byte boundary when T is a multiple of
-// 16 / gcd(row bytes, 16); the largest T (up to 16) whose tile fits 64 * K
-// granules with K <= 4, and the smallest such K.  forced_t > 0 asks for
-// that T.
-int pick_tile_rows(int64_t cols, int es, int forced_t) {
-    const int vec = 16 / es;
-    if (cols < vec || cols * es > 4096) return -1;
+// Rows per tile with K granules per lane for rows of `cols` elements of size
+// es: the largest multiple of P0 = 16 / gcd(row bytes, 16) (tiles of P0 rows
+// start on a 16-byte boundary), at most rws::kTileMaxT, whose tile fits 64 K
+// granules; 0 when fewer than 4 rows fit.
+int tile_rows_per_tile(int64_t cols, int es, int K) {
+    const int64_t rb = cols * es;
+    if (cols < 16 / es || rb > kTileMaxRowBytes) return 0;
     int g = 16;
-    while ((cols * es) % g) g /= 2;
-    const int p0 = 16 / g;  // rows per 16-byte period
-    int best = -1;
+    while (rb % g) g /= 2;
+    const int p0 = 16 / g;
+    int64_t T = std::min<int64_t>(rws::kTileMaxT, 64LL * K * 16 / rb);
+    T -= T % p0;
+    return T >= 4 ? (int)T : 0;
+}
+
+// tile_rows: the variant (granules per lane K) for rows of `cols` elements of
+// size es, or -1; its rows per tile in *T_out.  Every slot costs the same
+// instructions whether the tile fills it or not, so the choice is the K with
+// the fewest slots per row, 64 K / T (the fullest tiles); at equal fill the
+// larger tile (fewer waves).  forced_variant >= 0 asks for that K.
+int pick_tile_rows(int64_t cols, int es, int forced_variant, int* T_out) {
+    int best = -1, best_t = 0;
     for (int i = 0; i < rws::kNumTileRows; ++i) {
-        const rws::TileRowsVariant& v = rws::kTileRows[i];
-        if (v.T % p0 || (forced_t > 0 && v.T != forced_t)) continue;
-        const int64_t gran = (int64_t)v.T * cols * es / 16;
-        if (gran > 64LL * v.K) continue;
-        if (best < 0 || v.T > rws::kTileRows[best].T ||
-            (v.T == rws::kTileRows[best].T && v.K < rws::kTileRows[best].K))
-            best = i;
+        if (forced_variant >= 0 && i != forced_variant) continue;
+        const int K = rws::kTileRows[i].K;
+        const int T = tile_rows_per_tile(cols, es, K);
+        if (T == 0) continue;
+        if (best >= 0) {
+            const int64_t lhs = (int64_t)K * best_t, rhs = (int64_t)rws::kTileRows[best].K * T;
+            if (lhs > rhs || (lhs == rhs && T <= best_t)) continue;
+        }
+        best = i;
+        best_t = T;
     }
+    if (T_out) *T_out = best_t;
     return best;
 }
+
+// XCD runs of the tile kernels (log2 of tiles per run, xcd_run): adjacent
+// tiles that share a cache line then share an L2 instead of each XCD
+// fetching the line (fp16 RMSNorm [1000000,33] read 9% more than it wrote
+// in launch order).  Runs of 64 tiles against launch order, MI355X, fp16
+// unless noted, inputs in HBM: backward [1000000,33] 34.1 us vs 35.1,
+// [131072,250] 33.9 vs 34.8; RMSNorm [1000000,33] 25.1 vs 25.9; LayerNorm
+// [131072,250] 24.6 vs 25.5; softmax [131072,250] 25.3 vs 25.7, [262144,120]
+// 25.1 vs 25.6, fp32 [131072,125] 25.0 vs 25.8 ([1000000,33] 27.0 both).
+constexpr int kTileLgRunFwd = 6;
+constexpr int kTileLgRunBwd = 6;
+constexpr int kTileLgRunNorm = 6;
 
 // Rows per XCD run (log2) for the one-row-per-workgroup kernels that hold the
 // row in registers (block_onepass, the backward's bwd_block): on rows that are
@@ -505,21 +534,22 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
             const int es = elem_size(dtype);
             if ((uintptr_t)in % 16 || (uintptr_t)out % 16)
                 return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows needs 16-byte aligned in and out");
-            p->variant = pick_tile_rows(cols, es, 0);
+            int T = 0;
+            p->variant = pick_tile_rows(cols, es, -1, &T);
             if (forced_variant >= 0) {
                 if (forced_variant >= rws::kNumTileRows) return bad_variant(rws::kNumTileRows);
-                if (pick_tile_rows(cols, es, rws::kTileRows[forced_variant].T) < 0) return bad_variant(rws::kNumTileRows);
-                const rws::TileRowsVariant& f = rws::kTileRows[forced_variant];
-                if ((int64_t)f.T * cols * es / 16 > 64LL * f.K) return bad_variant(rws::kNumTileRows);
+                if (pick_tile_rows(cols, es, forced_variant, &T) < 0) return bad_variant(rws::kNumTileRows);
                 p->variant = forced_variant;
             }
             if (p->variant < 0)
                 return fail(RWS_ERR_UNSUPPORTED_SHAPE,
-                            "tile_rows takes rows of one granule to 4096 bytes");
+                            "tile_rows takes rows of one granule to 1024 bytes");
             p->aligned = false;
-            p->window = (int64_t)rws::kTileRows[p->variant].T * cols * es / 16;
+            p->tile_t = T;
+            p->lgrun = kTileLgRunFwd;
+            p->window = (int64_t)T * cols * es / 16;
             // tiles (workgroups) per launch below 2^31
-            p->max_rows_per_launch = (int64_t)rws::kTileRows[p->variant].T * ((int64_t)1 << 30);
+            p->max_rows_per_launch = (int64_t)T * ((int64_t)1 << 30);
             break;
         }
         case RWS_KERNEL_WAVE_ROW: {
@@ -1043,7 +1073,9 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
         } else {
             switch (p.family) {
                 case RWS_KERNEL_WAVE_ROW: e = rws::launch_wave_row(L, p.variant); break;
-                case RWS_KERNEL_TILE_ROWS: e = rws::launch_tile_rows(L, p.variant); break;
+                case RWS_KERNEL_TILE_ROWS:
+                    e = rws::launch_tile_rows(L, p.variant, rws::TileShape{p.tile_t, p.lgrun});
+                    break;
                 case RWS_KERNEL_BLOCK_ONEPASS: e = rws::launch_block_onepass(L, p.variant); break;
                 case RWS_KERNEL_TWO_PASS: e = rws::launch_two_pass(L, p.variant); break;
                 case RWS_KERNEL_SPLITK:
@@ -1201,6 +1233,7 @@ struct BwdPlan {
     bool aligned = false;
     bool same_phase = false;
     int lgrun = 0;
+    int tile_t = 0;  // tile_rows: rows per tile
     int64_t max_rows = 0;
 };
 
@@ -1267,15 +1300,17 @@ static int plan_bwd(int64_t rows, int64_t cols, int dtype, const void* y, const 
     if (family == RWS_KERNEL_TILE_ROWS) {
         if (!dy16 || (uintptr_t)y % 16 || (uintptr_t)dx % 16)
             return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows needs 16-byte aligned y, dy and dx");
-        const int v = pick_tile_rows(cols, elem_size(dtype), 0);
+        int T = 0;
+        const int v = pick_tile_rows(cols, elem_size(dtype), -1, &T);
         if (v < 0)
-            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows takes rows of one granule to 4096 bytes");
+            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows takes rows of one granule to 1024 bytes");
         bp->family = family;
         bp->variant = v;
         bp->aligned = false;
         bp->same_phase = true;
-        bp->lgrun = 0;
-        bp->max_rows = (int64_t)rws::kTileRows[v].T * ((int64_t)1 << 30);
+        bp->lgrun = kTileLgRunBwd;
+        bp->tile_t = T;
+        bp->max_rows = (int64_t)T * ((int64_t)1 << 30);
         return RWS_OK;
     }
     if (family == RWS_KERNEL_SPLITK_ORDERED) {
@@ -1377,7 +1412,7 @@ int softmax_bwd_kernel(const void* y, const void* dy, void* dx, int64_t rows, in
         B.stream = (hipStream_t)stream;
         hipError_t e = hipSuccess;
         if (family == RWS_KERNEL_TILE_ROWS)
-            e = rws::launch_bwd_tile(B, variant);
+            e = rws::launch_bwd_tile(B, variant, rws::TileShape{bp.tile_t, bp.lgrun});
         else if (family != RWS_KERNEL_SPLITK_ORDERED)
             e = rws::launch_bwd(B, family, variant);
         else if (tag_n == 0)
@@ -1408,6 +1443,7 @@ struct NormPlan {
     bool aligned = false;
     bool same_phase = false;
     int lgrun = 0;
+    int tile_t = 0;  // tile_rows: rows per tile
     int64_t max_rows = 0;
 };
 
@@ -1486,15 +1522,17 @@ static int plan_norm(int64_t rows, int64_t cols, int dtype, const void* in, cons
             return fail(RWS_ERR_UNSUPPORTED_SHAPE, "the tile_rows normalisation takes no weight or bias");
         if ((uintptr_t)in % 16 || (uintptr_t)out % 16)
             return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows needs 16-byte aligned in and out");
-        const int v = pick_tile_rows(cols, elem_size(dtype), 0);
+        int T = 0;
+        const int v = pick_tile_rows(cols, elem_size(dtype), -1, &T);
         if (v < 0)
-            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows takes rows of one granule to 4096 bytes");
+            return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows takes rows of one granule to 1024 bytes");
         np->family = family;
         np->variant = v;
         np->aligned = false;
         np->same_phase = true;
-        np->lgrun = 0;
-        np->max_rows = (int64_t)rws::kTileRows[v].T * ((int64_t)1 << 30);
+        np->lgrun = kTileLgRunNorm;
+        np->tile_t = T;
+        np->max_rows = (int64_t)T * ((int64_t)1 << 30);
         return RWS_OK;
     }
     if (family == RWS_KERNEL_SPLITK_ORDERED) {
@@ -1614,7 +1652,7 @@ static int norm_run(int mode, const void* in, void* out, int64_t rows, int64_t c
         L.stream = (hipStream_t)stream;
         hipError_t e = hipSuccess;
         if (family == RWS_KERNEL_TILE_ROWS)
-            e = rws::launch_norm_tile(L, variant);
+            e = rws::launch_norm_tile(L, variant, rws::TileShape{np.tile_t, np.lgrun});
         else if (family == 1)
             e = rws::launch_norm_wave(L, variant);
         else if (family != RWS_KERNEL_SPLITK_ORDERED)
@@ -1698,10 +1736,12 @@ static int describe_launch(int64_t rows, int64_t cols, int dtype, const void* in
     switch (p.family) {
         case RWS_KERNEL_TILE_ROWS: {
             const rws::TileRowsVariant& v = rws::kTileRows[p.variant];
-            std::snprintf(buf, (size_t)buflen, "tile_rows<%s,T=%d,K=%d> grid=%lld block=64 granules<=%lld",
-                          dtype_name(dtype), v.T, v.K,
-                          (long long)((std::min(rows, p.max_rows_per_launch) + v.T - 1) / v.T),
-                          (long long)wmax);
+            std::snprintf(buf, (size_t)buflen,
+                          "tile_rows<%s,T=%d,K=%d> grid=%lld block=64 granules<=%lld%s",
+                          dtype_name(dtype), p.tile_t, v.K,
+                          (long long)((std::min(rows, p.max_rows_per_launch) + p.tile_t - 1) /
+                                      p.tile_t),
+                          (long long)wmax, run);
             break;
         }
         case RWS_KERNEL_WAVE_ROW: {
@@ -1831,8 +1871,9 @@ int softmax_bwd_describe_launch(int64_t rows, int64_t cols, int dtype, const voi
     const int64_t r = std::min(rows, bp.max_rows);
     if (bp.family == RWS_KERNEL_TILE_ROWS) {
         const rws::TileRowsVariant& v = rws::kTileRows[bp.variant];
-        std::snprintf(buf, (size_t)buflen, "bwd_tile<%s,T=%d,K=%d> grid=%lld block=64",
-                      dtype_name(dtype), v.T, v.K, (long long)((r + v.T - 1) / v.T));
+        std::snprintf(buf, (size_t)buflen, "bwd_tile<%s,T=%d,K=%d> grid=%lld block=64 xcd_run=%d",
+                      dtype_name(dtype), bp.tile_t, v.K, (long long)((r + bp.tile_t - 1) / bp.tile_t),
+                      1 << bp.lgrun);
     } else if (bp.family == RWS_KERNEL_SPLITK_ORDERED) {
         std::snprintf(buf, (size_t)buflen,
                       "bwd_ordered<%s,%s,B=%d,KC=%d> P=%d grid=%lld (2 stages) block=%d",
@@ -1881,8 +1922,9 @@ int norm_describe_launch(int64_t rows, int64_t cols, int dtype, const void* in, 
     const long long wline = (long long)window_granules(geometry(cols, dtype, in, out), 128);
     if (np.family == RWS_KERNEL_TILE_ROWS) {
         const rws::TileRowsVariant& v = rws::kTileRows[np.variant];
-        std::snprintf(buf, (size_t)buflen, "norm_tile<%s,T=%d,K=%d> grid=%lld block=64",
-                      dtype_name(dtype), v.T, v.K, (long long)((r + v.T - 1) / v.T));
+        std::snprintf(buf, (size_t)buflen, "norm_tile<%s,T=%d,K=%d> grid=%lld block=64 xcd_run=%d",
+                      dtype_name(dtype), np.tile_t, v.K, (long long)((r + np.tile_t - 1) / np.tile_t),
+                      1 << np.lgrun);
     } else if (np.family == RWS_KERNEL_SPLITK_ORDERED) {
         std::snprintf(buf, (size_t)buflen,
                       "norm_ordered<%s,%s,B=%d,KC=%d> P=%d grid=%lld (2 stages) block=%d",

@@ -47,7 +47,14 @@ constexpr int softmax_window_align(int G) { return G * 16 > 128 ? 128 : 16; }
 struct OnepassVariant { int block, kr, kl; };    // threads, register granules, LDS granules
 struct TwoPassVariant { int block, u; };         // threads, granules per batch
 struct SplitkVariant { int block, kc; };         // threads, granules per thread per chunk
-struct TileRowsVariant { int T, K; };            // rows per tile, granules per lane
+struct TileRowsVariant { int K; };               // granules per lane
+// Tile of a tile_rows launch: T rows per one-wave workgroup (4..64, a whole
+// number of granules, at most 64 * K of them), tiles in XCD runs of 2^lgrun.
+struct TileShape {
+    int T;
+    int lgrun;
+};
+constexpr int kTileMaxT = 64;  // rows per tile at most (one lane per row)
 
 extern const WaveRowVariant kWaveRow[];
 extern const int kNumWaveRow;
@@ -78,10 +85,10 @@ inline int64_t wave_row_grid(const WaveRowVariant& v, int64_t rows) {
 }
 
 hipError_t launch_wave_row(const Launch& L, int variant);
-// Tiles of kTileRows[variant].T rows per one-wave workgroup; in and out
-// 16-byte aligned, T * cols * element size a multiple of 16, at most 64 * K
-// granules per tile.
-hipError_t launch_tile_rows(const Launch& L, int variant);
+// Tiles of t.T rows per one-wave workgroup, K = kTileRows[variant].K
+// granules per lane; in and out 16-byte aligned (hipErrorInvalidValue for a
+// shape the kernels do not take).
+hipError_t launch_tile_rows(const Launch& L, int variant, const TileShape& t);
 hipError_t launch_block_onepass(const Launch& L, int variant);
 hipError_t launch_two_pass(const Launch& L, int variant);
 // Both split-k stages; ws holds rows*P (m, d) pairs.
@@ -151,7 +158,7 @@ struct BwdLaunch {
 };
 // tile_rows form of the backward (kTileRows variants): y, dy and dx
 // 16-byte aligned, as launch_tile_rows.
-hipError_t launch_bwd_tile(const BwdLaunch& B, int variant);
+hipError_t launch_bwd_tile(const BwdLaunch& B, int variant, const TileShape& t);
 extern const WaveRowVariant kBwdWave[];
 extern const int kNumBwdWave;
 extern const TwoPassVariant kBwdBlock[];  // (threads, register granules per thread)
@@ -192,7 +199,7 @@ struct NormLaunch {
 };
 // tile_rows form of the normalisations without weight and bias
 // (kTileRows variants): in and out 16-byte aligned, as launch_tile_rows.
-hipError_t launch_norm_tile(const NormLaunch& N, int variant);
+hipError_t launch_norm_tile(const NormLaunch& N, int variant, const TileShape& t);
 extern const WaveRowVariant kNormWave[];
 extern const int kNumNormWave;
 extern const TwoPassVariant kNormBlock[];   // (threads, register granules per thread)

@@ -9,11 +9,14 @@
 // T rows, T a multiple of P0, starts and ends on a 16-byte boundary whenever
 // the tensor does.  One wave takes one tile: lane l holds the tile's granules
 // l, l + 64, ..., l + 64 (K - 1) -- coalesced 128-bit loads and stores,
-// every granule read and written once and whole.  Rows have at least one
-// granule of elements, so a granule holds elements of at most two rows: each
-// lane keeps two partials per granule, one for the row of its first element
-// ("a") and one for the next row ("b").  A row reduction then goes through
-// LDS: the partials are written, the 64 / T lanes of each row fold the
+// every granule read and written once and whole.  T is a launch argument
+// (at most 64), chosen per row length so that the tile fills as many of the
+// 64 K granule slots as it can: a slot past the tile costs the same
+// instructions as a full one.  Rows have at least one granule of elements,
+// so a granule holds elements of at most two rows: each lane keeps two
+// partials per granule, one for the row of its first element ("a") and one
+// for the next row ("b").  A row reduction then goes through LDS: the
+// partials are written, the 2^lg lanes of each row (2^lg * T <= 64) fold the
 // partials of the row's granules (the first granule gives its "b" partial
 // when the row starts inside it), a DPP reduction over those lanes finishes
 // the row, and one lane publishes the row's result for every lane to read.
@@ -34,27 +37,39 @@ __device__ inline uint32_t tile_div(uint32_t x, uint64_t M) {
     return (uint32_t)((hi + (lo >> 32)) >> 32);
 }
 
-// Where the granules a lane holds sit in its tile.
-template <int DT, int T, int K>
+// Where the granules a lane holds sit in its tile of nrows rows.
+template <int DT, int K>
 struct TileSlots {
     static constexpr int VEC = Elem<DT>::VEC;
     int nel;        // elements of the tile
-    int ra[K];      // tile row of granule i's first element (clamped to T - 1)
+    int last;       // the tile's last row
+    int ra[K];      // tile row of granule i's first element (clamped to last)
     int split[K];   // elements of granule i in that row (>= VEC: all of them)
 
     __device__ inline TileSlots(int nrows, int cols, uint64_t cmagic) {
         nel = nrows * cols;
+        last = nrows - 1;
 #pragma unroll
         for (int i = 0; i < K; ++i) {
             const int x = granule(i) * VEC;
             const int q = (int)tile_div((uint32_t)x, cmagic);
-            ra[i] = q < T - 1 ? q : T - 1;  // slots past the tile: clamped, never used
+            ra[i] = q < last ? q : last;  // slots past the tile: clamped, never used
             split[i] = (q + 1) * cols - x;
         }
     }
     __device__ static inline int granule(int i) { return (int)threadIdx.x + 64 * i; }
-    __device__ inline int rb(int i) const { return ra[i] + 1 < T ? ra[i] + 1 : T - 1; }
-    __device__ inline bool in_a(int i, int e) const { return e < split[i]; }
+    __device__ inline int rb(int i) const { return ra[i] < last ? ra[i] + 1 : last; }
+    // Element e of granule i is in row ra[i] when e < split[i], else in the
+    // next row.  split[i] as a value the compiler cannot match with earlier uses: each
+    // pass over the granules then compares afresh instead of keeping 2 K VEC
+    // lane masks (scalar register pairs) alive across the row reductions,
+    // which spilled them at K >= 3 (one compare per element and pass is
+    // cheaper than the spill traffic).
+    __device__ inline int split_pass(int i) const {
+        int sp = split[i];
+        asm volatile("" : "+v"(sp));
+        return sp;
+    }
 };
 
 // Granule i of a tile tensor (raw 16 bytes): whole, element by element where
@@ -90,17 +105,25 @@ __device__ inline void tile_store(char* g, int j, int nel, const float* v) {
     }
 }
 
+// Reduction over aligned groups of 2^lg lanes (lg uniform, 0..4).
+template <class Op>
+__device__ inline float group_reduce_lg(float v, int lg) {
+    if (lg >= 1) v = Op::f(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
+    if (lg >= 2) v = Op::f(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
+    if (lg >= 3) v = Op::f(v, dpp<0x141>(v));  // row_half_mirror: other quad of 8
+    if (lg >= 4) v = Op::f(v, dpp<0x140>(v));  // row_mirror: other half of 16
+    return v;
+}
+
 // One row reduction over a tile: pa[i] / pb[i] are granule i's partials for
 // its first row and for the next one.  On return row_out[r] holds
 // fin(reduction of row r) for the tile's rows (0 for rows past a partial
-// tile).  part_a / part_b: 64 * K floats of LDS each; the two barriers make
-// the call safe to repeat with the same arrays.
-template <int T, int K, class Op, class Fin>
+// tile).  part_a / part_b: 64 * K floats of LDS each, row_out kTileMaxT; the
+// two barriers make the call safe to repeat with the same arrays.
+template <int K, class Op, class Fin>
 __device__ inline void tile_fold(const float (&pa)[K], const float (&pb)[K], float* part_a,
-                                 float* part_b, float* row_out, int cols, int nrows, int vec,
-                                 float identity, Fin fin) {
-    constexpr int GL = 64 / T;  // lanes per row
-    static_assert(GL >= 4 && GL <= 64, "4..64 lanes per row");
+                                 float* part_b, float* row_out, int cols, int nrows, int lg,
+                                 int vec, float identity, Fin fin) {
     const int lane = threadIdx.x;
 #pragma unroll
     for (int i = 0; i < K; ++i) {
@@ -108,17 +131,19 @@ __device__ inline void tile_fold(const float (&pa)[K], const float (&pb)[K], flo
         part_b[lane + 64 * i] = pb[i];
     }
     __syncthreads();
-    const int r = lane / GL;
-    const int t = lane & (GL - 1);
-    const int j0 = (r * cols) / vec;
-    const int j1 = ((r + 1) * cols - 1) / vec;
-    const bool first_in_b = j0 * vec < r * cols;
+    const int r = lane >> lg;
+    const int gl = 1 << lg;
+    const int t = lane & (gl - 1);
     const bool live = r < nrows;
     float acc = identity;
-    if (live)
-        for (int j = j0 + t; j <= j1; j += GL)
+    if (live) {
+        const int j0 = (r * cols) / vec;
+        const int j1 = ((r + 1) * cols - 1) / vec;
+        const bool first_in_b = j0 * vec < r * cols;
+        for (int j = j0 + t; j <= j1; j += gl)
             acc = Op::f(acc, (j == j0 && first_in_b) ? part_b[j] : part_a[j]);
-    acc = group_reduce<GL, Op>(acc);
+    }
+    acc = group_reduce_lg<Op>(acc, lg);
     if (t == 0) row_out[r] = live ? fin(acc) : 0.0f;
     __syncthreads();
 }

@@ -16,46 +16,53 @@
 
 namespace rws {
 
+// Maxima of granule values v over its first row's elements (e < split) and
+// over the next row's, each as a tree of three-operand maxima.
+template <int VEC>
+__device__ inline void split_max(const float (&v)[VEC], int split, float& ma, float& mb) {
+    float a[VEC], b[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        const bool in_a = e < split;
+        a[e] = in_a ? v[e] : kNegInf;
+        b[e] = in_a ? kNegInf : v[e];
+    }
+    if (VEC == 8) {
+        ma = vmax(vmax(vmax(a[0], a[1]), a[2]), vmax(vmax(a[3], a[4]), vmax(vmax(a[5], a[6]), a[7])));
+        mb = vmax(vmax(vmax(b[0], b[1]), b[2]), vmax(vmax(b[3], b[4]), vmax(vmax(b[5], b[6]), b[7])));
+    } else {
+        ma = vmax(vmax(vmax(a[0], a[1]), a[2]), a[VEC - 1]);
+        mb = vmax(vmax(vmax(b[0], b[1]), b[2]), b[VEC - 1]);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // softmax
 // ---------------------------------------------------------------------------
-template <int DT, int T, int K, bool FULL>
+// Slots past the tile (and, in the tensor's last tile, elements past its
+// end) hold zeros; their partials are never folded into a row and they are
+// never stored.
+template <int DT, int K, bool FULL>
 __device__ inline void tile_softmax(const char* __restrict__ gin, char* __restrict__ gout,
-                                    int nrows, int cols, uint64_t cmagic, float* part_a,
+                                    int nrows, int cols, int lg, uint64_t cmagic, float* part_a,
                                     float* part_b, float* row_max, float* row_rcp) {
     constexpr int VEC = Elem<DT>::VEC;
-    const TileSlots<DT, T, K> S(nrows, cols, cmagic);
+    static_assert(VEC == 8 || VEC == 4, "granule of 4 or 8 elements");
+    const TileSlots<DT, K> S(nrows, cols, cmagic);
     u32x4 raw[K];
 #pragma unroll
     for (int i = 0; i < K; ++i) raw[i] = tile_load<DT, FULL>(gin, S.granule(i), S.nel);
 
-    // widen; slots past the tile are -inf (they belong to no row)
-    float v[K][VEC];
-#pragma unroll
-    for (int i = 0; i < K; ++i) {
-        Elem<DT>::widen(raw[i], v[i]);
-        const int x = S.granule(i) * VEC;
-        if (x + VEC > S.nel) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) v[i][e] = x + e < S.nel ? v[i][e] : kNegInf;
-        }
-    }
-
     // row maxima
+    float v[K][VEC];
     float pa[K], pb[K];
 #pragma unroll
     for (int i = 0; i < K; ++i) {
-        pa[i] = kNegInf;
-        pb[i] = kNegInf;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const bool in_a = S.in_a(i, e);
-            pa[i] = vmax(pa[i], in_a ? v[i][e] : kNegInf);
-            pb[i] = vmax(pb[i], in_a ? kNegInf : v[i][e]);
-        }
+        Elem<DT>::widen(raw[i], v[i]);
+        split_max<VEC>(v[i], S.split_pass(i), pa[i], pb[i]);
     }
-    tile_fold<T, K, OpMax>(pa, pb, part_a, part_b, row_max, cols, nrows, VEC, kNegInf,
-                           [](float m) { return m; });
+    tile_fold<K, OpMax>(pa, pb, part_a, part_b, row_max, cols, nrows, lg, VEC, kNegInf,
+                        [](float m) { return m; });
 
     // exponentials against each element's row maximum (one exp2 per element:
     // the FMA offset of the element's row is selected first; a granule with
@@ -64,12 +71,13 @@ __device__ inline void tile_softmax(const char* __restrict__ gin, char* __restri
 #pragma unroll
     for (int i = 0; i < K; ++i) {
         const RowExp ea(row_max[S.ra[i]]), eb(row_max[S.rb(i)]);
+        const int sp = S.split_pass(i);
         pa[i] = 0.0f;
         pb[i] = 0.0f;
         if (__builtin_expect(ea.big || eb.big, 0)) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const bool in_a = S.in_a(i, e);
+                const bool in_a = e < sp;
                 const float y = in_a ? ea.one(v[i][e]) : eb.one(v[i][e]);
                 v[i][e] = y;
                 pa[i] += in_a ? y : 0.0f;
@@ -78,7 +86,7 @@ __device__ inline void tile_softmax(const char* __restrict__ gin, char* __restri
         } else {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const bool in_a = S.in_a(i, e);
+                const bool in_a = e < sp;
                 const float y = __builtin_amdgcn_exp2f(
                     __builtin_fmaf(v[i][e], kLog2e, in_a ? ea.negc : eb.negc));
                 v[i][e] = y;
@@ -87,47 +95,55 @@ __device__ inline void tile_softmax(const char* __restrict__ gin, char* __restri
             }
         }
     }
-    tile_fold<T, K, OpSum>(pa, pb, part_a, part_b, row_rcp, cols, nrows, VEC, 0.0f,
-                           [](float s) { return __builtin_amdgcn_rcpf(s); });
+    tile_fold<K, OpSum>(pa, pb, part_a, part_b, row_rcp, cols, nrows, lg, VEC, 0.0f,
+                        [](float s) { return __builtin_amdgcn_rcpf(s); });
 
     // scale and store
 #pragma unroll
     for (int i = 0; i < K; ++i) {
         const float qa = row_rcp[S.ra[i]], qb = row_rcp[S.rb(i)];
+        const int sp = S.split_pass(i);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) v[i][e] *= S.in_a(i, e) ? qa : qb;
+        for (int e = 0; e < VEC; ++e) v[i][e] *= e < sp ? qa : qb;
         tile_store<DT, FULL>(gout, S.granule(i), S.nel, v[i]);
     }
 }
 
-template <int DT, int T, int K>
+// The tile a workgroup takes (XCD runs of 2^lgrun tiles, xcd_run) and its
+// first row.
+__device__ inline int64_t tile_row0(int T, int lgrun) {
+    return xcd_run(blockIdx.x, gridDim.x, lgrun) * T;
+}
+
+template <int DT, int K>
 __global__ __launch_bounds__(64) void k_tile_rows(const void* __restrict__ in,
                                                   void* __restrict__ out, int64_t rows, int cols,
-                                                  uint64_t cmagic) {
+                                                  uint64_t cmagic, int T, int lg, int lgrun) {
     __shared__ float part_a[64 * K];  // per granule: its first row's partial
     __shared__ float part_b[64 * K];  // per granule: the next row's partial
-    __shared__ float row_max[T];
-    __shared__ float row_rcp[T];
-    const int64_t row0 = (int64_t)blockIdx.x * T;
+    __shared__ float row_max[kTileMaxT];
+    __shared__ float row_rcp[kTileMaxT];
+    const int64_t row0 = tile_row0(T, lgrun);
     const int64_t off = row0 * cols * Elem<DT>::SIZE;
     const char* gin = (const char*)in + off;
     char* gout = (char*)out + off;
     if (rows - row0 >= T)
-        tile_softmax<DT, T, K, true>(gin, gout, T, cols, cmagic, part_a, part_b, row_max, row_rcp);
+        tile_softmax<DT, K, true>(gin, gout, T, cols, lg, cmagic, part_a, part_b, row_max, row_rcp);
     else
-        tile_softmax<DT, T, K, false>(gin, gout, (int)(rows - row0), cols, cmagic, part_a, part_b,
-                                      row_max, row_rcp);
+        tile_softmax<DT, K, false>(gin, gout, (int)(rows - row0), cols, lg, cmagic, part_a, part_b,
+                                   row_max, row_rcp);
 }
 
 // ---------------------------------------------------------------------------
 // softmax backward
 // ---------------------------------------------------------------------------
-template <int DT, int T, int K, bool FULL>
+template <int DT, int K, bool FULL>
 __device__ inline void tile_backward(const char* __restrict__ gy, const char* __restrict__ gdy,
-                                     char* __restrict__ gdx, int nrows, int cols, uint64_t cmagic,
-                                     float* part_a, float* part_b, float* row_dot) {
+                                     char* __restrict__ gdx, int nrows, int cols, int lg,
+                                     uint64_t cmagic, float* part_a, float* part_b,
+                                     float* row_dot) {
     constexpr int VEC = Elem<DT>::VEC;
-    const TileSlots<DT, T, K> S(nrows, cols, cmagic);
+    const TileSlots<DT, K> S(nrows, cols, cmagic);
     u32x4 ry[K], rdy[K];
 #pragma unroll
     for (int i = 0; i < K; ++i) {
@@ -143,55 +159,58 @@ __device__ inline void tile_backward(const char* __restrict__ gy, const char* __
         Elem<DT>::widen(rdy[i], d[i]);
         pa[i] = 0.0f;
         pb[i] = 0.0f;
+        const int sp = S.split_pass(i);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const float p = y[i][e] * d[i][e];
-            const bool in_a = S.in_a(i, e);
+            const bool in_a = e < sp;
             pa[i] += in_a ? p : 0.0f;
             pb[i] += in_a ? 0.0f : p;
         }
     }
-    tile_fold<T, K, OpSum>(pa, pb, part_a, part_b, row_dot, cols, nrows, VEC, 0.0f,
-                           [](float s) { return s; });
+    tile_fold<K, OpSum>(pa, pb, part_a, part_b, row_dot, cols, nrows, lg, VEC, 0.0f,
+                        [](float s) { return s; });
 #pragma unroll
     for (int i = 0; i < K; ++i) {
         const float sa = row_dot[S.ra[i]], sb = row_dot[S.rb(i)];
+        const int sp = S.split_pass(i);
         float o[VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) o[e] = y[i][e] * (d[i][e] - (S.in_a(i, e) ? sa : sb));
+        for (int e = 0; e < VEC; ++e) o[e] = y[i][e] * (d[i][e] - (e < sp ? sa : sb));
         tile_store<DT, FULL>(gdx, S.granule(i), S.nel, o);
     }
 }
 
-template <int DT, int T, int K>
+template <int DT, int K>
 __global__ __launch_bounds__(64) void k_bwd_tile(const void* __restrict__ y,
                                                  const void* __restrict__ dy,
                                                  void* __restrict__ dx, int64_t rows, int cols,
-                                                 uint64_t cmagic) {
+                                                 uint64_t cmagic, int T, int lg, int lgrun) {
     __shared__ float part_a[64 * K];
     __shared__ float part_b[64 * K];
-    __shared__ float row_dot[T];
-    const int64_t row0 = (int64_t)blockIdx.x * T;
+    __shared__ float row_dot[kTileMaxT];
+    const int64_t row0 = tile_row0(T, lgrun);
     const int64_t off = row0 * cols * Elem<DT>::SIZE;
     const char* gy = (const char*)y + off;
     const char* gdy = (const char*)dy + off;
     char* gdx = (char*)dx + off;
     if (rows - row0 >= T)
-        tile_backward<DT, T, K, true>(gy, gdy, gdx, T, cols, cmagic, part_a, part_b, row_dot);
+        tile_backward<DT, K, true>(gy, gdy, gdx, T, cols, lg, cmagic, part_a, part_b, row_dot);
     else
-        tile_backward<DT, T, K, false>(gy, gdy, gdx, (int)(rows - row0), cols, cmagic, part_a,
-                                       part_b, row_dot);
+        tile_backward<DT, K, false>(gy, gdy, gdx, (int)(rows - row0), cols, lg, cmagic, part_a,
+                                    part_b, row_dot);
 }
 
 // ---------------------------------------------------------------------------
 // LayerNorm / RMSNorm without weight and bias
 // ---------------------------------------------------------------------------
-template <int DT, int T, int K, int MODE, bool FULL>
+template <int DT, int K, int MODE, bool FULL>
 __device__ inline void tile_norm(const char* __restrict__ gin, char* __restrict__ gout, int nrows,
-                                 int cols, uint64_t cmagic, const NormArgs& A, int64_t row0,
-                                 float* part_a, float* part_b, float* row_mu, float* row_rstd) {
+                                 int cols, int lg, uint64_t cmagic, const NormArgs& A,
+                                 int64_t row0, float* part_a, float* part_b, float* row_mu,
+                                 float* row_rstd) {
     constexpr int VEC = Elem<DT>::VEC;
-    const TileSlots<DT, T, K> S(nrows, cols, cmagic);
+    const TileSlots<DT, K> S(nrows, cols, cmagic);
     u32x4 raw[K];
 #pragma unroll
     for (int i = 0; i < K; ++i) raw[i] = tile_load<DT, FULL>(gin, S.granule(i), S.nel);
@@ -204,24 +223,26 @@ __device__ inline void tile_norm(const char* __restrict__ gin, char* __restrict_
             Elem<DT>::widen(raw[i], v[i]);
             pa[i] = 0.0f;
             pb[i] = 0.0f;
+            const int sp = S.split_pass(i);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const bool in_a = S.in_a(i, e);
+                const bool in_a = e < sp;
                 pa[i] += in_a ? v[i][e] : 0.0f;
                 pb[i] += in_a ? 0.0f : v[i][e];
             }
         }
         const float n = A.n;
-        tile_fold<T, K, OpSum>(pa, pb, part_a, part_b, row_mu, cols, nrows, VEC, 0.0f,
-                               [n](float s) { return s / n; });
+        tile_fold<K, OpSum>(pa, pb, part_a, part_b, row_mu, cols, nrows, lg, VEC, 0.0f,
+                            [n](float s) { return s / n; });
 #pragma unroll
         for (int i = 0; i < K; ++i) {
             const float ma = row_mu[S.ra[i]], mb = row_mu[S.rb(i)];
             pa[i] = 0.0f;
             pb[i] = 0.0f;
+            const int sp = S.split_pass(i);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const bool in_a = S.in_a(i, e);
+                const bool in_a = e < sp;
                 const float c = v[i][e] - (in_a ? ma : mb);
                 pa[i] = in_a ? __builtin_fmaf(c, c, pa[i]) : pa[i];
                 pb[i] = in_a ? pb[i] : __builtin_fmaf(c, c, pb[i]);
@@ -233,17 +254,18 @@ __device__ inline void tile_norm(const char* __restrict__ gin, char* __restrict_
             Elem<DT>::widen(raw[i], v[i]);
             pa[i] = 0.0f;
             pb[i] = 0.0f;
+            const int sp = S.split_pass(i);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const bool in_a = S.in_a(i, e);
+                const bool in_a = e < sp;
                 pa[i] = in_a ? __builtin_fmaf(v[i][e], v[i][e], pa[i]) : pa[i];
                 pb[i] = in_a ? pb[i] : __builtin_fmaf(v[i][e], v[i][e], pb[i]);
             }
         }
     }
     const NormArgs Ac = A;
-    tile_fold<T, K, OpSum>(pa, pb, part_a, part_b, row_rstd, cols, nrows, VEC, 0.0f,
-                           [Ac](float q) { return norm_rstd(q, Ac); });
+    tile_fold<K, OpSum>(pa, pb, part_a, part_b, row_rstd, cols, nrows, lg, VEC, 0.0f,
+                        [Ac](float q) { return norm_rstd(q, Ac); });
     const int lane = threadIdx.x;
     if (lane < nrows) {
         if (MODE == kLayerNorm && A.mean) A.mean[row0 + lane] = row_mu[lane];
@@ -252,139 +274,163 @@ __device__ inline void tile_norm(const char* __restrict__ gin, char* __restrict_
 #pragma unroll
     for (int i = 0; i < K; ++i) {
         const float ra = row_rstd[S.ra[i]], rb = row_rstd[S.rb(i)];
+        const int sp = S.split_pass(i);
         float o[VEC];
         if (MODE == kLayerNorm) {
             const float ma = row_mu[S.ra[i]], mb = row_mu[S.rb(i)];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const bool in_a = S.in_a(i, e);
+                const bool in_a = e < sp;
                 o[e] = (v[i][e] - (in_a ? ma : mb)) * (in_a ? ra : rb);
             }
         } else {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) o[e] = v[i][e] * (S.in_a(i, e) ? ra : rb);
+            for (int e = 0; e < VEC; ++e) o[e] = v[i][e] * (e < sp ? ra : rb);
         }
         tile_store<DT, FULL>(gout, S.granule(i), S.nel, o);
     }
 }
 
-template <int DT, int T, int K, int MODE>
+template <int DT, int K, int MODE>
 __global__ __launch_bounds__(64) void k_norm_tile(const void* __restrict__ in,
                                                   void* __restrict__ out, int64_t rows, int cols,
-                                                  uint64_t cmagic, NormArgs A) {
+                                                  uint64_t cmagic, int T, int lg, int lgrun,
+                                                  NormArgs A) {
     __shared__ float part_a[64 * K];
     __shared__ float part_b[64 * K];
-    __shared__ float row_mu[T];
-    __shared__ float row_rstd[T];
-    const int64_t row0 = (int64_t)blockIdx.x * T;
+    __shared__ float row_mu[kTileMaxT];
+    __shared__ float row_rstd[kTileMaxT];
+    const int64_t row0 = tile_row0(T, lgrun);
     const int64_t off = row0 * cols * Elem<DT>::SIZE;
     const char* gin = (const char*)in + off;
     char* gout = (char*)out + off;
     if (rows - row0 >= T)
-        tile_norm<DT, T, K, MODE, true>(gin, gout, T, cols, cmagic, A, row0, part_a, part_b, row_mu,
-                                        row_rstd);
+        tile_norm<DT, K, MODE, true>(gin, gout, T, cols, lg, cmagic, A, row0, part_a, part_b,
+                                     row_mu, row_rstd);
     else
-        tile_norm<DT, T, K, MODE, false>(gin, gout, (int)(rows - row0), cols, cmagic, A, row0,
-                                         part_a, part_b, row_mu, row_rstd);
+        tile_norm<DT, K, MODE, false>(gin, gout, (int)(rows - row0), cols, lg, cmagic, A, row0,
+                                      part_a, part_b, row_mu, row_rstd);
 }
 
 // ---------------------------------------------------------------------------
 // variants and launchers
 // ---------------------------------------------------------------------------
-// (rows per tile, granules per lane)
-#define RWS_TILE_ROWS_VARIANTS(X) \
-    X(4, 1) X(4, 2) X(4, 4)       \
-    X(8, 1) X(8, 2) X(8, 4)       \
-    X(16, 1) X(16, 2) X(16, 4)
+// granules per lane
+#define RWS_TILE_ROWS_VARIANTS(X) X(1) X(2) X(3) X(4)
 
-#define RWS_ROW(t, k) {t, k},
+#define RWS_ROW(k) {k},
 const TileRowsVariant kTileRows[] = {RWS_TILE_ROWS_VARIANTS(RWS_ROW)};
 #undef RWS_ROW
 const int kNumTileRows = sizeof(kTileRows) / sizeof(kTileRows[0]);
 
-template <int DT, int T, int K>
-static hipError_t go(const Launch& L) {
-    const int64_t tiles = (L.rows + T - 1) / T;
-    hipLaunchKernelGGL((k_tile_rows<DT, T, K>), dim3((unsigned)tiles), dim3(64), 0, L.stream, L.in,
-                       L.out, L.rows, L.cols, remainder_magic((uint64_t)L.cols));
+// log2 of the lanes that fold one row: the largest power of two g with
+// g * T <= 64 (T >= 4, so at most 16 lanes)
+static int tile_lg(int T) {
+    int lg = 0;
+    while (lg < 4 && (T << (lg + 1)) <= 64) ++lg;
+    return lg;
+}
+
+// The shape the kernels assume: 4..64 rows per tile, tiles of whole
+// granules (so every tile starts 16-byte aligned), at most 64 * K of them,
+// fewer than 2^31 tiles.
+static bool tile_ok(const TileShape& t, int64_t rows, int cols, int es, int K) {
+    const int64_t bytes = (int64_t)t.T * cols * es;
+    return t.T >= 4 && t.T <= kTileMaxT && rows > 0 && cols * es >= 16 && bytes % 16 == 0 &&
+           bytes / 16 <= 64LL * K && (rows + t.T - 1) / t.T < ((int64_t)1 << 31) &&
+           t.lgrun >= 0 && t.lgrun <= 10;
+}
+
+template <int DT, int K>
+static hipError_t go(const Launch& L, const TileShape& t) {
+    if (!tile_ok(t, L.rows, L.cols, Elem<DT>::SIZE, K)) return hipErrorInvalidValue;
+    const int64_t tiles = (L.rows + t.T - 1) / t.T;
+    hipLaunchKernelGGL((k_tile_rows<DT, K>), dim3((unsigned)tiles), dim3(64), 0, L.stream, L.in,
+                       L.out, L.rows, L.cols, remainder_magic((uint64_t)L.cols), t.T, tile_lg(t.T),
+                       t.lgrun);
     return hipGetLastError();
 }
 
-template <int DT, int T, int K>
-static hipError_t go_bwd(const BwdLaunch& B) {
-    const int64_t tiles = (B.rows + T - 1) / T;
-    hipLaunchKernelGGL((k_bwd_tile<DT, T, K>), dim3((unsigned)tiles), dim3(64), 0, B.stream, B.y,
-                       B.dy, B.dx, B.rows, B.cols, remainder_magic((uint64_t)B.cols));
+template <int DT, int K>
+static hipError_t go_bwd(const BwdLaunch& B, const TileShape& t) {
+    if (!tile_ok(t, B.rows, B.cols, Elem<DT>::SIZE, K)) return hipErrorInvalidValue;
+    const int64_t tiles = (B.rows + t.T - 1) / t.T;
+    hipLaunchKernelGGL((k_bwd_tile<DT, K>), dim3((unsigned)tiles), dim3(64), 0, B.stream, B.y,
+                       B.dy, B.dx, B.rows, B.cols, remainder_magic((uint64_t)B.cols), t.T,
+                       tile_lg(t.T), t.lgrun);
     return hipGetLastError();
 }
 
-template <int DT, int T, int K>
-static hipError_t go_norm(const NormLaunch& N) {
-    const int64_t tiles = (N.rows + T - 1) / T;
+template <int DT, int K>
+static hipError_t go_norm(const NormLaunch& N, const TileShape& t) {
+    if (!tile_ok(t, N.rows, N.cols, Elem<DT>::SIZE, K)) return hipErrorInvalidValue;
+    const int64_t tiles = (N.rows + t.T - 1) / t.T;
     const uint64_t M = remainder_magic((uint64_t)N.cols);
     if (N.mode == kLayerNorm)
-        hipLaunchKernelGGL((k_norm_tile<DT, T, K, kLayerNorm>), dim3((unsigned)tiles), dim3(64), 0,
-                           N.stream, N.in, N.out, N.rows, N.cols, M, N.args);
+        hipLaunchKernelGGL((k_norm_tile<DT, K, kLayerNorm>), dim3((unsigned)tiles), dim3(64), 0,
+                           N.stream, N.in, N.out, N.rows, N.cols, M, t.T, tile_lg(t.T), t.lgrun,
+                           N.args);
     else
-        hipLaunchKernelGGL((k_norm_tile<DT, T, K, kRmsNorm>), dim3((unsigned)tiles), dim3(64), 0,
-                           N.stream, N.in, N.out, N.rows, N.cols, M, N.args);
+        hipLaunchKernelGGL((k_norm_tile<DT, K, kRmsNorm>), dim3((unsigned)tiles), dim3(64), 0,
+                           N.stream, N.in, N.out, N.rows, N.cols, M, t.T, tile_lg(t.T), t.lgrun,
+                           N.args);
     return hipGetLastError();
 }
 
-template <int T, int K>
-static hipError_t go_any(const Launch& L) {
+template <int K>
+static hipError_t go_any(const Launch& L, const TileShape& t) {
     switch (L.dtype) {
-        case kF32: return go<kF32, T, K>(L);
-        case kF16: return go<kF16, T, K>(L);
-        case kBF16: return go<kBF16, T, K>(L);
+        case kF32: return go<kF32, K>(L, t);
+        case kF16: return go<kF16, K>(L, t);
+        case kBF16: return go<kBF16, K>(L, t);
     }
     return hipErrorInvalidValue;
 }
 
-template <int T, int K>
-static hipError_t go_bwd_any(const BwdLaunch& B) {
+template <int K>
+static hipError_t go_bwd_any(const BwdLaunch& B, const TileShape& t) {
     switch (B.dtype) {
-        case kF32: return go_bwd<kF32, T, K>(B);
-        case kF16: return go_bwd<kF16, T, K>(B);
-        case kBF16: return go_bwd<kBF16, T, K>(B);
+        case kF32: return go_bwd<kF32, K>(B, t);
+        case kF16: return go_bwd<kF16, K>(B, t);
+        case kBF16: return go_bwd<kBF16, K>(B, t);
     }
     return hipErrorInvalidValue;
 }
 
-template <int T, int K>
-static hipError_t go_norm_any(const NormLaunch& N) {
+template <int K>
+static hipError_t go_norm_any(const NormLaunch& N, const TileShape& t) {
     switch (N.dtype) {
-        case kF32: return go_norm<kF32, T, K>(N);
-        case kF16: return go_norm<kF16, T, K>(N);
-        case kBF16: return go_norm<kBF16, T, K>(N);
+        case kF32: return go_norm<kF32, K>(N, t);
+        case kF16: return go_norm<kF16, K>(N, t);
+        case kBF16: return go_norm<kBF16, K>(N, t);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_tile_rows(const Launch& L, int variant) {
+hipError_t launch_tile_rows(const Launch& L, int variant, const TileShape& t) {
     int i = 0;
-#define RWS_CASE(t, k) \
-    if (variant == i) return go_any<t, k>(L); \
+#define RWS_CASE(k) \
+    if (variant == i) return go_any<k>(L, t); \
     ++i;
     RWS_TILE_ROWS_VARIANTS(RWS_CASE)
 #undef RWS_CASE
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_tile(const BwdLaunch& B, int variant) {
+hipError_t launch_bwd_tile(const BwdLaunch& B, int variant, const TileShape& t) {
     int i = 0;
-#define RWS_CASE(t, k) \
-    if (variant == i) return go_bwd_any<t, k>(B); \
+#define RWS_CASE(k) \
+    if (variant == i) return go_bwd_any<k>(B, t); \
     ++i;
     RWS_TILE_ROWS_VARIANTS(RWS_CASE)
 #undef RWS_CASE
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_norm_tile(const NormLaunch& N, int variant) {
+hipError_t launch_norm_tile(const NormLaunch& N, int variant, const TileShape& t) {
     int i = 0;
-#define RWS_CASE(t, k) \
-    if (variant == i) return go_norm_any<t, k>(N); \
+#define RWS_CASE(k) \
+    if (variant == i) return go_norm_any<k>(N, t); \
     ++i;
     RWS_TILE_ROWS_VARIANTS(RWS_CASE)
 #undef RWS_CASE

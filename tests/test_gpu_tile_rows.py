@@ -52,33 +52,53 @@ def _period(cols, es):
     return 16 // g
 
 
+def _rows_per_tile(cols, es, K):
+    """The tile height the library takes for K granules per lane: the largest
+    multiple of the rows' 16-byte period, at most 64, whose tile fits 64*K
+    granules (0 below 4 rows)."""
+    if cols * es > 1024 or cols < 16 // es:
+        return 0
+    p0 = _period(cols, es)
+    t = min(64, 64 * K * 16 // (cols * es))
+    t -= t % p0
+    return t if t >= 4 else 0
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_every_compiled_shape(dtype):
-    # for each (T, K): the longest rows it takes whose byte length is not a
-    # multiple of 16 (tiles filling its 64*K granule slots, boundaries inside
-    # granules), over three tiles and a partial fourth
+def test_every_variant_and_tile_height(dtype):
+    # every compiled K (granules per lane) over row lengths whose tiles range
+    # from 64 rows (one lane folds a row) down to 4 (sixteen lanes), row
+    # boundaries inside granules, three tiles and a partial fourth
     es = ES[dtype]
     vec = 16 // es
-    probe = torch.empty(64, vec, dtype=torch.float32 if es == 4 else torch.float16,
-                        device="cuda")
     n = rws.softmax_variant_count(TILE)
-    assert n >= 9
+    assert n == 4
+    lengths = [vec + 1, 13, 25, 33, 60, 100, 250 if es == 2 else 125, 500 if es == 2 else 250]
+    seen = set()
     for v in range(n):
-        d = _describe(4, vec, dtype, probe, probe, v)
-        T = int(d.split("T=")[1].split(",")[0])
-        K = int(d.split("K=")[1].split(">")[0])
-        cols = max(c for c in range(vec, 64 * K * 16 // (T * es) + 1)
-                   if (c * es) % 16 and T % _period(c, es) == 0)
-        rows = 3 * T + T // 2 + 1
-        g = np.random.Generator(np.random.PCG64(700 + v * 31 + cols))
-        x, xs = to_device(g.normal(0.0, 4.0, (rows, cols)), dtype)
-        y = empty_like_at(x)
-        desc = _describe(rows, cols, dtype, x, y, v)
-        assert f"T={T},K={K}" in desc, desc
-        _run_variant(x, y, v)
-        torch.cuda.synchronize()
-        print(f"{desc} rows={rows} cols={cols}", flush=True)
-        check(y.double().cpu().numpy(), oracle.safe_softmax(xs), dtype, f"{desc} cols={cols}")
+        K = v + 1
+        for cols in lengths:
+            T = _rows_per_tile(cols, es, K)
+            rows = 3 * max(T, 4) + max(T, 4) // 2 + 1
+            g = np.random.Generator(np.random.PCG64(700 + v * 31 + cols))
+            x, xs = to_device(g.normal(0.0, 4.0, (rows, cols)), dtype)
+            y = empty_like_at(x)
+            if T == 0:
+                st = rws.softmax_fwd_variant(x.data_ptr(), y.data_ptr(), rows, cols,
+                                             rws.dtype_code(x.dtype),
+                                             torch.cuda.current_stream().cuda_stream, TILE, v)
+                assert st == rws.RWS_ERR_UNSUPPORTED_SHAPE, (cols, K)
+                continue
+            desc = _describe(rows, cols, dtype, x, y, v)
+            assert f"T={T},K={K}>" in desc, (desc, T, K)
+            seen.add(T)
+            _run_variant(x, y, v)
+            torch.cuda.synchronize()
+            print(f"{desc} rows={rows} cols={cols}", flush=True)
+            check(y.double().cpu().numpy(), oracle.safe_softmax(xs), dtype, f"{desc} cols={cols}")
+    # heights with 1, 2, 4, 8 and 16 lanes per row all ran
+    assert any(t > 32 for t in seen) and any(16 < t <= 32 for t in seen)
+    assert any(8 < t <= 16 for t in seen) and any(4 < t <= 8 for t in seen) and 4 in seen
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
