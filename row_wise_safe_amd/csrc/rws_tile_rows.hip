@@ -17,15 +17,19 @@
 namespace rws {
 
 // Maxima of granule values v over its first row's elements (e < split) and
-// over the next row's, each as a tree of three-operand maxima.
+// over the next row's, each as a tree of three-operand maxima.  `ninf` is
+// -inf held in a register the compiler cannot see through: with the
+// constant, it rewrites max(x, e < split ? v : -inf) into a select of two
+// maxima per element, which the trees avoid.
 template <int VEC>
-__device__ inline void split_max(const float (&v)[VEC], int split, float& ma, float& mb) {
+__device__ inline void split_max(const float (&v)[VEC], int split, float ninf, float& ma,
+                                 float& mb) {
     float a[VEC], b[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
         const bool in_a = e < split;
-        a[e] = in_a ? v[e] : kNegInf;
-        b[e] = in_a ? kNegInf : v[e];
+        a[e] = in_a ? v[e] : ninf;
+        b[e] = in_a ? ninf : v[e];
     }
     if (VEC == 8) {
         ma = vmax(vmax(vmax(a[0], a[1]), a[2]), vmax(vmax(a[3], a[4]), vmax(vmax(a[5], a[6]), a[7])));
@@ -33,6 +37,44 @@ __device__ inline void split_max(const float (&v)[VEC], int split, float& ma, fl
     } else {
         ma = vmax(vmax(vmax(a[0], a[1]), a[2]), a[VEC - 1]);
         mb = vmax(vmax(vmax(b[0], b[1]), b[2]), b[VEC - 1]);
+    }
+}
+
+// The exponentials of a tile against each element's row maximum (one exp2
+// per element: the FMA offset of the element's row is selected first) and
+// their row partials.  EXACT: some row of the tile takes RowExp's exact form
+// (|max| above 2.9e6, or +inf / NaN), so every element decides per row
+// which form it takes; the branch is uniform over the wave.
+template <int DT, int K>
+__device__ inline void tile_exp(float (&v)[K][Elem<DT>::VEC], const TileSlots<DT, K>& S,
+                                const float* row_max, float (&pa)[K], float (&pb)[K]) {
+    constexpr int VEC = Elem<DT>::VEC;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        const RowExp ea(row_max[S.ra[i]]), eb(row_max[S.rb(i)]);
+        const int sp = S.split_pass(i);
+        pa[i] = 0.0f;
+        pb[i] = 0.0f;
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(ea.big || eb.big) != 0, 0)) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const bool in_a = e < sp;
+                const float y = in_a ? ea.one(v[i][e]) : eb.one(v[i][e]);
+                v[i][e] = y;
+                pa[i] += in_a ? y : 0.0f;
+                pb[i] += in_a ? 0.0f : y;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const bool in_a = e < sp;
+                const float y = __builtin_amdgcn_exp2f(
+                    __builtin_fmaf(v[i][e], kLog2e, in_a ? ea.negc : eb.negc));
+                v[i][e] = y;
+                pa[i] += in_a ? y : 0.0f;
+                pb[i] += in_a ? 0.0f : y;
+            }
+        }
     }
 }
 
@@ -54,47 +96,20 @@ __device__ inline void tile_softmax(const char* __restrict__ gin, char* __restri
     for (int i = 0; i < K; ++i) raw[i] = tile_load<DT, FULL>(gin, S.granule(i), S.nel);
 
     // row maxima
+    float ninf = kNegInf;
+    asm volatile("" : "+v"(ninf));
     float v[K][VEC];
     float pa[K], pb[K];
 #pragma unroll
     for (int i = 0; i < K; ++i) {
         Elem<DT>::widen(raw[i], v[i]);
-        split_max<VEC>(v[i], S.split_pass(i), pa[i], pb[i]);
+        split_max<VEC>(v[i], S.split_pass(i), ninf, pa[i], pb[i]);
     }
     tile_fold<K, OpMax>(pa, pb, part_a, part_b, row_max, cols, nrows, lg, VEC, kNegInf,
                         [](float m) { return m; });
 
-    // exponentials against each element's row maximum (one exp2 per element:
-    // the FMA offset of the element's row is selected first; a granule with
-    // a row whose maximum takes the exact form -- |max| above 2.9e6 or
-    // +inf -- takes it per element), row sums
-#pragma unroll
-    for (int i = 0; i < K; ++i) {
-        const RowExp ea(row_max[S.ra[i]]), eb(row_max[S.rb(i)]);
-        const int sp = S.split_pass(i);
-        pa[i] = 0.0f;
-        pb[i] = 0.0f;
-        if (__builtin_expect(ea.big || eb.big, 0)) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const bool in_a = e < sp;
-                const float y = in_a ? ea.one(v[i][e]) : eb.one(v[i][e]);
-                v[i][e] = y;
-                pa[i] += in_a ? y : 0.0f;
-                pb[i] += in_a ? 0.0f : y;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const bool in_a = e < sp;
-                const float y = __builtin_amdgcn_exp2f(
-                    __builtin_fmaf(v[i][e], kLog2e, in_a ? ea.negc : eb.negc));
-                v[i][e] = y;
-                pa[i] += in_a ? y : 0.0f;
-                pb[i] += in_a ? 0.0f : y;
-            }
-        }
-    }
+    // exponentials and row sums
+    tile_exp<DT, K>(v, S, row_max, pa, pb);
     tile_fold<K, OpSum>(pa, pb, part_a, part_b, row_rcp, cols, nrows, lg, VEC, 0.0f,
                         [](float s) { return __builtin_amdgcn_rcpf(s); });
 
