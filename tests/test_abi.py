@@ -457,3 +457,61 @@ def _try_describe(*args):
         return rws.softmax_describe_variant(*args)
     except rws.SoftmaxError:
         return ""
+
+
+def _tile_choice(cols, es):
+    """The tile the dispatcher takes for rows of cols elements of es bytes,
+    restated from its rule: for each K (granules per lane) the largest
+    multiple of the rows' 16-byte period, at most 64, whose tile fits 64*K
+    granules; then the K with the fewest slots per row (64*K / T), the
+    larger tile at equal fill."""
+    rb = cols * es
+    if cols < 16 // es or rb > 1024:
+        return None
+    g = 16
+    while rb % g:
+        g //= 2
+    p0 = 16 // g
+    best = None
+    for K in (1, 2, 3, 4):
+        T = min(64, 64 * K * 16 // rb)
+        T -= T % p0
+        if T < 4:
+            continue
+        if best is None or K * best[0] < best[1] * T or (K * best[0] == best[1] * T and T > best[0]):
+            best = (T, K)
+    return best
+
+
+@pytest.mark.parametrize("dtype,es", [(rws.RWS_F16, 2), (rws.RWS_BF16, 2), (rws.RWS_F32, 4)])
+def test_tile_height_choice(lib, dtype, es):
+    # every row length the tile form takes, plain softmax, backward and the
+    # normalisations: the height and K follow the rule, and the tile starts
+    # on a 16-byte boundary and holds at most 64*K granules
+    seen = set()
+    for cols in range(16 // es, 1024 // es + 1):
+        rb = cols * es
+        want = _tile_choice(cols, es)
+        fits = want is not None and rb % 128 != 0 and (rb % 16 != 0 or rb > 128)
+        desc = rws.softmax_describe_launch(4096, cols, dtype, 256, 512)
+        bwd = rws.softmax_bwd_describe_launch(4096, cols, dtype, 256, 512)
+        norm = rws.norm_describe_launch(4096, cols, dtype, 256, 512)
+        if not fits:
+            assert not desc.startswith("tile_rows<"), (cols, desc)
+            continue
+        T, K = want
+        assert (T * rb) % 16 == 0 and T * rb // 16 <= 64 * K and 4 <= T <= 64
+        tag = f"T={T},K={K}>"
+        assert desc.startswith("tile_rows<") and tag in desc, (cols, desc, want)
+        assert bwd.startswith("bwd_tile<") and tag in bwd, (cols, bwd, want)
+        assert norm.startswith("norm_tile<") and tag in norm, (cols, norm, want)
+        seen.add((T > 32, K))
+    # short rows take one lane per row, and every K is chosen somewhere
+    assert {k for _, k in seen} == {1, 2, 3, 4} and any(big for big, _ in seen)
+
+
+def test_tile_needs_enough_rows_and_aligned_pointers(lib):
+    assert rws.softmax_describe_launch(64, 250, rws.RWS_F16, 256, 512).startswith("tile_rows<")
+    assert not rws.softmax_describe_launch(63, 250, rws.RWS_F16, 256, 512).startswith("tile_rows<")
+    assert not rws.softmax_describe_launch(4096, 250, rws.RWS_F16, 258, 512).startswith("tile_rows<")
+    assert not rws.softmax_describe_launch(4096, 250, rws.RWS_F16, 256, 520).startswith("tile_rows<")
