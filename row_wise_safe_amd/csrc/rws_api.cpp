@@ -147,14 +147,14 @@ int softmax_wave_wa(const rws::WaveRowVariant& v) { return rws::softmax_window_a
 constexpr int64_t kTileMaxRowBytes = 1024;
 constexpr int64_t kTileMinRows = 64;
 
-int pick_tile_rows(int64_t cols, int es, int forced_variant, int* T_out);
+int pick_tile_rows(int64_t rows, int64_t cols, int es, int forced_variant, int* T_out);
 
 bool tile_rows_fits(int64_t rows, int64_t cols, int dtype, const void* in, const void* out) {
     const int es = elem_size(dtype);
     const int64_t rb = cols * es;
     return rows >= kTileMinRows && rb % 128 != 0 && (rb % 16 != 0 || rb > 128) &&
            rb <= kTileMaxRowBytes && (uintptr_t)in % 16 == 0 && (uintptr_t)out % 16 == 0 &&
-           pick_tile_rows(cols, es, -1, nullptr) >= 0;
+           pick_tile_rows(rows, cols, es, -1, nullptr) >= 0;
 }
 
 // Rows per tile with K granules per lane for rows of `cols` elements of size
@@ -172,12 +172,36 @@ int tile_rows_per_tile(int64_t cols, int es, int K) {
     return T >= 4 ? (int)T : 0;
 }
 
-// tile_rows: the variant (granules per lane K) for rows of `cols` elements of
-// size es, or -1; its rows per tile in *T_out.  Every slot costs the same
-// instructions whether the tile fills it or not, so the choice is the K with
-// the fewest slots per row, 64 K / T (the fullest tiles); at equal fill the
-// larger tile (fewer waves).  forced_variant >= 0 asks for that K.
-int pick_tile_rows(int64_t cols, int es, int forced_variant, int* T_out) {
+// tile_rows: the variant (granules per lane K) for `rows` rows of `cols`
+// elements of size es, or -1; its rows per tile in *T_out.  Every slot costs
+// the same instructions whether the tile fills it or not, so the cost of a K
+// is its slots per row, 64 K / T, weighted by what a K costs besides.  Up to
+// kTileSmallBytes per direction the larger K cost more: more registers per
+// lane (K = 4: 95 VGPRs, 5 waves per SIMD, against 8 at K = 2) and longer
+// waves, so a longer tail in a launch of a few rounds of waves; at K = 1 the
+// two row reductions work on one granule per lane.  Weights from sweeps of
+// every feasible K on MI355X (fp16 unless noted, 63-66 MB per direction, us
+// per call for K = 1/2/3/4, fill in parentheses): [262144,120] 26.6 / 23.9
+// / 24.1 / 24.6 (0.94 / 0.94 / 0.94 / 1.00); [524288,60] 26.6 / 24.0 / 24.0
+// / 24.8 (same fills); [1000000,33] 44.1 / 28.7 / 26.7 / 25.9 (0.52 / 0.77
+// / 0.86 / 0.90); [425000,77] - / 32.9 / 26.7 / 26.2 (- / 0.60 / 0.80 /
+// 0.90); [727000,45] 33.8 / 29.5 / 25.0 / 26.5 (0.70 / 0.70 / 0.94 / 0.88);
+// [131072,250] - / 24.4 / 29.1 / 24.6 (- / 0.98 / 0.65 / 0.98); fp32
+// [131072,125] - / 23.3 / 23.6 / 24.7 (- / 0.98 / 0.65 / 0.98); backward
+// [262144,120] 31.1 us (K = 2) against 33.2 (K = 4), RMSNorm 21.8 against
+// 24.8.  Larger launches run many rounds of waves and K = 4 leads at equal
+// fill: [1048576,100] 75.1 (K = 2) against 73.4 (K = 4), [1048576,120] 88.0
+// against 86.8, [524288,250] 89.7 against 87.1, backward [1048576,100]
+// 103.1 against 100.7, LayerNorm 75.1 against 71.9; there only K = 1 carries
+// a weight and the larger tile wins at equal cost.  forced_variant >= 0
+// asks for that K.
+constexpr int64_t kTileSmallBytes = (int64_t)1 << 27;
+
+int pick_tile_rows(int64_t rows, int64_t cols, int es, int forced_variant, int* T_out) {
+    static constexpr int kWeightSmall[5] = {0, 130, 100, 102, 107};  // percent, by K
+    static constexpr int kWeightLarge[5] = {0, 130, 100, 100, 100};
+    const bool small = rows * cols * es <= kTileSmallBytes;
+    const int* w = small ? kWeightSmall : kWeightLarge;
     int best = -1, best_t = 0;
     for (int i = 0; i < rws::kNumTileRows; ++i) {
         if (forced_variant >= 0 && i != forced_variant) continue;
@@ -185,8 +209,12 @@ int pick_tile_rows(int64_t cols, int es, int forced_variant, int* T_out) {
         const int T = tile_rows_per_tile(cols, es, K);
         if (T == 0) continue;
         if (best >= 0) {
-            const int64_t lhs = (int64_t)K * best_t, rhs = (int64_t)rws::kTileRows[best].K * T;
-            if (lhs > rhs || (lhs == rhs && T <= best_t)) continue;
+            // cost K * w(K) / T against the best so far; at equal cost the
+            // smaller K for small launches, the larger tile for large ones
+            const int Kb = rws::kTileRows[best].K;
+            const int64_t lhs = (int64_t)K * w[K] * best_t;
+            const int64_t rhs = (int64_t)Kb * w[Kb] * T;
+            if (lhs > rhs || (lhs == rhs && (small || T <= best_t))) continue;
         }
         best = i;
         best_t = T;
@@ -535,10 +563,10 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
             if ((uintptr_t)in % 16 || (uintptr_t)out % 16)
                 return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows needs 16-byte aligned in and out");
             int T = 0;
-            p->variant = pick_tile_rows(cols, es, -1, &T);
+            p->variant = pick_tile_rows(rows, cols, es, -1, &T);
             if (forced_variant >= 0) {
                 if (forced_variant >= rws::kNumTileRows) return bad_variant(rws::kNumTileRows);
-                if (pick_tile_rows(cols, es, forced_variant, &T) < 0) return bad_variant(rws::kNumTileRows);
+                if (pick_tile_rows(rows, cols, es, forced_variant, &T) < 0) return bad_variant(rws::kNumTileRows);
                 p->variant = forced_variant;
             }
             if (p->variant < 0)
@@ -1301,7 +1329,7 @@ static int plan_bwd(int64_t rows, int64_t cols, int dtype, const void* y, const 
         if (!dy16 || (uintptr_t)y % 16 || (uintptr_t)dx % 16)
             return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows needs 16-byte aligned y, dy and dx");
         int T = 0;
-        const int v = pick_tile_rows(cols, elem_size(dtype), -1, &T);
+        const int v = pick_tile_rows(rows, cols, elem_size(dtype), -1, &T);
         if (v < 0)
             return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows takes rows of one granule to 1024 bytes");
         bp->family = family;
@@ -1523,7 +1551,7 @@ static int plan_norm(int64_t rows, int64_t cols, int dtype, const void* in, cons
         if ((uintptr_t)in % 16 || (uintptr_t)out % 16)
             return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows needs 16-byte aligned in and out");
         int T = 0;
-        const int v = pick_tile_rows(cols, elem_size(dtype), -1, &T);
+        const int v = pick_tile_rows(rows, cols, elem_size(dtype), -1, &T);
         if (v < 0)
             return fail(RWS_ERR_UNSUPPORTED_SHAPE, "tile_rows takes rows of one granule to 1024 bytes");
         np->family = family;
