@@ -153,3 +153,29 @@ def test_tile_rows_form_in_place_and_refusals():
     _run(y2, dy2, dx2, "auto")
     torch.cuda.synchronize()
     _check(dx2.double().cpu().numpy(), ys2, gs2, "f16", "auto, dy unaligned")
+
+
+@pytest.mark.parametrize("dtype,rows,cols", [("f16", 1000003, 33), ("f16", 1048583, 100),
+                                             ("bf16", 262147, 120)])
+def test_tile_rows_form_large_launch_sampled_rows(dtype, rows, cols):
+    # the dispatcher's tile at full size: sampled rows (both ends, the
+    # partial last tile among them, and seeded random rows) against the oracle
+    from gpu_util import TORCH_DTYPE
+    gen = torch.Generator(device="cuda").manual_seed(rows * 5 + cols)
+    tdt = TORCH_DTYPE[dtype]
+    y = torch.softmax(torch.randn(rows, cols, generator=gen, device="cuda") * 2.0, dim=1).to(tdt)
+    dy = torch.randn(rows, cols, generator=gen, device="cuda").to(tdt)
+    dx = torch.empty_like(y)
+    desc = rws.softmax_bwd_describe_launch(rows, cols, rws.dtype_code(tdt), y.data_ptr(),
+                                           dx.data_ptr())
+    assert desc.startswith("bwd_tile<"), desc
+    rws.softmax_backward(y, dy, out=dx)
+    torch.cuda.synchronize()
+    print(desc, flush=True)
+    rng = np.random.Generator(np.random.PCG64(rows))
+    idx = np.unique(np.concatenate([np.arange(200), np.arange(rows - 200, rows),
+                                    rng.integers(0, rows, 600)]))
+    ti = torch.from_numpy(idx).cuda()
+    ys = y.index_select(0, ti).double().cpu().numpy()
+    gs = dy.index_select(0, ti).double().cpu().numpy()
+    _check(dx.index_select(0, ti).double().cpu().numpy(), ys, gs, dtype, f"{desc} sampled rows")

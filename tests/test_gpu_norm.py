@@ -341,3 +341,32 @@ def test_tile_rows_form_affine_and_constant_rows():
     y = rws.layer_norm(c, 1e-5, kernel="tile_rows")
     torch.cuda.synchronize()
     assert torch.all(y == 0)
+
+
+@pytest.mark.parametrize("mode", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("dtype,rows,cols", [("f16", 1000003, 33), ("f16", 1048583, 100),
+                                             ("bf16", 262147, 120)])
+def test_tile_rows_form_large_launch_sampled_rows(mode, dtype, rows, cols):
+    # the dispatcher's tile at full size with the statistics outputs: sampled
+    # rows (both ends, the partial last tile among them, and seeded random
+    # rows) against the oracle
+    from gpu_util import TORCH_DTYPE
+    gen = torch.Generator(device="cuda").manual_seed(rows * 3 + cols)
+    tdt = TORCH_DTYPE[dtype]
+    x = (torch.randn(rows, cols, generator=gen, device="cuda") * 2.0 + 0.5).to(tdt)
+    out = torch.empty_like(x)
+    mean = torch.empty(rows, dtype=torch.float32, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    desc = rws.norm_describe_launch(rows, cols, rws.dtype_code(tdt), x.data_ptr(), out.data_ptr())
+    assert desc.startswith("norm_tile<"), desc
+    _call(mode, x, out, 1e-5, None, None, mean, rstd, "auto")
+    print(desc, flush=True)
+    rng = np.random.Generator(np.random.PCG64(rows + 1))
+    idx = np.unique(np.concatenate([np.arange(200), np.arange(rows - 200, rows),
+                                    rng.integers(0, rows, 600)]))
+    ti = torch.from_numpy(idx).cuda()
+    xs = x.index_select(0, ti).double().cpu().numpy()
+    _check(mode, dtype, out.index_select(0, ti).double().cpu().numpy(), xs, 1e-5, None, None,
+           f"{mode} {desc} sampled rows",
+           mean=mean.index_select(0, ti).double().cpu().numpy() if mode == "layernorm" else None,
+           rstd=rstd.index_select(0, ti).double().cpu().numpy())

@@ -179,3 +179,39 @@ def test_refusals():
     desc = rws.softmax_describe_launch(1000, 100, rws.RWS_F16, x.data_ptr(), x.data_ptr(),
                                        masked=True)
     assert desc.startswith("wave_row<"), desc
+
+
+def _sample_rows(rows, seed, n_ends=200, n_random=600):
+    """Both ends of the tensor (the first tiles, and the partial last tile)
+    and seeded random rows in between."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    idx = np.concatenate([np.arange(min(rows, n_ends)), np.arange(max(0, rows - n_ends), rows),
+                          rng.integers(0, rows, n_random)])
+    return np.unique(idx)
+
+
+@pytest.mark.parametrize("dtype,rows,cols", [("f16", 1000003, 33), ("f16", 1048583, 100),
+                                             ("bf16", 262147, 120), ("f32", 131075, 125)])
+def test_large_launch_sampled_rows(dtype, rows, cols):
+    # the dispatcher's tile at full size (tens of thousands of tiles in XCD
+    # runs, a partial last tile): every row sum on the device, sampled rows
+    # against the oracle row by row
+    from gpu_util import TORCH_DTYPE
+    from tolerance import TOL
+    gen = torch.Generator(device="cuda").manual_seed(rows * 7 + cols)
+    x = (torch.randn(rows, cols, generator=gen, device="cuda") * 4.0).to(TORCH_DTYPE[dtype])
+    y = torch.empty_like(x)
+    desc = rws.softmax_describe_launch(rows, cols, rws.dtype_code(x.dtype), x.data_ptr(),
+                                       y.data_ptr())
+    assert desc.startswith("tile_rows<"), desc
+    rws.softmax(x, out=y)
+    torch.cuda.synchronize()
+    print(desc, flush=True)
+    assert torch.isfinite(y).all().item()
+    dev = (y.double().sum(dim=1) - 1.0).abs().max().item()
+    assert dev <= TOL[dtype]["rowsum"], f"{desc}: row sum off by {dev:.3e}"
+    idx = _sample_rows(rows, rows + cols)
+    ti = torch.from_numpy(idx).cuda()
+    xs = x.index_select(0, ti).double().cpu().numpy()
+    check(y.index_select(0, ti).double().cpu().numpy(), oracle.safe_softmax(xs), dtype,
+          f"{desc} sampled rows")
