@@ -42,9 +42,11 @@ __device__ inline void split_max(const float (&v)[VEC], int split, float ninf, f
 
 // The exponentials of a tile against each element's row maximum (one exp2
 // per element: the FMA offset of the element's row is selected first) and
-// their row partials.  EXACT: some row of the tile takes RowExp's exact form
-// (|max| above 2.9e6, or +inf / NaN), so every element decides per row
-// which form it takes; the branch is uniform over the wave.
+// their row partials.  When a granule slot of any lane holds a row whose
+// maximum takes RowExp's exact form (|max| above 2.9e6, or +inf / NaN), the
+// whole wave takes, for that slot, the path where every element picks its
+// row's form (a ballot keeps the branch uniform over the wave; both paths
+// give the same value for a row on the FMA form).
 template <int DT, int K>
 __device__ inline void tile_exp(float (&v)[K][Elem<DT>::VEC], const TileSlots<DT, K>& S,
                                 const float* row_max, float (&pa)[K], float (&pb)[K]) {
