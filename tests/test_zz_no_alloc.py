@@ -98,12 +98,16 @@ def test_rows_in_batches_that_fit_the_scratch():
 
 
 def test_plain_forward_shapes_match_softmax_fwd():
-    x, xs = to_device(np.random.Generator(np.random.PCG64(910)).normal(0, 8, (4096, 512)), "f16")
-    out = _noalloc(x, torch.empty_like(x))
-    ref_out = _existing(x, "auto")
-    torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
-    check(out.double().cpu().numpy(), oracle.safe_softmax(xs), "f16", "noalloc wave_row")
+    # a line-aligned shape (wave_row) and one of short unaligned rows (tile_rows)
+    for seed, (rows, cols) in ((910, (4096, 512)), (911, (1000, 250))):
+        x, xs = to_device(np.random.Generator(np.random.PCG64(seed)).normal(0, 8, (rows, cols)),
+                          "f16")
+        out = _noalloc(x, torch.empty_like(x))
+        ref_out = _existing(x, "auto")
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+        check(out.double().cpu().numpy(), oracle.safe_softmax(xs), "f16",
+              f"noalloc [{rows},{cols}]")
 
 
 def test_rows_longer_than_the_scratch_are_rejected():
