@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import row_wise_safe_amd as rws
-from gpu_util import empty_like_at, have_gpu, to_device
+from gpu_util import empty_like_at, have_gpu, tile_supports, to_device
 from tolerance import check
 
 pytestmark = [pytest.mark.gpu,
@@ -215,3 +215,24 @@ def test_large_launch_sampled_rows(dtype, rows, cols):
     xs = x.index_select(0, ti).double().cpu().numpy()
     check(y.index_select(0, ti).double().cpu().numpy(), oracle.safe_softmax(xs), dtype,
           f"{desc} sampled rows")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_fewer_rows_than_one_tile(dtype):
+    # forced onto tiles of 12 to 56 rows, tensors of 1..17 rows: mostly a
+    # single partial tile, the tensor ending inside its last granule
+    es = ES[dtype]
+    for cols in (9, 33, 77):
+        if not tile_supports(cols, dtype):
+            continue
+        for rows in (1, 2, 5, 17):
+            g = np.random.Generator(np.random.PCG64(rows * 101 + cols))
+            x, xs = to_device(g.normal(0.0, 3.0, (rows, cols)), dtype)
+            y = empty_like_at(x)
+            desc = rws.softmax_describe_launch(rows, cols, rws.dtype_code(x.dtype), x.data_ptr(),
+                                               y.data_ptr(), TILE)
+            assert desc.startswith("tile_rows<"), desc
+            rws.softmax(x, out=y, kernel="tile_rows")
+            torch.cuda.synchronize()
+            check(y.double().cpu().numpy(), oracle.safe_softmax(xs), dtype,
+                  f"{desc} rows={rows} es={es}")
