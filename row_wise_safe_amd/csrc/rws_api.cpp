@@ -193,8 +193,9 @@ int tile_rows_per_tile(int64_t cols, int es, int K) {
 // fill: [1048576,100] 75.1 (K = 2) against 73.4 (K = 4), [1048576,120] 88.0
 // against 86.8, [524288,250] 89.7 against 87.1, backward [1048576,100]
 // 103.1 against 100.7, LayerNorm 75.1 against 71.9; there only K = 1 carries
-// a weight and the larger tile wins at equal cost.  forced_variant >= 0
-// asks for that K.
+// a weight and the larger tile wins at equal cost.  The threshold lies
+// between the sizes measured (63-66 MB and 210-262 MB per direction).
+// forced_variant >= 0 asks for that K.
 constexpr int64_t kTileSmallBytes = (int64_t)1 << 27;
 
 int pick_tile_rows(int64_t rows, int64_t cols, int es, int forced_variant, int* T_out) {
