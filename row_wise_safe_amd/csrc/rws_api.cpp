@@ -193,8 +193,10 @@ int tile_rows_per_tile(int64_t cols, int es, int K) {
 // fill: [1048576,100] 75.1 (K = 2) against 73.4 (K = 4), [1048576,120] 88.0
 // against 86.8, [524288,250] 89.7 against 87.1, backward [1048576,100]
 // 103.1 against 100.7, LayerNorm 75.1 against 71.9; there only K = 1 carries
-// a weight and the larger tile wins at equal cost.  The threshold lies
-// between the sizes measured (63-66 MB and 210-262 MB per direction).
+// a weight and the larger tile wins at equal cost.  In between the two are
+// within 2 % either way ([393216,120] 34.9 against 35.6, [524288,120] 45.7
+// both, [196608,250] 36.0 against 35.3, [262144,250] 46.5 against 45.8,
+// [786432,100] 57.3 against 56.1), so the threshold is a round size there.
 // forced_variant >= 0 asks for that K.
 constexpr int64_t kTileSmallBytes = (int64_t)1 << 27;
 
