@@ -165,8 +165,7 @@ enum {
                                  granule to 1024 bytes, and a tile of at
                                  least 4 rows (RWS_ERR_UNSUPPORTED_SHAPE
                                  otherwise).  The dispatcher's choice for
-                                 many such rows (plain softmax; the masked
-                                 form has none) */
+                                 many such rows (plain and masked) */
 };
 
 /*
@@ -232,7 +231,10 @@ int softmax_fwd_noalloc(const void *in, void *out, int64_t rows, int64_t cols, i
  *               (r mod q) and sees keys j <= (r mod q) + cols - q (the last
  *               query sees every key)
  *   kernel_id : RWS_KERNEL_AUTO, or RWS_KERNEL_WAVE_ROW / BLOCK_ONEPASS /
- *               TWO_PASS (no split-k form; RWS_ERR_UNSUPPORTED_SHAPE)
+ *               TWO_PASS / TILE_ROWS (no split-k form;
+ *               RWS_ERR_UNSUPPORTED_SHAPE); the dispatcher takes TILE_ROWS
+ *               for many short rows that are not line-aligned, as for
+ *               softmax_fwd
  * A row whose every entry ends up -inf becomes NaN (0/0), as the definition
  * gives.  Other arguments, layout, streams and errors as softmax_fwd.
  */

@@ -529,7 +529,7 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
         const bool parks = onepass_fits && rws::kOnepass[ov].kl > 0;
         const bool splitk_rows =
             !onepass_fits || 2 * rows < cus || (2 * rows <= cus && parks);
-        if (!masked && tile_rows_fits(rows, cols, dtype, in, out)) {
+        if (tile_rows_fits(rows, cols, dtype, in, out)) {
             family = RWS_KERNEL_TILE_ROWS;
         } else if (pick_wave_row(g, masked, 1) >= 0) {
             family = RWS_KERNEL_WAVE_ROW;
@@ -547,16 +547,14 @@ int plan_launch_uncached(int64_t rows, int64_t cols, int dtype, const void* in, 
         }
     }
     if (masked && kernel_id == RWS_KERNEL_AUTO) {
-        // the masked forms exist for wave_row, register-only block_onepass
-        // and two_pass; long rows with few rows go to two_pass
+        // the masked forms exist for tile_rows, wave_row, register-only
+        // block_onepass and two_pass; long rows with few rows go to two_pass
         if (is_splitk(family)) family = RWS_KERNEL_TWO_PASS;
         if (family == RWS_KERNEL_BLOCK_ONEPASS && pick_onepass(wline, rows, cus, true, g.a128, dtype) < 0)
             family = RWS_KERNEL_TWO_PASS;
     }
     if (masked && is_splitk(family))
         return fail(RWS_ERR_UNSUPPORTED_SHAPE, "the masked form has no split-k kernel");
-    if (masked && family == RWS_KERNEL_TILE_ROWS)
-        return fail(RWS_ERR_UNSUPPORTED_SHAPE, "the masked form has no tile_rows kernel");
     p->family = family;
     p->aligned = g.a128;
     p->window = wline;
@@ -1099,6 +1097,10 @@ int run(const void* in, void* out, int64_t rows, int64_t cols, int dtype, void* 
                     e = rws::launch_block_onepass_masked(L, p.variant, M);
                     break;
                 case RWS_KERNEL_TWO_PASS: e = rws::launch_two_pass_masked(L, p.variant, M); break;
+                case RWS_KERNEL_TILE_ROWS:
+                    e = rws::launch_tile_rows_masked(L, p.variant, rws::TileShape{p.tile_t, p.lgrun},
+                                                     M);
+                    break;
                 default: e = hipErrorInvalidValue;
             }
         } else {

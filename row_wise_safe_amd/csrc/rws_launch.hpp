@@ -142,6 +142,9 @@ hipError_t launch_fill_words(uint64_t* p, int64_t n, uint64_t v, hipStream_t str
 hipError_t launch_wave_row_masked(const Launch& L, int variant, const MaskArgs& M);
 hipError_t launch_block_onepass_masked(const Launch& L, int variant, const MaskArgs& M);
 hipError_t launch_two_pass_masked(const Launch& L, int variant, const MaskArgs& M);
+// The masked form of tile_rows (kTileRows variants, as launch_tile_rows).
+hipError_t launch_tile_rows_masked(const Launch& L, int variant, const TileShape& t,
+                                  const MaskArgs& M);
 // Softmax backward: dx = y * (dy - sum(dy * y)) per row.
 struct BwdLaunch {
     const void* y;

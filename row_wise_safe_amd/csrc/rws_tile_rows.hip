@@ -83,30 +83,24 @@ __device__ inline void tile_exp(float (&v)[K][Elem<DT>::VEC], const TileSlots<DT
 // ---------------------------------------------------------------------------
 // softmax
 // ---------------------------------------------------------------------------
-// Slots past the tile (and, in the tensor's last tile, elements past its
-// end) hold zeros; their partials are never folded into a row and they are
-// never stored.
+// The row-wise softmax of a tile widened into v: row maxima, the
+// exponentials and row sums, the scaling, the stores.  Slots past the tile
+// (and, in the tensor's last tile, elements past its end) may hold any
+// value: their partials are never folded into a row and they are never
+// stored.
 template <int DT, int K, bool FULL>
-__device__ inline void tile_softmax(const char* __restrict__ gin, char* __restrict__ gout,
-                                    int nrows, int cols, int lg, uint64_t cmagic, float* part_a,
-                                    float* part_b, float* row_max, float* row_rcp) {
+__device__ inline void tile_softmax_rows(float (&v)[K][Elem<DT>::VEC], const TileSlots<DT, K>& S,
+                                         char* __restrict__ gout, int nrows, int cols, int lg,
+                                         float* part_a, float* part_b, float* row_max,
+                                         float* row_rcp) {
     constexpr int VEC = Elem<DT>::VEC;
     static_assert(VEC == 8 || VEC == 4, "granule of 4 or 8 elements");
-    const TileSlots<DT, K> S(nrows, cols, cmagic);
-    u32x4 raw[K];
-#pragma unroll
-    for (int i = 0; i < K; ++i) raw[i] = tile_load<DT, FULL>(gin, S.granule(i), S.nel);
-
     // row maxima
     float ninf = kNegInf;
     asm volatile("" : "+v"(ninf));
-    float v[K][VEC];
     float pa[K], pb[K];
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-        Elem<DT>::widen(raw[i], v[i]);
-        split_max<VEC>(v[i], S.split_pass(i), ninf, pa[i], pb[i]);
-    }
+    for (int i = 0; i < K; ++i) split_max<VEC>(v[i], S.split_pass(i), ninf, pa[i], pb[i]);
     tile_fold<K, OpMax>(pa, pb, part_a, part_b, row_max, cols, nrows, lg, VEC, kNegInf,
                         [](float m) { return m; });
 
@@ -124,6 +118,224 @@ __device__ inline void tile_softmax(const char* __restrict__ gin, char* __restri
         for (int e = 0; e < VEC; ++e) v[i][e] *= e < sp ? qa : qb;
         tile_store<DT, FULL>(gout, S.granule(i), S.nel, v[i]);
     }
+}
+
+template <int DT, int K, bool FULL>
+__device__ inline void tile_softmax(const char* __restrict__ gin, char* __restrict__ gout,
+                                    int nrows, int cols, int lg, uint64_t cmagic, float* part_a,
+                                    float* part_b, float* row_max, float* row_rcp) {
+    constexpr int VEC = Elem<DT>::VEC;
+    const TileSlots<DT, K> S(nrows, cols, cmagic);
+    u32x4 raw[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) raw[i] = tile_load<DT, FULL>(gin, S.granule(i), S.nel);
+    float v[K][VEC];
+#pragma unroll
+    for (int i = 0; i < K; ++i) Elem<DT>::widen(raw[i], v[i]);
+    tile_softmax_rows<DT, K, FULL>(v, S, gout, nrows, cols, lg, part_a, part_b, row_max, row_rcp);
+}
+
+// ---------------------------------------------------------------------------
+// masked softmax: z = scale * x + mask[row mod mask_rows, col], and -inf past
+// a row's causal limit (col > (row mod causal_q) + cols - causal_q), the
+// prologue of the masked entry point (rws_pre.hpp gives it to the other
+// forms), then the tile softmax above
+// ---------------------------------------------------------------------------
+struct TileMask {
+    float scale;
+    const char* mask;      // nullptr: no additive mask
+    const char* mask_end;  // one past the mask's mask_rows * cols elements
+    int64_t mask_rows;
+    int64_t causal_q;      // 0: no causal limit
+    int64_t row_base;      // global index of the launch's first row
+    uint64_t mask_M;       // remainder_magic(mask_rows)
+    uint64_t causal_M;     // remainder_magic(causal_q) when causal_q > 0
+};
+
+// Bytes [ph, ph + 16) of the 32 bytes lo ++ hi; ph in 1..15, uniform.
+__device__ inline u32x4 tile_shift16(u32x4 lo, u32x4 hi, int ph) {
+    const uint32_t w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const uint32_t b = (uint32_t)(ph & 3);
+    u32x4 r;
+    switch (ph >> 2) {
+#define RWS_SH(q)                                                                       \
+    case q:                                                                             \
+        r = u32x4{__builtin_amdgcn_alignbyte(w[q + 1], w[q], b),                        \
+                  __builtin_amdgcn_alignbyte(w[q + 2], w[q + 1], b),                    \
+                  __builtin_amdgcn_alignbyte(w[q + 3], w[q + 2], b),                    \
+                  __builtin_amdgcn_alignbyte(w[q + 4], w[q + 3], b)};                   \
+        break;
+        RWS_SH(0) RWS_SH(1) RWS_SH(2)
+#undef RWS_SH
+        default:
+            r = u32x4{__builtin_amdgcn_alignbyte(w[4], w[3], b),
+                      __builtin_amdgcn_alignbyte(w[5], w[4], b),
+                      __builtin_amdgcn_alignbyte(w[6], w[5], b),
+                      __builtin_amdgcn_alignbyte(w[7], w[6], b)};
+    }
+    return r;
+}
+
+// How a tile reads its mask (uniform over the wave).  A tile's mask rows
+// (grow0 + r) mod mask_rows follow each other unless they wrap inside the
+// tile; then the tile's mask bytes are one range laid out like the input
+// tile and are read granule by granule: one aligned load (kMaskWhole), or
+// two and a byte shift when the range is not 16-byte aligned (kMaskShift,
+// where the aligned pairs of the whole range lie inside the mask).  A tile
+// whose mask rows wrap, the tensor's partial last tile, and a shifted range
+// at an end of the mask read it element by element (kMaskElem).
+enum { kMaskNone = 0, kMaskWhole = 1, kMaskShift = 2, kMaskElem = 3 };
+
+// The prologue of a tile for one way of reading the mask (MODE) and with or
+// without a causal limit: loads (every load first, the input's and the
+// mask's, then the arithmetic) and z into v.  Element e of granule slot i
+// takes part when e < split ? e <= ta : e <= tb: ta and tb come from the
+// causal limits of the granule's two rows; no element of a row past the
+// tile's last one takes part, nor any of a slot past the tile.  Without a
+// causal limit every element of the tile takes part, and the values the
+// others get are never used.  Granules of which no element takes part
+// (past the causal limit of both their rows) load neither the input nor
+// the mask.
+template <int DT, int K, bool FULL, int MODE, bool CAUSAL>
+__device__ inline void tile_masked_prologue(float (&v)[K][Elem<DT>::VEC],
+                                            const TileSlots<DT, K>& S, const char* __restrict__ gin,
+                                            const TileMask& P, const char* mtile, int mph,
+                                            int cols, const int* row_lim,
+                                            const int64_t* row_mrow) {
+    constexpr int VEC = Elem<DT>::VEC;
+    constexpr int ES = Elem<DT>::SIZE;
+    int ta[K], tb[K];
+    u32x4 raw[K], mlo[K], mhi[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        const int j = S.granule(i);
+        const int x = j * VEC;
+        const int ra = S.ra[i];
+        const int c0a = x - ra * cols;  // column of element 0 in row ra
+        bool any = x < S.nel;
+        if (CAUSAL) {
+            const int sp = S.split_pass(i);
+            ta[i] = row_lim[ra] - c0a;
+            tb[i] = ra < S.last ? row_lim[ra + 1] - (c0a - cols) : -1;
+            any = ta[i] >= 0 || (sp < VEC && tb[i] >= sp);
+        }
+        raw[i] = u32x4{0u, 0u, 0u, 0u};
+        mlo[i] = u32x4{0u, 0u, 0u, 0u};
+        mhi[i] = u32x4{0u, 0u, 0u, 0u};
+        if (any) {
+            raw[i] = tile_load<DT, FULL>(gin, j, S.nel);
+            // whole granules only (a full tile: every slot inside it)
+            const char* p = mtile + (int64_t)j * 16;
+            if (MODE == kMaskWhole) {
+                mlo[i] = load16<false>(p);
+            } else if (MODE == kMaskShift) {
+                mlo[i] = load16<false>(p - mph);
+                mhi[i] = load16<false>(p - mph + 16);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        Elem<DT>::widen(raw[i], v[i]);
+        float mv[VEC];
+        if (MODE == kMaskWhole) {
+            Elem<DT>::widen(mlo[i], mv);
+        } else if (MODE == kMaskShift) {
+            Elem<DT>::widen(tile_shift16(mlo[i], mhi[i], mph), mv);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) mv[e] = 0.0f;
+        }
+        const int sp = S.split_pass(i);
+        if (MODE == kMaskElem) {
+            const int x = S.granule(i) * VEC;
+            const int ra = S.ra[i];
+            const int c0a = x - ra * cols;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const bool in_a = e < sp;
+                const bool ok = CAUSAL ? (in_a ? e <= ta[i] : e <= tb[i])
+                                       : x < S.nel && (in_a || ra < S.last);
+                if (ok) {
+                    const int64_t mr = row_mrow[in_a ? ra : ra + 1];
+                    const int col = (in_a ? c0a : c0a - cols) + e;
+                    mv[e] = Elem<DT>::load1(P.mask + (mr * cols + col) * ES);
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            if (CAUSAL) {
+                const bool ok = e < sp ? e <= ta[i] : e <= tb[i];
+                v[i][e] = ok ? __builtin_fmaf(P.scale, v[i][e], mv[e]) : kNegInf;
+            } else {
+                v[i][e] = __builtin_fmaf(P.scale, v[i][e], mv[e]);
+            }
+        }
+    }
+}
+
+template <int DT, int K, bool FULL, bool CAUSAL>
+__device__ inline void tile_masked_prologue_any(int mode, float (&v)[K][Elem<DT>::VEC],
+                                                const TileSlots<DT, K>& S, const char* gin,
+                                                const TileMask& P, const char* mtile, int mph,
+                                                int cols, const int* row_lim,
+                                                const int64_t* row_mrow) {
+    if (mode == kMaskNone)
+        tile_masked_prologue<DT, K, FULL, kMaskNone, CAUSAL>(v, S, gin, P, mtile, mph, cols,
+                                                            row_lim, row_mrow);
+    else if (FULL && mode == kMaskWhole)
+        tile_masked_prologue<DT, K, FULL, kMaskWhole, CAUSAL>(v, S, gin, P, mtile, mph, cols,
+                                                             row_lim, row_mrow);
+    else if (FULL && mode == kMaskShift)
+        tile_masked_prologue<DT, K, FULL, kMaskShift, CAUSAL>(v, S, gin, P, mtile, mph, cols,
+                                                             row_lim, row_mrow);
+    else
+        tile_masked_prologue<DT, K, FULL, kMaskElem, CAUSAL>(v, S, gin, P, mtile, mph, cols,
+                                                            row_lim, row_mrow);
+}
+
+template <int DT, int K, bool FULL>
+__device__ inline void tile_softmax_masked(const char* __restrict__ gin, char* __restrict__ gout,
+                                           int nrows, int cols, int lg, uint64_t cmagic,
+                                           const TileMask& P, int64_t grow0, float* part_a,
+                                           float* part_b, float* row_max, float* row_rcp,
+                                           int* row_lim, int64_t* row_mrow) {
+    constexpr int VEC = Elem<DT>::VEC;
+    constexpr int ES = Elem<DT>::SIZE;
+    const TileSlots<DT, K> S(nrows, cols, cmagic);
+    const int lane = threadIdx.x;
+    // per tile row: the last column that takes part, and the mask row
+    if (lane < nrows) {
+        const int64_t g = grow0 + lane;
+        row_lim[lane] = P.causal_q > 0
+                            ? (int)row_mod(g, P.causal_q, P.causal_M) + cols - (int)P.causal_q
+                            : cols - 1;
+        row_mrow[lane] = P.mask ? row_mod(g, P.mask_rows, P.mask_M) : 0;
+    }
+    __syncthreads();
+    const int64_t m0 = row_mrow[0];
+    const char* mtile = P.mask + m0 * cols * ES;
+    const int mph = (int)((uintptr_t)mtile & 15);
+    int mode = kMaskNone;
+    if (P.mask != nullptr) {
+        mode = kMaskElem;
+        if (FULL && m0 + nrows <= P.mask_rows) {
+            if (mph == 0)
+                mode = kMaskWhole;
+            else if (mtile - mph >= P.mask &&
+                     mtile - mph + (int64_t)nrows * cols * ES + 32 <= P.mask_end)
+                mode = kMaskShift;
+        }
+    }
+    float v[K][VEC];
+    if (P.causal_q > 0)
+        tile_masked_prologue_any<DT, K, FULL, true>(mode, v, S, gin, P, mtile, mph, cols, row_lim,
+                                                    row_mrow);
+    else
+        tile_masked_prologue_any<DT, K, FULL, false>(mode, v, S, gin, P, mtile, mph, cols,
+                                                     row_lim, row_mrow);
+    tile_softmax_rows<DT, K, FULL>(v, S, gout, nrows, cols, lg, part_a, part_b, row_max, row_rcp);
 }
 
 // The tile a workgroup takes (XCD runs of 2^lgrun tiles, xcd_run) and its
@@ -149,6 +361,30 @@ __global__ __launch_bounds__(64) void k_tile_rows(const void* __restrict__ in,
     else
         tile_softmax<DT, K, false>(gin, gout, (int)(rows - row0), cols, lg, cmagic, part_a, part_b,
                                    row_max, row_rcp);
+}
+
+template <int DT, int K>
+__global__ __launch_bounds__(64) void k_tile_rows_masked(const void* __restrict__ in,
+                                                         void* __restrict__ out, int64_t rows,
+                                                         int cols, uint64_t cmagic, int T, int lg,
+                                                         int lgrun, TileMask P) {
+    __shared__ float part_a[64 * K];
+    __shared__ float part_b[64 * K];
+    __shared__ float row_max[kTileMaxT];
+    __shared__ float row_rcp[kTileMaxT];
+    __shared__ int row_lim[kTileMaxT];
+    __shared__ int64_t row_mrow[kTileMaxT];
+    const int64_t row0 = tile_row0(T, lgrun);
+    const int64_t off = row0 * cols * Elem<DT>::SIZE;
+    const char* gin = (const char*)in + off;
+    char* gout = (char*)out + off;
+    if (rows - row0 >= T)
+        tile_softmax_masked<DT, K, true>(gin, gout, T, cols, lg, cmagic, P, P.row_base + row0,
+                                         part_a, part_b, row_max, row_rcp, row_lim, row_mrow);
+    else
+        tile_softmax_masked<DT, K, false>(gin, gout, (int)(rows - row0), cols, lg, cmagic, P,
+                                          P.row_base + row0, part_a, part_b, row_max, row_rcp,
+                                          row_lim, row_mrow);
 }
 
 // ---------------------------------------------------------------------------
@@ -369,6 +605,25 @@ static hipError_t go(const Launch& L, const TileShape& t) {
 }
 
 template <int DT, int K>
+static hipError_t go_masked(const Launch& L, const TileShape& t, const MaskArgs& M) {
+    if (!tile_ok(t, L.rows, L.cols, Elem<DT>::SIZE, K)) return hipErrorInvalidValue;
+    TileMask P;
+    P.scale = M.scale;
+    P.mask = (const char*)M.mask;
+    P.mask_rows = M.mask && M.mask_rows > 0 ? M.mask_rows : 1;
+    P.mask_end = P.mask ? P.mask + P.mask_rows * L.cols * Elem<DT>::SIZE : nullptr;
+    P.causal_q = M.causal_q;
+    P.row_base = M.row_base;
+    P.mask_M = remainder_magic((uint64_t)P.mask_rows);
+    P.causal_M = M.causal_q > 0 ? remainder_magic((uint64_t)M.causal_q) : 0;
+    const int64_t tiles = (L.rows + t.T - 1) / t.T;
+    hipLaunchKernelGGL((k_tile_rows_masked<DT, K>), dim3((unsigned)tiles), dim3(64), 0, L.stream,
+                       L.in, L.out, L.rows, L.cols, remainder_magic((uint64_t)L.cols), t.T,
+                       tile_lg(t.T), t.lgrun, P);
+    return hipGetLastError();
+}
+
+template <int DT, int K>
 static hipError_t go_bwd(const BwdLaunch& B, const TileShape& t) {
     if (!tile_ok(t, B.rows, B.cols, Elem<DT>::SIZE, K)) return hipErrorInvalidValue;
     const int64_t tiles = (B.rows + t.T - 1) / t.T;
@@ -405,6 +660,16 @@ static hipError_t go_any(const Launch& L, const TileShape& t) {
 }
 
 template <int K>
+static hipError_t go_masked_any(const Launch& L, const TileShape& t, const MaskArgs& M) {
+    switch (L.dtype) {
+        case kF32: return go_masked<kF32, K>(L, t, M);
+        case kF16: return go_masked<kF16, K>(L, t, M);
+        case kBF16: return go_masked<kBF16, K>(L, t, M);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int K>
 static hipError_t go_bwd_any(const BwdLaunch& B, const TileShape& t) {
     switch (B.dtype) {
         case kF32: return go_bwd<kF32, K>(B, t);
@@ -428,6 +693,17 @@ hipError_t launch_tile_rows(const Launch& L, int variant, const TileShape& t) {
     int i = 0;
 #define RWS_CASE(k) \
     if (variant == i) return go_any<k>(L, t); \
+    ++i;
+    RWS_TILE_ROWS_VARIANTS(RWS_CASE)
+#undef RWS_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_tile_rows_masked(const Launch& L, int variant, const TileShape& t,
+                                  const MaskArgs& M) {
+    int i = 0;
+#define RWS_CASE(k) \
+    if (variant == i) return go_masked_any<k>(L, t, M); \
     ++i;
     RWS_TILE_ROWS_VARIANTS(RWS_CASE)
 #undef RWS_CASE

@@ -518,6 +518,13 @@ def test_tile_height_choice(lib, dtype, es):
     assert {2, 3, 4} <= {k for _, k in seen} and any(big for big, _ in seen)
 
 
+def test_masked_form_takes_the_same_tiles(lib):
+    for cols in (33, 77, 197, 250):
+        plain = rws.softmax_describe_launch(4096, cols, rws.RWS_F16, 256, 512)
+        masked = rws.softmax_describe_launch(4096, cols, rws.RWS_F16, 256, 512, masked=True)
+        assert plain.startswith("tile_rows<") and masked == plain, (plain, masked)
+
+
 def test_tile_needs_enough_rows_and_aligned_pointers(lib):
     assert rws.softmax_describe_launch(64, 250, rws.RWS_F16, 256, 512).startswith("tile_rows<")
     assert not rws.softmax_describe_launch(63, 250, rws.RWS_F16, 256, 512).startswith("tile_rows<")

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import row_wise_safe_amd as rws
-from gpu_util import TORCH_DTYPE, have_gpu, to_device
+from gpu_util import TORCH_DTYPE, have_gpu, tile_supports, to_device
 from tolerance import check
 
 pytestmark = [pytest.mark.gpu,
@@ -160,3 +160,91 @@ def test_out_on_the_host_is_rejected_before_any_launch():
                  lambda: rws.rms_norm(x, out=host)):
         with pytest.raises(ValueError):
             call()
+
+
+# --------------------------------------------------------------------------
+# tile_rows: short rows that are not line-aligned, several per wave
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("S", [9, 33, 77, 197, 200, 250, 500])
+def test_tile_rows_attention_scores(dtype, S):
+    # [B*H*S, S] scores with a [S, S] mask (rows of it wrap inside most
+    # tiles when S is not a multiple of the tile height), causal or not
+    if not tile_supports(S, dtype):
+        pytest.skip("outside the tile rows")
+    BH = 6
+    g = np.random.Generator(np.random.PCG64(S * 3 + 1))
+    x64 = g.normal(0.0, 4.0, (BH * S, S))
+    m64 = g.normal(0.0, 2.0, (S, S))
+    m64[:, 3::7] = -math.inf if dtype != "bf16" else -1.0e30  # key 0 stays visible
+    x, xs = to_device(x64, dtype)
+    m, ms = to_device(m64, dtype)
+    scale = 0.125
+    es = 4 if dtype == "f32" else 2
+    for causal in (0, S):
+        ref = oracle.masked_softmax(xs, scale, ms, causal)
+        desc = rws.softmax_describe_launch(BH * S, S, rws.dtype_code(x.dtype), x.data_ptr(),
+                                           x.data_ptr(), masked=True)
+        if (S * es) % 128 and ((S * es) % 16 or S * es > 128) and BH * S >= 64:
+            assert desc.startswith("tile_rows<"), desc
+        for kernel in ("auto", "tile_rows"):
+            y = _masked(x, scale, m, causal, kernel)
+            check(y, ref, dtype, f"{kernel} {desc} S={S} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_tile_rows_mask_phase_rows_and_limits(dtype):
+    # a mask 16-byte aligned or not (one element in: two loads and a byte
+    # shift per granule, element loads where the pair would leave the mask),
+    # mask rows that do not divide the rows (a wrap in most tiles, or none
+    # when one row is broadcast), causal limits with more keys than queries,
+    # a partial last tile, no mask
+    cols = 77
+    rows = 3 * 7 * 24 + 5
+    g = np.random.Generator(np.random.PCG64(77))
+    x64 = g.normal(0.0, 3.0, (rows, cols))
+    x, xs = to_device(x64, dtype)
+    for mask_rows in (1, 5, 24, 77, 100):
+        m64 = g.normal(0.0, 2.0, (mask_rows, cols))
+        for moff in (0, 1):
+            m, ms = to_device(m64, dtype, offset=moff)
+            for causal in (0, 17, 77):
+                ref = oracle.masked_softmax(xs, 0.5, ms, causal)
+                y = _masked(x, 0.5, m, causal, "tile_rows")
+                check(y, ref, dtype, f"mask_rows={mask_rows} offset={moff} causal={causal}")
+    for causal in (0, 17):
+        ref = oracle.masked_softmax(xs, -1.25, None, causal)
+        check(_masked(x, -1.25, None, causal, "tile_rows"), ref, dtype, f"no mask causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_tile_rows_masked_full_size_vit_scores(dtype):
+    # ViT-like scores: 64 x 12 heads of 197 x 197, a [197,197] mask, causal;
+    # sampled rows (both ends and seeded random ones) against the oracle,
+    # every row sum on the device
+    S, BH = 197, 64 * 12
+    rows = BH * S
+    gen = torch.Generator(device="cuda").manual_seed(197)
+    x = (torch.randn(rows, S, generator=gen, device="cuda") * 4.0).to(TORCH_DTYPE[dtype])
+    m = (torch.randn(S, S, generator=gen, device="cuda") * 2.0).to(TORCH_DTYPE[dtype])
+    desc = rws.softmax_describe_launch(rows, S, rws.dtype_code(x.dtype), x.data_ptr(),
+                                       x.data_ptr(), masked=True)
+    assert desc.startswith("tile_rows<"), desc
+    out = torch.empty_like(x)
+    rws.softmax_masked(x, scale=0.125, mask=m, causal_q=S, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    assert (out.double().sum(dim=1) - 1.0).abs().max().item() <= 1e-2
+    rng = np.random.Generator(np.random.PCG64(5))
+    idx = np.unique(np.concatenate([np.arange(300), np.arange(rows - 300, rows),
+                                    rng.integers(0, rows, 600)]))
+    ti = torch.from_numpy(idx).cuda()
+    xs = x.index_select(0, ti).double().cpu().numpy()
+    ms = m.double().cpu().numpy()
+    # the oracle over the sampled rows: each keeps its global row's mask row
+    # and causal limit
+    ref = np.empty((idx.size, S))
+    for k, r in enumerate(idx):
+        full = oracle.masked_softmax(np.vstack([np.zeros((r % S, S)), xs[k:k + 1]]), 0.125, ms, S)
+        ref[k] = full[-1]
+    check(out.index_select(0, ti).double().cpu().numpy(), ref, dtype, f"{desc} sampled rows")

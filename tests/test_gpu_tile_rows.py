@@ -175,10 +175,10 @@ def test_refusals():
         st = rws.softmax_fwd_kernel(x.data_ptr(), x.data_ptr(), 2, cols, rws.RWS_F16,
                                     torch.cuda.current_stream().cuda_stream, TILE)
         assert st == rws.RWS_ERR_UNSUPPORTED_SHAPE
-    # the masked form has no tile form; its dispatcher keeps wave_row
+    # the masked form takes the same tile
     desc = rws.softmax_describe_launch(1000, 100, rws.RWS_F16, x.data_ptr(), x.data_ptr(),
                                        masked=True)
-    assert desc.startswith("wave_row<"), desc
+    assert desc.startswith("tile_rows<"), desc
 
 
 def _sample_rows(rows, seed, n_ends=200, n_random=600):
