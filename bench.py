@@ -56,7 +56,8 @@ KERNEL_SOURCES = {
     "splitk_fused": _SOFTMAX_COMMON + ["rws_ordered.hpp", "rws_splitk_fused.hip"],
     "splitk_ordered": _SOFTMAX_COMMON + ["rws_ordered.hpp", "rws_splitk_ordered.hip"],
     "tile_rows": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_tile.hpp", "rws_tile_rows.hip"],
-    "masked": _SOFTMAX_COMMON + ["rws_masked.hip"],
+    "masked": _SOFTMAX_COMMON + ["rws_masked.hip", "rws_launch.hpp", "rws_tile.hpp",
+                                 "rws_tile_rows.hip"],
     "backward": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_ordered.hpp", "rws_backward.hip",
                                    "rws_tile.hpp", "rws_tile_rows.hip"],
     "layernorm": _SOFTMAX_COMMON + ["rws_launch.hpp", "rws_ordered.hpp", "rws_norm.hpp",
@@ -64,12 +65,12 @@ KERNEL_SOURCES = {
                                     "rws_tile_rows.hip"],
 }
 KERNEL_SOURCES["rmsnorm"] = KERNEL_SOURCES["layernorm"]
-# Substring that names the step's kernels in a trace.
+# Substring (or substrings) that name the step's kernels in a trace.
 KERNEL_SYMBOL = {"wave_row": "k_wave_row", "block_onepass": "k_block_onepass",
                  "two_pass": "k_two_pass", "splitk": "k_splitk_stage",
                  "splitk_fused": "k_splitk_fused", "splitk_ordered": "k_splitk_ordered",
                  "tile_rows": "k_tile_rows",
-                 "masked": "MaskPre", "backward": "k_bwd_",
+                 "masked": ("MaskPre", "k_tile_rows_masked"), "backward": "k_bwd_",
                  "layernorm": "k_norm_", "rmsnorm": "k_norm_"}
 
 
@@ -104,7 +105,12 @@ def summarize_rocprof(directory: str, workload: str, kernel: str, command: str) 
     scaled by what the same counter reads for the 16-byte copy kernel, whose
     true traffic is known (its bytes read and written).
     """
-    sym = KERNEL_SYMBOL[kernel]
+    syms = KERNEL_SYMBOL[kernel]
+    syms = syms if isinstance(syms, tuple) else (syms,)
+
+    def step_kernel(name):
+        return any(s in name for s in syms)
+
     lines = [f"# rocprofv3 summary: {kernel} on {workload}", f"# command: {command}", ""]
     stats = glob.glob(os.path.join(directory, "trace", "**", "*kernel_stats.csv"), recursive=True)
     if stats:
@@ -144,7 +150,7 @@ def summarize_rocprof(directory: str, workload: str, kernel: str, command: str) 
         copy_name = next((n for n in fetch if "k_copy16" in n), None)
         f_c = avg(fetch.get(copy_name, [])) if copy_name else None
         w_c = avg(write.get(copy_name, [])) if copy_name else None
-        names = sorted(n for n in fetch if sym in n)
+        names = sorted(n for n in fetch if step_kernel(n))
         lines.append("## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch)")
         lines.append(f"copy kernel k_copy16 ({copy_bytes} B read + {copy_bytes} B written): "
                      f"FETCH_SIZE {f_c} KiB, WRITE_SIZE {w_c} KiB")
@@ -192,7 +198,7 @@ def summarize_rocprof(directory: str, workload: str, kernel: str, command: str) 
                      "(cycles), in flight = LEVEL / GRBM_GUI_ACTIVE (requests, all channels)")
         abs_total = None
         for n in sorted(ea):
-            if not (sym in n or "k_copy16" in n):
+            if not (step_kernel(n) or "k_copy16" in n):
                 continue
             per = ea[n]
             rq, r128, r64, r32 = (mean(per, c) for c in (
@@ -227,7 +233,7 @@ def summarize_rocprof(directory: str, workload: str, kernel: str, command: str) 
             if hit is not None and miss is not None and hit + miss > 0:
                 parts.append(f"L2 hit {hit:.0f} miss {miss:.0f} ({hit / (hit + miss):.3f})")
             lines.append(" ".join(parts))
-            if rd is not None and wr is not None and sym in n:
+            if rd is not None and wr is not None and step_kernel(n):
                 abs_total = (abs_total or 0.0) + rd + wr
         if abs_total is not None:
             lines.append(f"absolute_bytes_per_launch: {abs_total:.0f}"
@@ -235,7 +241,7 @@ def summarize_rocprof(directory: str, workload: str, kernel: str, command: str) 
                             if meta.get("bytes_per_call") else "")
                          + (f", / copy-calibrated {abs_total / traffic:.4f})" if traffic
                             else ")" if meta.get("bytes_per_call") else "")
-                         + ("  (sum of the step's kernels)" if sum(sym in n for n in ea) > 1
+                         + ("  (sum of the step's kernels)" if sum(step_kernel(n) for n in ea) > 1
                             else ""))
         lines.append("")
     # occupancy and vector-ALU activity (one derived metric per pass)
@@ -249,7 +255,7 @@ def summarize_rocprof(directory: str, workload: str, kernel: str, command: str) 
             continue
         per = {}
         for r in _read_csv(files[0]):
-            if r.get("Counter_Name") == metric and sym in r.get("Kernel_Name", ""):
+            if r.get("Counter_Name") == metric and step_kernel(r.get("Kernel_Name", "")):
                 per.setdefault(r["Kernel_Name"], []).append(float(r.get("Counter_Value", 0.0)))
         for n in sorted(per):
             extra.append(f"kernel {n}: {metric} {sum(per[n]) / len(per[n]):.2f} ({unit})")
