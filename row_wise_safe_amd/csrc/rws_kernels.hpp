@@ -53,10 +53,11 @@ __device__ inline void widen_zero(const Win& w, int k, u32x4 raw, float* v, cons
 // (load16); the prologue operand is shared by many rows and loads cached.
 template <bool NT = true, class Pre, class Win>
 __device__ inline void fetch_pre(const Pre& pre, const typename Pre::Ctx& pc, const Win& w, int k,
-                                 const char* tbeg, const char* tend, u32x4& raw, u32x4& praw) {
+                                 const char* tbeg, const char* tend, u32x4& raw,
+                                 typename Pre::Operand& praw) {
     if (Pre::kActive) {
         raw = u32x4{0u, 0u, 0u, 0u};
-        praw = u32x4{0u, 0u, 0u, 0u};
+        praw = typename Pre::Operand{};
         if (pre.needs_input(pc, w, k)) {
             raw = w.template fetch<NT>(k, tbeg, tend);
             praw = pre.fetch(pc, w, k);
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
     RowWin<DT, ALIGNED, WA> w[U];
     typename Pre::Ctx pc[U];  // prologue context of the row each set loads
     u32x4 raw[U][K];
-    u32x4 praw[Pre::kActive ? U : 1][Pre::kActive ? K : 1];  // prologue operands
+    typename Pre::Operand praw[Pre::kActive ? U : 1][Pre::kActive ? K : 1];  // prologue operands
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         int64_t row = row0 + u * RPS + sub;
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict_
     const typename Pre::Ctx pc = pre.ctx(row, w);
 
     u32x4 raw[KR];
-    u32x4 praw[Pre::kActive ? KR : 1];  // prologue operands
+    typename Pre::Operand praw[Pre::kActive ? KR : 1];  // prologue operands
 #pragma unroll
     for (int i = 0; i < KR; ++i)
         fetch_pre(pre, pc, w, t + BLOCK * i, tbeg, tend, raw[i], praw[Pre::kActive ? i : 0]);
@@ -430,7 +431,7 @@ __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
     float m = kNegInf, d = 0.0f;
     for (int k0 = t; k0 < w.ngran; k0 += BLOCK * U) {
         u32x4 raw[U];
-        u32x4 praw[Pre::kActive ? U : 1];
+        typename Pre::Operand praw[Pre::kActive ? U : 1];
 #pragma unroll
         for (int u = 0; u < U; ++u)  // cached: pass 2 reads the row again
             fetch_pre<false>(pre, pc, w, k0 + BLOCK * u, tbeg, tend, raw[u],
@@ -455,7 +456,7 @@ __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
 
     for (int k0 = t; k0 < w.ngran; k0 += BLOCK * U) {
         u32x4 raw[U];
-        u32x4 praw[Pre::kActive ? U : 1];
+        typename Pre::Operand praw[Pre::kActive ? U : 1];
 #pragma unroll
         for (int u = 0; u < U; ++u)
             fetch_pre(pre, pc, w, k0 + BLOCK * u, tbeg, tend, raw[u], praw[Pre::kActive ? u : 0]);

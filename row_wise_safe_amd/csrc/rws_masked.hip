@@ -8,12 +8,13 @@
 
 namespace rws {
 
-template <int DT>
-static MaskPre<DT> make_pre(const MaskArgs& M) {
-    MaskPre<DT> p;
+template <int DT, bool PAIR = true>
+static MaskPre<DT, PAIR> make_pre(const MaskArgs& M, int cols) {
+    MaskPre<DT, PAIR> p;
     p.scale = M.scale;
     p.mask = (const char*)M.mask;
     p.mask_rows = M.mask_rows > 0 ? M.mask_rows : 1;
+    p.mask_end = p.mask ? p.mask + p.mask_rows * cols * Elem<DT>::SIZE : nullptr;
     p.causal_q = M.causal_q;
     p.row_base = M.row_base;
     p.mask_M = remainder_magic((uint64_t)p.mask_rows);
@@ -27,7 +28,7 @@ static hipError_t wr(const Launch& L, const MaskArgs& M) {
     const WaveRowVariant v = {G, K, U};
     hipLaunchKernelGGL((k_wave_row<DT, AL, G, K, U, MaskPre<DT>>),
                        dim3((unsigned)wave_row_grid(v, L.rows)), dim3(kWaveGroupThreads), 0, L.stream, L.in,
-                       L.out, L.rows, L.cols, (int)L.same_phase, (int)L.wt, make_pre<DT>(M));
+                       L.out, L.rows, L.cols, (int)L.same_phase, (int)L.wt, make_pre<DT>(M, L.cols));
     return hipGetLastError();
 }
 
@@ -54,9 +55,10 @@ hipError_t launch_wave_row_masked(const Launch& L, int variant, const MaskArgs& 
 // ---- block_onepass (variants without LDS parking) --------------------------
 template <int DT, bool AL, int B, int KR>
 static hipError_t bo(const Launch& L, const MaskArgs& M) {
-    hipLaunchKernelGGL((k_block_onepass<DT, AL, B, KR, 0, MaskPre<DT>>), dim3((unsigned)L.rows),
+    constexpr bool kPair = B < 1024;
+    hipLaunchKernelGGL((k_block_onepass<DT, AL, B, KR, 0, MaskPre<DT, kPair>>), dim3((unsigned)L.rows),
                        dim3(B), 0, L.stream, L.in, L.out, L.rows, L.cols, (int)L.same_phase, L.lgrun,
-                       make_pre<DT>(M));
+                       make_pre<DT, kPair>(M, L.cols));
     return hipGetLastError();
 }
 
@@ -87,9 +89,10 @@ hipError_t launch_block_onepass_masked(const Launch& L, int variant, const MaskA
 // ---- two_pass ----------------------------------------------------------------
 template <int DT, bool AL, int B, int U>
 static hipError_t tp(const Launch& L, const MaskArgs& M) {
-    hipLaunchKernelGGL((k_two_pass<DT, AL, B, U, MaskPre<DT>>), dim3((unsigned)L.rows), dim3(B), 0,
+    constexpr bool kPair = B < 1024;
+    hipLaunchKernelGGL((k_two_pass<DT, AL, B, U, MaskPre<DT, kPair>>), dim3((unsigned)L.rows), dim3(B), 0,
                        L.stream, L.in, L.out, L.rows, L.cols, (int)L.same_phase, L.lgrun,
-                       make_pre<DT>(M));
+                       make_pre<DT, kPair>(M, L.cols));
     return hipGetLastError();
 }
 

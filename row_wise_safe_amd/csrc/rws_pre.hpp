@@ -4,17 +4,20 @@
 // (section 9) proposes to fold into the softmax kernel as a mask parameter.
 #pragma once
 
+#include <type_traits>
+
 #include "rws_device.hpp"
 
 namespace rws {
 
 // Interface.  ctx() computes what a prologue needs per row, once per row;
-// fetch() issues the prologue operand's load for granule k; apply() rewrites
-// the widened values; needs_input() says whether granule k of the input can
-// affect the result at all (a granule wholly past the causal limit becomes
-// -inf whatever it holds, so its load is skipped).
+// fetch() issues the loads of the prologue operand (Operand) of granule k;
+// apply() rewrites the widened values; needs_input() says whether granule k
+// of the input can affect the result at all (a granule wholly past the
+// causal limit becomes -inf whatever it holds, so its load is skipped).
 struct NoPre {
     static constexpr bool kActive = false;
+    using Operand = u32x4;
     struct Ctx {};
     template <class Win>
     __device__ inline Ctx ctx(int64_t, const Win&) const {
@@ -29,7 +32,7 @@ struct NoPre {
         return u32x4{0u, 0u, 0u, 0u};
     }
     template <class Win>
-    __device__ inline void apply(const Ctx&, const Win&, int, float*, u32x4) const {}
+    __device__ inline void apply(const Ctx&, const Win&, int, float*, Operand) const {}
 };
 
 // r mod d for r >= 0, d > 0.  When both fit 32 bits, by multiplication
@@ -54,27 +57,55 @@ __device__ inline int64_t row_mod(int64_t r, int64_t d, uint64_t M) {
     return r % d;
 }
 
+// Bytes [ph, ph + 16) of the 32 bytes lo ++ hi, ph in 1..15 and free to
+// differ between lanes: the dwords are picked by selects, then shifted.
+__device__ inline u32x4 shift16_lanes(u32x4 lo, u32x4 hi, int ph) {
+    const uint32_t w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const int q = ph >> 2;
+    const uint32_t b = (uint32_t)(ph & 3);
+    uint32_t s[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
+        s[k] = q == 0 ? w[k] : q == 1 ? w[k + 1] : q == 2 ? w[k + 2] : w[k + 3];
+    return u32x4{__builtin_amdgcn_alignbyte(s[1], s[0], b), __builtin_amdgcn_alignbyte(s[2], s[1], b),
+                 __builtin_amdgcn_alignbyte(s[3], s[2], b), __builtin_amdgcn_alignbyte(s[4], s[3], b)};
+}
+
 // z = scale * x + mask[row % mask_rows, c]; columns past the causal limit
 // (c > (row % causal_q) + cols - causal_q, when causal_q > 0) and slots
 // outside the row become -inf.  The mask has the input's dtype and row pitch.
-// fetch() issues a mask granule's 128-bit load together with the input's
-// (when the mask row has the input row's 16-byte phase and the granule lies
-// inside the row); apply() uses it, or reads the mask element by element
-// otherwise.
-template <int DT>
+// fetch() issues the mask granule's loads together with the input's, for
+// granules inside the row: one 128-bit load when the mask row has the input
+// row's 16-byte phase, else (PAIR) the two aligned granules around it,
+// shifted in apply(), when that pair stays inside the mask; apply() reads the
+// mask element by element otherwise.  PAIR doubles the registers that hold
+// the operands in flight: kernels of 1024 threads (128 registers a lane)
+// leave it off.
+template <int DT, bool PAIR = true>
 struct MaskPre {
     static constexpr bool kActive = true;
+    struct OperandPair {
+        u32x4 lo;  // the mask granule, or the aligned one below it
+        u32x4 hi;  // the aligned granule above it
+    };
+    struct OperandOne {
+        u32x4 lo;  // the mask granule
+    };
+    using Operand = typename std::conditional<PAIR, OperandPair, OperandOne>::type;
     float scale;
-    const char* mask;   // nullptr: no additive mask
+    const char* mask;      // nullptr: no additive mask
+    const char* mask_end;  // one past the mask's mask_rows * cols elements
     int64_t mask_rows;
-    int64_t causal_q;   // 0: no causal limit
-    int64_t row_base;   // global index of the launch's first row
-    uint64_t mask_M;    // remainder_magic(mask_rows)
-    uint64_t causal_M;  // remainder_magic(causal_q) when causal_q > 0
+    int64_t causal_q;      // 0: no causal limit
+    int64_t row_base;      // global index of the launch's first row
+    uint64_t mask_M;       // remainder_magic(mask_rows)
+    uint64_t causal_M;     // remainder_magic(causal_q) when causal_q > 0
 
     struct Ctx {
         const char* mrow;  // the row's mask row (nullptr: no mask)
         bool mvec;         // mask row has the input row's 16-byte phase
+        bool mpair;        // otherwise: pairs of aligned mask granules, in bounds
+        int mph;           // the mask row's 16-byte phase against the input row's
         int limit;         // last column that takes part
     };
 
@@ -84,10 +115,16 @@ struct MaskPre {
         Ctx c;
         c.mrow = nullptr;
         c.mvec = false;
+        c.mpair = false;
+        c.mph = 0;
         if (mask) {
             c.mrow = mask + row_mod(row, mask_rows, mask_M) * (int64_t)w.cols * Elem<DT>::SIZE;
             const char* xrow = w.gin + (int64_t)w.lead * Elem<DT>::SIZE;  // the input row start
-            c.mvec = (((uintptr_t)c.mrow - (uintptr_t)xrow) & 15u) == 0;
+            c.mph = (int)(((uintptr_t)c.mrow - (uintptr_t)xrow) & 15u);
+            c.mvec = c.mph == 0;
+            // the pairs of the row's inside granules span [mrow - mph, mrow + cols*size + 16)
+            c.mpair = PAIR && !c.mvec && c.mrow - c.mph >= mask &&
+                      c.mrow + (int64_t)w.cols * Elem<DT>::SIZE + 16 <= mask_end;
         }
         c.limit = w.cols - 1;
         if (causal_q > 0) c.limit = (int)row_mod(row, causal_q, causal_M) + w.cols - (int)causal_q;
@@ -103,16 +140,32 @@ struct MaskPre {
     }
 
     template <class Win>
-    __device__ inline u32x4 fetch(const Ctx& c, const Win& w, int k) const {
-        u32x4 g = {0u, 0u, 0u, 0u};
+    __device__ inline Operand fetch(const Ctx& c, const Win& w, int k) const {
+        Operand g{};
         const int c0 = k * Elem<DT>::VEC - w.lead;
-        if (c.mrow && c.mvec && c0 >= 0 && c0 + Elem<DT>::VEC <= w.cols)
-            g = *(const u32x4*)(c.mrow + (int64_t)c0 * Elem<DT>::SIZE);
+        if (c.mrow && c0 >= 0 && c0 + Elem<DT>::VEC <= w.cols) {
+            const char* p = c.mrow + (int64_t)c0 * Elem<DT>::SIZE;
+            if (c.mvec) {
+                g.lo = *(const u32x4*)p;
+            } else if constexpr (PAIR) {
+                if (c.mpair) {
+                    g.lo = *(const u32x4*)(p - c.mph);
+                    g.hi = *(const u32x4*)(p - c.mph + 16);
+                }
+            }
+        }
         return g;
     }
 
+    // The mask granule of a pair operand; (OperandOne: never called, as
+    // mpair is false without PAIR.)
+    __device__ static inline u32x4 shifted(const OperandPair& m, int ph) {
+        return shift16_lanes(m.lo, m.hi, ph);
+    }
+    __device__ static inline u32x4 shifted(const OperandOne& m, int) { return m.lo; }
+
     template <class Win>
-    __device__ inline void apply(const Ctx& c, const Win& w, int k, float* v, u32x4 mraw) const {
+    __device__ inline void apply(const Ctx& c, const Win& w, int k, float* v, Operand mraw) const {
         constexpr int VEC = Elem<DT>::VEC;
         constexpr int ES = Elem<DT>::SIZE;
         const int c0 = k * VEC - w.lead;
@@ -122,7 +175,9 @@ struct MaskPre {
         for (int e = 0; e < VEC; ++e) mv[e] = 0.0f;
         if (c.mrow) {
             if (c.mvec && inside) {
-                Elem<DT>::widen(mraw, mv);
+                Elem<DT>::widen(mraw.lo, mv);
+            } else if (c.mpair && inside) {
+                Elem<DT>::widen(shifted(mraw, c.mph), mv);
             } else {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {

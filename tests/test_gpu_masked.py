@@ -122,6 +122,28 @@ def test_mask_with_other_phase(dtype):
         check(_masked(x, 2.0, m, 0, kernel), ref, dtype, kernel)
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_mask_at_every_phase(dtype):
+    # mask rows at every 16-byte phase against the input rows: the mask
+    # granules are then read as aligned pairs and shifted into place, and
+    # element by element where such a pair would leave the mask (its first
+    # and last rows); input rows start at every phase too (odd cols)
+    vec = 4 if dtype == "f32" else 8
+    g = np.random.Generator(np.random.PCG64(14))
+    rows, mask_rows = 16, 7
+    for cols in (577, 1000, 3001):
+        for xoff in (0, 3):
+            x, xs = to_device(g.normal(0, 3, (rows, cols)), dtype, offset=xoff)
+            for moff in range(vec):
+                m, ms = to_device(g.normal(0, 2, (mask_rows, cols)), dtype, offset=moff)
+                for causal in (0, rows):
+                    ref = oracle.masked_softmax(xs, 0.5, ms, causal)
+                    for kernel in KERNELS:
+                        if _supports(kernel, cols, dtype):
+                            check(_masked(x, 0.5, m, causal, kernel), ref, dtype,
+                                  f"{kernel} cols={cols} x+{xoff} mask+{moff} causal={causal}")
+
+
 def test_fully_masked_rows_are_nan():
     x, xs = to_device(np.zeros((6, 4)), "f32")
     y = _masked(x, 1.0, None, 6, "auto")  # q > cols: queries 0 and 1 see no key
