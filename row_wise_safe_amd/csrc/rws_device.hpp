@@ -220,6 +220,8 @@ struct RowWin {
     static_assert(WA == 16 || WA == 32 || WA == 64 || WA == 128, "window alignment");
     static constexpr int VEC = Elem<DT>::VEC;
     static constexpr int ES = Elem<DT>::SIZE;
+    // each granule of the window lies wholly inside the row or wholly past it
+    static constexpr bool kWhole = ALIGNED;
     const char* gin;   // first granule of the window in `in` (line aligned)
     char* gout;        // same position in `out` (used when same_phase)
     char* rout;        // row start in `out`
@@ -265,6 +267,28 @@ struct RowWin {
         u32x4 raw = {0u, 0u, 0u, 0u};
         if (c0 + VEC > 0 && c0 < cols && g >= tbeg && g + 16 <= tend) raw = load16<NT>(g);
         return raw;
+    }
+
+    // Widen a fetched granule into v[0..VEC) for a kernel whose prologue
+    // drops every slot outside the row (their values are left as they come).
+    // Only a granule the tensor begins or ends inside was not loaded whole:
+    // its elements in the row are read one by one, all loads issued at once.
+    __device__ inline void widen_in_row(int k, u32x4 raw, float* v, const char* tbeg,
+                                        const char* tend) const {
+        Elem<DT>::widen(raw, v);
+        if (ALIGNED) return;
+        const char* g = gin + (int64_t)k * 16;
+        if (!(g >= tbeg && g + 16 <= tend)) {
+            const int c0 = k * VEC - lead;
+            const char* rin = gin + (int64_t)lead * ES;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const int c = c0 + e;
+                const bool in = c >= 0 && c < cols;
+                const float f = Elem<DT>::load1(in ? g + e * ES : rin);
+                v[e] = in ? f : 0.0f;
+            }
+        }
     }
 
     // Widen a fetched granule into v[0..VEC); elements outside the row are -inf.

@@ -118,10 +118,13 @@ __global__ __launch_bounds__(256) void k_wave_row(const void* __restrict__ in,
     for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int i = 0; i < K; ++i) {
-            w[u].widen(gl + G * i, raw[u][i], &v[u][i * VEC], tbeg, tend, full);
-            if (Pre::kActive)
+            if (Pre::kActive) {
+                w[u].widen_in_row(gl + G * i, raw[u][i], &v[u][i * VEC], tbeg, tend);
                 pre.apply(pc[u], w[u], gl + G * i, &v[u][i * VEC],
                           praw[Pre::kActive ? u : 0][Pre::kActive ? i : 0]);
+            } else {
+                w[u].widen(gl + G * i, raw[u][i], &v[u][i * VEC], tbeg, tend, full);
+            }
         }
         float mx = v[u][0];
 #pragma unroll
@@ -192,8 +195,12 @@ __global__ __launch_bounds__(BLOCK) void k_block_onepass(const void* __restrict_
     float v[N];
 #pragma unroll
     for (int i = 0; i < KR; ++i) {
-        w.widen(t + BLOCK * i, raw[i], &v[i * VEC], tbeg, tend);
-        if (Pre::kActive) pre.apply(pc, w, t + BLOCK * i, &v[i * VEC], praw[Pre::kActive ? i : 0]);
+        if (Pre::kActive) {
+            w.widen_in_row(t + BLOCK * i, raw[i], &v[i * VEC], tbeg, tend);
+            pre.apply(pc, w, t + BLOCK * i, &v[i * VEC], praw[Pre::kActive ? i : 0]);
+        } else {
+            w.widen(t + BLOCK * i, raw[i], &v[i * VEC], tbeg, tend);
+        }
     }
     float mx = kNegInf;
 #pragma unroll
@@ -440,12 +447,16 @@ __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k = k0 + BLOCK * u;
-            w.widen(k, raw[u], &v[u * VEC], tbeg, tend);
-            if (!ALIGNED && k >= w.ngran) {
+            if (Pre::kActive) {
+                w.widen_in_row(k, raw[u], &v[u * VEC], tbeg, tend);
+                pre.apply(pc, w, k, &v[u * VEC], praw[Pre::kActive ? u : 0]);
+            } else {
+                w.widen(k, raw[u], &v[u * VEC], tbeg, tend);
+                if (!ALIGNED && k >= w.ngran) {
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) v[u * VEC + e] = kNegInf;
+                    for (int e = 0; e < VEC; ++e) v[u * VEC + e] = kNegInf;
+                }
             }
-            if (Pre::kActive) pre.apply(pc, w, k, &v[u * VEC], praw[Pre::kActive ? u : 0]);
         }
         online_update(m, d, v);
     }
@@ -465,8 +476,12 @@ __global__ __launch_bounds__(BLOCK) void k_two_pass(const void* __restrict__ in,
             const int k = k0 + BLOCK * u;
             if (k < w.ngran) {
                 float f[VEC];
-                w.widen(k, raw[u], f, tbeg, tend);
-                if (Pre::kActive) pre.apply(pc, w, k, f, praw[Pre::kActive ? u : 0]);
+                if (Pre::kActive) {
+                    w.widen_in_row(k, raw[u], f, tbeg, tend);
+                    pre.apply(pc, w, k, f, praw[Pre::kActive ? u : 0]);
+                } else {
+                    w.widen(k, raw[u], f, tbeg, tend);
+                }
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) f[e] = er.one(f[e]) * r;
                 w.store(k, f, same_phase != 0);

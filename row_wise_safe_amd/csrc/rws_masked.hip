@@ -14,7 +14,9 @@ static MaskPre<DT, PAIR> make_pre(const MaskArgs& M, int cols) {
     p.scale = M.scale;
     p.mask = (const char*)M.mask;
     p.mask_rows = M.mask_rows > 0 ? M.mask_rows : 1;
-    p.mask_end = p.mask ? p.mask + p.mask_rows * cols * Elem<DT>::SIZE : nullptr;
+    const int64_t rowbytes = (int64_t)cols * Elem<DT>::SIZE;
+    p.edge_lo = (32 + rowbytes - 1) / rowbytes;
+    p.edge_hi = (p.mask_rows * rowbytes - 32) / rowbytes - 1;  // below edge_lo: no such row
     p.causal_q = M.causal_q;
     p.row_base = M.row_base;
     p.mask_M = remainder_magic((uint64_t)p.mask_rows);

@@ -12,7 +12,9 @@ namespace rws {
 
 // Interface.  ctx() computes what a prologue needs per row, once per row;
 // fetch() issues the loads of the prologue operand (Operand) of granule k;
-// apply() rewrites the widened values; needs_input() says whether granule k
+// apply() rewrites the widened values and sets every slot outside the row to
+// -inf (the kernels leave those slots as loaded when a prologue is active:
+// RowWin::widen_in_row); needs_input() says whether granule k
 // of the input can affect the result at all (a granule wholly past the
 // causal limit becomes -inf whatever it holds, so its load is skipped).
 struct NoPre {
@@ -74,13 +76,16 @@ __device__ inline u32x4 shift16_lanes(u32x4 lo, u32x4 hi, int ph) {
 // z = scale * x + mask[row % mask_rows, c]; columns past the causal limit
 // (c > (row % causal_q) + cols - causal_q, when causal_q > 0) and slots
 // outside the row become -inf.  The mask has the input's dtype and row pitch.
-// fetch() issues the mask granule's loads together with the input's, for
-// granules inside the row: one 128-bit load when the mask row has the input
-// row's 16-byte phase, else (PAIR) the two aligned granules around it,
-// shifted in apply(), when that pair stays inside the mask; apply() reads the
-// mask element by element otherwise.  PAIR doubles the registers that hold
-// the operands in flight: kernels of 1024 threads (128 registers a lane)
-// leave it off.
+// fetch() issues the mask granule's loads together with the input's: one
+// 128-bit load when the mask row has the input row's 16-byte phase, else
+// (PAIR) the two aligned granules around it, shifted in apply().  The row's
+// first and last granules take mask bytes from outside the mask row as well
+// (never used: those slots become -inf); they are loaded so for mask rows
+// edge_lo..edge_hi, where every such load stays inside the mask (all but the
+// mask's first and last rows).  Elsewhere apply() reads the mask element by
+// element.  PAIR
+// doubles the registers that hold the operands in flight: kernels of 1024
+// threads (128 registers a lane) leave it off.
 template <int DT, bool PAIR = true>
 struct MaskPre {
     static constexpr bool kActive = true;
@@ -94,8 +99,11 @@ struct MaskPre {
     using Operand = typename std::conditional<PAIR, OperandPair, OperandOne>::type;
     float scale;
     const char* mask;      // nullptr: no additive mask
-    const char* mask_end;  // one past the mask's mask_rows * cols elements
     int64_t mask_rows;
+    // Mask rows r with r * rowbytes >= 32 and (r + 1) * rowbytes + 32 <=
+    // mask_rows * rowbytes (rowbytes = cols * size): the granule loads of a
+    // row's ends reach at most 30 bytes before its mask row and 31 past it.
+    int64_t edge_lo, edge_hi;
     int64_t causal_q;      // 0: no causal limit
     int64_t row_base;      // global index of the launch's first row
     uint64_t mask_M;       // remainder_magic(mask_rows)
@@ -104,7 +112,8 @@ struct MaskPre {
     struct Ctx {
         const char* mrow;  // the row's mask row (nullptr: no mask)
         bool mvec;         // mask row has the input row's 16-byte phase
-        bool mpair;        // otherwise: pairs of aligned mask granules, in bounds
+        bool mpair;        // otherwise: pairs of aligned mask granules, all in bounds
+        bool medge;        // the row's partial end granules take granule loads too
         int mph;           // the mask row's 16-byte phase against the input row's
         int limit;         // last column that takes part
     };
@@ -116,15 +125,18 @@ struct MaskPre {
         c.mrow = nullptr;
         c.mvec = false;
         c.mpair = false;
+        c.medge = false;
         c.mph = 0;
         if (mask) {
-            c.mrow = mask + row_mod(row, mask_rows, mask_M) * (int64_t)w.cols * Elem<DT>::SIZE;
-            const char* xrow = w.gin + (int64_t)w.lead * Elem<DT>::SIZE;  // the input row start
+            constexpr int ES = Elem<DT>::SIZE;
+            const int64_t r = row_mod(row, mask_rows, mask_M);
+            c.mrow = mask + r * (int64_t)w.cols * ES;
+            const char* xrow = w.gin + (int64_t)w.lead * ES;  // the input row start
             c.mph = (int)(((uintptr_t)c.mrow - (uintptr_t)xrow) & 15u);
             c.mvec = c.mph == 0;
-            // the pairs of the row's inside granules span [mrow - mph, mrow + cols*size + 16)
-            c.mpair = PAIR && !c.mvec && c.mrow - c.mph >= mask &&
-                      c.mrow + (int64_t)w.cols * Elem<DT>::SIZE + 16 <= mask_end;
+            const bool in_range = r >= edge_lo && r <= edge_hi;
+            c.mpair = PAIR && !c.mvec && in_range;
+            c.medge = !Win::kWhole && in_range && (c.mvec || PAIR);
         }
         c.limit = w.cols - 1;
         if (causal_q > 0) c.limit = (int)row_mod(row, causal_q, causal_M) + w.cols - (int)causal_q;
@@ -143,7 +155,9 @@ struct MaskPre {
     __device__ inline Operand fetch(const Ctx& c, const Win& w, int k) const {
         Operand g{};
         const int c0 = k * Elem<DT>::VEC - w.lead;
-        if (c.mrow && c0 >= 0 && c0 + Elem<DT>::VEC <= w.cols) {
+        const bool inside = c0 >= 0 && c0 + Elem<DT>::VEC <= w.cols;
+        const bool overlaps = c0 + Elem<DT>::VEC > 0 && c0 < w.cols;
+        if (c.mrow && (c.medge ? overlaps : inside)) {
             const char* p = c.mrow + (int64_t)c0 * Elem<DT>::SIZE;
             if (c.mvec) {
                 g.lo = *(const u32x4*)p;
@@ -174,15 +188,21 @@ struct MaskPre {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) mv[e] = 0.0f;
         if (c.mrow) {
-            if (c.mvec && inside) {
+            // a granule past the row's ends was not loaded: its slots are
+            // all dropped below, whatever mv holds
+            if (c.mvec && (inside || c.medge)) {
                 Elem<DT>::widen(mraw.lo, mv);
-            } else if (c.mpair && inside) {
+            } else if (c.mpair) {
                 Elem<DT>::widen(shifted(mraw, c.mph), mv);
             } else {
+                // every load issued before the first is waited for: slots
+                // outside the row read the row's first element instead
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
                     const int col = c0 + e;
-                    if (col >= 0 && col < w.cols) mv[e] = Elem<DT>::load1(c.mrow + (int64_t)col * ES);
+                    const bool in = col >= 0 && col < w.cols;
+                    const float m = Elem<DT>::load1(c.mrow + (int64_t)(in ? col : 0) * ES);
+                    mv[e] = in ? m : 0.0f;
                 }
             }
         }
