@@ -304,7 +304,13 @@ int64_t block_rows_per_launch(int block) {
 // fp16 [131072,250] 34.2 us (32x2) vs 42.4 (64x1), [262144,120] 28.9 (16x2)
 // vs 37.4 (32x1), [524288,60] 35.4 (8x2) vs 40.6 (16x1); line-aligned rows
 // keep one granule per lane ([131072,256] 21.6 (32x1) vs 22.6 (16x2)).
-// max_k limits the granules per lane.
+// Windows of 65-96 granules: three granules on 32 lanes (two rows per wave)
+// instead of two on 64, for the masked form and rows that are not
+// line-aligned: plain fp16 [55392,577] 26.0 us vs 30.0, [31800,600] 15.7 vs
+// 16.9, [32200,700] 18.2 vs 18.7, fp32 [65400,300] 29.0 vs 29.6; masked
+// (causal, [S,S] mask) 577: 38.0 vs 40.1, 768: 16.3 vs 20.7, fp32 300: 26.3
+// vs 30.9.  Plain line-aligned rows keep two on 64 ([32256,768] 17.6 vs
+// 17.7).  max_k limits the granules per lane.
 int pick_wave_row(const Geometry& g, bool masked = false, int max_k = 1 << 30) {
     int best = -1;
     int64_t best_key = 0;
@@ -312,6 +318,7 @@ int pick_wave_row(const Geometry& g, bool masked = false, int max_k = 1 << 30) {
         const rws::WaveRowVariant& v = rws::kWaveRow[i];
         const int64_t w = window_granules(g, softmax_wave_wa(v));
         if ((int64_t)v.G * v.K < w || v.K > max_k) continue;
+        if (v.K == 3 && !masked && g.a128) continue;
         const int64_t cap = (int64_t)v.G * v.K;
         int pref = 2;
         if ((masked || !g.a128) && v.K == 2 && v.G < 64) pref = 0;

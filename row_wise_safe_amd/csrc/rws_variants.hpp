@@ -3,8 +3,9 @@
 // the resulting tables in rws_launch.hpp).
 #pragma once
 
-// (G lanes per row, K granules per lane, U row sets per wave); the last three
-// serve the masked form (two granules per lane on half the lanes)
+// (G lanes per row, K granules per lane, U row sets per wave); the last four
+// serve the masked form and rows that are not line-aligned (two or three
+// granules per lane on less than a wave)
 #define RWS_WAVE_ROW_VARIANTS(X) \
     X(4, 1, 1)                   \
     X(8, 1, 1)                   \
@@ -17,7 +18,8 @@
     X(64, 8, 1)                  \
     X(8, 2, 1)                   \
     X(16, 2, 1)                  \
-    X(32, 2, 1)
+    X(32, 2, 1)                  \
+    X(32, 3, 1)
 
 // (threads, register granules per thread, LDS granules per thread): one
 // granule per thread for launches with few waves, 2-5 for many rows (the

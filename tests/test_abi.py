@@ -314,6 +314,7 @@ def test_describe_mentions_alignment(lib):
     (256, "G=32,K=1,U=1", "G=16,K=2,U=1"),
     (192, "G=32,K=1,U=1", "G=16,K=2,U=1"),
     (128, "G=16,K=1,U=1", "G=8,K=2,U=1"),
+    (768, "G=64,K=2,U=1", "G=32,K=3,U=1"),
     (1024, "G=64,K=2,U=1", "G=64,K=2,U=1"),
 ])
 def test_masked_launch_choice(lib, cols, plain_group, masked_group):
@@ -325,6 +326,16 @@ def test_masked_launch_choice(lib, cols, plain_group, masked_group):
     masked = rws.softmax_describe_launch(rows, cols, rws.RWS_F16, 256, 512, masked=True)
     assert plain_group in plain and "block=64" in plain, plain
     assert masked_group in masked and "block=64" in masked, masked
+
+
+@pytest.mark.parametrize("cols,dtype", [(577, "f16"), (600, "f16"), (700, "f16"), (300, "f32")])
+def test_three_granule_lane_groups(lib, cols, dtype):
+    # rows of 65-96 granules that are not line-aligned: two rows per wave,
+    # three granules per lane on 32 lanes (plain and masked)
+    code = rws.RWS_F16 if dtype == "f16" else rws.RWS_F32
+    for masked in (False, True):
+        d = rws.softmax_describe_launch(64 * cols, cols, code, 256, 512, masked=masked)
+        assert d.startswith("wave_row<") and "G=32,K=3,U=1" in d, d
 
 
 def test_masked_argument_checks(lib):
