@@ -270,3 +270,40 @@ def test_tile_rows_masked_full_size_vit_scores(dtype):
         full = oracle.masked_softmax(np.vstack([np.zeros((r % S, S)), xs[k:k + 1]]), 0.125, ms, S)
         ref[k] = full[-1]
     check(out.index_select(0, ti).double().cpu().numpy(), ref, dtype, f"{desc} sampled rows")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("S,heads,family", [(577, 96, "wave_row<"), (1001, 32, "block_onepass<")])
+def test_long_masked_rows_full_size(dtype, S, heads, family):
+    # score rows longer than a tile holds, at full size: S = 577 (two rows
+    # per wave, three granules per lane) and S = 1001 (a workgroup per row),
+    # where most heads' mask rows have another 16-byte phase than their
+    # input rows (aligned mask pairs and a shift) and the mask's first and
+    # last rows read element by element; a [S,S] mask, causal.  Sampled rows
+    # (the ends of every eighth head, seeded random ones) against the oracle,
+    # every row sum on the device.
+    rows = heads * S
+    gen = torch.Generator(device="cuda").manual_seed(S)
+    x = (torch.randn(rows, S, generator=gen, device="cuda") * 4.0).to(TORCH_DTYPE[dtype])
+    m = (torch.randn(S, S, generator=gen, device="cuda") * 2.0).to(TORCH_DTYPE[dtype])
+    desc = rws.softmax_describe_launch(rows, S, rws.dtype_code(x.dtype), x.data_ptr(),
+                                       x.data_ptr(), masked=True)
+    assert desc.startswith(family), desc
+    out = torch.empty_like(x)
+    rws.softmax_masked(x, scale=0.125, mask=m, causal_q=S, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    assert (out.double().sum(dim=1) - 1.0).abs().max().item() <= 1e-2
+    rng = np.random.Generator(np.random.PCG64(S + 1))
+    ends = [h * S + r for h in range(0, heads, 8) for r in (0, 1, S - 2, S - 1)]
+    idx = np.unique(np.concatenate([np.array(ends), rng.integers(0, rows, 300)]))
+    ti = torch.from_numpy(idx).cuda()
+    xs = x.index_select(0, ti).double().cpu().numpy()
+    ms = m.double().cpu().numpy()
+    ref = np.empty((idx.size, S))
+    for k, r in enumerate(idx):
+        # the oracle on a block whose last row is global row r: same mask row
+        # and causal limit
+        full = oracle.masked_softmax(np.vstack([np.zeros((r % S, S)), xs[k:k + 1]]), 0.125, ms, S)
+        ref[k] = full[-1]
+    check(out.index_select(0, ti).double().cpu().numpy(), ref, dtype, f"{desc} sampled rows")
