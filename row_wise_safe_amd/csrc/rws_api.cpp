@@ -1594,7 +1594,9 @@ static int plan_norm(int64_t rows, int64_t cols, int dtype, const void* in, cons
         variant = pick_wave(kernel_id == RWS_KERNEL_AUTO ? 1 : 1 << 30);
         if (variant < 0)
             return fail(RWS_ERR_UNSUPPORTED_SHAPE, "normalisation wave kernel holds at most 512 granules");
-        aligned = wave_row_wa(rws::kNormWave[variant]) == 128 ? g.a128 : g.a16;
+        // with weight or bias, rows 16-byte aligned take row-start windows
+        // whatever the group (as the block form below)
+        aligned = wave_row_wa(rws::kNormWave[variant]) == 128 && !affine ? g.a128 : g.a16;
     } else if (family == 2) {
         variant = pick_block();
         if (variant < 0)
