@@ -43,7 +43,11 @@ namespace rws {
 // the element-by-element fallback is not compiled.  That fallback, present
 // in a kernel, costs registers even where no row takes it (fp16 norm_wave
 // (16,2) LayerNorm with weight and bias: 97 VGPRs with it, 59 without).
-template <int DT, class Win, bool PM = false>
+// BATCH: the fallback issues a granule's element loads before its first
+// wait (the lane groups: fp16 LayerNorm with weight and bias [131072,250]
+// 105 us against 144); the workgroup form keeps one wait per load, which
+// measured faster there ([55392,577] 104 us against 113.5).
+template <int DT, class Win, bool PM = false, bool BATCH = false>
 struct ColParam {
     static constexpr int VEC = Elem<DT>::VEC;
     static constexpr int ES = Elem<DT>::SIZE;
@@ -70,6 +74,17 @@ struct ColParam {
         const int c0 = k * VEC - w.lead;
         if (PM || (vec && c0 >= 0 && c0 + VEC <= w.cols)) {
             Elem<DT>::widen(raw, v);
+            return;
+        }
+        if (BATCH) {
+            // slots outside the row read column 0 instead
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const int c = c0 + e;
+                const bool in = c >= 0 && c < w.cols;
+                const float f = Elem<DT>::load1(p + (int64_t)(in ? c : 0) * ES);
+                v[e] = in ? f : 0.0f;
+            }
             return;
         }
 #pragma unroll
@@ -177,7 +192,7 @@ __global__ __launch_bounds__(256) void k_norm_wave(const void* __restrict__ in,
     constexpr int WA = G * 16 >= kLineBytes ? kLineBytes : 16;
     using Win = RowWin<DT, ALIGNED, WA>;
     static_assert(AFF != 2 || ALIGNED, "phase-matched parameters need aligned rows");
-    using CP = ColParam<DT, Win, AFF == 2>;
+    using CP = ColParam<DT, Win, AFF == 2, true>;
     const int lane = threadIdx.x & 63;
     const int gl = lane & (G - 1);
     const int sub = lane / G;
